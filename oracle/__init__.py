@@ -1,0 +1,9 @@
+"""fp64 CPU oracle of the hybrid block-sparse attention path (test infrastructure
+only: tests/, the smoke check and the benchmark's CPU-baseline leg use it; the
+GPU package never does)."""
+from .oracle import *  # noqa: F401,F403
+from .oracle import (Geometry, MaskResult, RowSelection, attention_block,
+                     block_scores, block_softmax, build_mask, ceil_k,
+                     dense_attention, pool, rank_order, real_slots, reorder,
+                     select_row, select_rows, sparse_attention, token_slots,
+                     top_p_count, unreorder, unreorder_rows, NEAR_TIE)

@@ -1,0 +1,354 @@
+"""Plain, slow fp64 CPU oracle of the hybrid block-sparse attention path.
+
+TEST INFRASTRUCTURE ONLY.  Only tests/, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of bench.py may import this module.  It shares no code with the
+GPU library (no kernels, headers, helpers or constants) and imports nothing from
+it; the two meet only in the seeded inputs from ``synth``.
+
+What it computes, step by step, in float64 (bfloat16 inputs convert exactly):
+
+1. Cube re-indexing of row-major video tokens.  VSA summary page ("VSA: Faster
+   Video Diffusion with Trainable Sparse Attention"), section "Cube Partitioning
+   and Token Re-Indexing": the block of token (t, h, w) is
+   (t//ct)*Nh*Nw + (h//ch)*Nw + (w//cw); the within-cube term of that formula
+   did not survive extraction, and row-major (t, h, w) order inside the cube is
+   the reading taken here.  Grids whose sides are not multiples of the cube are
+   padded per side ("Improving Video Sparse Attention with Fine-grained Router
+   and Sparse Rebasing", section 2.2, "Kernel Implementation"); pad slots are
+   excluded from pooling and masked out of attention.
+2. Mean pooling of Q and K per block (SpargeAttention2 summary page, section
+   "Block-Pooled Attention for Efficient Mask Construction", step 2; VSA page,
+   "The Coarse Stage"), over the block's real tokens only.
+3. Block scores S = Qbar Kbar^T / sqrt(d) and their row softmax P (SpargeAttention2
+   page, same section, step 3).
+4. Hybrid mask (SpargeAttention2 page, "The Hybrid Top-k+Top-p Masking Rule",
+   Eq. 9): per row, the union of Top-k (the ceil(k*Tn) largest entries) and
+   Top-p (the shortest prefix of the descending order whose cumulative
+   probability reaches or exceeds p).  Both are prefixes of one order (score
+   descending, lower block index first on equal scores), so the union is the
+   longer prefix, max(kc, pc).  Kept blocks are listed in ascending id.
+5. Block-sparse attention (SpargeAttention2 page, "Kernel Implementation of the
+   Hybrid-Masked Block-Sparse Attention", Algorithm 1, and the renormalised
+   sparse output o_s = (p*m/tau) V of "The Sparse Attention Error
+   Decomposition"): each real query token attends, with a softmax over exactly
+   the real keys of its row's kept blocks, to those keys; the natural-log
+   log-sum-exp of its scaled scores is returned beside it.  This is the plain
+   definition written out: no online softmax, no tiling.
+
+Readings where the pages are silent or garbled are listed in the repository's
+design notes; the ones this file depends on are repeated at each function.
+Every function here is pinned by the CPU tests (worked examples, closed forms,
+brute force, invariants, special cases).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+
+NEAR_TIE = 1e-6
+
+
+# ----------------------------------------------------------------------------
+# 1. geometry and re-indexing
+# ----------------------------------------------------------------------------
+@dataclass(frozen=True)
+class Geometry:
+    frames: int
+    height: int
+    width: int
+    ct: int = 4
+    ch: int = 4
+    cw: int = 4
+
+    @property
+    def block(self) -> int:
+        return self.ct * self.ch * self.cw
+
+    @property
+    def nt(self) -> int:
+        return -(-self.frames // self.ct)
+
+    @property
+    def nh(self) -> int:
+        return -(-self.height // self.ch)
+
+    @property
+    def nw(self) -> int:
+        return -(-self.width // self.cw)
+
+    @property
+    def nblk(self) -> int:
+        return self.nt * self.nh * self.nw
+
+    @property
+    def n_real(self) -> int:
+        return self.frames * self.height * self.width
+
+    @property
+    def n_pad(self) -> int:
+        return self.nblk * self.block
+
+
+def token_slots(g: Geometry) -> np.ndarray:
+    """Cube-major padded slot of every row-major token n = t*H*W + h*W + w."""
+    t, h, w = np.meshgrid(np.arange(g.frames), np.arange(g.height),
+                          np.arange(g.width), indexing="ij")
+    t, h, w = t.reshape(-1), h.reshape(-1), w.reshape(-1)
+    blk = (t // g.ct) * (g.nh * g.nw) + (h // g.ch) * g.nw + (w // g.cw)
+    within = ((t % g.ct) * g.ch + (h % g.ch)) * g.cw + (w % g.cw)
+    return blk * g.block + within
+
+
+def real_slots(g: Geometry) -> np.ndarray:
+    """Boolean [n_pad]: True where a slot holds a real token."""
+    m = np.zeros(g.n_pad, dtype=bool)
+    m[token_slots(g)] = True
+    return m
+
+
+def reorder(x: np.ndarray, g: Geometry) -> np.ndarray:
+    """[..., N, d] row-major tokens -> [..., n_pad, d] cube-major, pads = 0."""
+    out = np.zeros(x.shape[:-2] + (g.n_pad, x.shape[-1]), dtype=x.dtype)
+    out[..., token_slots(g), :] = x
+    return out
+
+
+def unreorder(xc: np.ndarray, g: Geometry) -> np.ndarray:
+    """Inverse of reorder: [..., n_pad, d] -> [..., N, d] (pad slots dropped)."""
+    return xc[..., token_slots(g), :]
+
+
+def unreorder_rows(xc: np.ndarray, g: Geometry) -> np.ndarray:
+    """Inverse re-indexing of a per-token scalar: [..., n_pad] -> [..., N]."""
+    return xc[..., token_slots(g)]
+
+
+# ----------------------------------------------------------------------------
+# 2.-3. pooling, block scores, block softmax
+# ----------------------------------------------------------------------------
+def pool(xc: np.ndarray, g: Geometry) -> np.ndarray:
+    """Mean of each block's real tokens: [..., n_pad, d] -> [..., nblk, d]."""
+    xc = np.asarray(xc, dtype=np.float64)
+    d = xc.shape[-1]
+    blocks = xc.reshape(xc.shape[:-2] + (g.nblk, g.block, d))
+    real = real_slots(g).reshape(g.nblk, g.block)
+    total = (blocks * real[..., None]).sum(axis=-2)
+    return total / real.sum(axis=1)[:, None]
+
+
+def block_scores(qbar: np.ndarray, kbar: np.ndarray, d: int) -> np.ndarray:
+    """S = Qbar Kbar^T / sqrt(d) over the last two axes."""
+    return np.matmul(qbar, np.swapaxes(kbar, -1, -2)) / math.sqrt(d)
+
+
+def block_softmax(s: np.ndarray) -> np.ndarray:
+    """Row softmax in float64."""
+    e = np.exp(s - s.max(axis=-1, keepdims=True))
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+# ----------------------------------------------------------------------------
+# 4. hybrid Top-k U Top-p selection
+# ----------------------------------------------------------------------------
+def ceil_k(k_frac: float, n: int) -> int:
+    """Top-k count ceil(k * n).  Reading: k * n is meant in decimal arithmetic,
+    so a binary-representation excess below 1e-9 does not round up (0.07 * 100
+    is 7, not 8); the SpargeAttention2 page's worked count, 3% of 1562 blocks
+    being 47, holds either way."""
+    if n <= 0:
+        return 0
+    c = math.ceil(k_frac * n - 1e-9)
+    return int(min(max(c, 0), n))
+
+
+def rank_order(s_row: np.ndarray) -> np.ndarray:
+    """Block ids sorted by score descending, lower id first on equal scores."""
+    j = np.arange(s_row.shape[0])
+    return np.lexsort((j, -s_row))
+
+
+@dataclass
+class RowSelection:
+    kept: np.ndarray        # ascending block ids
+    kc: int
+    pc: int
+    near_tie: bool
+    order: np.ndarray
+    cum: np.ndarray         # cumulative probability along `order`
+
+
+def top_p_count(cum: np.ndarray, p: float) -> int:
+    """Length of the shortest prefix whose cumulative probability >= p.
+    p <= 0 keeps nothing and p >= 1 keeps everything (the exact-arithmetic
+    answer, since no softmax entry is 0)."""
+    n = cum.shape[0]
+    if p <= 0.0:
+        return 0
+    if p >= 1.0:
+        return n
+    hit = np.nonzero(cum >= p)[0]
+    return int(hit[0]) + 1 if hit.size else n
+
+
+def select_row(s_row: np.ndarray, kc: int, p: float,
+               probs: Optional[np.ndarray] = None) -> RowSelection:
+    """Hybrid selection for one query block's row of block scores.
+
+    ``probs`` defaults to the row softmax of ``s_row``; a test may pass exact
+    probabilities for a worked example (the order still comes from s_row)."""
+    s_row = np.asarray(s_row, dtype=np.float64)
+    n = s_row.shape[0]
+    if probs is None:
+        probs = block_softmax(s_row)
+    order = rank_order(s_row)
+    cum = np.cumsum(probs[order])
+    pc = top_p_count(cum, p)
+    keep = max(kc, pc)
+    kept = np.sort(order[:keep])
+    near = _near_tie(s_row, order, cum, kc, pc, keep, p)
+    return RowSelection(kept, kc, pc, near, order, cum)
+
+
+def _near_tie(s_row, order, cum, kc, pc, keep, p) -> bool:
+    """True when a perturbation of relative size < 1e-6 could change the kept
+    set: (i) the last kept and first dropped scores differ by less than 1e-6 of
+    the row's largest |score|; (ii) some prefix length whose cumulative
+    probability lies within 1e-6 of p would give a different max(kc, pc)."""
+    n = s_row.shape[0]
+    scale = float(np.max(np.abs(s_row))) if n else 0.0
+    if 0 < keep < n:
+        gap = s_row[order[keep - 1]] - s_row[order[keep]]
+        if gap <= NEAR_TIE * scale:
+            return True
+    if 0.0 < p < 1.0:
+        prefix = np.concatenate(([0.0], cum))          # prefix[m] = sum of first m
+        close = np.nonzero(np.abs(prefix - p) < NEAR_TIE)[0]
+        for m in close:
+            # the perturbed Top-p count is m (if prefix[m] >= p) or m + 1
+            for alt in (int(m), int(m) + 1):
+                if 0 <= alt <= n and max(kc, alt) != keep:
+                    return True
+    return False
+
+
+@dataclass
+class MaskResult:
+    lut: np.ndarray         # [B, H, nblk, nblk] int32, -1 beyond counts
+    counts: np.ndarray      # [B, H, nblk] int32
+    near_tie: np.ndarray    # [B, H, nblk] bool
+    kc: np.ndarray          # [B, H, nblk] int32
+    pc: np.ndarray          # [B, H, nblk] int32
+    scores: np.ndarray      # [B, H, nblk, nblk] float64
+    qbar: np.ndarray
+    kbar: np.ndarray
+
+
+def build_mask(qc: np.ndarray, kc_: np.ndarray, g: Geometry, k_frac: float,
+               p: float, row_budget: Optional[np.ndarray] = None) -> MaskResult:
+    """Pool -> block scores -> hybrid selection for cube-major Q, K
+    [B, H, n_pad, d].  With ``row_budget`` [B, H, nblk] each row keeps exactly
+    its own count of top-scoring blocks (p must be 0): a per-query budget drawn
+    independently of the scores, the variable-count case of the VSA2 page."""
+    d = qc.shape[-1]
+    qbar = pool(qc, g)
+    kbar = pool(kc_, g)
+    s = block_scores(qbar, kbar, d)
+    B, H, n, _ = s.shape
+    lut = np.full((B, H, n, n), -1, dtype=np.int32)
+    counts = np.zeros((B, H, n), dtype=np.int32)
+    flags = np.zeros((B, H, n), dtype=bool)
+    kcs = np.zeros((B, H, n), dtype=np.int32)
+    pcs = np.zeros((B, H, n), dtype=np.int32)
+    k_default = ceil_k(k_frac, n)
+    for b in range(B):
+        for h in range(H):
+            probs = block_softmax(s[b, h])
+            for i in range(n):
+                kc_i = k_default if row_budget is None else int(row_budget[b, h, i])
+                sel = select_row(s[b, h, i], kc_i, p, probs[i])
+                c = sel.kept.shape[0]
+                lut[b, h, i, :c] = sel.kept
+                counts[b, h, i] = c
+                flags[b, h, i] = sel.near_tie
+                kcs[b, h, i] = kc_i
+                pcs[b, h, i] = sel.pc
+    return MaskResult(lut, counts, flags, kcs, pcs, s, qbar, kbar)
+
+
+def select_rows(s: np.ndarray, kc: int, p: float) -> List[RowSelection]:
+    """Hybrid selection of every row of one head's [nblk, nblk] score matrix."""
+    probs = block_softmax(s)
+    return [select_row(s[i], kc, p, probs[i]) for i in range(s.shape[0])]
+
+
+# ----------------------------------------------------------------------------
+# 5. block-sparse attention (renormalised over the kept real keys)
+# ----------------------------------------------------------------------------
+def attention_block(qc_h: np.ndarray, kc_h: np.ndarray, vc_h: np.ndarray,
+                    kept: Sequence[int], g: Geometry, i: int,
+                    scale: Optional[float] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """O [block, d] and LSE [block] of query block i of one (batch, head).
+
+    Each real query attends to the real keys of the kept blocks with a softmax
+    over exactly those keys; pad query slots, and every slot of a row that keeps
+    no block, get O = 0 and LSE = -inf."""
+    B_ = g.block
+    d = qc_h.shape[-1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    real = real_slots(g)
+    o = np.zeros((B_, d), dtype=np.float64)
+    lse = np.full(B_, -np.inf, dtype=np.float64)
+    kept = list(kept)
+    if not kept:
+        return o, lse
+    key_slots = np.concatenate([np.arange(j * B_, (j + 1) * B_) for j in kept])
+    key_slots = key_slots[real[key_slots]]
+    k = np.asarray(kc_h[key_slots], dtype=np.float64)
+    v = np.asarray(vc_h[key_slots], dtype=np.float64)
+    q_slots = np.arange(i * B_, (i + 1) * B_)
+    qmask = real[q_slots]
+    q = np.asarray(qc_h[q_slots[qmask]], dtype=np.float64)
+    s = (q @ k.T) * scale
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    l = e.sum(axis=1, keepdims=True)
+    o[qmask] = (e @ v) / l
+    lse[qmask] = (m + np.log(l))[:, 0]
+    return o, lse
+
+
+def sparse_attention(qc: np.ndarray, kc_: np.ndarray, vc: np.ndarray,
+                     lut: np.ndarray, counts: np.ndarray, g: Geometry,
+                     scale: Optional[float] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Block-sparse attention of every row: O [B, H, n_pad, d], LSE [B, H, n_pad]."""
+    B, H, n_pad, d = qc.shape
+    o = np.zeros((B, H, n_pad, d), dtype=np.float64)
+    lse = np.full((B, H, n_pad), -np.inf, dtype=np.float64)
+    blk = g.block
+    for b in range(B):
+        for h in range(H):
+            for i in range(g.nblk):
+                kept = lut[b, h, i, :counts[b, h, i]]
+                ob, lb = attention_block(qc[b, h], kc_[b, h], vc[b, h], kept, g, i, scale)
+                o[b, h, i * blk:(i + 1) * blk] = ob
+                lse[b, h, i * blk:(i + 1) * blk] = lb
+    return o, lse
+
+
+def dense_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
+                    scale: Optional[float] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Full softmax attention over the last two axes, O and natural-log LSE."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    s = np.matmul(q, np.swapaxes(k, -1, -2)) * scale
+    m = s.max(axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    l = e.sum(axis=-1, keepdims=True)
+    return np.matmul(e, v) / l, (m + np.log(l))[..., 0]

@@ -1,0 +1,486 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+None of these re-types the oracle's own formula: each checks it against a
+printed worked value, a closed form, a brute-force enumeration, an invariant,
+a special case with a known answer, or an independent library routine.
+"""
+import itertools
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle as O
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")
+
+
+@pytest.fixture(scope="module")
+def golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+# ----------------------------------------------------------------------------
+# worked examples printed on the pages
+# ----------------------------------------------------------------------------
+def test_topk_count_worked_example(golden):
+    g = golden["topk_count"]
+    assert O.ceil_k(g["k_frac"], g["n_blocks"]) == g["kept"]
+
+
+def test_ceil_k_edges():
+    assert O.ceil_k(0.07, 100) == 7          # binary excess must not round up
+    assert O.ceil_k(0.05, 1440) == 72
+    assert O.ceil_k(0.03, 1440) == 44
+    assert O.ceil_k(0.02, 1440) == 29
+    assert O.ceil_k(0.05, 624) == 32
+    assert O.ceil_k(0.25, 16) == 4
+    assert O.ceil_k(0.0, 16) == 0
+    assert O.ceil_k(1.0, 16) == 16
+    assert O.ceil_k(2.0, 16) == 16
+    assert O.ceil_k(-1.0, 16) == 0
+    assert O.ceil_k(1e-6, 16) == 1
+
+
+def _row_from_probs(probs):
+    """Scores whose softmax order matches the given probabilities."""
+    return np.log(np.asarray(probs, dtype=np.float64))
+
+
+def test_topp_sink_row_worked_example(golden):
+    g = golden["topp_sink_row"]
+    probs = np.asarray(g["probs"], dtype=np.float64)
+    sel = O.select_row(_row_from_probs(probs), 0, g["p"], probs)
+    assert list(sel.kept) == g["topp_kept"]
+    assert sel.pc == 1
+    # the hybrid union with a Top-k floor of 2 adds the informative block
+    sel2 = O.select_row(_row_from_probs(probs), 2, g["p"], probs)
+    assert list(sel2.kept) == [0, 1]
+
+
+def test_error_decomposition_worked_example(golden):
+    ex = golden["error_decomposition_example"]
+    for key in ("before", "after"):
+        p = np.asarray(ex[key]["probs"])
+        m = np.asarray(ex[key]["mask"])
+        assert (p * (1 - m)).sum() == pytest.approx(ex[key]["dropped_mass"], abs=1e-15)
+
+
+def test_vsa_sparsity_worked_example(golden):
+    ex = golden["vsa_sparsity"]
+    g = O.Geometry(16, 32, 32)                   # 16384 tokens, 4x8x8 = 256 cubes
+    assert g.n_real == ex["tokens"] and g.block == ex["cube"]
+    rng = np.random.default_rng(5)
+    s = rng.standard_normal((g.nblk, g.nblk))
+    kc = O.ceil_k(ex["kept_per_row"] / g.nblk, g.nblk)
+    rows = O.select_rows(s, kc, 0.0)
+    kept = sum(r.kept.size for r in rows)
+    assert 1 - kept / g.nblk ** 2 == pytest.approx(ex["sparsity"], abs=1e-15)
+
+
+def test_uniform_row_topp_keeps_fraction(golden):
+    ex = golden["uniform_row_topp"]
+    n = ex["n_blocks"]
+    sel = O.select_row(np.zeros(n), 0, ex["p"])
+    assert sel.kept.size == ex["kept"]
+    assert list(sel.kept) == list(range(ex["kept"]))   # lower ids first on ties
+
+
+# ----------------------------------------------------------------------------
+# geometry: closed form of the cube index, padding, round trip
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("grid", [(4, 16, 16), (5, 7, 9), (21, 30, 52), (1, 1, 1), (8, 4, 12)])
+def test_token_slots_closed_form(grid):
+    T, H, W = grid
+    g = O.Geometry(T, H, W)
+    slots = O.token_slots(g)
+    assert slots.shape == (T * H * W,)
+    assert np.unique(slots).size == slots.size                 # injective
+    assert slots.min() >= 0 and slots.max() < g.n_pad
+    assert g.n_pad - g.n_real == g.n_pad - slots.size           # pads = the rest
+    nt, nh, nw = -(-T // 4), -(-H // 4), -(-W // 4)
+    n = 0
+    for t in range(T):
+        for h in range(H):
+            for w in range(W):
+                cube = (t // 4) * nh * nw + (h // 4) * nw + (w // 4)
+                assert slots[n] // 64 == cube
+                n += 1
+    assert g.nblk == nt * nh * nw
+
+
+def test_reorder_round_trip_and_pads():
+    g = O.Geometry(5, 7, 9)
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((2, 3, g.n_real, 8))
+    xc = O.reorder(x, g)
+    assert xc.shape == (2, 3, g.n_pad, 8)
+    assert np.array_equal(O.unreorder(xc, g), x)
+    real = O.real_slots(g)
+    assert real.sum() == g.n_real
+    assert np.all(xc[..., ~real, :] == 0)
+
+
+def test_real_slot_counts_per_block():
+    # 21 x 45 x 80: the last temporal cube holds 1 of 4 frames, the last row-cube 1 of 4 rows
+    g = O.Geometry(21, 45, 80)
+    real = O.real_slots(g).reshape(g.nblk, 64).sum(axis=1)
+    assert g.nblk == 6 * 12 * 20 and g.n_pad == 92160
+    assert set(np.unique(real).tolist()) == {64, 16, 4}
+    assert real.sum() == 75600
+
+
+# ----------------------------------------------------------------------------
+# pooling: mean over each cube's real tokens, gathered by coordinates
+# ----------------------------------------------------------------------------
+def test_pool_equals_coordinate_gather_mean():
+    T, H, W, d = 5, 6, 9, 4
+    g = O.Geometry(T, H, W)
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((T * H * W, d))
+    got = O.pool(O.reorder(x, g), g)
+    want = np.zeros((g.nblk, d))
+    grid = x.reshape(T, H, W, d)
+    for bt in range(g.nt):
+        for bh in range(g.nh):
+            for bw in range(g.nw):
+                cube = grid[4 * bt:4 * bt + 4, 4 * bh:4 * bh + 4, 4 * bw:4 * bw + 4]
+                want[(bt * g.nh + bh) * g.nw + bw] = cube.reshape(-1, d).mean(axis=0)
+    np.testing.assert_allclose(got, want, rtol=1e-14, atol=1e-15)
+
+
+def test_pool_constant_block():
+    g = O.Geometry(6, 6, 6)
+    x = np.full((g.n_real, 3), 0.375)
+    np.testing.assert_array_equal(O.pool(O.reorder(x, g), g), 0.375)
+
+
+# ----------------------------------------------------------------------------
+# block scores + softmax against library routines
+# ----------------------------------------------------------------------------
+def test_block_probs_match_library_attention():
+    """softmax(Qbar Kbar^T / sqrt(d)) is the weight matrix that scaled
+    dot-product attention applies; with V = I the library returns it."""
+    rng = np.random.default_rng(3)
+    n, d = 12, 16
+    qb, kb = rng.standard_normal((n, d)), rng.standard_normal((n, d))
+    p = O.block_softmax(O.block_scores(qb, kb, d))
+    t = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(qb)[None], torch.from_numpy(kb)[None],
+        torch.eye(n, dtype=torch.float64)[None])[0].numpy()
+    np.testing.assert_allclose(p, t, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(p, scipy.special.softmax(qb @ kb.T / 4.0, axis=1), rtol=1e-13)
+    np.testing.assert_allclose(p.sum(axis=1), 1.0, rtol=1e-15)
+
+
+# ----------------------------------------------------------------------------
+# hybrid selection: brute force over all subsets on tiny rows
+# ----------------------------------------------------------------------------
+def _brute_force_union(probs, kc, p):
+    """Top-k = the size-kc subset of largest mass; Top-p = the smallest subset
+    whose mass reaches p (largest mass among those); ties between equal-mass
+    subsets go to the lexicographically smallest sorted id tuple.  Exact
+    rational sums; no sorting of the row is used."""
+    n = len(probs)
+    fr = [Fraction(float(x)) for x in probs]
+    total = sum(fr)
+    target = Fraction(p) * total
+
+    def best_of_size(size, need=None):
+        best = None
+        for sub in itertools.combinations(range(n), size):
+            m = sum(fr[j] for j in sub)
+            if need is not None and m < need:
+                continue
+            key = (-m, sub)
+            if best is None or key < best[0]:
+                best = (key, sub)
+        return None if best is None else set(best[1])
+
+    topk = best_of_size(kc) if kc > 0 else set()
+    if p <= 0:
+        topp = set()
+    elif p >= 1:
+        topp = set(range(n))
+    else:
+        topp = None
+        for size in range(0, n + 1):
+            topp = best_of_size(size, target)
+            if topp is not None:
+                break
+    return sorted(topk | topp)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_select_matches_brute_force(seed):
+    rng = np.random.default_rng(100 + seed)
+    n = int(rng.integers(1, 10))
+    spread = [0.05, 1.0, 4.0][seed % 3]
+    s = rng.standard_normal(n) * spread
+    if seed % 4 == 0 and n > 2:
+        s[0] += 6.0                                 # a sink block
+    probs = O.block_softmax(s)
+    for kc in sorted({0, 1, n // 2, n}):
+        for p in (0.0, 0.1, 0.5, 0.85, 0.99, 1.0):
+            sel = O.select_row(s, kc, p, probs)
+            if sel.near_tie:
+                continue
+            assert list(sel.kept) == _brute_force_union(probs, kc, p), (n, kc, p)
+
+
+def test_select_brute_force_with_exact_ties():
+    # dyadic probabilities with repeats: ties must go to the lower block id
+    probs = np.array([0.125, 0.25, 0.125, 0.25, 0.125, 0.125])
+    s = np.log(probs)
+    for kc in range(0, 7):
+        for p in (0.0, 0.25, 0.3, 0.5, 0.6, 0.75, 0.9):
+            sel = O.select_row(s, kc, p, probs)
+            assert list(sel.kept) == _brute_force_union(probs, kc, p), (kc, p)
+
+
+# ----------------------------------------------------------------------------
+# hybrid selection: invariants and special cases
+# ----------------------------------------------------------------------------
+def _check_invariants(s, probs, sel, kc, p):
+    kept = set(sel.kept.tolist())
+    n = s.size
+    assert len(kept) >= kc
+    mass = probs[list(kept)].sum() if kept else 0.0
+    if not sel.near_tie and 0 < p < 1:
+        assert mass >= p - 1e-12
+    dropped = [j for j in range(n) if j not in kept]
+    for a in kept:                                   # every kept outranks every dropped
+        for b in dropped:
+            assert s[a] > s[b] or (s[a] == s[b] and a < b)
+    if kept:                                         # minimality
+        last = sel.order[len(kept) - 1]
+        smaller = len(kept) - 1
+        smaller_mass = mass - probs[last]
+        assert smaller < kc or (p > 0 and smaller_mass < p + 1e-12) or sel.near_tie
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_select_invariants_random_rows(seed):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(2, 400))
+    s = rng.standard_normal(n) * float(rng.choice([0.01, 0.3, 2.0, 8.0]))
+    probs = O.block_softmax(s)
+    kc = int(rng.integers(0, n + 1))
+    p = float(rng.choice([0.0, 0.2, 0.5, 0.8, 0.9, 0.97, 1.0]))
+    sel = O.select_row(s, kc, p, probs)
+    _check_invariants(s, probs, sel, kc, p)
+
+
+def test_select_special_cases():
+    n = 16
+    zero = np.zeros(n)
+    assert O.select_row(zero, 0, 0.0).kept.size == 0            # k = p = 0 keeps none
+    assert list(O.select_row(zero, n, 0.0).kept) == list(range(n))
+    rng = np.random.default_rng(7)
+    s = rng.standard_normal(n)
+    assert list(O.select_row(s, 0, 1.0).kept) == list(range(n))  # p >= 1 keeps all
+    assert list(O.select_row(s, n, 0.3).kept) == list(range(n))  # k = all keeps all
+    # all-tied row (Q = 0): kept = the first max(kc, ceil(p n)) ids
+    for kc, p, want in [(2, 0.25, 4), (6, 0.25, 6), (0, 0.5, 8), (3, 0.0, 3)]:
+        assert list(O.select_row(zero, kc, p).kept) == list(range(want))
+
+
+def test_select_sink_row_takes_topk_floor():
+    """A sink-dominated row: Top-p collapses to the sink, Top-k adds the rest."""
+    n = 40
+    s = np.linspace(0.0, -1.0, n)
+    s[17] = 8.0                                     # sink at block 17
+    probs = O.block_softmax(s)
+    assert probs[17] > 0.9
+    sel = O.select_row(s, 5, 0.8, probs)
+    assert sel.pc == 1 and sel.kc == 5
+    assert list(sel.kept) == [0, 1, 2, 3, 17]
+
+
+def test_select_uniform_row_takes_topp():
+    n = 64
+    sel = O.select_row(np.zeros(n), 2, 0.25)
+    assert sel.pc == 16 and list(sel.kept) == list(range(16))
+
+
+def test_near_tie_flags():
+    s = np.array([1.0, 1.0 - 1e-9, 0.0, -1.0])
+    assert O.select_row(s, 1, 0.0).near_tie            # value margin 1e-9 < 1e-6
+    assert not O.select_row(s, 2, 0.0).near_tie
+    probs = np.array([0.5, 0.25, 0.125, 0.125])
+    assert O.select_row(np.log(probs), 0, 0.75, probs).near_tie   # cum == p exactly
+    assert not O.select_row(np.log(probs), 0, 0.7, probs).near_tie
+
+
+# ----------------------------------------------------------------------------
+# attention: dense equivalence, masked-dense brute force, Eq. 8, closed forms
+# ----------------------------------------------------------------------------
+def _tiny_inputs(grid=(4, 16, 16), heads=2, d=64, seed=0):
+    wl = synth.custom_workload(1, heads, d, *grid, head_types=["uniform", "skewed", "local"][:heads])
+    q, k, v = synth.make_qkv(wl, seed)
+    return wl, q.double().numpy(), k.double().numpy(), v.double().numpy()
+
+
+def test_all_blocks_kept_equals_dense_library_attention():
+    wl, q, k, v = _tiny_inputs(grid=(5, 6, 7), heads=2, d=32)
+    g = O.Geometry(*wl.grid)
+    qc, kc, vc = (O.reorder(x, g) for x in (q, k, v))
+    m = O.build_mask(qc, kc, g, 1.0, 0.0)
+    assert np.all(m.counts == g.nblk)
+    oc, lsec = O.sparse_attention(qc, kc, vc, m.lut, m.counts, g)
+    o = O.unreorder(oc, g)
+    lse = O.unreorder_rows(lsec, g)
+    tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+    want = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv).numpy()
+    np.testing.assert_allclose(o, want, rtol=1e-12, atol=1e-12)
+    want_lse = torch.logsumexp(tq @ tk.transpose(-1, -2) / math.sqrt(32), dim=-1).numpy()
+    np.testing.assert_allclose(lse, want_lse, rtol=1e-12, atol=1e-12)
+    # p = 1 must give the same as keeping every block
+    m1 = O.build_mask(qc, kc, g, 0.0, 1.0)
+    assert np.array_equal(m1.counts, m.counts)
+
+
+def test_block_sparse_equals_token_masked_dense():
+    """The block mask broadcast to tokens, applied as -inf in a dense masked
+    softmax over row-major tokens, gives the same O and LSE."""
+    wl, q, k, v = _tiny_inputs()
+    g = O.Geometry(*wl.grid)
+    qc, kc, vc = (O.reorder(x, g) for x in (q, k, v))
+    m = O.build_mask(qc, kc, g, 0.25, 0.5)
+    oc, lsec = O.sparse_attention(qc, kc, vc, m.lut, m.counts, g)
+    o, lse = O.unreorder(oc, g), O.unreorder_rows(lsec, g)
+    blk_of_token = O.token_slots(g) // 64
+    for h in range(q.shape[1]):
+        allow = np.zeros((g.nblk, g.nblk), dtype=bool)
+        for i in range(g.nblk):
+            allow[i, m.lut[0, h, i, :m.counts[0, h, i]]] = True
+        tok_allow = allow[blk_of_token][:, blk_of_token]
+        tq, tk, tv = (torch.from_numpy(x[0, h]) for x in (q, k, v))
+        want = torch.nn.functional.scaled_dot_product_attention(
+            tq[None], tk[None], tv[None], attn_mask=torch.from_numpy(tok_allow)[None])[0].numpy()
+        np.testing.assert_allclose(o[0, h], want, rtol=1e-12, atol=1e-12)
+        s = (tq @ tk.T).numpy() / math.sqrt(q.shape[-1])
+        s[~tok_allow] = -np.inf
+        np.testing.assert_allclose(lse[0, h], scipy.special.logsumexp(s, axis=1), rtol=1e-12)
+
+
+def test_error_decomposition_identity():
+    """Eq. 8: o - o_s = (p*(1-m) + (1 - 1/tau) p*m) V for the oracle's o_s."""
+    wl, q, k, v = _tiny_inputs(heads=1)
+    g = O.Geometry(*wl.grid)
+    qc, kc, vc = (O.reorder(x, g) for x in (q, k, v))
+    mres = O.build_mask(qc, kc, g, 0.25, 0.3)
+    oc, _ = O.sparse_attention(qc, kc, vc, mres.lut, mres.counts, g)
+    o_full, _ = O.dense_attention(qc[0, 0], kc[0, 0], vc[0, 0])  # no pads in this grid
+    d = q.shape[-1]
+    for i in range(g.nblk):
+        m = np.zeros(g.n_pad)
+        for j in mres.lut[0, 0, i, :mres.counts[0, 0, i]]:
+            m[j * 64:(j + 1) * 64] = 1.0
+        for r in range(i * 64, i * 64 + 64, 9):
+            s = qc[0, 0, r] @ kc[0, 0].T / math.sqrt(d)
+            p = scipy.special.softmax(s)
+            tau = (p * m).sum()
+            e = (p * (1 - m) + (1 - 1 / tau) * (p * m)) @ vc[0, 0]
+            np.testing.assert_allclose(o_full[r] - oc[0, 0, r], e, rtol=1e-9, atol=1e-12)
+
+
+def test_zero_queries_average_kept_values():
+    g = O.Geometry(5, 6, 7)                       # ragged: pad keys must be excluded
+    rng = np.random.default_rng(11)
+    d = 16
+    kc = O.reorder(rng.standard_normal((g.n_real, d)), g)
+    vc = O.reorder(rng.standard_normal((g.n_real, d)), g)
+    qc = np.zeros_like(kc)
+    real = O.real_slots(g)
+    kept = [0, 3, g.nblk - 1]
+    for i in (0, g.nblk - 1):
+        o, lse = O.attention_block(qc, kc, vc, kept, g, i)
+        slots = np.concatenate([np.arange(j * 64, j * 64 + 64) for j in kept])
+        slots = slots[real[slots]]
+        qreal = real[i * 64:(i + 1) * 64]
+        np.testing.assert_allclose(o[qreal], np.broadcast_to(vc[slots].mean(axis=0), o[qreal].shape), rtol=1e-13)
+        np.testing.assert_allclose(lse[qreal], math.log(slots.size), rtol=1e-14)
+        assert np.all(o[~qreal] == 0) and np.all(np.isneginf(lse[~qreal]))
+
+
+def test_attention_normalisation_and_hull():
+    g = O.Geometry(4, 8, 8)
+    rng = np.random.default_rng(12)
+    d = 8
+    qc, kc, vc = (O.reorder(rng.standard_normal((g.n_real, d)) * 2, g) for _ in range(3))
+    kept = [1, 2]
+    o, lse = O.attention_block(qc, kc, vc, kept, g, 0)
+    keys = np.concatenate([kc[64:128], kc[128:192]])
+    vals = np.concatenate([vc[64:128], vc[128:192]])
+    s = qc[:64] @ keys.T / math.sqrt(d)
+    np.testing.assert_allclose(np.exp(s - lse[:, None]).sum(axis=1), 1.0, rtol=1e-13)
+    assert np.all(o <= vals.max(axis=0) + 1e-12) and np.all(o >= vals.min(axis=0) - 1e-12)
+
+
+def test_empty_row_gives_zero_and_neg_inf():
+    g = O.Geometry(4, 4, 8)
+    x = np.ones((g.n_pad, 4))
+    o, lse = O.attention_block(x, x, x, [], g, 1)
+    assert np.all(o == 0) and np.all(np.isneginf(lse))
+
+
+def test_within_cube_order_does_not_matter():
+    """The within-cube term of the cube index did not survive extraction; any
+    order inside a cube gives the same pooled scores, mask and per-token output."""
+    wl, q, k, v = _tiny_inputs(grid=(5, 6, 7), heads=1, d=16)
+    g = O.Geometry(*wl.grid)
+    qc, kc, vc = (O.reorder(x, g) for x in (q, k, v))
+    rng = np.random.default_rng(9)
+    perm = np.concatenate([b * 64 + rng.permutation(64) for b in range(g.nblk)])
+
+    def permute(x):
+        return x[..., perm, :]
+    m1 = O.build_mask(qc, kc, g, 0.3, 0.7)
+    # pad slots move with the permutation, so the oracle's slot-validity map
+    # must follow: check pooled values directly by per-block means instead
+    np.testing.assert_allclose(O.pool(qc, g), m1.qbar)
+    real = O.real_slots(g)[perm]
+    qp, kp, vp = permute(qc), permute(kc), permute(vc)
+    blocks = qp.reshape(1, 1, g.nblk, 64, -1)
+    means = (blocks * real.reshape(g.nblk, 64)[..., None]).sum(3) / real.reshape(g.nblk, 64).sum(1)[:, None]
+    np.testing.assert_allclose(means, m1.qbar, rtol=1e-13, atol=1e-15)
+    # attention per real token is the same whichever slot the token sits in
+    oc, lsec = O.sparse_attention(qc, kc, vc, m1.lut, m1.counts, g)
+    for i in range(g.nblk):
+        kept = m1.lut[0, 0, i, :m1.counts[0, 0, i]]
+        ks = np.concatenate([perm[j * 64:(j + 1) * 64] for j in kept])
+        ks = ks[O.real_slots(g)[ks]]
+        for r in range(i * 64, i * 64 + 64):
+            src = perm[r]
+            if not O.real_slots(g)[src] or src // 64 != i:
+                continue
+            s = qc[0, 0, src] @ kc[0, 0, ks].T / math.sqrt(16)
+            w = scipy.special.softmax(s)
+            np.testing.assert_allclose(w @ vc[0, 0, ks], oc[0, 0, src], rtol=1e-12, atol=1e-13)
+
+
+def test_pool_ignores_pad_slot_contents():
+    """Pad slots are not tokens: whatever they hold must not reach the means."""
+    g = O.Geometry(5, 6, 9)
+    rng = np.random.default_rng(21)
+    xc = O.reorder(rng.standard_normal((g.n_real, 4)), g)
+    dirty = xc.copy()
+    dirty[~O.real_slots(g)] = 1e3
+    np.testing.assert_array_equal(O.pool(dirty, g), O.pool(xc, g))
+
+
+def test_p_one_keeps_every_block_even_when_sums_saturate():
+    """With p >= 1 every block is kept, also where the float cumulative sum
+    already rounds to 1 before the last (negligible) blocks."""
+    s = np.array([0.0, -50.0, -50.0, -60.0, -70.0])
+    probs = O.block_softmax(s)
+    assert np.cumsum(probs)[0] == 1.0                 # saturated after one block
+    assert list(O.select_row(s, 0, 1.0, probs).kept) == [0, 1, 2, 3, 4]
