@@ -1,0 +1,270 @@
+"""MI355X (gfx950) hybrid Top-k U Top-p block-sparse attention for video DiTs.
+
+Thin ctypes binding over ``libsparse_attn.so`` (C ABI in include/sparse_attn.h).
+The functions named ``sparse_attn_*`` mirror the C entry points one to one:
+they take torch tensors that already live on the GPU, pass their pointers and
+the current HIP stream, and raise :class:`SparseAttnError` on a negative status.
+Every step of the path runs in the library's HIP kernels; this module only
+marshals arguments (and, in the allocating helpers at the bottom, creates
+output tensors with ``torch.empty``).  There is no CPU fallback: without the
+built library the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsparse_attn.so")
+
+SA_OK = 0
+SA_ERR_INVALID_ARG = -1
+SA_ERR_UNSUPPORTED = -2
+SA_ERR_CAPACITY = -3
+SA_ERR_HIP = -4
+
+EXPORTED = (
+    "sparse_attn_geometry", "sparse_attn_ceil_k", "sparse_attn_reorder",
+    "sparse_attn_unreorder", "sparse_attn_pool", "sparse_attn_block_scores",
+    "sparse_attn_select", "sparse_attn_mask_workspace_bytes",
+    "sparse_attn_build_mask", "sparse_attn_fwd_workspace_bytes", "sparse_attn_fwd",
+    "sparse_attn_last_error",
+)
+
+
+class SparseAttnError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"sparse_attn error {code}: {message}")
+        self.code = code
+
+
+class Geom(ctypes.Structure):
+    """sa_geom of the C ABI."""
+    _fields_ = [(name, ctypes.c_int32) for name in (
+        "batch", "heads", "frames", "height", "width", "head_dim",
+        "cube_t", "cube_h", "cube_w")]
+
+    def __repr__(self):
+        return ("Geom(batch=%d, heads=%d, grid=%dx%dx%d, head_dim=%d, cube=%dx%dx%d)" %
+                (self.batch, self.heads, self.frames, self.height, self.width,
+                 self.head_dim, self.cube_t, self.cube_h, self.cube_w))
+
+
+def make_geom(batch: int, heads: int, frames: int, height: int, width: int,
+              head_dim: int, cube: Tuple[int, int, int] = (4, 4, 4)) -> Geom:
+    return Geom(batch, heads, frames, height, width, head_dim, *cube)
+
+
+_lib = None
+_lock = threading.Lock()
+_vp, _i32, _i64, _sz, _f64, _f32 = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                    ctypes.c_size_t, ctypes.c_double, ctypes.c_float)
+_GP = ctypes.POINTER(Geom)
+_SIGS = {
+    "sparse_attn_geometry": (_i32, [_GP, ctypes.POINTER(_i32), ctypes.POINTER(_i64), ctypes.POINTER(_i64)]),
+    "sparse_attn_ceil_k": (_i32, [_f64, _i32]),
+    "sparse_attn_reorder": (_i32, [_vp, _vp, _GP, _vp]),
+    "sparse_attn_unreorder": (_i32, [_vp, _vp, _vp, _vp, _GP, _vp]),
+    "sparse_attn_pool": (_i32, [_vp, _vp, _vp, _vp, _GP, _vp]),
+    "sparse_attn_block_scores": (_i32, [_vp, _vp, _vp, _f64, _GP, _vp]),
+    "sparse_attn_select": (_i32, [_vp, _GP, _f64, _f64, _vp, _vp, _vp, _i32, _vp]),
+    "sparse_attn_mask_workspace_bytes": (_sz, [_GP]),
+    "sparse_attn_build_mask": (_i32, [_vp, _vp, _GP, _i32, _f64, _f64, _vp, _vp, _vp, _i32, _vp, _sz, _vp]),
+    "sparse_attn_fwd_workspace_bytes": (_sz, [_GP]),
+    "sparse_attn_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _GP, _f32, _vp, _vp, _vp, _sz, _vp]),
+    "sparse_attn_last_error": (ctypes.c_char_p, []),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (built on first use if it has never been built)."""
+    global _lib
+    if _lib is None:
+        with _lock:
+            if _lib is None:
+                if not os.path.exists(LIB_PATH):
+                    from . import build as _build
+                    _build.build()
+                handle = ctypes.CDLL(LIB_PATH)
+                for name, (res, args) in _SIGS.items():
+                    fn = getattr(handle, name)
+                    fn.restype = res
+                    fn.argtypes = args
+                _lib = handle
+    return _lib
+
+
+def _check(code: int) -> int:
+    if code < 0:
+        msg = lib().sparse_attn_last_error().decode(errors="replace")
+        raise SparseAttnError(code, msg)
+    return code
+
+
+def _ptr(t: Optional[torch.Tensor], dtype=None, name: str = "tensor"):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, *tensors):
+    if stream is not None:
+        return ctypes.c_void_p(int(stream))
+    for t in tensors:
+        if isinstance(t, torch.Tensor) and t.is_cuda:
+            return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+    return None
+
+
+# ----------------------------------------------------------------------------
+# one-to-one C ABI mirrors
+# ----------------------------------------------------------------------------
+def sparse_attn_geometry(g: Geom) -> Tuple[int, int, int]:
+    nblk, n_real, n_pad = _i32(), _i64(), _i64()
+    _check(lib().sparse_attn_geometry(ctypes.byref(g), ctypes.byref(nblk), ctypes.byref(n_real),
+                                      ctypes.byref(n_pad)))
+    return nblk.value, n_real.value, n_pad.value
+
+
+def sparse_attn_ceil_k(k_frac: float, nblk: int) -> int:
+    return _check(lib().sparse_attn_ceil_k(float(k_frac), int(nblk)))
+
+
+def sparse_attn_reorder(x, xc, g: Geom, stream=None) -> None:
+    _check(lib().sparse_attn_reorder(_ptr(x, torch.bfloat16, "x"), _ptr(xc, torch.bfloat16, "xc"),
+                                     ctypes.byref(g), _stream(stream, x)))
+
+
+def sparse_attn_unreorder(oc, o, lse_c, lse, g: Geom, stream=None) -> None:
+    _check(lib().sparse_attn_unreorder(_ptr(oc, torch.bfloat16, "oc"), _ptr(o, torch.bfloat16, "o"),
+                                       _ptr(lse_c, torch.float32, "lse_c"), _ptr(lse, torch.float32, "lse"),
+                                       ctypes.byref(g), _stream(stream, oc)))
+
+
+def sparse_attn_pool(qc, kc, qbar, kbar, g: Geom, stream=None) -> None:
+    _check(lib().sparse_attn_pool(_ptr(qc, torch.bfloat16, "qc"), _ptr(kc, torch.bfloat16, "kc"),
+                                  _ptr(qbar, torch.float64, "qbar"), _ptr(kbar, torch.float64, "kbar"),
+                                  ctypes.byref(g), _stream(stream, qc)))
+
+
+def sparse_attn_block_scores(qbar, kbar, scores, scale: float, g: Geom, stream=None) -> None:
+    _check(lib().sparse_attn_block_scores(_ptr(qbar, torch.float64, "qbar"), _ptr(kbar, torch.float64, "kbar"),
+                                          _ptr(scores, torch.float64, "scores"), float(scale),
+                                          ctypes.byref(g), _stream(stream, qbar)))
+
+
+def sparse_attn_select(scores, g: Geom, k_frac: float, p: float, row_budget, lut, counts,
+                       cap: int, stream=None) -> None:
+    _check(lib().sparse_attn_select(_ptr(scores, torch.float64, "scores"), ctypes.byref(g),
+                                    float(k_frac), float(p), _ptr(row_budget, torch.int32, "row_budget"),
+                                    _ptr(lut, torch.int32, "lut"), _ptr(counts, torch.int32, "counts"),
+                                    int(cap), _stream(stream, scores)))
+
+
+def sparse_attn_mask_workspace_bytes(g: Geom) -> int:
+    return int(lib().sparse_attn_mask_workspace_bytes(ctypes.byref(g)))
+
+
+def sparse_attn_build_mask(qc, kc, g: Geom, block: int, k_frac: float, p: float, row_budget,
+                           lut, counts, cap: int, workspace, stream=None) -> None:
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().sparse_attn_build_mask(_ptr(qc, torch.bfloat16, "qc"), _ptr(kc, torch.bfloat16, "kc"),
+                                        ctypes.byref(g), int(block), float(k_frac), float(p),
+                                        _ptr(row_budget, torch.int32, "row_budget"),
+                                        _ptr(lut, torch.int32, "lut"), _ptr(counts, torch.int32, "counts"),
+                                        int(cap), _ptr(workspace, None, "workspace"), ws_bytes,
+                                        _stream(stream, qc)))
+
+
+def sparse_attn_fwd_workspace_bytes(g: Geom) -> int:
+    return int(lib().sparse_attn_fwd_workspace_bytes(ctypes.byref(g)))
+
+
+def sparse_attn_fwd(qc, kc, vc, lut, counts, cap: int, g: Geom, scale: float, oc, lse_c,
+                    workspace=None, stream=None) -> None:
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().sparse_attn_fwd(_ptr(qc, torch.bfloat16, "qc"), _ptr(kc, torch.bfloat16, "kc"),
+                                 _ptr(vc, torch.bfloat16, "vc"), _ptr(lut, torch.int32, "lut"),
+                                 _ptr(counts, torch.int32, "counts"), int(cap), ctypes.byref(g),
+                                 float(scale), _ptr(oc, torch.bfloat16, "oc"),
+                                 _ptr(lse_c, torch.float32, "lse_c"), _ptr(workspace, None, "workspace"),
+                                 ws_bytes, _stream(stream, qc)))
+
+
+def sparse_attn_last_error() -> str:
+    return lib().sparse_attn_last_error().decode(errors="replace")
+
+
+# ----------------------------------------------------------------------------
+# allocating helpers (torch.empty for outputs, then the entry points above)
+# ----------------------------------------------------------------------------
+def _empty(shape, dtype, like):
+    return torch.empty(shape, dtype=dtype, device=like.device)
+
+
+def reorder(x: torch.Tensor, g: Geom, stream=None) -> torch.Tensor:
+    nblk, n_real, n_pad = sparse_attn_geometry(g)
+    xc = _empty((g.batch, g.heads, n_pad, g.head_dim), torch.bfloat16, x)
+    sparse_attn_reorder(x, xc, g, stream)
+    return xc
+
+
+def unreorder(oc: torch.Tensor, lse_c: Optional[torch.Tensor], g: Geom, stream=None):
+    nblk, n_real, n_pad = sparse_attn_geometry(g)
+    o = _empty((g.batch, g.heads, n_real, g.head_dim), torch.bfloat16, oc)
+    lse = None if lse_c is None else _empty((g.batch, g.heads, n_real), torch.float32, oc)
+    sparse_attn_unreorder(oc, o, lse_c, lse, g, stream)
+    return o, lse
+
+
+def mask_workspace(g: Geom, device) -> torch.Tensor:
+    return torch.empty(sparse_attn_mask_workspace_bytes(g), dtype=torch.uint8, device=device)
+
+
+def build_mask(qc, kc, g: Geom, k_frac: float, p: float, row_budget=None, cap=None,
+               workspace=None, stream=None):
+    """Kept-block lists (lut [B,H,nblk,cap] int32) and counts [B,H,nblk] int32."""
+    nblk, _, _ = sparse_attn_geometry(g)
+    cap = nblk if cap is None else cap
+    lut = _empty((g.batch, g.heads, nblk, cap), torch.int32, qc)
+    counts = _empty((g.batch, g.heads, nblk), torch.int32, qc)
+    if workspace is None:
+        workspace = mask_workspace(g, qc.device)
+    sparse_attn_build_mask(qc, kc, g, 64, k_frac, p, row_budget, lut, counts, cap, workspace, stream)
+    return lut, counts
+
+
+def fwd(qc, kc, vc, lut, counts, g: Geom, scale: float = 0.0, stream=None):
+    """Block-sparse forward: cube-major O (bf16) and natural-log LSE (fp32)."""
+    _, _, n_pad = sparse_attn_geometry(g)
+    oc = _empty((g.batch, g.heads, n_pad, g.head_dim), torch.bfloat16, qc)
+    lse_c = _empty((g.batch, g.heads, n_pad), torch.float32, qc)
+    nws = sparse_attn_fwd_workspace_bytes(g)
+    ws = None if nws == 0 else torch.empty(nws, dtype=torch.uint8, device=qc.device)
+    sparse_attn_fwd(qc, kc, vc, lut, counts, lut.shape[-1], g, scale, oc, lse_c, ws, stream)
+    return oc, lse_c
+
+
+def attention(q, k, v, g: Geom, k_frac: float, p: float, row_budget=None, stream=None):
+    """Whole path on row-major tokens: reorder, build the hybrid mask, sparse
+    forward, unreorder.  Returns (O [B,H,N,d] bf16, LSE [B,H,N] fp32, lut, counts)."""
+    qc, kc, vc = (reorder(t, g, stream) for t in (q, k, v))
+    lut, counts = build_mask(qc, kc, g, k_frac, p, row_budget, stream=stream)
+    oc, lse_c = fwd(qc, kc, vc, lut, counts, g, stream=stream)
+    o, lse = unreorder(oc, lse_c, g, stream)
+    return o, lse, lut, counts
+
+
+def default_scale(head_dim: int) -> float:
+    return 1.0 / math.sqrt(head_dim)

@@ -1,0 +1,96 @@
+// Pooled block scores S = Qbar Kbar^T * scale on the float64 matrix cores
+// (gfx950 v_mfma_f64_16x16x4f64).
+//
+// SpargeAttention2 summary page, "Block-Pooled Attention for Efficient Mask
+// Construction", step 3; VSA2 section 2.2 (coarse branch scores).  The
+// contraction is small (2 nblk^2 d flops per head) but decides the kept-block
+// lists, so it runs in float64: an fp64 result leaves the selection's order
+// decisions to values that differ from an exact evaluation by ~1e-16
+// relative, far inside the 1e-6 near-tie margin the lists are checked with.
+//
+// Tiling: one workgroup of 4 waves computes a 64 x 64 tile of one head's
+// scores; each wave owns a 32 x 32 quarter as 2 x 2 MFMA tiles of 16 x 16.
+// Operand lanes: A row = lane % 16, B column = lane % 16, k = lane / 16; the
+// accumulator's register r of lane l holds row l / 16 + 4 r, column l % 16.
+// The k dimension (d) is staged through LDS 16 columns at a time.
+#include "sa_launch.h"
+
+namespace sa {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kTile = 64;
+constexpr int kKc = 16;            // k columns staged per step
+constexpr int kLd = kKc + 1;       // padded LDS row (doubles)
+
+__global__ __launch_bounds__(kThreads) void block_scores_kernel(const double* __restrict__ qbar,
+                                                                const double* __restrict__ kbar,
+                                                                double* __restrict__ scores,
+                                                                double scale, Geom g) {
+  __shared__ double As[kTile * kLd];
+  __shared__ double Bs[kTile * kLd];
+  const int n = g.nblk, d = g.d;
+  const int i0 = blockIdx.y * kTile, j0 = blockIdx.x * kTile;
+  const long long bh = blockIdx.z;
+  const double* qh = qbar + bh * (long long)n * d;
+  const double* kh = kbar + bh * (long long)n * d;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  f64x4 acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
+
+  const int lr = threadIdx.x >> 2;          // tile row this thread stages
+  const int lc = (threadIdx.x & 3) * 4;     // first of its 4 columns
+  for (int k0 = 0; k0 < d; k0 += kKc) {
+    {
+      const int gi = i0 + lr, gj = j0 + lr;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        As[lr * kLd + lc + e] = gi < n ? qh[(long long)gi * d + k0 + lc + e] : 0.0;
+        Bs[lr * kLd + lc + e] = gj < n ? kh[(long long)gj * d + k0 + lc + e] : 0.0;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < kKc; ks += 4) {
+      const int kk = ks + (lane >> 4);
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const double a = As[(wm * 32 + mt * 16 + (lane & 15)) * kLd + kk];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          const double b = Bs[(wn * 32 + nt * 16 + (lane & 15)) * kLd + kk];
+          acc[mt][nt] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, acc[mt][nt], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  double* out = scores + bh * (long long)n * n;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = i0 + wm * 32 + mt * 16 + (lane >> 4) + 4 * r;
+        const int col = j0 + wn * 32 + nt * 16 + (lane & 15);
+        if (row < n && col < n) out[(long long)row * n + col] = acc[mt][nt][r] * scale;
+      }
+}
+
+}  // namespace
+
+hipError_t launch_block_scores(const double* qbar, const double* kbar, double* scores,
+                               double scale, const Geom& g, hipStream_t s) {
+  const int tiles = (g.nblk + kTile - 1) / kTile;
+  dim3 grid(tiles, tiles, g.batch * g.heads);
+  block_scores_kernel<<<grid, kThreads, 0, s>>>(qbar, kbar, scores, scale, g);
+  return hipGetLastError();
+}
+
+}  // namespace sa

@@ -1,0 +1,272 @@
+// C ABI of the sparse-attention library: argument validation on the host, then
+// asynchronous kernel launches on the caller's stream.  Every check runs
+// before any HIP call, so an invalid call touches no device state.
+#include "../../include/sparse_attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "sa_launch.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int32_t fail(int32_t code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int32_t ok() {
+  g_last_error[0] = '\0';
+  return SA_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr int kMaxSelectBlocks = 4096;
+constexpr size_t kWsAlign = 256;
+
+size_t round_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+// Validates the geometry and fills the device-side description.
+int32_t make_geom(const sa_geom* g, sa::Geom& d) {
+  if (g == nullptr) return fail(SA_ERR_INVALID_ARG, "geometry pointer is NULL");
+  if (g->batch < 1 || g->heads < 1) return fail(SA_ERR_INVALID_ARG, "batch and heads must be >= 1");
+  if (g->frames < 1 || g->height < 1 || g->width < 1)
+    return fail(SA_ERR_INVALID_ARG, "frames, height and width must be >= 1");
+  if (g->cube_t < 1 || g->cube_h < 1 || g->cube_w < 1 ||
+      (long long)g->cube_t * g->cube_h * g->cube_w != 64)
+    return fail(SA_ERR_INVALID_ARG, "cube_t*cube_h*cube_w must be 64 (got %d x %d x %d)", g->cube_t,
+                g->cube_h, g->cube_w);
+  if (g->head_dim != 64 && g->head_dim != 128)
+    return fail(SA_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", g->head_dim);
+  d.batch = g->batch;
+  d.heads = g->heads;
+  d.frames = g->frames;
+  d.height = g->height;
+  d.width = g->width;
+  d.d = g->head_dim;
+  d.ct = g->cube_t;
+  d.ch = g->cube_h;
+  d.cw = g->cube_w;
+  const long long nt = (g->frames + g->cube_t - 1) / g->cube_t;
+  const long long nh = (g->height + g->cube_h - 1) / g->cube_h;
+  const long long nw = (g->width + g->cube_w - 1) / g->cube_w;
+  const long long nblk = nt * nh * nw;
+  if (nblk > (1 << 24)) return fail(SA_ERR_UNSUPPORTED, "too many blocks per head (%lld)", nblk);
+  const long long rows = nblk * g->batch * g->heads;
+  if (rows > 0x7fffffffLL) return fail(SA_ERR_UNSUPPORTED, "batch*heads*blocks exceeds 2^31");
+  d.nt = (int)nt;
+  d.nh = (int)nh;
+  d.nw = (int)nw;
+  d.nblk = (int)nblk;
+  d.n_real = (long long)g->frames * g->height * g->width;
+  d.n_pad = nblk * 64;
+  return SA_OK;
+}
+
+int32_t check_ptr(const void* p, size_t align, const char* name) {
+  if (p == nullptr) return fail(SA_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned(p, align)) return fail(SA_ERR_INVALID_ARG, "%s is not %zu-byte aligned", name, align);
+  return SA_OK;
+}
+
+int32_t hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(SA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+#define SA_TRY(expr)          \
+  do {                        \
+    const int32_t rc_ = (expr); \
+    if (rc_ != SA_OK) return rc_; \
+  } while (0)
+
+int32_t ceil_k_impl(double k_frac, int32_t nblk) {
+  if (nblk < 0 || !std::isfinite(k_frac)) return SA_ERR_INVALID_ARG;
+  if (nblk == 0) return 0;
+  const double c = std::ceil(k_frac * (double)nblk - 1e-9);
+  if (c <= 0.0) return 0;
+  if (c >= (double)nblk) return nblk;
+  return (int32_t)c;
+}
+
+int32_t check_select_args(const sa::Geom& d, double k_frac, double p, const int32_t* row_budget,
+                          const int32_t* lut, const int32_t* counts, int32_t cap, int& kc) {
+  if (d.nblk > kMaxSelectBlocks)
+    return fail(SA_ERR_UNSUPPORTED, "selection supports at most %d blocks per head (got %d)",
+                kMaxSelectBlocks, d.nblk);
+  if (!std::isfinite(k_frac) || !std::isfinite(p)) return fail(SA_ERR_INVALID_ARG, "k_frac and p must be finite");
+  if (row_budget != nullptr && p != 0.0)
+    return fail(SA_ERR_INVALID_ARG, "a row budget replaces Top-k and requires p == 0");
+  if (row_budget != nullptr) SA_TRY(check_ptr(row_budget, 4, "row_budget"));
+  SA_TRY(check_ptr(lut, 4, "lut"));
+  SA_TRY(check_ptr(counts, 4, "counts"));
+  kc = ceil_k_impl(k_frac, d.nblk);
+  const int need = (p > 0.0 || row_budget != nullptr) ? d.nblk : kc;
+  if (cap < 1 || cap < need)
+    return fail(SA_ERR_CAPACITY, "cap %d is below the largest possible row count %d", cap, need);
+  return SA_OK;
+}
+
+size_t mask_ws_bytes(const sa::Geom& d) {
+  const size_t rows = (size_t)d.batch * d.heads * d.nblk;
+  return 2 * round_up(rows * d.d * sizeof(double)) + round_up(rows * d.nblk * sizeof(double));
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t sparse_attn_geometry(const sa_geom* g, int32_t* nblk, int64_t* n_real, int64_t* n_pad) {
+  sa::Geom d;
+  SA_TRY(make_geom(g, d));
+  if (nblk) *nblk = d.nblk;
+  if (n_real) *n_real = d.n_real;
+  if (n_pad) *n_pad = d.n_pad;
+  return ok();
+}
+
+int32_t sparse_attn_ceil_k(double k_frac, int32_t nblk) {
+  const int32_t r = ceil_k_impl(k_frac, nblk);
+  if (r < 0) return fail(r, "ceil_k needs nblk >= 0 and a finite k_frac");
+  return r;
+}
+
+int32_t sparse_attn_reorder(const void* x, void* xc, const sa_geom* g, void* stream) {
+  sa::Geom d;
+  SA_TRY(make_geom(g, d));
+  SA_TRY(check_ptr(x, 16, "x"));
+  SA_TRY(check_ptr(xc, 16, "xc"));
+  if (x == xc) return fail(SA_ERR_INVALID_ARG, "x and xc must not overlap");
+  return hip_status(sa::launch_reorder(x, xc, d, (hipStream_t)stream), "reorder launch");
+}
+
+int32_t sparse_attn_unreorder(const void* oc, void* o, const float* lse_c, float* lse,
+                              const sa_geom* g, void* stream) {
+  sa::Geom d;
+  SA_TRY(make_geom(g, d));
+  SA_TRY(check_ptr(oc, 16, "oc"));
+  SA_TRY(check_ptr(o, 16, "o"));
+  if ((lse_c == nullptr) != (lse == nullptr))
+    return fail(SA_ERR_INVALID_ARG, "lse_c and lse must both be given or both be NULL");
+  if (lse_c != nullptr) {
+    SA_TRY(check_ptr(lse_c, 4, "lse_c"));
+    SA_TRY(check_ptr(lse, 4, "lse"));
+  }
+  return hip_status(sa::launch_unreorder(oc, o, lse_c, lse, d, (hipStream_t)stream), "unreorder launch");
+}
+
+int32_t sparse_attn_pool(const void* qc, const void* kc, double* qbar, double* kbar, const sa_geom* g,
+                         void* stream) {
+  sa::Geom d;
+  SA_TRY(make_geom(g, d));
+  SA_TRY(check_ptr(qc, 16, "qc"));
+  SA_TRY(check_ptr(kc, 16, "kc"));
+  SA_TRY(check_ptr(qbar, 8, "qbar"));
+  SA_TRY(check_ptr(kbar, 8, "kbar"));
+  return hip_status(sa::launch_pool(qc, kc, qbar, kbar, d, (hipStream_t)stream), "pool launch");
+}
+
+int32_t sparse_attn_block_scores(const double* qbar, const double* kbar, double* scores, double scale,
+                                 const sa_geom* g, void* stream) {
+  sa::Geom d;
+  SA_TRY(make_geom(g, d));
+  if (d.nblk > 64 * 65535) return fail(SA_ERR_UNSUPPORTED, "too many blocks for the score grid");
+  SA_TRY(check_ptr(qbar, 8, "qbar"));
+  SA_TRY(check_ptr(kbar, 8, "kbar"));
+  SA_TRY(check_ptr(scores, 8, "scores"));
+  if (!std::isfinite(scale)) return fail(SA_ERR_INVALID_ARG, "scale must be finite");
+  if (scale <= 0.0) scale = 1.0 / std::sqrt((double)d.d);
+  return hip_status(sa::launch_block_scores(qbar, kbar, scores, scale, d, (hipStream_t)stream),
+                    "block score launch");
+}
+
+int32_t sparse_attn_select(const double* scores, const sa_geom* g, double k_frac, double p,
+                           const int32_t* row_budget, int32_t* lut, int32_t* counts, int32_t cap,
+                           void* stream) {
+  sa::Geom d;
+  SA_TRY(make_geom(g, d));
+  SA_TRY(check_ptr(scores, 8, "scores"));
+  int kc = 0;
+  SA_TRY(check_select_args(d, k_frac, p, row_budget, lut, counts, cap, kc));
+  return hip_status(sa::launch_select(scores, d, kc, p, row_budget, lut, counts, cap, (hipStream_t)stream),
+                    "select launch");
+}
+
+size_t sparse_attn_mask_workspace_bytes(const sa_geom* g) {
+  sa::Geom d;
+  if (make_geom(g, d) != SA_OK) return 0;
+  return mask_ws_bytes(d);
+}
+
+int32_t sparse_attn_build_mask(const void* qc, const void* kc, const sa_geom* g, int32_t block,
+                               double k_frac, double p, const int32_t* row_budget, int32_t* lut,
+                               int32_t* counts, int32_t cap, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  sa::Geom d;
+  SA_TRY(make_geom(g, d));
+  if (block != 64) return fail(SA_ERR_UNSUPPORTED, "block must be 64 (got %d)", block);
+  SA_TRY(check_ptr(qc, 16, "qc"));
+  SA_TRY(check_ptr(kc, 16, "kc"));
+  int kcount = 0;
+  SA_TRY(check_select_args(d, k_frac, p, row_budget, lut, counts, cap, kcount));
+  SA_TRY(check_ptr(workspace, kWsAlign, "workspace"));
+  const size_t need = mask_ws_bytes(d);
+  if (workspace_bytes < need)
+    return fail(SA_ERR_CAPACITY, "workspace of %zu bytes is below the %zu needed", workspace_bytes, need);
+  const size_t rows = (size_t)d.batch * d.heads * d.nblk;
+  char* ws = static_cast<char*>(workspace);
+  double* qbar = reinterpret_cast<double*>(ws);
+  double* kbar = reinterpret_cast<double*>(ws + round_up(rows * d.d * sizeof(double)));
+  double* scores = reinterpret_cast<double*>(ws + 2 * round_up(rows * d.d * sizeof(double)));
+  hipStream_t s = (hipStream_t)stream;
+  SA_TRY(hip_status(sa::launch_pool(qc, kc, qbar, kbar, d, s), "pool launch"));
+  SA_TRY(hip_status(sa::launch_block_scores(qbar, kbar, scores, 1.0 / std::sqrt((double)d.d), d, s),
+                    "block score launch"));
+  return hip_status(sa::launch_select(scores, d, kcount, p, row_budget, lut, counts, cap, s), "select launch");
+}
+
+size_t sparse_attn_fwd_workspace_bytes(const sa_geom* g) {
+  sa::Geom d;
+  if (make_geom(g, d) != SA_OK) return 0;
+  return sa::fwd_workspace_bytes(d);
+}
+
+int32_t sparse_attn_fwd(const void* qc, const void* kc, const void* vc, const int32_t* lut,
+                        const int32_t* counts, int32_t cap, const sa_geom* g, float scale, void* oc,
+                        float* lse_c, void* workspace, size_t workspace_bytes, void* stream) {
+  sa::Geom d;
+  SA_TRY(make_geom(g, d));
+  SA_TRY(check_ptr(qc, 16, "qc"));
+  SA_TRY(check_ptr(kc, 16, "kc"));
+  SA_TRY(check_ptr(vc, 16, "vc"));
+  SA_TRY(check_ptr(lut, 4, "lut"));
+  SA_TRY(check_ptr(counts, 4, "counts"));
+  SA_TRY(check_ptr(oc, 16, "oc"));
+  SA_TRY(check_ptr(lse_c, 4, "lse_c"));
+  if (cap < 1) return fail(SA_ERR_INVALID_ARG, "cap must be >= 1");
+  if (!std::isfinite(scale)) return fail(SA_ERR_INVALID_ARG, "scale must be finite");
+  if (scale <= 0.f) scale = (float)(1.0 / std::sqrt((double)d.d));
+  const size_t need = sa::fwd_workspace_bytes(d);
+  if (need > 0) {
+    SA_TRY(check_ptr(workspace, kWsAlign, "workspace"));
+    if (workspace_bytes < need)
+      return fail(SA_ERR_CAPACITY, "workspace of %zu bytes is below the %zu needed", workspace_bytes, need);
+  }
+  return hip_status(sa::launch_fwd(qc, kc, vc, lut, counts, cap, d, scale, oc, lse_c, workspace,
+                                   (hipStream_t)stream),
+                    "fwd launch");
+}
+
+const char* sparse_attn_last_error(void) { return g_last_error; }
+
+}  // extern "C"

@@ -1,0 +1,27 @@
+// Host-side launchers of the gfx950 kernels.  Arguments are validated by the
+// C ABI layer before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sa_device.h"
+
+namespace sa {
+
+hipError_t launch_reorder(const void* x, void* xc, const Geom& g, hipStream_t s);
+hipError_t launch_unreorder(const void* oc, void* o, const float* lse_c, float* lse,
+                            const Geom& g, hipStream_t s);
+hipError_t launch_pool(const void* qc, const void* kc, double* qbar, double* kbar,
+                       const Geom& g, hipStream_t s);
+hipError_t launch_block_scores(const double* qbar, const double* kbar, double* scores,
+                               double scale, const Geom& g, hipStream_t s);
+hipError_t launch_select(const double* scores, const Geom& g, int kc_default, double p,
+                         const int32_t* row_budget, int32_t* lut, int32_t* counts,
+                         int cap, hipStream_t s);
+hipError_t launch_fwd(const void* qc, const void* kc, const void* vc, const int32_t* lut,
+                      const int32_t* counts, int cap, const Geom& g, float scale, void* oc,
+                      float* lse_c, void* workspace, hipStream_t s);
+size_t fwd_workspace_bytes(const Geom& g);
+
+}  // namespace sa

@@ -1,0 +1,201 @@
+/*
+ * sparse_attn.h -- C ABI of the MI355X (gfx950) hybrid block-sparse attention
+ * library for video diffusion transformers.
+ *
+ * The path (all steps are GPU kernels of this library):
+ *   reorder      row-major video tokens -> cube-major blocks of 64 tokens
+ *   pool         per-block mean of Q and K over the block's real tokens
+ *   block_scores S = Qbar Kbar^T * scale (float64 matrix cores)
+ *   select       per query block: hybrid Top-k U Top-p kept-block list
+ *   fwd          block-sparse attention over the kept blocks -> O, LSE
+ *   unreorder    cube-major O (and LSE) -> row-major tokens
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every tensor pointer is a DEVICE pointer that the caller allocated; the
+ *   library never allocates, frees or keeps caller-visible memory.  Scratch
+ *   memory comes in through a caller-provided `workspace` (device pointer,
+ *   256-byte aligned) whose size the *_workspace_bytes() functions report.
+ * - `stream` is a hipStream_t (NULL = the default stream).  All work is
+ *   enqueued asynchronously on it; nothing synchronises the host.
+ * - Tensors are dense and row-major with the shapes given at each function;
+ *   bf16 tensors must be 16-byte aligned, float64 8-byte, int32/float 4-byte.
+ * - A token grid of frames x height x width is flattened row-major,
+ *   n = t*height*width + h*width + w ("N" = real tokens).  Cube-major tensors
+ *   hold nblk blocks of 64 slots ("n_pad" = 64*nblk); block
+ *   (bt, bh, bw) is number (bt*Nh + bh)*Nw + bw and its slot for the token at
+ *   offset (tt, hh, ww) inside the cube is (tt*cube_h + hh)*cube_w + ww.
+ *   A grid side that is not a multiple of the cube side is padded up; pad
+ *   slots are never treated as tokens (pooling skips them, attention masks
+ *   them as keys and writes O = 0, LSE = -inf for them as queries).  Pad slots
+ *   must hold finite values (reorder writes zeros there).
+ * - Return value: SA_OK (0) or a negative SA_ERR_* code.  On an argument error
+ *   nothing is launched and no output is touched; sparse_attn_last_error()
+ *   gives a message (per calling thread).  A failed launch returns
+ *   SA_ERR_HIP.  Faults inside kernels surface at the caller's next
+ *   synchronisation, as for any HIP work.
+ * - Functions keep no state between calls and are safe to call from several
+ *   host threads.
+ *
+ * Citations name the pages this library follows by title and section:
+ *   [SA2]  "SpargeAttention2: Trainable Sparse Attention via Hybrid Top-k+Top-p
+ *          Masking and Distillation" (summary page)
+ *   [VSA]  "VSA: Faster Video Diffusion with Trainable Sparse Attention"
+ *          (summary page)
+ *   [VSA2] "Improving Video Sparse Attention with Fine-grained Router and
+ *          Sparse Rebasing"
+ */
+#ifndef SPARSE_ATTN_H
+#define SPARSE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  SA_OK = 0,
+  SA_ERR_INVALID_ARG = -1, /* null/misaligned pointer, bad size or parameter */
+  SA_ERR_UNSUPPORTED = -2, /* valid but outside what the kernels implement */
+  SA_ERR_CAPACITY = -3,    /* workspace or LUT capacity too small */
+  SA_ERR_HIP = -4          /* a HIP launch or runtime call failed */
+};
+
+/* Shape of one attention call.  [VSA] "Cube Partitioning and Token
+ * Re-Indexing": cubes of cube_t x cube_h x cube_w tokens (default 4x4x4).
+ * cube_t*cube_h*cube_w must be 64 (the block size of every kernel).
+ * head_dim must be 64 or 128. */
+typedef struct sa_geom {
+  int32_t batch;
+  int32_t heads;
+  int32_t frames;   /* latent frames T */
+  int32_t height;   /* latent rows */
+  int32_t width;    /* latent columns */
+  int32_t head_dim; /* d */
+  int32_t cube_t;
+  int32_t cube_h;
+  int32_t cube_w;
+} sa_geom;
+
+/* Host only.  Block count nblk = ceil(T/ct)*ceil(H/ch)*ceil(W/cw), real
+ * tokens N and padded tokens n_pad = 64*nblk of one (batch, head).
+ * Padding per side follows [VSA2] section 2.2, "Kernel Implementation".
+ * Any output pointer may be NULL. */
+int32_t sparse_attn_geometry(const sa_geom* g, int32_t* nblk, int64_t* n_real,
+                             int64_t* n_pad);
+
+/* Host only.  Top-k count ceil(k_frac * nblk) of [SA2] "The Hybrid Top-k+Top-p
+ * Masking Rule", clamped to [0, nblk]; an excess below 1e-9 from binary
+ * rounding of k_frac*nblk does not round up.  Returns the count, or
+ * SA_ERR_INVALID_ARG for nblk < 0 or a non-finite k_frac. */
+int32_t sparse_attn_ceil_k(double k_frac, int32_t nblk);
+
+/* Cube re-indexing, [VSA] "Cube Partitioning and Token Re-Indexing"; [VSA2]
+ * section 2.2 "Permutation".
+ *   x  [batch, heads, N, head_dim] bf16, row-major tokens      (input)
+ *   xc [batch, heads, n_pad, head_dim] bf16, cube-major        (output)
+ * Pad slots of xc are written with zeros.  x and xc must not overlap. */
+int32_t sparse_attn_reorder(const void* x, void* xc, const sa_geom* g,
+                            void* stream);
+
+/* Inverse re-indexing of the attention output (pad slots dropped).
+ *   oc    [batch, heads, n_pad, head_dim] bf16   (input)
+ *   o     [batch, heads, N, head_dim] bf16       (output)
+ *   lse_c [batch, heads, n_pad] float32          (input, may be NULL)
+ *   lse   [batch, heads, N] float32              (output, NULL iff lse_c is)
+ */
+int32_t sparse_attn_unreorder(const void* oc, void* o, const float* lse_c,
+                              float* lse, const sa_geom* g, void* stream);
+
+/* Mean pooling of each block's real tokens, [SA2] "Block-Pooled Attention for
+ * Efficient Mask Construction" step 2; [VSA] "The Coarse Stage".
+ *   qc, kc     [batch, heads, n_pad, head_dim] bf16, cube-major  (inputs)
+ *   qbar, kbar [batch, heads, nblk, head_dim] float64            (outputs)
+ * Sums are taken in float64 (exact for bf16 inputs) and divided by the block's
+ * real-token count. */
+int32_t sparse_attn_pool(const void* qc, const void* kc, double* qbar,
+                         double* kbar, const sa_geom* g, void* stream);
+
+/* Pooled block scores S = Qbar Kbar^T * scale, [SA2] "Block-Pooled Attention
+ * for Efficient Mask Construction" step 3, in float64 on the matrix cores.
+ *   qbar, kbar [batch, heads, nblk, head_dim] float64   (inputs)
+ *   scores     [batch, heads, nblk, nblk] float64       (output)
+ * scale <= 0 selects 1/sqrt(head_dim). */
+int32_t sparse_attn_block_scores(const double* qbar, const double* kbar,
+                                 double* scores, double scale,
+                                 const sa_geom* g, void* stream);
+
+/* Hybrid Top-k U Top-p selection, [SA2] "The Hybrid Top-k+Top-p Masking Rule"
+ * (Eq. 9), producing index lists as [VSA] "Kernel Implementation" describes
+ * (contiguous block ids, not a binary mask).
+ * Per row i (one query block of one batch/head), with the row's softmax P:
+ *   order = block ids by score descending, lower id first on equal scores;
+ *   kc    = row_budget ? row_budget[row] (clamped to [0, nblk])
+ *                      : sparse_attn_ceil_k(k_frac, nblk);
+ *   pc    = shortest prefix of `order` whose probability sum reaches p
+ *           (p <= 0: 0; p >= 1: nblk);
+ *   kept  = the first max(kc, pc) ids of `order`, written in ascending id.
+ *   scores [batch, heads, nblk, nblk] float64                 (input)
+ *   row_budget [batch, heads, nblk] int32 or NULL; when given, p must be 0
+ *   lut    [batch, heads, nblk, cap] int32: row r's ids in lut[r*cap ...]
+ *   counts [batch, heads, nblk] int32: number of ids in each row
+ * cap must be >= nblk when p > 0 or row_budget is given, else >= kc.
+ * Entries of lut beyond a row's count are left as they were.
+ * Probability mass is accumulated in 2^-40 fixed point from float32
+ * exponentials, so the result is deterministic; a row whose decision hinges on
+ * a cumulative sum within ~1e-7 of p may differ from an exact evaluation.
+ * nblk must be <= 4096. */
+int32_t sparse_attn_select(const double* scores, const sa_geom* g,
+                           double k_frac, double p, const int32_t* row_budget,
+                           int32_t* lut, int32_t* counts, int32_t cap,
+                           void* stream);
+
+/* Bytes of workspace sparse_attn_build_mask needs (Qbar, Kbar and scores in
+ * float64, each region 256-byte aligned). 0 on an invalid geometry. */
+size_t sparse_attn_mask_workspace_bytes(const sa_geom* g);
+
+/* pool + block_scores + select in one call (scale 1/sqrt(head_dim)).  block
+ * must be 64.  Arguments as for those functions; the float64 intermediates
+ * live in `workspace` (>= sparse_attn_mask_workspace_bytes, else
+ * SA_ERR_CAPACITY). */
+int32_t sparse_attn_build_mask(const void* qc, const void* kc,
+                               const sa_geom* g, int32_t block, double k_frac,
+                               double p, const int32_t* row_budget,
+                               int32_t* lut, int32_t* counts, int32_t cap,
+                               void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/* Bytes of workspace sparse_attn_fwd needs (its row schedule). */
+size_t sparse_attn_fwd_workspace_bytes(const sa_geom* g);
+
+/* Block-sparse attention forward, [SA2] "Kernel Implementation of the
+ * Hybrid-Masked Block-Sparse Attention" (Algorithm 1) and the renormalised
+ * output of "The Sparse Attention Error Decomposition"; [VSA] "The Fine
+ * Stage".  For every real query token of query block i, over the real keys
+ * of the blocks lut[row][0 .. counts[row]-1]:
+ *   O   = sum_j softmax_j(scale * q.k_j) v_j
+ *   LSE = ln sum_j exp(scale * q.k_j)
+ *   qc, kc, vc [batch, heads, n_pad, head_dim] bf16, cube-major   (inputs)
+ *   lut, counts as written by sparse_attn_select; at most cap ids per row are
+ *               read, ids outside [0, nblk) are skipped
+ *   oc    [batch, heads, n_pad, head_dim] bf16                    (output)
+ *   lse_c [batch, heads, n_pad] float32, natural log              (output)
+ * Rows with count 0 and pad query slots get O = 0, LSE = -inf.  Products run
+ * in bf16 on the matrix cores with float32 accumulation and an online
+ * softmax in float32.  scale <= 0 selects 1/sqrt(head_dim).  workspace may be
+ * NULL when sparse_attn_fwd_workspace_bytes() is 0. */
+int32_t sparse_attn_fwd(const void* qc, const void* kc, const void* vc,
+                        const int32_t* lut, const int32_t* counts, int32_t cap,
+                        const sa_geom* g, float scale, void* oc, float* lse_c,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Message describing the calling thread's last error ("" if none). */
+const char* sparse_attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_ATTN_H */

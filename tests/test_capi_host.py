@@ -1,0 +1,141 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load, export every function include/sparse_attn.h declares,
+and reject bad arguments before any HIP call.  Device pointers here are fake
+(aligned, non-null integers) and every call below is built to fail validation,
+so nothing is ever launched.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_attention_hybrid_amd as sa
+import oracle as O
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "sparse_attn.h")
+FAKE = ctypes.c_void_p(0x100000)       # aligned, never dereferenced
+FAKE_MISALIGNED = ctypes.c_void_p(0x100002)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sparse_attn_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert len(names) >= 12
+    lib = sa.lib()
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(sa.EXPORTED)
+
+
+def geom(**kw):
+    base = dict(batch=1, heads=2, frames=4, height=16, width=16, head_dim=64, cube=(4, 4, 4))
+    base.update(kw)
+    cube = base.pop("cube")
+    return sa.make_geom(base["batch"], base["heads"], base["frames"], base["height"],
+                        base["width"], base["head_dim"], cube)
+
+
+@pytest.mark.parametrize("grid,nblk,n_pad", [((4, 16, 16), 16, 1024), ((21, 30, 52), 624, 39936),
+                                             ((21, 45, 80), 1440, 92160), ((5, 7, 9), 12, 768)])
+def test_geometry_matches_oracle(grid, nblk, n_pad):
+    g = geom(frames=grid[0], height=grid[1], width=grid[2])
+    got = sa.sparse_attn_geometry(g)
+    og = O.Geometry(*grid)
+    assert got == (nblk, og.n_real, n_pad) == (og.nblk, og.n_real, og.n_pad)
+
+
+def test_geometry_other_cube_shapes():
+    g = geom(frames=6, height=20, width=20, cube=(2, 4, 8))
+    nblk, n_real, n_pad = sa.sparse_attn_geometry(g)
+    assert nblk == 3 * 5 * 3 and n_pad == 64 * nblk and n_real == 6 * 20 * 20
+
+
+def test_ceil_k_matches_worked_example_and_oracle():
+    assert sa.sparse_attn_ceil_k(0.03, 1562) == 47
+    for k, n in [(0.07, 100), (0.05, 1440), (0.03, 1440), (0.02, 1440), (0.25, 16), (0.0, 16),
+                 (1.0, 16), (3.0, 9), (-0.5, 9), (1e-6, 1440), (0.123456, 777)]:
+        assert sa.sparse_attn_ceil_k(k, n) == O.ceil_k(k, n), (k, n)
+    with pytest.raises(sa.SparseAttnError):
+        sa.sparse_attn_ceil_k(float("nan"), 16)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=96), sa.SA_ERR_UNSUPPORTED),
+    (dict(cube=(4, 4, 2)), sa.SA_ERR_INVALID_ARG),
+    (dict(cube=(0, 8, 8)), sa.SA_ERR_INVALID_ARG),
+    (dict(batch=0), sa.SA_ERR_INVALID_ARG),
+    (dict(frames=0), sa.SA_ERR_INVALID_ARG),
+])
+def test_bad_geometry_rejected(kw, code):
+    g = geom(**kw)
+    lib = sa.lib()
+    assert lib.sparse_attn_reorder(FAKE, FAKE, ctypes.byref(g), None) == code
+    assert sa.sparse_attn_last_error() != ""
+    assert lib.sparse_attn_mask_workspace_bytes(ctypes.byref(g)) == 0
+
+
+def test_null_and_misaligned_pointers_rejected():
+    g = geom()
+    lib = sa.lib()
+    B = ctypes.byref(g)
+    assert lib.sparse_attn_reorder(None, FAKE, B, None) == sa.SA_ERR_INVALID_ARG
+    assert lib.sparse_attn_reorder(FAKE, FAKE, B, None) == sa.SA_ERR_INVALID_ARG   # overlap
+    assert lib.sparse_attn_reorder(FAKE_MISALIGNED, FAKE, B, None) == sa.SA_ERR_INVALID_ARG
+    assert lib.sparse_attn_unreorder(FAKE, FAKE, FAKE, None, B, None) == sa.SA_ERR_INVALID_ARG
+    assert lib.sparse_attn_pool(FAKE, FAKE, None, FAKE, B, None) == sa.SA_ERR_INVALID_ARG
+    assert lib.sparse_attn_block_scores(FAKE, FAKE, None, 0.0, B, None) == sa.SA_ERR_INVALID_ARG
+    assert lib.sparse_attn_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, 16, B, 0.0, FAKE, None, None, 0,
+                               None) == sa.SA_ERR_INVALID_ARG
+    assert "lse_c" in sa.sparse_attn_last_error()
+    assert lib.sparse_attn_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, 0, B, 0.0, FAKE, FAKE, None, 0,
+                               None) == sa.SA_ERR_INVALID_ARG       # cap < 1
+    assert lib.sparse_attn_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, 16, B, float("nan"), FAKE, FAKE,
+                               None, 0, None) == sa.SA_ERR_INVALID_ARG
+
+
+def test_select_argument_rules():
+    g = geom()                                      # nblk = 16
+    lib = sa.lib()
+    B = ctypes.byref(g)
+    # Top-p may keep every block: cap must cover nblk
+    assert lib.sparse_attn_select(FAKE, B, 0.25, 0.5, None, FAKE, FAKE, 15, None) == sa.SA_ERR_CAPACITY
+    # Top-k only: cap must cover kc = 4
+    assert lib.sparse_attn_select(FAKE, B, 0.25, 0.0, None, FAKE, FAKE, 3, None) == sa.SA_ERR_CAPACITY
+    # a row budget replaces Top-k and needs p == 0
+    assert lib.sparse_attn_select(FAKE, B, 0.0, 0.5, FAKE, FAKE, FAKE, 16, None) == sa.SA_ERR_INVALID_ARG
+    assert lib.sparse_attn_select(FAKE, B, float("inf"), 0.5, None, FAKE, FAKE, 16, None) == sa.SA_ERR_INVALID_ARG
+    assert lib.sparse_attn_select(None, B, 0.25, 0.5, None, FAKE, FAKE, 16, None) == sa.SA_ERR_INVALID_ARG
+    big = geom(frames=64, height=64, width=68)      # 16*16*17 = 4352 blocks > 4096
+    assert lib.sparse_attn_select(FAKE, ctypes.byref(big), 0.1, 0.0, None, FAKE, FAKE, 5000,
+                                  None) == sa.SA_ERR_UNSUPPORTED
+
+
+def test_build_mask_argument_rules():
+    g = geom()
+    lib = sa.lib()
+    B = ctypes.byref(g)
+    need = lib.sparse_attn_mask_workspace_bytes(B)
+    assert need >= 3 * 16 * 64 * 8
+    assert lib.sparse_attn_build_mask(FAKE, FAKE, B, 128, 0.25, 0.5, None, FAKE, FAKE, 16, FAKE, need,
+                                      None) == sa.SA_ERR_UNSUPPORTED
+    assert lib.sparse_attn_build_mask(FAKE, FAKE, B, 64, 0.25, 0.5, None, FAKE, FAKE, 16, FAKE, need - 1,
+                                      None) == sa.SA_ERR_CAPACITY
+    assert lib.sparse_attn_build_mask(FAKE, FAKE, B, 64, 0.25, 0.5, None, FAKE, FAKE, 16,
+                                      ctypes.c_void_p(0x100010), need, None) == sa.SA_ERR_INVALID_ARG
+
+
+def test_python_binding_rejects_non_contiguous():
+    import torch
+    g = geom()
+    x = torch.zeros(1, 2, 1024, 128, dtype=torch.bfloat16)[..., :64]
+    with pytest.raises(ValueError):
+        sa.sparse_attn_reorder(x, x, g)
+    with pytest.raises(TypeError):
+        sa.sparse_attn_reorder(torch.zeros(4, dtype=torch.float32), x, g)

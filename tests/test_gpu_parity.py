@@ -1,0 +1,240 @@
+"""Parity of every HIP kernel with the fp64 oracle on small seeded inputs that
+still span several tiles and ragged tails.  All calls go through the C ABI."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_hybrid_amd as sa
+import oracle as O
+import synth
+from _helpers import (LSE_MAX_ABS, LSE_MEAN_ABS, O_MAX_ABS, O_MEAN_ABS, attn_errors,
+                      compare_lists, geom_of, lse_errors, ogeom_of, say, to64)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+# (name, batch, heads, d, grid, k_frac, p)
+SMALL = [
+    ("tiny", 1, 2, 64, (4, 16, 16), 0.25, 0.9),
+    ("ragged", 2, 3, 128, (5, 7, 9), 0.3, 0.6),
+    ("ragged-d64", 1, 3, 64, (9, 10, 11), 0.1, 0.5),
+    ("tall", 1, 2, 128, (6, 13, 22), 0.05, 0.3),
+    ("flat", 1, 1, 128, (1, 5, 70), 0.2, 0.0),
+]
+
+
+def case_inputs(name, batch, heads, d, grid, seed=0):
+    wl = synth.WORKLOADS[0] if name == "tiny" else synth.custom_workload(batch, heads, d, *grid)
+    q, k, v = synth.make_qkv(wl, seed)
+    return wl, q, k, v
+
+
+@pytest.fixture(scope="module", params=SMALL, ids=[c[0] for c in SMALL])
+def case(request):
+    name, batch, heads, d, grid, k_frac, p = request.param
+    say(f"[case {name}] B={batch} H={heads} d={d} grid={grid} k={k_frac} p={p}")
+    wl, q, k, v = case_inputs(name, batch, heads, d, grid)
+    g = geom_of(wl)
+    og = ogeom_of(wl)
+    qd, kd, vd = (t.to(DEV) for t in (q, k, v))
+    ref_qc, ref_kc, ref_vc = (O.reorder(to64(t), og) for t in (q, k, v))
+    ref_mask = O.build_mask(ref_qc, ref_kc, og, k_frac, p)
+    return dict(wl=wl, g=g, og=og, q=q, k=k, v=v, qd=qd, kd=kd, vd=vd, k_frac=k_frac, p=p,
+                ref_qc=ref_qc, ref_kc=ref_kc, ref_vc=ref_vc, ref_mask=ref_mask)
+
+
+def test_reorder_bit_exact(case):
+    g, og = case["g"], case["og"]
+    for t, tref in (("qd", "ref_qc"), ("vd", "ref_vc")):
+        xc = sa.reorder(case[t], g)
+        torch.cuda.synchronize()
+        assert np.array_equal(to64(xc), case[tref])
+        o, _ = sa.unreorder(xc, None, g)
+        torch.cuda.synchronize()
+        assert torch.equal(o.cpu(), case[t].cpu())
+
+
+def test_pool_and_scores_match_oracle(case):
+    g, og = case["g"], case["og"]
+    qc, kc = sa.reorder(case["qd"], g), sa.reorder(case["kd"], g)
+    nblk = og.nblk
+    B, H, d = g.batch, g.heads, g.head_dim
+    qbar = torch.empty(B, H, nblk, d, dtype=torch.float64, device=DEV)
+    kbar = torch.empty_like(qbar)
+    sa.sparse_attn_pool(qc, kc, qbar, kbar, g)
+    s = torch.empty(B, H, nblk, nblk, dtype=torch.float64, device=DEV)
+    sa.sparse_attn_block_scores(qbar, kbar, s, 0.0, g)
+    torch.cuda.synchronize()
+    ref = case["ref_mask"]
+    # exact float64 sums of bf16 values: the means are the correctly rounded ones
+    np.testing.assert_array_equal(qbar.cpu().numpy(), ref.qbar)
+    np.testing.assert_array_equal(kbar.cpu().numpy(), ref.kbar)
+    np.testing.assert_allclose(s.cpu().numpy(), ref.scores, rtol=1e-13,
+                               atol=1e-14 * np.abs(ref.scores).max())
+
+
+def test_select_on_oracle_scores(case):
+    """The selection kernel alone, fed the oracle's float64 scores."""
+    g, og, ref = case["g"], case["og"], case["ref_mask"]
+    s = torch.from_numpy(ref.scores).to(DEV)
+    nblk = og.nblk
+    lut = torch.full((g.batch, g.heads, nblk, nblk), -7, dtype=torch.int32, device=DEV)
+    counts = torch.empty((g.batch, g.heads, nblk), dtype=torch.int32, device=DEV)
+    sa.sparse_attn_select(s, g, case["k_frac"], case["p"], None, lut, counts, nblk)
+    torch.cuda.synchronize()
+    bad, near, invalid = compare_lists(lut.cpu().numpy(), counts.cpu().numpy(), ref, case["p"])
+    say(f"  select: {len(bad)} mismatched rows, {near} near ties ({len(invalid)} invalid)")
+    assert not bad and not invalid
+
+
+def test_build_mask_end_to_end(case):
+    g, og, ref = case["g"], case["og"], case["ref_mask"]
+    qc, kc = sa.reorder(case["qd"], g), sa.reorder(case["kd"], g)
+    lut, counts = sa.build_mask(qc, kc, g, case["k_frac"], case["p"])
+    torch.cuda.synchronize()
+    bad, near, invalid = compare_lists(lut.cpu().numpy(), counts.cpu().numpy(), ref, case["p"])
+    assert not bad and not invalid
+
+
+def test_fwd_with_oracle_lists(case):
+    g, og, ref = case["g"], case["og"], case["ref_mask"]
+    qc, kc, vc = (sa.reorder(case[t], g) for t in ("qd", "kd", "vd"))
+    lut = torch.from_numpy(ref.lut).to(DEV)
+    counts = torch.from_numpy(ref.counts).to(DEV)
+    oc, lse_c = sa.fwd(qc, kc, vc, lut, counts, g)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = O.sparse_attention(case["ref_qc"], case["ref_kc"], case["ref_vc"], ref.lut,
+                                        ref.counts, og)
+    mx, mean = attn_errors(to64(oc), o_ref)
+    lmx, lmean = lse_errors(lse_c.cpu().numpy().astype(np.float64), lse_ref)
+    say(f"  fwd: O max {mx:.3e} mean {mean:.3e}; LSE max {lmx:.3e} mean {lmean:.3e}")
+    assert mx <= O_MAX_ABS and mean <= O_MEAN_ABS
+    assert lmx <= LSE_MAX_ABS and lmean <= LSE_MEAN_ABS
+    # pad query slots: O = 0 and LSE = -inf
+    real = O.real_slots(og)
+    assert np.all(to64(oc)[:, :, ~real] == 0)
+    assert np.all(np.isneginf(lse_c.cpu().numpy()[:, :, ~real]))
+
+
+def test_whole_path_token_order(case):
+    g, og, ref = case["g"], case["og"], case["ref_mask"]
+    o, lse, lut, counts = sa.attention(case["qd"], case["kd"], case["vd"], g, case["k_frac"], case["p"])
+    torch.cuda.synchronize()
+    bad, _, invalid = compare_lists(lut.cpu().numpy(), counts.cpu().numpy(), ref, case["p"])
+    assert not bad and not invalid
+    # output against the oracle on the GPU's own lists (identical outside near ties)
+    o_ref_c, lse_ref_c = O.sparse_attention(case["ref_qc"], case["ref_kc"], case["ref_vc"],
+                                            lut.cpu().numpy(), counts.cpu().numpy(), og)
+    mx, mean = attn_errors(to64(o), O.unreorder(o_ref_c, og))
+    assert mx <= O_MAX_ABS and mean <= O_MEAN_ABS
+    lmx, lmean = lse_errors(lse.cpu().numpy().astype(np.float64), O.unreorder_rows(lse_ref_c, og))
+    assert lmx <= LSE_MAX_ABS and lmean <= LSE_MEAN_ABS
+
+
+def test_deterministic(case):
+    g = case["g"]
+    outs = []
+    for _ in range(2):
+        outs.append([t.cpu() for t in sa.attention(case["qd"], case["kd"], case["vd"], g,
+                                                   case["k_frac"], case["p"])])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+# ----------------------------------------------------------------------------
+# edge cases
+# ----------------------------------------------------------------------------
+def _small(d=128, grid=(5, 7, 9), heads=2, batch=1, seed=3):
+    wl = synth.custom_workload(batch, heads, d, *grid)
+    q, k, v = synth.make_qkv(wl, seed)
+    g, og = geom_of(wl), ogeom_of(wl)
+    return wl, g, og, q, k, v
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_all_blocks_kept_equals_dense(d):
+    say(f"[edge all-kept d={d}]")
+    wl, g, og, q, k, v = _small(d=d)
+    o, lse, lut, counts = sa.attention(q.to(DEV), k.to(DEV), v.to(DEV), g, 1.0, 0.0)
+    torch.cuda.synchronize()
+    assert torch.all(counts == og.nblk)
+    o_ref, lse_ref = O.dense_attention(to64(q), to64(k), to64(v))
+    mx, mean = attn_errors(to64(o), o_ref)
+    assert mx <= O_MAX_ABS and mean <= O_MEAN_ABS
+    lmx, _ = lse_errors(lse.cpu().double().numpy(), lse_ref)
+    assert lmx <= LSE_MAX_ABS
+    # p = 1 must keep everything as well
+    _, _, _, counts1 = sa.attention(q.to(DEV), k.to(DEV), v.to(DEV), g, 0.0, 1.0)
+    assert torch.all(counts1 == og.nblk)
+
+
+def test_keep_nothing_gives_zero_and_neg_inf():
+    say("[edge keep-none]")
+    wl, g, og, q, k, v = _small()
+    o, lse, lut, counts = sa.attention(q.to(DEV), k.to(DEV), v.to(DEV), g, 0.0, 0.0)
+    torch.cuda.synchronize()
+    assert torch.all(counts == 0)
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_row_budgets_and_variable_counts():
+    say("[edge row budgets]")
+    wl, g, og, q, k, v = _small(heads=3, grid=(8, 12, 12))
+    rng = np.random.default_rng(4)
+    budget = rng.integers(0, og.nblk + 3, size=(1, 3, og.nblk)).astype(np.int32)
+    qc, kc = (O.reorder(to64(t), og) for t in (q, k))
+    ref = O.build_mask(qc, kc, og, 0.0, 0.0, row_budget=np.clip(budget, 0, og.nblk))
+    qd, kd, vd = (sa.reorder(t.to(DEV), g) for t in (q, k, v))
+    lut, counts = sa.build_mask(qd, kd, g, 0.0, 0.0, row_budget=torch.from_numpy(budget).to(DEV))
+    torch.cuda.synchronize()
+    bad, _, invalid = compare_lists(lut.cpu().numpy(), counts.cpu().numpy(), ref, 0.0)
+    assert not bad and not invalid
+    oc, lse_c = sa.fwd(qd, kd, vd, lut, counts, g)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = O.sparse_attention(qc, kc, O.reorder(to64(v), og), lut.cpu().numpy(),
+                                        counts.cpu().numpy(), og)
+    mx, mean = attn_errors(to64(oc), o_ref)
+    assert mx <= O_MAX_ABS and mean <= O_MEAN_ABS
+    lmx, lmean = lse_errors(lse_c.cpu().double().numpy(), lse_ref)
+    assert lmx <= LSE_MAX_ABS and lmean <= LSE_MEAN_ABS
+
+
+def test_fwd_skips_out_of_range_ids_and_honours_cap():
+    say("[edge lut sanitising]")
+    wl, g, og, q, k, v = _small()
+    qd, kd, vd = (sa.reorder(t.to(DEV), g) for t in (q, k, v))
+    n = og.nblk
+    cap = 4
+    lut = torch.full((1, 2, n, cap), 0, dtype=torch.int32)
+    counts = torch.full((1, 2, n), 3, dtype=torch.int32)
+    lut[..., 0] = 1
+    lut[..., 1] = n + 5            # out of range: skipped
+    lut[..., 2] = -1               # out of range: skipped
+    lut[..., 3] = 2                # beyond the count: unused
+    counts[0, 1, :] = 9            # above cap: clamped to cap -> ids 1, (skip), (skip), 2
+    oc, lse_c = sa.fwd(qd, kd, vd, lut.to(DEV), counts.to(DEV), g)
+    torch.cuda.synchronize()
+    qc, kc, vc = (O.reorder(to64(t), og) for t in (q, k, v))
+    for h, kept in ((0, [1]), (1, [1, 2])):
+        for i in range(n):
+            o_ref, l_ref = O.attention_block(qc[0, h], kc[0, h], vc[0, h], kept, og, i)
+            got = to64(oc)[0, h, i * 64:(i + 1) * 64]
+            assert np.abs(got - o_ref).max() <= O_MAX_ABS
+
+
+def test_scale_argument():
+    say("[edge scale]")
+    wl, g, og, q, k, v = _small(grid=(4, 8, 8))
+    qd, kd, vd = (sa.reorder(t.to(DEV), g) for t in (q, k, v))
+    n = og.nblk
+    lut = torch.arange(n, dtype=torch.int32).repeat(1, 2, n, 1).reshape(1, 2, n, n)
+    counts = torch.full((1, 2, n), n, dtype=torch.int32)
+    oc, lse_c = sa.fwd(qd, kd, vd, lut.to(DEV), counts.to(DEV), g, scale=0.3)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = O.dense_attention(to64(q), to64(k), to64(v), scale=0.3)
+    o = O.unreorder(to64(oc), og)
+    mx, mean = attn_errors(o, o_ref)
+    assert mx <= O_MAX_ABS and mean <= O_MEAN_ABS
