@@ -1,0 +1,287 @@
+#!/usr/bin/env python3
+"""Throughput of the hybrid block-sparse attention hot path on one MI355X.
+
+One step = the whole path on one batch of resident synthetic input:
+reorder Q, K, V -> pool -> float64 block scores -> hybrid selection ->
+block-sparse forward -> unreorder O and LSE, all HIP kernels of
+libsparse_attn.so called through the C ABI.
+
+Headline workload: Wan2.1-14B-720p-shaped attention, B=1, H=40, d=128, latent
+grid 21x45x80 (75,600 tokens, 1,440 cubes of 4x4x4), Top-k 3% (the pages'
+value) and Top-p 0.073, which realises 95.0% block sparsity on these inputs
+with both rules active.  value = kept-block attention FLOPs (4*64*64*d per
+kept query-block/key-block pair) / step time.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import block_sparse_attention_hybrid_amd as sa  # noqa: E402
+import synth  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
+
+# name -> (synthetic workload id, k_frac, p, row budgets?)
+WORKLOADS = {
+    "720p-hybrid95": (2, 0.03, 0.073, False),
+    "720p-literal": (2, 0.03, 0.85, False),
+    "720p-extreme": (3, 0.02, 0.8, False),
+    "720p-varbudget": (4, 0.0, 0.0, True),
+    "480p": (1, 0.05, 0.9, False),
+}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="720p-hybrid95", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (HBM counter calibration)")
+    return ap.parse_args()
+
+
+class Path:
+    """Buffers and calls of one step."""
+
+    def __init__(self, wl, k_frac, p, budgets, dev):
+        self.wl, self.k_frac, self.p = wl, k_frac, p
+        self.g = sa.make_geom(wl.batch, wl.heads, wl.frames, wl.height, wl.width, wl.head_dim)
+        self.nblk, self.n_real, self.n_pad = sa.sparse_attn_geometry(self.g)
+        t0 = time.time()
+        q, k, v = synth.make_qkv(wl, 0)
+        log(f"[bench] inputs generated in {time.time() - t0:.1f}s")
+        self.q, self.k, self.v = (t.to(dev) for t in (q, k, v))
+        del q, k, v
+        B, H, d, n = wl.batch, wl.heads, wl.head_dim, self.nblk
+        shape_c = (B, H, self.n_pad, d)
+        self.qc, self.kc, self.vc, self.oc = (torch.empty(shape_c, dtype=torch.bfloat16, device=dev)
+                                              for _ in range(4))
+        self.o = torch.empty((B, H, self.n_real, d), dtype=torch.bfloat16, device=dev)
+        self.lse_c = torch.empty((B, H, self.n_pad), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((B, H, self.n_real), dtype=torch.float32, device=dev)
+        self.cap = n
+        self.lut = torch.empty((B, H, n, n), dtype=torch.int32, device=dev)
+        self.counts = torch.empty((B, H, n), dtype=torch.int32, device=dev)
+        self.ws = sa.mask_workspace(self.g, dev)
+        self.rb = None
+        if budgets:
+            self.rb = torch.from_numpy(synth.row_budgets(wl, 0)).to(dev)
+        nfw = sa.sparse_attn_fwd_workspace_bytes(self.g)
+        self.fws = torch.empty(max(nfw, 256), dtype=torch.uint8, device=dev)
+
+    def stages(self):
+        g = self.g
+        return [
+            ("reorder", lambda: [sa.sparse_attn_reorder(x, xc, lay, g) for x, xc, lay in
+                                 ((self.q, self.qc, sa.SA_LAYOUT_QK), (self.k, self.kc, sa.SA_LAYOUT_QK),
+                                  (self.v, self.vc, sa.SA_LAYOUT_V))]),
+            ("build_mask", lambda: sa.sparse_attn_build_mask(self.qc, self.kc, g, 64, self.k_frac, self.p,
+                                                             self.rb, self.lut, self.counts, self.cap,
+                                                             self.ws)),
+            ("fwd", lambda: sa.sparse_attn_fwd(self.qc, self.kc, self.vc, self.lut, self.counts, self.cap,
+                                               g, 0.0, self.oc, self.lse_c, self.fws)),
+            ("unreorder", lambda: sa.sparse_attn_unreorder(self.oc, self.o, self.lse_c, self.lse, g)),
+        ]
+
+    def step(self):
+        for _, fn in self.stages():
+            fn()
+
+
+def algorithmic_bytes(path):
+    """HBM bytes each stage must move at minimum (per step)."""
+    wl = path.wl
+    B, H, d, n = wl.batch, wl.heads, wl.head_dim, path.nblk
+    real, pad = path.n_real, path.n_pad
+    tok = 2 * d                                        # bf16 row bytes
+    kept = int(path.counts.sum().item())
+    return {
+        "reorder": 3 * B * H * (real + pad) * tok,
+        "build_mask": (B * H * (2 * pad * tok                 # read Q, K
+                                + 2 * n * d * 8 * 2           # Qbar, Kbar write + read
+                                + n * n * 8 * 2               # scores write + read
+                                + n * 4) + kept * 4),         # counts + kept ids
+        "unreorder": B * H * (real + pad) * (tok + 4),
+    }
+
+
+def cpu_baseline(path, seconds):
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    the mask of whole heads (pool, scores, selection of every row) and the
+    attention of sampled query blocks of those heads."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    wl = path.wl
+    og = O.Geometry(wl.frames, wl.height, wl.width)
+    kc_rows = O.ceil_k(path.k_frac, og.nblk)
+    rng = np.random.default_rng(0)
+    t_mask = t_attn = 0.0
+    flops = 0.0
+    heads_done = rows_done = 0
+    heads = list(range(min(3, wl.heads)))
+    budget_each = seconds / len(heads)
+    for h in heads:
+        q, k, v = synth.head_qkv(wl, 0, h, 0)
+        qc, kc, vc = (O.reorder(t.double().numpy(), og) for t in (q, k, v))
+        t0 = time.perf_counter()
+        s = O.block_scores(O.pool(qc, og), O.pool(kc, og), wl.head_dim)
+        if path.rb is not None:
+            rb = path.rb[0, h].cpu().numpy()
+            probs = O.block_softmax(s)
+            sels = [O.select_row(s[i], int(rb[i]), 0.0, probs[i]) for i in range(og.nblk)]
+        else:
+            sels = O.select_rows(s, kc_rows, path.p)
+        t_mask += time.perf_counter() - t0
+        heads_done += 1
+        t1 = time.perf_counter()
+        for i in rng.permutation(og.nblk):
+            O.attention_block(qc, kc, vc, sels[i].kept, og, int(i))
+            flops += sels[i].kept.size * 4.0 * 64 * 64 * wl.head_dim
+            rows_done += 1
+            if time.perf_counter() - t1 > budget_each:
+                break
+        t_attn += time.perf_counter() - t1
+    # mask time is charged pro rata to the rows whose attention was run
+    rows_per_head = og.nblk
+    charged = t_mask * rows_done / (heads_done * rows_per_head) + t_attn
+    return {
+        "value": flops / charged / 1e12,
+        "unit": "TFLOPS",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"fp64 numpy oracle: mask of {heads_done} whole heads (pool, scores, selection "
+                   f"of {rows_per_head} rows each; {t_mask:.2f}s) and attention of {rows_done} "
+                   f"sampled query blocks of those heads ({t_attn:.2f}s); mask time charged pro "
+                   f"rata to the sampled blocks"),
+        "seconds": round(t_mask + t_attn, 2),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        log("bench.py: only --gpus 1 is supported (the path is single-GPU; see the design notes "
+            "for how it would shard by head)")
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        log("bench.py needs a GPU")
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    wid, k_frac, p, budgets = WORKLOADS[args.workload]
+    wl = synth.WORKLOADS[wid]
+    path = Path(wl, k_frac, p, budgets, dev)
+    log(f"[bench] {args.workload}: {path.g}, nblk={path.nblk}, k_frac={k_frac}, p={p}")
+
+    for _ in range(args.warmup):
+        path.step()
+    torch.cuda.synchronize()
+
+    names = [n for n, _ in path.stages()]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        ev[s][0].record()
+        for j, (_, fn) in enumerate(path.stages()):
+            fn()
+            ev[s][j + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stage_ms = {n: float(np.mean([ev[s][j].elapsed_time(ev[s][j + 1]) for s in range(args.steps)]))
+                for j, n in enumerate(names)}
+    ms_per_step = wall * 1e3 / args.steps
+
+    kept = int(path.counts.sum().item())
+    rows = wl.batch * wl.heads * path.nblk
+    density = kept / (rows * path.nblk)
+    flops_kept = kept * 4.0 * 64 * 64 * wl.head_dim
+    flops_real = 4.0 * path.n_real ** 2 * wl.head_dim * wl.heads * wl.batch * density
+    value = flops_kept / (ms_per_step * 1e-3) / 1e12
+    fwd_tflops = flops_kept / (stage_ms["fwd"] * 1e-3) / 1e12
+    abytes = algorithmic_bytes(path)
+    gbps = {n: abytes[n] / (stage_ms[n] * 1e-3) / 1e9 for n in abytes}
+    mask_path_gbps = (abytes["reorder"] + abytes["build_mask"]) / (
+        (stage_ms["reorder"] + stage_ms["build_mask"]) * 1e-3) / 1e9
+
+    if args.copy_calibration:
+        x = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+
+    out = {
+        "metric": "sparse-attn effective TFLOPS @95% sparsity, 75.6K tok; % of bf16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; Wan2.1-720p-shaped Q/K/V, uniform/skewed/local heads)",
+        "config": {
+            "workload": (f"{args.workload}: B={wl.batch} H={wl.heads} d={wl.head_dim} grid "
+                         f"{wl.frames}x{wl.height}x{wl.width} ({path.n_real} tokens, {path.nblk} "
+                         f"blocks of 64), k_frac={k_frac}, p={p}"),
+            "global_batch": wl.batch,
+            "seq_len": path.n_real,
+            "parallelism": "single GPU",
+            "block_sparsity": round(1.0 - density, 5),
+            "kept_blocks": kept,
+        },
+        "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "fwd_tflops": round(fwd_tflops, 2),
+        "real_token_tflops": round(flops_real / (ms_per_step * 1e-3) / 1e12, 2),
+        "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "stage_gbps": {k: round(v, 1) for k, v in gbps.items()},
+        "mask_path_gbps": round(mask_path_gbps, 1),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(fwd_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline(path, args.cpu_seconds)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

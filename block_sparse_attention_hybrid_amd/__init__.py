@@ -27,6 +27,8 @@ SA_ERR_INVALID_ARG = -1
 SA_ERR_UNSUPPORTED = -2
 SA_ERR_CAPACITY = -3
 SA_ERR_HIP = -4
+SA_LAYOUT_QK = 0
+SA_LAYOUT_V = 1
 
 EXPORTED = (
     "sparse_attn_geometry", "sparse_attn_ceil_k", "sparse_attn_reorder",
@@ -68,7 +70,7 @@ _GP = ctypes.POINTER(Geom)
 _SIGS = {
     "sparse_attn_geometry": (_i32, [_GP, ctypes.POINTER(_i32), ctypes.POINTER(_i64), ctypes.POINTER(_i64)]),
     "sparse_attn_ceil_k": (_i32, [_f64, _i32]),
-    "sparse_attn_reorder": (_i32, [_vp, _vp, _GP, _vp]),
+    "sparse_attn_reorder": (_i32, [_vp, _vp, _i32, _GP, _vp]),
     "sparse_attn_unreorder": (_i32, [_vp, _vp, _vp, _vp, _GP, _vp]),
     "sparse_attn_pool": (_i32, [_vp, _vp, _vp, _vp, _GP, _vp]),
     "sparse_attn_block_scores": (_i32, [_vp, _vp, _vp, _f64, _GP, _vp]),
@@ -141,9 +143,9 @@ def sparse_attn_ceil_k(k_frac: float, nblk: int) -> int:
     return _check(lib().sparse_attn_ceil_k(float(k_frac), int(nblk)))
 
 
-def sparse_attn_reorder(x, xc, g: Geom, stream=None) -> None:
+def sparse_attn_reorder(x, xc, layout: int, g: Geom, stream=None) -> None:
     _check(lib().sparse_attn_reorder(_ptr(x, torch.bfloat16, "x"), _ptr(xc, torch.bfloat16, "xc"),
-                                     ctypes.byref(g), _stream(stream, x)))
+                                     int(layout), ctypes.byref(g), _stream(stream, x)))
 
 
 def sparse_attn_unreorder(oc, o, lse_c, lse, g: Geom, stream=None) -> None:
@@ -213,10 +215,12 @@ def _empty(shape, dtype, like):
     return torch.empty(shape, dtype=dtype, device=like.device)
 
 
-def reorder(x: torch.Tensor, g: Geom, stream=None) -> torch.Tensor:
+def reorder(x: torch.Tensor, g: Geom, layout: int = SA_LAYOUT_QK, stream=None) -> torch.Tensor:
+    """Cube-major copy of row-major tokens in the given block layout
+    (SA_LAYOUT_QK for queries and keys, SA_LAYOUT_V for values)."""
     nblk, n_real, n_pad = sparse_attn_geometry(g)
     xc = _empty((g.batch, g.heads, n_pad, g.head_dim), torch.bfloat16, x)
-    sparse_attn_reorder(x, xc, g, stream)
+    sparse_attn_reorder(x, xc, layout, g, stream)
     return xc
 
 
@@ -259,7 +263,9 @@ def fwd(qc, kc, vc, lut, counts, g: Geom, scale: float = 0.0, stream=None):
 def attention(q, k, v, g: Geom, k_frac: float, p: float, row_budget=None, stream=None):
     """Whole path on row-major tokens: reorder, build the hybrid mask, sparse
     forward, unreorder.  Returns (O [B,H,N,d] bf16, LSE [B,H,N] fp32, lut, counts)."""
-    qc, kc, vc = (reorder(t, g, stream) for t in (q, k, v))
+    qc = reorder(q, g, SA_LAYOUT_QK, stream)
+    kc = reorder(k, g, SA_LAYOUT_QK, stream)
+    vc = reorder(v, g, SA_LAYOUT_V, stream)
     lut, counts = build_mask(qc, kc, g, k_frac, p, row_budget, stream=stream)
     oc, lse_c = fwd(qc, kc, vc, lut, counts, g, stream=stream)
     o, lse = unreorder(oc, lse_c, g, stream)

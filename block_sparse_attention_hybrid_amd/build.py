@@ -20,8 +20,12 @@ OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsparse_attn.so")
 ARCH = "gfx950"
 
+# -amdgpu-mfma-vgpr-form: matrix-core accumulators live in VGPRs, which lets
+# the attention kernel load its K/V operands straight into AGPRs instead of
+# shuttling the output accumulator between the two register files
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
-          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def _hipcc() -> str:

@@ -141,13 +141,15 @@ int32_t sparse_attn_ceil_k(double k_frac, int32_t nblk) {
   return r;
 }
 
-int32_t sparse_attn_reorder(const void* x, void* xc, const sa_geom* g, void* stream) {
+int32_t sparse_attn_reorder(const void* x, void* xc, int32_t layout, const sa_geom* g, void* stream) {
   sa::Geom d;
   SA_TRY(make_geom(g, d));
   SA_TRY(check_ptr(x, 16, "x"));
   SA_TRY(check_ptr(xc, 16, "xc"));
+  if (layout != SA_LAYOUT_QK && layout != SA_LAYOUT_V)
+    return fail(SA_ERR_INVALID_ARG, "layout must be SA_LAYOUT_QK or SA_LAYOUT_V (got %d)", layout);
   if (x == xc) return fail(SA_ERR_INVALID_ARG, "x and xc must not overlap");
-  return hip_status(sa::launch_reorder(x, xc, d, (hipStream_t)stream), "reorder launch");
+  return hip_status(sa::launch_reorder(x, xc, layout, d, (hipStream_t)stream), "reorder launch");
 }
 
 int32_t sparse_attn_unreorder(const void* oc, void* o, const float* lse_c, float* lse,

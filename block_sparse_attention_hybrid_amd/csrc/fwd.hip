@@ -8,26 +8,27 @@
 // the kernel takes the block-index list directly.  Keys in pad slots of a
 // partial cube are masked out (VSA2 section 2.2, "Kernel Implementation").
 //
-// Mapping to CDNA4.  One workgroup = one query block of 64 tokens = 2 waves
-// of 32 queries.  Both products use v_mfma_f32_32x32x16_bf16 in transposed
-// form so that the probabilities never leave registers:
-//   S^T (32 keys x 32 queries) = K (A operand, rows from LDS) x Q^T (B
-//        operand, held in registers for the whole row);
-//   O^T (32 dims x 32 queries) += V^T (A operand, from a transposed LDS copy)
-//        x P^T (B operand).
-// The accumulator layout of the first product gives every lane one query and
-// 16 of its keys per 32-key tile; the second product's B operand wants one
-// query and 8 keys per lane, which is a subset of the same registers once
-// its k index is permuted -- and V^T's LDS reads use the same permutation.
-// Row statistics (max, sum) therefore live per lane; the two half-waves that
-// share a query combine their maxima with one cross-lane exchange.
+// Mapping to CDNA4.  One wavefront owns one query block (64 queries) for the
+// whole row, so every K/V byte brought into the CU is used by all 64 queries.
+// Both products run on v_mfma_f32_32x32x16_bf16 in transposed form:
+//   S^T (32 keys x 32 queries) = K (A operand) x Q^T (B operand),
+//   O^T (32 dims x 32 queries) += V^T (A operand) x P^T (B operand).
+// The accumulator layout of the first product leaves every lane with one
+// query and 16 of its keys per 32-key tile.  The K rows fed to lane r are
+// permuted (sigma below) so that, for each 16-key step of the second product,
+// a lane's 8 probabilities belong to 8 consecutive keys -- exactly the 8 keys
+// the V layout stores in that lane's 16-byte chunk.  P therefore never leaves
+// registers, and every K and V operand is one fully coalesced 1 KB wave load
+// (the QK and V block layouts of sa_layout.h).  The 16 KB of Q operands sit in
+// LDS for the whole row.
 //
-// K and V tiles (16 KB each at d = 128) are staged through LDS and shared by
-// the two waves; the next kept block's tiles are fetched into registers while
-// the current one is computed.  Rows are mapped to workgroups so that each
-// XCD (workgroups are dispatched round-robin over the 8 XCDs) processes a
-// contiguous range of rows: neighbouring query blocks of a head, whose kept
-// lists overlap, then share K/V tiles in that XCD's L2.
+// Software pipeline: the next block's K tile is requested as soon as the
+// current S^T is computed and its V tile as soon as the current O update is
+// issued, so each load has a GEMM plus a softmax of lead time.  The running
+// max is only raised when a block's max exceeds it by more than 2^8 (in the
+// base-2 exponent), which leaves the result exact (the final O/l ratio does
+// not depend on the reference max) and skips almost every rescale of the
+// 128-register output accumulator.
 #include "sa_launch.h"
 
 #include <math.h>
@@ -36,225 +37,212 @@ namespace sa {
 
 namespace {
 
-constexpr int kThreads = 128;
 constexpr int kXcds = 8;
 constexpr float kLn2 = 0.69314718055994531f;
+constexpr float kStaleMax = 8.f;  // allowed growth of the base-2 exponent before a rescale
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// two floats -> packed bf16 pair (round to nearest even), one v_cvt_pk_bf16_f32
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  const __bf16 x = (__bf16)a, y = (__bf16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 template <int D>
-struct Tile {
-  static constexpr int kLdK = D + 8;     // bf16 per K row in LDS (16-byte pad)
-  static constexpr int kLdV = 64 + 4;    // bf16 per V^T row in LDS (8-byte pad)
-  static constexpr int kCpr = D / 8;     // 16-byte chunks per K/V row
-  static constexpr int kKLoads = 64 * kCpr / kThreads;        // K chunks per thread
-  static constexpr int kVTiles = (64 / 4) * kCpr / kThreads;  // 4x8 V micro-tiles per thread
-};
+__global__ __launch_bounds__(64) void fwd_kernel(const u32x4* __restrict__ qc,
+                                                 const u32x4* __restrict__ kc,
+                                                 const u32x4* __restrict__ vc,
+                                                 const int32_t* __restrict__ lut,
+                                                 const int32_t* __restrict__ counts, int cap, Geom g,
+                                                 float sc_log2, bf16* __restrict__ oc,
+                                                 float* __restrict__ lse_c, int rows, int per_xcd) {
+  constexpr int NDS = D / 16;     // 16-dim steps of S^T
+  constexpr int NDT = D / 32;     // 32-dim tiles of O^T
+  constexpr int BLK = 64 * D / 8; // 16-byte units per block
 
-template <int D>
-__global__ __launch_bounds__(kThreads) void fwd_kernel(const bf16* __restrict__ qc,
-                                                       const bf16* __restrict__ kc,
-                                                       const bf16* __restrict__ vc,
-                                                       const int32_t* __restrict__ lut,
-                                                       const int32_t* __restrict__ counts, int cap,
-                                                       Geom g, float sc_log2, bf16* __restrict__ oc,
-                                                       float* __restrict__ lse_c, int rows,
-                                                       int per_xcd) {
-  using T = Tile<D>;
-  __shared__ __attribute__((aligned(16))) bf16 Ks[64 * T::kLdK];
-  __shared__ __attribute__((aligned(16))) bf16 Vt[D * T::kLdV];
-
+  // workgroups are dispatched round-robin over the 8 XCDs; give each XCD a
+  // contiguous run of rows so neighbouring query blocks (overlapping lists)
+  // share K/V tiles in that XCD's L2
   const int w = blockIdx.x;
   const int row = (w % kXcds) * per_xcd + w / kXcds;
   if (row >= rows) return;
   const long long bh = row / g.nblk;
   const int i = row - (int)(bh * g.nblk);
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int h = lane >> 5, ql = lane & 31;
-  const int q = wave * 32 + ql;  // query slot in the block
 
-  const long long head_off = bh * g.n_pad * D;
-  const bf16* kh = kc + head_off;
-  const bf16* vh = vc + head_off;
+  const int lane = threadIdx.x;
+  const int hf = lane >> 5, r = lane & 31;
+  // K row fed to A-operand lane r: sigma(8a + 4b + c) = 16(a/2) + 8b + 4(a%2) + c
+  const int sig = 16 * (r >> 4) + 8 * ((r >> 2) & 1) + 4 * ((r >> 3) & 1) + (r & 3);
+  const int kpos = hf * 32 + sig;
 
-  // Q^T operand: this lane's query, dims 16*ds + 8*h .. +7
-  bf16x8 qreg[D / 16];
-  {
-    const u32x4* qrow = reinterpret_cast<const u32x4*>(qc + head_off + ((long long)i * 64 + q) * D);
+  const long long head = bh * (g.n_pad / 64) * (long long)BLK;
+  const u32x4* qb = qc + head + (long long)i * BLK;
+  const u32x4* kh = kc + head;
+  const u32x4* vh = vc + head;
+
+  // Q^T operand chunks live in LDS (each lane reads back its own 16 bytes, so
+  // the reads are conflict-free); registers are kept for K, V, S, P and O
+  __shared__ u32x4 qlds[2 * NDS * 64];
 #pragma unroll
-    for (int ds = 0; ds < D / 16; ++ds) qreg[ds] = as_bf16x8(qrow[2 * ds + h]);
-  }
+  for (int c = 0; c < 2 * NDS; ++c) qlds[c * 64 + lane] = qb[c * 64 + lane];
+  __syncthreads();
 
   int count = counts[row];
   count = count < 0 ? 0 : (count > cap ? cap : count);
   const int32_t* lrow = lut + (long long)row * cap;
 
-  f32x16 acc[D / 32];
+  f32x16 acc[NDT][2];
 #pragma unroll
-  for (int t = 0; t < D / 32; ++t)
+  for (int t = 0; t < NDT; ++t)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
-  float m = -INFINITY, l = 0.f;
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[t][qt][e] = 0.f;
+  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
 
-  // register staging of one K/V tile
-  u32x4 kreg[T::kKLoads];
-  u32x4 vreg[T::kVTiles][4];
-  auto load_tile = [&](int j) {
-    const u32x4* kb = reinterpret_cast<const u32x4*>(kh + (long long)j * 64 * D);
-    const u32x4* vb = reinterpret_cast<const u32x4*>(vh + (long long)j * 64 * D);
+  u32x4 kreg[2][NDS];
+  u32x4 vreg[NDT][4];
+  auto valid_id = [&](int j) { return j >= 0 && j < g.nblk; };
+  // bit s set iff slot s of block j holds a real token (one slot per lane)
+  auto real_mask = [&](int j) -> uint64_t { return ballot(valid_id(j) && slot_token(g, j, lane) >= 0); };
+  auto load_k = [&](int j) {
+    const u32x4* kb = kh + (long long)(valid_id(j) ? j : 0) * BLK;
 #pragma unroll
-    for (int r = 0; r < T::kKLoads; ++r) kreg[r] = kb[tid + kThreads * r];
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-    for (int r = 0; r < T::kVTiles; ++r) {
-      const int mt = tid + kThreads * r;
-      const int kg = mt % 16, dc = mt / 16;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) vreg[r][kk] = vb[(4 * kg + kk) * T::kCpr + dc];
-    }
+      for (int ds = 0; ds < NDS; ++ds) kreg[kt][ds] = kb[(kt * NDS + ds) * 64 + kpos];
   };
-  auto store_tile = [&](uint64_t real) {
+  auto load_v = [&](int j) {
+    const u32x4* vb = vh + (long long)(valid_id(j) ? j : 0) * BLK;
 #pragma unroll
-    for (int r = 0; r < T::kKLoads; ++r) {
-      const int c = tid + kThreads * r;
-      const int key = c / T::kCpr, ch = c % T::kCpr;
-      u32x4 v = kreg[r];
-      if (!((real >> key) & 1ull)) v = u32x4{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(&Ks[key * T::kLdK + ch * 8]) = v;
-    }
+    for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-    for (int r = 0; r < T::kVTiles; ++r) {
-      const int mt = tid + kThreads * r;
-      const int kg = mt % 16, dc = mt / 16;
-      u32x4 x[4];
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        x[kk] = ((real >> (4 * kg + kk)) & 1ull) ? vreg[r][kk] : u32x4{0u, 0u, 0u, 0u};
-      // transpose a 4 (keys) x 8 (dims) micro-tile into 8 rows of 4 keys
-#pragma unroll
-      for (int dd = 0; dd < 8; ++dd) {
-        const int word = dd >> 1, hi = dd & 1;
-        uint32_t e[4];
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) e[kk] = hi ? (x[kk][word] >> 16) : (x[kk][word] & 0xffffu);
-        u32x2 pk = {e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
-        *reinterpret_cast<u32x2*>(&Vt[(8 * dc + dd) * T::kLdV + 4 * kg]) = pk;
-      }
-    }
-  };
-  auto lut_at = [&](int it, bool& ok) -> int {
-    const int j = lrow[it];
-    ok = (j >= 0 && j < g.nblk);
-    return ok ? j : 0;
+      for (int ks = 0; ks < 4; ++ks) vreg[dt][ks] = vb[(dt * 4 + ks) * 64 + lane];
   };
 
-  bool ok_cur = false;
-  int j_cur = 0;
+  int j_cur = count > 0 ? lrow[0] : 0;
   if (count > 0) {
-    j_cur = lut_at(0, ok_cur);
-    load_tile(j_cur);
-    store_tile(ok_cur ? block_real_mask(g, j_cur) : 0ull);
+    load_k(j_cur);
+    load_v(j_cur);
   }
   for (int it = 0; it < count; ++it) {
-    const uint64_t real = ok_cur ? block_real_mask(g, j_cur) : 0ull;
-    bool ok_next = false;
-    int j_next = 0;
-    __syncthreads();
-    if (it + 1 < count) {
-      j_next = lut_at(it + 1, ok_next);
-      load_tile(j_next);
-    }
+    const int j_next = (it + 1 < count) ? lrow[it + 1] : 0;
+    const uint64_t real = real_mask(j_cur);
+    const bool full = real == ~0ull;   // wave-uniform: most blocks have no pad slot
+    // this lane's 32 key bits: byte (kt, g) = keys 32 kt + 16 g + 8 hf .. +7
+    const uint32_t lmask = (uint32_t)((real >> (8 * hf)) & 0xffu) |
+                           ((uint32_t)((real >> (16 + 8 * hf)) & 0xffu) << 8) |
+                           ((uint32_t)((real >> (32 + 8 * hf)) & 0xffu) << 16) |
+                           ((uint32_t)((real >> (48 + 8 * hf)) & 0xffu) << 24);
 
-    // S^T = K Q^T for keys 0..31 and 32..63
-    f32x16 st[2];
+    // the two 32-query halves are processed one after the other: S^T and P of
+    // one half are live at a time, and the softmax of one half can overlap
+    // the matrix-core work of the other
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int qt = 0; qt < 2; ++qt) {
+      // S^T tiles of this query half (kt: keys 0-31 / 32-63)
+      f32x16 st[2];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) st[kt][r] = 0.f;
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int ds = 0; ds < D / 16; ++ds) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Ks[(32 * kt + ql) * T::kLdK + 16 * ds + 8 * h]);
-        st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ds], st[kt], 0, 0, 0);
+        for (int e = 0; e < 16; ++e) st[kt][e] = 0.f;
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) {
+        const u32x4 qv = qlds[(qt * NDS + ds) * 64 + lane];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+          st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kreg[kt][ds]), as_bf16x8(qv), st[kt],
+                                                           0, 0, 0);
       }
-    }
-    // scale into the log2 domain, mask pad keys, row max
-    float mloc = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = 32 * kt + 8 * (r >> 2) + 4 * h + (r & 3);
-        float v = st[kt][r] * sc_log2;
-        if (!((real >> key) & 1ull)) v = -INFINITY;
-        st[kt][r] = v;
-        mloc = fmaxf(mloc, v);
-      }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-    const float m_new = fmaxf(m, mloc);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m - m_use);
-    float lsum = 0.f;
-    uint32_t pw[2][8];  // P^T as packed bf16 pairs, in register order
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(st[kt][r] - m_use);
-        const float p1 = __builtin_amdgcn_exp2f(st[kt][r + 1] - m_use);
-        lsum += p0 + p1;
-        pw[kt][r >> 1] = pack_bf16x2(p0, p1);
-      }
-    l = l * alpha + lsum;
-    m = m_new;
-#pragma unroll
-    for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[t][r] *= alpha;
+      if (qt == 1 && it + 1 < count) load_k(j_next);
+      __builtin_amdgcn_sched_barrier(0);
 
-    // O^T += V^T P^T; k-step ks covers registers 8*(ks%2) .. +7 of key tile ks/2
+      // online softmax in the base-2 domain; register e of tile kt holds key
+      // 32 kt + 16 (e / 8) + 8 hf + e % 8, i.e. bit 16 kt + e of lmask.  The
+      // scale is positive, so the max is taken on the raw scores and the scale
+      // folds into the exponent's fma.
+      float mx = -INFINITY;
+      if (full) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int kt = ks >> 1, a0 = 2 * (ks & 1);
-      const u32x4 bw = {pw[kt][4 * (ks & 1)], pw[kt][4 * (ks & 1) + 1], pw[kt][4 * (ks & 1) + 2],
-                        pw[kt][4 * (ks & 1) + 3]};
-      const bf16x8 b = as_bf16x8(bw);
-      const int key0 = 32 * kt + 8 * a0 + 4 * h;
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-        const bf16* vrow = &Vt[(32 * dt + ql) * T::kLdV];
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + key0);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + key0 + 8);
-        const u32x4 aw = {lo[0], lo[1], hi[0], hi[1]};
-        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(aw), b, acc[dt], 0, 0, 0);
+          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, st[kt][e]);
+      } else {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, ((lmask >> (16 * kt + e)) & 1u) ? st[kt][e] : -INFINITY);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sc_log2;
+      const bool grow = mx > m[qt] + kStaleMax;
+      if (__any(grow)) {
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m[qt] - mx) : 1.f;
+        l[qt] *= alpha;
+#pragma unroll
+        for (int t = 0; t < NDT; ++t)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[t][qt][e] *= alpha;
+      }
+      if (grow) m[qt] = mx;
+      const float nmu = m[qt] == -INFINITY ? 0.f : -m[qt];
+      uint32_t pw[2][8];
+      float ls = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int e = 0; e < 16; e += 2) {
+          float p0 = __builtin_amdgcn_exp2f(fmaf(st[kt][e], sc_log2, nmu));
+          float p1 = __builtin_amdgcn_exp2f(fmaf(st[kt][e + 1], sc_log2, nmu));
+          if (!full) {
+            p0 = ((lmask >> (16 * kt + e)) & 1u) ? p0 : 0.f;
+            p1 = ((lmask >> (16 * kt + e + 1)) & 1u) ? p1 : 0.f;
+          }
+          ls += p0 + p1;
+          pw[kt][e >> 1] = pack_bf16x2(p0, p1);
+        }
+      l[qt] += ls;
+      __builtin_amdgcn_sched_barrier(0);
+
+      // O^T += V^T P^T; k-step ks covers keys 16 ks .. +15 = registers
+      // 8 (ks % 2) .. +7 of tile ks / 2
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int kt = ks >> 1, o4 = 4 * (ks & 1);
+        const u32x4 bw = {pw[kt][o4], pw[kt][o4 + 1], pw[kt][o4 + 2], pw[kt][o4 + 3]};
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+          acc[dt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vreg[dt][ks]), as_bf16x8(bw),
+                                                                acc[dt][qt], 0, 0, 0);
       }
     }
-    __syncthreads();
-    if (it + 1 < count) store_tile(ok_next ? block_real_mask(g, j_next) : 0ull);
+    if (it + 1 < count) load_v(j_next);
     j_cur = j_next;
-    ok_cur = ok_next;
   }
 
   // epilogue: O = acc / l, LSE = (m + log2 l) ln 2; pad queries and empty rows -> 0, -inf
-  const float l_tot = l + __shfl_xor(l, 32, 64);
-  const bool qreal = (block_real_mask(g, i) >> q) & 1ull;
-  const bool live = qreal && l_tot > 0.f;
-  const float inv = live ? 1.f / l_tot : 0.f;
-  bf16* orow = oc + head_off + ((long long)i * 64 + q) * D;
+  const uint64_t qreal = real_mask(i);
+  bf16* ob = oc + (bh * g.n_pad + (long long)i * 64) * D;
+  float* lb = lse_c + bh * g.n_pad + (long long)i * 64;
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
+  for (int qt = 0; qt < 2; ++qt) {
+    const float lt = l[qt] + __shfl_xor(l[qt], 32, 64);
+    const int q = 32 * qt + r;
+    const bool live = ((qreal >> q) & 1ull) && lt > 0.f;
+    const float inv = live ? 1.f / lt : 0.f;
+    bf16* orow = ob + (long long)q * D;
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const u32x2 v = {pack_bf16x2(acc[dt][4 * a] * inv, acc[dt][4 * a + 1] * inv),
-                       pack_bf16x2(acc[dt][4 * a + 2] * inv, acc[dt][4 * a + 3] * inv)};
-      *reinterpret_cast<u32x2*>(orow + 32 * dt + 8 * a + 4 * h) = v;
-    }
-  if (h == 0) {
-    lse_c[bh * g.n_pad + (long long)i * 64 + q] = live ? (m + __log2f(l_tot)) * kLn2 : -INFINITY;
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const u32x2 v = {pack_bf16x2(acc[dt][qt][4 * a] * inv, acc[dt][qt][4 * a + 1] * inv),
+                         pack_bf16x2(acc[dt][qt][4 * a + 2] * inv, acc[dt][qt][4 * a + 3] * inv)};
+        *reinterpret_cast<u32x2*>(orow + 32 * dt + 8 * a + 4 * hf) = v;
+      }
+    if (hf == 0) lb[q] = live ? (m[qt] + __log2f(lt)) * kLn2 : -INFINITY;
   }
 }
 
@@ -269,15 +257,15 @@ hipError_t launch_fwd(const void* qc, const void* kc, const void* vc, const int3
   const int per_xcd = (int)((rows + kXcds - 1) / kXcds);
   const float sc_log2 = scale * 1.4426950408889634f;
   const dim3 grid((unsigned)(per_xcd * kXcds));
-  if (g.d == 128) {
-    fwd_kernel<128><<<grid, kThreads, 0, s>>>(static_cast<const bf16*>(qc), static_cast<const bf16*>(kc),
-                                              static_cast<const bf16*>(vc), lut, counts, cap, g, sc_log2,
-                                              static_cast<bf16*>(oc), lse_c, (int)rows, per_xcd);
-  } else {
-    fwd_kernel<64><<<grid, kThreads, 0, s>>>(static_cast<const bf16*>(qc), static_cast<const bf16*>(kc),
-                                             static_cast<const bf16*>(vc), lut, counts, cap, g, sc_log2,
-                                             static_cast<bf16*>(oc), lse_c, (int)rows, per_xcd);
-  }
+  const u32x4* q = static_cast<const u32x4*>(qc);
+  const u32x4* k = static_cast<const u32x4*>(kc);
+  const u32x4* v = static_cast<const u32x4*>(vc);
+  if (g.d == 128)
+    fwd_kernel<128><<<grid, 64, 0, s>>>(q, k, v, lut, counts, cap, g, sc_log2, static_cast<bf16*>(oc), lse_c,
+                                        (int)rows, per_xcd);
+  else
+    fwd_kernel<64><<<grid, 64, 0, s>>>(q, k, v, lut, counts, cap, g, sc_log2, static_cast<bf16*>(oc), lse_c,
+                                       (int)rows, per_xcd);
   return hipGetLastError();
 }
 

@@ -5,12 +5,14 @@
 // permutation once at the ends of the transformer and pads each grid side up
 // to a multiple of the cube side.
 //
-// One workgroup per (batch*head, block).  Every destination block is 64 rows
-// of d bf16 values written contiguously; the source rows of a cube come in
-// runs of cw consecutive tokens.  Each lane moves 16-byte chunks, so a wave
-// reads and writes whole 256-byte rows (d = 128) and the traffic is the
-// algorithmic minimum: N rows read, n_pad rows written.
+// One workgroup per (batch*head, block).  The block's 64 source rows (runs of
+// cw consecutive tokens) are read with 16-byte lane loads into LDS, then
+// written out as 1 KB operand chunks in the QK or V element order (see
+// sa_layout.h), so both the reads and the writes are whole-row / whole-chunk
+// and the traffic is the algorithmic minimum: N rows read, n_pad rows written.
+// Pad slots are written as zeros.
 #include "sa_launch.h"
+#include "sa_layout.h"
 
 namespace sa {
 
@@ -18,19 +20,44 @@ namespace {
 
 constexpr int kThreads = 256;
 
+template <bool kV>
 __global__ __launch_bounds__(kThreads) void reorder_kernel(const u32x4* __restrict__ x,
                                                            u32x4* __restrict__ xc, Geom g) {
-  const int i = blockIdx.x;                    // block within the head
-  const long long bh = blockIdx.y;             // batch*heads + head
-  const int cpr = g.d / 8;                     // 16-byte chunks per row
+  // QK: tile[s][c] (row pitch d+8); V: tile[c][s] (row pitch 72)
+  __shared__ __attribute__((aligned(16))) uint16_t tile[128 * 72];
+  const int i = blockIdx.x;
+  const long long bh = blockIdx.y;
+  const int d = g.d, cpr = d / 8;
+  const int ldq = d + 8, ldv = 72;
   const long long src_head = bh * g.n_real * cpr;
   const long long dst_blk = (bh * g.n_pad + (long long)i * kBlock) * cpr;
   for (int idx = threadIdx.x; idx < kBlock * cpr; idx += kThreads) {
-    const int s = idx / cpr, c = idx - s * cpr;
+    const int s = idx / cpr, c8 = idx - s * cpr;
     const long long n = slot_token(g, i, s);
     u32x4 v = {0u, 0u, 0u, 0u};
-    if (n >= 0) v = x[src_head + n * cpr + c];
-    xc[dst_blk + idx] = v;
+    if (n >= 0) v = x[src_head + n * cpr + c8];
+    if (!kV) {
+      *reinterpret_cast<u32x4*>(&tile[s * ldq + c8 * 8]) = v;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t w = v[e >> 1];
+        tile[(c8 * 8 + e) * ldv + s] = (uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu));
+      }
+    }
+  }
+  __syncthreads();
+  for (int u = threadIdx.x; u < kBlock * cpr; u += kThreads) {
+    const int chunk = u >> 6, p = u & 63, h = p >> 5, r = p & 31;
+    u32x4 v;
+    if (!kV) {
+      const int t32 = chunk / (d / 16), ds = chunk % (d / 16);
+      v = *reinterpret_cast<const u32x4*>(&tile[(32 * t32 + r) * ldq + 16 * ds + 8 * h]);
+    } else {
+      const int dt = chunk >> 2, ks = chunk & 3;
+      v = *reinterpret_cast<const u32x4*>(&tile[(32 * dt + r) * ldv + 16 * ks + 8 * h]);
+    }
+    xc[dst_blk + u] = v;
   }
 }
 
@@ -57,9 +84,12 @@ __global__ __launch_bounds__(kThreads) void unreorder_kernel(const u32x4* __rest
 
 }  // namespace
 
-hipError_t launch_reorder(const void* x, void* xc, const Geom& g, hipStream_t s) {
+hipError_t launch_reorder(const void* x, void* xc, int layout, const Geom& g, hipStream_t s) {
   dim3 grid(g.nblk, g.batch * g.heads);
-  reorder_kernel<<<grid, kThreads, 0, s>>>(static_cast<const u32x4*>(x), static_cast<u32x4*>(xc), g);
+  if (layout == 1)
+    reorder_kernel<true><<<grid, kThreads, 0, s>>>(static_cast<const u32x4*>(x), static_cast<u32x4*>(xc), g);
+  else
+    reorder_kernel<false><<<grid, kThreads, 0, s>>>(static_cast<const u32x4*>(x), static_cast<u32x4*>(xc), g);
   return hipGetLastError();
 }
 

@@ -29,6 +29,18 @@
  *   slots are never treated as tokens (pooling skips them, attention masks
  *   them as keys and writes O = 0, LSE = -inf for them as queries).  Pad slots
  *   must hold finite values (reorder writes zeros there).
+ * - Every cube-major tensor is [batch, heads, nblk, 64*head_dim] bf16: block
+ *   b of a head occupies 64*d contiguous elements.  Inside a block the
+ *   element order depends on the tensor (d = head_dim, s = slot, c = dim):
+ *     SA_LAYOUT_QK (queries, keys): element (s, c) is at
+ *        ((s/32)*(d/16) + c/16)*512 + ((c/8)%2)*256 + (s%32)*8 + c%8
+ *     SA_LAYOUT_V (values): element (s, c) is at
+ *        ((c/32)*4 + s/16)*512 + ((s/8)%2)*256 + (c%32)*8 + s%8
+ *     slot-major (attention output O): element (s, c) is at s*d + c
+ *   The first two are the operand order of the 32x32x16 bf16 matrix-core
+ *   instruction, so the attention kernel loads every operand as whole,
+ *   contiguous kilobytes.  sparse_attn_reorder writes them; nothing else in
+ *   the caller needs to know them.
  * - Return value: SA_OK (0) or a negative SA_ERR_* code.  On an argument error
  *   nothing is launched and no output is touched; sparse_attn_last_error()
  *   gives a message (per calling thread).  A failed launch returns
@@ -54,6 +66,9 @@
 #ifdef __cplusplus
 extern "C" {
 #endif
+
+/* Element order of a cube-major tensor written by sparse_attn_reorder. */
+enum { SA_LAYOUT_QK = 0, SA_LAYOUT_V = 1 };
 
 enum {
   SA_OK = 0,
@@ -94,14 +109,15 @@ int32_t sparse_attn_ceil_k(double k_frac, int32_t nblk);
 
 /* Cube re-indexing, [VSA] "Cube Partitioning and Token Re-Indexing"; [VSA2]
  * section 2.2 "Permutation".
- *   x  [batch, heads, N, head_dim] bf16, row-major tokens      (input)
- *   xc [batch, heads, n_pad, head_dim] bf16, cube-major        (output)
+ *   x      [batch, heads, N, head_dim] bf16, row-major tokens         (input)
+ *   xc     [batch, heads, n_pad, head_dim] bf16, cube-major           (output)
+ *   layout SA_LAYOUT_QK for queries and keys, SA_LAYOUT_V for values
  * Pad slots of xc are written with zeros.  x and xc must not overlap. */
-int32_t sparse_attn_reorder(const void* x, void* xc, const sa_geom* g,
-                            void* stream);
+int32_t sparse_attn_reorder(const void* x, void* xc, int32_t layout,
+                            const sa_geom* g, void* stream);
 
 /* Inverse re-indexing of the attention output (pad slots dropped).
- *   oc    [batch, heads, n_pad, head_dim] bf16   (input)
+ *   oc    [batch, heads, n_pad, head_dim] bf16, slot-major  (input)
  *   o     [batch, heads, N, head_dim] bf16       (output)
  *   lse_c [batch, heads, n_pad] float32          (input, may be NULL)
  *   lse   [batch, heads, N] float32              (output, NULL iff lse_c is)
@@ -111,8 +127,8 @@ int32_t sparse_attn_unreorder(const void* oc, void* o, const float* lse_c,
 
 /* Mean pooling of each block's real tokens, [SA2] "Block-Pooled Attention for
  * Efficient Mask Construction" step 2; [VSA] "The Coarse Stage".
- *   qc, kc     [batch, heads, n_pad, head_dim] bf16, cube-major  (inputs)
- *   qbar, kbar [batch, heads, nblk, head_dim] float64            (outputs)
+ *   qc, kc     [batch, heads, n_pad, head_dim] bf16, SA_LAYOUT_QK  (inputs)
+ *   qbar, kbar [batch, heads, nblk, head_dim] float64              (outputs)
  * Sums are taken in float64 (exact for bf16 inputs) and divided by the block's
  * real-token count. */
 int32_t sparse_attn_pool(const void* qc, const void* kc, double* qbar,
@@ -177,10 +193,11 @@ size_t sparse_attn_fwd_workspace_bytes(const sa_geom* g);
  * of the blocks lut[row][0 .. counts[row]-1]:
  *   O   = sum_j softmax_j(scale * q.k_j) v_j
  *   LSE = ln sum_j exp(scale * q.k_j)
- *   qc, kc, vc [batch, heads, n_pad, head_dim] bf16, cube-major   (inputs)
+ *   qc, kc     [batch, heads, n_pad, head_dim] bf16, SA_LAYOUT_QK  (inputs)
+ *   vc         [batch, heads, n_pad, head_dim] bf16, SA_LAYOUT_V   (input)
  *   lut, counts as written by sparse_attn_select; at most cap ids per row are
  *               read, ids outside [0, nblk) are skipped
- *   oc    [batch, heads, n_pad, head_dim] bf16                    (output)
+ *   oc    [batch, heads, n_pad, head_dim] bf16, slot-major        (output)
  *   lse_c [batch, heads, n_pad] float32, natural log              (output)
  * Rows with count 0 and pad query slots get O = 0, LSE = -inf.  Products run
  * in bf16 on the matrix cores with float32 accumulation and an online

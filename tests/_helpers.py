@@ -35,6 +35,30 @@ def to64(t: torch.Tensor) -> np.ndarray:
     return t.detach().to("cpu").double().numpy()
 
 
+def _block_offsets(d: int, v_layout: bool) -> np.ndarray:
+    """Element offset inside a 64 x d block of (slot s, dim c), flattened s*d+c,
+    for the library's documented QK and V block layouts."""
+    s = np.arange(64)[:, None]
+    c = np.arange(d)[None, :]
+    if v_layout:
+        off = ((c // 32) * 4 + s // 16) * 512 + ((s // 8) % 2) * 256 + (c % 32) * 8 + s % 8
+    else:
+        off = ((s // 32) * (d // 16) + c // 16) * 512 + ((c // 8) % 2) * 256 + (s % 32) * 8 + c % 8
+    return off.reshape(-1)
+
+
+def to_layout(xc: np.ndarray, v_layout: bool) -> np.ndarray:
+    """Slot-major cube-major [..., n_pad, d] -> the library's block layout
+    (same shape; a pure permutation inside each 64 x d block)."""
+    d = xc.shape[-1]
+    lead = xc.shape[:-2]
+    nblk = xc.shape[-2] // 64
+    blocks = xc.reshape(lead + (nblk, 64 * d))
+    out = np.empty_like(blocks)
+    out[..., _block_offsets(d, v_layout)] = blocks
+    return out.reshape(xc.shape)
+
+
 def row_is_valid(kept: np.ndarray, s_row: np.ndarray, kc: int, p: float) -> bool:
     """A kept list is acceptable at a near tie when it is sorted, unique, in
     range, holds at least kc blocks, reaches the mass p up to the near-tie

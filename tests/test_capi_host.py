@@ -76,7 +76,7 @@ def test_ceil_k_matches_worked_example_and_oracle():
 def test_bad_geometry_rejected(kw, code):
     g = geom(**kw)
     lib = sa.lib()
-    assert lib.sparse_attn_reorder(FAKE, FAKE, ctypes.byref(g), None) == code
+    assert lib.sparse_attn_reorder(FAKE, ctypes.c_void_p(0x200000), 0, ctypes.byref(g), None) == code
     assert sa.sparse_attn_last_error() != ""
     assert lib.sparse_attn_mask_workspace_bytes(ctypes.byref(g)) == 0
 
@@ -85,9 +85,10 @@ def test_null_and_misaligned_pointers_rejected():
     g = geom()
     lib = sa.lib()
     B = ctypes.byref(g)
-    assert lib.sparse_attn_reorder(None, FAKE, B, None) == sa.SA_ERR_INVALID_ARG
-    assert lib.sparse_attn_reorder(FAKE, FAKE, B, None) == sa.SA_ERR_INVALID_ARG   # overlap
-    assert lib.sparse_attn_reorder(FAKE_MISALIGNED, FAKE, B, None) == sa.SA_ERR_INVALID_ARG
+    assert lib.sparse_attn_reorder(None, FAKE, 0, B, None) == sa.SA_ERR_INVALID_ARG
+    assert lib.sparse_attn_reorder(FAKE, FAKE, 0, B, None) == sa.SA_ERR_INVALID_ARG   # overlap
+    assert lib.sparse_attn_reorder(FAKE_MISALIGNED, FAKE, 0, B, None) == sa.SA_ERR_INVALID_ARG
+    assert lib.sparse_attn_reorder(FAKE, ctypes.c_void_p(0x200000), 2, B, None) == sa.SA_ERR_INVALID_ARG
     assert lib.sparse_attn_unreorder(FAKE, FAKE, FAKE, None, B, None) == sa.SA_ERR_INVALID_ARG
     assert lib.sparse_attn_pool(FAKE, FAKE, None, FAKE, B, None) == sa.SA_ERR_INVALID_ARG
     assert lib.sparse_attn_block_scores(FAKE, FAKE, None, 0.0, B, None) == sa.SA_ERR_INVALID_ARG
@@ -136,6 +137,6 @@ def test_python_binding_rejects_non_contiguous():
     g = geom()
     x = torch.zeros(1, 2, 1024, 128, dtype=torch.bfloat16)[..., :64]
     with pytest.raises(ValueError):
-        sa.sparse_attn_reorder(x, x, g)
+        sa.sparse_attn_reorder(x, x, 0, g)
     with pytest.raises(TypeError):
-        sa.sparse_attn_reorder(torch.zeros(4, dtype=torch.float32), x, g)
+        sa.sparse_attn_reorder(torch.zeros(4, dtype=torch.float32), x, 0, g)

@@ -10,7 +10,13 @@ import block_sparse_attention_hybrid_amd as sa
 import oracle as O
 import synth
 from _helpers import (LSE_MAX_ABS, LSE_MEAN_ABS, O_MAX_ABS, O_MEAN_ABS, attn_errors,
-                      compare_lists, geom_of, lse_errors, ogeom_of, say, to64)
+                      compare_lists, geom_of, lse_errors, ogeom_of, say, to64, to_layout)
+
+QK, V = sa.SA_LAYOUT_QK, sa.SA_LAYOUT_V
+
+
+def reorder3(q, k, v, g):
+    return sa.reorder(q, g, QK), sa.reorder(k, g, QK), sa.reorder(v, g, V)
 
 pytestmark = pytest.mark.gpu
 
@@ -48,18 +54,27 @@ def case(request):
 
 def test_reorder_bit_exact(case):
     g, og = case["g"], case["og"]
-    for t, tref in (("qd", "ref_qc"), ("vd", "ref_vc")):
-        xc = sa.reorder(case[t], g)
+    for t, tref, layout in (("qd", "ref_qc", QK), ("kd", "ref_kc", QK), ("vd", "ref_vc", V)):
+        xc = sa.reorder(case[t], g, layout)
         torch.cuda.synchronize()
-        assert np.array_equal(to64(xc), case[tref])
-        o, _ = sa.unreorder(xc, None, g)
-        torch.cuda.synchronize()
-        assert torch.equal(o.cpu(), case[t].cpu())
+        assert np.array_equal(to64(xc), to_layout(case[tref], layout == V))
+
+
+def test_unreorder_bit_exact(case):
+    """Slot-major cube-major rows and LSE back to row-major tokens."""
+    g, og = case["g"], case["og"]
+    rng = np.random.default_rng(8)
+    oc = torch.from_numpy(case["ref_vc"]).to(torch.bfloat16)
+    lse_c = torch.from_numpy(rng.standard_normal(oc.shape[:-1]).astype(np.float32))
+    o, lse = sa.unreorder(oc.to(DEV), lse_c.to(DEV), g)
+    torch.cuda.synchronize()
+    assert torch.equal(o.cpu(), case["v"])
+    assert np.array_equal(lse.cpu().numpy(), O.unreorder_rows(lse_c.numpy(), og))
 
 
 def test_pool_and_scores_match_oracle(case):
     g, og = case["g"], case["og"]
-    qc, kc = sa.reorder(case["qd"], g), sa.reorder(case["kd"], g)
+    qc, kc = sa.reorder(case["qd"], g, QK), sa.reorder(case["kd"], g, QK)
     nblk = og.nblk
     B, H, d = g.batch, g.heads, g.head_dim
     qbar = torch.empty(B, H, nblk, d, dtype=torch.float64, device=DEV)
@@ -92,7 +107,7 @@ def test_select_on_oracle_scores(case):
 
 def test_build_mask_end_to_end(case):
     g, og, ref = case["g"], case["og"], case["ref_mask"]
-    qc, kc = sa.reorder(case["qd"], g), sa.reorder(case["kd"], g)
+    qc, kc = sa.reorder(case["qd"], g, QK), sa.reorder(case["kd"], g, QK)
     lut, counts = sa.build_mask(qc, kc, g, case["k_frac"], case["p"])
     torch.cuda.synchronize()
     bad, near, invalid = compare_lists(lut.cpu().numpy(), counts.cpu().numpy(), ref, case["p"])
@@ -101,7 +116,7 @@ def test_build_mask_end_to_end(case):
 
 def test_fwd_with_oracle_lists(case):
     g, og, ref = case["g"], case["og"], case["ref_mask"]
-    qc, kc, vc = (sa.reorder(case[t], g) for t in ("qd", "kd", "vd"))
+    qc, kc, vc = reorder3(case["qd"], case["kd"], case["vd"], g)
     lut = torch.from_numpy(ref.lut).to(DEV)
     counts = torch.from_numpy(ref.counts).to(DEV)
     oc, lse_c = sa.fwd(qc, kc, vc, lut, counts, g)
@@ -187,7 +202,7 @@ def test_row_budgets_and_variable_counts():
     budget = rng.integers(0, og.nblk + 3, size=(1, 3, og.nblk)).astype(np.int32)
     qc, kc = (O.reorder(to64(t), og) for t in (q, k))
     ref = O.build_mask(qc, kc, og, 0.0, 0.0, row_budget=np.clip(budget, 0, og.nblk))
-    qd, kd, vd = (sa.reorder(t.to(DEV), g) for t in (q, k, v))
+    qd, kd, vd = reorder3(q.to(DEV), k.to(DEV), v.to(DEV), g)
     lut, counts = sa.build_mask(qd, kd, g, 0.0, 0.0, row_budget=torch.from_numpy(budget).to(DEV))
     torch.cuda.synchronize()
     bad, _, invalid = compare_lists(lut.cpu().numpy(), counts.cpu().numpy(), ref, 0.0)
@@ -205,7 +220,7 @@ def test_row_budgets_and_variable_counts():
 def test_fwd_skips_out_of_range_ids_and_honours_cap():
     say("[edge lut sanitising]")
     wl, g, og, q, k, v = _small()
-    qd, kd, vd = (sa.reorder(t.to(DEV), g) for t in (q, k, v))
+    qd, kd, vd = reorder3(q.to(DEV), k.to(DEV), v.to(DEV), g)
     n = og.nblk
     cap = 4
     lut = torch.full((1, 2, n, cap), 0, dtype=torch.int32)
@@ -228,7 +243,7 @@ def test_fwd_skips_out_of_range_ids_and_honours_cap():
 def test_scale_argument():
     say("[edge scale]")
     wl, g, og, q, k, v = _small(grid=(4, 8, 8))
-    qd, kd, vd = (sa.reorder(t.to(DEV), g) for t in (q, k, v))
+    qd, kd, vd = reorder3(q.to(DEV), k.to(DEV), v.to(DEV), g)
     n = og.nblk
     lut = torch.arange(n, dtype=torch.int32).repeat(1, 2, n, 1).reshape(1, 2, n, n)
     counts = torch.full((1, 2, n), n, dtype=torch.int32)

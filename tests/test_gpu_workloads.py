@@ -1,0 +1,99 @@
+"""Parity at the full workload sizes, in the launch configuration the benchmark
+times: the whole path runs on the GPU for every head; the oracle recomputes
+sampled heads' kept-block lists in full and sampled query blocks' attention
+(with its own lists fed to the GPU attention), and properties that hold at any
+size are checked on every row."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_hybrid_amd as sa
+import oracle as O
+import synth
+from _helpers import (LSE_MAX_ABS, LSE_MEAN_ABS, O_MAX_ABS, O_MEAN_ABS, attn_errors,
+                      compare_lists, geom_of, lse_errors, ogeom_of, say, to64)
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+DEV = "cuda:0"
+
+# name, workload id, k_frac, p, row budgets, sampled heads
+CASES = [
+    ("480p", 1, 0.05, 0.9, False, (0, 1, 2)),
+    ("720p-literal", 2, 0.03, 0.85, False, (0, 1, 2)),
+    ("720p-hybrid95", 2, 0.03, 0.073, False, (0, 1, 2, 39)),
+    ("720p-extreme", 3, 0.02, 0.8, False, (0, 7, 20, 22)),
+    ("720p-varbudget", 4, 0.0, 0.0, True, (0, 1, 2)),
+]
+
+
+@pytest.mark.parametrize("name,wid,k_frac,p,budgets,heads", CASES, ids=[c[0] for c in CASES])
+def test_workload(name, wid, k_frac, p, budgets, heads):
+    wl = synth.WORKLOADS[wid]
+    say(f"[workload {name}] H={wl.heads} d={wl.head_dim} grid={wl.grid} k={k_frac} p={p}")
+    g, og = geom_of(wl), ogeom_of(wl)
+    n = og.nblk
+    q, k, v = synth.make_qkv(wl, 0)
+    rb_np = synth.row_budgets(wl, 0) if budgets else None
+    rb = torch.from_numpy(rb_np).to(DEV) if budgets else None
+    qc = sa.reorder(q.to(DEV), g, sa.SA_LAYOUT_QK)
+    kc = sa.reorder(k.to(DEV), g, sa.SA_LAYOUT_QK)
+    vc = sa.reorder(v.to(DEV), g, sa.SA_LAYOUT_V)
+    lut, counts = sa.build_mask(qc, kc, g, k_frac, p, row_budget=rb)
+    oc, lse_c = sa.fwd(qc, kc, vc, lut, counts, g)
+    torch.cuda.synchronize()
+    say("  gpu path done")
+
+    # --- properties on every row --------------------------------------------
+    counts_h = counts.cpu().numpy()
+    kc_all = rb_np if budgets else np.full_like(counts_h, O.ceil_k(k_frac, n))
+    assert np.all(counts_h >= np.minimum(kc_all, n)) and np.all(counts_h <= n)
+    if budgets:
+        assert np.array_equal(counts_h, np.clip(rb_np, 0, n))
+    lut_h = lut.cpu().numpy()
+    pos = np.arange(n)[None, None, None, :]
+    live = pos < counts_h[..., None]
+    ids = np.where(live, lut_h, -1)
+    assert np.all(ids[live] >= 0) and np.all(ids[live] < n)
+    inc = np.diff(np.where(live, lut_h, n + pos), axis=-1)
+    assert np.all(inc > 0), "kept ids must be strictly ascending"
+    real = O.real_slots(og)
+    lse_h = lse_c.cpu().numpy()
+    assert np.all(np.isfinite(lse_h[..., real])) and np.all(np.isneginf(lse_h[..., ~real]))
+    assert bool(torch.isfinite(oc).all())
+    density = counts_h.sum() / (counts_h.size * n)
+    say(f"  density {density:.4f} (block sparsity {1 - density:.4f})")
+
+    # --- oracle on sampled heads ----------------------------------------------
+    sel = list(heads)
+    qs, ks, vs = (O.reorder(to64(t[:, sel]), og) for t in (q, k, v))
+    ref = O.build_mask(qs, ks, og, k_frac, p, row_budget=None if not budgets else rb_np[:, sel])
+    bad, near, invalid = compare_lists(lut_h[:, sel], counts_h[:, sel], ref, p)
+    say(f"  lists: {len(bad)} mismatches outside near ties, {near} near ties, {len(invalid)} invalid")
+    assert not bad and not invalid
+
+    # oracle lists fed to the GPU attention, on the sampled heads at full shape
+    gs = sa.make_geom(wl.batch, len(sel), wl.frames, wl.height, wl.width, wl.head_dim)
+    qcs, kcs, vcs = (x[:, sel].contiguous() for x in (qc, kc, vc))
+    ocs, lses = sa.fwd(qcs, kcs, vcs, torch.from_numpy(ref.lut).to(DEV),
+                       torch.from_numpy(ref.counts).to(DEV), gs)
+    torch.cuda.synchronize()
+    ocs_h, lses_h = to64(ocs), lses.cpu().double().numpy()
+    rng = np.random.default_rng(1)
+    rows = sorted(set([0, 1, n // 2, n - 1] + list(rng.integers(0, n, 4))))
+    worst = [0.0, 0.0, 0.0, 0.0]
+    for hi in range(len(sel)):
+        for i in rows:
+            kept = ref.lut[0, hi, i, :ref.counts[0, hi, i]]
+            o_ref, l_ref = O.attention_block(qs[0, hi], ks[0, hi], vs[0, hi], kept, og, i)
+            mx, mean = attn_errors(ocs_h[0, hi, i * 64:(i + 1) * 64], o_ref)
+            lmx, lmean = lse_errors(lses_h[0, hi, i * 64:(i + 1) * 64], l_ref)
+            worst = [max(worst[0], mx), max(worst[1], mean), max(worst[2], lmx), max(worst[3], lmean)]
+            assert mx <= O_MAX_ABS and mean <= O_MEAN_ABS, (sel[hi], i, mx, mean)
+            assert lmx <= LSE_MAX_ABS and lmean <= LSE_MEAN_ABS, (sel[hi], i, lmx, lmean)
+            # where the lists agree, the main run's output is the same computation
+            if counts_h[0, sel[hi], i] == kept.size and np.array_equal(lut_h[0, sel[hi], i, :kept.size], kept):
+                main = to64(oc[0, sel[hi], i * 64:(i + 1) * 64])
+                assert np.array_equal(main, ocs_h[0, hi, i * 64:(i + 1) * 64])
+    say(f"  attention: O max {worst[0]:.2e} mean {worst[1]:.2e}; LSE max {worst[2]:.2e} mean {worst[3]:.2e}")
