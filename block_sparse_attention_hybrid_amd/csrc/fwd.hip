@@ -19,8 +19,8 @@
 // a lane's 8 probabilities belong to 8 consecutive keys -- exactly the 8 keys
 // the V layout stores in that lane's 16-byte chunk.  P therefore never leaves
 // registers, and every K and V operand is one fully coalesced 1 KB wave load
-// (the QK and V block layouts of sa_layout.h).  The 16 KB of Q operands sit in
-// LDS for the whole row.
+// (the QK and V block layouts of sa_layout.h).  Only the 16 KB of Q operands
+// sit in LDS, read back once per block.
 //
 // Software pipeline: the next block's K tile is requested as soon as the
 // current S^T is computed and its V tile as soon as the current O update is
@@ -32,6 +32,8 @@
 #include "sa_launch.h"
 
 #include <math.h>
+
+#include <type_traits>
 
 namespace sa {
 
@@ -52,6 +54,44 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
+#ifndef SA_XCD_GROUP
+#define SA_XCD_GROUP 4
+#endif
+// Workgroups are dispatched round-robin over the 8 XCDs (XCD = w % 8).  The
+// XCDs form 8/G groups of G; group `grp` takes the contiguous row range
+// [grp*range, (grp+1)*range).  The range is cut into chunks of c = nblk/G
+// query blocks (one G-th of a head) dealt round-robin to the G XCDs of the
+// group, each XCD sweeping its chunks in order: G XCDs work on the same head
+// at once, each on neighbouring query blocks.
+struct RowMap {
+  int rows;     // batch * heads * nblk
+  int range;    // rows per XCD group
+  int chunk;    // rows per chunk
+  int per_xcd;  // workgroups per XCD
+};
+
+__host__ __device__ inline RowMap make_rowmap(int nblk, int heads_total) {
+  RowMap m;
+  m.rows = nblk * heads_total;
+  const int ranges = kXcds / SA_XCD_GROUP;
+  m.range = (m.rows + ranges - 1) / ranges;
+  m.chunk = (nblk + SA_XCD_GROUP - 1) / SA_XCD_GROUP;
+  const int chunks = (m.range + m.chunk - 1) / m.chunk;
+  m.per_xcd = (chunks + SA_XCD_GROUP - 1) / SA_XCD_GROUP * m.chunk;
+  return m;
+}
+
+// Row of workgroup w, or -1 if w has no row.
+__device__ __forceinline__ int row_of_workgroup(int w, const RowMap& m) {
+  const int x = w % kXcds, k = w / kXcds;
+  const int grp = x / SA_XCD_GROUP, sub = x % SA_XCD_GROUP;
+  const int q = k / m.chunk, o = k - q * m.chunk;
+  const long long in_range = ((long long)q * SA_XCD_GROUP + sub) * m.chunk + o;
+  const long long row = (long long)grp * m.range + in_range;
+  if (in_range >= m.range || row >= m.rows) return -1;
+  return (int)row;
+}
+
 template <int D>
 __global__ __launch_bounds__(64) void fwd_kernel(const u32x4* __restrict__ qc,
                                                  const u32x4* __restrict__ kc,
@@ -59,7 +99,7 @@ __global__ __launch_bounds__(64) void fwd_kernel(const u32x4* __restrict__ qc,
                                                  const int32_t* __restrict__ lut,
                                                  const int32_t* __restrict__ counts, int cap, Geom g,
                                                  float sc_log2, bf16* __restrict__ oc,
-                                                 float* __restrict__ lse_c, int rows, int per_xcd) {
+                                                 float* __restrict__ lse_c, RowMap map) {
   constexpr int NDS = D / 16;     // 16-dim steps of S^T
   constexpr int NDT = D / 32;     // 32-dim tiles of O^T
   constexpr int BLK = 64 * D / 8; // 16-byte units per block
@@ -67,9 +107,8 @@ __global__ __launch_bounds__(64) void fwd_kernel(const u32x4* __restrict__ qc,
   // workgroups are dispatched round-robin over the 8 XCDs; give each XCD a
   // contiguous run of rows so neighbouring query blocks (overlapping lists)
   // share K/V tiles in that XCD's L2
-  const int w = blockIdx.x;
-  const int row = (w % kXcds) * per_xcd + w / kXcds;
-  if (row >= rows) return;
+  const int row = row_of_workgroup(blockIdx.x, map);
+  if (row < 0) return;
   const long long bh = row / g.nblk;
   const int i = row - (int)(bh * g.nblk);
 
@@ -84,8 +123,9 @@ __global__ __launch_bounds__(64) void fwd_kernel(const u32x4* __restrict__ qc,
   const u32x4* kh = kc + head;
   const u32x4* vh = vc + head;
 
-  // Q^T operand chunks live in LDS (each lane reads back its own 16 bytes, so
-  // the reads are conflict-free); registers are kept for K, V, S, P and O
+  // Q^T operand chunks, kept in LDS for the whole row (each lane reads back
+  // its own 16 bytes, so the reads are conflict-free); the registers go to
+  // K, V, S, P and the output accumulator
   __shared__ u32x4 qlds[2 * NDS * 64];
 #pragma unroll
   for (int c = 0; c < 2 * NDS; ++c) qlds[c * 64 + lane] = qb[c * 64 + lane];
@@ -124,102 +164,182 @@ __global__ __launch_bounds__(64) void fwd_kernel(const u32x4* __restrict__ qc,
       for (int ks = 0; ks < 4; ++ks) vreg[dt][ks] = vb[(dt * 4 + ks) * 64 + lane];
   };
 
+  // ---- stages of one block, for one 32-query half qt ---------------------
+  // S^T = K Q^T, one MFMA per step (16 steps: ds = step / 2, kt = step % 2);
+  // q holds the Q^T chunk of this step's ds
+  auto gemm1_step = [&](f32x16 (&st)[2], const u32x4& q, int step) {
+    const int ds = step >> 1, kt = step & 1;
+    st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kreg[kt][ds]), as_bf16x8(q), st[kt], 0, 0, 0);
+  };
+  auto qchunk = [&](int qt, int ds) { return qlds[(qt * NDS + ds) * 64 + lane]; };
+  // the whole S^T half in one region (the scheduler places the LDS reads)
+  auto gemm1_half = [&](int qt, f32x16 (&st)[2]) {
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) {
+      const u32x4 q = qchunk(qt, ds);
+      gemm1_step(st, q, 2 * ds);
+      gemm1_step(st, q, 2 * ds + 1);
+    }
+  };
+  auto zero = [](f32x16 (&st)[2]) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) st[kt][e] = 0.f;
+  };
+  // Register e of tile kt holds key 32 kt + 16 (e / 8) + 8 hf + e % 8, i.e.
+  // bit 16 kt + e of the lane's key mask.  Pad keys of a partial block get
+  // S = -inf (so P = 0 and they never set the max); the asm pins the mask
+  // arithmetic inside the wave-uniform branch that calls this.
+  auto mask_st = [](f32x16 (&st)[2], uint32_t lm) {
+    asm volatile("" : "+v"(lm));
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) st[kt][e] = ((lm >> (16 * kt + e)) & 1u) ? st[kt][e] : -INFINITY;
+  };
+  // one register pair of P = exp2(scale S - m) (bf16-packed) and its sum
+  auto exp_pair = [&](const f32x16 (&st)[2], uint32_t (&pw)[2][8], float nmu, float& ls, int step) {
+    const int kt = step >> 3, e = 2 * (step & 7);
+    const float p0 = __builtin_amdgcn_exp2f(fmaf(st[kt][e], sc_log2, nmu));
+    const float p1 = __builtin_amdgcn_exp2f(fmaf(st[kt][e + 1], sc_log2, nmu));
+    ls += p0 + p1;
+    pw[kt][e >> 1] = pack_bf16x2(p0, p1);
+  };
+  // row max of one half (raw scores; the scale is positive)
+  auto half_max = [&](const f32x16 (&st)[2]) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, st[kt][e]);
+    // the two half-waves hold the two halves of every query's keys
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+    return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * sc_log2;
+  };
+  // O^T += V^T P^T, one MFMA per step (16 steps: ks = step / NDT, dt =
+  // step % NDT at d = 128); k-step ks covers keys 16 ks .. +15 = registers
+  // 8 (ks % 2) .. +7 of tile ks / 2
+  auto gemm2_step = [&](int qt, const uint32_t (&pw)[2][8], int step) {
+    const int ks = step / NDT, dt = step % NDT;
+    const int kt = ks >> 1, o4 = 4 * (ks & 1);
+    const u32x4 bw = {pw[kt][o4], pw[kt][o4 + 1], pw[kt][o4 + 2], pw[kt][o4 + 3]};
+    acc[dt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vreg[dt][ks]), as_bf16x8(bw), acc[dt][qt],
+                                                          0, 0, 0);
+  };
+  auto lane_mask = [&](uint64_t real) -> uint32_t {
+    // this lane's 32 key bits: byte (kt, g) = keys 32 kt + 16 g + 8 hf .. +7
+    return (uint32_t)((real >> (8 * hf)) & 0xffu) | ((uint32_t)((real >> (16 + 8 * hf)) & 0xffu) << 8) |
+           ((uint32_t)((real >> (32 + 8 * hf)) & 0xffu) << 16) |
+           ((uint32_t)((real >> (48 + 8 * hf)) & 0xffu) << 24);
+  };
+  // empty asm "uses": keep a stage's results computed in its own region (the
+  // compiler would otherwise sink the softmax past the next branch and lose
+  // the overlap with the matrix cores)
+  auto pin = [](const uint32_t (&pw)[2][8]) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) asm volatile("" ::"v"(pw[kt][e]));
+  };
+  // The reference max m only moves up when a block's max exceeds it by more
+  // than 2^8 (base 2), so the exponentials of a half are computed with the
+  // current m right away and checked afterwards; the rare half that raises m
+  // (always the first block) is redone with the new m after rescaling its
+  // accumulator.  The final O / l does not depend on m.
+  auto settle = [&](int qt, const f32x16 (&st)[2], uint32_t (&pw)[2][8], float& ls, float mx) {
+    const bool grow = mx > m[qt] + kStaleMax;
+    if (__any(grow)) {
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m[qt] - mx) : 1.f;
+      if (grow) m[qt] = mx;
+      l[qt] *= alpha;
+#pragma unroll
+      for (int t = 0; t < NDT; ++t)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[t][qt][e] *= alpha;
+      const float nmu = m[qt] == -INFINITY ? 0.f : -m[qt];
+      ls = 0.f;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) exp_pair(st, pw, nmu, ls, k);
+    }
+    l[qt] += ls;
+  };
+  auto neg_m = [&](int qt) { return m[qt] == -INFINITY ? 0.f : -m[qt]; };
+  constexpr int G1 = 2 * NDS;       // MFMA steps of S^T for one half
+  constexpr int G2 = 4 * NDT;       // MFMA steps of O^T for one half
+
+  // Software pipeline over the kept blocks, per block t (halves 0 and 1):
+  //   S^T(t,1) with exp(t,0) | settle(t,0) | O += (t,0) with exp(t,1) |
+  //   settle(t,1) | O += (t,1) and S^T(t+1,0)
+  // The exp steps are written between the MFMA steps and fenced with
+  // scheduling barriers, so the vector units work through one half's softmax
+  // while the matrix cores run the other half's product.  K(t+1) is requested
+  // once S^T(t,1) is issued, V(t+1) once O(t,1) is.  Pad keys are masked
+  // between the stages, in wave-uniform branches that full blocks skip.
+  f32x16 stA[2], stB[2];
+  uint32_t pA[2][8], pB[2][8];
   int j_cur = count > 0 ? lrow[0] : 0;
+  uint64_t real = 0;
   if (count > 0) {
     load_k(j_cur);
     load_v(j_cur);
+    real = real_mask(j_cur);
+    zero(stA);
+    gemm1_half(0, stA);
+    if (real != ~0ull) mask_st(stA, lane_mask(real));
   }
   for (int it = 0; it < count; ++it) {
-    const int j_next = (it + 1 < count) ? lrow[it + 1] : 0;
-    const uint64_t real = real_mask(j_cur);
+    // past the last block the "next" block is the current one again: the
+    // pipeline then does one redundant S^T half and reload instead of
+    // branching, which keeps each stage one straight-line region
+    const int j_next = lrow[it + 1 < count ? it + 1 : it];
     const bool full = real == ~0ull;   // wave-uniform: most blocks have no pad slot
-    // this lane's 32 key bits: byte (kt, g) = keys 32 kt + 16 g + 8 hf .. +7
-    const uint32_t lmask = (uint32_t)((real >> (8 * hf)) & 0xffu) |
-                           ((uint32_t)((real >> (16 + 8 * hf)) & 0xffu) << 8) |
-                           ((uint32_t)((real >> (32 + 8 * hf)) & 0xffu) << 16) |
-                           ((uint32_t)((real >> (48 + 8 * hf)) & 0xffu) << 24);
-
-    // the two 32-query halves are processed one after the other: S^T and P of
-    // one half are live at a time, and the softmax of one half can overlap
-    // the matrix-core work of the other
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      // S^T tiles of this query half (kt: keys 0-31 / 32-63)
-      f32x16 st[2];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) st[kt][e] = 0.f;
-#pragma unroll
-      for (int ds = 0; ds < NDS; ++ds) {
-        const u32x4 qv = qlds[(qt * NDS + ds) * 64 + lane];
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-          st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kreg[kt][ds]), as_bf16x8(qv), st[kt],
-                                                           0, 0, 0);
-      }
-      if (qt == 1 && it + 1 < count) load_k(j_next);
-      __builtin_amdgcn_sched_barrier(0);
-
-      // online softmax in the base-2 domain; register e of tile kt holds key
-      // 32 kt + 16 (e / 8) + 8 hf + e % 8, i.e. bit 16 kt + e of lmask.  The
-      // scale is positive, so the max is taken on the raw scores and the scale
-      // folds into the exponent's fma.
-      float mx = -INFINITY;
-      if (full) {
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, st[kt][e]);
-      } else {
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, ((lmask >> (16 * kt + e)) & 1u) ? st[kt][e] : -INFINITY);
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sc_log2;
-      const bool grow = mx > m[qt] + kStaleMax;
-      if (__any(grow)) {
-        const float alpha = grow ? __builtin_amdgcn_exp2f(m[qt] - mx) : 1.f;
-        l[qt] *= alpha;
-#pragma unroll
-        for (int t = 0; t < NDT; ++t)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) acc[t][qt][e] *= alpha;
-      }
-      if (grow) m[qt] = mx;
-      const float nmu = m[qt] == -INFINITY ? 0.f : -m[qt];
-      uint32_t pw[2][8];
+    {
+      const float nmu = neg_m(0);
       float ls = 0.f;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int e = 0; e < 16; e += 2) {
-          float p0 = __builtin_amdgcn_exp2f(fmaf(st[kt][e], sc_log2, nmu));
-          float p1 = __builtin_amdgcn_exp2f(fmaf(st[kt][e + 1], sc_log2, nmu));
-          if (!full) {
-            p0 = ((lmask >> (16 * kt + e)) & 1u) ? p0 : 0.f;
-            p1 = ((lmask >> (16 * kt + e + 1)) & 1u) ? p1 : 0.f;
-          }
-          ls += p0 + p1;
-          pw[kt][e >> 1] = pack_bf16x2(p0, p1);
-        }
-      l[qt] += ls;
+      zero(stB);
+      // Q^T chunks are read two dim-steps ahead of their MFMAs
+      u32x4 qa = qchunk(1, 0), qn = qchunk(1, 1);
       __builtin_amdgcn_sched_barrier(0);
-
-      // O^T += V^T P^T; k-step ks covers keys 16 ks .. +15 = registers
-      // 8 (ks % 2) .. +7 of tile ks / 2
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int kt = ks >> 1, o4 = 4 * (ks & 1);
-        const u32x4 bw = {pw[kt][o4], pw[kt][o4 + 1], pw[kt][o4 + 2], pw[kt][o4 + 3]};
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-          acc[dt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vreg[dt][ks]), as_bf16x8(bw),
-                                                                acc[dt][qt], 0, 0, 0);
+      for (int k = 0; k < 16; ++k) {
+        if (k < G1) {
+          gemm1_step(stB, qa, k);
+          if (k & 1) {
+            qa = qn;
+            if ((k >> 1) + 2 < NDS) qn = qchunk(1, (k >> 1) + 2);
+          }
+        }
+        exp_pair(stA, pA, nmu, ls, k);
+        __builtin_amdgcn_sched_barrier(0);
       }
+      const float mx = half_max(stA);
+      pin(pA);
+      load_k(j_next);
+      settle(0, stA, pA, ls, mx);
     }
-    if (it + 1 < count) load_v(j_next);
+    if (!full) mask_st(stB, lane_mask(real));
+    {
+      const float nmu = neg_m(1);
+      float ls = 0.f;
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        if (k < G2) gemm2_step(0, pA, k);
+        exp_pair(stB, pB, nmu, ls, k);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const float mx = half_max(stB);
+      pin(pB);
+      settle(1, stB, pB, ls, mx);
+    }
+#pragma unroll
+    for (int k = 0; k < G2; ++k) gemm2_step(1, pB, k);
+    real = real_mask(j_next);
+    zero(stA);
+    gemm1_half(0, stA);
+    load_v(j_next);
+    if (real != ~0ull) mask_st(stA, lane_mask(real));
     j_cur = j_next;
   }
 
@@ -253,19 +373,18 @@ size_t fwd_workspace_bytes(const Geom&) { return 0; }
 hipError_t launch_fwd(const void* qc, const void* kc, const void* vc, const int32_t* lut,
                       const int32_t* counts, int cap, const Geom& g, float scale, void* oc,
                       float* lse_c, void*, hipStream_t s) {
-  const long long rows = (long long)g.batch * g.heads * g.nblk;
-  const int per_xcd = (int)((rows + kXcds - 1) / kXcds);
+  const RowMap map = make_rowmap(g.nblk, g.batch * g.heads);
   const float sc_log2 = scale * 1.4426950408889634f;
-  const dim3 grid((unsigned)(per_xcd * kXcds));
+  const dim3 grid((unsigned)((long long)map.per_xcd * kXcds));
   const u32x4* q = static_cast<const u32x4*>(qc);
   const u32x4* k = static_cast<const u32x4*>(kc);
   const u32x4* v = static_cast<const u32x4*>(vc);
   if (g.d == 128)
     fwd_kernel<128><<<grid, 64, 0, s>>>(q, k, v, lut, counts, cap, g, sc_log2, static_cast<bf16*>(oc), lse_c,
-                                        (int)rows, per_xcd);
+                                        map);
   else
     fwd_kernel<64><<<grid, 64, 0, s>>>(q, k, v, lut, counts, cap, g, sc_log2, static_cast<bf16*>(oc), lse_c,
-                                       (int)rows, per_xcd);
+                                       map);
   return hipGetLastError();
 }
 
