@@ -17,6 +17,7 @@ kept query-block/key-block pair) / step time.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -34,6 +35,12 @@ import synth  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
+
+# HBM-side traffic of the forward kernel, measured by rocprofv3 counters and
+# recorded with a hash of the sources it was measured on
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kernels_720p-hybrid95_hbm_traffic.txt")
+FWD_SOURCES = ("block_sparse_attention_hybrid_amd/csrc/fwd.hip", "block_sparse_attention_hybrid_amd/csrc/sa_device.h",
+               "block_sparse_attention_hybrid_amd/csrc/sa_launch.h", "block_sparse_attention_hybrid_amd/build.py")
 
 # name -> (synthetic workload id, k_frac, p, row budgets?)
 WORKLOADS = {
@@ -109,6 +116,30 @@ class Path:
     def step(self):
         for _, fn in self.stages():
             fn()
+
+
+def fwd_source_hash():
+    h = hashlib.sha256()
+    for rel in FWD_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload):
+    """Bytes per forward launch from the committed counter summary, or None when
+    it was taken on another workload or on different kernel sources."""
+    if workload != "720p-hybrid95" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            parts = line.split()
+            if len(parts) == 2 and parts[0] in ("traffic_bytes_per_launch", "fwd_source_sha256"):
+                vals[parts[0]] = parts[1]
+    if vals.get("fwd_source_sha256") != fwd_source_hash() or "traffic_bytes_per_launch" not in vals:
+        return None
+    return int(float(vals["traffic_bytes_per_launch"]))
 
 
 def algorithmic_bytes(path):
@@ -274,7 +305,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": recorded_traffic(args.workload),
         },
     }
     if not args.no_cpu_baseline:
