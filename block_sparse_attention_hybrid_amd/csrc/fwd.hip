@@ -19,16 +19,21 @@
 // a lane's 8 probabilities belong to 8 consecutive keys -- exactly the 8 keys
 // the V layout stores in that lane's 16-byte chunk.  P therefore never leaves
 // registers, and every K and V operand is one fully coalesced 1 KB wave load
-// (the QK and V block layouts of sa_layout.h).  Only the 16 KB of Q operands
-// sit in LDS, read back once per block.
+// (the QK and V block layouts of sa_layout.h).  The 16 KB of Q operands stay
+// in registers for the whole row, so the loop touches no LDS at all.
 //
 // Software pipeline: the next block's K tile is requested as soon as the
 // current S^T is computed and its V tile as soon as the current O update is
-// issued, so each load has a GEMM plus a softmax of lead time.  The running
-// max is only raised when a block's max exceeds it by more than 2^8 (in the
-// base-2 exponent), which leaves the result exact (the final O/l ratio does
-// not depend on the reference max) and skips almost every rescale of the
-// 128-register output accumulator.
+// issued, so each load has a GEMM plus a softmax of lead time.
+//
+// Online softmax without a per-block row max: the exponentials of a block are
+// taken against the running reference m at once, and only when a lane's sum
+// over its 32 probabilities of a half exceeds 2^8 (so some probability could
+// be large) or m is still unset is the exact block max taken, m raised, the
+// accumulator rescaled and the probabilities redone.  The final O / l does
+// not depend on m, so the result is the same; every probability that reaches
+// the products is at most 2^8, and the rare slow path replaces a max over 64
+// scores per block.
 #include "sa_launch.h"
 
 #include <math.h>
@@ -41,7 +46,7 @@ namespace {
 
 constexpr int kXcds = 8;
 constexpr float kLn2 = 0.69314718055994531f;
-constexpr float kStaleMax = 8.f;  // allowed growth of the base-2 exponent before a rescale
+constexpr float kSumLimit = 256.f;  // a lane's block sum above this triggers an exact-max rescale
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -92,6 +97,28 @@ __device__ __forceinline__ int row_of_workgroup(int w, const RowMap& m) {
   return (int)row;
 }
 
+// Division by a run-time constant d (1 <= d < 2^24) for n < 2^24 with one
+// high multiply, an add and a shift (round-up multiplier method).
+struct FastDiv {
+  uint32_t m, l;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+  uint32_t l = 0;
+  while ((1u << l) < d) ++l;
+  FastDiv f;
+  f.m = (uint32_t)(((1ull << 32) * ((1ull << l) - d)) / d + 1);
+  f.l = l;
+  return f;
+}
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) { return (__umulhi(n, f.m) + n) >> f.l; }
+
+// block index -> cube coordinates: divisions by nw and nh
+struct CubeDiv {
+  FastDiv w, h;
+};
+
 template <int D>
 __global__ __launch_bounds__(64) void fwd_kernel(const u32x4* __restrict__ qc,
                                                  const u32x4* __restrict__ kc,
@@ -99,7 +126,7 @@ __global__ __launch_bounds__(64) void fwd_kernel(const u32x4* __restrict__ qc,
                                                  const int32_t* __restrict__ lut,
                                                  const int32_t* __restrict__ counts, int cap, Geom g,
                                                  float sc_log2, bf16* __restrict__ oc,
-                                                 float* __restrict__ lse_c, RowMap map) {
+                                                 float* __restrict__ lse_c, RowMap map, CubeDiv cd) {
   constexpr int NDS = D / 16;     // 16-dim steps of S^T
   constexpr int NDT = D / 32;     // 32-dim tiles of O^T
   constexpr int BLK = 64 * D / 8; // 16-byte units per block
@@ -123,13 +150,10 @@ __global__ __launch_bounds__(64) void fwd_kernel(const u32x4* __restrict__ qc,
   const u32x4* kh = kc + head;
   const u32x4* vh = vc + head;
 
-  // Q^T operand chunks, kept in LDS for the whole row (each lane reads back
-  // its own 16 bytes, so the reads are conflict-free); the registers go to
-  // K, V, S, P and the output accumulator
-  __shared__ u32x4 qlds[2 * NDS * 64];
+  // Q^T operand chunks, in registers for the whole row
+  u32x4 qreg[2 * NDS];
 #pragma unroll
-  for (int c = 0; c < 2 * NDS; ++c) qlds[c * 64 + lane] = qb[c * 64 + lane];
-  __syncthreads();
+  for (int c = 0; c < 2 * NDS; ++c) qreg[c] = qb[c * 64 + lane];
 
   int count = counts[row];
   count = count < 0 ? 0 : (count > cap ? cap : count);
@@ -148,7 +172,23 @@ __global__ __launch_bounds__(64) void fwd_kernel(const u32x4* __restrict__ qc,
   u32x4 vreg[NDT][4];
   auto valid_id = [&](int j) { return j >= 0 && j < g.nblk; };
   // bit s set iff slot s of block j holds a real token (one slot per lane)
-  auto real_mask = [&](int j) -> uint64_t { return ballot(valid_id(j) && slot_token(g, j, lane) >= 0); };
+  // slot offsets of this lane's key slot, fixed for the whole row
+  int lt, lh, lw;
+  slot_offsets(g, lane, lt, lh, lw);
+  // bit s set iff slot s of block j holds a real token; the cube coordinates
+  // are uniform (scalar unit), only partial cubes need a per-lane test
+  auto real_mask = [&](int j) -> uint64_t {
+    if (!valid_id(j)) return 0ull;
+    const uint32_t r = fdiv((uint32_t)j, cd.w);
+    const int bw = j - (int)r * g.nw;
+    const int bt = (int)fdiv(r, cd.h);
+    const int bh = (int)r - bt * g.nh;
+    const int rt = min(g.ct, g.frames - bt * g.ct);
+    const int rh = min(g.ch, g.height - bh * g.ch);
+    const int rw = min(g.cw, g.width - bw * g.cw);
+    if (rt == g.ct && rh == g.ch && rw == g.cw) return ~0ull;
+    return ballot(lt < rt && lh < rh && lw < rw);
+  };
   auto load_k = [&](int j) {
     const u32x4* kb = kh + (long long)(valid_id(j) ? j : 0) * BLK;
 #pragma unroll
@@ -171,7 +211,7 @@ __global__ __launch_bounds__(64) void fwd_kernel(const u32x4* __restrict__ qc,
     const int ds = step >> 1, kt = step & 1;
     st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kreg[kt][ds]), as_bf16x8(q), st[kt], 0, 0, 0);
   };
-  auto qchunk = [&](int qt, int ds) { return qlds[(qt * NDS + ds) * 64 + lane]; };
+  auto qchunk = [&](int qt, int ds) { return qreg[qt * NDS + ds]; };
   // the whole S^T half in one region (the scheduler places the LDS reads)
   auto gemm1_half = [&](int qt, f32x16 (&st)[2]) {
 #pragma unroll
@@ -242,16 +282,17 @@ __global__ __launch_bounds__(64) void fwd_kernel(const u32x4* __restrict__ qc,
 #pragma unroll
       for (int e = 0; e < 8; ++e) asm volatile("" ::"v"(pw[kt][e]));
   };
-  // The reference max m only moves up when a block's max exceeds it by more
-  // than 2^8 (base 2), so the exponentials of a half are computed with the
-  // current m right away and checked afterwards; the rare half that raises m
-  // (always the first block) is redone with the new m after rescaling its
-  // accumulator.  The final O / l does not depend on m.
-  auto settle = [&](int qt, const f32x16 (&st)[2], uint32_t (&pw)[2][8], float& ls, float mx) {
-    const bool grow = mx > m[qt] + kStaleMax;
-    if (__any(grow)) {
-      const float alpha = grow ? __builtin_amdgcn_exp2f(m[qt] - mx) : 1.f;
-      if (grow) m[qt] = mx;
+  // The exponentials of a half are computed with the current m right away and
+  // checked afterwards through their sum; the rare half whose sum exceeds the
+  // limit, or that finds m unset (always the first block), takes the exact
+  // max, raises m, rescales the accumulator and is redone with the new m.
+  auto settle = [&](int qt, const f32x16 (&st)[2], uint32_t (&pw)[2][8], float& ls) {
+    const bool trig = !(ls <= kSumLimit) || m[qt] == -INFINITY;
+    if (__any(trig)) {
+      const float mx = half_max(st);
+      const float mn = fmaxf(m[qt], mx);
+      const float alpha = (m[qt] == -INFINITY || mn == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[qt] - mn);
+      m[qt] = mn;
       l[qt] *= alpha;
 #pragma unroll
       for (int t = 0; t < NDT; ++t)
@@ -288,11 +329,14 @@ __global__ __launch_bounds__(64) void fwd_kernel(const u32x4* __restrict__ qc,
     gemm1_half(0, stA);
     if (real != ~0ull) mask_st(stA, lane_mask(real));
   }
+  // the list entry of the next block is read one iteration ahead
+  int j_ahead = count > 1 ? lrow[1] : j_cur;
   for (int it = 0; it < count; ++it) {
     // past the last block the "next" block is the current one again: the
     // pipeline then does one redundant S^T half and reload instead of
     // branching, which keeps each stage one straight-line region
-    const int j_next = lrow[it + 1 < count ? it + 1 : it];
+    const int j_next = j_ahead;
+    j_ahead = lrow[it + 2 < count ? it + 2 : count - 1];
     const bool full = real == ~0ull;   // wave-uniform: most blocks have no pad slot
     {
       const float nmu = neg_m(0);
@@ -313,10 +357,9 @@ __global__ __launch_bounds__(64) void fwd_kernel(const u32x4* __restrict__ qc,
         exp_pair(stA, pA, nmu, ls, k);
         __builtin_amdgcn_sched_barrier(0);
       }
-      const float mx = half_max(stA);
       pin(pA);
       load_k(j_next);
-      settle(0, stA, pA, ls, mx);
+      settle(0, stA, pA, ls);
     }
     if (!full) mask_st(stB, lane_mask(real));
     {
@@ -329,9 +372,8 @@ __global__ __launch_bounds__(64) void fwd_kernel(const u32x4* __restrict__ qc,
         exp_pair(stB, pB, nmu, ls, k);
         __builtin_amdgcn_sched_barrier(0);
       }
-      const float mx = half_max(stB);
       pin(pB);
-      settle(1, stB, pB, ls, mx);
+      settle(1, stB, pB, ls);
     }
 #pragma unroll
     for (int k = 0; k < G2; ++k) gemm2_step(1, pB, k);
@@ -374,6 +416,7 @@ hipError_t launch_fwd(const void* qc, const void* kc, const void* vc, const int3
                       const int32_t* counts, int cap, const Geom& g, float scale, void* oc,
                       float* lse_c, void*, hipStream_t s) {
   const RowMap map = make_rowmap(g.nblk, g.batch * g.heads);
+  const CubeDiv cd = {make_fastdiv((uint32_t)g.nw), make_fastdiv((uint32_t)g.nh)};
   const float sc_log2 = scale * 1.4426950408889634f;
   const dim3 grid((unsigned)((long long)map.per_xcd * kXcds));
   const u32x4* q = static_cast<const u32x4*>(qc);
@@ -381,10 +424,10 @@ hipError_t launch_fwd(const void* qc, const void* kc, const void* vc, const int3
   const u32x4* v = static_cast<const u32x4*>(vc);
   if (g.d == 128)
     fwd_kernel<128><<<grid, 64, 0, s>>>(q, k, v, lut, counts, cap, g, sc_log2, static_cast<bf16*>(oc), lse_c,
-                                        map);
+                                        map, cd);
   else
     fwd_kernel<64><<<grid, 64, 0, s>>>(q, k, v, lut, counts, cap, g, sc_log2, static_cast<bf16*>(oc), lse_c,
-                                       map);
+                                       map, cd);
   return hipGetLastError();
 }
 
