@@ -2,9 +2,9 @@
 """Throughput of the hybrid block-sparse attention hot path on one MI355X.
 
 One step = the whole path on one batch of resident synthetic input:
-reorder Q, K, V -> pool -> float64 block scores -> hybrid selection ->
-block-sparse forward -> unreorder O and LSE, all HIP kernels of
-libsparse_attn.so called through the C ABI.
+reorder Q and K (pooling them on the way) and V -> float64 block scores ->
+hybrid selection -> block-sparse forward -> unreorder O and LSE, all HIP
+kernels of libsparse_attn.so called through the C ABI.
 
 Headline workload: Wan2.1-14B-720p-shaped attention, B=1, H=40, d=128, latent
 grid 21x45x80 (75,600 tokens, 1,440 cubes of 4x4x4), Top-k 3% (the pages'
@@ -92,7 +92,8 @@ class Path:
         self.cap = n
         self.lut = torch.empty((B, H, n, n), dtype=torch.int32, device=dev)
         self.counts = torch.empty((B, H, n), dtype=torch.int32, device=dev)
-        self.ws = sa.mask_workspace(self.g, dev)
+        self.qbar, self.kbar = (torch.empty((B, H, n, d), dtype=torch.float64, device=dev) for _ in range(2))
+        self.scores = torch.empty((B, H, n, n), dtype=torch.float64, device=dev)
         self.rb = None
         if budgets:
             self.rb = torch.from_numpy(synth.row_budgets(wl, 0)).to(dev)
@@ -102,12 +103,12 @@ class Path:
     def stages(self):
         g = self.g
         return [
-            ("reorder", lambda: [sa.sparse_attn_reorder(x, xc, lay, g) for x, xc, lay in
-                                 ((self.q, self.qc, sa.SA_LAYOUT_QK), (self.k, self.kc, sa.SA_LAYOUT_QK),
-                                  (self.v, self.vc, sa.SA_LAYOUT_V))]),
-            ("build_mask", lambda: sa.sparse_attn_build_mask(self.qc, self.kc, g, 64, self.k_frac, self.p,
-                                                             self.rb, self.lut, self.counts, self.cap,
-                                                             self.ws)),
+            ("reorder", lambda: (sa.sparse_attn_reorder_pool(self.q, self.qc, self.qbar, g),
+                                 sa.sparse_attn_reorder_pool(self.k, self.kc, self.kbar, g),
+                                 sa.sparse_attn_reorder(self.v, self.vc, sa.SA_LAYOUT_V, g))),
+            ("mask", lambda: (sa.sparse_attn_block_scores(self.qbar, self.kbar, self.scores, 0.0, g),
+                              sa.sparse_attn_select(self.scores, g, self.k_frac, self.p, self.rb, self.lut,
+                                                    self.counts, self.cap))),
             ("fwd", lambda: sa.sparse_attn_fwd(self.qc, self.kc, self.vc, self.lut, self.counts, self.cap,
                                                g, 0.0, self.oc, self.lse_c, self.fws)),
             ("unreorder", lambda: sa.sparse_attn_unreorder(self.oc, self.o, self.lse_c, self.lse, g)),
@@ -150,11 +151,11 @@ def algorithmic_bytes(path):
     tok = 2 * d                                        # bf16 row bytes
     kept = int(path.counts.sum().item())
     return {
-        "reorder": 3 * B * H * (real + pad) * tok,
-        "build_mask": (B * H * (2 * pad * tok                 # read Q, K
-                                + 2 * n * d * 8 * 2           # Qbar, Kbar write + read
-                                + n * n * 8 * 2               # scores write + read
-                                + n * 4) + kept * 4),         # counts + kept ids
+        "reorder": B * H * (3 * (real + pad) * tok            # Q, K, V read and written
+                            + 2 * n * d * 8),                 # Qbar, Kbar written
+        "mask": (B * H * (2 * n * d * 8                       # Qbar, Kbar read
+                          + n * n * 8 * 2                     # scores written and read
+                          + n * 4) + kept * 4),               # counts + kept ids
         "unreorder": B * H * (real + pad) * (tok + 4),
     }
 
@@ -260,8 +261,8 @@ def main():
     fwd_tflops = flops_kept / (stage_ms["fwd"] * 1e-3) / 1e12
     abytes = algorithmic_bytes(path)
     gbps = {n: abytes[n] / (stage_ms[n] * 1e-3) / 1e9 for n in abytes}
-    mask_path_gbps = (abytes["reorder"] + abytes["build_mask"]) / (
-        (stage_ms["reorder"] + stage_ms["build_mask"]) * 1e-3) / 1e9
+    mask_path_gbps = (abytes["reorder"] + abytes["mask"]) / (
+        (stage_ms["reorder"] + stage_ms["mask"]) * 1e-3) / 1e9
 
     if args.copy_calibration:
         x = torch.empty(1 << 30, dtype=torch.uint8, device=dev)

@@ -32,7 +32,7 @@ SA_LAYOUT_V = 1
 
 EXPORTED = (
     "sparse_attn_geometry", "sparse_attn_ceil_k", "sparse_attn_reorder",
-    "sparse_attn_unreorder", "sparse_attn_pool", "sparse_attn_block_scores",
+    "sparse_attn_reorder_pool", "sparse_attn_unreorder", "sparse_attn_pool", "sparse_attn_block_scores",
     "sparse_attn_select", "sparse_attn_mask_workspace_bytes",
     "sparse_attn_build_mask", "sparse_attn_fwd_workspace_bytes", "sparse_attn_fwd",
     "sparse_attn_last_error",
@@ -71,6 +71,7 @@ _SIGS = {
     "sparse_attn_geometry": (_i32, [_GP, ctypes.POINTER(_i32), ctypes.POINTER(_i64), ctypes.POINTER(_i64)]),
     "sparse_attn_ceil_k": (_i32, [_f64, _i32]),
     "sparse_attn_reorder": (_i32, [_vp, _vp, _i32, _GP, _vp]),
+    "sparse_attn_reorder_pool": (_i32, [_vp, _vp, _vp, _GP, _vp]),
     "sparse_attn_unreorder": (_i32, [_vp, _vp, _vp, _vp, _GP, _vp]),
     "sparse_attn_pool": (_i32, [_vp, _vp, _vp, _vp, _GP, _vp]),
     "sparse_attn_block_scores": (_i32, [_vp, _vp, _vp, _f64, _GP, _vp]),
@@ -146,6 +147,12 @@ def sparse_attn_ceil_k(k_frac: float, nblk: int) -> int:
 def sparse_attn_reorder(x, xc, layout: int, g: Geom, stream=None) -> None:
     _check(lib().sparse_attn_reorder(_ptr(x, torch.bfloat16, "x"), _ptr(xc, torch.bfloat16, "xc"),
                                      int(layout), ctypes.byref(g), _stream(stream, x)))
+
+
+def sparse_attn_reorder_pool(x, xc, xbar, g: Geom, stream=None) -> None:
+    _check(lib().sparse_attn_reorder_pool(_ptr(x, torch.bfloat16, "x"), _ptr(xc, torch.bfloat16, "xc"),
+                                          _ptr(xbar, torch.float64, "xbar"), ctypes.byref(g),
+                                          _stream(stream, x)))
 
 
 def sparse_attn_unreorder(oc, o, lse_c, lse, g: Geom, stream=None) -> None:
@@ -224,6 +231,30 @@ def reorder(x: torch.Tensor, g: Geom, layout: int = SA_LAYOUT_QK, stream=None) -
     return xc
 
 
+def reorder_pool(x: torch.Tensor, g: Geom, stream=None):
+    """Cube-major copy in the QK layout and the float64 block means."""
+    nblk, n_real, n_pad = sparse_attn_geometry(g)
+    xc = _empty((g.batch, g.heads, n_pad, g.head_dim), torch.bfloat16, x)
+    xbar = _empty((g.batch, g.heads, nblk, g.head_dim), torch.float64, x)
+    sparse_attn_reorder_pool(x, xc, xbar, g, stream)
+    return xc, xbar
+
+
+def mask_from_pooled(qbar, kbar, g: Geom, k_frac: float, p: float, row_budget=None, cap=None,
+                     scores=None, stream=None):
+    """Pooled block scores and hybrid selection from block means (the rest of
+    build_mask once reorder_pool has pooled).  Returns (lut, counts)."""
+    nblk, _, _ = sparse_attn_geometry(g)
+    cap = nblk if cap is None else cap
+    if scores is None:
+        scores = _empty((g.batch, g.heads, nblk, nblk), torch.float64, qbar)
+    lut = _empty((g.batch, g.heads, nblk, cap), torch.int32, qbar)
+    counts = _empty((g.batch, g.heads, nblk), torch.int32, qbar)
+    sparse_attn_block_scores(qbar, kbar, scores, 0.0, g, stream)
+    sparse_attn_select(scores, g, k_frac, p, row_budget, lut, counts, cap, stream)
+    return lut, counts
+
+
 def unreorder(oc: torch.Tensor, lse_c: Optional[torch.Tensor], g: Geom, stream=None):
     nblk, n_real, n_pad = sparse_attn_geometry(g)
     o = _empty((g.batch, g.heads, n_real, g.head_dim), torch.bfloat16, oc)
@@ -261,12 +292,13 @@ def fwd(qc, kc, vc, lut, counts, g: Geom, scale: float = 0.0, stream=None):
 
 
 def attention(q, k, v, g: Geom, k_frac: float, p: float, row_budget=None, stream=None):
-    """Whole path on row-major tokens: reorder, build the hybrid mask, sparse
-    forward, unreorder.  Returns (O [B,H,N,d] bf16, LSE [B,H,N] fp32, lut, counts)."""
-    qc = reorder(q, g, SA_LAYOUT_QK, stream)
-    kc = reorder(k, g, SA_LAYOUT_QK, stream)
+    """Whole path on row-major tokens: reorder (pooling Q and K on the way),
+    pooled scores and hybrid selection, sparse forward, unreorder.
+    Returns (O [B,H,N,d] bf16, LSE [B,H,N] fp32, lut, counts)."""
+    qc, qbar = reorder_pool(q, g, stream)
+    kc, kbar = reorder_pool(k, g, stream)
     vc = reorder(v, g, SA_LAYOUT_V, stream)
-    lut, counts = build_mask(qc, kc, g, k_frac, p, row_budget, stream=stream)
+    lut, counts = mask_from_pooled(qbar, kbar, g, k_frac, p, row_budget, stream=stream)
     oc, lse_c = fwd(qc, kc, vc, lut, counts, g, stream=stream)
     o, lse = unreorder(oc, lse_c, g, stream)
     return o, lse, lut, counts

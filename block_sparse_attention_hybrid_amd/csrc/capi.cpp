@@ -152,6 +152,16 @@ int32_t sparse_attn_reorder(const void* x, void* xc, int32_t layout, const sa_ge
   return hip_status(sa::launch_reorder(x, xc, layout, d, (hipStream_t)stream), "reorder launch");
 }
 
+int32_t sparse_attn_reorder_pool(const void* x, void* xc, double* xbar, const sa_geom* g, void* stream) {
+  sa::Geom d;
+  SA_TRY(make_geom(g, d));
+  SA_TRY(check_ptr(x, 16, "x"));
+  SA_TRY(check_ptr(xc, 16, "xc"));
+  SA_TRY(check_ptr(xbar, 8, "xbar"));
+  if (x == xc) return fail(SA_ERR_INVALID_ARG, "x and xc must not overlap");
+  return hip_status(sa::launch_reorder_pool(x, xc, xbar, d, (hipStream_t)stream), "reorder_pool launch");
+}
+
 int32_t sparse_attn_unreorder(const void* oc, void* o, const float* lse_c, float* lse,
                               const sa_geom* g, void* stream) {
   sa::Geom d;

@@ -11,6 +11,13 @@
 // sa_layout.h), so both the reads and the writes are whole-row / whole-chunk
 // and the traffic is the algorithmic minimum: N rows read, n_pad rows written.
 // Pad slots are written as zeros.
+//
+// The fused form for queries and keys also takes the block's mean over its
+// real tokens (SpargeAttention2 summary page, "Block-Pooled Attention for
+// Efficient Mask Construction", step 2) from the tile while it sits in LDS, so
+// pooling costs no second pass over Q and K.  The sums are float64 (exact for
+// bf16 inputs) divided by the real-token count, the same values as the
+// separate pooling kernel.
 #include "sa_launch.h"
 #include "sa_layout.h"
 
@@ -20,20 +27,29 @@ namespace {
 
 constexpr int kThreads = 256;
 
-template <bool kV>
+// Row-major token index of every slot of block i (-1 for pad slots), in LDS.
+__device__ __forceinline__ void fill_slot_table(const Geom& g, int i, long long* tab) {
+  if (threadIdx.x < kBlock) tab[threadIdx.x] = slot_token(g, i, threadIdx.x);
+  __syncthreads();
+}
+
+template <bool kV, bool kPool>
 __global__ __launch_bounds__(kThreads) void reorder_kernel(const u32x4* __restrict__ x,
-                                                           u32x4* __restrict__ xc, Geom g) {
+                                                           u32x4* __restrict__ xc,
+                                                           double* __restrict__ xbar, Geom g) {
   // QK: tile[s][c] (row pitch d+8); V: tile[c][s] (row pitch 72)
   __shared__ __attribute__((aligned(16))) uint16_t tile[128 * 72];
+  __shared__ long long tok[kBlock];
   const int i = blockIdx.x;
   const long long bh = blockIdx.y;
   const int d = g.d, cpr = d / 8;
   const int ldq = d + 8, ldv = 72;
   const long long src_head = bh * g.n_real * cpr;
   const long long dst_blk = (bh * g.n_pad + (long long)i * kBlock) * cpr;
+  fill_slot_table(g, i, tok);
   for (int idx = threadIdx.x; idx < kBlock * cpr; idx += kThreads) {
     const int s = idx / cpr, c8 = idx - s * cpr;
-    const long long n = slot_token(g, i, s);
+    const long long n = tok[s];
     u32x4 v = {0u, 0u, 0u, 0u};
     if (n >= 0) v = x[src_head + n * cpr + c8];
     if (!kV) {
@@ -59,6 +75,23 @@ __global__ __launch_bounds__(kThreads) void reorder_kernel(const u32x4* __restri
     }
     xc[dst_blk + u] = v;
   }
+  if (kPool) {
+    // per = kThreads / d threads share a dim, each summing 64 / per slots
+    // (pad slots hold zeros); partial sums meet in LDS in a fixed order
+    __shared__ double part[kThreads];
+    const int per = kThreads / d, c = threadIdx.x % d, grp = threadIdx.x / d;
+    const int ns = kBlock / per;
+    double acc = 0.0;
+    for (int s = grp * ns; s < (grp + 1) * ns; ++s)
+      acc += (double)__uint_as_float((uint32_t)tile[s * ldq + c] << 16);
+    part[threadIdx.x] = acc;
+    __syncthreads();
+    if (threadIdx.x < d) {
+      double sum = 0.0;
+      for (int q = 0; q < per; ++q) sum += part[q * d + c];
+      xbar[(bh * g.nblk + i) * (long long)d + c] = sum / (double)block_real_count(g, i);
+    }
+  }
 }
 
 __global__ __launch_bounds__(kThreads) void unreorder_kernel(const u32x4* __restrict__ oc,
@@ -67,17 +100,19 @@ __global__ __launch_bounds__(kThreads) void unreorder_kernel(const u32x4* __rest
                                                              float* __restrict__ lse, Geom g) {
   const int i = blockIdx.x;
   const long long bh = blockIdx.y;
+  __shared__ long long tok[kBlock];
   const int cpr = g.d / 8;
   const long long dst_head = bh * g.n_real * cpr;
   const long long src_blk = (bh * g.n_pad + (long long)i * kBlock) * cpr;
+  fill_slot_table(g, i, tok);
   for (int idx = threadIdx.x; idx < kBlock * cpr; idx += kThreads) {
     const int s = idx / cpr, c = idx - s * cpr;
-    const long long n = slot_token(g, i, s);
+    const long long n = tok[s];
     if (n >= 0) o[dst_head + n * cpr + c] = oc[src_blk + idx];
   }
   if (lse_c != nullptr && threadIdx.x < kBlock) {
     const int s = threadIdx.x;
-    const long long n = slot_token(g, i, s);
+    const long long n = tok[s];
     if (n >= 0) lse[bh * g.n_real + n] = lse_c[bh * g.n_pad + (long long)i * kBlock + s];
   }
 }
@@ -86,10 +121,19 @@ __global__ __launch_bounds__(kThreads) void unreorder_kernel(const u32x4* __rest
 
 hipError_t launch_reorder(const void* x, void* xc, int layout, const Geom& g, hipStream_t s) {
   dim3 grid(g.nblk, g.batch * g.heads);
+  const u32x4* src = static_cast<const u32x4*>(x);
+  u32x4* dst = static_cast<u32x4*>(xc);
   if (layout == 1)
-    reorder_kernel<true><<<grid, kThreads, 0, s>>>(static_cast<const u32x4*>(x), static_cast<u32x4*>(xc), g);
+    reorder_kernel<true, false><<<grid, kThreads, 0, s>>>(src, dst, nullptr, g);
   else
-    reorder_kernel<false><<<grid, kThreads, 0, s>>>(static_cast<const u32x4*>(x), static_cast<u32x4*>(xc), g);
+    reorder_kernel<false, false><<<grid, kThreads, 0, s>>>(src, dst, nullptr, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_reorder_pool(const void* x, void* xc, double* xbar, const Geom& g, hipStream_t s) {
+  dim3 grid(g.nblk, g.batch * g.heads);
+  reorder_kernel<false, true><<<grid, kThreads, 0, s>>>(static_cast<const u32x4*>(x), static_cast<u32x4*>(xc),
+                                                         xbar, g);
   return hipGetLastError();
 }
 

@@ -10,6 +10,7 @@
 namespace sa {
 
 hipError_t launch_reorder(const void* x, void* xc, int layout, const Geom& g, hipStream_t s);
+hipError_t launch_reorder_pool(const void* x, void* xc, double* xbar, const Geom& g, hipStream_t s);
 hipError_t launch_unreorder(const void* oc, void* o, const float* lse_c, float* lse,
                             const Geom& g, hipStream_t s);
 hipError_t launch_pool(const void* qc, const void* kc, double* qbar, double* kbar,

@@ -116,6 +116,17 @@ int32_t sparse_attn_ceil_k(double k_frac, int32_t nblk);
 int32_t sparse_attn_reorder(const void* x, void* xc, int32_t layout,
                             const sa_geom* g, void* stream);
 
+/* sparse_attn_reorder with SA_LAYOUT_QK, fused with the block means of
+ * sparse_attn_pool: [VSA] "Cube Partitioning and Token Re-Indexing"; [SA2]
+ * "Block-Pooled Attention for Efficient Mask Construction" step 2.
+ *   x     [batch, heads, N, head_dim] bf16, row-major tokens          (input)
+ *   xc    [batch, heads, n_pad, head_dim] bf16, SA_LAYOUT_QK          (output)
+ *   xbar  [batch, heads, nblk, head_dim] float64 block means          (output)
+ * xc is bit-identical to sparse_attn_reorder's and xbar to sparse_attn_pool's
+ * output for the same tokens; pooling then costs no second read of xc. */
+int32_t sparse_attn_reorder_pool(const void* x, void* xc, double* xbar,
+                                 const sa_geom* g, void* stream);
+
 /* Inverse re-indexing of the attention output (pad slots dropped).
  *   oc    [batch, heads, n_pad, head_dim] bf16, slot-major  (input)
  *   o     [batch, heads, N, head_dim] bf16       (output)

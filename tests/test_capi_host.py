@@ -89,6 +89,10 @@ def test_null_and_misaligned_pointers_rejected():
     assert lib.sparse_attn_reorder(FAKE, FAKE, 0, B, None) == sa.SA_ERR_INVALID_ARG   # overlap
     assert lib.sparse_attn_reorder(FAKE_MISALIGNED, FAKE, 0, B, None) == sa.SA_ERR_INVALID_ARG
     assert lib.sparse_attn_reorder(FAKE, ctypes.c_void_p(0x200000), 2, B, None) == sa.SA_ERR_INVALID_ARG
+    assert lib.sparse_attn_reorder_pool(FAKE, ctypes.c_void_p(0x200000), None, B, None) == sa.SA_ERR_INVALID_ARG
+    assert lib.sparse_attn_reorder_pool(FAKE, FAKE, ctypes.c_void_p(0x300000), B, None) == sa.SA_ERR_INVALID_ARG
+    assert lib.sparse_attn_reorder_pool(FAKE, ctypes.c_void_p(0x200000), ctypes.c_void_p(0x300004), B,
+                                        None) == sa.SA_ERR_INVALID_ARG   # xbar misaligned
     assert lib.sparse_attn_unreorder(FAKE, FAKE, FAKE, None, B, None) == sa.SA_ERR_INVALID_ARG
     assert lib.sparse_attn_pool(FAKE, FAKE, None, FAKE, B, None) == sa.SA_ERR_INVALID_ARG
     assert lib.sparse_attn_block_scores(FAKE, FAKE, None, 0.0, B, None) == sa.SA_ERR_INVALID_ARG

@@ -12,13 +12,13 @@ import synth
 from _helpers import (LSE_MAX_ABS, LSE_MEAN_ABS, O_MAX_ABS, O_MEAN_ABS, attn_errors,
                       compare_lists, geom_of, lse_errors, ogeom_of, say, to64, to_layout)
 
+pytestmark = pytest.mark.gpu
+
 QK, V = sa.SA_LAYOUT_QK, sa.SA_LAYOUT_V
 
 
 def reorder3(q, k, v, g):
     return sa.reorder(q, g, QK), sa.reorder(k, g, QK), sa.reorder(v, g, V)
-
-pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
 
@@ -89,6 +89,31 @@ def test_pool_and_scores_match_oracle(case):
     np.testing.assert_array_equal(kbar.cpu().numpy(), ref.kbar)
     np.testing.assert_allclose(s.cpu().numpy(), ref.scores, rtol=1e-13,
                                atol=1e-14 * np.abs(ref.scores).max())
+
+
+def test_reorder_pool_fused(case):
+    """The fused reorder + pooling: the same cube-major bytes as reorder and
+    the same (exact) block means as the oracle."""
+    g, ref = case["g"], case["ref_mask"]
+    for t, tref, want in (("qd", "ref_qc", ref.qbar), ("kd", "ref_kc", ref.kbar)):
+        xc, xbar = sa.reorder_pool(case[t], g)
+        torch.cuda.synchronize()
+        assert np.array_equal(to64(xc), to_layout(case[tref], False))
+        np.testing.assert_array_equal(xbar.cpu().numpy(), want)
+
+
+def test_mask_from_pooled_matches_build_mask(case):
+    g, ref = case["g"], case["ref_mask"]
+    qc, qbar = sa.reorder_pool(case["qd"], g)
+    kc, kbar = sa.reorder_pool(case["kd"], g)
+    lut, counts = sa.mask_from_pooled(qbar, kbar, g, case["k_frac"], case["p"])
+    lut2, counts2 = sa.build_mask(qc, kc, g, case["k_frac"], case["p"])
+    torch.cuda.synchronize()
+    assert torch.equal(counts, counts2)
+    c = counts.cpu().numpy()
+    a, b = lut.cpu().numpy(), lut2.cpu().numpy()
+    for idx in np.ndindex(c.shape):
+        assert np.array_equal(a[idx][:c[idx]], b[idx][:c[idx]])
 
 
 def test_select_on_oracle_scores(case):
