@@ -178,16 +178,17 @@ __global__ __launch_bounds__(64) void fwd_kernel(const u32x4* __restrict__ qc,
   // bit s set iff slot s of block j holds a real token; the cube coordinates
   // are uniform (scalar unit), only partial cubes need a per-lane test
   auto real_mask = [&](int j) -> uint64_t {
-    if (!valid_id(j)) return 0ull;
-    const uint32_t r = fdiv((uint32_t)j, cd.w);
-    const int bw = j - (int)r * g.nw;
+    const bool ok = valid_id(j);
+    const uint32_t jj = ok ? (uint32_t)j : 0u;
+    const uint32_t r = fdiv(jj, cd.w);
+    const int bw = (int)jj - (int)r * g.nw;
     const int bt = (int)fdiv(r, cd.h);
     const int bh = (int)r - bt * g.nh;
     const int rt = min(g.ct, g.frames - bt * g.ct);
     const int rh = min(g.ch, g.height - bh * g.ch);
     const int rw = min(g.cw, g.width - bw * g.cw);
-    if (rt == g.ct && rh == g.ch && rw == g.cw) return ~0ull;
-    return ballot(lt < rt && lh < rh && lw < rw);
+    const uint64_t b = ballot(lt < rt && lh < rh && lw < rw);
+    return ok ? b : 0ull;
   };
   auto load_k = [&](int j) {
     const u32x4* kb = kh + (long long)(valid_id(j) ? j : 0) * BLK;
@@ -204,6 +205,14 @@ __global__ __launch_bounds__(64) void fwd_kernel(const u32x4* __restrict__ qc,
       for (int ks = 0; ks < 4; ++ks) vreg[dt][ks] = vb[(dt * 4 + ks) * 64 + lane];
   };
 
+  auto lane_mask = [&](uint64_t real) -> uint32_t {
+    // this lane's 32 key bits: byte (kt, g) = keys 32 kt + 16 g + 8 hf .. +7
+    return (uint32_t)((real >> (8 * hf)) & 0xffu) | ((uint32_t)((real >> (16 + 8 * hf)) & 0xffu) << 8) |
+           ((uint32_t)((real >> (32 + 8 * hf)) & 0xffu) << 16) |
+           ((uint32_t)((real >> (48 + 8 * hf)) & 0xffu) << 24);
+  };  constexpr int G1 = 2 * NDS;       // MFMA steps of S^T for one half
+  constexpr int G2 = 4 * NDT;       // MFMA steps of O^T for one half
+
   // ---- stages of one block, for one 32-query half qt ---------------------
   // S^T = K Q^T, one MFMA per step (16 steps: ds = step / 2, kt = step % 2);
   // q holds the Q^T chunk of this step's ds
@@ -212,31 +221,35 @@ __global__ __launch_bounds__(64) void fwd_kernel(const u32x4* __restrict__ qc,
     st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kreg[kt][ds]), as_bf16x8(q), st[kt], 0, 0, 0);
   };
   auto qchunk = [&](int qt, int ds) { return qreg[qt * NDS + ds]; };
-  // the whole S^T half in one region (the scheduler places the LDS reads)
-  auto gemm1_half = [&](int qt, f32x16 (&st)[2]) {
-#pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) {
-      const u32x4 q = qchunk(qt, ds);
-      gemm1_step(st, q, 2 * ds);
-      gemm1_step(st, q, 2 * ds + 1);
-    }
-  };
-  auto zero = [](f32x16 (&st)[2]) {
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) st[kt][e] = 0.f;
-  };
   // Register e of tile kt holds key 32 kt + 16 (e / 8) + 8 hf + e % 8, i.e.
   // bit 16 kt + e of the lane's key mask.  Pad keys of a partial block get
-  // S = -inf (so P = 0 and they never set the max); the asm pins the mask
-  // arithmetic inside the wave-uniform branch that calls this.
-  auto mask_st = [](f32x16 (&st)[2], uint32_t lm) {
-    asm volatile("" : "+v"(lm));
+  // S = -inf (so P = 0 and they never set the max) by starting their
+  // accumulators at -inf instead of 0: the first MFMA of each tile reads the
+  // start value, so a full block (wave-uniform branch) keeps the free zero
+  // operand and a partial one pays 32 selects that wait on nothing.
+  auto gemm1_first = [&](f32x16 (&st)[2], const u32x4& q, uint64_t real) {
+    if (real == ~0ull) {
+      const f32x16 z = {};
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < 2; ++kt)
+        st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kreg[kt][0]), as_bf16x8(q), z, 0, 0, 0);
+    } else {
+      uint32_t lm = lane_mask(real);
+      asm volatile("" : "+v"(lm));
 #pragma unroll
-      for (int e = 0; e < 16; ++e) st[kt][e] = ((lm >> (16 * kt + e)) & 1u) ? st[kt][e] : -INFINITY;
+      for (int kt = 0; kt < 2; ++kt) {
+        f32x16 init;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) init[e] = ((lm >> (16 * kt + e)) & 1u) ? 0.f : -INFINITY;
+        st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kreg[kt][0]), as_bf16x8(q), init, 0, 0, 0);
+      }
+    }
+  };
+  // the whole S^T half in one region
+  auto gemm1_half = [&](int qt, f32x16 (&st)[2], uint64_t real) {
+    gemm1_first(st, qchunk(qt, 0), real);
+#pragma unroll
+    for (int k = 2; k < G1; ++k) gemm1_step(st, qchunk(qt, k >> 1), k);
   };
   // one register pair of P = exp2(scale S - m) (bf16-packed) and its sum
   auto exp_pair = [&](const f32x16 (&st)[2], uint32_t (&pw)[2][8], float nmu, float& ls, int step) {
@@ -267,12 +280,7 @@ __global__ __launch_bounds__(64) void fwd_kernel(const u32x4* __restrict__ qc,
     acc[dt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vreg[dt][ks]), as_bf16x8(bw), acc[dt][qt],
                                                           0, 0, 0);
   };
-  auto lane_mask = [&](uint64_t real) -> uint32_t {
-    // this lane's 32 key bits: byte (kt, g) = keys 32 kt + 16 g + 8 hf .. +7
-    return (uint32_t)((real >> (8 * hf)) & 0xffu) | ((uint32_t)((real >> (16 + 8 * hf)) & 0xffu) << 8) |
-           ((uint32_t)((real >> (32 + 8 * hf)) & 0xffu) << 16) |
-           ((uint32_t)((real >> (48 + 8 * hf)) & 0xffu) << 24);
-  };
+
   // empty asm "uses": keep a stage's results computed in its own region (the
   // compiler would otherwise sink the softmax past the next branch and lose
   // the overlap with the matrix cores)
@@ -306,17 +314,13 @@ __global__ __launch_bounds__(64) void fwd_kernel(const u32x4* __restrict__ qc,
     l[qt] += ls;
   };
   auto neg_m = [&](int qt) { return m[qt] == -INFINITY ? 0.f : -m[qt]; };
-  constexpr int G1 = 2 * NDS;       // MFMA steps of S^T for one half
-  constexpr int G2 = 4 * NDT;       // MFMA steps of O^T for one half
-
   // Software pipeline over the kept blocks, per block t (halves 0 and 1):
   //   S^T(t,1) with exp(t,0) | settle(t,0) | O += (t,0) with exp(t,1) |
   //   settle(t,1) | O += (t,1) and S^T(t+1,0)
   // The exp steps are written between the MFMA steps and fenced with
   // scheduling barriers, so the vector units work through one half's softmax
   // while the matrix cores run the other half's product.  K(t+1) is requested
-  // once S^T(t,1) is issued, V(t+1) once O(t,1) is.  Pad keys are masked
-  // between the stages, in wave-uniform branches that full blocks skip.
+  // once S^T(t,1) is issued, V(t+1) once O(t,1) is.
   f32x16 stA[2], stB[2];
   uint32_t pA[2][8], pB[2][8];
   int j_cur = count > 0 ? lrow[0] : 0;
@@ -325,9 +329,7 @@ __global__ __launch_bounds__(64) void fwd_kernel(const u32x4* __restrict__ qc,
     load_k(j_cur);
     load_v(j_cur);
     real = real_mask(j_cur);
-    zero(stA);
-    gemm1_half(0, stA);
-    if (real != ~0ull) mask_st(stA, lane_mask(real));
+    gemm1_half(0, stA, real);
   }
   // the list entry of the next block is read one iteration ahead
   int j_ahead = count > 1 ? lrow[1] : j_cur;
@@ -337,23 +339,15 @@ __global__ __launch_bounds__(64) void fwd_kernel(const u32x4* __restrict__ qc,
     // branching, which keeps each stage one straight-line region
     const int j_next = j_ahead;
     j_ahead = lrow[it + 2 < count ? it + 2 : count - 1];
-    const bool full = real == ~0ull;   // wave-uniform: most blocks have no pad slot
+    uint64_t real_next;
     {
       const float nmu = neg_m(0);
       float ls = 0.f;
-      zero(stB);
-      // Q^T chunks are read two dim-steps ahead of their MFMAs
-      u32x4 qa = qchunk(1, 0), qn = qchunk(1, 1);
+      gemm1_first(stB, qchunk(1, 0), real);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
-        if (k < G1) {
-          gemm1_step(stB, qa, k);
-          if (k & 1) {
-            qa = qn;
-            if ((k >> 1) + 2 < NDS) qn = qchunk(1, (k >> 1) + 2);
-          }
-        }
+        if (k + 2 < G1) gemm1_step(stB, qchunk(1, (k + 2) >> 1), k + 2);
         exp_pair(stA, pA, nmu, ls, k);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -361,7 +355,6 @@ __global__ __launch_bounds__(64) void fwd_kernel(const u32x4* __restrict__ qc,
       load_k(j_next);
       settle(0, stA, pA, ls);
     }
-    if (!full) mask_st(stB, lane_mask(real));
     {
       const float nmu = neg_m(1);
       float ls = 0.f;
@@ -370,6 +363,7 @@ __global__ __launch_bounds__(64) void fwd_kernel(const u32x4* __restrict__ qc,
       for (int k = 0; k < 16; ++k) {
         if (k < G2) gemm2_step(0, pA, k);
         exp_pair(stB, pB, nmu, ls, k);
+        if (k == 4) real_next = real_mask(j_next);   // scalar work between matrix ops
         __builtin_amdgcn_sched_barrier(0);
       }
       pin(pB);
@@ -377,11 +371,9 @@ __global__ __launch_bounds__(64) void fwd_kernel(const u32x4* __restrict__ qc,
     }
 #pragma unroll
     for (int k = 0; k < G2; ++k) gemm2_step(1, pB, k);
-    real = real_mask(j_next);
-    zero(stA);
-    gemm1_half(0, stA);
+    real = real_next;
+    gemm1_half(0, stA, real);
     load_v(j_next);
-    if (real != ~0ull) mask_st(stA, lane_mask(real));
     j_cur = j_next;
   }
 
