@@ -35,6 +35,7 @@ EXPORTED = (
     "sparse_attn_reorder_pool", "sparse_attn_unreorder", "sparse_attn_pool", "sparse_attn_block_scores",
     "sparse_attn_select", "sparse_attn_mask_workspace_bytes",
     "sparse_attn_build_mask", "sparse_attn_fwd_workspace_bytes", "sparse_attn_fwd",
+    "sparse_attn_coarse",
     "sparse_attn_last_error",
 )
 
@@ -71,7 +72,7 @@ _SIGS = {
     "sparse_attn_geometry": (_i32, [_GP, ctypes.POINTER(_i32), ctypes.POINTER(_i64), ctypes.POINTER(_i64)]),
     "sparse_attn_ceil_k": (_i32, [_f64, _i32]),
     "sparse_attn_reorder": (_i32, [_vp, _vp, _i32, _GP, _vp]),
-    "sparse_attn_reorder_pool": (_i32, [_vp, _vp, _vp, _GP, _vp]),
+    "sparse_attn_reorder_pool": (_i32, [_vp, _vp, _i32, _vp, _GP, _vp]),
     "sparse_attn_unreorder": (_i32, [_vp, _vp, _vp, _vp, _GP, _vp]),
     "sparse_attn_pool": (_i32, [_vp, _vp, _vp, _vp, _GP, _vp]),
     "sparse_attn_block_scores": (_i32, [_vp, _vp, _vp, _f64, _GP, _vp]),
@@ -80,6 +81,7 @@ _SIGS = {
     "sparse_attn_build_mask": (_i32, [_vp, _vp, _GP, _i32, _f64, _f64, _vp, _vp, _vp, _i32, _vp, _sz, _vp]),
     "sparse_attn_fwd_workspace_bytes": (_sz, [_GP]),
     "sparse_attn_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _GP, _f32, _vp, _vp, _vp, _sz, _vp]),
+    "sparse_attn_coarse": (_i32, [_vp, _vp, _vp, _GP, _vp]),
     "sparse_attn_last_error": (ctypes.c_char_p, []),
 }
 
@@ -149,9 +151,9 @@ def sparse_attn_reorder(x, xc, layout: int, g: Geom, stream=None) -> None:
                                      int(layout), ctypes.byref(g), _stream(stream, x)))
 
 
-def sparse_attn_reorder_pool(x, xc, xbar, g: Geom, stream=None) -> None:
+def sparse_attn_reorder_pool(x, xc, layout: int, xbar, g: Geom, stream=None) -> None:
     _check(lib().sparse_attn_reorder_pool(_ptr(x, torch.bfloat16, "x"), _ptr(xc, torch.bfloat16, "xc"),
-                                          _ptr(xbar, torch.float64, "xbar"), ctypes.byref(g),
+                                          int(layout), _ptr(xbar, torch.float64, "xbar"), ctypes.byref(g),
                                           _stream(stream, x)))
 
 
@@ -211,6 +213,11 @@ def sparse_attn_fwd(qc, kc, vc, lut, counts, cap: int, g: Geom, scale: float, oc
                                  ws_bytes, _stream(stream, qc)))
 
 
+def sparse_attn_coarse(scores, vbar, oc, g: Geom, stream=None) -> None:
+    _check(lib().sparse_attn_coarse(_ptr(scores, torch.float64, "scores"), _ptr(vbar, torch.float64, "vbar"),
+                                    _ptr(oc, torch.float64, "oc"), ctypes.byref(g), _stream(stream, scores)))
+
+
 def sparse_attn_last_error() -> str:
     return lib().sparse_attn_last_error().decode(errors="replace")
 
@@ -231,12 +238,12 @@ def reorder(x: torch.Tensor, g: Geom, layout: int = SA_LAYOUT_QK, stream=None) -
     return xc
 
 
-def reorder_pool(x: torch.Tensor, g: Geom, stream=None):
-    """Cube-major copy in the QK layout and the float64 block means."""
+def reorder_pool(x: torch.Tensor, g: Geom, layout: int = SA_LAYOUT_QK, stream=None):
+    """Cube-major copy in the given block layout and the float64 block means."""
     nblk, n_real, n_pad = sparse_attn_geometry(g)
     xc = _empty((g.batch, g.heads, n_pad, g.head_dim), torch.bfloat16, x)
     xbar = _empty((g.batch, g.heads, nblk, g.head_dim), torch.float64, x)
-    sparse_attn_reorder_pool(x, xc, xbar, g, stream)
+    sparse_attn_reorder_pool(x, xc, layout, xbar, g, stream)
     return xc, xbar
 
 
@@ -295,13 +302,20 @@ def attention(q, k, v, g: Geom, k_frac: float, p: float, row_budget=None, stream
     """Whole path on row-major tokens: reorder (pooling Q and K on the way),
     pooled scores and hybrid selection, sparse forward, unreorder.
     Returns (O [B,H,N,d] bf16, LSE [B,H,N] fp32, lut, counts)."""
-    qc, qbar = reorder_pool(q, g, stream)
-    kc, kbar = reorder_pool(k, g, stream)
+    qc, qbar = reorder_pool(q, g, SA_LAYOUT_QK, stream)
+    kc, kbar = reorder_pool(k, g, SA_LAYOUT_QK, stream)
     vc = reorder(v, g, SA_LAYOUT_V, stream)
     lut, counts = mask_from_pooled(qbar, kbar, g, k_frac, p, row_budget, stream=stream)
     oc, lse_c = fwd(qc, kc, vc, lut, counts, g, stream=stream)
     o, lse = unreorder(oc, lse_c, g, stream)
     return o, lse, lut, counts
+
+
+def coarse(scores, vbar, g: Geom, stream=None) -> torch.Tensor:
+    """Coarse branch output per block: softmax(scores) @ vbar, [B,H,nblk,d] float64."""
+    oc = _empty(tuple(vbar.shape), torch.float64, vbar)
+    sparse_attn_coarse(scores, vbar, oc, g, stream)
+    return oc
 
 
 def default_scale(head_dim: int) -> float:

@@ -48,6 +48,8 @@ int32_t make_geom(const sa_geom* g, sa::Geom& d) {
                 g->cube_h, g->cube_w);
   if (g->head_dim != 64 && g->head_dim != 128)
     return fail(SA_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", g->head_dim);
+  if ((long long)g->batch * g->heads > 65535)
+    return fail(SA_ERR_UNSUPPORTED, "batch*heads must be <= 65535 (got %lld)", (long long)g->batch * g->heads);
   d.batch = g->batch;
   d.heads = g->heads;
   d.frames = g->frames;
@@ -152,14 +154,17 @@ int32_t sparse_attn_reorder(const void* x, void* xc, int32_t layout, const sa_ge
   return hip_status(sa::launch_reorder(x, xc, layout, d, (hipStream_t)stream), "reorder launch");
 }
 
-int32_t sparse_attn_reorder_pool(const void* x, void* xc, double* xbar, const sa_geom* g, void* stream) {
+int32_t sparse_attn_reorder_pool(const void* x, void* xc, int32_t layout, double* xbar, const sa_geom* g,
+                                 void* stream) {
   sa::Geom d;
   SA_TRY(make_geom(g, d));
   SA_TRY(check_ptr(x, 16, "x"));
   SA_TRY(check_ptr(xc, 16, "xc"));
   SA_TRY(check_ptr(xbar, 8, "xbar"));
+  if (layout != SA_LAYOUT_QK && layout != SA_LAYOUT_V)
+    return fail(SA_ERR_INVALID_ARG, "layout must be SA_LAYOUT_QK or SA_LAYOUT_V (got %d)", layout);
   if (x == xc) return fail(SA_ERR_INVALID_ARG, "x and xc must not overlap");
-  return hip_status(sa::launch_reorder_pool(x, xc, xbar, d, (hipStream_t)stream), "reorder_pool launch");
+  return hip_status(sa::launch_reorder_pool(x, xc, layout, xbar, d, (hipStream_t)stream), "reorder_pool launch");
 }
 
 int32_t sparse_attn_unreorder(const void* oc, void* o, const float* lse_c, float* lse,
@@ -186,6 +191,17 @@ int32_t sparse_attn_pool(const void* qc, const void* kc, double* qbar, double* k
   SA_TRY(check_ptr(qbar, 8, "qbar"));
   SA_TRY(check_ptr(kbar, 8, "kbar"));
   return hip_status(sa::launch_pool(qc, kc, qbar, kbar, d, (hipStream_t)stream), "pool launch");
+}
+
+int32_t sparse_attn_coarse(const double* scores, const double* vbar, double* oc, const sa_geom* g, void* stream) {
+  sa::Geom d;
+  SA_TRY(make_geom(g, d));
+  SA_TRY(check_ptr(scores, 8, "scores"));
+  SA_TRY(check_ptr(vbar, 8, "vbar"));
+  SA_TRY(check_ptr(oc, 8, "oc"));
+  if ((const void*)oc == (const void*)scores || (const void*)oc == (const void*)vbar)
+    return fail(SA_ERR_INVALID_ARG, "oc must not overlap its inputs");
+  return hip_status(sa::launch_coarse(scores, vbar, oc, d, (hipStream_t)stream), "coarse launch");
 }
 
 int32_t sparse_attn_block_scores(const double* qbar, const double* kbar, double* scores, double scale,

@@ -12,12 +12,13 @@
 // and the traffic is the algorithmic minimum: N rows read, n_pad rows written.
 // Pad slots are written as zeros.
 //
-// The fused form for queries and keys also takes the block's mean over its
-// real tokens (SpargeAttention2 summary page, "Block-Pooled Attention for
-// Efficient Mask Construction", step 2) from the tile while it sits in LDS, so
-// pooling costs no second pass over Q and K.  The sums are float64 (exact for
-// bf16 inputs) divided by the real-token count, the same values as the
-// separate pooling kernel.
+// The fused form also takes the block's mean over its real tokens from the
+// tile while it sits in LDS (SpargeAttention2 summary page, "Block-Pooled
+// Attention for Efficient Mask Construction", step 2, for queries and keys;
+// VSA summary page, "The Coarse Stage", for values), so pooling costs no
+// second pass over the tensor.  The sums are float64 (exact for bf16 inputs)
+// divided by the real-token count, the same values as the separate pooling
+// kernel.
 #include "sa_launch.h"
 #include "sa_layout.h"
 
@@ -83,7 +84,7 @@ __global__ __launch_bounds__(kThreads) void reorder_kernel(const u32x4* __restri
     const int ns = kBlock / per;
     double acc = 0.0;
     for (int s = grp * ns; s < (grp + 1) * ns; ++s)
-      acc += (double)__uint_as_float((uint32_t)tile[s * ldq + c] << 16);
+      acc += (double)__uint_as_float((uint32_t)tile[kV ? c * ldv + s : s * ldq + c] << 16);
     part[threadIdx.x] = acc;
     __syncthreads();
     if (threadIdx.x < d) {
@@ -130,10 +131,15 @@ hipError_t launch_reorder(const void* x, void* xc, int layout, const Geom& g, hi
   return hipGetLastError();
 }
 
-hipError_t launch_reorder_pool(const void* x, void* xc, double* xbar, const Geom& g, hipStream_t s) {
+hipError_t launch_reorder_pool(const void* x, void* xc, int layout, double* xbar, const Geom& g,
+                               hipStream_t s) {
   dim3 grid(g.nblk, g.batch * g.heads);
-  reorder_kernel<false, true><<<grid, kThreads, 0, s>>>(static_cast<const u32x4*>(x), static_cast<u32x4*>(xc),
-                                                         xbar, g);
+  const u32x4* src = static_cast<const u32x4*>(x);
+  u32x4* dst = static_cast<u32x4*>(xc);
+  if (layout == 1)
+    reorder_kernel<true, true><<<grid, kThreads, 0, s>>>(src, dst, xbar, g);
+  else
+    reorder_kernel<false, true><<<grid, kThreads, 0, s>>>(src, dst, xbar, g);
   return hipGetLastError();
 }
 

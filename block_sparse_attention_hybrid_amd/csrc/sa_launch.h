@@ -10,7 +10,8 @@
 namespace sa {
 
 hipError_t launch_reorder(const void* x, void* xc, int layout, const Geom& g, hipStream_t s);
-hipError_t launch_reorder_pool(const void* x, void* xc, double* xbar, const Geom& g, hipStream_t s);
+hipError_t launch_reorder_pool(const void* x, void* xc, int layout, double* xbar, const Geom& g,
+                               hipStream_t s);
 hipError_t launch_unreorder(const void* oc, void* o, const float* lse_c, float* lse,
                             const Geom& g, hipStream_t s);
 hipError_t launch_pool(const void* qc, const void* kc, double* qbar, double* kbar,
@@ -24,5 +25,6 @@ hipError_t launch_fwd(const void* qc, const void* kc, const void* vc, const int3
                       const int32_t* counts, int cap, const Geom& g, float scale, void* oc,
                       float* lse_c, void* workspace, hipStream_t s);
 size_t fwd_workspace_bytes(const Geom& g);
+hipError_t launch_coarse(const double* scores, const double* vbar, double* oc, const Geom& g, hipStream_t s);
 
 }  // namespace sa

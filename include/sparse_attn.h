@@ -8,6 +8,7 @@
  *   block_scores S = Qbar Kbar^T * scale (float64 matrix cores)
  *   select       per query block: hybrid Top-k U Top-p kept-block list
  *   fwd          block-sparse attention over the kept blocks -> O, LSE
+ *   coarse       block-level attention on pooled Q, K, V (coarse branch)
  *   unreorder    cube-major O (and LSE) -> row-major tokens
  *
  * Conventions shared by every entry point
@@ -81,7 +82,8 @@ enum {
 /* Shape of one attention call.  [VSA] "Cube Partitioning and Token
  * Re-Indexing": cubes of cube_t x cube_h x cube_w tokens (default 4x4x4).
  * cube_t*cube_h*cube_w must be 64 (the block size of every kernel).
- * head_dim must be 64 or 128. */
+ * head_dim must be 64 or 128; batch*heads at most 65535; nblk at most 2^24
+ * and batch*heads*nblk below 2^31 (SA_ERR_UNSUPPORTED otherwise). */
 typedef struct sa_geom {
   int32_t batch;
   int32_t heads;
@@ -116,16 +118,18 @@ int32_t sparse_attn_ceil_k(double k_frac, int32_t nblk);
 int32_t sparse_attn_reorder(const void* x, void* xc, int32_t layout,
                             const sa_geom* g, void* stream);
 
-/* sparse_attn_reorder with SA_LAYOUT_QK, fused with the block means of
- * sparse_attn_pool: [VSA] "Cube Partitioning and Token Re-Indexing"; [SA2]
- * "Block-Pooled Attention for Efficient Mask Construction" step 2.
- *   x     [batch, heads, N, head_dim] bf16, row-major tokens          (input)
- *   xc    [batch, heads, n_pad, head_dim] bf16, SA_LAYOUT_QK          (output)
- *   xbar  [batch, heads, nblk, head_dim] float64 block means          (output)
+/* sparse_attn_reorder fused with the block means of sparse_attn_pool:
+ * [VSA] "Cube Partitioning and Token Re-Indexing"; [SA2] "Block-Pooled
+ * Attention for Efficient Mask Construction" step 2 (queries, keys); [VSA]
+ * "The Coarse Stage" (pooled values for the coarse output).
+ *   x      [batch, heads, N, head_dim] bf16, row-major tokens         (input)
+ *   xc     [batch, heads, n_pad, head_dim] bf16 in `layout`           (output)
+ *   layout SA_LAYOUT_QK or SA_LAYOUT_V
+ *   xbar   [batch, heads, nblk, head_dim] float64 block means         (output)
  * xc is bit-identical to sparse_attn_reorder's and xbar to sparse_attn_pool's
  * output for the same tokens; pooling then costs no second read of xc. */
-int32_t sparse_attn_reorder_pool(const void* x, void* xc, double* xbar,
-                                 const sa_geom* g, void* stream);
+int32_t sparse_attn_reorder_pool(const void* x, void* xc, int32_t layout,
+                                 double* xbar, const sa_geom* g, void* stream);
 
 /* Inverse re-indexing of the attention output (pad slots dropped).
  *   oc    [batch, heads, n_pad, head_dim] bf16, slot-major  (input)
@@ -153,6 +157,20 @@ int32_t sparse_attn_pool(const void* qc, const void* kc, double* qbar,
 int32_t sparse_attn_block_scores(const double* qbar, const double* kbar,
                                  double* scores, double scale,
                                  const sa_geom* g, void* stream);
+
+/* Coarse branch output, [VSA] "The Coarse Stage" ([VSA2] section 2.2):
+ * attention at block granularity on the pooled tokens,
+ *   oc[i] = sum_j softmax(scores[i, :])_j * vbar[j],
+ * in float64; row i is the coarse output of every real token of block i (the
+ * gate that would mix it with the fine output needs trained weights and is
+ * not part of the library).
+ *   scores [batch, heads, nblk, nblk] float64 (sparse_attn_block_scores)  (input)
+ *   vbar   [batch, heads, nblk, head_dim] float64 pooled values
+ *          (sparse_attn_reorder_pool with SA_LAYOUT_V)                     (input)
+ *   oc     [batch, heads, nblk, head_dim] float64                          (output)
+ * oc must not overlap the inputs. */
+int32_t sparse_attn_coarse(const double* scores, const double* vbar, double* oc,
+                           const sa_geom* g, void* stream);
 
 /* Hybrid Top-k U Top-p selection, [SA2] "The Hybrid Top-k+Top-p Masking Rule"
  * (Eq. 9), producing index lists as [VSA] "Kernel Implementation" describes

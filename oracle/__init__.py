@@ -3,7 +3,8 @@ only: tests/, the smoke check and the benchmark's CPU-baseline leg use it; the
 GPU package never does)."""
 from .oracle import *  # noqa: F401,F403
 from .oracle import (Geometry, MaskResult, RowSelection, attention_block,
-                     block_scores, block_softmax, build_mask, ceil_k,
+                     block_scores, block_softmax, build_mask, ceil_k, coarse_output,
+                     expand_blocks,
                      dense_attention, pool, rank_order, real_slots, reorder,
                      select_row, select_rows, sparse_attention, token_slots,
                      top_p_count, unreorder, unreorder_rows, NEAR_TIE)

@@ -35,6 +35,12 @@ What it computes, step by step, in float64 (bfloat16 inputs convert exactly):
    log-sum-exp of its scaled scores is returned beside it.  This is the plain
    definition written out: no online softmax, no tiling.
 
+6. Coarse branch output (VSA summary page, "The Coarse Stage"; "Improving
+   Video Sparse Attention ...", section 2.2): attention at block granularity on
+   the pooled Q, K and V, O_c = softmax(Qbar Kbar^T / sqrt(d)) Vbar, whose row i
+   is repeated to every real token of block i.  The gate that mixes it with the
+   fine output needs trained weights and is not part of this oracle.
+
 Readings where the pages are silent or garbled are listed in the repository's
 design notes; the ones this file depends on are repeated at each function.
 Every function here is pinned by the CPU tests (worked examples, closed forms,
@@ -352,3 +358,30 @@ def dense_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
     e = np.exp(s - m)
     l = e.sum(axis=-1, keepdims=True)
     return np.matmul(e, v) / l, (m + np.log(l))[..., 0]
+
+
+# ----------------------------------------------------------------------------
+# 6. coarse branch output
+# ----------------------------------------------------------------------------
+def coarse_output(qc: np.ndarray, kc_: np.ndarray, vc: np.ndarray, g: Geometry,
+                  scale: Optional[float] = None) -> np.ndarray:
+    """Block-level attention on pooled tokens: [..., n_pad, d] x3 -> [..., nblk, d].
+
+    VSA summary page, "The Coarse Stage": queries, keys and values are
+    mean-pooled per cube (real tokens only, as in step 2) and attend to each
+    other at block granularity; row i is the coarse output of every token of
+    block i."""
+    qbar, kbar, vbar = pool(qc, g), pool(kc_, g), pool(vc, g)
+    d = qbar.shape[-1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    p = block_softmax(np.matmul(qbar, np.swapaxes(kbar, -1, -2)) * scale)
+    return np.matmul(p, vbar)
+
+
+def expand_blocks(xb: np.ndarray, g: Geometry) -> np.ndarray:
+    """Repeat each block row to the block's real token slots (pads get 0):
+    [..., nblk, d] -> [..., n_pad, d] in cube-major slot order."""
+    out = np.repeat(np.asarray(xb, dtype=np.float64), g.block, axis=-2)
+    out[..., ~real_slots(g), :] = 0.0
+    return out

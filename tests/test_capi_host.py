@@ -72,6 +72,7 @@ def test_ceil_k_matches_worked_example_and_oracle():
     (dict(cube=(0, 8, 8)), sa.SA_ERR_INVALID_ARG),
     (dict(batch=0), sa.SA_ERR_INVALID_ARG),
     (dict(frames=0), sa.SA_ERR_INVALID_ARG),
+    (dict(batch=256, heads=256), sa.SA_ERR_UNSUPPORTED),
 ])
 def test_bad_geometry_rejected(kw, code):
     g = geom(**kw)
@@ -89,13 +90,17 @@ def test_null_and_misaligned_pointers_rejected():
     assert lib.sparse_attn_reorder(FAKE, FAKE, 0, B, None) == sa.SA_ERR_INVALID_ARG   # overlap
     assert lib.sparse_attn_reorder(FAKE_MISALIGNED, FAKE, 0, B, None) == sa.SA_ERR_INVALID_ARG
     assert lib.sparse_attn_reorder(FAKE, ctypes.c_void_p(0x200000), 2, B, None) == sa.SA_ERR_INVALID_ARG
-    assert lib.sparse_attn_reorder_pool(FAKE, ctypes.c_void_p(0x200000), None, B, None) == sa.SA_ERR_INVALID_ARG
-    assert lib.sparse_attn_reorder_pool(FAKE, FAKE, ctypes.c_void_p(0x300000), B, None) == sa.SA_ERR_INVALID_ARG
-    assert lib.sparse_attn_reorder_pool(FAKE, ctypes.c_void_p(0x200000), ctypes.c_void_p(0x300004), B,
+    assert lib.sparse_attn_reorder_pool(FAKE, ctypes.c_void_p(0x200000), 0, None, B, None) == sa.SA_ERR_INVALID_ARG
+    assert lib.sparse_attn_reorder_pool(FAKE, FAKE, 0, ctypes.c_void_p(0x300000), B, None) == sa.SA_ERR_INVALID_ARG
+    assert lib.sparse_attn_reorder_pool(FAKE, ctypes.c_void_p(0x200000), 0, ctypes.c_void_p(0x300004), B,
                                         None) == sa.SA_ERR_INVALID_ARG   # xbar misaligned
+    assert lib.sparse_attn_reorder_pool(FAKE, ctypes.c_void_p(0x200000), 3, ctypes.c_void_p(0x300000), B,
+                                        None) == sa.SA_ERR_INVALID_ARG   # layout
     assert lib.sparse_attn_unreorder(FAKE, FAKE, FAKE, None, B, None) == sa.SA_ERR_INVALID_ARG
     assert lib.sparse_attn_pool(FAKE, FAKE, None, FAKE, B, None) == sa.SA_ERR_INVALID_ARG
     assert lib.sparse_attn_block_scores(FAKE, FAKE, None, 0.0, B, None) == sa.SA_ERR_INVALID_ARG
+    assert lib.sparse_attn_coarse(FAKE, FAKE, None, B, None) == sa.SA_ERR_INVALID_ARG
+    assert lib.sparse_attn_coarse(FAKE, ctypes.c_void_p(0x200000), FAKE, B, None) == sa.SA_ERR_INVALID_ARG
     assert lib.sparse_attn_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, 16, B, 0.0, FAKE, None, None, 0,
                                None) == sa.SA_ERR_INVALID_ARG
     assert "lse_c" in sa.sparse_attn_last_error()

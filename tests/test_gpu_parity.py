@@ -278,3 +278,28 @@ def test_scale_argument():
     o = O.unreorder(to64(oc), og)
     mx, mean = attn_errors(o, o_ref)
     assert mx <= O_MAX_ABS and mean <= O_MEAN_ABS
+
+
+def test_coarse_output_matches_oracle(case):
+    """Coarse branch: the kernel on the oracle's scores and pooled values, and
+    end to end from the fused reorders."""
+    g, og = case["g"], case["og"]
+    ref = case["ref_mask"]
+    want = O.coarse_output(case["ref_qc"], case["ref_kc"], case["ref_vc"], og)
+    vbar_ref = O.pool(case["ref_vc"], og)
+    scale = max(1.0, float(np.abs(want).max()))
+    got = sa.coarse(torch.from_numpy(ref.scores).to(DEV), torch.from_numpy(vbar_ref).to(DEV), g)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(got.cpu().numpy(), want, rtol=1e-12, atol=1e-13 * scale)
+    # end to end: pooled values come from the V reorder, scores from the GPU
+    vc, vbar = sa.reorder_pool(case["vd"], g, V)
+    qc, qbar = sa.reorder_pool(case["qd"], g)
+    kc, kbar = sa.reorder_pool(case["kd"], g)
+    nblk = og.nblk
+    s = torch.empty(g.batch, g.heads, nblk, nblk, dtype=torch.float64, device=DEV)
+    sa.sparse_attn_block_scores(qbar, kbar, s, 0.0, g)
+    got2 = sa.coarse(s, vbar, g)
+    torch.cuda.synchronize()
+    assert np.array_equal(to64(vc), to_layout(case["ref_vc"], True))
+    np.testing.assert_array_equal(vbar.cpu().numpy(), vbar_ref)
+    np.testing.assert_allclose(got2.cpu().numpy(), want, rtol=1e-11, atol=1e-12 * scale)

@@ -484,3 +484,85 @@ def test_p_one_keeps_every_block_even_when_sums_saturate():
     probs = O.block_softmax(s)
     assert np.cumsum(probs)[0] == 1.0                 # saturated after one block
     assert list(O.select_row(s, 0, 1.0, probs).kept) == [0, 1, 2, 3, 4]
+
+
+# ----------------------------------------------------------------------------
+# coarse branch output: attention on pooled tokens
+# ----------------------------------------------------------------------------
+def _gather_block_means(x, grid, cube=(4, 4, 4)):
+    """Block means straight from row-major tokens by (t, h, w) coordinates
+    (independent of the oracle's reorder and pool)."""
+    T, H, W = grid
+    ct, ch, cw = cube
+    nt, nh, nw = -(-T // ct), -(-H // ch), -(-W // cw)
+    out = np.zeros(x.shape[:-2] + (nt * nh * nw, x.shape[-1]))
+    for bt in range(nt):
+        for bh in range(nh):
+            for bw in range(nw):
+                idx = [(t * H + h) * W + w for t in range(bt * ct, min(T, bt * ct + ct))
+                       for h in range(bh * ch, min(H, bh * ch + ch))
+                       for w in range(bw * cw, min(W, bw * cw + cw))]
+                out[..., (bt * nh + bh) * nw + bw, :] = x[..., idx, :].mean(axis=-2)
+    return out
+
+
+def test_coarse_output_is_library_attention_on_pooled_tokens():
+    wl, q, k, v = _tiny_inputs(grid=(5, 6, 9), heads=2, d=32, seed=4)
+    g = O.Geometry(*wl.grid)
+    got = O.coarse_output(*(O.reorder(x, g) for x in (q, k, v)), g)
+    qb, kb, vb = (torch.from_numpy(_gather_block_means(x, wl.grid)) for x in (q, k, v))
+    want = torch.nn.functional.scaled_dot_product_attention(qb, kb, vb).numpy()
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-13)
+
+
+def test_coarse_output_two_block_closed_form():
+    """Two blocks: row i is sigmoid(s_i0 - s_i1) Vbar_0 + sigmoid(s_i1 - s_i0) Vbar_1."""
+    rng = np.random.default_rng(21)
+    g = O.Geometry(8, 4, 4)
+    assert g.nblk == 2
+    d = 8
+    q, k, v = (rng.standard_normal((g.n_real, d)) for _ in range(3))
+    qb, kb, vb = (_gather_block_means(x, (8, 4, 4)) for x in (q, k, v))
+    got = O.coarse_output(*(O.reorder(x, g) for x in (q, k, v)), g)
+    for i in range(2):
+        s0 = sum(qb[i, c] * kb[0, c] for c in range(d)) / math.sqrt(d)
+        s1 = sum(qb[i, c] * kb[1, c] for c in range(d)) / math.sqrt(d)
+        w0 = 1.0 / (1.0 + math.exp(s1 - s0))
+        np.testing.assert_allclose(got[i], w0 * vb[0] + (1.0 - w0) * vb[1], rtol=1e-12, atol=1e-14)
+
+
+def test_coarse_output_constant_values_and_dominant_block():
+    rng = np.random.default_rng(22)
+    g = O.Geometry(5, 7, 9)
+    d = 16
+    q, k = rng.standard_normal((g.n_real, d)), rng.standard_normal((g.n_real, d))
+    # rows of the block softmax sum to one: constant values come back unchanged
+    v = np.tile(np.linspace(-1.0, 1.0, d), (g.n_real, 1))
+    got = O.coarse_output(O.reorder(q, g), O.reorder(k, g), O.reorder(v, g), g)
+    np.testing.assert_allclose(got, np.broadcast_to(v[0], got.shape), rtol=1e-13, atol=1e-14)
+    # one key block far ahead of the rest takes all the weight
+    v = rng.standard_normal((g.n_real, d))
+    qc, kc_, vc = O.reorder(q, g), O.reorder(k, g), O.reorder(v, g)
+    u = np.ones(d) / math.sqrt(d)
+    qc[:, :] += 50.0 * u
+    kc_[5 * g.block:6 * g.block] += 200.0 * u
+    got = O.coarse_output(qc, kc_, vc, g)
+    np.testing.assert_allclose(got, np.broadcast_to(O.pool(vc, g)[5], got.shape), rtol=1e-9, atol=1e-9)
+
+
+def test_coarse_output_ignores_pads_and_expands_to_real_tokens():
+    rng = np.random.default_rng(23)
+    g = O.Geometry(5, 6, 7)
+    d = 8
+    q, k, v = (rng.standard_normal((g.n_real, d)) for _ in range(3))
+    qc, kc_, vc = (O.reorder(x, g) for x in (q, k, v))
+    base = O.coarse_output(qc, kc_, vc, g)
+    pads = ~O.real_slots(g)
+    for x in (qc, kc_, vc):
+        x[pads] = rng.standard_normal((int(pads.sum()), d)) * 100.0
+    np.testing.assert_array_equal(O.coarse_output(qc, kc_, vc, g), base)
+    full = O.expand_blocks(base, g)
+    slots = O.token_slots(g)              # cube-major slot of each row-major token
+    blk_of_token = slots // g.block
+    np.testing.assert_array_equal(full[slots], base[blk_of_token])
+    assert np.all(full[pads] == 0.0)
