@@ -41,6 +41,18 @@ What it computes, step by step, in float64 (bfloat16 inputs convert exactly):
    is repeated to every real token of block i.  The gate that mixes it with the
    fine output needs trained weights and is not part of this oracle.
 
+7. Fine-grained router ("Improving Video Sparse Attention with Fine-grained
+   Router and Sparse Rebasing", section 2.2, Figure 2, the router equations):
+   Q and K are mean-pooled over sub-cubes of R = (rt, rh, rw) tokens (G = 64/R
+   sub-cubes per cube), the router attention Softmax(Q_r K_r^T / sqrt(d)) is
+   taken over all sub-cube keys of the head, and a G x G aggregation turns it
+   into block-level scores P_r.  Readings: the aggregation sums over the key
+   sub-cubes of a block and averages over the query sub-cubes, so each row of
+   P_r is a probability row (it sums to 1) and the hybrid rule applies to it
+   unchanged; sub-cubes holding only pad slots of a partial cube take no part
+   (as keys or as queries).  The scores handed to the selection are log P_r,
+   whose row softmax is P_r itself.
+
 Readings where the pages are silent or garbled are listed in the repository's
 design notes; the ones this file depends on are repeated at each function.
 Every function here is pinned by the CPU tests (worked examples, closed forms,
@@ -385,3 +397,64 @@ def expand_blocks(xb: np.ndarray, g: Geometry) -> np.ndarray:
     out = np.repeat(np.asarray(xb, dtype=np.float64), g.block, axis=-2)
     out[..., ~real_slots(g), :] = 0.0
     return out
+
+
+# ----------------------------------------------------------------------------
+# 7. fine-grained router (sub-cube pooling, softmax, G x G aggregation)
+# ----------------------------------------------------------------------------
+def subcube_of_slot(g: Geometry, R: Tuple[int, int, int]) -> np.ndarray:
+    """Sub-cube index a in [0, G) of each of the 64 slots of a cube, for
+    sub-cubes of rt x rh x rw tokens (row-major over the sub-cube grid)."""
+    rt, rh, rw = R
+    if g.ct % rt or g.ch % rh or g.cw % rw:
+        raise ValueError("the sub-cube must tile the cube")
+    s = np.arange(g.block)
+    tt, rem = np.divmod(s, g.ch * g.cw)
+    hh, ww = np.divmod(rem, g.cw)
+    return ((tt // rt) * (g.ch // rh) + hh // rh) * (g.cw // rw) + ww // rw
+
+
+def pool_r(xc: np.ndarray, g: Geometry, R: Tuple[int, int, int]):
+    """Sub-cube means over real tokens: [..., n_pad, d] -> ([..., nblk*G, d],
+    present [nblk*G]); a sub-cube with no real token has mean 0 and is absent."""
+    xc = np.asarray(xc, dtype=np.float64)
+    d = xc.shape[-1]
+    G = g.block // (R[0] * R[1] * R[2])
+    sub = subcube_of_slot(g, R)
+    real = real_slots(g).reshape(g.nblk, g.block)
+    blocks = xc.reshape(xc.shape[:-2] + (g.nblk, g.block, d))
+    sums = np.zeros(xc.shape[:-2] + (g.nblk, G, d))
+    cnt = np.zeros((g.nblk, G))
+    for a in range(G):
+        w = real & (sub == a)[None, :]
+        sums[..., a, :] = (blocks * w[..., None]).sum(axis=-2)
+        cnt[:, a] = w.sum(axis=1)
+    present = cnt > 0
+    means = np.where(present[..., None], sums / np.maximum(cnt, 1)[..., None], 0.0)
+    return means.reshape(xc.shape[:-2] + (g.nblk * G, d)), present.reshape(-1)
+
+
+def router_scores(qc: np.ndarray, kc_: np.ndarray, g: Geometry, R: Tuple[int, int, int] = (2, 2, 2),
+                  scale: Optional[float] = None) -> np.ndarray:
+    """log P_r of one or more heads: [..., n_pad, d] x2 -> [..., nblk, nblk].
+
+    P_hat = Softmax(Q_r K_r^T * scale) over the present sub-cube keys of the
+    head; P_r[i, j] = mean over the present query sub-cubes a of block i of
+    sum over the key sub-cubes b of block j of P_hat[(i, a), (j, b)]."""
+    qr, present = pool_r(qc, g, R)
+    kr, _ = pool_r(kc_, g, R)
+    d = qr.shape[-1]
+    G = g.block // (R[0] * R[1] * R[2])
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    s = np.matmul(qr, np.swapaxes(kr, -1, -2)) * scale
+    s = np.where(present[None, :], s, -np.inf)
+    p = np.exp(s - s.max(axis=-1, keepdims=True))
+    p = p / p.sum(axis=-1, keepdims=True)
+    lead = p.shape[:-2]
+    p = p.reshape(lead + (g.nblk, G, g.nblk, G))
+    per_query = p.sum(axis=-1)                                   # [..., i, a, j]
+    pres = present.reshape(g.nblk, G)
+    pr = (per_query * pres[:, :, None]).sum(axis=-2) / pres.sum(axis=1)[:, None]
+    with np.errstate(divide="ignore"):
+        return np.log(pr)

@@ -566,3 +566,76 @@ def test_coarse_output_ignores_pads_and_expands_to_real_tokens():
     blk_of_token = slots // g.block
     np.testing.assert_array_equal(full[slots], base[blk_of_token])
     assert np.all(full[pads] == 0.0)
+
+
+# ----------------------------------------------------------------------------
+# fine-grained router: sub-cube pooling, router softmax, G x G aggregation
+# ----------------------------------------------------------------------------
+def _coordinate_router(q, k, grid, R, cube=(4, 4, 4)):
+    """The router by explicit token coordinates: sub-cube means, softmax over
+    the sub-cube keys (library softmax), then sum over key sub-cubes of a block
+    and mean over the query sub-cubes present in a block."""
+    T, H, W = grid
+    ct, ch, cw = cube
+    nh, nw = -(-H // ch), -(-W // cw)
+    groups = {}
+    for t in range(T):
+        for h in range(H):
+            for w in range(W):
+                blk = ((t // ct) * nh + h // ch) * nw + w // cw
+                sub = ((t % ct) // R[0], (h % ch) // R[1], (w % cw) // R[2])
+                groups.setdefault((blk, sub), []).append((t * H + h) * W + w)
+    keys = sorted(groups)
+    qr = np.stack([q[groups[key_]].mean(axis=0) for key_ in keys])
+    kr = np.stack([k[groups[key_]].mean(axis=0) for key_ in keys])
+    blk_of = np.array([key_[0] for key_ in keys])
+    nblk = blk_of.max() + 1
+    p = torch.softmax(torch.from_numpy(qr @ kr.T / math.sqrt(q.shape[1])), dim=1).numpy()
+    out = np.zeros((nblk, nblk))
+    for i in range(nblk):
+        rows = np.nonzero(blk_of == i)[0]
+        for j in range(nblk):
+            cols = np.nonzero(blk_of == j)[0]
+            out[i, j] = p[np.ix_(rows, cols)].sum(axis=1).mean()
+    return out
+
+
+@pytest.mark.parametrize("grid", [(5, 6, 7), (4, 8, 8), (3, 5, 6)])
+def test_router_matches_coordinate_definition(grid):
+    rng = np.random.default_rng(31)
+    g = O.Geometry(*grid)
+    d = 16
+    q, k = rng.standard_normal((g.n_real, d)), rng.standard_normal((g.n_real, d))
+    got = np.exp(O.router_scores(O.reorder(q, g), O.reorder(k, g), g, (2, 2, 2)))
+    np.testing.assert_allclose(got, _coordinate_router(q, k, grid, (2, 2, 2)), rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(got.sum(axis=1), 1.0, rtol=1e-13)
+
+
+def test_router_with_cube_sized_pooling_is_the_block_softmax():
+    """R = the cube (G = 1): the router reduces to the block-pooled softmax."""
+    rng = np.random.default_rng(32)
+    g = O.Geometry(6, 9, 5)
+    d = 8
+    q, k = rng.standard_normal((g.n_real, d)), rng.standard_normal((g.n_real, d))
+    qc, kc_ = O.reorder(q, g), O.reorder(k, g)
+    got = O.router_scores(qc, kc_, g, (4, 4, 4))
+    want = np.log(O.block_softmax(O.block_scores(O.pool(qc, g), O.pool(kc_, g), d)))
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+def test_router_with_token_pooling_is_pooled_token_attention():
+    """R = one token (G = 64): P_r averages the full token-level softmax over a
+    query block's real tokens and sums it over a key block's real tokens."""
+    rng = np.random.default_rng(33)
+    grid = (5, 4, 6)
+    g = O.Geometry(*grid)
+    d = 8
+    q, k = rng.standard_normal((g.n_real, d)), rng.standard_normal((g.n_real, d))
+    got = np.exp(O.router_scores(O.reorder(q, g), O.reorder(k, g), g, (1, 1, 1)))
+    p = torch.softmax(torch.from_numpy(q @ k.T / math.sqrt(d)), dim=1).numpy()
+    blk = O.token_slots(g) // g.block
+    want = np.zeros((g.nblk, g.nblk))
+    for i in range(g.nblk):
+        for j in range(g.nblk):
+            want[i, j] = p[np.ix_(blk == i, blk == j)].sum(axis=1).mean()
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-15)
