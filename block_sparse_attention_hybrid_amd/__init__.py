@@ -35,7 +35,7 @@ EXPORTED = (
     "sparse_attn_reorder_pool", "sparse_attn_unreorder", "sparse_attn_pool", "sparse_attn_block_scores",
     "sparse_attn_select", "sparse_attn_mask_workspace_bytes",
     "sparse_attn_build_mask", "sparse_attn_fwd_workspace_bytes", "sparse_attn_fwd",
-    "sparse_attn_coarse",
+    "sparse_attn_coarse", "sparse_attn_router_pool", "sparse_attn_router_scores",
     "sparse_attn_last_error",
 )
 
@@ -82,6 +82,8 @@ _SIGS = {
     "sparse_attn_fwd_workspace_bytes": (_sz, [_GP]),
     "sparse_attn_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _GP, _f32, _vp, _vp, _vp, _sz, _vp]),
     "sparse_attn_coarse": (_i32, [_vp, _vp, _vp, _GP, _vp]),
+    "sparse_attn_router_pool": (_i32, [_vp, _vp, _GP, _i32, _i32, _i32, _vp]),
+    "sparse_attn_router_scores": (_i32, [_vp, _vp, _vp, _f64, _GP, _i32, _i32, _i32, _vp]),
     "sparse_attn_last_error": (ctypes.c_char_p, []),
 }
 
@@ -218,6 +220,18 @@ def sparse_attn_coarse(scores, vbar, oc, g: Geom, stream=None) -> None:
                                     _ptr(oc, torch.float64, "oc"), ctypes.byref(g), _stream(stream, scores)))
 
 
+def sparse_attn_router_pool(xc, xr, g: Geom, sub=(2, 2, 2), stream=None) -> None:
+    _check(lib().sparse_attn_router_pool(_ptr(xc, torch.bfloat16, "xc"), _ptr(xr, torch.float64, "xr"),
+                                         ctypes.byref(g), int(sub[0]), int(sub[1]), int(sub[2]),
+                                         _stream(stream, xc)))
+
+
+def sparse_attn_router_scores(qr, kr, scores, scale: float, g: Geom, sub=(2, 2, 2), stream=None) -> None:
+    _check(lib().sparse_attn_router_scores(_ptr(qr, torch.float64, "qr"), _ptr(kr, torch.float64, "kr"),
+                                           _ptr(scores, torch.float64, "scores"), float(scale), ctypes.byref(g),
+                                           int(sub[0]), int(sub[1]), int(sub[2]), _stream(stream, qr)))
+
+
 def sparse_attn_last_error() -> str:
     return lib().sparse_attn_last_error().decode(errors="replace")
 
@@ -316,6 +330,25 @@ def coarse(scores, vbar, g: Geom, stream=None) -> torch.Tensor:
     oc = _empty(tuple(vbar.shape), torch.float64, vbar)
     sparse_attn_coarse(scores, vbar, oc, g, stream)
     return oc
+
+
+def router_mask(qc, kc, g: Geom, k_frac: float, p: float, sub=(2, 2, 2), row_budget=None, cap=None,
+                stream=None):
+    """Hybrid selection on the fine-grained router's block scores.
+    Returns (lut, counts, scores = log P_r)."""
+    nblk, _, _ = sparse_attn_geometry(g)
+    G = 64 // (sub[0] * sub[1] * sub[2])
+    cap = nblk if cap is None else cap
+    qr = _empty((g.batch, g.heads, nblk * G, g.head_dim), torch.float64, qc)
+    kr = torch.empty_like(qr)
+    scores = _empty((g.batch, g.heads, nblk, nblk), torch.float64, qc)
+    lut = _empty((g.batch, g.heads, nblk, cap), torch.int32, qc)
+    counts = _empty((g.batch, g.heads, nblk), torch.int32, qc)
+    sparse_attn_router_pool(qc, qr, g, sub, stream)
+    sparse_attn_router_pool(kc, kr, g, sub, stream)
+    sparse_attn_router_scores(qr, kr, scores, 0.0, g, sub, stream)
+    sparse_attn_select(scores, g, k_frac, p, row_budget, lut, counts, cap, stream)
+    return lut, counts, scores
 
 
 def default_scale(head_dim: int) -> float:

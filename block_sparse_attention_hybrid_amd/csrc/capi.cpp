@@ -204,6 +204,39 @@ int32_t sparse_attn_coarse(const double* scores, const double* vbar, double* oc,
   return hip_status(sa::launch_coarse(scores, vbar, oc, d, (hipStream_t)stream), "coarse launch");
 }
 
+static int32_t check_subcube(const sa::Geom& d, int32_t rt, int32_t rh, int32_t rw) {
+  if (rt < 1 || rh < 1 || rw < 1 || d.ct % rt || d.ch % rh || d.cw % rw)
+    return fail(SA_ERR_INVALID_ARG, "sub-cube %d x %d x %d must tile the %d x %d x %d cube", rt, rh, rw, d.ct,
+                d.ch, d.cw);
+  const long long G = 64 / ((long long)rt * rh * rw);
+  if ((long long)d.nblk * G * d.batch * d.heads > 0x7fffffffLL)
+    return fail(SA_ERR_UNSUPPORTED, "too many sub-cubes (%lld per head)", (long long)d.nblk * G);
+  return SA_OK;
+}
+
+int32_t sparse_attn_router_pool(const void* xc, double* xr, const sa_geom* g, int32_t rt, int32_t rh, int32_t rw,
+                                void* stream) {
+  sa::Geom d;
+  SA_TRY(make_geom(g, d));
+  SA_TRY(check_subcube(d, rt, rh, rw));
+  SA_TRY(check_ptr(xc, 16, "xc"));
+  SA_TRY(check_ptr(xr, 8, "xr"));
+  return hip_status(sa::launch_router_pool(xc, xr, d, rt, rh, rw, (hipStream_t)stream), "router_pool launch");
+}
+
+int32_t sparse_attn_router_scores(const double* qr, const double* kr, double* scores, double scale,
+                                  const sa_geom* g, int32_t rt, int32_t rh, int32_t rw, void* stream) {
+  sa::Geom d;
+  SA_TRY(make_geom(g, d));
+  SA_TRY(check_subcube(d, rt, rh, rw));
+  SA_TRY(check_ptr(qr, 8, "qr"));
+  SA_TRY(check_ptr(kr, 8, "kr"));
+  SA_TRY(check_ptr(scores, 8, "scores"));
+  if (!std::isfinite(scale)) return fail(SA_ERR_INVALID_ARG, "scale must be finite");
+  if (scale <= 0.0) scale = 1.0 / std::sqrt((double)d.d);
+  return hip_status(sa::launch_router(qr, kr, scores, scale, d, rt, rh, rw, (hipStream_t)stream), "router launch");
+}
+
 int32_t sparse_attn_block_scores(const double* qbar, const double* kbar, double* scores, double scale,
                                  const sa_geom* g, void* stream) {
   sa::Geom d;

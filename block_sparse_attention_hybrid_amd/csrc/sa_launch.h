@@ -25,6 +25,9 @@ hipError_t launch_fwd(const void* qc, const void* kc, const void* vc, const int3
                       const int32_t* counts, int cap, const Geom& g, float scale, void* oc,
                       float* lse_c, void* workspace, hipStream_t s);
 size_t fwd_workspace_bytes(const Geom& g);
+hipError_t launch_router_pool(const void* xc, double* xr, const Geom& g, int rt, int rh, int rw, hipStream_t s);
+hipError_t launch_router(const double* qr, const double* kr, double* scores, double scale, const Geom& g,
+                         int rt, int rh, int rw, hipStream_t s);
 hipError_t launch_coarse(const double* scores, const double* vbar, double* oc, const Geom& g, hipStream_t s);
 
 }  // namespace sa

@@ -9,6 +9,7 @@
  *   select       per query block: hybrid Top-k U Top-p kept-block list
  *   fwd          block-sparse attention over the kept blocks -> O, LSE
  *   coarse       block-level attention on pooled Q, K, V (coarse branch)
+ *   router       fine-grained router scores (sub-cube pooling, G x G pooling)
  *   unreorder    cube-major O (and LSE) -> row-major tokens
  *
  * Conventions shared by every entry point
@@ -171,6 +172,33 @@ int32_t sparse_attn_block_scores(const double* qbar, const double* kbar,
  * oc must not overlap the inputs. */
 int32_t sparse_attn_coarse(const double* scores, const double* vbar, double* oc,
                            const sa_geom* g, void* stream);
+
+/* Fine-grained router, [VSA2] section 2.2 (router equations, Figure 2,
+ * "Kernel Implementation"): Q and K pooled over sub-cubes of rt x rh x rw
+ * tokens (G = 64 / (rt*rh*rw) sub-cubes per cube; the sub-cube must tile the
+ * cube), the router softmax over every sub-cube key of the head, and a G x G
+ * aggregation into block scores P_r.  Readings of the aggregation: sum over
+ * the key sub-cubes of a block, mean over the query sub-cubes, so each row of
+ * P_r sums to 1; sub-cubes holding only pad slots take no part.
+ *
+ * sparse_attn_router_pool: sub-cube means of a QK-layout tensor.
+ *   xc [batch, heads, n_pad, head_dim] bf16, SA_LAYOUT_QK            (input)
+ *   xr [batch, heads, nblk*G, head_dim] float64, row blk*G + a       (output)
+ *      (sub-cube a row-major over the cube's sub-cube grid; an all-pad
+ *      sub-cube gets zeros)
+ * sparse_attn_router_scores: log P_r, float64, computed twice over the
+ * sub-cube scores (log-sum-exp, then softmax and aggregation) without
+ * materialising the router softmax.
+ *   qr, kr [batch, heads, nblk*G, head_dim] float64                  (inputs)
+ *   scores [batch, heads, nblk, nblk] float64 = log P_r               (output)
+ *   scale <= 0 selects 1/sqrt(head_dim).
+ * The scores go to sparse_attn_select unchanged: their row softmax is P_r. */
+int32_t sparse_attn_router_pool(const void* xc, double* xr, const sa_geom* g,
+                                int32_t rt, int32_t rh, int32_t rw, void* stream);
+int32_t sparse_attn_router_scores(const double* qr, const double* kr,
+                                  double* scores, double scale,
+                                  const sa_geom* g, int32_t rt, int32_t rh,
+                                  int32_t rw, void* stream);
 
 /* Hybrid Top-k U Top-p selection, [SA2] "The Hybrid Top-k+Top-p Masking Rule"
  * (Eq. 9), producing index lists as [VSA] "Kernel Implementation" describes

@@ -303,3 +303,46 @@ def test_coarse_output_matches_oracle(case):
     assert np.array_equal(to64(vc), to_layout(case["ref_vc"], True))
     np.testing.assert_array_equal(vbar.cpu().numpy(), vbar_ref)
     np.testing.assert_allclose(got2.cpu().numpy(), want, rtol=1e-11, atol=1e-12 * scale)
+
+
+def _ref_lists(scores, kc, p):
+    """Oracle selection of every row of scores [B, H, n, n] -> lut, counts,
+    near-tie flags and kc in the layout compare_lists expects."""
+    B, H, n, _ = scores.shape
+    lut = np.zeros((B, H, n, n), dtype=np.int32)
+    counts = np.zeros((B, H, n), dtype=np.int32)
+    near = np.zeros((B, H, n), dtype=bool)
+    for b in range(B):
+        for h in range(H):
+            for i, sel in enumerate(O.select_rows(scores[b, h], kc, p)):
+                counts[b, h, i] = sel.kept.size
+                lut[b, h, i, :sel.kept.size] = sel.kept
+                near[b, h, i] = sel.near_tie
+    return O.MaskResult(lut=lut, counts=counts, near_tie=near, kc=np.full((B, H, n), kc), pc=None,
+                        scores=scores, qbar=None, kbar=None)
+
+
+@pytest.mark.parametrize("sub", [(2, 2, 2), (1, 2, 2), (4, 4, 4)])
+def test_router_matches_oracle(case, sub):
+    g, og = case["g"], case["og"]
+    nblk = og.nblk
+    G = 64 // (sub[0] * sub[1] * sub[2])
+    qc, kc = sa.reorder(case["qd"], g, QK), sa.reorder(case["kd"], g, QK)
+    qr = torch.empty(g.batch, g.heads, nblk * G, g.head_dim, dtype=torch.float64, device=DEV)
+    kr = torch.empty_like(qr)
+    sa.sparse_attn_router_pool(qc, qr, g, sub)
+    sa.sparse_attn_router_pool(kc, kr, g, sub)
+    torch.cuda.synchronize()
+    want_qr, _ = O.pool_r(case["ref_qc"], og, sub)
+    want_kr, _ = O.pool_r(case["ref_kc"], og, sub)
+    np.testing.assert_array_equal(qr.cpu().numpy(), want_qr)
+    np.testing.assert_array_equal(kr.cpu().numpy(), want_kr)
+    want = O.router_scores(case["ref_qc"], case["ref_kc"], og, sub)
+    lut, counts, scores = sa.router_mask(qc, kc, g, case["k_frac"], case["p"], sub)
+    torch.cuda.synchronize()
+    got = scores.cpu().numpy()
+    np.testing.assert_allclose(got, want, rtol=1e-11, atol=1e-12)
+    ref = _ref_lists(want, O.ceil_k(case["k_frac"], nblk), case["p"])
+    bad, near, invalid = compare_lists(lut.cpu().numpy(), counts.cpu().numpy(), ref, case["p"])
+    say(f"  router {sub}: {len(bad)} mismatched rows, {near} near ties ({len(invalid)} invalid)")
+    assert not bad and not invalid

@@ -97,3 +97,27 @@ def test_workload(name, wid, k_frac, p, budgets, heads):
                 main = to64(oc[0, sel[hi], i * 64:(i + 1) * 64])
                 assert np.array_equal(main, ocs_h[0, hi, i * 64:(i + 1) * 64])
     say(f"  attention: O max {worst[0]:.2e} mean {worst[1]:.2e}; LSE max {worst[2]:.2e} mean {worst[3]:.2e}")
+
+
+def test_router_full_size():
+    """Fine-grained router (2x2x2 sub-cubes, G = 8) at the 720p shape on two
+    heads (a uniform and a skewed one): scores and kept lists against the oracle."""
+    wl = synth.WORKLOADS[2]
+    heads = [0, 1]
+    say(f"[router 720p] heads {heads} grid={wl.grid}")
+    q, k, _ = synth.make_qkv(wl, 0, heads=heads)
+    g = sa.make_geom(1, len(heads), wl.frames, wl.height, wl.width, wl.head_dim)
+    og = ogeom_of(wl)
+    qc, kc = sa.reorder(q.to(DEV), g, sa.SA_LAYOUT_QK), sa.reorder(k.to(DEV), g, sa.SA_LAYOUT_QK)
+    lut, counts, scores = sa.router_mask(qc, kc, g, 0.03, 0.073)
+    torch.cuda.synchronize()
+    say("  gpu router done")
+    ref_qc, ref_kc = O.reorder(to64(q), og), O.reorder(to64(k), og)
+    want = np.stack([O.router_scores(ref_qc[0, h], ref_kc[0, h], og) for h in range(len(heads))])[None]
+    np.testing.assert_allclose(scores.cpu().numpy(), want, rtol=1e-10, atol=1e-11)
+    from test_gpu_parity import _ref_lists
+    ref = _ref_lists(want, O.ceil_k(0.03, og.nblk), 0.073)
+    bad, near, invalid = compare_lists(lut.cpu().numpy(), counts.cpu().numpy(), ref, 0.073)
+    density = counts.cpu().numpy().sum() / (counts.numel() * og.nblk)
+    say(f"  router lists: {len(bad)} mismatches outside near ties, {near} near ties, density {density:.4f}")
+    assert not bad and not invalid
