@@ -53,6 +53,12 @@ What it computes, step by step, in float64 (bfloat16 inputs convert exactly):
    (as keys or as queries).  The scores handed to the selection are log P_r,
    whose row softmax is P_r itself.
 
+8. Backward pass of the block-sparse attention (the pages require the kernel
+   to be differentiable for fine-tuning: SpargeAttention2 summary page, "Why
+   this implementation is trainable"): the gradients of step 5's outputs with
+   respect to Q, K and V, by the chain rule through the renormalised softmax
+   over each row's kept real keys (the mask itself carries no gradient).
+
 Readings where the pages are silent or garbled are listed in the repository's
 design notes; the ones this file depends on are repeated at each function.
 Every function here is pinned by the CPU tests (worked examples, closed forms,
@@ -458,3 +464,51 @@ def router_scores(qc: np.ndarray, kc_: np.ndarray, g: Geometry, R: Tuple[int, in
     pr = (per_query * pres[:, :, None]).sum(axis=-2) / pres.sum(axis=1)[:, None]
     with np.errstate(divide="ignore"):
         return np.log(pr)
+
+
+# ----------------------------------------------------------------------------
+# 8. backward pass of the block-sparse attention
+# ----------------------------------------------------------------------------
+def sparse_attention_backward(qc: np.ndarray, kc_: np.ndarray, vc: np.ndarray, doc: np.ndarray,
+                              lut: np.ndarray, counts: np.ndarray, g: Geometry,
+                              scale: Optional[float] = None):
+    """dQ, dK, dV [B, H, n_pad, d] of L = sum(dO * O) for step 5's O.
+
+    Per query block i with kept real keys y and its real queries x:
+    P = softmax(q k^T * scale) over those keys, O = P v, D_x = sum_c dO_xc O_xc,
+    dV_y += P^T dO, dP = dO v^T, dS = P * (dP - D), dQ_x = scale dS k,
+    dK_y += scale dS^T q.  Pad slots get zero gradients."""
+    B, H, n_pad, d = qc.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    real = real_slots(g)
+    blk = g.block
+    dq = np.zeros((B, H, n_pad, d))
+    dk = np.zeros((B, H, n_pad, d))
+    dv = np.zeros((B, H, n_pad, d))
+    for b in range(B):
+        for h in range(H):
+            q_h = np.asarray(qc[b, h], dtype=np.float64)
+            k_h = np.asarray(kc_[b, h], dtype=np.float64)
+            v_h = np.asarray(vc[b, h], dtype=np.float64)
+            do_h = np.asarray(doc[b, h], dtype=np.float64)
+            for i in range(g.nblk):
+                kept = list(lut[b, h, i, :counts[b, h, i]])
+                if not kept:
+                    continue
+                ys = np.concatenate([np.arange(j * blk, (j + 1) * blk) for j in kept])
+                ys = ys[real[ys]]
+                xs = np.arange(i * blk, (i + 1) * blk)
+                xs = xs[real[xs]]
+                s = (q_h[xs] @ k_h[ys].T) * scale
+                p = np.exp(s - s.max(axis=1, keepdims=True))
+                p /= p.sum(axis=1, keepdims=True)
+                o = p @ v_h[ys]
+                dO = do_h[xs]
+                D = (dO * o).sum(axis=1, keepdims=True)
+                dv[b, h, ys] += p.T @ dO
+                dp = dO @ v_h[ys].T
+                ds = p * (dp - D)
+                dq[b, h, xs] += scale * (ds @ k_h[ys])
+                dk[b, h, ys] += scale * (ds.T @ q_h[xs])
+    return dq, dk, dv

@@ -639,3 +639,73 @@ def test_router_with_token_pooling_is_pooled_token_attention():
         for j in range(g.nblk):
             want[i, j] = p[np.ix_(blk == i, blk == j)].sum(axis=1).mean()
     np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-15)
+
+
+# ----------------------------------------------------------------------------
+# backward pass: library autograd, finite differences, invariants
+# ----------------------------------------------------------------------------
+def test_backward_all_kept_equals_library_autograd():
+    wl, q, k, v = _tiny_inputs(grid=(5, 6, 7), heads=2, d=16, seed=5)
+    g = O.Geometry(*wl.grid)
+    rng = np.random.default_rng(41)
+    do = rng.standard_normal(q.shape)
+    qc, kc_, vc, doc = (O.reorder(x, g) for x in (q, k, v, do))
+    m = O.build_mask(qc, kc_, g, 1.0, 0.0)
+    dq, dk, dv = (O.unreorder(x, g) for x in O.sparse_attention_backward(qc, kc_, vc, doc, m.lut, m.counts, g))
+    tq, tk, tv = (torch.from_numpy(x).requires_grad_(True) for x in (q, k, v))
+    out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv)
+    out.backward(torch.from_numpy(do))
+    for got, want in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+        np.testing.assert_allclose(got, want.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_backward_matches_finite_differences_on_a_sparse_mask():
+    rng = np.random.default_rng(42)
+    g = O.Geometry(5, 6, 7)          # 8 blocks, partial cubes
+    d = 4
+    qc, kc_, vc = (O.reorder(rng.standard_normal((g.n_real, d)), g)[None, None] for _ in range(3))
+    doc = O.reorder(rng.standard_normal((g.n_real, d)), g)[None, None]
+    lut = np.zeros((1, 1, g.nblk, g.nblk), dtype=np.int32)
+    counts = np.zeros((1, 1, g.nblk), dtype=np.int32)
+    for i in range(g.nblk):
+        kept = np.sort(rng.choice(g.nblk, size=rng.integers(1, 4), replace=False))
+        lut[0, 0, i, :kept.size] = kept
+        counts[0, 0, i] = kept.size
+    grads = O.sparse_attention_backward(qc, kc_, vc, doc, lut, counts, g)
+
+    def loss(a, b, c):
+        o, _ = O.sparse_attention(a, b, c, lut, counts, g)
+        return float((o * doc).sum())
+    real_idx = np.nonzero(O.real_slots(g))[0]
+    eps = 1e-6
+    for which in range(3):
+        for slot in rng.choice(real_idx, size=6, replace=False):
+            for c in range(d):
+                args = [qc.copy(), kc_.copy(), vc.copy()]
+                args[which][0, 0, slot, c] += eps
+                up = loss(*args)
+                args[which][0, 0, slot, c] -= 2 * eps
+                down = loss(*args)
+                fd = (up - down) / (2 * eps)
+                assert abs(fd - grads[which][0, 0, slot, c]) < 1e-6 * max(1.0, abs(fd)), (which, slot, c)
+    pads = ~O.real_slots(g)
+    for gr in grads:
+        assert np.all(gr[0, 0, pads] == 0.0)
+
+
+def test_backward_invariants():
+    """Rows of P sum to one, so the value gradients add up to the output
+    gradients; softmax ignores a shift shared by all keys, so dQ does too."""
+    wl, q, k, v = _tiny_inputs(grid=(4, 8, 8), heads=2, d=16, seed=6)
+    g = O.Geometry(*wl.grid)
+    rng = np.random.default_rng(43)
+    do = rng.standard_normal(q.shape)
+    qc, kc_, vc, doc = (O.reorder(x, g) for x in (q, k, v, do))
+    m = O.build_mask(qc, kc_, g, 0.25, 0.5)
+    dq, dk, dv = O.sparse_attention_backward(qc, kc_, vc, doc, m.lut, m.counts, g)
+    # per row i: sum over its keys of dV equals sum over its queries of dO; with
+    # every row keeping at least one block, the totals match per head
+    np.testing.assert_allclose(dv.sum(axis=2), doc.sum(axis=2), rtol=1e-10, atol=1e-10)
+    shifted = kc_ + rng.standard_normal(kc_.shape[-1])[None, None, None, :] * O.real_slots(g)[None, None, :, None]
+    dq2, _, _ = O.sparse_attention_backward(qc, shifted, vc, doc, m.lut, m.counts, g)
+    np.testing.assert_allclose(dq2, dq, rtol=1e-9, atol=1e-10)
