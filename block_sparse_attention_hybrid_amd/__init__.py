@@ -36,6 +36,8 @@ EXPORTED = (
     "sparse_attn_select", "sparse_attn_mask_workspace_bytes",
     "sparse_attn_build_mask", "sparse_attn_fwd_workspace_bytes", "sparse_attn_fwd",
     "sparse_attn_coarse", "sparse_attn_router_pool", "sparse_attn_router_scores",
+    "sparse_attn_bwd_delta", "sparse_attn_transpose_workspace_bytes", "sparse_attn_transpose_lut",
+    "sparse_attn_bwd",
     "sparse_attn_last_error",
 )
 
@@ -63,6 +65,13 @@ def make_geom(batch: int, heads: int, frames: int, height: int, width: int,
     return Geom(batch, heads, frames, height, width, head_dim, *cube)
 
 
+class BwdArgs(ctypes.Structure):
+    """sa_bwd_args of the C ABI."""
+    _fields_ = [(n, ctypes.c_void_p) for n in ("q", "k", "v_qk", "q_v", "k_v", "do_qk", "do_v", "lse", "delta",
+                                               "lut", "counts")] + [("cap", ctypes.c_int32)] + \
+               [(n, ctypes.c_void_p) for n in ("lut_t", "counts_t")] + [("cap_t", ctypes.c_int32)]
+
+
 _lib = None
 _lock = threading.Lock()
 _vp, _i32, _i64, _sz, _f64, _f32 = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
@@ -84,6 +93,10 @@ _SIGS = {
     "sparse_attn_coarse": (_i32, [_vp, _vp, _vp, _GP, _vp]),
     "sparse_attn_router_pool": (_i32, [_vp, _vp, _GP, _i32, _i32, _i32, _vp]),
     "sparse_attn_router_scores": (_i32, [_vp, _vp, _vp, _f64, _GP, _i32, _i32, _i32, _vp]),
+    "sparse_attn_bwd_delta": (_i32, [_vp, _vp, _vp, _GP, _vp]),
+    "sparse_attn_transpose_workspace_bytes": (_sz, [_GP]),
+    "sparse_attn_transpose_lut": (_i32, [_vp, _vp, _i32, _vp, _vp, _i32, _GP, _vp, _sz, _vp]),
+    "sparse_attn_bwd": (_i32, [ctypes.POINTER(BwdArgs), _GP, _f32, _vp, _vp, _vp, _vp]),
     "sparse_attn_last_error": (ctypes.c_char_p, []),
 }
 
@@ -232,6 +245,30 @@ def sparse_attn_router_scores(qr, kr, scores, scale: float, g: Geom, sub=(2, 2, 
                                            int(sub[0]), int(sub[1]), int(sub[2]), _stream(stream, qr)))
 
 
+def sparse_attn_bwd_delta(oc, do_qk, delta, g: Geom, stream=None) -> None:
+    _check(lib().sparse_attn_bwd_delta(_ptr(oc, torch.bfloat16, "oc"), _ptr(do_qk, torch.bfloat16, "do_qk"),
+                                       _ptr(delta, torch.float32, "delta"), ctypes.byref(g), _stream(stream, oc)))
+
+
+def sparse_attn_transpose_workspace_bytes(g: Geom) -> int:
+    return int(lib().sparse_attn_transpose_workspace_bytes(ctypes.byref(g)))
+
+
+def sparse_attn_transpose_lut(lut, counts, cap: int, lut_t, counts_t, cap_t: int, g: Geom, workspace,
+                              stream=None) -> None:
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().sparse_attn_transpose_lut(_ptr(lut, torch.int32, "lut"), _ptr(counts, torch.int32, "counts"),
+                                           int(cap), _ptr(lut_t, torch.int32, "lut_t"),
+                                           _ptr(counts_t, torch.int32, "counts_t"), int(cap_t), ctypes.byref(g),
+                                           _ptr(workspace, None, "workspace"), ws_bytes, _stream(stream, lut)))
+
+
+def sparse_attn_bwd(args: BwdArgs, g: Geom, scale: float, dq, dk, dv, stream=None, like=None) -> None:
+    _check(lib().sparse_attn_bwd(ctypes.byref(args), ctypes.byref(g), float(scale),
+                                 _ptr(dq, torch.bfloat16, "dq"), _ptr(dk, torch.bfloat16, "dk"),
+                                 _ptr(dv, torch.bfloat16, "dv"), _stream(stream, dq)))
+
+
 def sparse_attn_last_error() -> str:
     return lib().sparse_attn_last_error().decode(errors="replace")
 
@@ -349,6 +386,37 @@ def router_mask(qc, kc, g: Geom, k_frac: float, p: float, sub=(2, 2, 2), row_bud
     sparse_attn_router_scores(qr, kr, scores, 0.0, g, sub, stream)
     sparse_attn_select(scores, g, k_frac, p, row_budget, lut, counts, cap, stream)
     return lut, counts, scores
+
+
+def transpose_lut(lut, counts, g: Geom, stream=None):
+    """For every key block, the ascending list of query blocks that keep it."""
+    nblk, _, _ = sparse_attn_geometry(g)
+    lut_t = _empty((g.batch, g.heads, nblk, nblk), torch.int32, lut)
+    counts_t = _empty((g.batch, g.heads, nblk), torch.int32, lut)
+    ws = torch.empty(max(sparse_attn_transpose_workspace_bytes(g), 256), dtype=torch.uint8, device=lut.device)
+    sparse_attn_transpose_lut(lut, counts, lut.shape[-1], lut_t, counts_t, nblk, g, ws, stream)
+    return lut_t, counts_t
+
+
+def backward(q, k, v, do, oc, lse_c, lut, counts, g: Geom, scale: float = 0.0, stream=None):
+    """Gradients of the block-sparse attention from row-major q, k, v and dO and
+    the forward's cube-major O, LSE and lists.  Returns cube-major slot-major
+    (dq, dk, dv) bf16; unreorder(x, None, g) brings each to token order."""
+    QKL, VL = SA_LAYOUT_QK, SA_LAYOUT_V
+    lay = {}
+    for name, x, layout in (("q", q, QKL), ("k", k, QKL), ("v_qk", v, QKL), ("q_v", q, VL), ("k_v", k, VL),
+                            ("do_qk", do, QKL), ("do_v", do, VL)):
+        lay[name] = reorder(x, g, layout, stream)
+    _, _, n_pad = sparse_attn_geometry(g)
+    delta = _empty((g.batch, g.heads, n_pad), torch.float32, q)
+    sparse_attn_bwd_delta(oc, lay["do_qk"], delta, g, stream)
+    lut_t, counts_t = transpose_lut(lut, counts, g, stream)
+    args = BwdArgs(*(lay[n].data_ptr() for n in ("q", "k", "v_qk", "q_v", "k_v", "do_qk", "do_v")),
+                   lse_c.data_ptr(), delta.data_ptr(), lut.data_ptr(), counts.data_ptr(), lut.shape[-1],
+                   lut_t.data_ptr(), counts_t.data_ptr(), lut_t.shape[-1])
+    dq, dk, dv = (_empty(tuple(oc.shape), torch.bfloat16, oc) for _ in range(3))
+    sparse_attn_bwd(args, g, scale, dq, dk, dv, stream)
+    return dq, dk, dv
 
 
 def default_scale(head_dim: int) -> float:

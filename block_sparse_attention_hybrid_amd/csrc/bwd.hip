@@ -1,0 +1,416 @@
+// Backward pass of the block-sparse attention (gfx950).
+//
+// SpargeAttention2 summary page, "Why this implementation is trainable": the
+// kernel must carry gradients through the kept blocks (the mask itself has
+// none).  For query block i with kept key blocks j, with P recomputed from the
+// saved log-sum-exp,
+//   D = rowsum(dO * O),  dP = dO V^T,  dS = P * (dP - D),
+//   dV_j += P^T dO,  dK_j += scale dS^T Q,  dQ_i += scale dS K.
+// Two kernels avoid atomics and keep the result deterministic:
+//   * dq: one wavefront per query block walks the block's kept list (as the
+//     forward does) and accumulates dQ^T = K^T dS^T in registers;
+//   * dkv: one workgroup per key block walks the transposed list (the query
+//     blocks that keep it, from sparse_attn_transpose_lut); each of its two
+//     waves owns 32 of the block's keys and accumulates dV^T = dO^T P and
+//     dK^T = Q^T dS in registers, reading the query block's operands from
+//     LDS, where the workgroup stages them once.
+// Operand orders follow the forward kernel: every MFMA operand is one 16-byte
+// chunk per lane of a QK- or V-layout block (sa_layout.h), and the rows fed
+// to the first product are permuted (sigma) so that a lane's accumulator
+// registers hold 8 consecutive tokens for each 16-token step of the second
+// product, which then takes them straight from registers as bf16 pairs.
+#include "sa_launch.h"
+#include "sa_layout.h"
+
+#include <math.h>
+
+namespace sa {
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Row r of a 32-row MFMA tile is fed token sigma(r) (see the forward kernel).
+__device__ __forceinline__ int sigma32(int r) {
+  return 16 * (r >> 4) + 8 * ((r >> 2) & 1) + 4 * ((r >> 3) & 1) + (r & 3);
+}
+
+// D = rowsum(dO * O) of every slot: one wavefront per block, lane = slot.
+__global__ __launch_bounds__(64) void bwd_delta_kernel(const u32x4* __restrict__ oc,
+                                                       const u32x4* __restrict__ do_qk,
+                                                       float* __restrict__ delta, Geom g) {
+  const int i = blockIdx.x;
+  const long long bh = blockIdx.y;
+  const int s = threadIdx.x, d = g.d, cpr = d / 8;
+  const long long base = (bh * g.n_pad + (long long)i * kBlock) * cpr;
+  float acc = 0.f;
+  for (int c8 = 0; c8 < cpr; ++c8) {
+    const u32x4 o = oc[base + (long long)s * cpr + c8];
+    const u32x4 w = do_qk[base + qk_offset(s, 8 * c8, d) / 8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc += lo_bf16(o[e]) * lo_bf16(w[e]) + hi_bf16(o[e]) * hi_bf16(w[e]);
+  }
+  delta[bh * g.n_pad + (long long)i * kBlock + s] = acc;
+}
+
+__global__ void zero_words_kernel(uint32_t* __restrict__ p, long long n) {
+  for (long long x = blockIdx.x * (long long)blockDim.x + threadIdx.x; x < n; x += (long long)gridDim.x * blockDim.x)
+    p[x] = 0u;
+}
+
+// Bit i of row j of a head's bitmap: query block i keeps key block j.
+__global__ __launch_bounds__(64) void lut_mark_kernel(const int32_t* __restrict__ lut,
+                                                      const int32_t* __restrict__ counts, int cap,
+                                                      uint32_t* __restrict__ bits, Geom g, int words) {
+  const long long row = blockIdx.x;
+  const long long bh = row / g.nblk;
+  const int i = (int)(row - bh * g.nblk);
+  int cnt = counts[row];
+  cnt = cnt < 0 ? 0 : (cnt > cap ? cap : cnt);
+  const int32_t* l = lut + row * cap;
+  for (int e = threadIdx.x; e < cnt; e += 64) {
+    const int j = l[e];
+    if (j >= 0 && j < g.nblk) atomicOr(&bits[(bh * g.nblk + j) * words + (i >> 5)], 1u << (i & 31));
+  }
+}
+
+// Ascending list of the query blocks that keep key block j (one wave per j).
+__global__ __launch_bounds__(64) void lut_gather_kernel(const uint32_t* __restrict__ bits,
+                                                        int32_t* __restrict__ lut_t,
+                                                        int32_t* __restrict__ counts_t, int cap_t, int words) {
+  const long long col = blockIdx.x;
+  const int lane = threadIdx.x;
+  const uint32_t* wrow = bits + col * words;
+  int32_t* out = lut_t + col * cap_t;
+  int written = 0;
+  for (int w0 = 0; w0 < words; w0 += 64) {
+    const int w = w0 + lane;
+    uint32_t word = w < words ? wrow[w] : 0u;
+    const int c = __popc(word);
+    int incl = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += t;
+    }
+    int pos = written + incl - c;
+    while (word) {
+      const int b = __ffs(word) - 1;
+      word &= word - 1u;
+      if (pos < cap_t) out[pos] = w * 32 + b;
+      ++pos;
+    }
+    written += __shfl(incl, 63, 64);
+  }
+  if (lane == 0) counts_t[col] = written;
+}
+
+// Log2-domain LSE of a query slot: +inf for slots without attention (pad
+// slots, empty rows), so that their recomputed probabilities are 0.
+__device__ __forceinline__ float lse2_of(float lse) { return lse > -INFINITY ? lse * kLog2e : INFINITY; }
+
+template <int D>
+__global__ __launch_bounds__(64) void bwd_dq_kernel(const u32x4* __restrict__ q, const u32x4* __restrict__ k,
+                                                    const u32x4* __restrict__ v_qk, const u32x4* __restrict__ k_v,
+                                                    const u32x4* __restrict__ do_qk, const float* __restrict__ lse,
+                                                    const float* __restrict__ delta, const int32_t* __restrict__ lut,
+                                                    const int32_t* __restrict__ counts, int cap, Geom g,
+                                                    float sc_log2, float scale, bf16* __restrict__ dq) {
+  constexpr int NDS = D / 16, NDT = D / 32, BLK = 64 * D / 8;
+  const int i = blockIdx.x;
+  const long long bh = blockIdx.y;
+  const long long row = bh * g.nblk + i;
+  const int lane = threadIdx.x, hf = lane >> 5, r = lane & 31;
+  const int kpos = hf * 32 + sigma32(r);
+  const long long head = bh * (long long)g.nblk * BLK;
+
+  __shared__ u32x4 qlds[2 * NDS * 64];
+  __shared__ u32x4 dolds[2 * NDS * 64];
+  const u32x4* qb = q + head + (long long)i * BLK;
+  const u32x4* dob = do_qk + head + (long long)i * BLK;
+#pragma unroll
+  for (int c = 0; c < 2 * NDS; ++c) {
+    qlds[c * 64 + lane] = qb[c * 64 + lane];
+    dolds[c * 64 + lane] = dob[c * 64 + lane];
+  }
+  __syncthreads();
+  float l2[2], dl[2];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const long long slot = bh * g.n_pad + (long long)i * kBlock + 32 * qt + r;
+    l2[qt] = lse2_of(lse[slot]);
+    dl[qt] = delta[slot];
+  }
+
+  f32x16 acc[NDT][2];
+#pragma unroll
+  for (int t = 0; t < NDT; ++t)
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[t][qt][e] = 0.f;
+
+  int count = counts[row];
+  count = count < 0 ? 0 : (count > cap ? cap : count);
+  const int32_t* lrow = lut + row * cap;
+  for (int it = 0; it < count; ++it) {
+    const int j0 = lrow[it];
+    const bool ok = j0 >= 0 && j0 < g.nblk;
+    const int j = ok ? j0 : 0;
+    // this lane's 32 key bits: register e of tile kt <-> key 32 kt + 16 (e / 8) + 8 hf + e % 8
+    const uint64_t real = ok ? block_real_mask(g, j) : 0ull;
+    const uint32_t lm = (uint32_t)((real >> (8 * hf)) & 0xffu) | ((uint32_t)((real >> (16 + 8 * hf)) & 0xffu) << 8) |
+                        ((uint32_t)((real >> (32 + 8 * hf)) & 0xffu) << 16) |
+                        ((uint32_t)((real >> (48 + 8 * hf)) & 0xffu) << 24);
+    const u32x4* kb = k + head + (long long)j * BLK;
+    const u32x4* vb = v_qk + head + (long long)j * BLK;
+    const u32x4* kvb = k_v + head + (long long)j * BLK;
+    u32x4 kreg[2][NDS], vreg[2][NDS];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) {
+        kreg[kt][ds] = kb[(kt * NDS + ds) * 64 + kpos];
+        vreg[kt][ds] = vb[(kt * NDS + ds) * 64 + kpos];
+      }
+    // phase 1: dS^T of both query halves (bf16 pairs); phase 2: dQ^T += K^T dS^T
+    uint32_t dsw[2][2][8];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      f32x16 st[2], dpt[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) st[kt][e] = dpt[kt][e] = 0.f;
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) {
+        const u32x4 qa = qlds[(qt * NDS + ds) * 64 + lane];
+        const u32x4 da = dolds[(qt * NDS + ds) * 64 + lane];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kreg[kt][ds]), as_bf16x8(qa), st[kt], 0, 0, 0);
+          dpt[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vreg[kt][ds]), as_bf16x8(da), dpt[kt], 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int e = 0; e < 16; e += 2) {
+          float v2[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const bool real = (lm >> (16 * kt + e + u)) & 1u;
+            const float p = real ? __builtin_amdgcn_exp2f(fmaf(st[kt][e + u], sc_log2, -l2[qt])) : 0.f;
+            v2[u] = p * (dpt[kt][e + u] - dl[qt]);
+          }
+          dsw[qt][kt][e >> 1] = pack_bf16x2(v2[0], v2[1]);
+        }
+    }
+    u32x4 kvreg[NDT][4];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) kvreg[dt][ks] = kvb[(dt * 4 + ks) * 64 + lane];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+      for (int step = 0; step < 4 * NDT; ++step) {
+        const int ks = step / NDT, dt = step % NDT;
+        const int kt = ks >> 1, o4 = 4 * (ks & 1);
+        const u32x4 bw = {dsw[qt][kt][o4], dsw[qt][kt][o4 + 1], dsw[qt][kt][o4 + 2], dsw[qt][kt][o4 + 3]};
+        acc[dt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kvreg[dt][ks]), as_bf16x8(bw), acc[dt][qt],
+                                                              0, 0, 0);
+      }
+  }
+  bf16* ob = dq + (bh * g.n_pad + (long long)i * 64) * D;
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    bf16* orow = ob + (long long)(32 * qt + r) * D;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const u32x2 v = {pack_bf16x2(acc[dt][qt][4 * a] * scale, acc[dt][qt][4 * a + 1] * scale),
+                         pack_bf16x2(acc[dt][qt][4 * a + 2] * scale, acc[dt][qt][4 * a + 3] * scale)};
+        *reinterpret_cast<u32x2*>(orow + 32 * dt + 8 * a + 4 * hf) = v;
+      }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(128) void bwd_dkv_kernel(const u32x4* __restrict__ q, const u32x4* __restrict__ k,
+                                                      const u32x4* __restrict__ v_qk, const u32x4* __restrict__ q_v,
+                                                      const u32x4* __restrict__ do_qk,
+                                                      const u32x4* __restrict__ do_v, const float* __restrict__ lse,
+                                                      const float* __restrict__ delta,
+                                                      const int32_t* __restrict__ lut_t,
+                                                      const int32_t* __restrict__ counts_t, int cap_t, Geom g,
+                                                      float sc_log2, float scale, bf16* __restrict__ dk,
+                                                      bf16* __restrict__ dv) {
+  constexpr int NDS = D / 16, NDT = D / 32, BLK = 64 * D / 8;
+  const int j = blockIdx.x;
+  const long long bh = blockIdx.y;
+  const long long col = bh * g.nblk + j;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, hf = lane >> 5, r = lane & 31;
+  const int qpos = hf * 32 + sigma32(r);
+  const long long head = bh * (long long)g.nblk * BLK;
+
+  __shared__ u32x4 qs[2 * NDS * 64], dos[2 * NDS * 64], qvs[NDT * 4 * 64], dovs[NDT * 4 * 64];
+  __shared__ float l2s[kBlock], dls[kBlock];
+
+  // this wave's 32 keys (B operands, chunk t32 = w) and whether this lane's key is real
+  u32x4 kreg[NDS], vreg[NDS];
+  const u32x4* kb = k + head + (long long)j * BLK;
+  const u32x4* vb = v_qk + head + (long long)j * BLK;
+#pragma unroll
+  for (int ds = 0; ds < NDS; ++ds) {
+    kreg[ds] = kb[(w * NDS + ds) * 64 + lane];
+    vreg[ds] = vb[(w * NDS + ds) * 64 + lane];
+  }
+  const bool key_real = slot_token(g, j, 32 * w + r) >= 0;
+
+  f32x16 adk[NDT], adv[NDT];
+#pragma unroll
+  for (int t = 0; t < NDT; ++t)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) adk[t][e] = adv[t][e] = 0.f;
+
+  int count = counts_t[col];
+  count = count < 0 ? 0 : (count > cap_t ? cap_t : count);
+  const int32_t* list = lut_t + col * cap_t;
+  for (int it = 0; it < count; ++it) {
+    const int i0 = list[it];
+    const int i = (i0 >= 0 && i0 < g.nblk) ? i0 : -1;
+    __syncthreads();   // the previous query block's operands are no longer read
+    if (i >= 0) {
+      const long long ob = head + (long long)i * BLK;
+      for (int u = threadIdx.x; u < 2 * NDS * 64; u += 128) {
+        qs[u] = q[ob + u];
+        dos[u] = do_qk[ob + u];
+        qvs[u] = q_v[ob + u];
+        dovs[u] = do_v[ob + u];
+      }
+      if (threadIdx.x < kBlock) {
+        const long long slot = bh * g.n_pad + (long long)i * kBlock + threadIdx.x;
+        l2s[threadIdx.x] = lse2_of(lse[slot]);
+        dls[threadIdx.x] = delta[slot];
+      }
+    }
+    __syncthreads();
+    if (i < 0) continue;   // uniform across the workgroup
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) {
+      f32x16 s, dp;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[e] = dp[e] = 0.f;
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) {
+        const u32x4 qa = qs[(qq * NDS + ds) * 64 + qpos];
+        const u32x4 da = dos[(qq * NDS + ds) * 64 + qpos];
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qa), as_bf16x8(kreg[ds]), s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(da), as_bf16x8(vreg[ds]), dp, 0, 0, 0);
+      }
+      // register e <-> query 32 qq + 16 (e / 8) + 8 hf + e % 8; the lane's column is its key
+      uint32_t pw[8], dsw[8];
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) {
+        float pv[2], sv[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int qi = 32 * qq + 16 * ((e + u) >> 3) + 8 * hf + ((e + u) & 7);
+          const float p = key_real ? __builtin_amdgcn_exp2f(fmaf(s[e + u], sc_log2, -l2s[qi])) : 0.f;
+          pv[u] = p;
+          sv[u] = p * (dp[e + u] - dls[qi]);
+        }
+        pw[e >> 1] = pack_bf16x2(pv[0], pv[1]);
+        dsw[e >> 1] = pack_bf16x2(sv[0], sv[1]);
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int ks = 2 * qq + kk;
+        const u32x4 bp = {pw[4 * kk], pw[4 * kk + 1], pw[4 * kk + 2], pw[4 * kk + 3]};
+        const u32x4 bs = {dsw[4 * kk], dsw[4 * kk + 1], dsw[4 * kk + 2], dsw[4 * kk + 3]};
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          adv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(dovs[(dt * 4 + ks) * 64 + lane]), as_bf16x8(bp),
+                                                            adv[dt], 0, 0, 0);
+          adk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qvs[(dt * 4 + ks) * 64 + lane]), as_bf16x8(bs),
+                                                            adk[dt], 0, 0, 0);
+        }
+      }
+    }
+  }
+  const long long orow = (bh * g.n_pad + (long long)j * 64 + 32 * w + r) * D;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const u32x2 kv2 = {pack_bf16x2(adk[dt][4 * a] * scale, adk[dt][4 * a + 1] * scale),
+                         pack_bf16x2(adk[dt][4 * a + 2] * scale, adk[dt][4 * a + 3] * scale)};
+      const u32x2 vv2 = {pack_bf16x2(adv[dt][4 * a], adv[dt][4 * a + 1]),
+                         pack_bf16x2(adv[dt][4 * a + 2], adv[dt][4 * a + 3])};
+      *reinterpret_cast<u32x2*>(dk + orow + 32 * dt + 8 * a + 4 * hf) = kv2;
+      *reinterpret_cast<u32x2*>(dv + orow + 32 * dt + 8 * a + 4 * hf) = vv2;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_bwd_delta(const void* oc, const void* do_qk, float* delta, const Geom& g, hipStream_t s) {
+  dim3 grid(g.nblk, g.batch * g.heads);
+  bwd_delta_kernel<<<grid, 64, 0, s>>>(static_cast<const u32x4*>(oc), static_cast<const u32x4*>(do_qk), delta, g);
+  return hipGetLastError();
+}
+
+size_t transpose_workspace_bytes(const Geom& g) {
+  const size_t words = (size_t)(g.nblk + 31) / 32;
+  return (size_t)g.batch * g.heads * g.nblk * words * sizeof(uint32_t);
+}
+
+hipError_t launch_transpose_lut(const int32_t* lut, const int32_t* counts, int cap, int32_t* lut_t,
+                                int32_t* counts_t, int cap_t, const Geom& g, void* workspace, hipStream_t s) {
+  const int words = (g.nblk + 31) / 32;
+  const long long rows = (long long)g.batch * g.heads * g.nblk;
+  uint32_t* bits = static_cast<uint32_t*>(workspace);
+  const long long n = rows * words;
+  const long long blocks = (n + 255) / 256;
+  zero_words_kernel<<<(unsigned)(blocks < 65536 ? blocks : 65536), 256, 0, s>>>(bits, n);
+  lut_mark_kernel<<<(unsigned)rows, 64, 0, s>>>(lut, counts, cap, bits, g, words);
+  lut_gather_kernel<<<(unsigned)rows, 64, 0, s>>>(bits, lut_t, counts_t, cap_t, words);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd(const BwdArgs& a, const Geom& g, float scale, void* dq, void* dk, void* dv, hipStream_t s) {
+  const float sc_log2 = scale * kLog2e;
+  dim3 grid(g.nblk, g.batch * g.heads);
+  auto U = [](const void* p) { return static_cast<const u32x4*>(p); };
+  if (g.d == 128) {
+    bwd_dq_kernel<128><<<grid, 64, 0, s>>>(U(a.q), U(a.k), U(a.v_qk), U(a.k_v), U(a.do_qk), a.lse, a.delta, a.lut,
+                                           a.counts, a.cap, g, sc_log2, scale, static_cast<bf16*>(dq));
+    bwd_dkv_kernel<128><<<grid, 128, 0, s>>>(U(a.q), U(a.k), U(a.v_qk), U(a.q_v), U(a.do_qk), U(a.do_v), a.lse,
+                                             a.delta, a.lut_t, a.counts_t, a.cap_t, g, sc_log2, scale,
+                                             static_cast<bf16*>(dk), static_cast<bf16*>(dv));
+  } else {
+    bwd_dq_kernel<64><<<grid, 64, 0, s>>>(U(a.q), U(a.k), U(a.v_qk), U(a.k_v), U(a.do_qk), a.lse, a.delta, a.lut,
+                                          a.counts, a.cap, g, sc_log2, scale, static_cast<bf16*>(dq));
+    bwd_dkv_kernel<64><<<grid, 128, 0, s>>>(U(a.q), U(a.k), U(a.v_qk), U(a.q_v), U(a.do_qk), U(a.do_v), a.lse,
+                                            a.delta, a.lut_t, a.counts_t, a.cap_t, g, sc_log2, scale,
+                                            static_cast<bf16*>(dk), static_cast<bf16*>(dv));
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sa

@@ -237,6 +237,85 @@ int32_t sparse_attn_router_scores(const double* qr, const double* kr, double* sc
   return hip_status(sa::launch_router(qr, kr, scores, scale, d, rt, rh, rw, (hipStream_t)stream), "router launch");
 }
 
+int32_t sparse_attn_bwd_delta(const void* oc, const void* do_qk, float* delta, const sa_geom* g, void* stream) {
+  sa::Geom d;
+  SA_TRY(make_geom(g, d));
+  SA_TRY(check_ptr(oc, 16, "oc"));
+  SA_TRY(check_ptr(do_qk, 16, "do_qk"));
+  SA_TRY(check_ptr(delta, 4, "delta"));
+  return hip_status(sa::launch_bwd_delta(oc, do_qk, delta, d, (hipStream_t)stream), "bwd_delta launch");
+}
+
+size_t sparse_attn_transpose_workspace_bytes(const sa_geom* g) {
+  sa::Geom d;
+  if (make_geom(g, d) != SA_OK) return 0;
+  return sa::transpose_workspace_bytes(d);
+}
+
+int32_t sparse_attn_transpose_lut(const int32_t* lut, const int32_t* counts, int32_t cap, int32_t* lut_t,
+                                  int32_t* counts_t, int32_t cap_t, const sa_geom* g, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  sa::Geom d;
+  SA_TRY(make_geom(g, d));
+  SA_TRY(check_ptr(lut, 4, "lut"));
+  SA_TRY(check_ptr(counts, 4, "counts"));
+  SA_TRY(check_ptr(lut_t, 4, "lut_t"));
+  SA_TRY(check_ptr(counts_t, 4, "counts_t"));
+  SA_TRY(check_ptr(workspace, 256, "workspace"));
+  if (cap < 1) return fail(SA_ERR_INVALID_ARG, "cap must be >= 1");
+  if (cap_t < d.nblk) return fail(SA_ERR_CAPACITY, "cap_t %d is below nblk %d", cap_t, d.nblk);
+  if (workspace_bytes < sa::transpose_workspace_bytes(d))
+    return fail(SA_ERR_CAPACITY, "workspace of %zu bytes is below the %zu needed", workspace_bytes,
+                sa::transpose_workspace_bytes(d));
+  return hip_status(sa::launch_transpose_lut(lut, counts, cap, lut_t, counts_t, cap_t, d, workspace,
+                                             (hipStream_t)stream),
+                    "transpose_lut launch");
+}
+
+int32_t sparse_attn_bwd(const sa_bwd_args* a, const sa_geom* g, float scale, void* dq, void* dk, void* dv,
+                        void* stream) {
+  sa::Geom d;
+  SA_TRY(make_geom(g, d));
+  if (a == nullptr) return fail(SA_ERR_INVALID_ARG, "args pointer is NULL");
+  SA_TRY(check_ptr(a->q, 16, "q"));
+  SA_TRY(check_ptr(a->k, 16, "k"));
+  SA_TRY(check_ptr(a->v_qk, 16, "v_qk"));
+  SA_TRY(check_ptr(a->q_v, 16, "q_v"));
+  SA_TRY(check_ptr(a->k_v, 16, "k_v"));
+  SA_TRY(check_ptr(a->do_qk, 16, "do_qk"));
+  SA_TRY(check_ptr(a->do_v, 16, "do_v"));
+  SA_TRY(check_ptr(a->lse, 4, "lse"));
+  SA_TRY(check_ptr(a->delta, 4, "delta"));
+  SA_TRY(check_ptr(a->lut, 4, "lut"));
+  SA_TRY(check_ptr(a->counts, 4, "counts"));
+  SA_TRY(check_ptr(a->lut_t, 4, "lut_t"));
+  SA_TRY(check_ptr(a->counts_t, 4, "counts_t"));
+  SA_TRY(check_ptr(dq, 16, "dq"));
+  SA_TRY(check_ptr(dk, 16, "dk"));
+  SA_TRY(check_ptr(dv, 16, "dv"));
+  if (a->cap < 1 || a->cap_t < 1) return fail(SA_ERR_INVALID_ARG, "cap and cap_t must be >= 1");
+  if (dq == dk || dq == dv || dk == dv) return fail(SA_ERR_INVALID_ARG, "dq, dk and dv must not overlap");
+  if (!std::isfinite(scale)) return fail(SA_ERR_INVALID_ARG, "scale must be finite");
+  if (scale <= 0.f) scale = 1.f / std::sqrt((float)d.d);
+  sa::BwdArgs b;
+  b.q = a->q;
+  b.k = a->k;
+  b.v_qk = a->v_qk;
+  b.q_v = a->q_v;
+  b.k_v = a->k_v;
+  b.do_qk = a->do_qk;
+  b.do_v = a->do_v;
+  b.lse = a->lse;
+  b.delta = a->delta;
+  b.lut = a->lut;
+  b.counts = a->counts;
+  b.cap = a->cap;
+  b.lut_t = a->lut_t;
+  b.counts_t = a->counts_t;
+  b.cap_t = a->cap_t;
+  return hip_status(sa::launch_bwd(b, d, scale, dq, dk, dv, (hipStream_t)stream), "bwd launch");
+}
+
 int32_t sparse_attn_block_scores(const double* qbar, const double* kbar, double* scores, double scale,
                                  const sa_geom* g, void* stream) {
   sa::Geom d;

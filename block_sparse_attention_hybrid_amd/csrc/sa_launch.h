@@ -28,6 +28,20 @@ size_t fwd_workspace_bytes(const Geom& g);
 hipError_t launch_router_pool(const void* xc, double* xr, const Geom& g, int rt, int rh, int rw, hipStream_t s);
 hipError_t launch_router(const double* qr, const double* kr, double* scores, double scale, const Geom& g,
                          int rt, int rh, int rw, hipStream_t s);
+// Operands of the backward pass (device pointers, see sparse_attn_bwd).
+struct BwdArgs {
+  const void *q, *k, *v_qk, *q_v, *k_v, *do_qk, *do_v;
+  const float *lse, *delta;
+  const int32_t *lut, *counts;
+  int cap;
+  const int32_t *lut_t, *counts_t;
+  int cap_t;
+};
+hipError_t launch_bwd_delta(const void* oc, const void* do_qk, float* delta, const Geom& g, hipStream_t s);
+size_t transpose_workspace_bytes(const Geom& g);
+hipError_t launch_transpose_lut(const int32_t* lut, const int32_t* counts, int cap, int32_t* lut_t,
+                                int32_t* counts_t, int cap_t, const Geom& g, void* workspace, hipStream_t s);
+hipError_t launch_bwd(const BwdArgs& a, const Geom& g, float scale, void* dq, void* dk, void* dv, hipStream_t s);
 hipError_t launch_coarse(const double* scores, const double* vbar, double* oc, const Geom& g, hipStream_t s);
 
 }  // namespace sa

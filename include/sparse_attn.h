@@ -10,6 +10,7 @@
  *   fwd          block-sparse attention over the kept blocks -> O, LSE
  *   coarse       block-level attention on pooled Q, K, V (coarse branch)
  *   router       fine-grained router scores (sub-cube pooling, G x G pooling)
+ *   bwd          gradients of the block-sparse attention (dQ, dK, dV)
  *   unreorder    cube-major O (and LSE) -> row-major tokens
  *
  * Conventions shared by every entry point
@@ -199,6 +200,67 @@ int32_t sparse_attn_router_scores(const double* qr, const double* kr,
                                   double* scores, double scale,
                                   const sa_geom* g, int32_t rt, int32_t rh,
                                   int32_t rw, void* stream);
+
+/* ---- backward pass of the block-sparse attention ------------------------
+ * [SA2] "Why this implementation is trainable": gradients flow through the
+ * kept blocks (the mask carries none).  For query block i and its kept key
+ * blocks, with P recomputed from the forward's LSE:
+ *   D = rowsum(dO * O), dP = dO V^T, dS = P * (dP - D),
+ *   dV += P^T dO, dK += scale dS^T Q, dQ += scale dS K.
+ * The caller runs sparse_attn_bwd_delta, sparse_attn_transpose_lut and then
+ * sparse_attn_bwd.  dQ is accumulated per query block along the kept list,
+ * dK and dV per key block along the transposed list, without atomics, so the
+ * results are deterministic. */
+
+/* D = rowsum(dO * O) per slot.
+ *   oc     [batch, heads, n_pad, head_dim] bf16, slot-major (sparse_attn_fwd) (input)
+ *   do_qk  [batch, heads, n_pad, head_dim] bf16 dO in SA_LAYOUT_QK          (input)
+ *   delta  [batch, heads, n_pad] float32                                  (output) */
+int32_t sparse_attn_bwd_delta(const void* oc, const void* do_qk, float* delta,
+                              const sa_geom* g, void* stream);
+
+/* Bytes of workspace sparse_attn_transpose_lut needs (a bitmap of
+ * nblk x ceil(nblk/32) words per head).  0 on an invalid geometry. */
+size_t sparse_attn_transpose_workspace_bytes(const sa_geom* g);
+
+/* Transposed kept lists: for every key block j, the query blocks whose list
+ * holds j, in ascending order.
+ *   lut, counts, cap      forward lists as sparse_attn_select writes them (inputs)
+ *   lut_t [batch, heads, nblk, cap_t] int32, counts_t [batch, heads, nblk] (outputs)
+ * cap_t must be >= nblk (SA_ERR_CAPACITY otherwise); the workspace is
+ * cleared by the call itself. */
+int32_t sparse_attn_transpose_lut(const int32_t* lut, const int32_t* counts,
+                                  int32_t cap, int32_t* lut_t, int32_t* counts_t,
+                                  int32_t cap_t, const sa_geom* g,
+                                  void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
+/* Operands of sparse_attn_bwd (device pointers).  Tensors are cube-major
+ * [batch, heads, n_pad, head_dim] bf16 in the layout named. */
+typedef struct sa_bwd_args {
+  const void* q;         /* queries, SA_LAYOUT_QK */
+  const void* k;         /* keys, SA_LAYOUT_QK */
+  const void* v_qk;      /* values, SA_LAYOUT_QK */
+  const void* q_v;       /* queries, SA_LAYOUT_V */
+  const void* k_v;       /* keys, SA_LAYOUT_V */
+  const void* do_qk;     /* output gradient, SA_LAYOUT_QK */
+  const void* do_v;      /* output gradient, SA_LAYOUT_V */
+  const float* lse;      /* [batch, heads, n_pad] natural-log LSE of sparse_attn_fwd */
+  const float* delta;    /* [batch, heads, n_pad] from sparse_attn_bwd_delta */
+  const int32_t* lut;    /* forward lists [batch, heads, nblk, cap] */
+  const int32_t* counts;
+  int32_t cap;
+  const int32_t* lut_t;  /* transposed lists [batch, heads, nblk, cap_t] */
+  const int32_t* counts_t;
+  int32_t cap_t;
+} sa_bwd_args;
+
+/* Gradients of sparse_attn_fwd's O with respect to Q, K and V.
+ *   dq, dk, dv [batch, heads, n_pad, head_dim] bf16, slot-major like oc
+ *   (pad slots get zeros; sparse_attn_unreorder brings them to token order)
+ * scale must be the forward's (<= 0 selects 1/sqrt(head_dim)). */
+int32_t sparse_attn_bwd(const sa_bwd_args* args, const sa_geom* g, float scale,
+                        void* dq, void* dk, void* dv, void* stream);
 
 /* Hybrid Top-k U Top-p selection, [SA2] "The Hybrid Top-k+Top-p Masking Rule"
  * (Eq. 9), producing index lists as [VSA] "Kernel Implementation" describes

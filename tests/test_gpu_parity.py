@@ -346,3 +346,40 @@ def test_router_matches_oracle(case, sub):
     bad, near, invalid = compare_lists(lut.cpu().numpy(), counts.cpu().numpy(), ref, case["p"])
     say(f"  router {sub}: {len(bad)} mismatched rows, {near} near ties ({len(invalid)} invalid)")
     assert not bad and not invalid
+
+
+def test_transpose_lut_exact(case):
+    g, og, ref = case["g"], case["og"], case["ref_mask"]
+    lut_t, counts_t = sa.transpose_lut(torch.from_numpy(ref.lut).to(DEV), torch.from_numpy(ref.counts).to(DEV), g)
+    torch.cuda.synchronize()
+    ct, lt = counts_t.cpu().numpy(), lut_t.cpu().numpy()
+    B, H, n = ref.counts.shape
+    for b in range(B):
+        for h in range(H):
+            want = [[] for _ in range(n)]
+            for i in range(n):
+                for j in ref.lut[b, h, i, :ref.counts[b, h, i]]:
+                    want[j].append(i)
+            for j in range(n):
+                assert ct[b, h, j] == len(want[j])
+                assert list(lt[b, h, j, :ct[b, h, j]]) == want[j]
+
+
+def test_backward_matches_oracle(case):
+    """dQ, dK, dV of the block-sparse attention against the float64 oracle,
+    with the oracle's lists and the GPU forward's O and LSE."""
+    g, og, ref = case["g"], case["og"], case["ref_mask"]
+    lut, counts = torch.from_numpy(ref.lut).to(DEV), torch.from_numpy(ref.counts).to(DEV)
+    qc, kc, vc = reorder3(case["qd"], case["kd"], case["vd"], g)
+    oc, lse_c = sa.fwd(qc, kc, vc, lut, counts, g)
+    rng = np.random.default_rng(17)
+    do = torch.from_numpy(rng.standard_normal(tuple(case["q"].shape)).astype(np.float32)).to(torch.bfloat16)
+    dq, dk, dv = sa.backward(case["qd"], case["kd"], case["vd"], do.to(DEV), oc, lse_c, lut, counts, g)
+    torch.cuda.synchronize()
+    want = O.sparse_attention_backward(case["ref_qc"], case["ref_kc"], case["ref_vc"], O.reorder(to64(do), og),
+                                       ref.lut, ref.counts, og)
+    for got, w, name in zip((dq, dk, dv), want, ("dq", "dk", "dv")):
+        err = np.abs(to64(got) - w)
+        scale = float(np.abs(w).max())
+        say(f"  {name}: max err {err.max():.2e} mean {err.mean():.2e} (max |grad| {scale:.2e})")
+        assert err.max() <= 2e-2 * scale and err.mean() <= 2e-3 * scale, name
