@@ -35,6 +35,7 @@ import synth  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
+PEAK_FP64_TFLOPS = 78.6        # MI355X float64 (vector and matrix)
 
 # HBM-side traffic of the forward kernel, measured by rocprofv3 counters and
 # recorded with a hash of the sources it was measured on
@@ -65,6 +66,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--no-next-rows", action="store_true",
+                    help="skip timing the coarse-output and router kernels")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
     return ap.parse_args()
@@ -89,6 +92,8 @@ class Path:
         self.o = torch.empty((B, H, self.n_real, d), dtype=torch.bfloat16, device=dev)
         self.lse_c = torch.empty((B, H, self.n_pad), dtype=torch.float32, device=dev)
         self.lse = torch.empty((B, H, self.n_real), dtype=torch.float32, device=dev)
+        gen = torch.Generator(device="cpu").manual_seed(7)
+        self.o_grad = torch.randn((B, H, self.n_real, d), generator=gen).to(torch.bfloat16).to(dev)
         self.cap = n
         self.lut = torch.empty((B, H, n, n), dtype=torch.int32, device=dev)
         self.counts = torch.empty((B, H, n), dtype=torch.int32, device=dev)
@@ -103,8 +108,8 @@ class Path:
     def stages(self):
         g = self.g
         return [
-            ("reorder", lambda: (sa.sparse_attn_reorder_pool(self.q, self.qc, self.qbar, g),
-                                 sa.sparse_attn_reorder_pool(self.k, self.kc, self.kbar, g),
+            ("reorder", lambda: (sa.sparse_attn_reorder_pool(self.q, self.qc, sa.SA_LAYOUT_QK, self.qbar, g),
+                                 sa.sparse_attn_reorder_pool(self.k, self.kc, sa.SA_LAYOUT_QK, self.kbar, g),
                                  sa.sparse_attn_reorder(self.v, self.vc, sa.SA_LAYOUT_V, g))),
             ("mask", lambda: (sa.sparse_attn_block_scores(self.qbar, self.kbar, self.scores, 0.0, g),
                               sa.sparse_attn_select(self.scores, g, self.k_frac, self.p, self.rb, self.lut,
@@ -158,6 +163,74 @@ def algorithmic_bytes(path):
                           + n * 4) + kept * 4),               # counts + kept ids
         "unreorder": B * H * (real + pad) * (tok + 4),
     }
+
+
+def time_call(fn, reps):
+    """Mean event-timed duration (ms) of fn on the current stream."""
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def next_rows(path, reps=3):
+    """Kernels beyond the timed step (coarse branch output, fine-grained
+    router), timed on the same resident inputs; not part of `value`."""
+    wl, g, n = path.wl, path.g, path.nblk
+    B, H, d = wl.batch, wl.heads, wl.head_dim
+    dev = path.q.device
+    vbar = torch.empty((B, H, n, d), dtype=torch.float64, device=dev)
+    ocb = torch.empty_like(vbar)
+    out = {}
+    t_vpool = time_call(lambda: sa.sparse_attn_reorder_pool(path.v, path.vc, sa.SA_LAYOUT_V, vbar, g), reps)
+    t_coarse = time_call(lambda: sa.sparse_attn_coarse(path.scores, vbar, ocb, g), reps)
+    fl = 2.0 * B * H * n * n * d
+    out["coarse"] = {"ms": round(t_coarse, 4), "tflops_fp64": round(fl / t_coarse / 1e9, 2),
+                     "frac_of_fp64_peak": round(fl / t_coarse / 1e9 / PEAK_FP64_TFLOPS, 4),
+                     "v_reorder_with_pooling_ms": round(t_vpool, 4)}
+    sub, G = (2, 2, 2), 8
+    qr = torch.empty((B, H, n * G, d), dtype=torch.float64, device=dev)
+    kr = torch.empty_like(qr)
+    rs = torch.empty((B, H, n, n), dtype=torch.float64, device=dev)
+    t_rpool = time_call(lambda: (sa.sparse_attn_router_pool(path.qc, qr, g, sub),
+                                 sa.sparse_attn_router_pool(path.kc, kr, g, sub)), reps)
+    t_router = time_call(lambda: sa.sparse_attn_router_scores(qr, kr, rs, 0.0, g, sub), 1)
+    fl = 2 * 2.0 * B * H * (n * G) ** 2 * d          # two passes over the sub-cube scores
+    out["router_2x2x2"] = {"ms": round(t_router, 3), "pool_ms": round(t_rpool, 4),
+                           "tflops_fp64": round(fl / t_router / 1e9, 2),
+                           "frac_of_fp64_peak": round(fl / t_router / 1e9 / PEAK_FP64_TFLOPS, 4)}
+    del qr, kr, rs
+    # backward over the same lists: operand layouts prepared untimed
+    lay = {}
+    for name, x, layout in (("q", path.q, sa.SA_LAYOUT_QK), ("k", path.k, sa.SA_LAYOUT_QK),
+                            ("v_qk", path.v, sa.SA_LAYOUT_QK), ("q_v", path.q, sa.SA_LAYOUT_V),
+                            ("k_v", path.k, sa.SA_LAYOUT_V), ("do_qk", path.o_grad, sa.SA_LAYOUT_QK),
+                            ("do_v", path.o_grad, sa.SA_LAYOUT_V)):
+        lay[name] = sa.reorder(x, g, layout)
+    delta = torch.empty((B, H, path.n_pad), dtype=torch.float32, device=dev)
+    lut_t = torch.empty((B, H, n, n), dtype=torch.int32, device=dev)
+    counts_t = torch.empty((B, H, n), dtype=torch.int32, device=dev)
+    ws = torch.empty(max(sa.sparse_attn_transpose_workspace_bytes(g), 256), dtype=torch.uint8, device=dev)
+    dq, dk, dv = (torch.empty_like(path.oc) for _ in range(3))
+    args = sa.BwdArgs(*(lay[k_].data_ptr() for k_ in ("q", "k", "v_qk", "q_v", "k_v", "do_qk", "do_v")),
+                      path.lse_c.data_ptr(), delta.data_ptr(), path.lut.data_ptr(), path.counts.data_ptr(),
+                      path.cap, lut_t.data_ptr(), counts_t.data_ptr(), n)
+    t_delta = time_call(lambda: sa.sparse_attn_bwd_delta(path.oc, lay["do_qk"], delta, g), reps)
+    t_tr = time_call(lambda: sa.sparse_attn_transpose_lut(path.lut, path.counts, path.cap, lut_t, counts_t, n, g,
+                                                          ws), reps)
+    t_bwd = time_call(lambda: sa.sparse_attn_bwd(args, g, 0.0, dq, dk, dv), reps)
+    kept = int(path.counts.sum().item())
+    fl = kept * 10.0 * 64 * 64 * d                    # five 64x64xd products per kept pair
+    out["backward"] = {"ms": round(t_bwd, 4), "delta_ms": round(t_delta, 4), "transpose_ms": round(t_tr, 4),
+                       "tflops": round(fl / t_bwd / 1e9, 2),
+                       "frac_of_bf16_peak": round(fl / t_bwd / 1e9 / PEAK_BF16_TFLOPS, 4),
+                       "flops_note": "10*64*64*d per kept block pair (the five products of the gradient)"}
+    return out
 
 
 def cpu_baseline(path, seconds):
@@ -309,6 +382,9 @@ def main():
             "traffic": recorded_traffic(args.workload),
         },
     }
+    if not args.no_next_rows:
+        log("[bench] timing the coarse-output and router kernels")
+        out["next_rows"] = next_rows(path)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(path, args.cpu_seconds)

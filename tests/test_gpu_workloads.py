@@ -121,3 +121,33 @@ def test_router_full_size():
     density = counts.cpu().numpy().sum() / (counts.numel() * og.nblk)
     say(f"  router lists: {len(bad)} mismatches outside near ties, {near} near ties, density {density:.4f}")
     assert not bad and not invalid
+
+
+def test_backward_full_size():
+    """Backward at the 720p shape with the hybrid-95 mask on two heads; the
+    float64 oracle recomputes head 0's gradients in full."""
+    wl = synth.WORKLOADS[2]
+    heads = [0, 1]
+    say(f"[backward 720p] heads {heads}")
+    q, k, v = synth.make_qkv(wl, 0, heads=heads)
+    g = sa.make_geom(1, len(heads), wl.frames, wl.height, wl.width, wl.head_dim)
+    og = ogeom_of(wl)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    o, lse, lut, counts = sa.attention(qd, kd, vd, g, 0.03, 0.073)
+    qc, kc, vc = (sa.reorder(x, g, lay) for x, lay in ((qd, sa.SA_LAYOUT_QK), (kd, sa.SA_LAYOUT_QK),
+                                                       (vd, sa.SA_LAYOUT_V)))
+    oc, lse_c = sa.fwd(qc, kc, vc, lut, counts, g)
+    rng = np.random.default_rng(5)
+    do = torch.from_numpy(rng.standard_normal(tuple(q.shape)).astype(np.float32)).to(torch.bfloat16)
+    dq, dk, dv = sa.backward(qd, kd, vd, do.to(DEV), oc, lse_c, lut, counts, g)
+    torch.cuda.synchronize()
+    say("  gpu backward done")
+    h = 0
+    ref_q, ref_k, ref_v, ref_do = (O.reorder(to64(x[:, h:h + 1]), og) for x in (q, k, v, do))
+    want = O.sparse_attention_backward(ref_q, ref_k, ref_v, ref_do, lut[:, h:h + 1].cpu().numpy(),
+                                       counts[:, h:h + 1].cpu().numpy(), og)
+    for got, w, name in zip((dq, dk, dv), want, ("dq", "dk", "dv")):
+        err = np.abs(to64(got[:, h:h + 1]) - w)
+        scale = float(np.abs(w).max())
+        say(f"  {name}: max err {err.max():.2e} mean {err.mean():.2e} (max |grad| {scale:.2e})")
+        assert err.max() <= 2e-2 * scale and err.mean() <= 2e-3 * scale, name
