@@ -230,6 +230,17 @@ def next_rows(path, reps=3):
                        "tflops": round(fl / t_bwd / 1e9, 2),
                        "frac_of_bf16_peak": round(fl / t_bwd / 1e9 / PEAK_BF16_TFLOPS, 4),
                        "flops_note": "10*64*64*d per kept block pair (the five products of the gradient)"}
+    del lay, dq, dk, dv, lut_t
+    # mask quality of the timed lists against dense attention (every block kept)
+    t0 = time.perf_counter()
+    mass, tau, rel = sa.mask_quality(path.qc, path.kc, path.vc, path.lut, path.counts, path.scores, g)
+    torch.cuda.synchronize()
+    real = tau > 0
+    out["mask_quality"] = {"seconds": round(time.perf_counter() - t0, 3),
+                           "mean_pooled_mass": round(float(mass.mean()), 5),
+                           "mean_tau": round(float(tau[real].mean()), 5),
+                           "min_tau": round(float(tau[real].min()), 5),
+                           "mean_rel_l1": round(float(rel.mean()), 5)}
     return out
 
 

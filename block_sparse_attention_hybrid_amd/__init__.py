@@ -37,7 +37,7 @@ EXPORTED = (
     "sparse_attn_build_mask", "sparse_attn_fwd_workspace_bytes", "sparse_attn_fwd",
     "sparse_attn_coarse", "sparse_attn_router_pool", "sparse_attn_router_scores",
     "sparse_attn_bwd_delta", "sparse_attn_transpose_workspace_bytes", "sparse_attn_transpose_lut",
-    "sparse_attn_bwd",
+    "sparse_attn_bwd", "sparse_attn_pooled_mass", "sparse_attn_mask_error",
     "sparse_attn_last_error",
 )
 
@@ -97,6 +97,8 @@ _SIGS = {
     "sparse_attn_transpose_workspace_bytes": (_sz, [_GP]),
     "sparse_attn_transpose_lut": (_i32, [_vp, _vp, _i32, _vp, _vp, _i32, _GP, _vp, _sz, _vp]),
     "sparse_attn_bwd": (_i32, [ctypes.POINTER(BwdArgs), _GP, _f32, _vp, _vp, _vp, _vp]),
+    "sparse_attn_pooled_mass": (_i32, [_vp, _vp, _vp, _i32, _GP, _vp, _vp]),
+    "sparse_attn_mask_error": (_i32, [_vp, _vp, _vp, _vp, _GP, _vp, _vp, _vp]),
     "sparse_attn_last_error": (ctypes.c_char_p, []),
 }
 
@@ -269,6 +271,19 @@ def sparse_attn_bwd(args: BwdArgs, g: Geom, scale: float, dq, dk, dv, stream=Non
                                  _ptr(dv, torch.bfloat16, "dv"), _stream(stream, dq)))
 
 
+def sparse_attn_pooled_mass(scores, lut, counts, cap: int, g: Geom, mass, stream=None) -> None:
+    _check(lib().sparse_attn_pooled_mass(_ptr(scores, torch.float64, "scores"), _ptr(lut, torch.int32, "lut"),
+                                         _ptr(counts, torch.int32, "counts"), int(cap), ctypes.byref(g),
+                                         _ptr(mass, torch.float64, "mass"), _stream(stream, scores)))
+
+
+def sparse_attn_mask_error(lse_s, lse_d, oc_s, oc_d, g: Geom, tau, rel_l1, stream=None) -> None:
+    _check(lib().sparse_attn_mask_error(_ptr(lse_s, torch.float32, "lse_s"), _ptr(lse_d, torch.float32, "lse_d"),
+                                        _ptr(oc_s, torch.bfloat16, "oc_s"), _ptr(oc_d, torch.bfloat16, "oc_d"),
+                                        ctypes.byref(g), _ptr(tau, torch.float32, "tau"),
+                                        _ptr(rel_l1, torch.float32, "rel_l1"), _stream(stream, lse_s)))
+
+
 def sparse_attn_last_error() -> str:
     return lib().sparse_attn_last_error().decode(errors="replace")
 
@@ -417,6 +432,25 @@ def backward(q, k, v, do, oc, lse_c, lut, counts, g: Geom, scale: float = 0.0, s
     dq, dk, dv = (_empty(tuple(oc.shape), torch.bfloat16, oc) for _ in range(3))
     sparse_attn_bwd(args, g, scale, dq, dk, dv, stream)
     return dq, dk, dv
+
+
+def mask_quality(qc, kc, vc, lut, counts, scores, g: Geom, stream=None):
+    """Diagnostics of a kept-block mask: pooled mass per row (from the scores
+    the mask was selected on), retained attention mass tau per query and the
+    relative L1 error per query block against dense attention (run here with
+    every block kept).  Returns (mass, tau, rel_l1)."""
+    nblk, _, n_pad = sparse_attn_geometry(g)
+    mass = _empty((g.batch, g.heads, nblk), torch.float64, qc)
+    sparse_attn_pooled_mass(scores, lut, counts, lut.shape[-1], g, mass, stream)
+    full = _empty((g.batch, g.heads, nblk, nblk), torch.int32, qc)
+    full_counts = _empty((g.batch, g.heads, nblk), torch.int32, qc)
+    sparse_attn_select(scores, g, 0.0, 1.0, None, full, full_counts, nblk, stream)
+    oc_s, lse_s = fwd(qc, kc, vc, lut, counts, g, stream=stream)
+    oc_d, lse_d = fwd(qc, kc, vc, full, full_counts, g, stream=stream)
+    tau = _empty((g.batch, g.heads, n_pad), torch.float32, qc)
+    rel = _empty((g.batch, g.heads, nblk), torch.float32, qc)
+    sparse_attn_mask_error(lse_s, lse_d, oc_s, oc_d, g, tau, rel, stream)
+    return mass, tau, rel
 
 
 def default_scale(head_dim: int) -> float:

@@ -316,6 +316,33 @@ int32_t sparse_attn_bwd(const sa_bwd_args* a, const sa_geom* g, float scale, voi
   return hip_status(sa::launch_bwd(b, d, scale, dq, dk, dv, (hipStream_t)stream), "bwd launch");
 }
 
+int32_t sparse_attn_pooled_mass(const double* scores, const int32_t* lut, const int32_t* counts, int32_t cap,
+                                const sa_geom* g, double* mass, void* stream) {
+  sa::Geom d;
+  SA_TRY(make_geom(g, d));
+  SA_TRY(check_ptr(scores, 8, "scores"));
+  SA_TRY(check_ptr(lut, 4, "lut"));
+  SA_TRY(check_ptr(counts, 4, "counts"));
+  SA_TRY(check_ptr(mass, 8, "mass"));
+  if (cap < 1) return fail(SA_ERR_INVALID_ARG, "cap must be >= 1");
+  return hip_status(sa::launch_pooled_mass(scores, lut, counts, cap, d, mass, (hipStream_t)stream),
+                    "pooled_mass launch");
+}
+
+int32_t sparse_attn_mask_error(const float* lse_s, const float* lse_d, const void* oc_s, const void* oc_d,
+                               const sa_geom* g, float* tau, float* rel_l1, void* stream) {
+  sa::Geom d;
+  SA_TRY(make_geom(g, d));
+  SA_TRY(check_ptr(lse_s, 4, "lse_s"));
+  SA_TRY(check_ptr(lse_d, 4, "lse_d"));
+  SA_TRY(check_ptr(oc_s, 16, "oc_s"));
+  SA_TRY(check_ptr(oc_d, 16, "oc_d"));
+  SA_TRY(check_ptr(tau, 4, "tau"));
+  SA_TRY(check_ptr(rel_l1, 4, "rel_l1"));
+  return hip_status(sa::launch_mask_error(lse_s, lse_d, oc_s, oc_d, d, tau, rel_l1, (hipStream_t)stream),
+                    "mask_error launch");
+}
+
 int32_t sparse_attn_block_scores(const double* qbar, const double* kbar, double* scores, double scale,
                                  const sa_geom* g, void* stream) {
   sa::Geom d;

@@ -42,6 +42,10 @@ size_t transpose_workspace_bytes(const Geom& g);
 hipError_t launch_transpose_lut(const int32_t* lut, const int32_t* counts, int cap, int32_t* lut_t,
                                 int32_t* counts_t, int cap_t, const Geom& g, void* workspace, hipStream_t s);
 hipError_t launch_bwd(const BwdArgs& a, const Geom& g, float scale, void* dq, void* dk, void* dv, hipStream_t s);
+hipError_t launch_pooled_mass(const double* scores, const int32_t* lut, const int32_t* counts, int cap,
+                              const Geom& g, double* mass, hipStream_t s);
+hipError_t launch_mask_error(const float* lse_s, const float* lse_d, const void* o_s, const void* o_d,
+                             const Geom& g, float* tau, float* rel, hipStream_t s);
 hipError_t launch_coarse(const double* scores, const double* vbar, double* oc, const Geom& g, hipStream_t s);
 
 }  // namespace sa

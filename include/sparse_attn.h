@@ -11,6 +11,7 @@
  *   coarse       block-level attention on pooled Q, K, V (coarse branch)
  *   router       fine-grained router scores (sub-cube pooling, G x G pooling)
  *   bwd          gradients of the block-sparse attention (dQ, dK, dV)
+ *   quality      retained pooled mass, retained attention mass, L1 error
  *   unreorder    cube-major O (and LSE) -> row-major tokens
  *
  * Conventions shared by every entry point
@@ -261,6 +262,30 @@ typedef struct sa_bwd_args {
  * scale must be the forward's (<= 0 selects 1/sqrt(head_dim)). */
 int32_t sparse_attn_bwd(const sa_bwd_args* args, const sa_geom* g, float scale,
                         void* dq, void* dk, void* dv, void* stream);
+
+/* ---- mask-quality diagnostics --------------------------------------------
+ * [SA2] "The Sparse Attention Error Decomposition" (Eq. 8's tau, Table 1's L1
+ * error); [VSA] on the attention mass the selected cubes capture.
+ *
+ * sparse_attn_pooled_mass: per row, the mass the kept blocks hold in the row
+ * softmax of `scores` (block scores or router scores), float64.
+ *   scores [batch, heads, nblk, nblk] float64; lut, counts, cap as selected
+ *   mass   [batch, heads, nblk] float64                                (output)
+ * sparse_attn_mask_error: from a sparse forward (lists) and a dense one
+ * (every block kept, e.g. sparse_attn_select with p = 1):
+ *   lse_s, lse_d [batch, heads, n_pad] float32 (inputs)
+ *   oc_s, oc_d   [batch, heads, n_pad, head_dim] bf16 slot-major (inputs)
+ *   tau    [batch, heads, n_pad] float32 = exp(lse_s - lse_d), the dense
+ *          softmax mass on the kept real keys (0 on pad slots)       (output)
+ *   rel_l1 [batch, heads, nblk] float32 = sum|o_s - o_d| / sum|o_d| over the
+ *          block's real queries                                        (output) */
+int32_t sparse_attn_pooled_mass(const double* scores, const int32_t* lut,
+                                const int32_t* counts, int32_t cap,
+                                const sa_geom* g, double* mass, void* stream);
+int32_t sparse_attn_mask_error(const float* lse_s, const float* lse_d,
+                               const void* oc_s, const void* oc_d,
+                               const sa_geom* g, float* tau, float* rel_l1,
+                               void* stream);
 
 /* Hybrid Top-k U Top-p selection, [SA2] "The Hybrid Top-k+Top-p Masking Rule"
  * (Eq. 9), producing index lists as [VSA] "Kernel Implementation" describes

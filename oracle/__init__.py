@@ -5,7 +5,7 @@ from .oracle import *  # noqa: F401,F403
 from .oracle import (Geometry, MaskResult, RowSelection, attention_block,
                      block_scores, block_softmax, build_mask, ceil_k, coarse_output,
                      expand_blocks, pool_r, router_scores, subcube_of_slot,
-                     sparse_attention_backward,
+                     sparse_attention_backward, pooled_mass, mask_error,
                      dense_attention, pool, rank_order, real_slots, reorder,
                      select_row, select_rows, sparse_attention, token_slots,
                      top_p_count, unreorder, unreorder_rows, NEAR_TIE)

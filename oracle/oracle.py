@@ -59,6 +59,14 @@ What it computes, step by step, in float64 (bfloat16 inputs convert exactly):
    respect to Q, K and V, by the chain rule through the renormalised softmax
    over each row's kept real keys (the mask itself carries no gradient).
 
+9. Mask-quality diagnostics (SpargeAttention2 summary page, "The Sparse
+   Attention Error Decomposition", Eq. 8, and Table 1's L1 error; VSA summary
+   page on the attention mass the selected cubes capture): per row the pooled
+   probability mass the kept blocks hold; per query the true retained mass
+   tau = sum of the dense softmax over the kept keys (the tau of Eq. 8); per
+   query block the relative L1 error sum|o - o_s| / sum|o| of the sparse output
+   against dense attention.
+
 Readings where the pages are silent or garbled are listed in the repository's
 design notes; the ones this file depends on are repeated at each function.
 Every function here is pinned by the CPU tests (worked examples, closed forms,
@@ -512,3 +520,54 @@ def sparse_attention_backward(qc: np.ndarray, kc_: np.ndarray, vc: np.ndarray, d
                 dq[b, h, xs] += scale * (ds @ k_h[ys])
                 dk[b, h, ys] += scale * (ds.T @ q_h[xs])
     return dq, dk, dv
+
+
+# ----------------------------------------------------------------------------
+# 9. mask-quality diagnostics
+# ----------------------------------------------------------------------------
+def pooled_mass(scores: np.ndarray, lut: np.ndarray, counts: np.ndarray) -> np.ndarray:
+    """Per row: sum over the kept blocks of the row softmax of the scores."""
+    p = block_softmax(np.asarray(scores, dtype=np.float64))
+    out = np.zeros(counts.shape)
+    for idx in np.ndindex(counts.shape):
+        out[idx] = p[idx][lut[idx][:counts[idx]]].sum()
+    return out
+
+
+def mask_error(qc: np.ndarray, kc_: np.ndarray, vc: np.ndarray, lut: np.ndarray, counts: np.ndarray,
+               g: Geometry, scale: Optional[float] = None):
+    """tau [B, H, n_pad] (dense softmax mass on the kept real keys; 0 on pad
+    slots) and rel_l1 [B, H, nblk] (sum|o - o_s| / sum|o| over the block's real
+    queries) of the sparse output o_s against dense attention o."""
+    B, H, n_pad, d = qc.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    real = real_slots(g)
+    blk = g.block
+    tau = np.zeros((B, H, n_pad))
+    rel = np.zeros((B, H, g.nblk))
+    o_s, _ = sparse_attention(qc, kc_, vc, lut, counts, g, scale)
+    for b in range(B):
+        for h in range(H):
+            q = np.asarray(qc[b, h], dtype=np.float64)[real]
+            k = np.asarray(kc_[b, h], dtype=np.float64)[real]
+            v = np.asarray(vc[b, h], dtype=np.float64)[real]
+            s = (q @ k.T) * scale
+            p = np.exp(s - s.max(axis=1, keepdims=True))
+            p /= p.sum(axis=1, keepdims=True)
+            o = np.zeros((n_pad, d))
+            o[real] = p @ v
+            key_blk = np.nonzero(real)[0] // blk
+            t = np.zeros(n_pad)
+            for i in range(g.nblk):
+                kept = np.zeros(g.nblk, dtype=bool)
+                kept[lut[b, h, i, :counts[b, h, i]]] = True
+                rows = np.arange(i * blk, (i + 1) * blk)
+                rows = rows[real[rows]]
+                ridx = np.searchsorted(np.nonzero(real)[0], rows)
+                t[rows] = p[ridx][:, kept[key_blk]].sum(axis=1)
+                num = np.abs(o[rows] - o_s[b, h, rows]).sum()
+                den = np.abs(o[rows]).sum()
+                rel[b, h, i] = num / den if den > 0 else 0.0
+            tau[b, h] = t
+    return tau, rel

@@ -383,3 +383,21 @@ def test_backward_matches_oracle(case):
         scale = float(np.abs(w).max())
         say(f"  {name}: max err {err.max():.2e} mean {err.mean():.2e} (max |grad| {scale:.2e})")
         assert err.max() <= 2e-2 * scale and err.mean() <= 2e-3 * scale, name
+
+
+def test_mask_quality_matches_oracle(case):
+    """Diagnostics: pooled mass (float64, tight), tau from the two LSEs and the
+    relative L1 error from bf16 outputs (their rounding sets the bar)."""
+    g, og, ref = case["g"], case["og"], case["ref_mask"]
+    qc, kc, vc = reorder3(case["qd"], case["kd"], case["vd"], g)
+    lut, counts = torch.from_numpy(ref.lut).to(DEV), torch.from_numpy(ref.counts).to(DEV)
+    mass, tau, rel = sa.mask_quality(qc, kc, vc, lut, counts, torch.from_numpy(ref.scores).to(DEV), g)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(mass.cpu().numpy(), O.pooled_mass(ref.scores, ref.lut, ref.counts),
+                               rtol=1e-12, atol=1e-14)
+    want_tau, want_rel = O.mask_error(case["ref_qc"], case["ref_kc"], case["ref_vc"], ref.lut, ref.counts, og)
+    t_err = np.abs(tau.cpu().numpy() - want_tau).max()
+    r_err = np.abs(rel.cpu().numpy() - want_rel)
+    say(f"  tau max err {t_err:.2e}; rel-L1 max err {r_err.max():.2e} (max rel-L1 {want_rel.max():.2e})")
+    assert t_err <= 1e-4
+    assert np.all(r_err <= 1e-2 + 2e-2 * want_rel)

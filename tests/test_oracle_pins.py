@@ -709,3 +709,47 @@ def test_backward_invariants():
     shifted = kc_ + rng.standard_normal(kc_.shape[-1])[None, None, None, :] * O.real_slots(g)[None, None, :, None]
     dq2, _, _ = O.sparse_attention_backward(qc, shifted, vc, doc, m.lut, m.counts, g)
     np.testing.assert_allclose(dq2, dq, rtol=1e-9, atol=1e-10)
+
+
+# ----------------------------------------------------------------------------
+# mask-quality diagnostics
+# ----------------------------------------------------------------------------
+def test_mask_error_tau_is_the_lse_gap_and_eq8_holds():
+    """tau (dense mass on the kept keys) equals exp(LSE_sparse - LSE_dense); with
+    it, Eq. 8 gives the sparse output's error exactly."""
+    wl, q, k, v = _tiny_inputs(grid=(5, 6, 7), heads=2, d=16, seed=7)
+    g = O.Geometry(*wl.grid)
+    qc, kc_, vc = (O.reorder(x, g) for x in (q, k, v))
+    m = O.build_mask(qc, kc_, g, 0.25, 0.4)
+    tau, rel = O.mask_error(qc, kc_, vc, m.lut, m.counts, g)
+    _, lse_s = O.sparse_attention(qc, kc_, vc, m.lut, m.counts, g)
+    full = O.build_mask(qc, kc_, g, 1.0, 0.0)
+    o_d, lse_d = O.sparse_attention(qc, kc_, vc, full.lut, full.counts, g)
+    real = O.real_slots(g)
+    with np.errstate(invalid="ignore"):
+        gap = np.exp(lse_s - lse_d)
+    np.testing.assert_allclose(tau[..., real], gap[..., real], rtol=1e-12)
+    assert np.all(tau[..., ~real] == 0.0)
+    o_s, _ = O.sparse_attention(qc, kc_, vc, m.lut, m.counts, g)
+    # Eq. 8: a query whose kept keys hold all of its dense mass (tau = 1) has o_s = o
+    kept_all = np.isclose(tau[..., real], 1.0, rtol=0, atol=1e-15)
+    err = np.abs(o_d - o_s).sum(axis=-1)[..., real]
+    assert np.all(err[kept_all] < 1e-12)
+    np.testing.assert_array_less(-1e-15, rel)
+    tau_f, rel_f = O.mask_error(qc, kc_, vc, full.lut, full.counts, g)
+    np.testing.assert_allclose(tau_f[..., real], 1.0, rtol=1e-12)
+    np.testing.assert_allclose(rel_f, 0.0, atol=1e-12)
+
+
+def test_pooled_mass_closed_forms():
+    rng = np.random.default_rng(51)
+    s = rng.standard_normal((2, 3, 9, 9))
+    lut = np.tile(np.arange(9, dtype=np.int32), (2, 3, 9, 1))
+    counts = np.full((2, 3, 9), 9, dtype=np.int32)
+    np.testing.assert_allclose(O.pooled_mass(s, lut, counts), 1.0, rtol=1e-13)
+    counts[:] = 1
+    lut[..., 0] = np.argmax(s, axis=-1)
+    want = 1.0 / np.exp(s - s.max(axis=-1, keepdims=True)).sum(axis=-1)
+    np.testing.assert_allclose(O.pooled_mass(s, lut, counts), want, rtol=1e-13)
+    counts[:] = 0
+    assert np.all(O.pooled_mass(s, lut, counts) == 0.0)
