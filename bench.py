@@ -66,6 +66,12 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--serial", action="store_true",
+                    help="launch the stages from Python one after another instead of the library's "
+                         "whole-path call")
+    ap.add_argument("--overlap", type=int, default=0, metavar="ROWS",
+                    help="overlap the mask of one chunk of ROWS batch*head rows with the forward of the "
+                         "previous chunk on a second stream (0: one stream)")
     ap.add_argument("--no-next-rows", action="store_true",
                     help="skip timing the coarse-output and router kernels")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -104,6 +110,12 @@ class Path:
             self.rb = torch.from_numpy(synth.row_budgets(wl, 0)).to(dev)
         nfw = sa.sparse_attn_fwd_workspace_bytes(self.g)
         self.fws = torch.empty(max(nfw, 256), dtype=torch.uint8, device=dev)
+        ptr = lambda t: t.data_ptr()
+        self.buf = sa.PathBuffers(ptr(self.q), ptr(self.k), ptr(self.v), ptr(self.qc), ptr(self.kc), ptr(self.vc),
+                                  ptr(self.qbar), ptr(self.kbar), ptr(self.scores), ptr(self.lut),
+                                  ptr(self.counts), self.cap, None if self.rb is None else ptr(self.rb),
+                                  ptr(self.oc), ptr(self.lse_c), ptr(self.o), ptr(self.lse))
+        self.aux = torch.cuda.Stream(device=dev)
 
     def stages(self):
         g = self.g
@@ -122,6 +134,13 @@ class Path:
     def step(self):
         for _, fn in self.stages():
             fn()
+
+    def step_call(self, overlap_rows):
+        """The whole path as one library call (sparse_attn_attention); with
+        overlap_rows > 0 the mask of a chunk of rows is built on the main stream
+        while the previous chunk's forward runs on an auxiliary stream."""
+        sa.sparse_attn_attention(self.buf, self.g, self.k_frac, self.p, 0.0, max(1, overlap_rows),
+                                 aux_stream=self.aux.cuda_stream if overlap_rows > 0 else None)
 
 
 def fwd_source_hash():
@@ -317,24 +336,30 @@ def main():
     path = Path(wl, k_frac, p, budgets, dev)
     log(f"[bench] {args.workload}: {path.g}, nblk={path.nblk}, k_frac={k_frac}, p={p}")
 
+    step = path.step if args.serial else (lambda: path.step_call(args.overlap))
     for _ in range(args.warmup):
-        path.step()
-    torch.cuda.synchronize()
-
-    names = [n for n, _ in path.stages()]
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+        step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(args.steps):
-        ev[s][0].record()
-        for j, (_, fn) in enumerate(path.stages()):
-            fn()
-            ev[s][j + 1].record()
+    for _ in range(args.steps):
+        step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    stage_ms = {n: float(np.mean([ev[s][j].elapsed_time(ev[s][j + 1]) for s in range(args.steps)]))
-                for j, n in enumerate(names)}
     ms_per_step = wall * 1e3 / args.steps
+
+    # per-stage breakdown: the same kernels one after another, event-timed
+    names = [n for n, _ in path.stages()]
+    nst = max(3, min(args.steps, 10))
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(nst)]
+    torch.cuda.synchronize()
+    for s_ in range(nst):
+        ev[s_][0].record()
+        for j, (_, fn) in enumerate(path.stages()):
+            fn()
+            ev[s_][j + 1].record()
+    torch.cuda.synchronize()
+    stage_ms = {n: float(np.mean([ev[s_][j].elapsed_time(ev[s_][j + 1]) for s_ in range(nst)]))
+                for j, n in enumerate(names)}
 
     kept = int(path.counts.sum().item())
     rows = wl.batch * wl.heads * path.nblk
@@ -375,6 +400,10 @@ def main():
             "global_batch": wl.batch,
             "seq_len": path.n_real,
             "parallelism": "single GPU",
+            "schedule": ("stages launched from Python on one stream" if args.serial else
+                         "sparse_attn_attention on one stream" if args.overlap <= 0 else
+                         f"sparse_attn_attention, mask of chunk c+1 beside forward of chunk c "
+                         f"({args.overlap} rows per chunk, two streams)"),
             "block_sparsity": round(1.0 - density, 5),
             "kept_blocks": kept,
         },

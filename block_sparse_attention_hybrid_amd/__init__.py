@@ -37,7 +37,7 @@ EXPORTED = (
     "sparse_attn_build_mask", "sparse_attn_fwd_workspace_bytes", "sparse_attn_fwd",
     "sparse_attn_coarse", "sparse_attn_router_pool", "sparse_attn_router_scores",
     "sparse_attn_bwd_delta", "sparse_attn_transpose_workspace_bytes", "sparse_attn_transpose_lut",
-    "sparse_attn_bwd", "sparse_attn_pooled_mass", "sparse_attn_mask_error",
+    "sparse_attn_bwd", "sparse_attn_pooled_mass", "sparse_attn_mask_error", "sparse_attn_attention",
     "sparse_attn_last_error",
 )
 
@@ -72,6 +72,13 @@ class BwdArgs(ctypes.Structure):
                [(n, ctypes.c_void_p) for n in ("lut_t", "counts_t")] + [("cap_t", ctypes.c_int32)]
 
 
+class PathBuffers(ctypes.Structure):
+    """sa_path_buffers of the C ABI."""
+    _fields_ = ([(n, ctypes.c_void_p) for n in ("q", "k", "v", "qc", "kc", "vc", "qbar", "kbar", "scores", "lut",
+                                                "counts")] + [("cap", ctypes.c_int32)] +
+                [(n, ctypes.c_void_p) for n in ("row_budget", "oc", "lse_c", "o", "lse")])
+
+
 _lib = None
 _lock = threading.Lock()
 _vp, _i32, _i64, _sz, _f64, _f32 = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
@@ -99,6 +106,7 @@ _SIGS = {
     "sparse_attn_bwd": (_i32, [ctypes.POINTER(BwdArgs), _GP, _f32, _vp, _vp, _vp, _vp]),
     "sparse_attn_pooled_mass": (_i32, [_vp, _vp, _vp, _i32, _GP, _vp, _vp]),
     "sparse_attn_mask_error": (_i32, [_vp, _vp, _vp, _vp, _GP, _vp, _vp, _vp]),
+    "sparse_attn_attention": (_i32, [ctypes.POINTER(PathBuffers), _GP, _f64, _f64, _f32, _i32, _vp, _vp]),
     "sparse_attn_last_error": (ctypes.c_char_p, []),
 }
 
@@ -284,6 +292,14 @@ def sparse_attn_mask_error(lse_s, lse_d, oc_s, oc_d, g: Geom, tau, rel_l1, strea
                                         _ptr(rel_l1, torch.float32, "rel_l1"), _stream(stream, lse_s)))
 
 
+def sparse_attn_attention(buffers: PathBuffers, g: Geom, k_frac: float, p: float, scale: float = 0.0,
+                          head_chunk: int = 8, stream=None, aux_stream=None) -> None:
+    s = torch.cuda.current_stream().cuda_stream if stream is None else int(stream)
+    a = None if aux_stream is None else ctypes.c_void_p(int(aux_stream))
+    _check(lib().sparse_attn_attention(ctypes.byref(buffers), ctypes.byref(g), float(k_frac), float(p),
+                                       float(scale), int(head_chunk), ctypes.c_void_p(s), a))
+
+
 def sparse_attn_last_error() -> str:
     return lib().sparse_attn_last_error().decode(errors="replace")
 
@@ -451,6 +467,32 @@ def mask_quality(qc, kc, vc, lut, counts, scores, g: Geom, stream=None):
     rel = _empty((g.batch, g.heads, nblk), torch.float32, qc)
     sparse_attn_mask_error(lse_s, lse_d, oc_s, oc_d, g, tau, rel, stream)
     return mass, tau, rel
+
+
+def path_buffers(q, k, v, g: Geom, row_budget=None):
+    """Allocate every buffer of sparse_attn_attention for row-major q, k, v.
+    Returns (PathBuffers, dict of the tensors, which must outlive the call)."""
+    nblk, n_real, n_pad = sparse_attn_geometry(g)
+    B, H, d = g.batch, g.heads, g.head_dim
+    t = dict(q=q, k=k, v=v)
+    for n in ("qc", "kc", "vc", "oc"):
+        t[n] = _empty((B, H, n_pad, d), torch.bfloat16, q)
+    t["qbar"], t["kbar"] = (_empty((B, H, nblk, d), torch.float64, q) for _ in range(2))
+    t["scores"] = _empty((B, H, nblk, nblk), torch.float64, q)
+    t["lut"] = _empty((B, H, nblk, nblk), torch.int32, q)
+    t["counts"] = _empty((B, H, nblk), torch.int32, q)
+    t["lse_c"] = _empty((B, H, n_pad), torch.float32, q)
+    t["o"] = _empty((B, H, n_real, d), torch.bfloat16, q)
+    t["lse"] = _empty((B, H, n_real), torch.float32, q)
+    for n in ("q", "k", "v"):
+        _ptr(t[n], torch.bfloat16, n)
+    ptr = lambda n: t[n].data_ptr()
+    buf = PathBuffers(ptr("q"), ptr("k"), ptr("v"), ptr("qc"), ptr("kc"), ptr("vc"), ptr("qbar"), ptr("kbar"),
+                      ptr("scores"), ptr("lut"), ptr("counts"), nblk,
+                      None if row_budget is None else row_budget.data_ptr(),
+                      ptr("oc"), ptr("lse_c"), ptr("o"), ptr("lse"))
+    t["row_budget"] = row_budget
+    return buf, t
 
 
 def default_scale(head_dim: int) -> float:

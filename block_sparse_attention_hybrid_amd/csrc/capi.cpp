@@ -343,6 +343,38 @@ int32_t sparse_attn_mask_error(const float* lse_s, const float* lse_d, const voi
                     "mask_error launch");
 }
 
+}  // extern "C"
+
+int32_t sa_hip_status(hipError_t e, const char* what) { return hip_status(e, what); }
+
+int32_t sa_validate_path(const sa_path_buffers* b, const sa_geom* g, double k_frac, double p, float scale,
+                         int32_t head_chunk, sa::Geom& d, int& kcount, float& scale_out) {
+  SA_TRY(make_geom(g, d));
+  if (b == nullptr) return fail(SA_ERR_INVALID_ARG, "buffers pointer is NULL");
+  if (d.nblk > 64 * 65535) return fail(SA_ERR_UNSUPPORTED, "too many blocks for the score grid");
+  SA_TRY(check_ptr(b->q, 16, "q"));
+  SA_TRY(check_ptr(b->k, 16, "k"));
+  SA_TRY(check_ptr(b->v, 16, "v"));
+  SA_TRY(check_ptr(b->qc, 16, "qc"));
+  SA_TRY(check_ptr(b->kc, 16, "kc"));
+  SA_TRY(check_ptr(b->vc, 16, "vc"));
+  SA_TRY(check_ptr(b->qbar, 8, "qbar"));
+  SA_TRY(check_ptr(b->kbar, 8, "kbar"));
+  SA_TRY(check_ptr(b->scores, 8, "scores"));
+  SA_TRY(check_ptr(b->oc, 16, "oc"));
+  SA_TRY(check_ptr(b->lse_c, 4, "lse_c"));
+  SA_TRY(check_ptr(b->o, 16, "o"));
+  SA_TRY(check_ptr(b->lse, 4, "lse"));
+  if (b->q == b->qc || b->k == b->kc || b->v == b->vc) return fail(SA_ERR_INVALID_ARG, "inputs and outputs overlap");
+  SA_TRY(check_select_args(d, k_frac, p, b->row_budget, b->lut, b->counts, b->cap, kcount));
+  if (head_chunk < 1) return fail(SA_ERR_INVALID_ARG, "head_chunk must be >= 1");
+  if (!std::isfinite(scale)) return fail(SA_ERR_INVALID_ARG, "scale must be finite");
+  scale_out = scale <= 0.f ? 1.f / std::sqrt((float)d.d) : scale;
+  return ok();
+}
+
+extern "C" {
+
 int32_t sparse_attn_block_scores(const double* qbar, const double* kbar, double* scores, double scale,
                                  const sa_geom* g, void* stream) {
   sa::Geom d;

@@ -1,0 +1,117 @@
+// The whole path in one call, optionally overlapped across two streams.
+//
+// Order of the work (the path of the summary pages: cube re-indexing and
+// pooling, pooled scores, hybrid selection, block-sparse forward, inverse
+// re-indexing).  With an auxiliary stream the call splits the batch*heads rows
+// into chunks and runs the forward of chunk c on the auxiliary stream while
+// the main stream builds the mask of chunk c + 1; the value reorder also runs
+// on the auxiliary stream beside the query and key reorders.  The forward
+// keeps only one wave per SIMD resident (its register budget), so the mask
+// kernels find room on the same compute units.  Events order the two streams;
+// the main stream waits for the auxiliary one at the end, so the caller sees
+// completion on the stream it passed.
+#include "../../include/sparse_attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <vector>
+
+#include "sa_launch.h"
+
+namespace {
+
+// Events reused across calls (one pool per thread).
+struct EventPool {
+  std::vector<hipEvent_t> ev;
+  hipError_t get(size_t n) {
+    while (ev.size() < n) {
+      hipEvent_t e;
+      const hipError_t r = hipEventCreateWithFlags(&e, hipEventDisableTiming);
+      if (r != hipSuccess) return r;
+      ev.push_back(e);
+    }
+    return hipSuccess;
+  }
+};
+thread_local EventPool g_events;
+
+// Geometry of rows [r0, r0 + nr) of the flattened batch*heads dimension.
+sa::Geom rows_of(const sa::Geom& d, int nr) {
+  sa::Geom s = d;
+  s.batch = 1;
+  s.heads = nr;
+  return s;
+}
+
+}  // namespace
+
+// defined in capi.cpp
+int32_t sa_validate_path(const sa_path_buffers* b, const sa_geom* g, double k_frac, double p, float scale,
+                         int32_t head_chunk, sa::Geom& d, int& kcount, float& scale_out);
+int32_t sa_hip_status(hipError_t e, const char* what);
+
+extern "C" int32_t sparse_attn_attention(const sa_path_buffers* b, const sa_geom* g, double k_frac, double p,
+                                         float scale, int32_t head_chunk, void* stream, void* aux_stream) {
+  sa::Geom d;
+  int kcount = 0;
+  float sc = 0.f;
+  const int32_t v = sa_validate_path(b, g, k_frac, p, scale, head_chunk, d, kcount, sc);
+  if (v != SA_OK) return v;
+  hipStream_t s = (hipStream_t)stream;
+  hipStream_t a = aux_stream != nullptr ? (hipStream_t)aux_stream : s;
+  const bool two = aux_stream != nullptr && aux_stream != stream;
+  const int rows = d.batch * d.heads;
+  const int chunk = two ? (head_chunk < rows ? head_chunk : rows) : rows;
+  const int nchunks = (rows + chunk - 1) / chunk;
+  const double bscale = 1.0 / std::sqrt((double)d.d);
+  const size_t tok = (size_t)d.d;             // elements per token row
+  const size_t head_c = (size_t)d.n_pad * tok;
+  const size_t head_r = (size_t)d.n_real * tok;
+  const size_t nb = (size_t)d.nblk;
+  hipError_t e;
+  if (two) {
+    if ((e = g_events.get(nchunks + 2)) != hipSuccess) return sa_hip_status(e, "event creation");
+    // the auxiliary stream starts after everything already queued on the main one
+    if ((e = hipEventRecord(g_events.ev[0], s)) != hipSuccess) return sa_hip_status(e, "event record");
+    if ((e = hipStreamWaitEvent(a, g_events.ev[0], 0)) != hipSuccess) return sa_hip_status(e, "stream wait");
+  }
+  if ((e = sa::launch_reorder(b->v, b->vc, 1, d, a)) != hipSuccess) return sa_hip_status(e, "reorder launch");
+  if ((e = sa::launch_reorder_pool(b->q, b->qc, 0, b->qbar, d, s)) != hipSuccess)
+    return sa_hip_status(e, "reorder_pool launch");
+  if ((e = sa::launch_reorder_pool(b->k, b->kc, 0, b->kbar, d, s)) != hipSuccess)
+    return sa_hip_status(e, "reorder_pool launch");
+  for (int c = 0; c < nchunks; ++c) {
+    const int r0 = c * chunk, nr = (rows - r0) < chunk ? (rows - r0) : chunk;
+    const sa::Geom gc = rows_of(d, nr);
+    const double* qbar = b->qbar + (size_t)r0 * nb * tok;
+    const double* kbar = b->kbar + (size_t)r0 * nb * tok;
+    double* scores = b->scores + (size_t)r0 * nb * nb;
+    int32_t* lut = b->lut + (size_t)r0 * nb * b->cap;
+    int32_t* counts = b->counts + (size_t)r0 * nb;
+    const int32_t* rb = b->row_budget ? b->row_budget + (size_t)r0 * nb : nullptr;
+    if ((e = sa::launch_block_scores(qbar, kbar, scores, bscale, gc, s)) != hipSuccess)
+      return sa_hip_status(e, "block score launch");
+    if ((e = sa::launch_select(scores, gc, kcount, p, rb, lut, counts, b->cap, s)) != hipSuccess)
+      return sa_hip_status(e, "select launch");
+    if (two) {
+      if ((e = hipEventRecord(g_events.ev[1 + c], s)) != hipSuccess) return sa_hip_status(e, "event record");
+      if ((e = hipStreamWaitEvent(a, g_events.ev[1 + c], 0)) != hipSuccess) return sa_hip_status(e, "stream wait");
+    }
+    const char* qc = static_cast<const char*>(b->qc) + (size_t)r0 * head_c * 2;
+    const char* kc = static_cast<const char*>(b->kc) + (size_t)r0 * head_c * 2;
+    const char* vc = static_cast<const char*>(b->vc) + (size_t)r0 * head_c * 2;
+    char* oc = static_cast<char*>(b->oc) + (size_t)r0 * head_c * 2;
+    float* lse_c = b->lse_c + (size_t)r0 * d.n_pad;
+    if ((e = sa::launch_fwd(qc, kc, vc, lut, counts, b->cap, gc, sc, oc, lse_c, nullptr, a)) != hipSuccess)
+      return sa_hip_status(e, "fwd launch");
+  }
+  (void)head_r;
+  if ((e = sa::launch_unreorder(b->oc, b->o, b->lse_c, b->lse, d, a)) != hipSuccess)
+    return sa_hip_status(e, "unreorder launch");
+  if (two) {
+    if ((e = hipEventRecord(g_events.ev[nchunks + 1], a)) != hipSuccess) return sa_hip_status(e, "event record");
+    if ((e = hipStreamWaitEvent(s, g_events.ev[nchunks + 1], 0)) != hipSuccess) return sa_hip_status(e, "stream wait");
+  }
+  return SA_OK;
+}

@@ -61,12 +61,17 @@ __global__ __launch_bounds__(64) void mask_error_kernel(const float* __restrict_
   tau[slot] = t;
   double num = 0.0, den = 0.0;
   if (real) {
-    const bf16* a = o_s + slot * d;
-    const bf16* b = o_d + slot * d;
-    for (int c = 0; c < d; ++c) {
-      const double x = (double)(float)a[c], y = (double)(float)b[c];
-      num += fabs(x - y);
-      den += fabs(y);
+    const u32x4* a = reinterpret_cast<const u32x4*>(o_s + slot * d);
+    const u32x4* b = reinterpret_cast<const u32x4*>(o_d + slot * d);
+    for (int c8 = 0; c8 < d / 8; ++c8) {
+      const u32x4 x = a[c8], y = b[c8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x0 = __uint_as_float(x[e] << 16), x1 = __uint_as_float(x[e] & 0xffff0000u);
+        const float y0 = __uint_as_float(y[e] << 16), y1 = __uint_as_float(y[e] & 0xffff0000u);
+        num += (double)fabsf(x0 - y0) + (double)fabsf(x1 - y1);
+        den += (double)fabsf(y0) + (double)fabsf(y1);
+      }
     }
   }
   num = wave_sum(num);

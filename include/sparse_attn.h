@@ -12,6 +12,7 @@
  *   router       fine-grained router scores (sub-cube pooling, G x G pooling)
  *   bwd          gradients of the block-sparse attention (dQ, dK, dV)
  *   quality      retained pooled mass, retained attention mass, L1 error
+ *   attention    the whole path in one call, overlapped over two streams
  *   unreorder    cube-major O (and LSE) -> row-major tokens
  *
  * Conventions shared by every entry point
@@ -201,6 +202,44 @@ int32_t sparse_attn_router_scores(const double* qr, const double* kr,
                                   double* scores, double scale,
                                   const sa_geom* g, int32_t rt, int32_t rh,
                                   int32_t rw, void* stream);
+
+/* ---- the whole path in one call ------------------------------------------
+ * Buffers of sparse_attn_attention (device pointers the caller allocated). */
+typedef struct sa_path_buffers {
+  const void* q;        /* [batch, heads, N, head_dim] bf16, row-major tokens (inputs) */
+  const void* k;
+  const void* v;
+  void* qc;             /* [batch, heads, n_pad, head_dim] bf16, cube-major operands (written) */
+  void* kc;
+  void* vc;
+  double* qbar;         /* [batch, heads, nblk, head_dim] float64 block means (written) */
+  double* kbar;
+  double* scores;       /* [batch, heads, nblk, nblk] float64 pooled scores (written) */
+  int32_t* lut;         /* [batch, heads, nblk, cap] kept lists (written) */
+  int32_t* counts;      /* [batch, heads, nblk] */
+  int32_t cap;
+  const int32_t* row_budget; /* [batch, heads, nblk] or NULL, as for sparse_attn_select */
+  void* oc;             /* [batch, heads, n_pad, head_dim] bf16 slot-major output (written) */
+  float* lse_c;         /* [batch, heads, n_pad] (written) */
+  void* o;              /* [batch, heads, N, head_dim] bf16 output in token order (written) */
+  float* lse;           /* [batch, heads, N] (written) */
+} sa_path_buffers;
+
+/* reorder_pool(Q), reorder_pool(K), reorder(V), block_scores, select, fwd,
+ * unreorder -- the path of [SA2] Algorithm 1 and [VSA]'s two stages -- in one
+ * call.  Block scores use 1/sqrt(head_dim); `scale` (<= 0: 1/sqrt(head_dim))
+ * is the attention scale.  With aux_stream NULL (or equal to stream) the
+ * kernels run in order on `stream`.  Otherwise the batch*heads rows are cut
+ * into chunks of head_chunk rows: the mask of a chunk is built on `stream`
+ * while the forward of the previous chunk runs on aux_stream (and the value
+ * reorder runs on aux_stream beside the query/key reorders); `stream` waits
+ * for aux_stream before the call returns, so completion is observed on
+ * `stream`.  The results are the same either way.  Both streams must belong
+ * to the current device. */
+int32_t sparse_attn_attention(const sa_path_buffers* buffers, const sa_geom* g,
+                              double k_frac, double p, float scale,
+                              int32_t head_chunk, void* stream,
+                              void* aux_stream);
 
 /* ---- backward pass of the block-sparse attention ------------------------
  * [SA2] "Why this implementation is trainable": gradients flow through the

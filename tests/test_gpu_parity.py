@@ -401,3 +401,26 @@ def test_mask_quality_matches_oracle(case):
     say(f"  tau max err {t_err:.2e}; rel-L1 max err {r_err.max():.2e} (max rel-L1 {want_rel.max():.2e})")
     assert t_err <= 1e-4
     assert np.all(r_err <= 1e-2 + 2e-2 * want_rel)
+
+
+@pytest.mark.parametrize("chunk", [1, 2])
+def test_whole_path_call_overlapped_equals_sequential(case, chunk):
+    """sparse_attn_attention on two streams (rows cut into chunks) gives the
+    same bytes as the step-by-step path on one stream."""
+    g = case["g"]
+    o, lse, lut, counts = sa.attention(case["qd"], case["kd"], case["vd"], g, case["k_frac"], case["p"])
+    buf, t = sa.path_buffers(case["qd"], case["kd"], case["vd"], g)
+    aux = torch.cuda.Stream()
+    sa.sparse_attn_attention(buf, g, case["k_frac"], case["p"], 0.0, chunk, aux_stream=aux.cuda_stream)
+    torch.cuda.synchronize()
+    assert torch.equal(t["counts"], counts)
+    c = counts.cpu().numpy()
+    a, b = t["lut"].cpu().numpy(), lut.cpu().numpy()
+    for idx in np.ndindex(c.shape):
+        assert np.array_equal(a[idx][:c[idx]], b[idx][:c[idx]])
+    assert torch.equal(t["o"], o) and torch.equal(t["lse"], lse)
+    # one stream
+    buf2, t2 = sa.path_buffers(case["qd"], case["kd"], case["vd"], g)
+    sa.sparse_attn_attention(buf2, g, case["k_frac"], case["p"], 0.0, chunk)
+    torch.cuda.synchronize()
+    assert torch.equal(t2["o"], o) and torch.equal(t2["lse"], lse)
