@@ -6,11 +6,14 @@
 // to a multiple of the cube side.
 //
 // One workgroup per (batch*head, block).  The block's 64 source rows (runs of
-// cw consecutive tokens) are read with 16-byte lane loads into LDS, then
-// written out as 1 KB operand chunks in the QK or V element order (see
-// sa_layout.h), so both the reads and the writes are whole-row / whole-chunk
-// and the traffic is the algorithmic minimum: N rows read, n_pad rows written.
-// Pad slots are written as zeros.
+// cw consecutive tokens) are read with 16-byte lane loads into a token-major
+// LDS tile, then written out as 1 KB operand chunks in the QK or V element
+// order (see sa_layout.h), so both the reads and the writes are whole-row /
+// whole-chunk and the traffic is the algorithmic minimum: N rows read, n_pad
+// rows written.  QK chunks are 16-byte rows of the tile; a V chunk lane holds
+// 8 tokens of one dim, gathered as 2-byte reads down a tile column (lanes of
+// a wave read adjacent columns, so the reads spread over the banks).  Pad
+// slots are written as zeros.
 //
 // The fused form also takes the block's mean over its real tokens from the
 // tile while it sits in LDS (SpargeAttention2 summary page, "Block-Pooled
@@ -38,13 +41,13 @@ template <bool kV, bool kPool>
 __global__ __launch_bounds__(kThreads) void reorder_kernel(const u32x4* __restrict__ x,
                                                            u32x4* __restrict__ xc,
                                                            double* __restrict__ xbar, Geom g) {
-  // QK: tile[s][c] (row pitch d+8); V: tile[c][s] (row pitch 72)
-  __shared__ __attribute__((aligned(16))) uint16_t tile[128 * 72];
+  // tile[s][c], token-major with row pitch d+8 (16-byte rows), for both layouts
+  __shared__ __attribute__((aligned(16))) uint16_t tile[kBlock * (128 + 8)];
   __shared__ long long tok[kBlock];
   const int i = blockIdx.x;
   const long long bh = blockIdx.y;
   const int d = g.d, cpr = d / 8;
-  const int ldq = d + 8, ldv = 72;
+  const int ldq = d + 8;
   const long long src_head = bh * g.n_real * cpr;
   const long long dst_blk = (bh * g.n_pad + (long long)i * kBlock) * cpr;
   fill_slot_table(g, i, tok);
@@ -53,15 +56,7 @@ __global__ __launch_bounds__(kThreads) void reorder_kernel(const u32x4* __restri
     const long long n = tok[s];
     u32x4 v = {0u, 0u, 0u, 0u};
     if (n >= 0) v = x[src_head + n * cpr + c8];
-    if (!kV) {
-      *reinterpret_cast<u32x4*>(&tile[s * ldq + c8 * 8]) = v;
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t w = v[e >> 1];
-        tile[(c8 * 8 + e) * ldv + s] = (uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu));
-      }
-    }
+    *reinterpret_cast<u32x4*>(&tile[s * ldq + c8 * 8]) = v;
   }
   __syncthreads();
   for (int u = threadIdx.x; u < kBlock * cpr; u += kThreads) {
@@ -71,8 +66,12 @@ __global__ __launch_bounds__(kThreads) void reorder_kernel(const u32x4* __restri
       const int t32 = chunk / (d / 16), ds = chunk % (d / 16);
       v = *reinterpret_cast<const u32x4*>(&tile[(32 * t32 + r) * ldq + 16 * ds + 8 * h]);
     } else {
+      // 8 consecutive tokens of one dim: a column of the tile, packed in pairs
       const int dt = chunk >> 2, ks = chunk & 3;
-      v = *reinterpret_cast<const u32x4*>(&tile[(32 * dt + r) * ldv + 16 * ks + 8 * h]);
+      const uint16_t* col = &tile[(16 * ks + 8 * h) * ldq + 32 * dt + r];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        v[t] = (uint32_t)col[(2 * t) * ldq] | ((uint32_t)col[(2 * t + 1) * ldq] << 16);
     }
     xc[dst_blk + u] = v;
   }
@@ -84,7 +83,7 @@ __global__ __launch_bounds__(kThreads) void reorder_kernel(const u32x4* __restri
     const int ns = kBlock / per;
     double acc = 0.0;
     for (int s = grp * ns; s < (grp + 1) * ns; ++s)
-      acc += (double)__uint_as_float((uint32_t)tile[kV ? c * ldv + s : s * ldq + c] << 16);
+      acc += (double)__uint_as_float((uint32_t)tile[s * ldq + c] << 16);
     part[threadIdx.x] = acc;
     __syncthreads();
     if (threadIdx.x < d) {
