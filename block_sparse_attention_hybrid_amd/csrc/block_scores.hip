@@ -12,7 +12,8 @@
 // scores; each wave owns a 32 x 32 quarter as 2 x 2 MFMA tiles of 16 x 16.
 // Operand lanes: A row = lane % 16, B column = lane % 16, k = lane / 16; the
 // accumulator's register r of lane l holds row l / 16 + 4 r, column l % 16.
-// The k dimension (d) is staged through LDS 16 columns at a time.
+// The k dimension (d) is staged through LDS 16 columns at a time; the global
+// loads of the next 16 columns are in flight while the current ones are used.
 #include "sa_launch.h"
 
 namespace sa {
@@ -45,16 +46,31 @@ __global__ __launch_bounds__(kThreads) void block_scores_kernel(const double* __
 
   const int lr = threadIdx.x >> 2;          // tile row this thread stages
   const int lc = (threadIdx.x & 3) * 4;     // first of its 4 columns
-  for (int k0 = 0; k0 < d; k0 += kKc) {
-    {
-      const int gi = i0 + lr, gj = j0 + lr;
+  const int gi = i0 + lr, gj = j0 + lr;
+  const double* qrow = qh + (long long)(gi < n ? gi : n - 1) * d + lc;
+  const double* krow = kh + (long long)(gj < n ? gj : n - 1) * d + lc;
+  // the next step's operands are loaded into registers while this step's
+  // products run (rows past n read a clamped row and are zeroed)
+  double an[4], bn[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        As[lr * kLd + lc + e] = gi < n ? qh[(long long)gi * d + k0 + lc + e] : 0.0;
-        Bs[lr * kLd + lc + e] = gj < n ? kh[(long long)gj * d + k0 + lc + e] : 0.0;
-      }
+  for (int e = 0; e < 4; ++e) {
+    an[e] = qrow[e];
+    bn[e] = krow[e];
+  }
+  for (int k0 = 0; k0 < d; k0 += kKc) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      As[lr * kLd + lc + e] = gi < n ? an[e] : 0.0;
+      Bs[lr * kLd + lc + e] = gj < n ? bn[e] : 0.0;
     }
     __syncthreads();
+    if (k0 + kKc < d) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        an[e] = qrow[k0 + kKc + e];
+        bn[e] = krow[k0 + kKc + e];
+      }
+    }
 #pragma unroll
     for (int ks = 0; ks < kKc; ks += 4) {
       const int kk = ks + (lane >> 4);

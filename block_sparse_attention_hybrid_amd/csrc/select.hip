@@ -28,8 +28,8 @@
 // workgroup, wave w holding the contiguous ids [64 E w, 64 E (w + 1)) as E
 // registers per lane, so every wave compacts its own kept ids in ascending
 // order with ballots and only per-wave totals cross waves (through LDS).  The
-// histogram is shared; every wave reads all of it and runs the same scan, so
-// the decisions need no broadcast.
+// histogram is shared; wave 0 scans it and posts each round's decision in
+// LDS.
 //
 // Probabilities are exp2 of the float64 score differences in float32, summed
 // as 2^-40 fixed-point integers: integer LDS atomics make the histograms (and
@@ -195,6 +195,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const double* __restri
   __shared__ double xlo[kWaves], xhi[kWaves];
   __shared__ unsigned long long xk0[kWaves], xk1[kWaves];
   __shared__ int xn[kWaves];
+  __shared__ unsigned long long xdec[5];   // bucket, its count, count and mass before it, target
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
   const int first_id = wave * kWave * E;
   const uint64_t lt = lanemask_lt();
@@ -345,60 +346,72 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const double* __restri
         }
       __syncthreads();
 
-      // every wave scans all 256 buckets, lane L taking buckets 4L .. 4L+3
-      uint32_t c4[4];
-      unsigned long long m4[4];
-      uint32_t lc = 0;
-      unsigned long long lm = 0;
+      // wave 0 scans the 256 buckets (lane L taking buckets 4L .. 4L+3) and
+      // posts the decision; the other waves read it after the barrier
+      if (wave == 0) {
+        uint32_t c4[4];
+        unsigned long long m4[4];
+        uint32_t lc = 0;
+        unsigned long long lm = 0;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const unsigned long long hw = hist[lane * 4 + t];
-        if constexpr (kPacked) {
-          c4[t] = (uint32_t)(hw >> kCountShift);
-          m4[t] = hw & kMassMask;
-        } else {
-          c4[t] = hcnt[lane * 4 + t];
-          m4[t] = hw;
+        for (int t = 0; t < 4; ++t) {
+          const unsigned long long hw = hist[lane * 4 + t];
+          if constexpr (kPacked) {
+            c4[t] = (uint32_t)(hw >> kCountShift);
+            m4[t] = hw & kMassMask;
+          } else {
+            c4[t] = hcnt[lane * 4 + t];
+            m4[t] = hw;
+          }
+          lc += c4[t];
+          lm += m4[t];
         }
-        lc += c4[t];
-        lm += m4[t];
-      }
-      uint32_t ic = lc;
-      uint64_t im = lm;
-      wave_scan(ic, im, lane);
-      if (round == 0) {  // every element is a member: the total is Z
-        const unsigned long long z = readlane64(im, kWave - 1);
-        target = p > 0.0 ? (unsigned long long)ceil(p * (double)z) : 0ull;
-      }
-      uint32_t xc = ic - lc;            // exclusive prefix of this lane's first bucket
-      unsigned long long xm = im - lm;
-      int first = 4;
-      uint32_t first_xc = 0, first_c = 0;
-      unsigned long long first_xm = 0;
+        uint32_t ic = lc;
+        uint64_t im = lm;
+        wave_scan(ic, im, lane);
+        if (round == 0) {  // every element is a member: the total is Z
+          const unsigned long long z = readlane64(im, kWave - 1);
+          target = p > 0.0 ? (unsigned long long)ceil(p * (double)z) : 0ull;
+        }
+        uint32_t xc = ic - lc;            // exclusive prefix of this lane's first bucket
+        unsigned long long xm = im - lm;
+        int first = 4;
+        uint32_t first_xc = 0, first_c = 0;
+        unsigned long long first_xm = 0;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const bool ok = (cnt_above + (long long)(xc + c4[t]) >= kc) && (mass_above + xm + m4[t] >= target);
-        if (ok && first == 4) {
-          first = t;
-          first_xc = xc;
-          first_xm = xm;
-          first_c = c4[t];
+        for (int t = 0; t < 4; ++t) {
+          const bool ok = (cnt_above + (long long)(xc + c4[t]) >= kc) && (mass_above + xm + m4[t] >= target);
+          if (ok && first == 4) {
+            first = t;
+            first_xc = xc;
+            first_xm = xm;
+            first_c = c4[t];
+          }
+          xc += c4[t];
+          xm += m4[t];
         }
-        xc += c4[t];
-        xm += m4[t];
+        const uint64_t hit = ballot(first < 4);
+        const int src = hit ? (__ffsll((long long)hit) - 1) : (kWave - 1);
+        if (!hit && lane == kWave - 1) {  // unreachable: all members always satisfy both
+          first = 3;
+          first_xc = ic - c4[3];
+          first_xm = im - m4[3];
+          first_c = c4[3];
+        }
+        if (lane == 0) {
+          xdec[0] = (unsigned long long)(4 * src + (int)readlane((uint32_t)first, src));
+          xdec[1] = readlane(first_c, src);
+          xdec[2] = readlane(first_xc, src);
+          xdec[3] = readlane64(first_xm, src);
+          xdec[4] = target;
+        }
       }
-      const uint64_t hit = ballot(first < 4);
-      const int src = hit ? (__ffsll((long long)hit) - 1) : (kWave - 1);
-      if (!hit && lane == kWave - 1) {  // unreachable: all members always satisfy both
-        first = 3;
-        first_xc = ic - c4[3];
-        first_xm = im - m4[3];
-        first_c = c4[3];
-      }
-      const int bstar = 4 * src + (int)readlane((uint32_t)first, src);
-      cnt_above += (long long)readlane(first_xc, src);
-      mass_above += readlane64(first_xm, src);
-      m = (int)readlane(first_c, src);
+      __syncthreads();
+      const int bstar = (int)xdec[0];
+      m = (int)xdec[1];
+      cnt_above += (long long)xdec[2];
+      mass_above += xdec[3];
+      target = xdec[4];
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         const bool mem = (member >> e) & 1ull;
