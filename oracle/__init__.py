@@ -8,4 +8,5 @@ from .oracle import (Geometry, MaskResult, RowSelection, attention_block,
                      sparse_attention_backward, pooled_mass, mask_error,
                      dense_attention, pool, rank_order, real_slots, reorder,
                      select_row, select_rows, sparse_attention, token_slots,
-                     top_p_count, unreorder, unreorder_rows, NEAR_TIE)
+                     top_p_count, unreorder, unreorder_rows, NEAR_TIE,
+                     group_count, pool_groups, build_mask_groups, expand_group_lists)

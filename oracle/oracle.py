@@ -67,6 +67,15 @@ What it computes, step by step, in float64 (bfloat16 inputs convert exactly):
    query block the relative L1 error sum|o - o_s| / sum|o| of the sparse output
    against dense attention.
 
+10. Asymmetric blocks (SpargeAttention2 summary page, "Block-Pooled Attention
+   for Efficient Mask Construction": query blocks of b_q tokens and key blocks
+   of b_kv tokens, b_q = 128 and b_kv = 64 there).  Reading in the cube-major
+   order: a query block is qg consecutive cubes (qg = 2 gives 128 query
+   slots), pooled over its real tokens; key blocks stay single cubes.  Each
+   query block's row of nblk block scores is selected with the unchanged rule
+   (kc = ceil(k * nblk)), and every cube of the group attends through that
+   one list.
+
 Readings where the pages are silent or garbled are listed in the repository's
 design notes; the ones this file depends on are repeated at each function.
 Every function here is pinned by the CPU tests (worked examples, closed forms,
@@ -571,3 +580,62 @@ def mask_error(qc: np.ndarray, kc_: np.ndarray, vc: np.ndarray, lut: np.ndarray,
                 rel[b, h, i] = num / den if den > 0 else 0.0
             tau[b, h] = t
     return tau, rel
+
+
+# ----------------------------------------------------------------------------
+# 10. asymmetric blocks: query blocks of qg cubes, key blocks of one cube
+# ----------------------------------------------------------------------------
+def group_count(nblk: int, qg: int) -> int:
+    """Query blocks per head when each holds qg consecutive cubes (the last
+    one may hold fewer)."""
+    return -(-nblk // qg)
+
+
+def pool_groups(xc: np.ndarray, g: Geometry, qg: int) -> np.ndarray:
+    """Mean over the real tokens of each group of qg consecutive blocks:
+    [..., n_pad, d] -> [..., ceil(nblk / qg), d]."""
+    xc = np.asarray(xc, dtype=np.float64)
+    d = xc.shape[-1]
+    real = real_slots(g)
+    nq = group_count(g.nblk, qg)
+    out = np.zeros(xc.shape[:-2] + (nq, d))
+    for a in range(nq):
+        lo, hi = a * qg * g.block, min((a + 1) * qg, g.nblk) * g.block
+        keep = np.nonzero(real[lo:hi])[0] + lo
+        out[..., a, :] = xc[..., keep, :].sum(axis=-2) / keep.size
+    return out
+
+
+def build_mask_groups(qc: np.ndarray, kc_: np.ndarray, g: Geometry, qg: int,
+                      k_frac: float, p: float) -> MaskResult:
+    """Pool (queries per group of qg cubes, keys per cube) -> block scores
+    [B, H, nq, nblk] -> hybrid selection of every query block's row with
+    kc = ceil(k_frac * nblk).  Lists are [B, H, nq, nblk]."""
+    d = qc.shape[-1]
+    qbar = pool_groups(qc, g, qg)
+    kbar = pool(kc_, g)
+    s = block_scores(qbar, kbar, d)
+    B, H, nq, n = s.shape
+    lut = np.full((B, H, nq, n), -1, dtype=np.int32)
+    counts = np.zeros((B, H, nq), dtype=np.int32)
+    flags = np.zeros((B, H, nq), dtype=bool)
+    pcs = np.zeros((B, H, nq), dtype=np.int32)
+    kc = ceil_k(k_frac, n)
+    for b in range(B):
+        for h in range(H):
+            probs = block_softmax(s[b, h])
+            for i in range(nq):
+                sel = select_row(s[b, h, i], kc, p, probs[i])
+                c = sel.kept.shape[0]
+                lut[b, h, i, :c] = sel.kept
+                counts[b, h, i] = c
+                flags[b, h, i] = sel.near_tie
+                pcs[b, h, i] = sel.pc
+    return MaskResult(lut, counts, flags, np.full((B, H, nq), kc, dtype=np.int32), pcs, s, qbar, kbar)
+
+
+def expand_group_lists(lut: np.ndarray, counts: np.ndarray, qg: int, nblk: int):
+    """Per-cube lists for sparse_attention: cube i uses the list of its query
+    block i // qg."""
+    rows = np.arange(nblk) // qg
+    return lut[..., rows, :], counts[..., rows]

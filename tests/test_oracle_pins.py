@@ -753,3 +753,67 @@ def test_pooled_mass_closed_forms():
     np.testing.assert_allclose(O.pooled_mass(s, lut, counts), want, rtol=1e-13)
     counts[:] = 0
     assert np.all(O.pooled_mass(s, lut, counts) == 0.0)
+
+
+# ----------------------------------------------------------------------------
+# asymmetric blocks: query blocks of qg cubes
+# ----------------------------------------------------------------------------
+def test_pool_groups_equals_coordinate_gather_mean():
+    # a query block is qg consecutive cubes in cube order; its mean is taken
+    # straight from the row-major tokens by their coordinates
+    T, H, W, d = 5, 6, 9, 3
+    g = O.Geometry(T, H, W)
+    rng = np.random.default_rng(61)
+    x = rng.standard_normal((T * H * W, d))
+    t, h, w = np.meshgrid(np.arange(T), np.arange(H), np.arange(W), indexing="ij")
+    cube = ((t // 4) * g.nh + h // 4) * g.nw + w // 4
+    for qg in (1, 2, 3):
+        got = O.pool_groups(O.reorder(x, g), g, qg)
+        assert got.shape == (O.group_count(g.nblk, qg), d)
+        grp = (cube // qg).reshape(-1)
+        want = np.stack([x[grp == a].mean(axis=0) for a in range(got.shape[0])])
+        np.testing.assert_allclose(got, want, rtol=1e-14, atol=1e-15)
+
+
+def test_pool_groups_weighted_cube_means_and_identity():
+    g = O.Geometry(9, 9, 9)                   # partial cubes on every side, odd nblk
+    assert g.nblk % 2 == 1
+    rng = np.random.default_rng(62)
+    xc = O.reorder(rng.standard_normal((2, g.n_real, 4)), g)
+    np.testing.assert_array_equal(O.pool_groups(xc, g, 1), O.pool(xc, g))
+    cube = O.pool(xc, g)
+    r = O.real_slots(g).reshape(g.nblk, g.block).sum(axis=1).astype(float)
+    grp = O.pool_groups(xc, g, 2)
+    for a in range(g.nblk // 2):
+        i, j = 2 * a, 2 * a + 1
+        want = (r[i] * cube[:, i] + r[j] * cube[:, j]) / (r[i] + r[j])
+        np.testing.assert_allclose(grp[:, a], want, rtol=1e-13)
+    np.testing.assert_allclose(grp[:, -1], cube[:, -1], rtol=1e-15)   # the lone last cube
+
+
+def test_build_mask_groups_rows_counts_and_scores():
+    g = O.Geometry(4, 8, 12)
+    rng = np.random.default_rng(63)
+    qc = O.reorder(rng.standard_normal((1, 2, g.n_real, 8)), g)
+    kc_ = O.reorder(rng.standard_normal((1, 2, g.n_real, 8)), g)
+    one = O.build_mask_groups(qc, kc_, g, 1, 0.2, 0.5)
+    ref = O.build_mask(qc, kc_, g, 0.2, 0.5)
+    np.testing.assert_array_equal(one.lut, ref.lut)
+    np.testing.assert_array_equal(one.counts, ref.counts)
+    two = O.build_mask_groups(qc, kc_, g, 2, 0.25, 0.0)
+    nq = O.group_count(g.nblk, 2)
+    assert two.lut.shape == (1, 2, nq, g.nblk)
+    # the Top-k count is a fraction of the key blocks, not of the query blocks
+    assert np.all(two.counts == O.ceil_k(0.25, g.nblk))
+    qbar = O.pool_groups(qc, g, 2)
+    kbar = O.pool(kc_, g)
+    want = np.einsum("bhid,bhjd->bhij", qbar, kbar) / math.sqrt(8)
+    np.testing.assert_allclose(two.scores, want, rtol=1e-13, atol=1e-15)
+    for i in range(nq):
+        top = np.argsort(-want[0, 1, i], kind="stable")[:two.counts[0, 1, i]]
+        np.testing.assert_array_equal(two.lut[0, 1, i, :two.counts[0, 1, i]], np.sort(top))
+    lut_e, cnt_e = O.expand_group_lists(two.lut, two.counts, 2, g.nblk)
+    assert lut_e.shape == (1, 2, g.nblk, g.nblk)
+    for i in range(g.nblk):
+        np.testing.assert_array_equal(lut_e[:, :, i], two.lut[:, :, i // 2])
+        np.testing.assert_array_equal(cnt_e[:, :, i], two.counts[:, :, i // 2])
