@@ -250,6 +250,24 @@ def next_rows(path, reps=3):
                        "frac_of_bf16_peak": round(fl / t_bwd / 1e9 / PEAK_BF16_TFLOPS, 4),
                        "flops_note": "10*64*64*d per kept block pair (the five products of the gradient)"}
     del lay, dq, dk, dv, lut_t
+    # asymmetric blocks: query blocks of 2 cubes (128 query slots), one list each
+    nq = -(-n // 2)
+    lut2 = torch.empty((B, H, nq, n), dtype=torch.int32, device=dev)
+    counts2 = torch.empty((B, H, nq), dtype=torch.int32, device=dev)
+    ws2 = torch.empty(sa.sparse_attn_mask_groups_workspace_bytes(g, 2), dtype=torch.uint8, device=dev)
+    t_m2 = time_call(lambda: sa.sparse_attn_build_mask_groups(path.qc, path.kc, g, 2, path.k_frac, path.p, lut2,
+                                                              counts2, n, ws2), reps)
+    oc2, lse2 = torch.empty_like(path.oc), torch.empty_like(path.lse_c)
+    t_f2 = time_call(lambda: sa.sparse_attn_fwd_groups(path.qc, path.kc, path.vc, lut2, counts2, n, 2, g, 0.0,
+                                                       oc2, lse2), reps)
+    c2 = counts2.to(torch.int64)
+    pairs = int(2 * c2.sum().item() - (c2[..., -1].sum().item() if n % 2 else 0))
+    fl = pairs * 4.0 * 64 * 64 * d
+    out["query_blocks_128"] = {"mask_ms": round(t_m2, 4), "fwd_ms": round(t_f2, 4),
+                               "density": round(pairs / (B * H * n * n), 4),
+                               "fwd_tflops": round(fl / t_f2 / 1e9, 2),
+                               "frac_of_bf16_peak": round(fl / t_f2 / 1e9 / PEAK_BF16_TFLOPS, 4)}
+    del lut2, oc2
     # mask quality of the timed lists against dense attention (every block kept)
     t0 = time.perf_counter()
     mass, tau, rel = sa.mask_quality(path.qc, path.kc, path.vc, path.lut, path.counts, path.scores, g)

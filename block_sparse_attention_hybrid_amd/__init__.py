@@ -38,6 +38,7 @@ EXPORTED = (
     "sparse_attn_coarse", "sparse_attn_router_pool", "sparse_attn_router_scores",
     "sparse_attn_bwd_delta", "sparse_attn_transpose_workspace_bytes", "sparse_attn_transpose_lut",
     "sparse_attn_bwd", "sparse_attn_pooled_mass", "sparse_attn_mask_error", "sparse_attn_attention",
+    "sparse_attn_mask_groups_workspace_bytes", "sparse_attn_build_mask_groups", "sparse_attn_fwd_groups",
     "sparse_attn_last_error",
 )
 
@@ -107,6 +108,9 @@ _SIGS = {
     "sparse_attn_pooled_mass": (_i32, [_vp, _vp, _vp, _i32, _GP, _vp, _vp]),
     "sparse_attn_mask_error": (_i32, [_vp, _vp, _vp, _vp, _GP, _vp, _vp, _vp]),
     "sparse_attn_attention": (_i32, [ctypes.POINTER(PathBuffers), _GP, _f64, _f64, _f32, _i32, _vp, _vp]),
+    "sparse_attn_mask_groups_workspace_bytes": (_sz, [_GP, _i32]),
+    "sparse_attn_build_mask_groups": (_i32, [_vp, _vp, _GP, _i32, _f64, _f64, _vp, _vp, _i32, _vp, _sz, _vp]),
+    "sparse_attn_fwd_groups": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _GP, _f32, _vp, _vp, _vp]),
     "sparse_attn_last_error": (ctypes.c_char_p, []),
 }
 
@@ -352,6 +356,29 @@ def unreorder(oc: torch.Tensor, lse_c: Optional[torch.Tensor], g: Geom, stream=N
     return o, lse
 
 
+def sparse_attn_mask_groups_workspace_bytes(g: Geom, qgroup: int) -> int:
+    return int(lib().sparse_attn_mask_groups_workspace_bytes(ctypes.byref(g), int(qgroup)))
+
+
+def sparse_attn_build_mask_groups(qc, kc, g: Geom, qgroup: int, k_frac: float, p: float, lut, counts,
+                                  cap: int, workspace, stream=None) -> None:
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().sparse_attn_build_mask_groups(_ptr(qc, torch.bfloat16, "qc"), _ptr(kc, torch.bfloat16, "kc"),
+                                               ctypes.byref(g), int(qgroup), float(k_frac), float(p),
+                                               _ptr(lut, torch.int32, "lut"), _ptr(counts, torch.int32, "counts"),
+                                               int(cap), _ptr(workspace, None, "workspace"), ws_bytes,
+                                               _stream(stream, qc)))
+
+
+def sparse_attn_fwd_groups(qc, kc, vc, lut, counts, cap: int, qgroup: int, g: Geom, scale: float, oc, lse_c,
+                           stream=None) -> None:
+    _check(lib().sparse_attn_fwd_groups(_ptr(qc, torch.bfloat16, "qc"), _ptr(kc, torch.bfloat16, "kc"),
+                                        _ptr(vc, torch.bfloat16, "vc"), _ptr(lut, torch.int32, "lut"),
+                                        _ptr(counts, torch.int32, "counts"), int(cap), int(qgroup),
+                                        ctypes.byref(g), float(scale), _ptr(oc, torch.bfloat16, "oc"),
+                                        _ptr(lse_c, torch.float32, "lse_c"), _stream(stream, qc)))
+
+
 def mask_workspace(g: Geom, device) -> torch.Tensor:
     return torch.empty(sparse_attn_mask_workspace_bytes(g), dtype=torch.uint8, device=device)
 
@@ -377,6 +404,28 @@ def fwd(qc, kc, vc, lut, counts, g: Geom, scale: float = 0.0, stream=None):
     nws = sparse_attn_fwd_workspace_bytes(g)
     ws = None if nws == 0 else torch.empty(nws, dtype=torch.uint8, device=qc.device)
     sparse_attn_fwd(qc, kc, vc, lut, counts, lut.shape[-1], g, scale, oc, lse_c, ws, stream)
+    return oc, lse_c
+
+
+def build_mask_groups(qc, kc, g: Geom, qgroup: int, k_frac: float, p: float, cap=None, stream=None):
+    """Lists of the asymmetric blocks: one per query block of qgroup cubes
+    (lut [B,H,nq,cap] int32, counts [B,H,nq] int32, nq = ceil(nblk/qgroup))."""
+    nblk, _, _ = sparse_attn_geometry(g)
+    nq = -(-nblk // qgroup)
+    cap = nblk if cap is None else cap
+    lut = _empty((g.batch, g.heads, nq, cap), torch.int32, qc)
+    counts = _empty((g.batch, g.heads, nq), torch.int32, qc)
+    ws = torch.empty(sparse_attn_mask_groups_workspace_bytes(g, qgroup), dtype=torch.uint8, device=qc.device)
+    sparse_attn_build_mask_groups(qc, kc, g, qgroup, k_frac, p, lut, counts, cap, ws, stream)
+    return lut, counts
+
+
+def fwd_groups(qc, kc, vc, lut, counts, g: Geom, qgroup: int, scale: float = 0.0, stream=None):
+    """Forward over lists shared by the qgroup cubes of each query block."""
+    _, _, n_pad = sparse_attn_geometry(g)
+    oc = _empty((g.batch, g.heads, n_pad, g.head_dim), torch.bfloat16, qc)
+    lse_c = _empty((g.batch, g.heads, n_pad), torch.float32, qc)
+    sparse_attn_fwd_groups(qc, kc, vc, lut, counts, lut.shape[-1], qgroup, g, scale, oc, lse_c, stream)
     return oc, lse_c
 
 

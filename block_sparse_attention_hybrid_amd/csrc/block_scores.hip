@@ -28,13 +28,13 @@ constexpr int kLd = kKc + 1;       // padded LDS row (doubles)
 __global__ __launch_bounds__(kThreads) void block_scores_kernel(const double* __restrict__ qbar,
                                                                 const double* __restrict__ kbar,
                                                                 double* __restrict__ scores,
-                                                                double scale, Geom g) {
+                                                                double scale, Geom g, int nrows) {
   __shared__ double As[kTile * kLd];
   __shared__ double Bs[kTile * kLd];
-  const int n = g.nblk, d = g.d;
+  const int n = g.nblk, d = g.d;   // n key blocks; nrows query rows (n, or n / qg groups)
   const int i0 = blockIdx.y * kTile, j0 = blockIdx.x * kTile;
   const long long bh = blockIdx.z;
-  const double* qh = qbar + bh * (long long)n * d;
+  const double* qh = qbar + bh * (long long)nrows * d;
   const double* kh = kbar + bh * (long long)n * d;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -47,7 +47,7 @@ __global__ __launch_bounds__(kThreads) void block_scores_kernel(const double* __
   const int lr = threadIdx.x >> 2;          // tile row this thread stages
   const int lc = (threadIdx.x & 3) * 4;     // first of its 4 columns
   const int gi = i0 + lr, gj = j0 + lr;
-  const double* qrow = qh + (long long)(gi < n ? gi : n - 1) * d + lc;
+  const double* qrow = qh + (long long)(gi < nrows ? gi : nrows - 1) * d + lc;
   const double* krow = kh + (long long)(gj < n ? gj : n - 1) * d + lc;
   // the next step's operands are loaded into registers while this step's
   // products run (rows past n read a clamped row and are zeroed)
@@ -60,7 +60,7 @@ __global__ __launch_bounds__(kThreads) void block_scores_kernel(const double* __
   for (int k0 = 0; k0 < d; k0 += kKc) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      As[lr * kLd + lc + e] = gi < n ? an[e] : 0.0;
+      As[lr * kLd + lc + e] = gi < nrows ? an[e] : 0.0;
       Bs[lr * kLd + lc + e] = gj < n ? bn[e] : 0.0;
     }
     __syncthreads();
@@ -86,7 +86,7 @@ __global__ __launch_bounds__(kThreads) void block_scores_kernel(const double* __
     }
     __syncthreads();
   }
-  double* out = scores + bh * (long long)n * n;
+  double* out = scores + bh * (long long)nrows * n;
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -95,17 +95,18 @@ __global__ __launch_bounds__(kThreads) void block_scores_kernel(const double* __
       for (int r = 0; r < 4; ++r) {
         const int row = i0 + wm * 32 + mt * 16 + (lane >> 4) + 4 * r;
         const int col = j0 + wn * 32 + nt * 16 + (lane & 15);
-        if (row < n && col < n) out[(long long)row * n + col] = acc[mt][nt][r] * scale;
+        if (row < nrows && col < n) out[(long long)row * n + col] = acc[mt][nt][r] * scale;
       }
 }
 
 }  // namespace
 
 hipError_t launch_block_scores(const double* qbar, const double* kbar, double* scores,
-                               double scale, const Geom& g, hipStream_t s) {
-  const int tiles = (g.nblk + kTile - 1) / kTile;
-  dim3 grid(tiles, tiles, g.batch * g.heads);
-  block_scores_kernel<<<grid, kThreads, 0, s>>>(qbar, kbar, scores, scale, g);
+                               double scale, const Geom& g, hipStream_t s, int nrows) {
+  if (nrows < 0) nrows = g.nblk;
+  const int ctiles = (g.nblk + kTile - 1) / kTile, rtiles = (nrows + kTile - 1) / kTile;
+  dim3 grid(ctiles, rtiles, g.batch * g.heads);
+  block_scores_kernel<<<grid, kThreads, 0, s>>>(qbar, kbar, scores, scale, g, nrows);
   return hipGetLastError();
 }
 

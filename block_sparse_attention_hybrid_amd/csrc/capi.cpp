@@ -124,6 +124,22 @@ size_t mask_ws_bytes(const sa::Geom& d) {
   return 2 * round_up(rows * d.d * sizeof(double)) + round_up(rows * d.nblk * sizeof(double));
 }
 
+// qgroup in {1, 2, 4}; returns log2(qgroup) in shift
+int32_t check_qgroup(int32_t qgroup, int& shift) {
+  if (qgroup != 1 && qgroup != 2 && qgroup != 4)
+    return fail(SA_ERR_INVALID_ARG, "qgroup must be 1, 2 or 4 (got %d)", qgroup);
+  shift = qgroup == 1 ? 0 : (qgroup == 2 ? 1 : 2);
+  return SA_OK;
+}
+
+// group means of Q [rows_q, d], block means of K [rows, d], scores [rows_q, nblk]
+size_t mask_groups_ws_bytes(const sa::Geom& d, int qgroup) {
+  const size_t bh = (size_t)d.batch * d.heads;
+  const size_t nq = (size_t)(d.nblk + qgroup - 1) / qgroup;
+  return round_up(bh * nq * d.d * sizeof(double)) + round_up(bh * d.nblk * d.d * sizeof(double)) +
+         round_up(bh * nq * d.nblk * sizeof(double));
+}
+
 }  // namespace
 
 extern "C" {
@@ -432,6 +448,65 @@ int32_t sparse_attn_build_mask(const void* qc, const void* kc, const sa_geom* g,
   SA_TRY(hip_status(sa::launch_block_scores(qbar, kbar, scores, 1.0 / std::sqrt((double)d.d), d, s),
                     "block score launch"));
   return hip_status(sa::launch_select(scores, d, kcount, p, row_budget, lut, counts, cap, s), "select launch");
+}
+
+size_t sparse_attn_mask_groups_workspace_bytes(const sa_geom* g, int32_t qgroup) {
+  sa::Geom d;
+  int shift = 0;
+  if (make_geom(g, d) != SA_OK || check_qgroup(qgroup, shift) != SA_OK) return 0;
+  return mask_groups_ws_bytes(d, qgroup);
+}
+
+int32_t sparse_attn_build_mask_groups(const void* qc, const void* kc, const sa_geom* g, int32_t qgroup,
+                                      double k_frac, double p, int32_t* lut, int32_t* counts, int32_t cap,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  sa::Geom d;
+  SA_TRY(make_geom(g, d));
+  int shift = 0;
+  SA_TRY(check_qgroup(qgroup, shift));
+  SA_TRY(check_ptr(qc, 16, "qc"));
+  SA_TRY(check_ptr(kc, 16, "kc"));
+  int kcount = 0;
+  SA_TRY(check_select_args(d, k_frac, p, nullptr, lut, counts, cap, kcount));
+  SA_TRY(check_ptr(workspace, kWsAlign, "workspace"));
+  const size_t need = mask_groups_ws_bytes(d, qgroup);
+  if (workspace_bytes < need)
+    return fail(SA_ERR_CAPACITY, "workspace of %zu bytes is below the %zu needed", workspace_bytes, need);
+  const size_t bh = (size_t)d.batch * d.heads;
+  const int nq = (d.nblk + qgroup - 1) / qgroup;
+  char* ws = static_cast<char*>(workspace);
+  double* qbar = reinterpret_cast<double*>(ws);
+  double* kbar = reinterpret_cast<double*>(ws + round_up(bh * nq * d.d * sizeof(double)));
+  double* scores = reinterpret_cast<double*>(ws + round_up(bh * nq * d.d * sizeof(double)) +
+                                             round_up(bh * d.nblk * d.d * sizeof(double)));
+  hipStream_t s = (hipStream_t)stream;
+  SA_TRY(hip_status(sa::launch_pool_groups(qc, qbar, qgroup, d, s), "group pool launch"));
+  SA_TRY(hip_status(sa::launch_pool_groups(kc, kbar, 1, d, s), "pool launch"));
+  SA_TRY(hip_status(sa::launch_block_scores(qbar, kbar, scores, 1.0 / std::sqrt((double)d.d), d, s, nq),
+                    "block score launch"));
+  return hip_status(sa::launch_select(scores, d, kcount, p, nullptr, lut, counts, cap, s, nq), "select launch");
+}
+
+int32_t sparse_attn_fwd_groups(const void* qc, const void* kc, const void* vc, const int32_t* lut,
+                               const int32_t* counts, int32_t cap, int32_t qgroup, const sa_geom* g,
+                               float scale, void* oc, float* lse_c, void* stream) {
+  sa::Geom d;
+  SA_TRY(make_geom(g, d));
+  int shift = 0;
+  SA_TRY(check_qgroup(qgroup, shift));
+  SA_TRY(check_ptr(qc, 16, "qc"));
+  SA_TRY(check_ptr(kc, 16, "kc"));
+  SA_TRY(check_ptr(vc, 16, "vc"));
+  SA_TRY(check_ptr(lut, 4, "lut"));
+  SA_TRY(check_ptr(counts, 4, "counts"));
+  SA_TRY(check_ptr(oc, 16, "oc"));
+  SA_TRY(check_ptr(lse_c, 4, "lse_c"));
+  if (cap < 1) return fail(SA_ERR_INVALID_ARG, "cap must be >= 1");
+  if (!std::isfinite(scale)) return fail(SA_ERR_INVALID_ARG, "scale must be finite");
+  if (scale <= 0.f) scale = (float)(1.0 / std::sqrt((double)d.d));
+  return hip_status(sa::launch_fwd(qc, kc, vc, lut, counts, cap, d, scale, oc, lse_c, nullptr,
+                                   (hipStream_t)stream, shift),
+                    "fwd launch");
 }
 
 size_t sparse_attn_fwd_workspace_bytes(const sa_geom* g) {

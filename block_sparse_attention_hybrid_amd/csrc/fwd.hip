@@ -126,7 +126,8 @@ __global__ __launch_bounds__(64) void fwd_kernel(const u32x4* __restrict__ qc,
                                                  const int32_t* __restrict__ lut,
                                                  const int32_t* __restrict__ counts, int cap, Geom g,
                                                  float sc_log2, bf16* __restrict__ oc,
-                                                 float* __restrict__ lse_c, RowMap map, CubeDiv cd) {
+                                                 float* __restrict__ lse_c, RowMap map, CubeDiv cd,
+                                                 int qg_shift) {
   constexpr int NDS = D / 16;     // 16-dim steps of S^T
   constexpr int NDT = D / 32;     // 32-dim tiles of O^T
   constexpr int BLK = 64 * D / 8; // 16-byte units per block
@@ -155,9 +156,13 @@ __global__ __launch_bounds__(64) void fwd_kernel(const u32x4* __restrict__ qc,
 #pragma unroll
   for (int c = 0; c < 2 * NDS; ++c) qreg[c] = qb[c * 64 + lane];
 
-  int count = counts[row];
+  // the list of this query block: one per cube, or one per group of
+  // 2^qg_shift consecutive cubes (asymmetric query blocks)
+  const int nlists = (g.nblk + (1 << qg_shift) - 1) >> qg_shift;
+  const long long lrow_i = bh * nlists + (i >> qg_shift);
+  int count = counts[lrow_i];
   count = count < 0 ? 0 : (count > cap ? cap : count);
-  const int32_t* lrow = lut + (long long)row * cap;
+  const int32_t* lrow = lut + lrow_i * cap;
 
   f32x16 acc[NDT][2];
 #pragma unroll
@@ -406,7 +411,7 @@ size_t fwd_workspace_bytes(const Geom&) { return 0; }
 
 hipError_t launch_fwd(const void* qc, const void* kc, const void* vc, const int32_t* lut,
                       const int32_t* counts, int cap, const Geom& g, float scale, void* oc,
-                      float* lse_c, void*, hipStream_t s) {
+                      float* lse_c, void*, hipStream_t s, int qg_shift) {
   const RowMap map = make_rowmap(g.nblk, g.batch * g.heads);
   const CubeDiv cd = {make_fastdiv((uint32_t)g.nw), make_fastdiv((uint32_t)g.nh)};
   const float sc_log2 = scale * 1.4426950408889634f;
@@ -416,10 +421,10 @@ hipError_t launch_fwd(const void* qc, const void* kc, const void* vc, const int3
   const u32x4* v = static_cast<const u32x4*>(vc);
   if (g.d == 128)
     fwd_kernel<128><<<grid, 64, 0, s>>>(q, k, v, lut, counts, cap, g, sc_log2, static_cast<bf16*>(oc), lse_c,
-                                        map, cd);
+                                        map, cd, qg_shift);
   else
     fwd_kernel<64><<<grid, 64, 0, s>>>(q, k, v, lut, counts, cap, g, sc_log2, static_cast<bf16*>(oc), lse_c,
-                                       map, cd);
+                                       map, cd, qg_shift);
   return hipGetLastError();
 }
 

@@ -5,6 +5,11 @@
 // summary page, "The Coarse Stage".  Pad slots of a partial cube are not
 // tokens and are skipped; the sum is divided by the block's real-token count.
 //
+// The grouped form pools queries over query blocks of qg consecutive cubes
+// (SpargeAttention2's b_q = 128 against b_kv = 64 is qg = 2): the sums of the
+// group's cubes meet in the same accumulators and are divided by the group's
+// real-token count.
+//
 // One workgroup per (batch*head, block) reads the block's 64 x d bf16 values
 // of Q and of K once, as whole 1 KB chunks of the QK layout (sa_layout.h),
 // and sums them in float64 -- exact for bf16 inputs -- so the pooled vectors
@@ -29,57 +34,65 @@ __device__ __forceinline__ void add_bf16x8(double acc[8], const u32x4 v) {
   }
 }
 
-template <int D>
+// NT tensors (Q, or Q and K) pooled over groups of qg cubes (qg = 1: blocks)
+template <int D, int NT>
 __global__ __launch_bounds__(kThreads) void pool_kernel(const u32x4* __restrict__ qc,
                                                         const u32x4* __restrict__ kc,
                                                         double* __restrict__ qbar,
-                                                        double* __restrict__ kbar, Geom g) {
+                                                        double* __restrict__ kbar, Geom g, int qg,
+                                                        int ngroups) {
   constexpr int NDS = D / 16;            // 16-dim chunks per 32 tokens
   constexpr int J = kBlock * D / 8 / kThreads;   // 16-byte units per thread
   constexpr int NSLOT = NDS / 4;         // distinct ds values per thread
-  const int i = blockIdx.x;
+  const int a = blockIdx.x;              // group (the block itself when qg == 1)
   const long long bh = blockIdx.y;
   const int p = threadIdx.x & 63, h = p >> 5, r = p & 31;
   const int c0 = threadIdx.x >> 6;       // wave index = first ds of this thread
-  const uint64_t real = block_real_mask(g, i);
-  const long long base = (bh * g.n_pad + (long long)i * kBlock) * (D / 8);
-  // unit j of this thread is u = threadIdx + 256 j, in chunk c0 + 4 j:
-  // ds = (c0 + 4 j) % NDS (slot j % NSLOT), token 32 ((c0 + 4 j) / NDS) + r
-  u32x4 vq[J], vk[J];
+  double acc[NT][NSLOT][8];
 #pragma unroll
-  for (int j = 0; j < J; ++j) {
-    vq[j] = qc[base + threadIdx.x + kThreads * j];
-    vk[j] = kc[base + threadIdx.x + kThreads * j];
-  }
-  double aq[NSLOT][8], ak[NSLOT][8];
+  for (int t = 0; t < NT; ++t)
 #pragma unroll
-  for (int a = 0; a < NSLOT; ++a)
+    for (int s = 0; s < NSLOT; ++s)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) aq[a][e] = ak[a][e] = 0.0;
+      for (int e = 0; e < 8; ++e) acc[t][s][e] = 0.0;
+  const int i_end = min((a + 1) * qg, g.nblk);
+  int count = 0;
+  for (int i = a * qg; i < i_end; ++i) {
+    const uint64_t real = block_real_mask(g, i);
+    count += block_real_count(g, i);
+    const long long base = (bh * g.n_pad + (long long)i * kBlock) * (D / 8);
+    // unit j of this thread is u = threadIdx + 256 j, in chunk c0 + 4 j:
+    // ds = (c0 + 4 j) % NDS (slot j % NSLOT), token 32 ((c0 + 4 j) / NDS) + r
+    u32x4 v[NT][J];
 #pragma unroll
-  for (int j = 0; j < J; ++j) {
-    const int chunk = c0 + 4 * j;
-    const int s = 32 * (chunk / NDS) + r;
-    if ((real >> s) & 1ull) {
-      add_bf16x8(aq[j % NSLOT], vq[j]);
-      add_bf16x8(ak[j % NSLOT], vk[j]);
+    for (int j = 0; j < J; ++j) {
+      v[0][j] = qc[base + threadIdx.x + kThreads * j];
+      if constexpr (NT == 2) v[NT - 1][j] = kc[base + threadIdx.x + kThreads * j];
+    }
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int chunk = c0 + 4 * j;
+      const int s = 32 * (chunk / NDS) + r;
+      if ((real >> s) & 1ull) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) add_bf16x8(acc[t][j % NSLOT], v[t][j]);
+      }
     }
   }
   // Sum over the 32 token residues held by the 32 lanes of each half-wave,
   // as a reduce-scatter: at each butterfly step a lane keeps the half of its
   // values whose index matches its lane bit and adds the partner's copy of
-  // that half, so after 5 steps lane r holds the complete sum of value r
-  // (31 exchanges instead of 5 per value).  Fixed order: the result does not
-  // depend on scheduling (and the sums are exact anyway).
-  constexpr int NV = 2 * NSLOT * 8;      // values per lane: [tensor][slot][e]
+  // that half, so after 5 steps lane r holds the complete sum of value
+  // r / (32 / NV) (NV - 1 exchanges instead of 5 per value).  Fixed order: the
+  // result does not depend on scheduling (and the sums are exact anyway).
+  constexpr int NV = NT * NSLOT * 8;     // values per lane: [tensor][slot][e]
   double v[NV];
 #pragma unroll
-  for (int a = 0; a < NSLOT; ++a)
+  for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      v[a * 8 + e] = aq[a][e];
-      v[NSLOT * 8 + a * 8 + e] = ak[a][e];
-    }
+    for (int s = 0; s < NSLOT; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[(t * NSLOT + s) * 8 + e] = acc[t][s][e];
 #pragma unroll
   for (int step = 0; step < 5; ++step) {
     const int o = 16 >> step;            // partner distance
@@ -96,15 +109,12 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(const u32x4* __restrict_
       v[0] += __shfl_xor(v[0], o, kWave);
     }
   }
-  // lane r now holds value index (r / (32 / NV)) -- for NV = 32 that is r,
-  // for NV = 16 the pairs (r, r ^ 1) hold the same index r / 2
   const int idx = r / (32 / NV);
   if ((r % (32 / NV)) == 0) {
-    const double count = (double)block_real_count(g, i);
-    const long long out = (bh * g.nblk + i) * (long long)D;
-    const int tensor = idx / (NSLOT * 8), a = (idx / 8) % NSLOT, e = idx % 8;
-    const int ds = c0 + 4 * a;
-    (tensor == 0 ? qbar : kbar)[out + 16 * ds + 8 * h + e] = v[0] / count;
+    const long long out = (bh * ngroups + a) * (long long)D;
+    const int tensor = idx / (NSLOT * 8), s = (idx / 8) % NSLOT, e = idx % 8;
+    const int ds = c0 + 4 * s;
+    (tensor == 0 ? qbar : kbar)[out + 16 * ds + 8 * h + e] = v[0] / (double)count;
   }
 }
 
@@ -113,12 +123,23 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(const u32x4* __restrict_
 hipError_t launch_pool(const void* qc, const void* kc, double* qbar, double* kbar,
                        const Geom& g, hipStream_t s) {
   dim3 grid(g.nblk, g.batch * g.heads);
+  const u32x4* q = static_cast<const u32x4*>(qc);
+  const u32x4* k = static_cast<const u32x4*>(kc);
   if (g.d == 128)
-    pool_kernel<128><<<grid, kThreads, 0, s>>>(static_cast<const u32x4*>(qc), static_cast<const u32x4*>(kc),
-                                               qbar, kbar, g);
+    pool_kernel<128, 2><<<grid, kThreads, 0, s>>>(q, k, qbar, kbar, g, 1, g.nblk);
   else
-    pool_kernel<64><<<grid, kThreads, 0, s>>>(static_cast<const u32x4*>(qc), static_cast<const u32x4*>(kc),
-                                              qbar, kbar, g);
+    pool_kernel<64, 2><<<grid, kThreads, 0, s>>>(q, k, qbar, kbar, g, 1, g.nblk);
+  return hipGetLastError();
+}
+
+hipError_t launch_pool_groups(const void* xc, double* xbar, int qg, const Geom& g, hipStream_t s) {
+  const int ngroups = (g.nblk + qg - 1) / qg;
+  dim3 grid(ngroups, g.batch * g.heads);
+  const u32x4* x = static_cast<const u32x4*>(xc);
+  if (g.d == 128)
+    pool_kernel<128, 1><<<grid, kThreads, 0, s>>>(x, x, xbar, xbar, g, qg, ngroups);
+  else
+    pool_kernel<64, 1><<<grid, kThreads, 0, s>>>(x, x, xbar, xbar, g, qg, ngroups);
   return hipGetLastError();
 }
 

@@ -16,14 +16,21 @@ hipError_t launch_unreorder(const void* oc, void* o, const float* lse_c, float* 
                             const Geom& g, hipStream_t s);
 hipError_t launch_pool(const void* qc, const void* kc, double* qbar, double* kbar,
                        const Geom& g, hipStream_t s);
+// Query groups: qg consecutive cubes form one query block (qg = 1: the cube
+// itself); a head then has (nblk + qg - 1) / qg query blocks.
+hipError_t launch_pool_groups(const void* xc, double* xbar, int qg, const Geom& g, hipStream_t s);
+// nrows query rows per head (default nblk) against nblk key blocks
 hipError_t launch_block_scores(const double* qbar, const double* kbar, double* scores,
-                               double scale, const Geom& g, hipStream_t s);
+                               double scale, const Geom& g, hipStream_t s, int nrows = -1);
+// rows_per_head rows of nblk scores per head (default nblk)
 hipError_t launch_select(const double* scores, const Geom& g, int kc_default, double p,
                          const int32_t* row_budget, int32_t* lut, int32_t* counts,
-                         int cap, hipStream_t s);
+                         int cap, hipStream_t s, int rows_per_head = -1);
+// cube i of a head reads list row i >> qg_shift of its head's nlists rows
+// (default: one list per cube)
 hipError_t launch_fwd(const void* qc, const void* kc, const void* vc, const int32_t* lut,
                       const int32_t* counts, int cap, const Geom& g, float scale, void* oc,
-                      float* lse_c, void* workspace, hipStream_t s);
+                      float* lse_c, void* workspace, hipStream_t s, int qg_shift = 0);
 size_t fwd_workspace_bytes(const Geom& g);
 hipError_t launch_router_pool(const void* xc, double* xr, const Geom& g, int rt, int rh, int rw, hipStream_t s);
 hipError_t launch_router(const double* qr, const double* kr, double* scores, double scale, const Geom& g,

@@ -511,8 +511,8 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const double* __restri
 
 template <int E>
 hipError_t launch_e(const double* scores, const Geom& g, int kc, double p, const int32_t* rb,
-                    int32_t* lut, int32_t* counts, int cap, hipStream_t s) {
-  const long long rows = (long long)g.batch * g.heads * g.nblk;
+                    int32_t* lut, int32_t* counts, int cap, hipStream_t s, int rows_per_head) {
+  const long long rows = (long long)g.batch * g.heads * rows_per_head;
   if (rows == 0) return hipSuccess;
   select_kernel<E><<<dim3((unsigned)rows), kThreads, 0, s>>>(scores, g.nblk, kc, p, rb, lut, counts, cap);
   return hipGetLastError();
@@ -522,15 +522,16 @@ hipError_t launch_e(const double* scores, const Geom& g, int kc, double p, const
 
 hipError_t launch_select(const double* scores, const Geom& g, int kc_default, double p,
                          const int32_t* row_budget, int32_t* lut, int32_t* counts, int cap,
-                         hipStream_t s) {
+                         hipStream_t s, int rows_per_head) {
   const int n = g.nblk;  // at most 4096 (checked by the caller)
-  if (n <= 256) return launch_e<1>(scores, g, kc_default, p, row_budget, lut, counts, cap, s);
-  if (n <= 512) return launch_e<2>(scores, g, kc_default, p, row_budget, lut, counts, cap, s);
-  if (n <= 1024) return launch_e<4>(scores, g, kc_default, p, row_budget, lut, counts, cap, s);
-  if (n <= 1536) return launch_e<6>(scores, g, kc_default, p, row_budget, lut, counts, cap, s);
-  if (n <= 2048) return launch_e<8>(scores, g, kc_default, p, row_budget, lut, counts, cap, s);
-  if (n <= 3072) return launch_e<12>(scores, g, kc_default, p, row_budget, lut, counts, cap, s);
-  return launch_e<16>(scores, g, kc_default, p, row_budget, lut, counts, cap, s);
+  if (rows_per_head < 0) rows_per_head = n;
+  if (n <= 256) return launch_e<1>(scores, g, kc_default, p, row_budget, lut, counts, cap, s, rows_per_head);
+  if (n <= 512) return launch_e<2>(scores, g, kc_default, p, row_budget, lut, counts, cap, s, rows_per_head);
+  if (n <= 1024) return launch_e<4>(scores, g, kc_default, p, row_budget, lut, counts, cap, s, rows_per_head);
+  if (n <= 1536) return launch_e<6>(scores, g, kc_default, p, row_budget, lut, counts, cap, s, rows_per_head);
+  if (n <= 2048) return launch_e<8>(scores, g, kc_default, p, row_budget, lut, counts, cap, s, rows_per_head);
+  if (n <= 3072) return launch_e<12>(scores, g, kc_default, p, row_budget, lut, counts, cap, s, rows_per_head);
+  return launch_e<16>(scores, g, kc_default, p, row_budget, lut, counts, cap, s, rows_per_head);
 }
 
 }  // namespace sa

@@ -13,6 +13,8 @@
  *   bwd          gradients of the block-sparse attention (dQ, dK, dV)
  *   quality      retained pooled mass, retained attention mass, L1 error
  *   attention    the whole path in one call, overlapped over two streams
+ *   groups       asymmetric blocks: masks and forward for query blocks of
+ *                2 or 4 cubes against single-cube key blocks
  *   unreorder    cube-major O (and LSE) -> row-major tokens
  *
  * Conventions shared by every entry point
@@ -390,6 +392,45 @@ int32_t sparse_attn_fwd(const void* qc, const void* kc, const void* vc,
                         const int32_t* lut, const int32_t* counts, int32_t cap,
                         const sa_geom* g, float scale, void* oc, float* lse_c,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- asymmetric blocks: query blocks of qgroup cubes --------------------
+ * [SA2] "Block-Pooled Attention for Efficient Mask Construction": query
+ * blocks of b_q tokens against key blocks of b_kv tokens (b_q = 128,
+ * b_kv = 64 there).  In the cube-major order a query block is qgroup
+ * consecutive cubes (qgroup 2: 128 query slots; 1, 2 or 4 accepted, else
+ * SA_ERR_INVALID_ARG); key blocks stay single cubes.  A head has
+ * nq = ceil(nblk / qgroup) query blocks.
+ *
+ * Bytes of workspace sparse_attn_build_mask_groups needs: group means of Q
+ * [batch, heads, nq, head_dim], block means of K [batch, heads, nblk,
+ * head_dim] and scores [batch, heads, nq, nblk], float64, in that order,
+ * each region 256-byte aligned.  0 on an invalid geometry or qgroup. */
+size_t sparse_attn_mask_groups_workspace_bytes(const sa_geom* g, int32_t qgroup);
+
+/* Mask of the asymmetric blocks: Q pooled over each query block's real
+ * tokens, K per cube, scores Qbar Kbar^T / sqrt(head_dim) [nq x nblk] per
+ * head, then the hybrid rule on every query block's row with
+ * kc = ceil(k_frac * nblk) (sparse_attn_ceil_k of nblk).
+ *   qc, kc  [batch, heads, n_pad, head_dim] bf16, SA_LAYOUT_QK   (inputs)
+ *   lut     [batch, heads, nq, cap] int32, counts [batch, heads, nq] (outputs)
+ * cap as for sparse_attn_select; workspace >= the size above (else
+ * SA_ERR_CAPACITY). */
+int32_t sparse_attn_build_mask_groups(const void* qc, const void* kc,
+                                      const sa_geom* g, int32_t qgroup,
+                                      double k_frac, double p, int32_t* lut,
+                                      int32_t* counts, int32_t cap,
+                                      void* workspace, size_t workspace_bytes,
+                                      void* stream);
+
+/* sparse_attn_fwd with one kept list per query block of qgroup cubes: cube i
+ * of a head attends through list row i / qgroup of lut [batch, heads, nq,
+ * cap] and counts [batch, heads, nq].  Outputs as sparse_attn_fwd; qgroup 1
+ * is sparse_attn_fwd itself. */
+int32_t sparse_attn_fwd_groups(const void* qc, const void* kc, const void* vc,
+                               const int32_t* lut, const int32_t* counts,
+                               int32_t cap, int32_t qgroup, const sa_geom* g,
+                               float scale, void* oc, float* lse_c,
+                               void* stream);
 
 /* Message describing the calling thread's last error ("" if none). */
 const char* sparse_attn_last_error(void);

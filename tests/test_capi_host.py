@@ -154,3 +154,28 @@ def test_python_binding_rejects_non_contiguous():
         sa.sparse_attn_reorder(x, x, 0, g)
     with pytest.raises(TypeError):
         sa.sparse_attn_reorder(torch.zeros(4, dtype=torch.float32), x, 0, g)
+
+
+def test_grouped_mask_and_fwd_argument_rules():
+    g = geom()                                      # nblk = 16, B*H = 2
+    lib = sa.lib()
+    B = ctypes.byref(g)
+    for qg in (0, 3, 8, -2):
+        assert lib.sparse_attn_mask_groups_workspace_bytes(B, qg) == 0
+        assert lib.sparse_attn_build_mask_groups(FAKE, FAKE, B, qg, 0.25, 0.5, FAKE, FAKE, 16, FAKE, 1 << 20,
+                                                 None) == sa.SA_ERR_INVALID_ARG
+        assert lib.sparse_attn_fwd_groups(FAKE, FAKE, FAKE, FAKE, FAKE, 16, qg, B, 0.0, FAKE, FAKE,
+                                          None) == sa.SA_ERR_INVALID_ARG
+    # group means [2, 8, 64] + block means [2, 16, 64] + scores [2, 8, 16], float64, 256-byte regions
+    need = lib.sparse_attn_mask_groups_workspace_bytes(B, 2)
+    assert need == 2 * 8 * 64 * 8 + 2 * 16 * 64 * 8 + 2 * 8 * 16 * 8
+    assert lib.sparse_attn_mask_groups_workspace_bytes(B, 1) == lib.sparse_attn_mask_workspace_bytes(B)
+    assert lib.sparse_attn_build_mask_groups(FAKE, FAKE, B, 2, 0.25, 0.5, FAKE, FAKE, 16, FAKE, need - 1,
+                                             None) == sa.SA_ERR_CAPACITY
+    # Top-p may keep every key block: cap must cover nblk, not nq
+    assert lib.sparse_attn_build_mask_groups(FAKE, FAKE, B, 2, 0.25, 0.5, FAKE, FAKE, 15, FAKE, need,
+                                             None) == sa.SA_ERR_CAPACITY
+    assert lib.sparse_attn_fwd_groups(FAKE, FAKE, None, FAKE, FAKE, 16, 2, B, 0.0, FAKE, FAKE,
+                                      None) == sa.SA_ERR_INVALID_ARG
+    assert lib.sparse_attn_fwd_groups(FAKE, FAKE, FAKE, FAKE, FAKE, 16, 2, B, float("nan"), FAKE, FAKE,
+                                      None) == sa.SA_ERR_INVALID_ARG

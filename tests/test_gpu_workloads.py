@@ -151,3 +151,38 @@ def test_backward_full_size():
         scale = float(np.abs(w).max())
         say(f"  {name}: max err {err.max():.2e} mean {err.mean():.2e} (max |grad| {scale:.2e})")
         assert err.max() <= 2e-2 * scale and err.mean() <= 2e-3 * scale, name
+
+
+def test_grouped_blocks_full_size():
+    """Query blocks of 2 cubes (128 query slots) against single-cube key blocks
+    at the 720p shape on two heads: every list against the oracle, and the
+    forward of sampled query blocks on the GPU's lists."""
+    wl = synth.WORKLOADS[2]
+    heads = [0, 1]
+    say(f"[groups 720p] heads {heads} grid={wl.grid}")
+    q, k, v = synth.make_qkv(wl, 0, heads=heads)
+    g = sa.make_geom(1, len(heads), wl.frames, wl.height, wl.width, wl.head_dim)
+    og = ogeom_of(wl)
+    qc, kc = sa.reorder(q.to(DEV), g, sa.SA_LAYOUT_QK), sa.reorder(k.to(DEV), g, sa.SA_LAYOUT_QK)
+    vc = sa.reorder(v.to(DEV), g, sa.SA_LAYOUT_V)
+    lut, counts = sa.build_mask_groups(qc, kc, g, 2, 0.03, 0.073)
+    oc, lse_c = sa.fwd_groups(qc, kc, vc, lut, counts, g, 2)
+    torch.cuda.synchronize()
+    say("  gpu groups done")
+    ref_qc, ref_kc, ref_vc = (O.reorder(to64(t), og) for t in (q, k, v))
+    ref = O.build_mask_groups(ref_qc, ref_kc, og, 2, 0.03, 0.073)
+    lut_h, counts_h = lut.cpu().numpy(), counts.cpu().numpy()
+    bad, near, invalid = compare_lists(lut_h, counts_h, ref, 0.073)
+    say(f"  group lists: {len(bad)} mismatches outside near ties, {near} near ties")
+    assert not bad and not invalid
+    rng = np.random.default_rng(5)
+    oc_h, lse_h = to64(oc), lse_c.cpu().numpy().astype(np.float64)
+    for h in range(len(heads)):
+        for i in rng.choice(og.nblk, 12, replace=False):
+            a = i // 2
+            kept = lut_h[0, h, a, :counts_h[0, h, a]]
+            o_ref, lse_ref = O.attention_block(ref_qc[0, h], ref_kc[0, h], ref_vc[0, h], kept, og, int(i))
+            sl = slice(64 * i, 64 * i + 64)
+            mx, mean = attn_errors(oc_h[0, h, sl], o_ref)
+            lmx, _ = lse_errors(lse_h[0, h, sl], lse_ref)
+            assert mx <= O_MAX_ABS and mean <= O_MEAN_ABS and lmx <= LSE_MAX_ABS, (h, i, mx, mean, lmx)
