@@ -76,6 +76,17 @@ What it computes, step by step, in float64 (bfloat16 inputs convert exactly):
    (kc = ceil(k * nblk)), and every cube of the group attends through that
    one list.
 
+11. Per-sequence Top-K ("Improving Video Sparse Attention ...", section 1 and
+   the ablation on the scope of the TopK selection): the budget is fixed for
+   the whole sequence (one head) rather than per query block, so rows get
+   different counts.  Reading: the budget equals per-row Top-k's total,
+   T = rows * ceil(k * nblk); the T largest entries of the head's row-softmax
+   block probabilities win, equal probabilities going to the lower row-major
+   index first; each row's count c_i is how many of its entries won, and the
+   row keeps its c_i top-scoring blocks (the Top-k rule with c_i for kc, so
+   the selection within a row follows the scores as everywhere else).  A row
+   may get no block at all.
+
 Readings where the pages are silent or garbled are listed in the repository's
 design notes; the ones this file depends on are repeated at each function.
 Every function here is pinned by the CPU tests (worked examples, closed forms,
@@ -639,3 +650,65 @@ def expand_group_lists(lut: np.ndarray, counts: np.ndarray, qg: int, nblk: int):
     block i // qg."""
     rows = np.arange(nblk) // qg
     return lut[..., rows, :], counts[..., rows]
+
+
+# ----------------------------------------------------------------------------
+# 11. per-sequence Top-K: one budget per head, variable counts per row
+# ----------------------------------------------------------------------------
+def sequence_budget(rows: int, nblk: int, k_frac: float) -> int:
+    """The head's total: what per-row Top-k would keep."""
+    return rows * ceil_k(k_frac, nblk)
+
+
+def per_sequence_counts(s: np.ndarray, total: int) -> np.ndarray:
+    """Per-row counts of the `total` largest entries of the row softmax of one
+    head's scores [rows, nblk]; equal probabilities go to the lower row-major
+    index first."""
+    prob = block_softmax(np.asarray(s, dtype=np.float64))
+    flat = prob.reshape(-1)
+    order = np.lexsort((np.arange(flat.size), -flat))
+    won = np.zeros(flat.size, dtype=bool)
+    won[order[:max(0, min(total, flat.size))]] = True
+    return won.reshape(prob.shape).sum(axis=1).astype(np.int32)
+
+
+def per_sequence_near_tie(s: np.ndarray, total: int) -> np.ndarray:
+    """Rows whose count could change under a relative perturbation below 1e-6
+    of the probabilities: rows holding an entry within that margin of the
+    last winning probability (when a losing entry lies within it too)."""
+    prob = block_softmax(np.asarray(s, dtype=np.float64))
+    flat = np.sort(prob.reshape(-1))[::-1]
+    if total <= 0 or total >= flat.size:
+        return np.zeros(prob.shape[0], dtype=bool)
+    last, first_out = flat[total - 1], flat[total]
+    if last - first_out > NEAR_TIE * last:
+        return np.zeros(prob.shape[0], dtype=bool)
+    close = np.abs(prob - last) <= NEAR_TIE * last
+    return close.any(axis=1)
+
+
+def build_mask_per_sequence(qc: np.ndarray, kc_: np.ndarray, g: Geometry, k_frac: float) -> MaskResult:
+    """Pool -> block scores -> per-head budget T = nblk * ceil(k * nblk) ->
+    per-row counts -> each row's top-scoring blocks (lists [B, H, nblk, nblk])."""
+    d = qc.shape[-1]
+    qbar = pool(qc, g)
+    kbar = pool(kc_, g)
+    s = block_scores(qbar, kbar, d)
+    B, H, n, _ = s.shape
+    lut = np.full((B, H, n, n), -1, dtype=np.int32)
+    counts = np.zeros((B, H, n), dtype=np.int32)
+    flags = np.zeros((B, H, n), dtype=bool)
+    kcs = np.zeros((B, H, n), dtype=np.int32)
+    total = sequence_budget(n, n, k_frac)
+    for b in range(B):
+        for h in range(H):
+            c = per_sequence_counts(s[b, h], total)
+            flags[b, h] = per_sequence_near_tie(s[b, h], total)
+            probs = block_softmax(s[b, h])
+            for i in range(n):
+                sel = select_row(s[b, h, i], int(c[i]), 0.0, probs[i])
+                lut[b, h, i, :sel.kept.size] = sel.kept
+                counts[b, h, i] = sel.kept.size
+                flags[b, h, i] |= sel.near_tie
+                kcs[b, h, i] = c[i]
+    return MaskResult(lut, counts, flags, kcs, np.zeros((B, H, n), dtype=np.int32), s, qbar, kbar)

@@ -817,3 +817,69 @@ def test_build_mask_groups_rows_counts_and_scores():
     for i in range(g.nblk):
         np.testing.assert_array_equal(lut_e[:, :, i], two.lut[:, :, i // 2])
         np.testing.assert_array_equal(cnt_e[:, :, i], two.counts[:, :, i // 2])
+
+
+# ----------------------------------------------------------------------------
+# per-sequence Top-K
+# ----------------------------------------------------------------------------
+def _greedy_counts(s, total):
+    """Independent route: take the largest remaining probability `total`
+    times (lower row-major index first on equal values)."""
+    e = np.exp(s - s.max(axis=1, keepdims=True))
+    prob = (e / e.sum(axis=1, keepdims=True)).tolist()
+    rows, n = len(prob), len(prob[0])
+    taken = [[False] * n for _ in range(rows)]
+    counts = [0] * rows
+    for _ in range(total):
+        best = None
+        for i in range(rows):
+            for j in range(n):
+                if not taken[i][j] and (best is None or prob[i][j] > prob[best[0]][best[1]]):
+                    best = (i, j)
+        taken[best[0]][best[1]] = True
+        counts[best[0]] += 1
+    return counts
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_per_sequence_counts_match_greedy(seed):
+    rng = np.random.default_rng(70 + seed)
+    rows, n = 7, 9
+    s = rng.standard_normal((rows, n)) * rng.uniform(0.2, 3.0, (rows, 1))
+    if seed == 3:
+        s = np.round(s * 2) / 2          # exact ties inside and across rows
+        s[2] = s[5]
+    for total in (0, 1, 5, 21, 40, rows * n):
+        got = O.per_sequence_counts(s, total)
+        assert got.sum() == total
+        assert got.tolist() == _greedy_counts(s, total), (total, got)
+
+
+def test_per_sequence_closed_forms():
+    rng = np.random.default_rng(75)
+    row = rng.standard_normal(12)
+    same = np.tile(row, (5, 1))                    # identical rows: kc each
+    for kc in (0, 1, 4, 12):
+        assert np.all(O.per_sequence_counts(same, 5 * kc) == kc)
+    # a peaked row against flat rows: the peaked row's leaders outrank every flat entry
+    flat = np.zeros((4, 12))
+    flat[0] = np.concatenate(([6.0, 5.0, 4.0], np.zeros(9)))
+    c = O.per_sequence_counts(flat, 3)
+    assert c.tolist() == [3, 0, 0, 0]
+    assert O.sequence_budget(1440, 1440, 0.03) == 1440 * 44
+
+
+def test_build_mask_per_sequence_total_and_rows():
+    g = O.Geometry(4, 12, 12)
+    rng = np.random.default_rng(76)
+    qc = O.reorder(rng.standard_normal((1, 2, g.n_real, 8)), g)
+    kc_ = O.reorder(rng.standard_normal((1, 2, g.n_real, 8)) * 2.0, g)
+    m = O.build_mask_per_sequence(qc, kc_, g, 0.1)
+    total = O.sequence_budget(g.nblk, g.nblk, 0.1)
+    assert np.all(m.counts.sum(axis=-1) == total)
+    assert len(set(m.counts.reshape(-1).tolist())) > 1          # counts vary across rows
+    for h in range(2):
+        for i in range(g.nblk):
+            c = m.counts[0, h, i]
+            top = np.sort(np.argsort(-m.scores[0, h, i], kind="stable")[:c])
+            np.testing.assert_array_equal(m.lut[0, h, i, :c], top)
