@@ -268,6 +268,17 @@ def next_rows(path, reps=3):
                                "fwd_tflops": round(fl / t_f2 / 1e9, 2),
                                "frac_of_bf16_peak": round(fl / t_f2 / 1e9 / PEAK_BF16_TFLOPS, 4)}
     del lut2, oc2
+    # per-sequence Top-K on the same block scores (one budget per head)
+    lut3 = torch.empty((B, H, n, n), dtype=torch.int32, device=dev)
+    counts3 = torch.empty((B, H, n), dtype=torch.int32, device=dev)
+    ws3 = torch.empty(sa.sparse_attn_sequence_workspace_bytes(g), dtype=torch.uint8, device=dev)
+    t_seq = time_call(lambda: sa.sparse_attn_select_per_sequence(path.scores, g, path.k_frac, lut3, counts3, n,
+                                                                 ws3), reps)
+    c3 = counts3.to(torch.float64)
+    out["per_sequence_topk"] = {"ms": round(t_seq, 4), "budget_per_head": int(n * sa.sparse_attn_ceil_k(path.k_frac, n)),
+                                "row_count_min": int(c3.min()), "row_count_max": int(c3.max()),
+                                "rows_empty_frac": round(float((c3 == 0).to(torch.float64).mean()), 4)}
+    del lut3
     # mask quality of the timed lists against dense attention (every block kept)
     t0 = time.perf_counter()
     mass, tau, rel = sa.mask_quality(path.qc, path.kc, path.vc, path.lut, path.counts, path.scores, g)

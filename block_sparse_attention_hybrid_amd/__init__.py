@@ -39,6 +39,7 @@ EXPORTED = (
     "sparse_attn_bwd_delta", "sparse_attn_transpose_workspace_bytes", "sparse_attn_transpose_lut",
     "sparse_attn_bwd", "sparse_attn_pooled_mass", "sparse_attn_mask_error", "sparse_attn_attention",
     "sparse_attn_mask_groups_workspace_bytes", "sparse_attn_build_mask_groups", "sparse_attn_fwd_groups",
+    "sparse_attn_sequence_workspace_bytes", "sparse_attn_select_per_sequence",
     "sparse_attn_last_error",
 )
 
@@ -111,6 +112,8 @@ _SIGS = {
     "sparse_attn_mask_groups_workspace_bytes": (_sz, [_GP, _i32]),
     "sparse_attn_build_mask_groups": (_i32, [_vp, _vp, _GP, _i32, _f64, _f64, _vp, _vp, _i32, _vp, _sz, _vp]),
     "sparse_attn_fwd_groups": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _GP, _f32, _vp, _vp, _vp]),
+    "sparse_attn_sequence_workspace_bytes": (_sz, [_GP]),
+    "sparse_attn_select_per_sequence": (_i32, [_vp, _GP, _f64, _vp, _vp, _i32, _vp, _sz, _vp]),
     "sparse_attn_last_error": (ctypes.c_char_p, []),
 }
 
@@ -379,6 +382,20 @@ def sparse_attn_fwd_groups(qc, kc, vc, lut, counts, cap: int, qgroup: int, g: Ge
                                         _ptr(lse_c, torch.float32, "lse_c"), _stream(stream, qc)))
 
 
+def sparse_attn_sequence_workspace_bytes(g: Geom) -> int:
+    return int(lib().sparse_attn_sequence_workspace_bytes(ctypes.byref(g)))
+
+
+def sparse_attn_select_per_sequence(scores, g: Geom, k_frac: float, lut, counts, cap: int, workspace,
+                                    stream=None) -> None:
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().sparse_attn_select_per_sequence(_ptr(scores, torch.float64, "scores"), ctypes.byref(g),
+                                                 float(k_frac), _ptr(lut, torch.int32, "lut"),
+                                                 _ptr(counts, torch.int32, "counts"), int(cap),
+                                                 _ptr(workspace, None, "workspace"), ws_bytes,
+                                                 _stream(stream, scores)))
+
+
 def mask_workspace(g: Geom, device) -> torch.Tensor:
     return torch.empty(sparse_attn_mask_workspace_bytes(g), dtype=torch.uint8, device=device)
 
@@ -427,6 +444,17 @@ def fwd_groups(qc, kc, vc, lut, counts, g: Geom, qgroup: int, scale: float = 0.0
     lse_c = _empty((g.batch, g.heads, n_pad), torch.float32, qc)
     sparse_attn_fwd_groups(qc, kc, vc, lut, counts, lut.shape[-1], qgroup, g, scale, oc, lse_c, stream)
     return oc, lse_c
+
+
+def select_per_sequence(scores, g: Geom, k_frac: float, stream=None):
+    """Per-sequence Top-K lists of block scores [B,H,nblk,nblk] float64:
+    (lut [B,H,nblk,nblk] int32, counts [B,H,nblk] int32)."""
+    nblk, _, _ = sparse_attn_geometry(g)
+    lut = _empty((g.batch, g.heads, nblk, nblk), torch.int32, scores)
+    counts = _empty((g.batch, g.heads, nblk), torch.int32, scores)
+    ws = torch.empty(sparse_attn_sequence_workspace_bytes(g), dtype=torch.uint8, device=scores.device)
+    sparse_attn_select_per_sequence(scores, g, k_frac, lut, counts, nblk, ws, stream)
+    return lut, counts
 
 
 def attention(q, k, v, g: Geom, k_frac: float, p: float, row_budget=None, stream=None):

@@ -509,6 +509,38 @@ int32_t sparse_attn_fwd_groups(const void* qc, const void* kc, const void* vc, c
                     "fwd launch");
 }
 
+size_t sparse_attn_sequence_workspace_bytes(const sa_geom* g) {
+  sa::Geom d;
+  if (make_geom(g, d) != SA_OK) return 0;
+  return sa::sequence_workspace_bytes(d);
+}
+
+int32_t sparse_attn_select_per_sequence(const double* scores, const sa_geom* g, double k_frac, int32_t* lut,
+                                        int32_t* counts, int32_t cap, void* workspace, size_t workspace_bytes,
+                                        void* stream) {
+  sa::Geom d;
+  SA_TRY(make_geom(g, d));
+  SA_TRY(check_ptr(scores, 8, "scores"));
+  if (d.nblk > kMaxSelectBlocks)
+    return fail(SA_ERR_UNSUPPORTED, "selection supports at most %d blocks per head (got %d)",
+                kMaxSelectBlocks, d.nblk);
+  if (!std::isfinite(k_frac)) return fail(SA_ERR_INVALID_ARG, "k_frac must be finite");
+  SA_TRY(check_ptr(lut, 4, "lut"));
+  SA_TRY(check_ptr(counts, 4, "counts"));
+  // a row may win every block: the lists need room for nblk ids
+  if (cap < d.nblk) return fail(SA_ERR_CAPACITY, "cap %d is below the largest possible row count %d", cap, d.nblk);
+  const int kcount = ceil_k_impl(k_frac, d.nblk);
+  SA_TRY(check_ptr(workspace, kWsAlign, "workspace"));
+  const size_t need = sa::sequence_workspace_bytes(d);
+  if (workspace_bytes < need)
+    return fail(SA_ERR_CAPACITY, "workspace of %zu bytes is below the %zu needed", workspace_bytes, need);
+  const long long total = (long long)d.nblk * kcount;
+  hipStream_t s = (hipStream_t)stream;
+  int32_t* budget = nullptr;
+  SA_TRY(hip_status(sa::launch_sequence_budget(scores, d, total, workspace, &budget, s), "budget launch"));
+  return hip_status(sa::launch_select(scores, d, 0, 0.0, budget, lut, counts, cap, s), "select launch");
+}
+
 size_t sparse_attn_fwd_workspace_bytes(const sa_geom* g) {
   sa::Geom d;
   if (make_geom(g, d) != SA_OK) return 0;

@@ -53,6 +53,12 @@ hipError_t launch_pooled_mass(const double* scores, const int32_t* lut, const in
                               const Geom& g, double* mass, hipStream_t s);
 hipError_t launch_mask_error(const float* lse_s, const float* lse_d, const void* o_s, const void* o_d,
                              const Geom& g, float* tau, float* rel, hipStream_t s);
+// Per-sequence Top-K: per-row counts of the head-wide budget `total` over the
+// row-softmax of block scores, written to a region of the workspace
+// (*budget_out, [batch*heads*nblk] int32).
+size_t sequence_workspace_bytes(const Geom& g);
+hipError_t launch_sequence_budget(const double* scores, const Geom& g, long long total, void* workspace,
+                                  int32_t** budget_out, hipStream_t s);
 hipError_t launch_coarse(const double* scores, const double* vbar, double* oc, const Geom& g, hipStream_t s);
 
 }  // namespace sa

@@ -15,6 +15,7 @@
  *   attention    the whole path in one call, overlapped over two streams
  *   groups       asymmetric blocks: masks and forward for query blocks of
  *                2 or 4 cubes against single-cube key blocks
+ *   sequence     per-sequence Top-K: one block budget per head
  *   unreorder    cube-major O (and LSE) -> row-major tokens
  *
  * Conventions shared by every entry point
@@ -431,6 +432,26 @@ int32_t sparse_attn_fwd_groups(const void* qc, const void* kc, const void* vc,
                                int32_t cap, int32_t qgroup, const sa_geom* g,
                                float scale, void* oc, float* lse_c,
                                void* stream);
+
+/* ---- per-sequence Top-K -------------------------------------------------
+ * [VSA2] section 1 and its ablation of the TopK scope: one budget per head
+ * instead of per query block.  The budget is what per-row Top-k would keep,
+ * T = nblk * ceil(k_frac * nblk) (sparse_attn_ceil_k); the T largest entries of
+ * the head's row-softmax block probabilities (row i of softmax(scores)) win,
+ * equal probabilities going to the lower row-major index first; row i keeps
+ * its c_i = (entries of row i that won) top-scoring blocks, ascending ids, as
+ * sparse_attn_select with row_budget c would.  A row may keep no block.
+ *   scores [batch, heads, nblk, nblk] float64 (block or router scores) (input)
+ *   lut [batch, heads, nblk, cap], counts [batch, heads, nblk]       (outputs)
+ * cap must be >= nblk (SA_ERR_CAPACITY); workspace (>= the size below, else
+ * SA_ERR_CAPACITY) holds row log-sum-exps, radix-select state and the counts.
+ * nblk is at most 4096 (SA_ERR_UNSUPPORTED). */
+size_t sparse_attn_sequence_workspace_bytes(const sa_geom* g);
+int32_t sparse_attn_select_per_sequence(const double* scores, const sa_geom* g,
+                                        double k_frac, int32_t* lut,
+                                        int32_t* counts, int32_t cap,
+                                        void* workspace, size_t workspace_bytes,
+                                        void* stream);
 
 /* Message describing the calling thread's last error ("" if none). */
 const char* sparse_attn_last_error(void);

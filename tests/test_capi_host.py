@@ -179,3 +179,22 @@ def test_grouped_mask_and_fwd_argument_rules():
                                       None) == sa.SA_ERR_INVALID_ARG
     assert lib.sparse_attn_fwd_groups(FAKE, FAKE, FAKE, FAKE, FAKE, 16, 2, B, float("nan"), FAKE, FAKE,
                                       None) == sa.SA_ERR_INVALID_ARG
+
+
+def test_per_sequence_argument_rules():
+    g = geom()                                      # nblk = 16
+    lib = sa.lib()
+    B = ctypes.byref(g)
+    need = lib.sparse_attn_sequence_workspace_bytes(B)
+    assert need > 0
+    assert lib.sparse_attn_select_per_sequence(FAKE, B, 0.25, FAKE, FAKE, 15, FAKE, need,
+                                               None) == sa.SA_ERR_CAPACITY       # cap < nblk
+    assert lib.sparse_attn_select_per_sequence(FAKE, B, 0.25, FAKE, FAKE, 16, FAKE, need - 1,
+                                               None) == sa.SA_ERR_CAPACITY
+    assert lib.sparse_attn_select_per_sequence(FAKE, B, float("nan"), FAKE, FAKE, 16, FAKE, need,
+                                               None) == sa.SA_ERR_INVALID_ARG
+    assert lib.sparse_attn_select_per_sequence(None, B, 0.25, FAKE, FAKE, 16, FAKE, need,
+                                               None) == sa.SA_ERR_INVALID_ARG
+    big = geom(frames=64, height=64, width=68)      # 4352 blocks
+    assert lib.sparse_attn_select_per_sequence(FAKE, ctypes.byref(big), 0.1, FAKE, FAKE, 5000, FAKE, 1 << 40,
+                                               None) == sa.SA_ERR_UNSUPPORTED

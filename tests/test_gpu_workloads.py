@@ -186,3 +186,25 @@ def test_grouped_blocks_full_size():
             mx, mean = attn_errors(oc_h[0, h, sl], o_ref)
             lmx, _ = lse_errors(lse_h[0, h, sl], lse_ref)
             assert mx <= O_MAX_ABS and mean <= O_MEAN_ABS and lmx <= LSE_MAX_ABS, (h, i, mx, mean, lmx)
+
+
+def test_per_sequence_full_size():
+    """Per-sequence Top-K at the 720p shape on three heads (one of each type),
+    on the GPU's own block scores."""
+    wl = synth.WORKLOADS[2]
+    heads = [0, 1, 2]
+    say(f"[per-sequence 720p] heads {heads}")
+    q, k, _ = synth.make_qkv(wl, 0, heads=heads)
+    g = sa.make_geom(1, len(heads), wl.frames, wl.height, wl.width, wl.head_dim)
+    qc, qbar = sa.reorder_pool(q.to(DEV), g)
+    kc, kbar = sa.reorder_pool(k.to(DEV), g)
+    n = sa.sparse_attn_geometry(g)[0]
+    s = torch.empty((1, len(heads), n, n), dtype=torch.float64, device=DEV)
+    sa.sparse_attn_block_scores(qbar, kbar, s, 1.0 / math.sqrt(wl.head_dim), g)
+    lut, counts = sa.select_per_sequence(s, g, 0.03)
+    torch.cuda.synchronize()
+    from test_gpu_parity import check_per_sequence
+    c = counts.cpu().numpy()
+    bad, near = check_per_sequence(lut.cpu().numpy(), c, s.cpu().numpy(), 0.03)
+    say(f"  per-sequence: {bad} count mismatches, {near} near-tie rows; counts min {c.min()} max {c.max()}")
+    assert bad == 0
