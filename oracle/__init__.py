@@ -10,4 +10,5 @@ from .oracle import (Geometry, MaskResult, RowSelection, attention_block,
                      select_row, select_rows, sparse_attention, token_slots,
                      top_p_count, unreorder, unreorder_rows, NEAR_TIE,
                      group_count, pool_groups, build_mask_groups, expand_group_lists,
-                     sequence_budget, per_sequence_counts, per_sequence_near_tie, build_mask_per_sequence)
+                     sequence_budget, per_sequence_counts, per_sequence_near_tie, build_mask_per_sequence,
+                     ideal_block_mass, mask_recall)

@@ -87,6 +87,15 @@ What it computes, step by step, in float64 (bfloat16 inputs convert exactly):
    the selection within a row follows the scores as everywhere else).  A row
    may get no block at all.
 
+12. Ideal block scores and mask recall ("Improving Video Sparse Attention ...",
+   section 2.2: the oracle block scores MeanPool of the full attention matrix,
+   the target a router approximates): P_ideal[i, j] is the full softmax mass
+   that block i's real queries put on block j's real keys, averaged over those
+   queries (every row sums to 1).  Recall of a kept list of c blocks: the share
+   of the c blocks with the largest P_ideal (lower id first on equal values)
+   that the list holds.  The retained mass of the list under P_ideal is the
+   block mean of the tau of item 9.
+
 Readings where the pages are silent or garbled are listed in the repository's
 design notes; the ones this file depends on are repeated at each function.
 Every function here is pinned by the CPU tests (worked examples, closed forms,
@@ -712,3 +721,42 @@ def build_mask_per_sequence(qc: np.ndarray, kc_: np.ndarray, g: Geometry, k_frac
                 flags[b, h, i] |= sel.near_tie
                 kcs[b, h, i] = c[i]
     return MaskResult(lut, counts, flags, kcs, np.zeros((B, H, n), dtype=np.int32), s, qbar, kbar)
+
+
+# ----------------------------------------------------------------------------
+# 12. ideal block scores (block-pooled full attention) and mask recall
+# ----------------------------------------------------------------------------
+def ideal_block_mass(qc: np.ndarray, kc_: np.ndarray, g: Geometry,
+                     scale: Optional[float] = None) -> np.ndarray:
+    """P_ideal [B, H, nblk, nblk]: mean over block i's real queries of the
+    full softmax mass on block j's real keys."""
+    B, H, n_pad, d = qc.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    real = real_slots(g)
+    blk_of = np.nonzero(real)[0] // g.block
+    out = np.zeros((B, H, g.nblk, g.nblk))
+    for b in range(B):
+        for h in range(H):
+            q = np.asarray(qc[b, h], dtype=np.float64)[real]
+            k = np.asarray(kc_[b, h], dtype=np.float64)[real]
+            s_ = (q @ k.T) * scale
+            p = np.exp(s_ - s_.max(axis=1, keepdims=True))
+            p /= p.sum(axis=1, keepdims=True)
+            per_key_block = np.zeros((p.shape[0], g.nblk))
+            np.add.at(per_key_block.T, blk_of, p.T)
+            for i in range(g.nblk):
+                out[b, h, i] = per_key_block[blk_of == i].mean(axis=0)
+    return out
+
+
+def mask_recall(mass: np.ndarray, lut: np.ndarray, counts: np.ndarray) -> np.ndarray:
+    """Per row: |kept & top-c of mass| / c (c = the row's count; 1 when c = 0)."""
+    out = np.ones(counts.shape)
+    for idx in np.ndindex(counts.shape):
+        c = int(counts[idx])
+        if c == 0:
+            continue
+        top = rank_order(np.asarray(mass[idx], dtype=np.float64))[:c]
+        out[idx] = np.intersect1d(top, lut[idx][:c]).size / c
+    return out

@@ -883,3 +883,43 @@ def test_build_mask_per_sequence_total_and_rows():
             c = m.counts[0, h, i]
             top = np.sort(np.argsort(-m.scores[0, h, i], kind="stable")[:c])
             np.testing.assert_array_equal(m.lut[0, h, i, :c], top)
+
+
+# ----------------------------------------------------------------------------
+# ideal block scores and recall
+# ----------------------------------------------------------------------------
+def test_ideal_block_mass_rows_closed_forms_and_tau():
+    g = O.Geometry(5, 6, 9)                       # partial cubes
+    rng = np.random.default_rng(81)
+    qc = O.reorder(rng.standard_normal((1, 2, g.n_real, 8)), g)
+    kc_ = O.reorder(rng.standard_normal((1, 2, g.n_real, 8)), g)
+    vc = O.reorder(rng.standard_normal((1, 2, g.n_real, 8)), g)
+    m = O.ideal_block_mass(qc, kc_, g)
+    np.testing.assert_allclose(m.sum(axis=-1), 1.0, rtol=1e-13)
+    # zero queries: every key equally likely, so block j gets its share of real keys
+    r = O.real_slots(g).reshape(g.nblk, g.block).sum(axis=1)
+    z = O.ideal_block_mass(np.zeros_like(qc), kc_, g)
+    np.testing.assert_allclose(z, np.broadcast_to(r / r.sum(), z.shape), rtol=1e-13)
+    # the retained mass of a list under P_ideal is the block mean of tau
+    mk = O.build_mask(qc, kc_, g, 0.2, 0.3)
+    tau, _ = O.mask_error(qc, kc_, vc, mk.lut, mk.counts, g)
+    real = O.real_slots(g)
+    for h in range(2):
+        for i in range(g.nblk):
+            kept = mk.lut[0, h, i, :mk.counts[0, h, i]]
+            rows = np.arange(64 * i, 64 * i + 64)
+            want = tau[0, h, rows[real[rows]]].mean()
+            np.testing.assert_allclose(m[0, h, i, kept].sum(), want, rtol=1e-12)
+
+
+def test_mask_recall_cases():
+    mass = np.array([[[[0.1, 0.4, 0.2, 0.3], [0.25, 0.25, 0.25, 0.25]]]])
+    lut = np.array([[[[1, 3, -1, -1], [0, 3, -1, -1]]]], dtype=np.int32)
+    counts = np.array([[[2, 2]]], dtype=np.int32)
+    # row 0: top-2 = {1, 3} -> recall 1; row 1: ties -> top-2 = {0, 1}, list {0, 3} -> 1/2
+    np.testing.assert_allclose(O.mask_recall(mass, lut, counts), [[[1.0, 0.5]]])
+    counts[:] = 0
+    np.testing.assert_allclose(O.mask_recall(mass, lut, counts), 1.0)
+    lut = np.array([[[[0, 2, -1, -1], [1, 2, -1, -1]]]], dtype=np.int32)
+    counts[:] = 2
+    np.testing.assert_allclose(O.mask_recall(mass, lut, counts), [[[0.0, 0.5]]])
