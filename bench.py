@@ -289,6 +289,22 @@ def next_rows(path, reps=3):
                            "mean_tau": round(float(tau[real].mean()), 5),
                            "min_tau": round(float(tau[real].min()), 5),
                            "mean_rel_l1": round(float(rel.mean()), 5)}
+    del mass, tau, rel
+    # ideal block scores (block-pooled full attention) and the recall of the timed lists
+    full = torch.empty((B, H, n, n), dtype=torch.int32, device=dev)
+    full_counts = torch.empty((B, H, n), dtype=torch.int32, device=dev)
+    sa.sparse_attn_select(path.scores, g, 0.0, 1.0, None, full, full_counts, n)
+    _, lse_d = sa.fwd(path.qc, path.kc, path.vc, full, full_counts, g)
+    del full
+    ideal = torch.empty((B, H, n, n), dtype=torch.float64, device=dev)
+    t_ideal = time_call(lambda: sa.sparse_attn_ideal_block_mass(path.qc, path.kc, lse_d, g, 0.0, ideal), 1)
+    recall = torch.empty((B, H, n), dtype=torch.float64, device=dev)
+    ws_r = torch.empty(sa.sparse_attn_recall_workspace_bytes(g), dtype=torch.uint8, device=dev)
+    t_rec = time_call(lambda: sa.sparse_attn_mask_recall(ideal, path.lut, path.counts, path.cap, g, recall, ws_r), 1)
+    fl = 2.0 * B * H * (n * 64) ** 2 * d
+    out["ideal_mass_recall"] = {"ideal_mass_ms": round(t_ideal, 3), "recall_ms": round(t_rec, 3),
+                                "ideal_mass_tflops": round(fl / t_ideal / 1e9, 1),
+                                "mean_recall": round(float(recall.mean()), 5)}
     return out
 
 

@@ -40,6 +40,7 @@ EXPORTED = (
     "sparse_attn_bwd", "sparse_attn_pooled_mass", "sparse_attn_mask_error", "sparse_attn_attention",
     "sparse_attn_mask_groups_workspace_bytes", "sparse_attn_build_mask_groups", "sparse_attn_fwd_groups",
     "sparse_attn_sequence_workspace_bytes", "sparse_attn_select_per_sequence",
+    "sparse_attn_ideal_block_mass", "sparse_attn_recall_workspace_bytes", "sparse_attn_mask_recall",
     "sparse_attn_last_error",
 )
 
@@ -114,6 +115,9 @@ _SIGS = {
     "sparse_attn_fwd_groups": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _GP, _f32, _vp, _vp, _vp]),
     "sparse_attn_sequence_workspace_bytes": (_sz, [_GP]),
     "sparse_attn_select_per_sequence": (_i32, [_vp, _GP, _f64, _vp, _vp, _i32, _vp, _sz, _vp]),
+    "sparse_attn_ideal_block_mass": (_i32, [_vp, _vp, _vp, _GP, _f32, _vp, _vp]),
+    "sparse_attn_recall_workspace_bytes": (_sz, [_GP]),
+    "sparse_attn_mask_recall": (_i32, [_vp, _vp, _vp, _i32, _GP, _vp, _vp, _sz, _vp]),
     "sparse_attn_last_error": (ctypes.c_char_p, []),
 }
 
@@ -396,6 +400,24 @@ def sparse_attn_select_per_sequence(scores, g: Geom, k_frac: float, lut, counts,
                                                  _stream(stream, scores)))
 
 
+def sparse_attn_ideal_block_mass(qc, kc, lse_d, g: Geom, scale: float, mass, stream=None) -> None:
+    _check(lib().sparse_attn_ideal_block_mass(_ptr(qc, torch.bfloat16, "qc"), _ptr(kc, torch.bfloat16, "kc"),
+                                              _ptr(lse_d, torch.float32, "lse_d"), ctypes.byref(g), float(scale),
+                                              _ptr(mass, torch.float64, "mass"), _stream(stream, qc)))
+
+
+def sparse_attn_recall_workspace_bytes(g: Geom) -> int:
+    return int(lib().sparse_attn_recall_workspace_bytes(ctypes.byref(g)))
+
+
+def sparse_attn_mask_recall(mass, lut, counts, cap: int, g: Geom, recall, workspace, stream=None) -> None:
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().sparse_attn_mask_recall(_ptr(mass, torch.float64, "mass"), _ptr(lut, torch.int32, "lut"),
+                                         _ptr(counts, torch.int32, "counts"), int(cap), ctypes.byref(g),
+                                         _ptr(recall, torch.float64, "recall"), _ptr(workspace, None, "workspace"),
+                                         ws_bytes, _stream(stream, mass)))
+
+
 def mask_workspace(g: Geom, device) -> torch.Tensor:
     return torch.empty(sparse_attn_mask_workspace_bytes(g), dtype=torch.uint8, device=device)
 
@@ -544,6 +566,24 @@ def mask_quality(qc, kc, vc, lut, counts, scores, g: Geom, stream=None):
     rel = _empty((g.batch, g.heads, nblk), torch.float32, qc)
     sparse_attn_mask_error(lse_s, lse_d, oc_s, oc_d, g, tau, rel, stream)
     return mass, tau, rel
+
+
+def mask_recall(qc, kc, vc, lut, counts, scores, g: Geom, stream=None):
+    """Ideal block scores (from a dense run with every block kept) and the
+    recall of the lists against them: (mass [B,H,nblk,nblk] float64,
+    recall [B,H,nblk] float64).  `scores` are the block scores the lists were
+    selected from (used only to list every block for the dense run)."""
+    nblk, _, _ = sparse_attn_geometry(g)
+    full = _empty((g.batch, g.heads, nblk, nblk), torch.int32, qc)
+    full_counts = _empty((g.batch, g.heads, nblk), torch.int32, qc)
+    sparse_attn_select(scores, g, 0.0, 1.0, None, full, full_counts, nblk, stream)
+    _, lse_d = fwd(qc, kc, vc, full, full_counts, g, stream=stream)
+    mass = _empty((g.batch, g.heads, nblk, nblk), torch.float64, qc)
+    sparse_attn_ideal_block_mass(qc, kc, lse_d, g, 0.0, mass, stream)
+    recall = _empty((g.batch, g.heads, nblk), torch.float64, qc)
+    ws = torch.empty(sparse_attn_recall_workspace_bytes(g), dtype=torch.uint8, device=qc.device)
+    sparse_attn_mask_recall(mass, lut, counts, lut.shape[-1], g, recall, ws, stream)
+    return mass, recall
 
 
 def path_buffers(q, k, v, g: Geom, row_budget=None):

@@ -541,6 +541,53 @@ int32_t sparse_attn_select_per_sequence(const double* scores, const sa_geom* g, 
   return hip_status(sa::launch_select(scores, d, 0, 0.0, budget, lut, counts, cap, s), "select launch");
 }
 
+int32_t sparse_attn_ideal_block_mass(const void* qc, const void* kc, const float* lse_d, const sa_geom* g,
+                                     float scale, double* mass, void* stream) {
+  sa::Geom d;
+  SA_TRY(make_geom(g, d));
+  SA_TRY(check_ptr(qc, 16, "qc"));
+  SA_TRY(check_ptr(kc, 16, "kc"));
+  SA_TRY(check_ptr(lse_d, 4, "lse_d"));
+  SA_TRY(check_ptr(mass, 8, "mass"));
+  if (!std::isfinite(scale)) return fail(SA_ERR_INVALID_ARG, "scale must be finite");
+  if (scale <= 0.f) scale = (float)(1.0 / std::sqrt((double)d.d));
+  return hip_status(sa::launch_ideal_mass(qc, kc, lse_d, d, scale, mass, (hipStream_t)stream), "ideal mass launch");
+}
+
+size_t sparse_attn_recall_workspace_bytes(const sa_geom* g) {
+  sa::Geom d;
+  if (make_geom(g, d) != SA_OK) return 0;
+  const size_t rows = (size_t)d.batch * d.heads * d.nblk;
+  return round_up(rows * d.nblk * sizeof(int32_t)) + round_up(rows * sizeof(int32_t));
+}
+
+int32_t sparse_attn_mask_recall(const double* mass, const int32_t* lut, const int32_t* counts, int32_t cap,
+                                const sa_geom* g, double* recall, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  sa::Geom d;
+  SA_TRY(make_geom(g, d));
+  if (d.nblk > kMaxSelectBlocks)
+    return fail(SA_ERR_UNSUPPORTED, "selection supports at most %d blocks per head (got %d)",
+                kMaxSelectBlocks, d.nblk);
+  SA_TRY(check_ptr(mass, 8, "mass"));
+  SA_TRY(check_ptr(lut, 4, "lut"));
+  SA_TRY(check_ptr(counts, 4, "counts"));
+  SA_TRY(check_ptr(recall, 8, "recall"));
+  if (cap < 1) return fail(SA_ERR_INVALID_ARG, "cap must be >= 1");
+  SA_TRY(check_ptr(workspace, kWsAlign, "workspace"));
+  const size_t rows = (size_t)d.batch * d.heads * d.nblk;
+  const size_t need = round_up(rows * d.nblk * sizeof(int32_t)) + round_up(rows * sizeof(int32_t));
+  if (workspace_bytes < need)
+    return fail(SA_ERR_CAPACITY, "workspace of %zu bytes is below the %zu needed", workspace_bytes, need);
+  int32_t* top = static_cast<int32_t*>(workspace);
+  int32_t* top_counts = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
+                                                   round_up(rows * d.nblk * sizeof(int32_t)));
+  hipStream_t s = (hipStream_t)stream;
+  // the top list of each row has the row's own count: selection with the counts as budgets
+  SA_TRY(hip_status(sa::launch_select(mass, d, 0, 0.0, counts, top, top_counts, d.nblk, s), "select launch"));
+  return hip_status(sa::launch_recall(lut, counts, cap, top, d, recall, s), "recall launch");
+}
+
 size_t sparse_attn_fwd_workspace_bytes(const sa_geom* g) {
   sa::Geom d;
   if (make_geom(g, d) != SA_OK) return 0;

@@ -59,6 +59,12 @@ hipError_t launch_mask_error(const float* lse_s, const float* lse_d, const void*
 size_t sequence_workspace_bytes(const Geom& g);
 hipError_t launch_sequence_budget(const double* scores, const Geom& g, long long total, void* workspace,
                                   int32_t** budget_out, hipStream_t s);
+// P_ideal [batch*heads, nblk, nblk] float64 from a dense run's LSE
+hipError_t launch_ideal_mass(const void* qc, const void* kc, const float* lse_d, const Geom& g, float scale,
+                             double* mass, hipStream_t s);
+// recall per row of kept lists against top lists [batch*heads*nblk, nblk] of the same counts
+hipError_t launch_recall(const int32_t* lut, const int32_t* counts, int cap, const int32_t* top, const Geom& g,
+                         double* recall, hipStream_t s);
 hipError_t launch_coarse(const double* scores, const double* vbar, double* oc, const Geom& g, hipStream_t s);
 
 }  // namespace sa

@@ -11,7 +11,8 @@
  *   coarse       block-level attention on pooled Q, K, V (coarse branch)
  *   router       fine-grained router scores (sub-cube pooling, G x G pooling)
  *   bwd          gradients of the block-sparse attention (dQ, dK, dV)
- *   quality      retained pooled mass, retained attention mass, L1 error
+ *   quality      retained pooled mass, retained attention mass, L1 error,
+ *                ideal block scores and the recall of kept lists
  *   attention    the whole path in one call, overlapped over two streams
  *   groups       asymmetric blocks: masks and forward for query blocks of
  *                2 or 4 cubes against single-cube key blocks
@@ -393,6 +394,35 @@ int32_t sparse_attn_fwd(const void* qc, const void* kc, const void* vc,
                         const int32_t* lut, const int32_t* counts, int32_t cap,
                         const sa_geom* g, float scale, void* oc, float* lse_c,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Ideal block scores ([VSA2] section 2.2: MeanPool of the full attention
+ * matrix, the target a router approximates): mass[i][j] = the full softmax
+ * mass that block i's real queries put on block j's real keys, averaged over
+ * those queries (rows sum to 1), recomputed from a dense run's LSE.
+ *   qc, kc [batch, heads, n_pad, head_dim] bf16, SA_LAYOUT_QK        (inputs)
+ *   lse_d  [batch, heads, n_pad] float32, natural-log LSE of sparse_attn_fwd
+ *          with every block kept (pad slots -inf)                     (input)
+ *   mass   [batch, heads, nblk, nblk] float64                         (output)
+ * scale <= 0 selects 1/sqrt(head_dim) and must match the dense run's. */
+int32_t sparse_attn_ideal_block_mass(const void* qc, const void* kc,
+                                     const float* lse_d, const sa_geom* g,
+                                     float scale, double* mass, void* stream);
+
+/* Recall of kept lists against the ideal block scores: per row, the share of
+ * the counts[row] blocks with the largest mass (lower id first on equal
+ * values) that the row's list holds; 1 for an empty list.
+ *   mass [batch, heads, nblk, nblk] float64; lut, counts, cap as selected,
+ *   with counts <= cap                                                (inputs)
+ *   recall [batch, heads, nblk] float64                               (output)
+ * workspace >= sparse_attn_recall_workspace_bytes (the top lists, [batch,
+ * heads, nblk, nblk] int32, and their counts), else SA_ERR_CAPACITY; nblk at
+ * most 4096 (SA_ERR_UNSUPPORTED). */
+size_t sparse_attn_recall_workspace_bytes(const sa_geom* g);
+int32_t sparse_attn_mask_recall(const double* mass, const int32_t* lut,
+                                const int32_t* counts, int32_t cap,
+                                const sa_geom* g, double* recall,
+                                void* workspace, size_t workspace_bytes,
+                                void* stream);
 
 /* ---- asymmetric blocks: query blocks of qgroup cubes --------------------
  * [SA2] "Block-Pooled Attention for Efficient Mask Construction": query

@@ -198,3 +198,17 @@ def test_per_sequence_argument_rules():
     big = geom(frames=64, height=64, width=68)      # 4352 blocks
     assert lib.sparse_attn_select_per_sequence(FAKE, ctypes.byref(big), 0.1, FAKE, FAKE, 5000, FAKE, 1 << 40,
                                                None) == sa.SA_ERR_UNSUPPORTED
+
+
+def test_ideal_mass_and_recall_argument_rules():
+    g = geom()
+    lib = sa.lib()
+    B = ctypes.byref(g)
+    assert lib.sparse_attn_ideal_block_mass(FAKE, FAKE, None, B, 0.0, FAKE, None) == sa.SA_ERR_INVALID_ARG
+    assert lib.sparse_attn_ideal_block_mass(FAKE, FAKE, FAKE, B, float("inf"), FAKE, None) == sa.SA_ERR_INVALID_ARG
+    need = lib.sparse_attn_recall_workspace_bytes(B)
+    assert need >= 2 * 16 * 16 * 4
+    assert lib.sparse_attn_mask_recall(FAKE, FAKE, FAKE, 16, B, FAKE, FAKE, need - 1, None) == sa.SA_ERR_CAPACITY
+    assert lib.sparse_attn_mask_recall(FAKE, FAKE, FAKE, 0, B, FAKE, FAKE, need, None) == sa.SA_ERR_INVALID_ARG
+    assert lib.sparse_attn_mask_recall(FAKE, FAKE, FAKE, 16, B, FAKE_MISALIGNED, FAKE, need,
+                                       None) == sa.SA_ERR_INVALID_ARG

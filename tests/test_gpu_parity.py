@@ -508,3 +508,24 @@ def test_per_sequence_exact_ties_across_rows():
         assert np.array_equal(counts.cpu().numpy()[0, 0], want)
         bad, _ = check_per_sequence(lut.cpu().numpy(), counts.cpu().numpy(), s, k_frac)
         assert bad == 0
+
+
+# ----------------------------------------------------------------------------
+# ideal block scores and recall
+# ----------------------------------------------------------------------------
+def test_ideal_mass_and_recall_match_oracle(case):
+    g, og, ref = case["g"], case["og"], case["ref_mask"]
+    qc, kc, vc = reorder3(case["qd"], case["kd"], case["vd"], g)
+    lut = torch.from_numpy(ref.lut).to(DEV)
+    counts = torch.from_numpy(ref.counts).to(DEV)
+    scores = torch.from_numpy(ref.scores).to(DEV)
+    mass, recall = sa.mask_recall(qc, kc, vc, lut, counts, scores, g)
+    torch.cuda.synchronize()
+    want = O.ideal_block_mass(case["ref_qc"], case["ref_kc"], og)
+    m = mass.cpu().numpy()
+    err = np.abs(m - want).max()
+    say(f"  ideal mass: max abs err {err:.2e}")
+    np.testing.assert_allclose(m, want, rtol=1e-4, atol=1e-7)
+    np.testing.assert_allclose(m.sum(axis=-1), 1.0, rtol=1e-5)
+    # recall is a ranking: judged on the GPU's own masses, it must be exact
+    np.testing.assert_array_equal(recall.cpu().numpy(), O.mask_recall(m, ref.lut, ref.counts))
