@@ -250,8 +250,34 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(const u32x4* __restrict__ q,
   }
 }
 
+// Direct global-to-LDS copy, 16 bytes per lane: lane l's bytes land at
+// dst + 16 l (dst wave-uniform).  The builtin exists only for the device; the
+// host pass of this file sees an empty body.
+__device__ __forceinline__ void copy_to_lds(const u32x4* src, u32x4* dst) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+#else
+  (void)src;
+  (void)dst;
+#endif
+}
+
+// s_waitcnt immediates: vmcnt(n) alone (expcnt and lgkmcnt at their maxima),
+// and lgkmcnt(0) alone (vmcnt and expcnt at their maxima)
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+constexpr int kLgkm0 = 0xC07F;
+
+// One workgroup of 4 waves per key block j.  Wave w owns keys 32 (w % 2) ..
+// +31 and query half w / 2 of every query block in j's transposed list, and
+// accumulates dV^T = dO^T P and dK^T = Q^T dS for those keys over that half;
+// the two halves are added in LDS at the end (fixed order).  The query
+// block's operands (Q and dO in both layouts, 64 KB at d = 128) and its LSE
+// and D rows are copied into LDS with direct global-to-LDS loads, double
+// buffered: the copy of the next block is in flight while the current one is
+// used, with explicit vmcnt waits and barriers (no fence that would drain the
+// copy in flight).
 template <int D>
-__global__ __launch_bounds__(128) void bwd_dkv_kernel(const u32x4* __restrict__ q, const u32x4* __restrict__ k,
+__global__ __launch_bounds__(256) void bwd_dkv_kernel(const u32x4* __restrict__ q, const u32x4* __restrict__ k,
                                                       const u32x4* __restrict__ v_qk, const u32x4* __restrict__ q_v,
                                                       const u32x4* __restrict__ do_qk,
                                                       const u32x4* __restrict__ do_v, const float* __restrict__ lse,
@@ -261,26 +287,33 @@ __global__ __launch_bounds__(128) void bwd_dkv_kernel(const u32x4* __restrict__ 
                                                       float sc_log2, float scale, bf16* __restrict__ dk,
                                                       bf16* __restrict__ dv) {
   constexpr int NDS = D / 16, NDT = D / 32, BLK = 64 * D / 8;
+  constexpr int NARR = 2 * NDS;          // 1 KB chunks per array (= 4 * NDT)
+  constexpr int NCH = 4 * NARR;          // chunks per query block: Q, dO (QK layout), Q, dO (V layout)
+  constexpr int PER_WAVE = NCH / 4;      // chunk copies issued by each wave
   const int j = blockIdx.x;
   const long long bh = blockIdx.y;
   const long long col = bh * g.nblk + j;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, hf = lane >> 5, r = lane & 31;
+  // the wave index is uniform: keep it (and the copy addresses) on the scalar unit
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, hf = lane >> 5, r = lane & 31;
+  const int kh = wave & 1, qq = wave >> 1;
   const int qpos = hf * 32 + sigma32(r);
   const long long head = bh * (long long)g.nblk * BLK;
 
-  __shared__ u32x4 qs[2 * NDS * 64], dos[2 * NDS * 64], qvs[NDT * 4 * 64], dovs[NDT * 4 * 64];
-  __shared__ float l2s[kBlock], dls[kBlock];
+  // per buffer: the NCH operand chunks, then one chunk whose first 256 bytes
+  // hold the LSE row and the next 256 bytes the D row
+  __shared__ u32x4 stage[2][(NCH + 1) * 64];
 
-  // this wave's 32 keys (B operands, chunk t32 = w) and whether this lane's key is real
+  // this wave's 32 keys (B operands, chunk t32 = kh) and whether this lane's key is real
   u32x4 kreg[NDS], vreg[NDS];
   const u32x4* kb = k + head + (long long)j * BLK;
   const u32x4* vb = v_qk + head + (long long)j * BLK;
 #pragma unroll
   for (int ds = 0; ds < NDS; ++ds) {
-    kreg[ds] = kb[(w * NDS + ds) * 64 + lane];
-    vreg[ds] = vb[(w * NDS + ds) * 64 + lane];
+    kreg[ds] = kb[(kh * NDS + ds) * 64 + lane];
+    vreg[ds] = vb[(kh * NDS + ds) * 64 + lane];
   }
-  const bool key_real = slot_token(g, j, 32 * w + r) >= 0;
+  const bool key_real = slot_token(g, j, 32 * kh + r) >= 0;
 
   f32x16 adk[NDT], adv[NDT];
 #pragma unroll
@@ -291,28 +324,49 @@ __global__ __launch_bounds__(128) void bwd_dkv_kernel(const u32x4* __restrict__ 
   int count = counts_t[col];
   count = count < 0 ? 0 : (count > cap_t ? cap_t : count);
   const int32_t* list = lut_t + col * cap_t;
-  for (int it = 0; it < count; ++it) {
+  auto valid = [&](int i) { return i >= 0 && i < g.nblk; };
+  // copy query block list[it] into buffer b: wave w copies array w (chunks
+  // [w NARR, (w + 1) NARR)); waves 0 and 1 also copy the LSE and D rows
+  static_assert(PER_WAVE == NARR, "one array per wave");
+  const u32x4* my_src = wave == 0 ? q : (wave == 1 ? do_qk : (wave == 2 ? q_v : do_v));
+  // (wave 0 also copies the LSE and D rows: one 16-byte-lane copy whose lanes
+  // 0-15 take the 64 LSE values and lanes 16-31 the 64 D values; lanes 32-63
+  // repeat them into a part of the slot that is not read)
+  const u32x4* row_src = reinterpret_cast<const u32x4*>((lane & 16) ? delta : lse);
+  auto issue = [&](int b, int it) {
     const int i0 = list[it];
-    const int i = (i0 >= 0 && i0 < g.nblk) ? i0 : -1;
-    __syncthreads();   // the previous query block's operands are no longer read
-    if (i >= 0) {
-      const long long ob = head + (long long)i * BLK;
-      for (int u = threadIdx.x; u < 2 * NDS * 64; u += 128) {
-        qs[u] = q[ob + u];
-        dos[u] = do_qk[ob + u];
-        qvs[u] = q_v[ob + u];
-        dovs[u] = do_v[ob + u];
-      }
-      if (threadIdx.x < kBlock) {
-        const long long slot = bh * g.n_pad + (long long)i * kBlock + threadIdx.x;
-        l2s[threadIdx.x] = lse2_of(lse[slot]);
-        dls[threadIdx.x] = delta[slot];
-      }
-    }
-    __syncthreads();
-    if (i < 0) continue;   // uniform across the workgroup
+    const int i = valid(i0) ? i0 : 0;
+    const long long ob = head + (long long)i * BLK;
 #pragma unroll
-    for (int qq = 0; qq < 2; ++qq) {
+    for (int cc = 0; cc < NARR; ++cc)
+      copy_to_lds(my_src + ob + cc * 64 + lane, &stage[b][(wave * NARR + cc) * 64]);
+    if (wave == 0)
+      copy_to_lds(row_src + (bh * g.n_pad + (long long)i * kBlock) / 4 + (lane & 15), &stage[b][NCH * 64]);
+  };
+
+  // the key operands are in registers before any copy is queued behind them,
+  // so no wait inside the loop has to cover them
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  if (count > 0) issue(0, 0);
+  for (int it = 0; it < count; ++it) {
+    const int b = it & 1;
+    if (it + 1 < count) {
+      issue(b ^ 1, it + 1);
+      // this block's copies are done once only the next block's remain in flight
+      if (wave == 0)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER_WAVE + 1));
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER_WAVE));
+    } else {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    }
+    __builtin_amdgcn_s_barrier();   // every wave's copies of buffer b have landed
+    if (valid(list[it])) {
+      const u32x4* qs = &stage[b][0];
+      const u32x4* dos = &stage[b][NARR * 64];
+      const u32x4* qvs = &stage[b][2 * NARR * 64];
+      const u32x4* dovs = &stage[b][3 * NARR * 64];
+      const float* lrow = reinterpret_cast<const float*>(&stage[b][NCH * 64]);
       f32x16 s, dp;
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[e] = dp[e] = 0.f;
@@ -331,9 +385,10 @@ __global__ __launch_bounds__(128) void bwd_dkv_kernel(const u32x4* __restrict__ 
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const int qi = 32 * qq + 16 * ((e + u) >> 3) + 8 * hf + ((e + u) & 7);
-          const float p = key_real ? __builtin_amdgcn_exp2f(fmaf(s[e + u], sc_log2, -l2s[qi])) : 0.f;
+          const float p = key_real ? __builtin_amdgcn_exp2f(fmaf(s[e + u], sc_log2, -lse2_of(lrow[qi])))
+                                   : 0.f;
           pv[u] = p;
-          sv[u] = p * (dp[e + u] - dls[qi]);
+          sv[u] = p * (dp[e + u] - lrow[kBlock + qi]);
         }
         pw[e >> 1] = pack_bf16x2(pv[0], pv[1]);
         dsw[e >> 1] = pack_bf16x2(sv[0], sv[1]);
@@ -345,15 +400,39 @@ __global__ __launch_bounds__(128) void bwd_dkv_kernel(const u32x4* __restrict__ 
         const u32x4 bs = {dsw[4 * kk], dsw[4 * kk + 1], dsw[4 * kk + 2], dsw[4 * kk + 3]};
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-          adv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(dovs[(dt * 4 + ks) * 64 + lane]), as_bf16x8(bp),
-                                                            adv[dt], 0, 0, 0);
-          adk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qvs[(dt * 4 + ks) * 64 + lane]), as_bf16x8(bs),
-                                                            adk[dt], 0, 0, 0);
+          adv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(dovs[(dt * 4 + ks) * 64 + lane]),
+                                                            as_bf16x8(bp), adv[dt], 0, 0, 0);
+          adk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qvs[(dt * 4 + ks) * 64 + lane]),
+                                                            as_bf16x8(bs), adk[dt], 0, 0, 0);
         }
       }
     }
+    __builtin_amdgcn_s_waitcnt(kLgkm0);   // this wave's LDS reads are complete
+    __builtin_amdgcn_s_barrier();         // ... and every wave's, before b is refilled
   }
-  const long long orow = (bh * g.n_pad + (long long)j * 64 + 32 * w + r) * D;
+
+  // query half 1 hands its partial sums to query half 0 through LDS
+  float* red = reinterpret_cast<float*>(&stage[0][0]);   // 2 key halves x 2 NDT x 16 x 64 floats
+  float* mine = red + (size_t)kh * (2 * NDT * 16 * 64);
+  if (qq == 1) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        mine[((2 * dt) * 16 + e) * 64 + lane] = adk[dt][e];
+        mine[((2 * dt + 1) * 16 + e) * 64 + lane] = adv[dt][e];
+      }
+  }
+  __syncthreads();
+  if (qq == 1) return;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      adk[dt][e] += mine[((2 * dt) * 16 + e) * 64 + lane];
+      adv[dt][e] += mine[((2 * dt + 1) * 16 + e) * 64 + lane];
+    }
+  const long long orow = (bh * g.n_pad + (long long)j * 64 + 32 * kh + r) * D;
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -395,18 +474,20 @@ hipError_t launch_transpose_lut(const int32_t* lut, const int32_t* counts, int c
 
 hipError_t launch_bwd(const BwdArgs& a, const Geom& g, float scale, void* dq, void* dk, void* dv, hipStream_t s) {
   const float sc_log2 = scale * kLog2e;
+  // (an XCD-aware order as in the forward cut the traffic beyond L2 by a
+  // third but made neither kernel faster: both wait on their own chains)
   dim3 grid(g.nblk, g.batch * g.heads);
   auto U = [](const void* p) { return static_cast<const u32x4*>(p); };
   if (g.d == 128) {
     bwd_dq_kernel<128><<<grid, 64, 0, s>>>(U(a.q), U(a.k), U(a.v_qk), U(a.k_v), U(a.do_qk), a.lse, a.delta, a.lut,
                                            a.counts, a.cap, g, sc_log2, scale, static_cast<bf16*>(dq));
-    bwd_dkv_kernel<128><<<grid, 128, 0, s>>>(U(a.q), U(a.k), U(a.v_qk), U(a.q_v), U(a.do_qk), U(a.do_v), a.lse,
+    bwd_dkv_kernel<128><<<grid, 256, 0, s>>>(U(a.q), U(a.k), U(a.v_qk), U(a.q_v), U(a.do_qk), U(a.do_v), a.lse,
                                              a.delta, a.lut_t, a.counts_t, a.cap_t, g, sc_log2, scale,
                                              static_cast<bf16*>(dk), static_cast<bf16*>(dv));
   } else {
     bwd_dq_kernel<64><<<grid, 64, 0, s>>>(U(a.q), U(a.k), U(a.v_qk), U(a.k_v), U(a.do_qk), a.lse, a.delta, a.lut,
                                           a.counts, a.cap, g, sc_log2, scale, static_cast<bf16*>(dq));
-    bwd_dkv_kernel<64><<<grid, 128, 0, s>>>(U(a.q), U(a.k), U(a.v_qk), U(a.q_v), U(a.do_qk), U(a.do_v), a.lse,
+    bwd_dkv_kernel<64><<<grid, 256, 0, s>>>(U(a.q), U(a.k), U(a.v_qk), U(a.q_v), U(a.do_qk), U(a.do_v), a.lse,
                                             a.delta, a.lut_t, a.counts_t, a.cap_t, g, sc_log2, scale,
                                             static_cast<bf16*>(dk), static_cast<bf16*>(dv));
   }

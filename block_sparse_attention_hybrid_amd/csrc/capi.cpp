@@ -300,8 +300,8 @@ int32_t sparse_attn_bwd(const sa_bwd_args* a, const sa_geom* g, float scale, voi
   SA_TRY(check_ptr(a->k_v, 16, "k_v"));
   SA_TRY(check_ptr(a->do_qk, 16, "do_qk"));
   SA_TRY(check_ptr(a->do_v, 16, "do_v"));
-  SA_TRY(check_ptr(a->lse, 4, "lse"));
-  SA_TRY(check_ptr(a->delta, 4, "delta"));
+  SA_TRY(check_ptr(a->lse, 16, "lse"));
+  SA_TRY(check_ptr(a->delta, 16, "delta"));
   SA_TRY(check_ptr(a->lut, 4, "lut"));
   SA_TRY(check_ptr(a->counts, 4, "counts"));
   SA_TRY(check_ptr(a->lut_t, 4, "lut_t"));
