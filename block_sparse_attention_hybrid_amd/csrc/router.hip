@@ -100,14 +100,31 @@ __device__ __forceinline__ void score_tile(const double* __restrict__ qh, const 
 #pragma unroll
     for (int b = 0; b < 2; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
   const int lr = threadIdx.x >> 2, lc = (threadIdx.x & 3) * 4;
+  const int gi = r0 + lr, gj = c0 + lr;
+  const double* qrow = qh + (long long)(gi < nr ? gi : nr - 1) * d + lc;
+  const double* krow = kh + (long long)(gj < nr ? gj : nr - 1) * d + lc;
+  // the next k step's operands are loaded into registers while this step's
+  // products run (rows past nr read a clamped row and are zeroed)
+  double an[4], bn[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    an[e] = qrow[e];
+    bn[e] = krow[e];
+  }
   for (int k0 = 0; k0 < d; k0 += kKc) {
-    const int gi = r0 + lr, gj = c0 + lr;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      As[lr * kLd + lc + e] = gi < nr ? qh[(long long)gi * d + k0 + lc + e] : 0.0;
-      Bs[lr * kLd + lc + e] = gj < nr ? kh[(long long)gj * d + k0 + lc + e] : 0.0;
+      As[lr * kLd + lc + e] = gi < nr ? an[e] : 0.0;
+      Bs[lr * kLd + lc + e] = gj < nr ? bn[e] : 0.0;
     }
     __syncthreads();
+    if (k0 + kKc < d) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        an[e] = qrow[k0 + kKc + e];
+        bn[e] = krow[k0 + kKc + e];
+      }
+    }
 #pragma unroll
     for (int ks = 0; ks < kKc; ks += 4) {
       const int kk = ks + (lane >> 4);
