@@ -214,7 +214,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const double* __restri
 
   int kc = row_budget != nullptr ? row_budget[row] : kc_default;
   kc = kc < 0 ? 0 : (kc > n ? n : kc);
-  uint64_t valid = 0;
+  uint32_t valid = 0;   // per-lane element masks: E <= 16 bits
   double mx = -INFINITY, lo0 = INFINITY;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
@@ -222,7 +222,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const double* __restri
     const double v = s[e] == 0.0 ? 0.0 : s[e];  // -0 and +0 are the same score
     s[e] = in ? v : 0.0;
     ev[e] = 0.f;
-    valid |= (uint64_t)in << e;
+    valid |= (uint32_t)in << e;
     mx = fmax(mx, in ? v : -INFINITY);
     lo0 = fmin(lo0, in ? v : INFINITY);
   }
@@ -241,7 +241,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const double* __restri
 
   const bool keep_all = (p >= 1.0) || (kc >= n);
   const bool keep_none = !keep_all && kc == 0 && !(p > 0.0);
-  uint64_t above = 0, member = 0;
+  uint32_t above = 0, member = 0;
   uint64_t kept_rank = 0;    // members kept by rank: bit = member index in ascending id
   long long take = -1;       // >= 0: the first `take` members by id are kept
   int mbase = 0;             // members held by the waves before this one
@@ -250,7 +250,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const double* __restri
     above = valid;
   } else if (!keep_none) {
 #pragma unroll
-    for (int e = 0; e < E; ++e) ev[e] = ((valid >> e) & 1ull) ? prob(s[e], mx) : 0.f;
+    for (int e = 0; e < E; ++e) ev[e] = ((valid >> e) & 1u) ? prob(s[e], mx) : 0.f;
 
     member = valid;
     int m = n;                 // members left (uniform over the workgroup)
@@ -265,7 +265,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const double* __restri
         hi = -INFINITY;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-          const bool mem = (member >> e) & 1ull;
+          const bool mem = (member >> e) & 1u;
           lo = fmin(lo, mem ? s[e] : INFINITY);
           hi = fmax(hi, mem ? s[e] : -INFINITY);
         }
@@ -299,7 +299,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const double* __restri
         uint64_t kmin = ~0ull, kmax = 0;
 #pragma unroll
         for (int e = 0; e < E; ++e)
-          if ((member >> e) & 1ull) {
+          if ((member >> e) & 1u) {
             const uint64_t k = desc_key(fresh(s[e]));
             kmin = k < kmin ? k : kmin;
             kmax = k > kmax ? k : kmax;
@@ -334,7 +334,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const double* __restri
       __syncthreads();
 #pragma unroll
       for (int e = 0; e < E; ++e)
-        if ((member >> e) & 1ull) {
+        if ((member >> e) & 1u) {
           const int b = bucket(fresh(s[e]));
           const unsigned long long f = to_fixed(fresh(ev[e]));
           if constexpr (kPacked) {
@@ -414,17 +414,17 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const double* __restri
       target = xdec[4];
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        const bool mem = (member >> e) & 1ull;
+        const bool mem = (member >> e) & 1u;
         const int b = bucket(fresh(s[e]));
-        above |= (uint64_t)(mem && b < bstar) << e;
-        member &= ~((uint64_t)(mem && b != bstar) << e);
+        above |= (uint32_t)(mem && b < bstar) << e;
+        member &= ~((uint32_t)(mem && b != bstar) << e);
       }
     }
 
     // members of the waves before this one (ascending id across the row)
     int nm = 0;
 #pragma unroll
-    for (int e = 0; e < E; ++e) nm += __popcll(ballot((member >> e) & 1ull));
+    for (int e = 0; e < E; ++e) nm += __popcll(ballot((member >> e) & 1u));
     if (lane == 0) xn[wave] = nm;
     __syncthreads();
     for (int v = 0; v < wave; ++v) mbase += xn[v];
@@ -434,7 +434,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const double* __restri
       int seen = mbase;
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        const bool is_mem = (member >> e) & 1ull;
+        const bool is_mem = (member >> e) & 1u;
         const uint64_t bm = ballot(is_mem);
         if (bm) {
           if (is_mem) {
@@ -478,21 +478,30 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const double* __restri
   // ids follow those kept by the waves before it
   uint64_t bk[E];
   int nk = 0;
-  long long seen = mbase;
+  if (ballot(member != 0u) == 0ull) {
+    // no members in this wave (the common case): kept = above
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const bool is_mem = (member >> e) & 1ull;
-    const uint64_t bm = ballot(is_mem);
-    const long long rank = seen + __popcll(bm & lt);
-    seen += __popcll(bm);
-    const bool sel = take >= 0 ? rank < take : (rank < kWave && ((kept_rank >> rank) & 1ull));
-    bk[e] = ballot(((above >> e) & 1ull) || (is_mem && sel));
-    nk += __popcll(bk[e]);
+    for (int e = 0; e < E; ++e) {
+      bk[e] = ballot((above >> e) & 1u);
+      nk += __popcll(bk[e]);
+    }
+  } else {
+    int seen = mbase;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const bool is_mem = (member >> e) & 1u;
+      const uint64_t bm = ballot(is_mem);
+      const int rank = seen + __popcll(bm & lt);
+      seen += __popcll(bm);
+      const bool sel = take >= 0 ? rank < take : (rank < kWave && ((kept_rank >> rank) & 1ull));
+      bk[e] = ballot(((above >> e) & 1u) || (is_mem && sel));
+      nk += __popcll(bk[e]);
+    }
   }
   __syncthreads();  // the member counts have been read before they are overwritten
   if (lane == 0) xn[wave] = nk;
   __syncthreads();
-  long long written = 0, total = 0;
+  int written = 0, total = 0;
 #pragma unroll
   for (int v = 0; v < kWaves; ++v) {
     written += v < wave ? xn[v] : 0;
@@ -502,7 +511,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const double* __restri
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const bool keep = (bk[e] >> lane) & 1ull;
-    const long long pos = written + __popcll(bk[e] & lt);
+    const int pos = written + __popcll(bk[e] & lt);
     written += __popcll(bk[e]);
     if (keep && pos < cap) out[pos] = first_id + e * kWave + lane;
   }
