@@ -308,6 +308,23 @@ def next_rows(path, reps=3):
     return out
 
 
+def machine_check(dev):
+    """The box's own ceilings beside the published peaks: a plain 1 GiB
+    device copy (HBM read + write) and a dense bf16 GEMM through the vendor
+    library (torch.matmul), each event-timed."""
+    x = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    y = torch.empty_like(x)
+    t_copy = time_call(lambda: y.copy_(x), 10)
+    m = 8192
+    a = torch.randn((m, m), dtype=torch.bfloat16, device=dev)
+    b = torch.randn((m, m), dtype=torch.bfloat16, device=dev)
+    t_mm = time_call(lambda: torch.matmul(a, b), 10)
+    del x, y, a, b
+    return {"copy_gbps": round(2 * (1 << 30) / (t_copy * 1e-3) / 1e9, 1),
+            "dense_bf16_gemm_tflops": round(2.0 * m ** 3 / (t_mm * 1e-3) / 1e12, 1),
+            "note": "1 GiB device copy (bytes read + written); 8192^3 bf16 torch.matmul"}
+
+
 def cpu_baseline(path, seconds):
     """The oracle, as it stands, on a bounded sample of the same workload:
     the mask of whole heads (pool, scores, selection of every row) and the
@@ -470,6 +487,7 @@ def main():
     if not args.no_next_rows:
         log("[bench] timing the coarse-output and router kernels")
         out["next_rows"] = next_rows(path)
+        out["machine_check"] = machine_check(dev)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(path, args.cpu_seconds)
