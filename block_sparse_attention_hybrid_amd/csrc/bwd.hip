@@ -166,26 +166,51 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(const u32x4* __restrict__ q,
   int count = counts[row];
   count = count < 0 ? 0 : (count > cap ? cap : count);
   const int32_t* lrow = lut + row * cap;
-  for (int it = 0; it < count; ++it) {
+
+  // slot offsets of this lane's key slot, for the per-block padding ballot
+  int lt, lh, lw;
+  slot_offsets(g, lane, lt, lh, lw);
+
+  // K and V (QK layout) of the current block, K in the V layout
+  u32x4 kreg[2][NDS], vreg[2][NDS], kvreg[NDT][4];
+  auto block_id = [&](int it) {
     const int j0 = lrow[it];
-    const bool ok = j0 >= 0 && j0 < g.nblk;
-    const int j = ok ? j0 : 0;
+    return (j0 >= 0 && j0 < g.nblk) ? j0 : -1;
+  };
+  auto load_kv = [&](int j) {
+    const long long o = head + (long long)(j < 0 ? 0 : j) * BLK;
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        kreg[kt][ds] = k[o + (kt * NDS + ds) * 64 + kpos];
+        vreg[kt][ds] = v_qk[o + (kt * NDS + ds) * 64 + kpos];
+      }
+  };
+  auto load_kvv = [&](int j) {
+    const long long o = head + (long long)(j < 0 ? 0 : j) * BLK;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) kvreg[dt][ks] = k_v[o + (dt * 4 + ks) * 64 + lane];
+  };
+
+  // Pipeline per kept block t: K_v(t) is requested as the block starts (it
+  // is first used by the third product); K(t+1) and V(t+1) go into the
+  // registers of K(t) and V(t) once the score products of t are issued.
+  int j = count > 0 ? block_id(0) : -1;
+  if (count > 0) load_kv(j);
+  for (int it = 0; it < count; ++it) {
+    load_kvv(j);
+    const uint64_t real = j >= 0 ? block_real_mask_wave(g, j, lt, lh, lw) : 0ull;
     // this lane's 32 key bits: register e of tile kt <-> key 32 kt + 16 (e / 8) + 8 hf + e % 8
-    const uint64_t real = ok ? block_real_mask(g, j) : 0ull;
     const uint32_t lm = (uint32_t)((real >> (8 * hf)) & 0xffu) | ((uint32_t)((real >> (16 + 8 * hf)) & 0xffu) << 8) |
                         ((uint32_t)((real >> (32 + 8 * hf)) & 0xffu) << 16) |
                         ((uint32_t)((real >> (48 + 8 * hf)) & 0xffu) << 24);
-    const u32x4* kb = k + head + (long long)j * BLK;
-    const u32x4* vb = v_qk + head + (long long)j * BLK;
-    const u32x4* kvb = k_v + head + (long long)j * BLK;
-    u32x4 kreg[2][NDS], vreg[2][NDS];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int ds = 0; ds < NDS; ++ds) {
-        kreg[kt][ds] = kb[(kt * NDS + ds) * 64 + kpos];
-        vreg[kt][ds] = vb[(kt * NDS + ds) * 64 + kpos];
-      }
+    // Q and dO are read from LDS at each use rather than held in registers
+    // across the loop: the registers go to K, V and K_v, so all of a block's
+    // loads are in flight at once
+    asm volatile("" ::: "memory");
     // phase 1: dS^T of both query halves (bf16 pairs); phase 2: dQ^T += K^T dS^T
     uint32_t dsw[2][2][8];
 #pragma unroll
@@ -212,18 +237,15 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(const u32x4* __restrict__ q,
           float v2[2];
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
-            const bool real = (lm >> (16 * kt + e + u)) & 1u;
-            const float p = real ? __builtin_amdgcn_exp2f(fmaf(st[kt][e + u], sc_log2, -l2[qt])) : 0.f;
+            const bool live = (lm >> (16 * kt + e + u)) & 1u;
+            const float p = live ? __builtin_amdgcn_exp2f(fmaf(st[kt][e + u], sc_log2, -l2[qt])) : 0.f;
             v2[u] = p * (dpt[kt][e + u] - dl[qt]);
           }
           dsw[qt][kt][e >> 1] = pack_bf16x2(v2[0], v2[1]);
         }
     }
-    u32x4 kvreg[NDT][4];
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) kvreg[dt][ks] = kvb[(dt * 4 + ks) * 64 + lane];
+    const int jn = it + 1 < count ? block_id(it + 1) : j;
+    if (it + 1 < count) load_kv(jn);
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
@@ -234,6 +256,7 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(const u32x4* __restrict__ q,
         acc[dt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kvreg[dt][ks]), as_bf16x8(bw), acc[dt][qt],
                                                               0, 0, 0);
       }
+    j = jn;
   }
   bf16* ob = dq + (bh * g.n_pad + (long long)i * 64) * D;
 #pragma unroll

@@ -70,6 +70,18 @@ __device__ __forceinline__ uint64_t block_real_mask(const Geom& g, int i) {
   return m;
 }
 
+// The same mask from a whole wavefront at once: lane l passes the offsets of
+// slot l (slot_offsets(g, l, ...)), i is wave-uniform and every lane is
+// active.  One ballot instead of a loop over the 64 slots.
+__device__ __forceinline__ uint64_t block_real_mask_wave(const Geom& g, int i, int lt, int lh, int lw) {
+  int bt, bh, bw;
+  block_coords(g, i, bt, bh, bw);
+  const int rt = min(g.ct, g.frames - bt * g.ct);
+  const int rh = min(g.ch, g.height - bh * g.ch);
+  const int rw = min(g.cw, g.width - bw * g.cw);
+  return __ballot(lt < rt && lh < rh && lw < rw);
+}
+
 // Row-major token index of slot s of block i, or -1 for a pad slot.
 __device__ __forceinline__ long long slot_token(const Geom& g, int i, int s) {
   int bt, bh, bw, tt, hh, ww;
