@@ -336,7 +336,10 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(const u32x4* __restrict__ 
     kreg[ds] = kb[(kh * NDS + ds) * 64 + lane];
     vreg[ds] = vb[(kh * NDS + ds) * 64 + lane];
   }
-  const bool key_real = slot_token(g, j, 32 * kh + r) >= 0;
+  // all ones for a real key, zero for a pad slot; opaque so that the
+  // compiler blends with it instead of branching around the exponentials
+  uint32_t key_bits = slot_token(g, j, 32 * kh + r) >= 0 ? 0xffffffffu : 0u;
+  asm volatile("" : "+v"(key_bits));
 
   f32x16 adk[NDT], adv[NDT];
 #pragma unroll
@@ -408,8 +411,9 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(const u32x4* __restrict__ 
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const int qi = 32 * qq + 16 * ((e + u) >> 3) + 8 * hf + ((e + u) & 7);
-          const float p = key_real ? __builtin_amdgcn_exp2f(fmaf(s[e + u], sc_log2, -lse2_of(lrow[qi])))
-                                   : 0.f;
+          // pad keys: exponent -inf (bit blend), so p = 0 with no branch around the exponential
+          const uint32_t xb = __float_as_uint(fmaf(s[e + u], sc_log2, -lse2_of(lrow[qi])));
+          const float p = __builtin_amdgcn_exp2f(__uint_as_float((xb & key_bits) | (0xff800000u & ~key_bits)));
           pv[u] = p;
           sv[u] = p * (dp[e + u] - lrow[kBlock + qi]);
         }
