@@ -21,6 +21,7 @@
 // product, which then takes them straight from registers as bf16 pairs.
 #include "sa_launch.h"
 #include "sa_layout.h"
+#include "sa_rowmap.h"
 
 #include <math.h>
 
@@ -29,6 +30,10 @@ namespace sa {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+#ifndef SA_DQ_XCD_GROUP
+#define SA_DQ_XCD_GROUP 4
+#endif
+constexpr int kDqXcdGroup = SA_DQ_XCD_GROUP;   // XCDs sweeping one head together in the dq kernel
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -128,11 +133,16 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(const u32x4* __restrict__ q,
                                                     const u32x4* __restrict__ do_qk, const float* __restrict__ lse,
                                                     const float* __restrict__ delta, const int32_t* __restrict__ lut,
                                                     const int32_t* __restrict__ counts, int cap, Geom g,
-                                                    float sc_log2, float scale, bf16* __restrict__ dq) {
+                                                    float sc_log2, float scale, bf16* __restrict__ dq,
+                                                    RowMap map) {
   constexpr int NDS = D / 16, NDT = D / 32, BLK = 64 * D / 8;
-  const int i = blockIdx.x;
-  const long long bh = blockIdx.y;
-  const long long row = bh * g.nblk + i;
+  // XCD-aware order: each XCD sweeps neighbouring query blocks of one head,
+  // whose kept lists overlap, so more of their K/V tiles hit its L2
+  const int wrow = row_of_workgroup<kDqXcdGroup>(blockIdx.x, map);
+  if (wrow < 0) return;
+  const long long bh = wrow / g.nblk;
+  const int i = wrow - (int)(bh * g.nblk);
+  const long long row = wrow;
   const int lane = threadIdx.x, hf = lane >> 5, r = lane & 31;
   const int kpos = hf * 32 + sigma32(r);
   const long long head = bh * (long long)g.nblk * BLK;
@@ -177,75 +187,129 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(const u32x4* __restrict__ q,
     const int j0 = lrow[it];
     return (j0 >= 0 && j0 < g.nblk) ? j0 : -1;
   };
-  auto load_kv = [&](int j) {
-    const long long o = head + (long long)(j < 0 ? 0 : j) * BLK;
+  auto base_of = [&](int j) { return head + (long long)(j < 0 ? 0 : j) * BLK; };
+  auto load_k = [&](int j) {
+    const long long o = base_of(j);
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds)
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        kreg[kt][ds] = k[o + (kt * NDS + ds) * 64 + kpos];
-        vreg[kt][ds] = v_qk[o + (kt * NDS + ds) * 64 + kpos];
-      }
+      for (int kt = 0; kt < 2; ++kt) kreg[kt][ds] = k[o + (kt * NDS + ds) * 64 + kpos];
+  };
+  auto load_v = [&](int j) {
+    const long long o = base_of(j);
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) vreg[kt][ds] = v_qk[o + (kt * NDS + ds) * 64 + kpos];
   };
   auto load_kvv = [&](int j) {
-    const long long o = head + (long long)(j < 0 ? 0 : j) * BLK;
+    const long long o = base_of(j);
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) kvreg[dt][ks] = k_v[o + (dt * 4 + ks) * 64 + lane];
   };
+  // S^T and dP^T of one query half: one product over d with K or V as the
+  // A operand.  The first MFMA takes the start value: the free zero operand,
+  // or for S^T of a block with pad keys 0 (real key) / -inf (pad key), so
+  // that P = 0 on pad keys with no select per element.
+  const f32x16 zero = {};
+  // the B operands of one product (this half's Q or dO chunks) are read from
+  // LDS together, ahead of the MFMAs, so the read latency is paid once
+  auto read_ops = [&](const u32x4* ops, int qt, u32x4 (&b)[NDS]) {
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) b[ds] = ops[(qt * NDS + ds) * 64 + lane];
+  };
+  auto product_rest = [&](const u32x4 (&a)[2][NDS], const u32x4 (&b)[NDS], f32x16 (&acc2)[2]) {
+#pragma unroll
+    for (int ds = 1; ds < NDS; ++ds)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+        acc2[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[kt][ds]), as_bf16x8(b[ds]), acc2[kt], 0, 0, 0);
+  };
+  auto scores_s = [&](int qt, f32x16 (&st)[2], uint64_t real, uint32_t lm) {
+    u32x4 b[NDS];
+    read_ops(qlds, qt, b);
+    if (real == ~0ull) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+        st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kreg[kt][0]), as_bf16x8(b[0]), zero, 0, 0, 0);
+    } else {
+      asm volatile("" : "+v"(lm));
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        f32x16 init;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) init[e] = ((lm >> (16 * kt + e)) & 1u) ? 0.f : -INFINITY;
+        st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kreg[kt][0]), as_bf16x8(b[0]), init, 0, 0, 0);
+      }
+    }
+    product_rest(kreg, b, st);
+  };
+  auto scores_dp = [&](int qt, f32x16 (&dpt)[2]) {
+    u32x4 b[NDS];
+    read_ops(dolds, qt, b);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+      dpt[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vreg[kt][0]), as_bf16x8(b[0]), zero, 0, 0, 0);
+    product_rest(vreg, b, dpt);
+  };
+  // dS^T = P^T * (dP^T - D) of one query half, as bf16 pairs
+  auto grad_scores = [&](const f32x16 (&st)[2], const f32x16 (&dpt)[2], int qt, uint32_t (&dsw)[2][8]) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) {
+        float v2[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(st[kt][e + u], sc_log2, -l2[qt]));
+          v2[u] = p * (dpt[kt][e + u] - dl[qt]);
+        }
+        dsw[kt][e >> 1] = pack_bf16x2(v2[0], v2[1]);
+      }
+  };
 
-  // Pipeline per kept block t: K_v(t) is requested as the block starts (it
-  // is first used by the third product); K(t+1) and V(t+1) go into the
-  // registers of K(t) and V(t) once the score products of t are issued.
+  // Per kept block t, each operand's registers are refilled for block t+1
+  // as soon as their last product of block t is issued: K after the two
+  // score products, V after the two dP products, K_v after the dQ products.
+  // Every load thereby has most of a block of work as lead time.  Past the
+  // last block the "next" block is the current one again (a redundant
+  // reload rather than a branch, which would make the compiler wait for
+  // every load in flight where the paths meet).
   int j = count > 0 ? block_id(0) : -1;
-  if (count > 0) load_kv(j);
-  for (int it = 0; it < count; ++it) {
+  if (count > 0) {
+    load_k(j);
+    load_v(j);
     load_kvv(j);
+  }
+  for (int it = 0; it < count; ++it) {
+    const bool more = it + 1 < count;
+    const int jn = more ? block_id(it + 1) : j;
     const uint64_t real = j >= 0 ? block_real_mask_wave(g, j, lt, lh, lw) : 0ull;
     // this lane's 32 key bits: register e of tile kt <-> key 32 kt + 16 (e / 8) + 8 hf + e % 8
     const uint32_t lm = (uint32_t)((real >> (8 * hf)) & 0xffu) | ((uint32_t)((real >> (16 + 8 * hf)) & 0xffu) << 8) |
                         ((uint32_t)((real >> (32 + 8 * hf)) & 0xffu) << 16) |
                         ((uint32_t)((real >> (48 + 8 * hf)) & 0xffu) << 24);
     // Q and dO are read from LDS at each use rather than held in registers
-    // across the loop: the registers go to K, V and K_v, so all of a block's
-    // loads are in flight at once
+    // across the loop, which leaves the registers to the operands in flight
     asm volatile("" ::: "memory");
-    // phase 1: dS^T of both query halves (bf16 pairs); phase 2: dQ^T += K^T dS^T
+    f32x16 st0[2], st1[2], dpt[2];
     uint32_t dsw[2][2][8];
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      f32x16 st[2], dpt[2];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) st[kt][e] = dpt[kt][e] = 0.f;
-#pragma unroll
-      for (int ds = 0; ds < NDS; ++ds) {
-        const u32x4 qa = qlds[(qt * NDS + ds) * 64 + lane];
-        const u32x4 da = dolds[(qt * NDS + ds) * 64 + lane];
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kreg[kt][ds]), as_bf16x8(qa), st[kt], 0, 0, 0);
-          dpt[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vreg[kt][ds]), as_bf16x8(da), dpt[kt], 0, 0, 0);
-        }
-      }
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int e = 0; e < 16; e += 2) {
-          float v2[2];
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const bool live = (lm >> (16 * kt + e + u)) & 1u;
-            const float p = live ? __builtin_amdgcn_exp2f(fmaf(st[kt][e + u], sc_log2, -l2[qt])) : 0.f;
-            v2[u] = p * (dpt[kt][e + u] - dl[qt]);
-          }
-          dsw[qt][kt][e >> 1] = pack_bf16x2(v2[0], v2[1]);
-        }
-    }
-    const int jn = it + 1 < count ? block_id(it + 1) : j;
-    if (it + 1 < count) load_kv(jn);
+    // (scheduling barriers keep each refill where it is written: the
+    // compiler would otherwise sink it to the next use to save registers)
+    scores_s(0, st0, real, lm);
+    scores_s(1, st1, real, lm);
+    __builtin_amdgcn_sched_barrier(0);
+    load_k(jn);
+    __builtin_amdgcn_sched_barrier(0);
+    scores_dp(0, dpt);
+    grad_scores(st0, dpt, 0, dsw[0]);
+    scores_dp(1, dpt);
+    __builtin_amdgcn_sched_barrier(0);
+    load_v(jn);
+    __builtin_amdgcn_sched_barrier(0);
+    grad_scores(st1, dpt, 1, dsw[1]);
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
@@ -256,6 +320,9 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(const u32x4* __restrict__ q,
         acc[dt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kvreg[dt][ks]), as_bf16x8(bw), acc[dt][qt],
                                                               0, 0, 0);
       }
+    __builtin_amdgcn_sched_barrier(0);
+    load_kvv(jn);
+    __builtin_amdgcn_sched_barrier(0);
     j = jn;
   }
   bf16* ob = dq + (bh * g.n_pad + (long long)i * 64) * D;
@@ -313,6 +380,8 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(const u32x4* __restrict__ 
   constexpr int NARR = 2 * NDS;          // 1 KB chunks per array (= 4 * NDT)
   constexpr int NCH = 4 * NARR;          // chunks per query block: Q, dO (QK layout), Q, dO (V layout)
   constexpr int PER_WAVE = NCH / 4;      // chunk copies issued by each wave
+  // (plain order: the transposed lists differ widely in length, and a static
+  // split of contiguous key blocks over the XCDs leaves them unbalanced)
   const int j = blockIdx.x;
   const long long bh = blockIdx.y;
   const long long col = bh * g.nblk + j;
@@ -501,20 +570,20 @@ hipError_t launch_transpose_lut(const int32_t* lut, const int32_t* counts, int c
 
 hipError_t launch_bwd(const BwdArgs& a, const Geom& g, float scale, void* dq, void* dk, void* dv, hipStream_t s) {
   const float sc_log2 = scale * kLog2e;
-  // (an XCD-aware order as in the forward cut the traffic beyond L2 by a
-  // third but made neither kernel faster: both wait on their own chains)
-  dim3 grid(g.nblk, g.batch * g.heads);
+  const RowMap map = make_rowmap<kDqXcdGroup>(g.nblk, g.batch * g.heads);
+  const dim3 grid((unsigned)((long long)map.per_xcd * kXcds));   // dq, XCD-aware
+  const dim3 grid_kv(g.nblk, g.batch * g.heads);
   auto U = [](const void* p) { return static_cast<const u32x4*>(p); };
   if (g.d == 128) {
     bwd_dq_kernel<128><<<grid, 64, 0, s>>>(U(a.q), U(a.k), U(a.v_qk), U(a.k_v), U(a.do_qk), a.lse, a.delta, a.lut,
-                                           a.counts, a.cap, g, sc_log2, scale, static_cast<bf16*>(dq));
-    bwd_dkv_kernel<128><<<grid, 256, 0, s>>>(U(a.q), U(a.k), U(a.v_qk), U(a.q_v), U(a.do_qk), U(a.do_v), a.lse,
+                                           a.counts, a.cap, g, sc_log2, scale, static_cast<bf16*>(dq), map);
+    bwd_dkv_kernel<128><<<grid_kv, 256, 0, s>>>(U(a.q), U(a.k), U(a.v_qk), U(a.q_v), U(a.do_qk), U(a.do_v), a.lse,
                                              a.delta, a.lut_t, a.counts_t, a.cap_t, g, sc_log2, scale,
                                              static_cast<bf16*>(dk), static_cast<bf16*>(dv));
   } else {
     bwd_dq_kernel<64><<<grid, 64, 0, s>>>(U(a.q), U(a.k), U(a.v_qk), U(a.k_v), U(a.do_qk), a.lse, a.delta, a.lut,
-                                          a.counts, a.cap, g, sc_log2, scale, static_cast<bf16*>(dq));
-    bwd_dkv_kernel<64><<<grid, 256, 0, s>>>(U(a.q), U(a.k), U(a.v_qk), U(a.q_v), U(a.do_qk), U(a.do_v), a.lse,
+                                          a.counts, a.cap, g, sc_log2, scale, static_cast<bf16*>(dq), map);
+    bwd_dkv_kernel<64><<<grid_kv, 256, 0, s>>>(U(a.q), U(a.k), U(a.v_qk), U(a.q_v), U(a.do_qk), U(a.do_v), a.lse,
                                             a.delta, a.lut_t, a.counts_t, a.cap_t, g, sc_log2, scale,
                                             static_cast<bf16*>(dk), static_cast<bf16*>(dv));
   }

@@ -35,6 +35,7 @@
 // the products is at most 2^8, and the rare slow path replaces a max over 64
 // scores per block.
 #include "sa_launch.h"
+#include "sa_rowmap.h"
 
 #include <math.h>
 
@@ -44,7 +45,6 @@ namespace sa {
 
 namespace {
 
-constexpr int kXcds = 8;
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kSumLimit = 256.f;  // a lane's block sum above this triggers an exact-max rescale
 
@@ -57,44 +57,6 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   const f32x2 v = {a, b};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-}
-
-#ifndef SA_XCD_GROUP
-#define SA_XCD_GROUP 4
-#endif
-// Workgroups are dispatched round-robin over the 8 XCDs (XCD = w % 8).  The
-// XCDs form 8/G groups of G; group `grp` takes the contiguous row range
-// [grp*range, (grp+1)*range).  The range is cut into chunks of c = nblk/G
-// query blocks (one G-th of a head) dealt round-robin to the G XCDs of the
-// group, each XCD sweeping its chunks in order: G XCDs work on the same head
-// at once, each on neighbouring query blocks.
-struct RowMap {
-  int rows;     // batch * heads * nblk
-  int range;    // rows per XCD group
-  int chunk;    // rows per chunk
-  int per_xcd;  // workgroups per XCD
-};
-
-__host__ __device__ inline RowMap make_rowmap(int nblk, int heads_total) {
-  RowMap m;
-  m.rows = nblk * heads_total;
-  const int ranges = kXcds / SA_XCD_GROUP;
-  m.range = (m.rows + ranges - 1) / ranges;
-  m.chunk = (nblk + SA_XCD_GROUP - 1) / SA_XCD_GROUP;
-  const int chunks = (m.range + m.chunk - 1) / m.chunk;
-  m.per_xcd = (chunks + SA_XCD_GROUP - 1) / SA_XCD_GROUP * m.chunk;
-  return m;
-}
-
-// Row of workgroup w, or -1 if w has no row.
-__device__ __forceinline__ int row_of_workgroup(int w, const RowMap& m) {
-  const int x = w % kXcds, k = w / kXcds;
-  const int grp = x / SA_XCD_GROUP, sub = x % SA_XCD_GROUP;
-  const int q = k / m.chunk, o = k - q * m.chunk;
-  const long long in_range = ((long long)q * SA_XCD_GROUP + sub) * m.chunk + o;
-  const long long row = (long long)grp * m.range + in_range;
-  if (in_range >= m.range || row >= m.rows) return -1;
-  return (int)row;
 }
 
 // Division by a run-time constant d (1 <= d < 2^24) for n < 2^24 with one
