@@ -41,7 +41,8 @@ PEAK_FP64_TFLOPS = 78.6        # MI355X float64 (vector and matrix)
 # recorded with a hash of the sources it was measured on
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kernels_720p-hybrid95_hbm_traffic.txt")
 FWD_SOURCES = ("block_sparse_attention_hybrid_amd/csrc/fwd.hip", "block_sparse_attention_hybrid_amd/csrc/sa_device.h",
-               "block_sparse_attention_hybrid_amd/csrc/sa_launch.h", "block_sparse_attention_hybrid_amd/build.py")
+               "block_sparse_attention_hybrid_amd/csrc/sa_launch.h", "block_sparse_attention_hybrid_amd/csrc/sa_rowmap.h",
+               "block_sparse_attention_hybrid_amd/build.py")
 
 # name -> (synthetic workload id, k_frac, p, row budgets?)
 WORKLOADS = {
