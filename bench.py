@@ -228,16 +228,15 @@ def next_rows(path, reps=3):
     # backward over the same lists: operand layouts prepared untimed
     lay = {}
     for name, x, layout in (("q", path.q, sa.SA_LAYOUT_QK), ("k", path.k, sa.SA_LAYOUT_QK),
-                            ("v_qk", path.v, sa.SA_LAYOUT_QK), ("q_v", path.q, sa.SA_LAYOUT_V),
-                            ("k_v", path.k, sa.SA_LAYOUT_V), ("do_qk", path.o_grad, sa.SA_LAYOUT_QK),
-                            ("do_v", path.o_grad, sa.SA_LAYOUT_V)):
+                            ("v_qk", path.v, sa.SA_LAYOUT_QK), ("k_v", path.k, sa.SA_LAYOUT_V),
+                            ("do_qk", path.o_grad, sa.SA_LAYOUT_QK)):
         lay[name] = sa.reorder(x, g, layout)
     delta = torch.empty((B, H, path.n_pad), dtype=torch.float32, device=dev)
     lut_t = torch.empty((B, H, n, n), dtype=torch.int32, device=dev)
     counts_t = torch.empty((B, H, n), dtype=torch.int32, device=dev)
     ws = torch.empty(max(sa.sparse_attn_transpose_workspace_bytes(g), 256), dtype=torch.uint8, device=dev)
     dq, dk, dv = (torch.empty_like(path.oc) for _ in range(3))
-    args = sa.BwdArgs(*(lay[k_].data_ptr() for k_ in ("q", "k", "v_qk", "q_v", "k_v", "do_qk", "do_v")),
+    args = sa.BwdArgs(*(lay[k_].data_ptr() for k_ in ("q", "k", "v_qk", "k_v", "do_qk")),
                       path.lse_c.data_ptr(), delta.data_ptr(), path.lut.data_ptr(), path.counts.data_ptr(),
                       path.cap, lut_t.data_ptr(), counts_t.data_ptr(), n)
     t_delta = time_call(lambda: sa.sparse_attn_bwd_delta(path.oc, lay["do_qk"], delta, g), reps)

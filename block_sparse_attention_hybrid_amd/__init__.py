@@ -70,7 +70,7 @@ def make_geom(batch: int, heads: int, frames: int, height: int, width: int,
 
 class BwdArgs(ctypes.Structure):
     """sa_bwd_args of the C ABI."""
-    _fields_ = [(n, ctypes.c_void_p) for n in ("q", "k", "v_qk", "q_v", "k_v", "do_qk", "do_v", "lse", "delta",
+    _fields_ = [(n, ctypes.c_void_p) for n in ("q", "k", "v_qk", "k_v", "do_qk", "lse", "delta",
                                                "lut", "counts")] + [("cap", ctypes.c_int32)] + \
                [(n, ctypes.c_void_p) for n in ("lut_t", "counts_t")] + [("cap_t", ctypes.c_int32)]
 
@@ -534,14 +534,13 @@ def backward(q, k, v, do, oc, lse_c, lut, counts, g: Geom, scale: float = 0.0, s
     (dq, dk, dv) bf16; unreorder(x, None, g) brings each to token order."""
     QKL, VL = SA_LAYOUT_QK, SA_LAYOUT_V
     lay = {}
-    for name, x, layout in (("q", q, QKL), ("k", k, QKL), ("v_qk", v, QKL), ("q_v", q, VL), ("k_v", k, VL),
-                            ("do_qk", do, QKL), ("do_v", do, VL)):
+    for name, x, layout in (("q", q, QKL), ("k", k, QKL), ("v_qk", v, QKL), ("k_v", k, VL), ("do_qk", do, QKL)):
         lay[name] = reorder(x, g, layout, stream)
     _, _, n_pad = sparse_attn_geometry(g)
     delta = _empty((g.batch, g.heads, n_pad), torch.float32, q)
     sparse_attn_bwd_delta(oc, lay["do_qk"], delta, g, stream)
     lut_t, counts_t = transpose_lut(lut, counts, g, stream)
-    args = BwdArgs(*(lay[n].data_ptr() for n in ("q", "k", "v_qk", "q_v", "k_v", "do_qk", "do_v")),
+    args = BwdArgs(*(lay[n].data_ptr() for n in ("q", "k", "v_qk", "k_v", "do_qk")),
                    lse_c.data_ptr(), delta.data_ptr(), lut.data_ptr(), counts.data_ptr(), lut.shape[-1],
                    lut_t.data_ptr(), counts_t.data_ptr(), lut_t.shape[-1])
     dq, dk, dv = (_empty(tuple(oc.shape), torch.bfloat16, oc) for _ in range(3))

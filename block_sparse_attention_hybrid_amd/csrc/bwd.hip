@@ -10,10 +10,11 @@
 //   * dq: one wavefront per query block walks the block's kept list (as the
 //     forward does) and accumulates dQ^T = K^T dS^T in registers;
 //   * dkv: one workgroup per key block walks the transposed list (the query
-//     blocks that keep it, from sparse_attn_transpose_lut); each of its two
-//     waves owns 32 of the block's keys and accumulates dV^T = dO^T P and
-//     dK^T = Q^T dS in registers, reading the query block's operands from
-//     LDS, where the workgroup stages them once.
+//     blocks that keep it, from sparse_attn_transpose_lut); each of its four
+//     waves owns 32 of the block's keys and one query half and accumulates
+//     dV^T = dO^T P and dK^T = Q^T dS in registers, reading the query
+//     block's Q and dO from LDS, where the workgroup stages them once (in the
+//     QK layout only: the products over queries read them transposed).
 // Operand orders follow the forward kernel: every MFMA operand is one 16-byte
 // chunk per lane of a QK- or V-layout block (sa_layout.h), and the rows fed
 // to the first product are permuted (sigma) so that a lane's accumulator
@@ -357,20 +358,41 @@ __device__ __forceinline__ void copy_to_lds(const u32x4* src, u32x4* dst) {
 constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 constexpr int kLgkm0 = 0xC07F;
 
+// LDS transpose read (ds_read_b64_tr_b16), 8 bytes per lane.  Within each
+// group of 16 lanes, result lane i receives as its element e the (i % 4)-th
+// 16-bit value of the 8 bytes addressed by lane 4 e + i / 4 of the group (a
+// probe on gfx950 checked this mapping).  byte_off is wave-uniform plus this
+// lane's part; the host pass sees an empty body.
+__device__ __forceinline__ u32x2 read_tr16(const u32x4* lds_base, int byte_off) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+  typedef __attribute__((address_space(3))) char lds_char;
+  const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)((lds_char*)lds_base + byte_off));
+  return __builtin_bit_cast(u32x2, r);
+#else
+  (void)lds_base;
+  (void)byte_off;
+  return u32x2{0u, 0u};
+#endif
+}
+
 // One workgroup of 4 waves per key block j.  Wave w owns keys 32 (w % 2) ..
 // +31 and query half w / 2 of every query block in j's transposed list, and
 // accumulates dV^T = dO^T P and dK^T = Q^T dS for those keys over that half;
 // the two halves are added in LDS at the end (fixed order).  The query
-// block's operands (Q and dO in both layouts, 64 KB at d = 128) and its LSE
-// and D rows are copied into LDS with direct global-to-LDS loads, double
-// buffered: the copy of the next block is in flight while the current one is
-// used, with explicit vmcnt waits and barriers (no fence that would drain the
-// copy in flight).
+// block's Q and dO (QK layout, 32 KB at d = 128) and its LSE and D rows are
+// copied into LDS with direct global-to-LDS loads, double buffered: the copy
+// of the next block is in flight while the current one is used, with
+// explicit vmcnt waits and barriers (no fence that would drain the copy in
+// flight).  The second and third products contract over queries, so their A
+// operands (dO^T and Q^T: 8 consecutive queries of one dim per lane) are
+// formed from the same staged QK-layout data with LDS transpose reads, two
+// per operand; no second copy of Q and dO is needed.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_dkv_kernel(const u32x4* __restrict__ q, const u32x4* __restrict__ k,
-                                                      const u32x4* __restrict__ v_qk, const u32x4* __restrict__ q_v,
-                                                      const u32x4* __restrict__ do_qk,
-                                                      const u32x4* __restrict__ do_v, const float* __restrict__ lse,
+                                                      const u32x4* __restrict__ v_qk,
+                                                      const u32x4* __restrict__ do_qk, const float* __restrict__ lse,
                                                       const float* __restrict__ delta,
                                                       const int32_t* __restrict__ lut_t,
                                                       const int32_t* __restrict__ counts_t, int cap_t, Geom g,
@@ -378,7 +400,7 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(const u32x4* __restrict__ 
                                                       bf16* __restrict__ dv) {
   constexpr int NDS = D / 16, NDT = D / 32, BLK = 64 * D / 8;
   constexpr int NARR = 2 * NDS;          // 1 KB chunks per array (= 4 * NDT)
-  constexpr int NCH = 4 * NARR;          // chunks per query block: Q, dO (QK layout), Q, dO (V layout)
+  constexpr int NCH = 2 * NARR;          // chunks per query block: Q, dO (QK layout)
   constexpr int PER_WAVE = NCH / 4;      // chunk copies issued by each wave
   // (plain order: the transposed lists differ widely in length, and a static
   // split of contiguous key blocks over the XCDs leaves them unbalanced)
@@ -410,6 +432,25 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(const u32x4* __restrict__ 
   uint32_t key_bits = slot_token(g, j, 32 * kh + r) >= 0 ? 0xffffffffu : 0u;
   asm volatile("" : "+v"(key_bits));
 
+  // Transpose-read addresses.  The A operand of k-step ks (16 queries) and
+  // dim tile dt needs, in lane (r, hf), queries 16 ks + 8 hf .. +7 of dim
+  // 32 dt + r.  Read h (h = 0, 1) delivers queries 16 ks + 8 hf + 4 h .. +3:
+  // lane s = 16 gq + 4 e + m of group gq supplies the 8 bytes holding dims
+  // 32 dt + 16 (gq % 2) + 4 m .. +3 of query 16 ks + 8 (gq / 2) + 4 h + e.
+  // In the QK layout that is byte
+  //   ((ks / 2) NDS + 2 dt) 1024 + (16 (ks % 2) + 4 h) 16   (uniform)
+  //   + (gq % 2) 1024 + (32 (m / 2) + 8 (gq / 2) + e) 16 + 8 (m % 2)   (this lane)
+  const int tr_lane = [&] {
+    const int gq = lane >> 4, e = (lane >> 2) & 3, m = lane & 3;
+    return (gq & 1) * 1024 + (32 * (m >> 1) + 8 * (gq >> 1) + e) * 16 + 8 * (m & 1);
+  }();
+  auto tr_operand = [&](const u32x4* arr, int dt, int ks) {
+    const int base = ((ks >> 1) * NDS + 2 * dt) * 1024 + (16 * (ks & 1)) * 16 + tr_lane;
+    const u32x2 lo = read_tr16(arr, base);
+    const u32x2 hi = read_tr16(arr, base + 4 * 16);
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+  };
+
   f32x16 adk[NDT], adv[NDT];
 #pragma unroll
   for (int t = 0; t < NDT; ++t)
@@ -420,21 +461,21 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(const u32x4* __restrict__ 
   count = count < 0 ? 0 : (count > cap_t ? cap_t : count);
   const int32_t* list = lut_t + col * cap_t;
   auto valid = [&](int i) { return i >= 0 && i < g.nblk; };
-  // copy query block list[it] into buffer b: wave w copies array w (chunks
-  // [w NARR, (w + 1) NARR)); waves 0 and 1 also copy the LSE and D rows
-  static_assert(PER_WAVE == NARR, "one array per wave");
-  const u32x4* my_src = wave == 0 ? q : (wave == 1 ? do_qk : (wave == 2 ? q_v : do_v));
-  // (wave 0 also copies the LSE and D rows: one 16-byte-lane copy whose lanes
-  // 0-15 take the 64 LSE values and lanes 16-31 the 64 D values; lanes 32-63
-  // repeat them into a part of the slot that is not read)
+  // copy query block list[it] into buffer b: waves 0 and 1 copy the two
+  // halves of Q, waves 2 and 3 those of dO; wave 0 also copies the LSE and D
+  // rows (one 16-byte-lane copy whose lanes 0-15 take the 64 LSE values and
+  // lanes 16-31 the 64 D values; lanes 32-63 repeat them into a part of the
+  // slot that is not read)
+  static_assert(2 * PER_WAVE == NARR, "half an array per wave");
+  const u32x4* my_src = (wave < 2 ? q : do_qk) + (wave & 1) * PER_WAVE * 64;
   const u32x4* row_src = reinterpret_cast<const u32x4*>((lane & 16) ? delta : lse);
   auto issue = [&](int b, int it) {
     const int i0 = list[it];
     const int i = valid(i0) ? i0 : 0;
     const long long ob = head + (long long)i * BLK;
 #pragma unroll
-    for (int cc = 0; cc < NARR; ++cc)
-      copy_to_lds(my_src + ob + cc * 64 + lane, &stage[b][(wave * NARR + cc) * 64]);
+    for (int cc = 0; cc < PER_WAVE; ++cc)
+      copy_to_lds(my_src + ob + cc * 64 + lane, &stage[b][(wave * PER_WAVE + cc) * 64]);
     if (wave == 0)
       copy_to_lds(row_src + (bh * g.n_pad + (long long)i * kBlock) / 4 + (lane & 15), &stage[b][NCH * 64]);
   };
@@ -459,8 +500,6 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(const u32x4* __restrict__ 
     if (valid(list[it])) {
       const u32x4* qs = &stage[b][0];
       const u32x4* dos = &stage[b][NARR * 64];
-      const u32x4* qvs = &stage[b][2 * NARR * 64];
-      const u32x4* dovs = &stage[b][3 * NARR * 64];
       const float* lrow = reinterpret_cast<const float*>(&stage[b][NCH * 64]);
       f32x16 s, dp;
 #pragma unroll
@@ -496,10 +535,10 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(const u32x4* __restrict__ 
         const u32x4 bs = {dsw[4 * kk], dsw[4 * kk + 1], dsw[4 * kk + 2], dsw[4 * kk + 3]};
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-          adv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(dovs[(dt * 4 + ks) * 64 + lane]),
-                                                            as_bf16x8(bp), adv[dt], 0, 0, 0);
-          adk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qvs[(dt * 4 + ks) * 64 + lane]),
-                                                            as_bf16x8(bs), adk[dt], 0, 0, 0);
+          adv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(tr_operand(dos, dt, ks)), as_bf16x8(bp),
+                                                            adv[dt], 0, 0, 0);
+          adk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(tr_operand(qs, dt, ks)), as_bf16x8(bs),
+                                                            adk[dt], 0, 0, 0);
         }
       }
     }
@@ -577,13 +616,13 @@ hipError_t launch_bwd(const BwdArgs& a, const Geom& g, float scale, void* dq, vo
   if (g.d == 128) {
     bwd_dq_kernel<128><<<grid, 64, 0, s>>>(U(a.q), U(a.k), U(a.v_qk), U(a.k_v), U(a.do_qk), a.lse, a.delta, a.lut,
                                            a.counts, a.cap, g, sc_log2, scale, static_cast<bf16*>(dq), map);
-    bwd_dkv_kernel<128><<<grid_kv, 256, 0, s>>>(U(a.q), U(a.k), U(a.v_qk), U(a.q_v), U(a.do_qk), U(a.do_v), a.lse,
+    bwd_dkv_kernel<128><<<grid_kv, 256, 0, s>>>(U(a.q), U(a.k), U(a.v_qk), U(a.do_qk), a.lse,
                                              a.delta, a.lut_t, a.counts_t, a.cap_t, g, sc_log2, scale,
                                              static_cast<bf16*>(dk), static_cast<bf16*>(dv));
   } else {
     bwd_dq_kernel<64><<<grid, 64, 0, s>>>(U(a.q), U(a.k), U(a.v_qk), U(a.k_v), U(a.do_qk), a.lse, a.delta, a.lut,
                                           a.counts, a.cap, g, sc_log2, scale, static_cast<bf16*>(dq), map);
-    bwd_dkv_kernel<64><<<grid_kv, 256, 0, s>>>(U(a.q), U(a.k), U(a.v_qk), U(a.q_v), U(a.do_qk), U(a.do_v), a.lse,
+    bwd_dkv_kernel<64><<<grid_kv, 256, 0, s>>>(U(a.q), U(a.k), U(a.v_qk), U(a.do_qk), a.lse,
                                             a.delta, a.lut_t, a.counts_t, a.cap_t, g, sc_log2, scale,
                                             static_cast<bf16*>(dk), static_cast<bf16*>(dv));
   }

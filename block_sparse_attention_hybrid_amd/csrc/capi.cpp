@@ -296,10 +296,8 @@ int32_t sparse_attn_bwd(const sa_bwd_args* a, const sa_geom* g, float scale, voi
   SA_TRY(check_ptr(a->q, 16, "q"));
   SA_TRY(check_ptr(a->k, 16, "k"));
   SA_TRY(check_ptr(a->v_qk, 16, "v_qk"));
-  SA_TRY(check_ptr(a->q_v, 16, "q_v"));
   SA_TRY(check_ptr(a->k_v, 16, "k_v"));
   SA_TRY(check_ptr(a->do_qk, 16, "do_qk"));
-  SA_TRY(check_ptr(a->do_v, 16, "do_v"));
   SA_TRY(check_ptr(a->lse, 16, "lse"));
   SA_TRY(check_ptr(a->delta, 16, "delta"));
   SA_TRY(check_ptr(a->lut, 4, "lut"));
@@ -317,10 +315,8 @@ int32_t sparse_attn_bwd(const sa_bwd_args* a, const sa_geom* g, float scale, voi
   b.q = a->q;
   b.k = a->k;
   b.v_qk = a->v_qk;
-  b.q_v = a->q_v;
   b.k_v = a->k_v;
   b.do_qk = a->do_qk;
-  b.do_v = a->do_v;
   b.lse = a->lse;
   b.delta = a->delta;
   b.lut = a->lut;

@@ -37,7 +37,7 @@ hipError_t launch_router(const double* qr, const double* kr, double* scores, dou
                          int rt, int rh, int rw, hipStream_t s);
 // Operands of the backward pass (device pointers, see sparse_attn_bwd).
 struct BwdArgs {
-  const void *q, *k, *v_qk, *q_v, *k_v, *do_qk, *do_v;
+  const void *q, *k, *v_qk, *k_v, *do_qk;
   const float *lse, *delta;
   const int32_t *lut, *counts;
   int cap;

@@ -285,10 +285,8 @@ typedef struct sa_bwd_args {
   const void* q;         /* queries, SA_LAYOUT_QK */
   const void* k;         /* keys, SA_LAYOUT_QK */
   const void* v_qk;      /* values, SA_LAYOUT_QK */
-  const void* q_v;       /* queries, SA_LAYOUT_V */
   const void* k_v;       /* keys, SA_LAYOUT_V */
   const void* do_qk;     /* output gradient, SA_LAYOUT_QK */
-  const void* do_v;      /* output gradient, SA_LAYOUT_V */
   const float* lse;      /* [batch, heads, n_pad] natural-log LSE of sparse_attn_fwd (16-byte aligned) */
   const float* delta;    /* [batch, heads, n_pad] from sparse_attn_bwd_delta (16-byte aligned) */
   const int32_t* lut;    /* forward lists [batch, heads, nblk, cap] */
