@@ -157,19 +157,21 @@ __global__ __launch_bounds__(64) void fwd_kernel(const u32x4* __restrict__ qc,
     const uint64_t b = ballot(lt < rt && lh < rh && lw < rw);
     return ok ? b : 0ull;
   };
+  // both tiles are requested in the order the products consume them, so a
+  // product waits only for the chunks it uses
   auto load_k = [&](int j) {
     const u32x4* kb = kh + (long long)(valid_id(j) ? j : 0) * BLK;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int ds = 0; ds < NDS; ++ds)
 #pragma unroll
-      for (int ds = 0; ds < NDS; ++ds) kreg[kt][ds] = kb[(kt * NDS + ds) * 64 + kpos];
+      for (int kt = 0; kt < 2; ++kt) kreg[kt][ds] = kb[(kt * NDS + ds) * 64 + kpos];
   };
   auto load_v = [&](int j) {
     const u32x4* vb = vh + (long long)(valid_id(j) ? j : 0) * BLK;
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
+    for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) vreg[dt][ks] = vb[(dt * 4 + ks) * 64 + lane];
+      for (int dt = 0; dt < NDT; ++dt) vreg[dt][ks] = vb[(dt * 4 + ks) * 64 + lane];
   };
 
   auto lane_mask = [&](uint64_t real) -> uint32_t {
