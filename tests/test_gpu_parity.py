@@ -385,6 +385,56 @@ def test_backward_matches_oracle(case):
         assert err.max() <= 2e-2 * scale and err.mean() <= 2e-3 * scale, name
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_backward_variable_empty_and_invalid_lists(d):
+    """The backward on lists of every length from 0 to nblk (row budgets), so
+    some query blocks keep nothing and some key blocks are kept by no query
+    block (empty transposed lists), on a grid with partial cubes; a few list
+    entries are then replaced by out-of-range ids, which both passes skip.
+    Against the oracle on the same lists with those entries removed."""
+    say(f"[edge backward lists d={d}]")
+    wl, g, og, q, k, v = _small(d=d, heads=2, grid=(5, 7, 9))
+    n = og.nblk
+    rng = np.random.default_rng(23)
+    budget = rng.integers(0, n + 1, size=(1, 2, n)).astype(np.int32)
+    budget[0, 0, :3] = 0                       # a few query blocks keep nothing
+    qd, kd, vd = reorder3(q.to(DEV), k.to(DEV), v.to(DEV), g)
+    lut, counts = sa.build_mask(qd, kd, g, 0.0, 0.0, row_budget=torch.from_numpy(budget).to(DEV))
+    torch.cuda.synchronize()
+    lut_h, counts_h = lut.cpu().numpy().copy(), counts.cpu().numpy().copy()
+    # out-of-range ids in a few rows, inside their counts
+    clean_lut, clean_counts = lut_h.copy(), counts_h.copy()
+    for (h, i, bad) in ((0, 5, -1), (1, 7, n + 3), (1, 11, -7)):
+        c = counts_h[0, h, i]
+        if c == 0:
+            continue
+        lut_h[0, h, i, c // 2] = bad
+        kept = [x for x in clean_lut[0, h, i, :c] if x != clean_lut[0, h, i, c // 2]]
+        clean_lut[0, h, i, :c - 1] = kept
+        clean_counts[0, h, i] = c - 1
+    lut_d, counts_d = torch.from_numpy(lut_h).to(DEV), torch.from_numpy(counts_h).to(DEV)
+    oc, lse_c = sa.fwd(qd, kd, vd, lut_d, counts_d, g)
+    do = torch.from_numpy(rng.standard_normal(tuple(q.shape)).astype(np.float32)).to(torch.bfloat16)
+    dq, dk, dv = sa.backward(q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV), oc, lse_c, lut_d, counts_d, g)
+    torch.cuda.synchronize()
+    qc, kc, vc = (O.reorder(to64(t), og) for t in (q, k, v))
+    want = O.sparse_attention_backward(qc, kc, vc, O.reorder(to64(do), og), clean_lut, clean_counts, og)
+    for got, w, name in zip((dq, dk, dv), want, ("dq", "dk", "dv")):
+        got = to64(got)
+        err = np.abs(got - w)
+        scale = float(np.abs(w).max())
+        say(f"  {name}: max err {err.max():.2e} mean {err.mean():.2e} (max |grad| {scale:.2e})")
+        assert err.max() <= 2e-2 * scale and err.mean() <= 2e-3 * scale, name
+    # query blocks with no kept block get dQ = 0 exactly
+    for i in np.nonzero(clean_counts[0, 0] == 0)[0]:
+        assert not np.any(to64(dq)[0, 0, i * 64:(i + 1) * 64]), i
+    # key blocks no query block keeps get dK = dV = 0 exactly
+    for h in range(2):
+        used = set(int(x) for i in range(n) for x in clean_lut[0, h, i, :clean_counts[0, h, i]])
+        for j in sorted(set(range(n)) - used):
+            assert not np.any(to64(dk)[0, h, j * 64:(j + 1) * 64]) and not np.any(to64(dv)[0, h, j * 64:(j + 1) * 64])
+
+
 def test_mask_quality_matches_oracle(case):
     """Diagnostics: pooled mass (float64, tight), tau from the two LSEs and the
     relative L1 error from bf16 outputs (their rounding sets the bar)."""
