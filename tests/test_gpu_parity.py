@@ -435,6 +435,42 @@ def test_backward_variable_empty_and_invalid_lists(d):
             assert not np.any(to64(dk)[0, h, j * 64:(j + 1) * 64]) and not np.any(to64(dv)[0, h, j * 64:(j + 1) * 64])
 
 
+@pytest.mark.parametrize("d,grid", [(64, (1, 1, 1)), (128, (3, 2, 4)), (128, (4, 4, 4)), (64, (5, 4, 4)),
+                                    (128, (1, 1, 9))])
+def test_one_and_two_cube_grids(d, grid):
+    """The whole path and the backward where the grid holds one or two cubes
+    (one token; a lone partial cube; one full cube; a full and a partial cube;
+    a 1 x 1 x 9 line): every list is a single block or two."""
+    say(f"[edge tiny grid d={d} grid={grid}]")
+    wl, g, og, q, k, v = _small(d=d, grid=grid, heads=2, batch=1)
+    o, lse, lut, counts = sa.attention(q.to(DEV), k.to(DEV), v.to(DEV), g, 0.5, 0.5)
+    torch.cuda.synchronize()
+    qc, kc, vc = (O.reorder(to64(t), og) for t in (q, k, v))
+    ref = O.build_mask(qc, kc, og, 0.5, 0.5)
+    for b, h, i in zip(*np.nonzero(~ref.near_tie)):
+        c = ref.counts[b, h, i]
+        assert counts[b, h, i].item() == c
+        assert np.array_equal(lut[b, h, i, :c].cpu().numpy(), ref.lut[b, h, i, :c])
+    lut_h, counts_h = lut.cpu().numpy(), counts.cpu().numpy()
+    o_ref, lse_ref = O.sparse_attention(qc, kc, vc, lut_h, counts_h, og)
+    mx, mean = attn_errors(to64(o), O.unreorder(o_ref, og))
+    assert mx <= O_MAX_ABS and mean <= O_MEAN_ABS
+    lmx, _ = lse_errors(lse.cpu().double().numpy(), O.unreorder_rows(lse_ref, og))
+    assert lmx <= LSE_MAX_ABS
+    # backward on the same lists
+    qd, kd, vd = reorder3(q.to(DEV), k.to(DEV), v.to(DEV), g)
+    oc, lse_c = sa.fwd(qd, kd, vd, lut, counts, g)
+    rng = np.random.default_rng(5)
+    do = torch.from_numpy(rng.standard_normal(tuple(q.shape)).astype(np.float32)).to(torch.bfloat16)
+    dq, dk, dv = sa.backward(q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV), oc, lse_c, lut, counts, g)
+    torch.cuda.synchronize()
+    want = O.sparse_attention_backward(qc, kc, vc, O.reorder(to64(do), og), lut_h, counts_h, og)
+    for got, w, name in zip((dq, dk, dv), want, ("dq", "dk", "dv")):
+        err = np.abs(to64(got) - w)
+        scale = max(float(np.abs(w).max()), 1e-30)
+        assert err.max() <= 2e-2 * scale and err.mean() <= 2e-3 * scale, name
+
+
 def test_mask_quality_matches_oracle(case):
     """Diagnostics: pooled mass (float64, tight), tau from the two LSEs and the
     relative L1 error from bf16 outputs (their rounding sets the bar)."""
