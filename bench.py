@@ -70,9 +70,10 @@ def parse():
     ap.add_argument("--serial", action="store_true",
                     help="launch the stages from Python one after another instead of the library's "
                          "whole-path call")
-    ap.add_argument("--overlap", type=int, default=0, metavar="ROWS",
-                    help="overlap the mask of one chunk of ROWS batch*head rows with the forward of the "
-                         "previous chunk on a second stream (0: one stream)")
+    ap.add_argument("--overlap", type=int, default=-1, metavar="ROWS",
+                    help="two streams: -1 runs all rows as one chunk, the value reorder beside the scores "
+                         "and selection; ROWS > 0 also overlaps the mask of one chunk of ROWS batch*head "
+                         "rows with the forward of the previous chunk; 0 uses one stream")
     ap.add_argument("--no-next-rows", action="store_true",
                     help="skip timing the coarse-output and router kernels")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -137,11 +138,15 @@ class Path:
             fn()
 
     def step_call(self, overlap_rows):
-        """The whole path as one library call (sparse_attn_attention); with
-        overlap_rows > 0 the mask of a chunk of rows is built on the main stream
-        while the previous chunk's forward runs on an auxiliary stream."""
-        sa.sparse_attn_attention(self.buf, self.g, self.k_frac, self.p, 0.0, max(1, overlap_rows),
-                                 aux_stream=self.aux.cuda_stream if overlap_rows > 0 else None)
+        """The whole path as one library call (sparse_attn_attention).  With
+        overlap_rows != 0 it runs on two streams: the value reorder on the
+        auxiliary one beside the scores and selection, and with overlap_rows > 0
+        the mask of a chunk of rows on the main stream while the previous
+        chunk's forward runs on the auxiliary one."""
+        rows = self.g.batch * self.g.heads
+        chunk = rows if overlap_rows < 0 else max(1, overlap_rows)
+        sa.sparse_attn_attention(self.buf, self.g, self.k_frac, self.p, 0.0, chunk,
+                                 aux_stream=self.aux.cuda_stream if overlap_rows != 0 else None)
 
 
 def fwd_source_hash():
@@ -463,7 +468,9 @@ def main():
             "seq_len": path.n_real,
             "parallelism": "single GPU",
             "schedule": ("stages launched from Python on one stream" if args.serial else
-                         "sparse_attn_attention on one stream" if args.overlap <= 0 else
+                         "sparse_attn_attention on one stream" if args.overlap == 0 else
+                         "sparse_attn_attention on two streams: the value reorder beside the scores and "
+                         "selection" if args.overlap < 0 else
                          f"sparse_attn_attention, mask of chunk c+1 beside forward of chunk c "
                          f"({args.overlap} rows per chunk, two streams)"),
             "block_sparsity": round(1.0 - density, 5),

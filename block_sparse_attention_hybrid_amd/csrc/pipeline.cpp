@@ -5,7 +5,7 @@
 // re-indexing).  With an auxiliary stream the call splits the batch*heads rows
 // into chunks and runs the forward of chunk c on the auxiliary stream while
 // the main stream builds the mask of chunk c + 1; the value reorder also runs
-// on the auxiliary stream beside the query and key reorders.  The forward
+// on the auxiliary stream, beside the first chunk's scores and selection.  The forward
 // keeps only one wave per SIMD resident (its register budget), so the mask
 // kernels find room on the same compute units.  Events order the two streams;
 // the main stream waits for the auxiliary one at the end, so the caller sees
@@ -70,17 +70,19 @@ extern "C" int32_t sparse_attn_attention(const sa_path_buffers* b, const sa_geom
   const size_t head_r = (size_t)d.n_real * tok;
   const size_t nb = (size_t)d.nblk;
   hipError_t e;
-  if (two) {
-    if ((e = g_events.get(nchunks + 2)) != hipSuccess) return sa_hip_status(e, "event creation");
-    // the auxiliary stream starts after everything already queued on the main one
-    if ((e = hipEventRecord(g_events.ev[0], s)) != hipSuccess) return sa_hip_status(e, "event record");
-    if ((e = hipStreamWaitEvent(a, g_events.ev[0], 0)) != hipSuccess) return sa_hip_status(e, "stream wait");
-  }
-  if ((e = sa::launch_reorder(b->v, b->vc, 1, d, a)) != hipSuccess) return sa_hip_status(e, "reorder launch");
   if ((e = sa::launch_reorder_pool(b->q, b->qc, 0, b->qbar, d, s)) != hipSuccess)
     return sa_hip_status(e, "reorder_pool launch");
   if ((e = sa::launch_reorder_pool(b->k, b->kc, 0, b->kbar, d, s)) != hipSuccess)
     return sa_hip_status(e, "reorder_pool launch");
+  if (two) {
+    // the auxiliary stream starts once the query and key reorders are queued
+    // (so the value reorder, bound by HBM like them, runs beside the
+    // compute-bound scores and selection instead)
+    if ((e = g_events.get(nchunks + 2)) != hipSuccess) return sa_hip_status(e, "event creation");
+    if ((e = hipEventRecord(g_events.ev[0], s)) != hipSuccess) return sa_hip_status(e, "event record");
+    if ((e = hipStreamWaitEvent(a, g_events.ev[0], 0)) != hipSuccess) return sa_hip_status(e, "stream wait");
+  }
+  if ((e = sa::launch_reorder(b->v, b->vc, 1, d, a)) != hipSuccess) return sa_hip_status(e, "reorder launch");
   for (int c = 0; c < nchunks; ++c) {
     const int r0 = c * chunk, nr = (rows - r0) < chunk ? (rows - r0) : chunk;
     const sa::Geom gc = rows_of(d, nr);

@@ -489,10 +489,10 @@ def test_mask_quality_matches_oracle(case):
     assert np.all(r_err <= 1e-2 + 2e-2 * want_rel)
 
 
-@pytest.mark.parametrize("chunk", [1, 2])
+@pytest.mark.parametrize("chunk", [1, 2, 1 << 20])
 def test_whole_path_call_overlapped_equals_sequential(case, chunk):
-    """sparse_attn_attention on two streams (rows cut into chunks) gives the
-    same bytes as the step-by-step path on one stream."""
+    """sparse_attn_attention on two streams (rows cut into chunks, or all rows
+    in one chunk) gives the same bytes as the step-by-step path on one stream."""
     g = case["g"]
     o, lse, lut, counts = sa.attention(case["qd"], case["kd"], case["vd"], g, case["k_frac"], case["p"])
     buf, t = sa.path_buffers(case["qd"], case["kd"], case["vd"], g)
