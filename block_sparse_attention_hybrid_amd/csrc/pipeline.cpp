@@ -2,14 +2,12 @@
 //
 // Order of the work (the path of the summary pages: cube re-indexing and
 // pooling, pooled scores, hybrid selection, block-sparse forward, inverse
-// re-indexing).  With an auxiliary stream the call splits the batch*heads rows
-// into chunks and runs the forward of chunk c on the auxiliary stream while
-// the main stream builds the mask of chunk c + 1; the value reorder also runs
-// on the auxiliary stream, beside the first chunk's scores and selection.  The forward
-// keeps only one wave per SIMD resident (its register budget), so the mask
-// kernels find room on the same compute units.  Events order the two streams;
-// the main stream waits for the auxiliary one at the end, so the caller sees
-// completion on the stream it passed.
+// re-indexing).  With an auxiliary stream the value reorder runs there beside
+// the scores and selection (which run on the main stream), and the forward
+// runs there chunk by chunk while the main stream re-indexes the output of the
+// previous chunk.  Events order the two streams; the main stream's last work
+// waits for the last forward chunk, so the caller sees completion on the
+// stream it passed.
 #include "../../include/sparse_attn.h"
 
 #include <hip/hip_runtime.h>
@@ -75,31 +73,31 @@ extern "C" int32_t sparse_attn_attention(const sa_path_buffers* b, const sa_geom
   if ((e = sa::launch_reorder_pool(b->k, b->kc, 0, b->kbar, d, s)) != hipSuccess)
     return sa_hip_status(e, "reorder_pool launch");
   if (two) {
+    if ((e = g_events.get(nchunks + 2)) != hipSuccess) return sa_hip_status(e, "event creation");
     // the auxiliary stream starts once the query and key reorders are queued
     // (so the value reorder, bound by HBM like them, runs beside the
     // compute-bound scores and selection instead)
-    if ((e = g_events.get(nchunks + 2)) != hipSuccess) return sa_hip_status(e, "event creation");
     if ((e = hipEventRecord(g_events.ev[0], s)) != hipSuccess) return sa_hip_status(e, "event record");
     if ((e = hipStreamWaitEvent(a, g_events.ev[0], 0)) != hipSuccess) return sa_hip_status(e, "stream wait");
   }
   if ((e = sa::launch_reorder(b->v, b->vc, 1, d, a)) != hipSuccess) return sa_hip_status(e, "reorder launch");
+  // the mask of every row, on the main stream
+  if ((e = sa::launch_block_scores(b->qbar, b->kbar, b->scores, bscale, d, s)) != hipSuccess)
+    return sa_hip_status(e, "block score launch");
+  if ((e = sa::launch_select(b->scores, d, kcount, p, b->row_budget, b->lut, b->counts, b->cap, s)) != hipSuccess)
+    return sa_hip_status(e, "select launch");
+  if (two) {
+    if ((e = hipEventRecord(g_events.ev[1], s)) != hipSuccess) return sa_hip_status(e, "event record");
+    if ((e = hipStreamWaitEvent(a, g_events.ev[1], 0)) != hipSuccess) return sa_hip_status(e, "stream wait");
+  }
+  // the forward chunk by chunk on the auxiliary stream; each chunk's output is
+  // re-indexed on the main stream while the next chunk's forward runs (the
+  // re-indexing kernel is small enough to share the compute units with it)
   for (int c = 0; c < nchunks; ++c) {
     const int r0 = c * chunk, nr = (rows - r0) < chunk ? (rows - r0) : chunk;
     const sa::Geom gc = rows_of(d, nr);
-    const double* qbar = b->qbar + (size_t)r0 * nb * tok;
-    const double* kbar = b->kbar + (size_t)r0 * nb * tok;
-    double* scores = b->scores + (size_t)r0 * nb * nb;
-    int32_t* lut = b->lut + (size_t)r0 * nb * b->cap;
-    int32_t* counts = b->counts + (size_t)r0 * nb;
-    const int32_t* rb = b->row_budget ? b->row_budget + (size_t)r0 * nb : nullptr;
-    if ((e = sa::launch_block_scores(qbar, kbar, scores, bscale, gc, s)) != hipSuccess)
-      return sa_hip_status(e, "block score launch");
-    if ((e = sa::launch_select(scores, gc, kcount, p, rb, lut, counts, b->cap, s)) != hipSuccess)
-      return sa_hip_status(e, "select launch");
-    if (two) {
-      if ((e = hipEventRecord(g_events.ev[1 + c], s)) != hipSuccess) return sa_hip_status(e, "event record");
-      if ((e = hipStreamWaitEvent(a, g_events.ev[1 + c], 0)) != hipSuccess) return sa_hip_status(e, "stream wait");
-    }
+    const int32_t* lut = b->lut + (size_t)r0 * nb * b->cap;
+    const int32_t* counts = b->counts + (size_t)r0 * nb;
     const char* qc = static_cast<const char*>(b->qc) + (size_t)r0 * head_c * 2;
     const char* kc = static_cast<const char*>(b->kc) + (size_t)r0 * head_c * 2;
     const char* vc = static_cast<const char*>(b->vc) + (size_t)r0 * head_c * 2;
@@ -107,13 +105,14 @@ extern "C" int32_t sparse_attn_attention(const sa_path_buffers* b, const sa_geom
     float* lse_c = b->lse_c + (size_t)r0 * d.n_pad;
     if ((e = sa::launch_fwd(qc, kc, vc, lut, counts, b->cap, gc, sc, oc, lse_c, nullptr, a)) != hipSuccess)
       return sa_hip_status(e, "fwd launch");
-  }
-  (void)head_r;
-  if ((e = sa::launch_unreorder(b->oc, b->o, b->lse_c, b->lse, d, a)) != hipSuccess)
-    return sa_hip_status(e, "unreorder launch");
-  if (two) {
-    if ((e = hipEventRecord(g_events.ev[nchunks + 1], a)) != hipSuccess) return sa_hip_status(e, "event record");
-    if ((e = hipStreamWaitEvent(s, g_events.ev[nchunks + 1], 0)) != hipSuccess) return sa_hip_status(e, "stream wait");
+    if (two) {
+      if ((e = hipEventRecord(g_events.ev[2 + c], a)) != hipSuccess) return sa_hip_status(e, "event record");
+      if ((e = hipStreamWaitEvent(s, g_events.ev[2 + c], 0)) != hipSuccess) return sa_hip_status(e, "stream wait");
+    }
+    char* o = static_cast<char*>(b->o) + (size_t)r0 * head_r * 2;
+    float* lse = b->lse + (size_t)r0 * d.n_real;
+    if ((e = sa::launch_unreorder(oc, o, lse_c, lse, gc, s)) != hipSuccess)
+      return sa_hip_status(e, "unreorder launch");
   }
   return SA_OK;
 }

@@ -233,13 +233,14 @@ typedef struct sa_path_buffers {
  * unreorder -- the path of [SA2] Algorithm 1 and [VSA]'s two stages -- in one
  * call.  Block scores use 1/sqrt(head_dim); `scale` (<= 0: 1/sqrt(head_dim))
  * is the attention scale.  With aux_stream NULL (or equal to stream) the
- * kernels run in order on `stream`.  Otherwise the batch*heads rows are cut
- * into chunks of head_chunk rows: the mask of a chunk is built on `stream`
- * while the forward of the previous chunk runs on aux_stream (and the value
- * reorder runs on aux_stream beside the query/key reorders); `stream` waits
- * for aux_stream before the call returns, so completion is observed on
- * `stream`.  The results are the same either way.  Both streams must belong
- * to the current device. */
+ * kernels run in order on `stream`.  Otherwise two streams share the work:
+ * the value reorder runs on aux_stream beside the block scores and selection
+ * on `stream`; the forward then runs on aux_stream in chunks of head_chunk
+ * batch*heads rows (head_chunk >= batch*heads: one chunk), and `stream`
+ * re-indexes each chunk's output while the next chunk's forward runs.  The
+ * last work on `stream` waits for the last forward chunk, so completion is
+ * observed on `stream`.  The results are the same either way.  Both streams
+ * must belong to the current device. */
 int32_t sparse_attn_attention(const sa_path_buffers* buffers, const sa_geom* g,
                               double k_frac, double p, float scale,
                               int32_t head_chunk, void* stream,
