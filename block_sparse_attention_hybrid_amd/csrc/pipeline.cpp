@@ -2,10 +2,11 @@
 //
 // Order of the work (the path of the summary pages: cube re-indexing and
 // pooling, pooled scores, hybrid selection, block-sparse forward, inverse
-// re-indexing).  With an auxiliary stream the value reorder runs there beside
-// the scores and selection (which run on the main stream), and the forward
-// runs there chunk by chunk while the main stream re-indexes the output of the
-// previous chunk.  Events order the two streams; the main stream's last work
+// re-indexing).  With an auxiliary stream the rows are taken in two parts for
+// the first steps: the query/key re-indexing of part B and the value
+// re-indexing (bound by HBM) run there beside the mask of part A (bound by
+// compute) on the main stream.  The forward then runs there chunk by chunk
+// while the main stream re-indexes the output of the previous chunk.  Events order the two streams; the main stream's last work
 // waits for the last forward chunk, so the caller sees completion on the
 // stream it passed.
 #include "../../include/sparse_attn.h"
@@ -68,27 +69,50 @@ extern "C" int32_t sparse_attn_attention(const sa_path_buffers* b, const sa_geom
   const size_t head_r = (size_t)d.n_real * tok;
   const size_t nb = (size_t)d.nblk;
   hipError_t e;
-  if ((e = sa::launch_reorder_pool(b->q, b->qc, 0, b->qbar, d, s)) != hipSuccess)
-    return sa_hip_status(e, "reorder_pool launch");
-  if ((e = sa::launch_reorder_pool(b->k, b->kc, 0, b->kbar, d, s)) != hipSuccess)
-    return sa_hip_status(e, "reorder_pool launch");
-  if (two) {
-    if ((e = g_events.get(nchunks + 2)) != hipSuccess) return sa_hip_status(e, "event creation");
-    // the auxiliary stream starts once the query and key reorders are queued
-    // (so the value reorder, bound by HBM like them, runs beside the
-    // compute-bound scores and selection instead)
+  // the query and key reorders (with pooling) and the mask of rows [r0, r0 + nr)
+  auto qk_reorder = [&](int r0, int nr, hipStream_t st) -> hipError_t {
+    const sa::Geom gc = rows_of(d, nr);
+    hipError_t r = sa::launch_reorder_pool(static_cast<const char*>(b->q) + (size_t)r0 * head_r * 2,
+                                           static_cast<char*>(b->qc) + (size_t)r0 * head_c * 2, 0,
+                                           b->qbar + (size_t)r0 * nb * tok, gc, st);
+    if (r != hipSuccess) return r;
+    return sa::launch_reorder_pool(static_cast<const char*>(b->k) + (size_t)r0 * head_r * 2,
+                                   static_cast<char*>(b->kc) + (size_t)r0 * head_c * 2, 0,
+                                   b->kbar + (size_t)r0 * nb * tok, gc, st);
+  };
+  auto mask = [&](int r0, int nr, hipStream_t st) -> hipError_t {
+    const sa::Geom gc = rows_of(d, nr);
+    double* scores = b->scores + (size_t)r0 * nb * nb;
+    hipError_t r = sa::launch_block_scores(b->qbar + (size_t)r0 * nb * tok, b->kbar + (size_t)r0 * nb * tok,
+                                           scores, bscale, gc, st);
+    if (r != hipSuccess) return r;
+    return sa::launch_select(scores, gc, kcount, p, b->row_budget ? b->row_budget + (size_t)r0 * nb : nullptr,
+                             b->lut + (size_t)r0 * nb * b->cap, b->counts + (size_t)r0 * nb, b->cap, st);
+  };
+  if (!two) {
+    if ((e = qk_reorder(0, rows, s)) != hipSuccess) return sa_hip_status(e, "reorder_pool launch");
+    if ((e = sa::launch_reorder(b->v, b->vc, 1, d, s)) != hipSuccess) return sa_hip_status(e, "reorder launch");
+    if ((e = mask(0, rows, s)) != hipSuccess) return sa_hip_status(e, "mask launch");
+  } else {
+    // Rows are taken in two parts.  The main stream re-indexes part A's
+    // queries and keys and builds its mask while the auxiliary stream
+    // re-indexes part B's; the main stream then builds part B's mask while the
+    // auxiliary stream re-indexes the values (the re-indexing is bound by HBM,
+    // the scores and selection by compute).
+    const int part = rows > 1 ? rows / 2 : rows;
+    if ((e = g_events.get(nchunks + 3)) != hipSuccess) return sa_hip_status(e, "event creation");
+    if ((e = qk_reorder(0, part, s)) != hipSuccess) return sa_hip_status(e, "reorder_pool launch");
     if ((e = hipEventRecord(g_events.ev[0], s)) != hipSuccess) return sa_hip_status(e, "event record");
     if ((e = hipStreamWaitEvent(a, g_events.ev[0], 0)) != hipSuccess) return sa_hip_status(e, "stream wait");
-  }
-  if ((e = sa::launch_reorder(b->v, b->vc, 1, d, a)) != hipSuccess) return sa_hip_status(e, "reorder launch");
-  // the mask of every row, on the main stream
-  if ((e = sa::launch_block_scores(b->qbar, b->kbar, b->scores, bscale, d, s)) != hipSuccess)
-    return sa_hip_status(e, "block score launch");
-  if ((e = sa::launch_select(b->scores, d, kcount, p, b->row_budget, b->lut, b->counts, b->cap, s)) != hipSuccess)
-    return sa_hip_status(e, "select launch");
-  if (two) {
-    if ((e = hipEventRecord(g_events.ev[1], s)) != hipSuccess) return sa_hip_status(e, "event record");
-    if ((e = hipStreamWaitEvent(a, g_events.ev[1], 0)) != hipSuccess) return sa_hip_status(e, "stream wait");
+    if (rows > part && (e = qk_reorder(part, rows - part, a)) != hipSuccess)
+      return sa_hip_status(e, "reorder_pool launch");
+    if ((e = hipEventRecord(g_events.ev[1], a)) != hipSuccess) return sa_hip_status(e, "event record");
+    if ((e = sa::launch_reorder(b->v, b->vc, 1, d, a)) != hipSuccess) return sa_hip_status(e, "reorder launch");
+    if ((e = mask(0, part, s)) != hipSuccess) return sa_hip_status(e, "mask launch");
+    if ((e = hipStreamWaitEvent(s, g_events.ev[1], 0)) != hipSuccess) return sa_hip_status(e, "stream wait");
+    if (rows > part && (e = mask(part, rows - part, s)) != hipSuccess) return sa_hip_status(e, "mask launch");
+    if ((e = hipEventRecord(g_events.ev[2], s)) != hipSuccess) return sa_hip_status(e, "event record");
+    if ((e = hipStreamWaitEvent(a, g_events.ev[2], 0)) != hipSuccess) return sa_hip_status(e, "stream wait");
   }
   // the forward chunk by chunk on the auxiliary stream; each chunk's output is
   // re-indexed on the main stream while the next chunk's forward runs (the
@@ -106,8 +130,8 @@ extern "C" int32_t sparse_attn_attention(const sa_path_buffers* b, const sa_geom
     if ((e = sa::launch_fwd(qc, kc, vc, lut, counts, b->cap, gc, sc, oc, lse_c, nullptr, a)) != hipSuccess)
       return sa_hip_status(e, "fwd launch");
     if (two) {
-      if ((e = hipEventRecord(g_events.ev[2 + c], a)) != hipSuccess) return sa_hip_status(e, "event record");
-      if ((e = hipStreamWaitEvent(s, g_events.ev[2 + c], 0)) != hipSuccess) return sa_hip_status(e, "stream wait");
+      if ((e = hipEventRecord(g_events.ev[3 + c], a)) != hipSuccess) return sa_hip_status(e, "event record");
+      if ((e = hipStreamWaitEvent(s, g_events.ev[3 + c], 0)) != hipSuccess) return sa_hip_status(e, "stream wait");
     }
     char* o = static_cast<char*>(b->o) + (size_t)r0 * head_r * 2;
     float* lse = b->lse + (size_t)r0 * d.n_real;

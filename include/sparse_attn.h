@@ -234,8 +234,10 @@ typedef struct sa_path_buffers {
  * call.  Block scores use 1/sqrt(head_dim); `scale` (<= 0: 1/sqrt(head_dim))
  * is the attention scale.  With aux_stream NULL (or equal to stream) the
  * kernels run in order on `stream`.  Otherwise two streams share the work:
- * the value reorder runs on aux_stream beside the block scores and selection
- * on `stream`; the forward then runs on aux_stream in chunks of head_chunk
+ * `stream` re-indexes the queries and keys of the first half of the
+ * batch*heads rows and builds their mask while aux_stream re-indexes the
+ * second half's and then the values, and `stream` then builds the second
+ * half's mask; the forward then runs on aux_stream in chunks of head_chunk
  * batch*heads rows (head_chunk >= batch*heads: one chunk), and `stream`
  * re-indexes each chunk's output while the next chunk's forward runs.  The
  * last work on `stream` waits for the last forward chunk, so completion is
