@@ -71,9 +71,9 @@ def parse():
                     help="launch the stages from Python one after another instead of the library's "
                          "whole-path call")
     ap.add_argument("--overlap", type=int, default=-1, metavar="ROWS",
-                    help="two streams: -1 runs all rows as one chunk, the value reorder beside the scores "
-                         "and selection; ROWS > 0 also overlaps the mask of one chunk of ROWS batch*head "
-                         "rows with the forward of the previous chunk; 0 uses one stream")
+                    help="two streams: re-indexing beside the scores and selection, and the forward in "
+                         "chunks of ROWS batch*head rows with each chunk's output re-indexed beside the "
+                         "next (-1: one chunk); 0 uses one stream")
     ap.add_argument("--no-next-rows", action="store_true",
                     help="skip timing the coarse-output and router kernels")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -139,10 +139,9 @@ class Path:
 
     def step_call(self, overlap_rows):
         """The whole path as one library call (sparse_attn_attention).  With
-        overlap_rows != 0 it runs on two streams: the value reorder on the
-        auxiliary one beside the scores and selection, and with overlap_rows > 0
-        the mask of a chunk of rows on the main stream while the previous
-        chunk's forward runs on the auxiliary one."""
+        overlap_rows != 0 it runs on two streams: re-indexing beside the scores
+        and selection, then the forward in chunks of overlap_rows rows (all rows
+        when negative) with each chunk's output re-indexed beside the next."""
         rows = self.g.batch * self.g.heads
         chunk = rows if overlap_rows < 0 else max(1, overlap_rows)
         sa.sparse_attn_attention(self.buf, self.g, self.k_frac, self.p, 0.0, chunk,
@@ -469,8 +468,8 @@ def main():
             "parallelism": "single GPU",
             "schedule": ("stages launched from Python on one stream" if args.serial else
                          "sparse_attn_attention on one stream" if args.overlap == 0 else
-                         "sparse_attn_attention on two streams: the value reorder beside the scores and "
-                         "selection" if args.overlap < 0 else
+                         "sparse_attn_attention on two streams: re-indexing of one half of the heads "
+                         "(and of the values) beside the scores and selection of the other" if args.overlap < 0 else
                          f"sparse_attn_attention, mask of chunk c+1 beside forward of chunk c "
                          f"({args.overlap} rows per chunk, two streams)"),
             "block_sparsity": round(1.0 - density, 5),
