@@ -116,7 +116,7 @@ class Path:
         self.buf = sa.PathBuffers(ptr(self.q), ptr(self.k), ptr(self.v), ptr(self.qc), ptr(self.kc), ptr(self.vc),
                                   ptr(self.qbar), ptr(self.kbar), ptr(self.scores), ptr(self.lut),
                                   ptr(self.counts), self.cap, None if self.rb is None else ptr(self.rb),
-                                  ptr(self.oc), ptr(self.lse_c), ptr(self.o), ptr(self.lse))
+                                  None, None, ptr(self.o), ptr(self.lse))   # token order straight from the forward
         self.aux = torch.cuda.Stream(device=dev)
 
     def stages(self):

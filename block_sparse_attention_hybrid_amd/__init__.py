@@ -585,24 +585,26 @@ def mask_recall(qc, kc, vc, lut, counts, scores, g: Geom, stream=None):
     return mass, recall
 
 
-def path_buffers(q, k, v, g: Geom, row_budget=None):
+def path_buffers(q, k, v, g: Geom, row_budget=None, slot_major: bool = True):
     """Allocate every buffer of sparse_attn_attention for row-major q, k, v.
-    Returns (PathBuffers, dict of the tensors, which must outlive the call)."""
+    slot_major=False leaves oc and lse_c NULL (the forward then writes token
+    order directly).  Returns (PathBuffers, dict of the tensors, which must
+    outlive the call)."""
     nblk, n_real, n_pad = sparse_attn_geometry(g)
     B, H, d = g.batch, g.heads, g.head_dim
     t = dict(q=q, k=k, v=v)
-    for n in ("qc", "kc", "vc", "oc"):
+    for n in ("qc", "kc", "vc") + (("oc",) if slot_major else ()):
         t[n] = _empty((B, H, n_pad, d), torch.bfloat16, q)
     t["qbar"], t["kbar"] = (_empty((B, H, nblk, d), torch.float64, q) for _ in range(2))
     t["scores"] = _empty((B, H, nblk, nblk), torch.float64, q)
     t["lut"] = _empty((B, H, nblk, nblk), torch.int32, q)
     t["counts"] = _empty((B, H, nblk), torch.int32, q)
-    t["lse_c"] = _empty((B, H, n_pad), torch.float32, q)
+    t["lse_c"] = _empty((B, H, n_pad), torch.float32, q) if slot_major else None
     t["o"] = _empty((B, H, n_real, d), torch.bfloat16, q)
     t["lse"] = _empty((B, H, n_real), torch.float32, q)
     for n in ("q", "k", "v"):
         _ptr(t[n], torch.bfloat16, n)
-    ptr = lambda n: t[n].data_ptr()
+    ptr = lambda n: None if t.get(n) is None else t[n].data_ptr()
     buf = PathBuffers(ptr("q"), ptr("k"), ptr("v"), ptr("qc"), ptr("kc"), ptr("vc"), ptr("qbar"), ptr("kbar"),
                       ptr("scores"), ptr("lut"), ptr("counts"), nblk,
                       None if row_budget is None else row_budget.data_ptr(),

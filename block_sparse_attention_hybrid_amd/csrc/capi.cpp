@@ -373,8 +373,13 @@ int32_t sa_validate_path(const sa_path_buffers* b, const sa_geom* g, double k_fr
   SA_TRY(check_ptr(b->qbar, 8, "qbar"));
   SA_TRY(check_ptr(b->kbar, 8, "kbar"));
   SA_TRY(check_ptr(b->scores, 8, "scores"));
-  SA_TRY(check_ptr(b->oc, 16, "oc"));
-  SA_TRY(check_ptr(b->lse_c, 4, "lse_c"));
+  // oc and lse_c: both given (slot-major O and LSE are written too) or both NULL
+  if ((b->oc == nullptr) != (b->lse_c == nullptr))
+    return fail(SA_ERR_INVALID_ARG, "oc and lse_c must both be given or both be NULL");
+  if (b->oc != nullptr) {
+    SA_TRY(check_ptr(b->oc, 16, "oc"));
+    SA_TRY(check_ptr(b->lse_c, 4, "lse_c"));
+  }
   SA_TRY(check_ptr(b->o, 16, "o"));
   SA_TRY(check_ptr(b->lse, 4, "lse"));
   if (b->q == b->qc || b->k == b->kc || b->v == b->vc) return fail(SA_ERR_INVALID_ARG, "inputs and outputs overlap");

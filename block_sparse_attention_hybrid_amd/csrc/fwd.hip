@@ -81,7 +81,10 @@ struct CubeDiv {
   FastDiv w, h;
 };
 
-template <int D>
+// TOK = false: O and LSE slot-major (oc [.., n_pad, D], lse_c [.., n_pad]);
+// TOK = true: straight to token order (o [.., N, D], lse [.., N]), pad slots
+// not written -- the inverse re-indexing fused into the epilogue.
+template <int D, bool TOK>
 __global__ __launch_bounds__(64) void fwd_kernel(const u32x4* __restrict__ qc,
                                                  const u32x4* __restrict__ kc,
                                                  const u32x4* __restrict__ vc,
@@ -350,13 +353,31 @@ __global__ __launch_bounds__(64) void fwd_kernel(const u32x4* __restrict__ qc,
   const uint64_t qreal = real_mask(i);
   bf16* ob = oc + (bh * g.n_pad + (long long)i * 64) * D;
   float* lb = lse_c + bh * g.n_pad + (long long)i * 64;
+  // token order: cube coordinates of this query block (one division each on the scalar unit)
+  int ct0 = 0, ch0 = 0, cw0 = 0;
+  if (TOK) {
+    const uint32_t rr = fdiv((uint32_t)i, cd.w);
+    cw0 = (i - (int)rr * g.nw) * g.cw;
+    const int bt = (int)fdiv(rr, cd.h);
+    ch0 = ((int)rr - bt * g.nh) * g.ch;
+    ct0 = bt * g.ct;
+  }
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
     const float lt = l[qt] + __shfl_xor(l[qt], 32, 64);
     const int q = 32 * qt + r;
-    const bool live = ((qreal >> q) & 1ull) && lt > 0.f;
+    const bool real_q = (qreal >> q) & 1ull;
+    const bool live = real_q && lt > 0.f;
     const float inv = live ? 1.f / lt : 0.f;
     bf16* orow = ob + (long long)q * D;
+    long long tok = 0;
+    if (TOK) {
+      int tt, hh, ww;
+      slot_offsets(g, q, tt, hh, ww);
+      tok = ((long long)(ct0 + tt) * g.height + (ch0 + hh)) * g.width + (cw0 + ww);
+      orow = oc + (bh * g.n_real + tok) * D;
+      if (!real_q) continue;   // pad slots have no token row
+    }
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -365,7 +386,13 @@ __global__ __launch_bounds__(64) void fwd_kernel(const u32x4* __restrict__ qc,
                          pack_bf16x2(acc[dt][qt][4 * a + 2] * inv, acc[dt][qt][4 * a + 3] * inv)};
         *reinterpret_cast<u32x2*>(orow + 32 * dt + 8 * a + 4 * hf) = v;
       }
-    if (hf == 0) lb[q] = live ? (m[qt] + __log2f(lt)) * kLn2 : -INFINITY;
+    const float lse_q = live ? (m[qt] + __log2f(lt)) * kLn2 : -INFINITY;
+    if (hf == 0) {
+      if (TOK)
+        lse_c[bh * g.n_real + tok] = lse_q;
+      else
+        lb[q] = lse_q;
+    }
   }
 }
 
@@ -373,9 +400,10 @@ __global__ __launch_bounds__(64) void fwd_kernel(const u32x4* __restrict__ qc,
 
 size_t fwd_workspace_bytes(const Geom&) { return 0; }
 
-hipError_t launch_fwd(const void* qc, const void* kc, const void* vc, const int32_t* lut,
-                      const int32_t* counts, int cap, const Geom& g, float scale, void* oc,
-                      float* lse_c, void*, hipStream_t s, int qg_shift) {
+template <bool TOK>
+static hipError_t launch_fwd_any(const void* qc, const void* kc, const void* vc, const int32_t* lut,
+                                 const int32_t* counts, int cap, const Geom& g, float scale, void* out,
+                                 float* lse_out, hipStream_t s, int qg_shift) {
   const RowMap map = make_rowmap(g.nblk, g.batch * g.heads);
   const CubeDiv cd = {make_fastdiv((uint32_t)g.nw), make_fastdiv((uint32_t)g.nh)};
   const float sc_log2 = scale * 1.4426950408889634f;
@@ -384,12 +412,24 @@ hipError_t launch_fwd(const void* qc, const void* kc, const void* vc, const int3
   const u32x4* k = static_cast<const u32x4*>(kc);
   const u32x4* v = static_cast<const u32x4*>(vc);
   if (g.d == 128)
-    fwd_kernel<128><<<grid, 64, 0, s>>>(q, k, v, lut, counts, cap, g, sc_log2, static_cast<bf16*>(oc), lse_c,
-                                        map, cd, qg_shift);
+    fwd_kernel<128, TOK><<<grid, 64, 0, s>>>(q, k, v, lut, counts, cap, g, sc_log2, static_cast<bf16*>(out),
+                                             lse_out, map, cd, qg_shift);
   else
-    fwd_kernel<64><<<grid, 64, 0, s>>>(q, k, v, lut, counts, cap, g, sc_log2, static_cast<bf16*>(oc), lse_c,
-                                       map, cd, qg_shift);
+    fwd_kernel<64, TOK><<<grid, 64, 0, s>>>(q, k, v, lut, counts, cap, g, sc_log2, static_cast<bf16*>(out),
+                                            lse_out, map, cd, qg_shift);
   return hipGetLastError();
+}
+
+hipError_t launch_fwd(const void* qc, const void* kc, const void* vc, const int32_t* lut,
+                      const int32_t* counts, int cap, const Geom& g, float scale, void* oc,
+                      float* lse_c, void*, hipStream_t s, int qg_shift) {
+  return launch_fwd_any<false>(qc, kc, vc, lut, counts, cap, g, scale, oc, lse_c, s, qg_shift);
+}
+
+hipError_t launch_fwd_tokens(const void* qc, const void* kc, const void* vc, const int32_t* lut,
+                             const int32_t* counts, int cap, const Geom& g, float scale, void* o,
+                             float* lse, hipStream_t s) {
+  return launch_fwd_any<true>(qc, kc, vc, lut, counts, cap, g, scale, o, lse, s, 0);
 }
 
 }  // namespace sa

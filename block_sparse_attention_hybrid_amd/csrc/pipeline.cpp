@@ -6,7 +6,9 @@
 // the first steps: the query/key re-indexing of part B and the value
 // re-indexing (bound by HBM) run there beside the mask of part A (bound by
 // compute) on the main stream.  The forward then runs there chunk by chunk
-// while the main stream re-indexes the output of the previous chunk.  Events order the two streams; the main stream's last work
+// while the main stream re-indexes the output of the previous chunk; when the
+// caller wants no slot-major copy of O and LSE, the forward writes token order
+// itself and there is nothing left to re-index.  Events order the two streams; the main stream's last work
 // waits for the last forward chunk, so the caller sees completion on the
 // stream it passed.
 #include "../../include/sparse_attn.h"
@@ -125,6 +127,19 @@ extern "C" int32_t sparse_attn_attention(const sa_path_buffers* b, const sa_geom
     const char* qc = static_cast<const char*>(b->qc) + (size_t)r0 * head_c * 2;
     const char* kc = static_cast<const char*>(b->kc) + (size_t)r0 * head_c * 2;
     const char* vc = static_cast<const char*>(b->vc) + (size_t)r0 * head_c * 2;
+    char* o = static_cast<char*>(b->o) + (size_t)r0 * head_r * 2;
+    float* lse = b->lse + (size_t)r0 * d.n_real;
+    if (b->oc == nullptr) {
+      // no slot-major copy wanted: the forward writes token order itself
+      if ((e = sa::launch_fwd_tokens(qc, kc, vc, lut, counts, b->cap, gc, sc, o, lse, a)) != hipSuccess)
+        return sa_hip_status(e, "fwd launch");
+      if (two) {
+        if ((e = hipEventRecord(g_events.ev[3 + c], a)) != hipSuccess) return sa_hip_status(e, "event record");
+        if ((e = hipStreamWaitEvent(s, g_events.ev[3 + c], 0)) != hipSuccess)
+          return sa_hip_status(e, "stream wait");
+      }
+      continue;
+    }
     char* oc = static_cast<char*>(b->oc) + (size_t)r0 * head_c * 2;
     float* lse_c = b->lse_c + (size_t)r0 * d.n_pad;
     if ((e = sa::launch_fwd(qc, kc, vc, lut, counts, b->cap, gc, sc, oc, lse_c, nullptr, a)) != hipSuccess)
@@ -133,8 +148,6 @@ extern "C" int32_t sparse_attn_attention(const sa_path_buffers* b, const sa_geom
       if ((e = hipEventRecord(g_events.ev[3 + c], a)) != hipSuccess) return sa_hip_status(e, "event record");
       if ((e = hipStreamWaitEvent(s, g_events.ev[3 + c], 0)) != hipSuccess) return sa_hip_status(e, "stream wait");
     }
-    char* o = static_cast<char*>(b->o) + (size_t)r0 * head_r * 2;
-    float* lse = b->lse + (size_t)r0 * d.n_real;
     if ((e = sa::launch_unreorder(oc, o, lse_c, lse, gc, s)) != hipSuccess)
       return sa_hip_status(e, "unreorder launch");
   }

@@ -31,6 +31,11 @@ hipError_t launch_select(const double* scores, const Geom& g, int kc_default, do
 hipError_t launch_fwd(const void* qc, const void* kc, const void* vc, const int32_t* lut,
                       const int32_t* counts, int cap, const Geom& g, float scale, void* oc,
                       float* lse_c, void* workspace, hipStream_t s, int qg_shift = 0);
+// the forward with the inverse re-indexing fused: O [.., N, d] and LSE [.., N]
+// in token order (pad slots not written)
+hipError_t launch_fwd_tokens(const void* qc, const void* kc, const void* vc, const int32_t* lut,
+                             const int32_t* counts, int cap, const Geom& g, float scale, void* o,
+                             float* lse, hipStream_t s);
 size_t fwd_workspace_bytes(const Geom& g);
 hipError_t launch_router_pool(const void* xc, double* xr, const Geom& g, int rt, int rh, int rw, hipStream_t s);
 hipError_t launch_router(const double* qr, const double* kr, double* scores, double scale, const Geom& g,

@@ -223,8 +223,11 @@ typedef struct sa_path_buffers {
   int32_t* counts;      /* [batch, heads, nblk] */
   int32_t cap;
   const int32_t* row_budget; /* [batch, heads, nblk] or NULL, as for sparse_attn_select */
-  void* oc;             /* [batch, heads, n_pad, head_dim] bf16 slot-major output (written) */
-  float* lse_c;         /* [batch, heads, n_pad] (written) */
+  void* oc;             /* [batch, heads, n_pad, head_dim] bf16 slot-major output (written), or
+                           NULL together with lse_c: the forward then writes o and lse in token
+                           order directly and the slot-major copy (which sparse_attn_bwd_delta
+                           and sparse_attn_bwd take) is not produced */
+  float* lse_c;         /* [batch, heads, n_pad] (written), or NULL with oc */
   void* o;              /* [batch, heads, N, head_dim] bf16 output in token order (written) */
   float* lse;           /* [batch, heads, N] (written) */
 } sa_path_buffers;

@@ -212,3 +212,32 @@ def test_ideal_mass_and_recall_argument_rules():
     assert lib.sparse_attn_mask_recall(FAKE, FAKE, FAKE, 0, B, FAKE, FAKE, need, None) == sa.SA_ERR_INVALID_ARG
     assert lib.sparse_attn_mask_recall(FAKE, FAKE, FAKE, 16, B, FAKE_MISALIGNED, FAKE, need,
                                        None) == sa.SA_ERR_INVALID_ARG
+
+
+def test_whole_path_argument_rules():
+    """sparse_attn_attention: every operand buffer is required except the
+    row budgets and the slot-major outputs oc / lse_c, which go together."""
+    g = geom()
+    lib = sa.lib()
+    B = ctypes.byref(g)
+    F = 0x100000
+
+    def buffers(**kw):
+        names = ("q", "k", "v", "qc", "kc", "vc", "qbar", "kbar", "scores", "lut", "counts", "oc", "lse_c",
+                 "o", "lse")
+        vals = {n: F + 0x10000 * x for x, n in enumerate(names)}     # distinct, aligned, never dereferenced
+        vals.update(cap=16, row_budget=None)
+        vals.update(kw)
+        return sa.PathBuffers(*(vals[n] for n, _ in sa.PathBuffers._fields_))
+
+    def call(buf, k_frac=0.25, p=0.5, chunk=1):
+        return lib.sparse_attn_attention(ctypes.byref(buf), B, k_frac, p, 0.0, chunk, None, None)
+
+    assert call(buffers(q=None)) == sa.SA_ERR_INVALID_ARG
+    assert call(buffers(o=None)) == sa.SA_ERR_INVALID_ARG
+    assert call(buffers(oc=None)) == sa.SA_ERR_INVALID_ARG          # oc without lse_c
+    assert "oc and lse_c" in sa.sparse_attn_last_error()
+    assert call(buffers(lse_c=None)) == sa.SA_ERR_INVALID_ARG
+    assert call(buffers(cap=15)) == sa.SA_ERR_CAPACITY               # Top-p may keep all 16 blocks
+    assert call(buffers(), k_frac=float("nan")) == sa.SA_ERR_INVALID_ARG
+    assert call(buffers(), chunk=0) == sa.SA_ERR_INVALID_ARG

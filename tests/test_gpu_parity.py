@@ -510,6 +510,12 @@ def test_whole_path_call_overlapped_equals_sequential(case, chunk):
     sa.sparse_attn_attention(buf2, g, case["k_frac"], case["p"], 0.0, chunk)
     torch.cuda.synchronize()
     assert torch.equal(t2["o"], o) and torch.equal(t2["lse"], lse)
+    # no slot-major copy: the forward writes token order itself (both stream modes)
+    for aux_s in (None, aux.cuda_stream):
+        buf3, t3 = sa.path_buffers(case["qd"], case["kd"], case["vd"], g, slot_major=False)
+        sa.sparse_attn_attention(buf3, g, case["k_frac"], case["p"], 0.0, chunk, aux_stream=aux_s)
+        torch.cuda.synchronize()
+        assert torch.equal(t3["o"], o) and torch.equal(t3["lse"], lse)
 
 
 # ----------------------------------------------------------------------------
