@@ -3,8 +3,9 @@
 
 One step = the whole path on one batch of resident synthetic input:
 reorder Q and K (pooling them on the way) and V -> float64 block scores ->
-hybrid selection -> block-sparse forward -> unreorder O and LSE, all HIP
-kernels of libsparse_attn.so called through the C ABI.
+hybrid selection -> block-sparse forward writing O and LSE back in token order
+(the inverse re-indexing fused into its epilogue), all HIP kernels of
+libsparse_attn.so called through the C ABI.
 
 Headline workload: Wan2.1-14B-720p-shaped attention, B=1, H=40, d=128, latent
 grid 21x45x80 (75,600 tokens, 1,440 cubes of 4x4x4), Top-k 3% (the pages'
@@ -128,9 +129,9 @@ class Path:
             ("mask", lambda: (sa.sparse_attn_block_scores(self.qbar, self.kbar, self.scores, 0.0, g),
                               sa.sparse_attn_select(self.scores, g, self.k_frac, self.p, self.rb, self.lut,
                                                     self.counts, self.cap))),
-            ("fwd", lambda: sa.sparse_attn_fwd(self.qc, self.kc, self.vc, self.lut, self.counts, self.cap,
-                                               g, 0.0, self.oc, self.lse_c, self.fws)),
-            ("unreorder", lambda: sa.sparse_attn_unreorder(self.oc, self.o, self.lse_c, self.lse, g)),
+            # the forward with the inverse re-indexing fused (O and LSE in token order)
+            ("fwd", lambda: sa.sparse_attn_fwd_tokens(self.qc, self.kc, self.vc, self.lut, self.counts, self.cap,
+                                                      g, 0.0, self.o, self.lse)),
         ]
 
     def step(self):
@@ -185,7 +186,6 @@ def algorithmic_bytes(path):
         "mask": (B * H * (2 * n * d * 8                       # Qbar, Kbar read
                           + n * n * 8 * 2                     # scores written and read
                           + n * 4) + kept * 4),               # counts + kept ids
-        "unreorder": B * H * (real + pad) * (tok + 4),
     }
 
 
@@ -229,7 +229,10 @@ def next_rows(path, reps=3):
                            "tflops_fp64": round(fl / t_router / 1e9, 2),
                            "frac_of_fp64_peak": round(fl / t_router / 1e9 / PEAK_FP64_TFLOPS, 4)}
     del qr, kr, rs
-    # backward over the same lists: operand layouts prepared untimed
+    # backward over the same lists: the slot-major forward outputs and the
+    # operand layouts it reads are prepared untimed
+    sa.sparse_attn_fwd(path.qc, path.kc, path.vc, path.lut, path.counts, path.cap, g, 0.0, path.oc, path.lse_c,
+                       path.fws)
     lay = {}
     for name, x, layout in (("q", path.q, sa.SA_LAYOUT_QK), ("k", path.k, sa.SA_LAYOUT_QK),
                             ("v_qk", path.v, sa.SA_LAYOUT_QK), ("k_v", path.k, sa.SA_LAYOUT_V),

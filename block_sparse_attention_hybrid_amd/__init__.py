@@ -33,7 +33,7 @@ SA_LAYOUT_V = 1
 EXPORTED = (
     "sparse_attn_geometry", "sparse_attn_ceil_k", "sparse_attn_reorder",
     "sparse_attn_reorder_pool", "sparse_attn_unreorder", "sparse_attn_pool", "sparse_attn_block_scores",
-    "sparse_attn_select", "sparse_attn_mask_workspace_bytes",
+    "sparse_attn_select", "sparse_attn_mask_workspace_bytes", "sparse_attn_fwd_tokens",
     "sparse_attn_build_mask", "sparse_attn_fwd_workspace_bytes", "sparse_attn_fwd",
     "sparse_attn_coarse", "sparse_attn_router_pool", "sparse_attn_router_scores",
     "sparse_attn_bwd_delta", "sparse_attn_transpose_workspace_bytes", "sparse_attn_transpose_lut",
@@ -100,6 +100,7 @@ _SIGS = {
     "sparse_attn_build_mask": (_i32, [_vp, _vp, _GP, _i32, _f64, _f64, _vp, _vp, _vp, _i32, _vp, _sz, _vp]),
     "sparse_attn_fwd_workspace_bytes": (_sz, [_GP]),
     "sparse_attn_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _GP, _f32, _vp, _vp, _vp, _sz, _vp]),
+    "sparse_attn_fwd_tokens": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _GP, _f32, _vp, _vp, _vp]),
     "sparse_attn_coarse": (_i32, [_vp, _vp, _vp, _GP, _vp]),
     "sparse_attn_router_pool": (_i32, [_vp, _vp, _GP, _i32, _i32, _i32, _vp]),
     "sparse_attn_router_scores": (_i32, [_vp, _vp, _vp, _f64, _GP, _i32, _i32, _i32, _vp]),
@@ -236,6 +237,15 @@ def sparse_attn_build_mask(qc, kc, g: Geom, block: int, k_frac: float, p: float,
 
 def sparse_attn_fwd_workspace_bytes(g: Geom) -> int:
     return int(lib().sparse_attn_fwd_workspace_bytes(ctypes.byref(g)))
+
+
+def sparse_attn_fwd_tokens(qc, kc, vc, lut, counts, cap: int, g: Geom, scale: float, o, lse,
+                           stream=None) -> None:
+    _check(lib().sparse_attn_fwd_tokens(_ptr(qc, torch.bfloat16, "qc"), _ptr(kc, torch.bfloat16, "kc"),
+                                        _ptr(vc, torch.bfloat16, "vc"), _ptr(lut, torch.int32, "lut"),
+                                        _ptr(counts, torch.int32, "counts"), int(cap), ctypes.byref(g),
+                                        float(scale), _ptr(o, torch.bfloat16, "o"),
+                                        _ptr(lse, torch.float32, "lse"), _stream(stream, qc)))
 
 
 def sparse_attn_fwd(qc, kc, vc, lut, counts, cap: int, g: Geom, scale: float, oc, lse_c,
@@ -444,6 +454,16 @@ def fwd(qc, kc, vc, lut, counts, g: Geom, scale: float = 0.0, stream=None):
     ws = None if nws == 0 else torch.empty(nws, dtype=torch.uint8, device=qc.device)
     sparse_attn_fwd(qc, kc, vc, lut, counts, lut.shape[-1], g, scale, oc, lse_c, ws, stream)
     return oc, lse_c
+
+
+def fwd_tokens(qc, kc, vc, lut, counts, g: Geom, scale: float = 0.0, stream=None):
+    """Block-sparse forward with the inverse re-indexing fused: O [B,H,N,d]
+    (bf16) and natural-log LSE [B,H,N] (fp32) in token order."""
+    _, n_real, _ = sparse_attn_geometry(g)
+    o = _empty((g.batch, g.heads, n_real, g.head_dim), torch.bfloat16, qc)
+    lse = _empty((g.batch, g.heads, n_real), torch.float32, qc)
+    sparse_attn_fwd_tokens(qc, kc, vc, lut, counts, lut.shape[-1], g, scale, o, lse, stream)
+    return o, lse
 
 
 def build_mask_groups(qc, kc, g: Geom, qgroup: int, k_frac: float, p: float, cap=None, stream=None):

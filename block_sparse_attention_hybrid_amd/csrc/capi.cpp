@@ -621,6 +621,25 @@ int32_t sparse_attn_fwd(const void* qc, const void* kc, const void* vc, const in
                     "fwd launch");
 }
 
+int32_t sparse_attn_fwd_tokens(const void* qc, const void* kc, const void* vc, const int32_t* lut,
+                               const int32_t* counts, int32_t cap, const sa_geom* g, float scale, void* o,
+                               float* lse, void* stream) {
+  sa::Geom d;
+  SA_TRY(make_geom(g, d));
+  SA_TRY(check_ptr(qc, 16, "qc"));
+  SA_TRY(check_ptr(kc, 16, "kc"));
+  SA_TRY(check_ptr(vc, 16, "vc"));
+  SA_TRY(check_ptr(lut, 4, "lut"));
+  SA_TRY(check_ptr(counts, 4, "counts"));
+  SA_TRY(check_ptr(o, 16, "o"));
+  SA_TRY(check_ptr(lse, 4, "lse"));
+  if (cap < 1) return fail(SA_ERR_INVALID_ARG, "cap must be >= 1");
+  if (!std::isfinite(scale)) return fail(SA_ERR_INVALID_ARG, "scale must be finite");
+  if (scale <= 0.f) scale = (float)(1.0 / std::sqrt((double)d.d));
+  return hip_status(sa::launch_fwd_tokens(qc, kc, vc, lut, counts, cap, d, scale, o, lse, (hipStream_t)stream),
+                    "fwd launch");
+}
+
 const char* sparse_attn_last_error(void) { return g_last_error; }
 
 }  // extern "C"

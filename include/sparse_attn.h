@@ -399,6 +399,19 @@ int32_t sparse_attn_fwd(const void* qc, const void* kc, const void* vc,
                         const sa_geom* g, float scale, void* oc, float* lse_c,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/* The same forward with the inverse re-indexing ([VSA2] section 2.2,
+ * "Permutation") fused into its epilogue: O and LSE go straight to token
+ * order, as sparse_attn_unreorder would leave them, and no slot-major copy
+ * is written (the backward needs that copy: use sparse_attn_fwd there).
+ *   qc, kc, vc, lut, counts, cap, scale as for sparse_attn_fwd     (inputs)
+ *   o    [batch, heads, N, head_dim] bf16, token order            (output)
+ *   lse  [batch, heads, N] float32, natural log                   (output)
+ * Bit-identical to sparse_attn_fwd followed by sparse_attn_unreorder. */
+int32_t sparse_attn_fwd_tokens(const void* qc, const void* kc, const void* vc,
+                               const int32_t* lut, const int32_t* counts,
+                               int32_t cap, const sa_geom* g, float scale,
+                               void* o, float* lse, void* stream);
+
 /* Ideal block scores ([VSA2] section 2.2: MeanPool of the full attention
  * matrix, the target a router approximates): mass[i][j] = the full softmax
  * mass that block i's real queries put on block j's real keys, averaged over

@@ -241,3 +241,21 @@ def test_whole_path_argument_rules():
     assert call(buffers(cap=15)) == sa.SA_ERR_CAPACITY               # Top-p may keep all 16 blocks
     assert call(buffers(), k_frac=float("nan")) == sa.SA_ERR_INVALID_ARG
     assert call(buffers(), chunk=0) == sa.SA_ERR_INVALID_ARG
+
+
+def test_fused_forward_argument_rules():
+    g = geom()
+    lib = sa.lib()
+    B = ctypes.byref(g)
+    O_ = ctypes.c_void_p(0x200000)
+    assert lib.sparse_attn_fwd_tokens(FAKE, FAKE, FAKE, FAKE, FAKE, 16, B, 0.0, O_, None, None) == \
+        sa.SA_ERR_INVALID_ARG
+    assert "lse" in sa.sparse_attn_last_error()
+    assert lib.sparse_attn_fwd_tokens(FAKE, FAKE, FAKE, FAKE, FAKE, 16, B, 0.0, FAKE_MISALIGNED, FAKE, None) == \
+        sa.SA_ERR_INVALID_ARG                                          # o misaligned
+    assert lib.sparse_attn_fwd_tokens(FAKE, FAKE, FAKE, FAKE, FAKE, 0, B, 0.0, O_, FAKE, None) == \
+        sa.SA_ERR_INVALID_ARG                                          # cap < 1
+    assert lib.sparse_attn_fwd_tokens(FAKE, FAKE, FAKE, FAKE, FAKE, 16, B, float("nan"), O_, FAKE, None) == \
+        sa.SA_ERR_INVALID_ARG
+    assert lib.sparse_attn_fwd_tokens(FAKE, FAKE, FAKE, FAKE, FAKE, 16, None, 0.0, O_, FAKE, None) == \
+        sa.SA_ERR_INVALID_ARG                                          # no geometry

@@ -211,6 +211,19 @@ def test_all_blocks_kept_equals_dense(d):
     assert torch.all(counts1 == og.nblk)
 
 
+def test_fused_forward_equals_forward_then_unreorder(case):
+    """sparse_attn_fwd_tokens (re-indexing fused into the forward's epilogue)
+    gives the bytes of sparse_attn_fwd followed by sparse_attn_unreorder."""
+    g, ref = case["g"], case["ref_mask"]
+    qc, kc, vc = reorder3(case["qd"], case["kd"], case["vd"], g)
+    lut, counts = torch.from_numpy(ref.lut).to(DEV), torch.from_numpy(ref.counts).to(DEV)
+    oc, lse_c = sa.fwd(qc, kc, vc, lut, counts, g)
+    o, lse = sa.unreorder(oc, lse_c, g)
+    o2, lse2 = sa.fwd_tokens(qc, kc, vc, lut, counts, g)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, o) and torch.equal(lse2, lse)
+
+
 def test_keep_nothing_gives_zero_and_neg_inf():
     say("[edge keep-none]")
     wl, g, og, q, k, v = _small()
