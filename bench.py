@@ -385,7 +385,20 @@ def cpu_baseline(path, seconds):
                    f"sampled query blocks of those heads ({t_attn:.2f}s); mask time charged pro "
                    f"rata to the sampled blocks"),
         "seconds": round(t_mask + t_attn, 2),
+        "cpu_model": cpu_model(),
     }
+
+
+def cpu_model():
+    """The host CPU's model name, as /proc/cpuinfo gives it (None elsewhere)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def main():
