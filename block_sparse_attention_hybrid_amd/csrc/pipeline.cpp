@@ -22,8 +22,12 @@
 
 namespace {
 
-// Events reused across calls (one pool per thread).
+// Events reused across calls: one pool per thread and device (an event
+// belongs to the device that was current when it was created).  Re-recording
+// an event is safe while an earlier wait on it is still pending: a wait
+// refers to the record that preceded it.
 struct EventPool {
+  int device = -1;
   std::vector<hipEvent_t> ev;
   hipError_t get(size_t n) {
     while (ev.size() < n) {
@@ -35,7 +39,23 @@ struct EventPool {
     return hipSuccess;
   }
 };
-thread_local EventPool g_events;
+thread_local std::vector<EventPool> g_pools;
+
+// The current device's pool, holding at least n events.
+hipError_t events_for_current_device(size_t n, std::vector<hipEvent_t>*& out) {
+  int dev = 0;
+  const hipError_t r = hipGetDevice(&dev);
+  if (r != hipSuccess) return r;
+  for (EventPool& p : g_pools)
+    if (p.device == dev) {
+      out = &p.ev;
+      return p.get(n);
+    }
+  g_pools.push_back(EventPool{});
+  g_pools.back().device = dev;
+  out = &g_pools.back().ev;
+  return g_pools.back().get(n);
+}
 
 // Geometry of rows [r0, r0 + nr) of the flattened batch*heads dimension.
 sa::Geom rows_of(const sa::Geom& d, int nr) {
@@ -71,6 +91,7 @@ extern "C" int32_t sparse_attn_attention(const sa_path_buffers* b, const sa_geom
   const size_t head_r = (size_t)d.n_real * tok;
   const size_t nb = (size_t)d.nblk;
   hipError_t e;
+  std::vector<hipEvent_t>* evp = nullptr;   // this device's events (two-stream form only)
   // the query and key reorders (with pooling) and the mask of rows [r0, r0 + nr)
   auto qk_reorder = [&](int r0, int nr, hipStream_t st) -> hipError_t {
     const sa::Geom gc = rows_of(d, nr);
@@ -102,19 +123,19 @@ extern "C" int32_t sparse_attn_attention(const sa_path_buffers* b, const sa_geom
     // auxiliary stream re-indexes the values (the re-indexing is bound by HBM,
     // the scores and selection by compute).
     const int part = rows > 1 ? rows / 2 : rows;
-    if ((e = g_events.get(nchunks + 3)) != hipSuccess) return sa_hip_status(e, "event creation");
+    if ((e = events_for_current_device(nchunks + 3, evp)) != hipSuccess) return sa_hip_status(e, "event creation");
     if ((e = qk_reorder(0, part, s)) != hipSuccess) return sa_hip_status(e, "reorder_pool launch");
-    if ((e = hipEventRecord(g_events.ev[0], s)) != hipSuccess) return sa_hip_status(e, "event record");
-    if ((e = hipStreamWaitEvent(a, g_events.ev[0], 0)) != hipSuccess) return sa_hip_status(e, "stream wait");
+    if ((e = hipEventRecord((*evp)[0], s)) != hipSuccess) return sa_hip_status(e, "event record");
+    if ((e = hipStreamWaitEvent(a, (*evp)[0], 0)) != hipSuccess) return sa_hip_status(e, "stream wait");
     if (rows > part && (e = qk_reorder(part, rows - part, a)) != hipSuccess)
       return sa_hip_status(e, "reorder_pool launch");
-    if ((e = hipEventRecord(g_events.ev[1], a)) != hipSuccess) return sa_hip_status(e, "event record");
+    if ((e = hipEventRecord((*evp)[1], a)) != hipSuccess) return sa_hip_status(e, "event record");
     if ((e = sa::launch_reorder(b->v, b->vc, 1, d, a)) != hipSuccess) return sa_hip_status(e, "reorder launch");
     if ((e = mask(0, part, s)) != hipSuccess) return sa_hip_status(e, "mask launch");
-    if ((e = hipStreamWaitEvent(s, g_events.ev[1], 0)) != hipSuccess) return sa_hip_status(e, "stream wait");
+    if ((e = hipStreamWaitEvent(s, (*evp)[1], 0)) != hipSuccess) return sa_hip_status(e, "stream wait");
     if (rows > part && (e = mask(part, rows - part, s)) != hipSuccess) return sa_hip_status(e, "mask launch");
-    if ((e = hipEventRecord(g_events.ev[2], s)) != hipSuccess) return sa_hip_status(e, "event record");
-    if ((e = hipStreamWaitEvent(a, g_events.ev[2], 0)) != hipSuccess) return sa_hip_status(e, "stream wait");
+    if ((e = hipEventRecord((*evp)[2], s)) != hipSuccess) return sa_hip_status(e, "event record");
+    if ((e = hipStreamWaitEvent(a, (*evp)[2], 0)) != hipSuccess) return sa_hip_status(e, "stream wait");
   }
   // the forward chunk by chunk on the auxiliary stream; each chunk's output is
   // re-indexed on the main stream while the next chunk's forward runs (the
@@ -134,8 +155,8 @@ extern "C" int32_t sparse_attn_attention(const sa_path_buffers* b, const sa_geom
       if ((e = sa::launch_fwd_tokens(qc, kc, vc, lut, counts, b->cap, gc, sc, o, lse, a)) != hipSuccess)
         return sa_hip_status(e, "fwd launch");
       if (two) {
-        if ((e = hipEventRecord(g_events.ev[3 + c], a)) != hipSuccess) return sa_hip_status(e, "event record");
-        if ((e = hipStreamWaitEvent(s, g_events.ev[3 + c], 0)) != hipSuccess)
+        if ((e = hipEventRecord((*evp)[3 + c], a)) != hipSuccess) return sa_hip_status(e, "event record");
+        if ((e = hipStreamWaitEvent(s, (*evp)[3 + c], 0)) != hipSuccess)
           return sa_hip_status(e, "stream wait");
       }
       continue;
@@ -145,8 +166,8 @@ extern "C" int32_t sparse_attn_attention(const sa_path_buffers* b, const sa_geom
     if ((e = sa::launch_fwd(qc, kc, vc, lut, counts, b->cap, gc, sc, oc, lse_c, nullptr, a)) != hipSuccess)
       return sa_hip_status(e, "fwd launch");
     if (two) {
-      if ((e = hipEventRecord(g_events.ev[3 + c], a)) != hipSuccess) return sa_hip_status(e, "event record");
-      if ((e = hipStreamWaitEvent(s, g_events.ev[3 + c], 0)) != hipSuccess) return sa_hip_status(e, "stream wait");
+      if ((e = hipEventRecord((*evp)[3 + c], a)) != hipSuccess) return sa_hip_status(e, "event record");
+      if ((e = hipStreamWaitEvent(s, (*evp)[3 + c], 0)) != hipSuccess) return sa_hip_status(e, "stream wait");
     }
     if ((e = sa::launch_unreorder(oc, o, lse_c, lse, gc, s)) != hipSuccess)
       return sa_hip_status(e, "unreorder launch");
