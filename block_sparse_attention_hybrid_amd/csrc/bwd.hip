@@ -411,12 +411,18 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(const u32x4* __restrict__ 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, hf = lane >> 5, r = lane & 31;
   const int kh = wave & 1, qq = wave >> 1;
-  const int qpos = hf * 32 + sigma32(r);
   const long long head = bh * (long long)g.nblk * BLK;
 
   // per buffer: the NCH operand chunks, then one chunk whose first 256 bytes
-  // hold the LSE row and the next 256 bytes the D row
+  // hold the LSE row and the next 256 bytes the D row.  Inside a staged
+  // chunk the token slots are rotated: QK-layout slot (h, r) of a chunk of
+  // dim step ds sits at LDS slot h*32 + (r + 4h + 8 (ds % 2)) % 32.  A
+  // transpose read takes both halves of 8 tokens from the chunks of two
+  // neighbouring dim steps; with the rotation each half-wave of it meets
+  // every bank once (unrotated, the halves 512 bytes apart and the chunks
+  // 1 KB apart fell on the same banks).
   __shared__ u32x4 stage[2][(NCH + 1) * 64];
+  auto lds_slot = [](int ds_odd, int h, int rr) { return h * 32 + ((rr + 4 * h + 8 * ds_odd) & 31); };
 
   // this wave's 32 keys (B operands, chunk t32 = kh) and whether this lane's key is real
   u32x4 kreg[NDS], vreg[NDS];
@@ -436,18 +442,24 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(const u32x4* __restrict__ 
   // dim tile dt needs, in lane (r, hf), queries 16 ks + 8 hf .. +7 of dim
   // 32 dt + r.  Read h (h = 0, 1) delivers queries 16 ks + 8 hf + 4 h .. +3:
   // lane s = 16 gq + 4 e + m of group gq supplies the 8 bytes holding dims
-  // 32 dt + 16 (gq % 2) + 4 m .. +3 of query 16 ks + 8 (gq / 2) + 4 h + e.
-  // In the QK layout that is byte
-  //   ((ks / 2) NDS + 2 dt) 1024 + (16 (ks % 2) + 4 h) 16   (uniform)
-  //   + (gq % 2) 1024 + (32 (m / 2) + 8 (gq / 2) + e) 16 + 8 (m % 2)   (this lane)
-  const int tr_lane = [&] {
+  // 32 dt + 16 (gq % 2) + 4 m .. +3 of query 16 ks + 8 (gq / 2) + 4 h + e,
+  // i.e. half m / 2 of token slot 16 (ks % 2) + 4 h + 8 (gq / 2) + e of
+  // chunk ((ks / 2) NDS + 2 dt + gq % 2).  This wave's k-steps have
+  // ks / 2 = qq, so the lane part depends on (ks % 2, h) only: four offsets.
+  int tr_lane[2][2];
+  {
     const int gq = lane >> 4, e = (lane >> 2) & 3, m = lane & 3;
-    return (gq & 1) * 1024 + (32 * (m >> 1) + 8 * (gq >> 1) + e) * 16 + 8 * (m & 1);
-  }();
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        tr_lane[kk][h] = (gq & 1) * 1024 + lds_slot(gq & 1, m >> 1, 16 * kk + 4 * h + 8 * (gq >> 1) + e) * 16 +
+                         8 * (m & 1);
+  }
   auto tr_operand = [&](const u32x4* arr, int dt, int ks) {
-    const int base = ((ks >> 1) * NDS + 2 * dt) * 1024 + (16 * (ks & 1)) * 16 + tr_lane;
-    const u32x2 lo = read_tr16(arr, base);
-    const u32x2 hi = read_tr16(arr, base + 4 * 16);
+    const int base = ((ks >> 1) * NDS + 2 * dt) * 1024;
+    const u32x2 lo = read_tr16(arr, base + tr_lane[ks & 1][0]);
+    const u32x2 hi = read_tr16(arr, base + tr_lane[ks & 1][1]);
     return u32x4{lo[0], lo[1], hi[0], hi[1]};
   };
 
@@ -467,15 +479,19 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(const u32x4* __restrict__ 
   // lanes 16-31 the 64 D values; lanes 32-63 repeat them into a part of the
   // slot that is not read)
   static_assert(2 * PER_WAVE == NARR, "half an array per wave");
+  static_assert(PER_WAVE % 2 == 0 && NDS % 2 == 0, "a copied chunk's dim-step parity is cc % 2");
   const u32x4* my_src = (wave < 2 ? q : do_qk) + (wave & 1) * PER_WAVE * 64;
   const u32x4* row_src = reinterpret_cast<const u32x4*>((lane & 16) ? delta : lse);
+  // LDS slot `lane` of a chunk of dim-step parity o receives QK-layout slot
+  // (h, (lane - 4h - 8o) % 32), h = lane / 32 (the inverse of lds_slot)
+  const int src_slot[2] = {hf * 32 + ((r - 4 * hf) & 31), hf * 32 + ((r - 4 * hf - 8) & 31)};
   auto issue = [&](int b, int it) {
     const int i0 = list[it];
     const int i = valid(i0) ? i0 : 0;
     const long long ob = head + (long long)i * BLK;
 #pragma unroll
     for (int cc = 0; cc < PER_WAVE; ++cc)
-      copy_to_lds(my_src + ob + cc * 64 + lane, &stage[b][(wave * PER_WAVE + cc) * 64]);
+      copy_to_lds(my_src + ob + cc * 64 + src_slot[cc & 1], &stage[b][(wave * PER_WAVE + cc) * 64]);
     if (wave == 0)
       copy_to_lds(row_src + (bh * g.n_pad + (long long)i * kBlock) / 4 + (lane & 15), &stage[b][NCH * 64]);
   };
@@ -506,6 +522,7 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(const u32x4* __restrict__ 
       for (int e = 0; e < 16; ++e) s[e] = dp[e] = 0.f;
 #pragma unroll
       for (int ds = 0; ds < NDS; ++ds) {
+        const int qpos = lds_slot(ds & 1, hf, sigma32(r));
         const u32x4 qa = qs[(qq * NDS + ds) * 64 + qpos];
         const u32x4 da = dos[(qq * NDS + ds) * 64 + qpos];
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qa), as_bf16x8(kreg[ds]), s, 0, 0, 0);
