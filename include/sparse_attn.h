@@ -8,6 +8,7 @@
  *   block_scores S = Qbar Kbar^T * scale (float64 matrix cores)
  *   select       per query block: hybrid Top-k U Top-p kept-block list
  *   fwd          block-sparse attention over the kept blocks -> O, LSE
+ *                (fwd_tokens: the same, writing token order -- unreorder fused)
  *   coarse       block-level attention on pooled Q, K, V (coarse branch)
  *   router       fine-grained router scores (sub-cube pooling, G x G pooling)
  *   bwd          gradients of the block-sparse attention (dQ, dK, dV)
@@ -55,8 +56,9 @@
  *   gives a message (per calling thread).  A failed launch returns
  *   SA_ERR_HIP.  Faults inside kernels surface at the caller's next
  *   synchronisation, as for any HIP work.
- * - Functions keep no state between calls and are safe to call from several
- *   host threads.
+ * - Functions keep no caller-visible state between calls and are safe to
+ *   call from several host threads.  (sparse_attn_attention on two streams
+ *   reuses HIP events it creates, one pool per host thread and device.)
  *
  * Citations name the pages this library follows by title and section:
  *   [SA2]  "SpargeAttention2: Trainable Sparse Attention via Hybrid Top-k+Top-p
