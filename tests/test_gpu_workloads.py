@@ -65,6 +65,21 @@ def test_workload(name, wid, k_frac, p, budgets, heads):
     density = counts_h.sum() / (counts_h.size * n)
     say(f"  density {density:.4f} (block sparsity {1 - density:.4f})")
 
+    # --- the configuration the bench times: the whole-path call on two streams,
+    # all rows in one chunk, O and LSE straight to token order.  Same lists, and
+    # the same bytes as the checked step-by-step path re-indexed.
+    o_ref_path, lse_ref_path = sa.unreorder(oc, lse_c, g)
+    buf, t = sa.path_buffers(q.to(DEV), k.to(DEV), v.to(DEV), g, row_budget=rb, slot_major=False)
+    aux = torch.cuda.Stream()
+    sa.sparse_attn_attention(buf, g, k_frac, p, 0.0, g.batch * g.heads, aux_stream=aux.cuda_stream)
+    torch.cuda.synchronize()
+    assert torch.equal(t["counts"], counts)
+    live_t = torch.arange(n, device=DEV) < counts[..., None]
+    assert torch.equal(torch.where(live_t, t["lut"], 0), torch.where(live_t, lut, 0))
+    assert torch.equal(t["o"], o_ref_path) and torch.equal(t["lse"], lse_ref_path)
+    del buf, t, o_ref_path, lse_ref_path
+    say("  whole-path call (bench configuration) identical")
+
     # --- oracle on sampled heads ----------------------------------------------
     sel = list(heads)
     qs, ks, vs = (O.reorder(to64(t[:, sel]), og) for t in (q, k, v))
