@@ -327,8 +327,8 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const double* __restri
         return (int)((desc_key(v) >> shift) & 255ull);
       };
 
-      // the exchange above (or, in round 0, the one before the loop) orders
-      // the previous round's histogram reads before this clear
+      // the exchange above (or, in the first histogram pass, the one before the loop) orders
+      // the previous pass's histogram reads before this clear
       hist[threadIdx.x] = 0ull;
       if constexpr (!kPacked) hcnt[threadIdx.x] = 0u;
       __syncthreads();
