@@ -531,6 +531,40 @@ def test_whole_path_call_overlapped_equals_sequential(case, chunk):
         assert torch.equal(t3["o"], o) and torch.equal(t3["lse"], lse)
 
 
+def test_whole_path_call_from_two_threads(case):
+    """Two host threads run the whole-path call at the same time, each on its
+    own pair of streams and its own buffers, three times in a row (the event
+    pools are per thread and re-recorded on every call).  Both give the bytes
+    of the step-by-step path."""
+    import threading
+    g = case["g"]
+    o, lse, _, _ = sa.attention(case["qd"], case["kd"], case["vd"], g, case["k_frac"], case["p"])
+    jobs = []
+    for slot_major in (True, False):
+        buf, t = sa.path_buffers(case["qd"], case["kd"], case["vd"], g, slot_major=slot_major)
+        jobs.append((buf, t, torch.cuda.Stream(), torch.cuda.Stream()))
+    torch.cuda.synchronize()
+    errors = []
+
+    def run(buf, main, aux):
+        try:
+            for _ in range(3):
+                sa.sparse_attn_attention(buf, g, case["k_frac"], case["p"], 0.0, 1 << 20,
+                                         stream=main.cuda_stream, aux_stream=aux.cuda_stream)
+        except Exception as exc:   # re-raised on the test's thread below
+            errors.append(exc)
+
+    threads = [threading.Thread(target=run, args=(buf, s, a)) for buf, _, s, a in jobs]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for _, t, _, _ in jobs:
+        assert torch.equal(t["o"], o) and torch.equal(t["lse"], lse)
+
+
 # ----------------------------------------------------------------------------
 # asymmetric blocks: query blocks of qg cubes
 # ----------------------------------------------------------------------------
