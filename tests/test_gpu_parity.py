@@ -565,6 +565,41 @@ def test_whole_path_call_from_two_threads(case):
         assert torch.equal(t["o"], o) and torch.equal(t["lse"], lse)
 
 
+def test_whole_path_call_in_a_graph(case):
+    """The two-stream whole-path call captured once in a HIP graph (the
+    auxiliary stream forks from and joins the capturing stream through the
+    call's events) and replayed three times. Before each replay the outputs
+    are cleared and the inputs rewritten in place by eager work; every replay
+    gives the bytes of an eager step-by-step run on the same inputs."""
+    g = case["g"]
+    q, k, v = (x.clone() for x in (case["qd"], case["kd"], case["vd"]))
+    buf, t = sa.path_buffers(q, k, v, g, slot_major=False)
+    cap_stream, aux = torch.cuda.Stream(), torch.cuda.Stream()
+    call = lambda: sa.sparse_attn_attention(buf, g, case["k_frac"], case["p"], 0.0, 1 << 20,
+                                            aux_stream=aux.cuda_stream)
+    cap_stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap_stream):
+        call()                       # eager warm-up on the capturing stream
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cap_stream):
+        call()
+    torch.cuda.synchronize()
+    inputs = [(case["qd"], case["kd"], case["vd"]),
+              (case["kd"], case["qd"], case["vd"]),          # queries and keys swapped
+              (case["qd"], case["kd"], -case["vd"])]
+    for qi, ki, vi in inputs:
+        q.copy_(qi); k.copy_(ki); v.copy_(vi)
+        for n in ("o", "lse", "lut", "counts"):
+            t[n].zero_()
+        want_o, want_lse, want_lut, want_counts = sa.attention(qi, ki, vi, g, case["k_frac"], case["p"])
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(t["counts"], want_counts)
+        assert torch.equal(t["o"], want_o) and torch.equal(t["lse"], want_lse)
+
+
 # ----------------------------------------------------------------------------
 # asymmetric blocks: query blocks of qg cubes
 # ----------------------------------------------------------------------------
