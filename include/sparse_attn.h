@@ -244,10 +244,17 @@ typedef struct sa_path_buffers {
  * second half's and then the values, and `stream` then builds the second
  * half's mask; the forward then runs on aux_stream in chunks of head_chunk
  * batch*heads rows (head_chunk >= batch*heads: one chunk), and `stream`
- * re-indexes each chunk's output while the next chunk's forward runs.  The
- * last work on `stream` waits for the last forward chunk, so completion is
- * observed on `stream`.  The results are the same either way.  Both streams
- * must belong to the current device. */
+ * re-indexes each chunk's output while the next chunk's forward runs (with
+ * buffers->oc NULL the forward writes token order itself and `stream` only
+ * waits for each chunk).  The last work on `stream` waits for the last
+ * forward chunk, so completion is observed on `stream`.  The results are the
+ * same either way.  Both streams must belong to the current device.
+ *
+ * The call neither allocates nor synchronises the host, so it can be captured
+ * in a HIP graph on `stream`.  aux_stream forks from the capture through the
+ * call's events and joins it again before the call returns.  The first call
+ * on a host thread creates those events; making one call before capturing
+ * keeps their creation out of the captured region. */
 int32_t sparse_attn_attention(const sa_path_buffers* buffers, const sa_geom* g,
                               double k_frac, double p, float scale,
                               int32_t head_chunk, void* stream,
