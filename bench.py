@@ -404,10 +404,10 @@ def cpu_model():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "the library runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
-        log("bench.py: only --gpus 1 is supported (the path is single-GPU; see the design notes "
-            "for how it would shard by head)")
+        log("bench.py: only --gpus 1 is supported (the path runs on one GPU; it would shard by "
+            "(batch, head), with no exchange inside the attention)")
         sys.exit(2)
     if not torch.cuda.is_available():
         log("bench.py needs a GPU")
