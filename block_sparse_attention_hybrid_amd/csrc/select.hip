@@ -68,7 +68,7 @@ __device__ __forceinline__ uint64_t desc_key(double s) {
 }
 
 // An opaque copy: per-element work on it is redone where it is used instead of
-// being hoisted out of the round loop, which would keep a precomputed copy of
+// being hoisted out of the histogram-pass loop, which would keep a precomputed copy of
 // every element in registers.
 template <typename T>
 __device__ __forceinline__ T fresh(T x) {
@@ -461,7 +461,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const double* __restri
       const int rstar = wmin_i32(ok ? r : kWave);
       kept_rank = ballot(mine && r <= rstar);
     } else {
-      // more than 64 members of one score (the round limit is never reached):
+      // more than 64 members of one score (the pass limit is never reached):
       // equal masses u, so the count taken is a division
       (void)equal;
       const unsigned long long u = to_fixed(prob(eq, mx));

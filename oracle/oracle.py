@@ -96,8 +96,8 @@ What it computes, step by step, in float64 (bfloat16 inputs convert exactly):
    that the list holds.  The retained mass of the list under P_ideal is the
    block mean of the tau of item 9.
 
-Readings where the pages are silent or garbled are listed in the repository's
-design notes; the ones this file depends on are repeated at each function.
+Where the pages are silent or garbled, the reading taken is stated at the
+function that depends on it.
 Every function here is pinned by the CPU tests (worked examples, closed forms,
 brute force, invariants, special cases).
 """
