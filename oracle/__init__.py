@@ -11,4 +11,4 @@ from .oracle import (Geometry, MaskResult, RowSelection, attention_block,
                      top_p_count, unreorder, unreorder_rows, NEAR_TIE,
                      group_count, pool_groups, build_mask_groups, expand_group_lists,
                      sequence_budget, per_sequence_counts, per_sequence_near_tie, build_mask_per_sequence,
-                     ideal_block_mass, mask_recall)
+                     ideal_block_mass, mask_recall, error_terms, mask_report)

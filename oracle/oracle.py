@@ -96,6 +96,13 @@ What it computes, step by step, in float64 (bfloat16 inputs convert exactly):
    that the list holds.  The retained mass of the list under P_ideal is the
    block mean of the tau of item 9.
 
+13. Eq. 8's two error terms and a mask summary (SpargeAttention2 summary
+   page, "The Sparse Attention Error Decomposition"; the sink rows of "Where
+   Prior Approaches Fall Short"): per query block, the L1 norms of the dropped
+   term p(1 - m)V and of the renormalisation term (1 - 1/tau)(p m)V relative
+   to the dense output; per head, the realised block density, the mean block
+   probability on block 0 and the mean row entropy of the block softmax.
+
 Where the pages are silent or garbled, the reading taken is stated at the
 function that depends on it.
 Every function here is pinned by the CPU tests (worked examples, closed forms,
@@ -600,6 +607,69 @@ def mask_error(qc: np.ndarray, kc_: np.ndarray, vc: np.ndarray, lut: np.ndarray,
                 rel[b, h, i] = num / den if den > 0 else 0.0
             tau[b, h] = t
     return tau, rel
+
+
+def error_terms(qc: np.ndarray, kc_: np.ndarray, vc: np.ndarray, lut: np.ndarray, counts: np.ndarray,
+                g: Geometry, scale: Optional[float] = None):
+    """The two terms of Eq. 8 (SpargeAttention2 summary page, "The Sparse
+    Attention Error Decomposition") per query block, as L1 norms relative to
+    the dense output: for each real query with dense softmax p over the real
+    keys, kept-key indicator m and tau = sum(p * m),
+        dropped term       e_drop = (p * (1 - m)) V,
+        renormalisation    e_ren  = (1 - 1/tau) (p * m) V,
+    and per block rel_drop = sum|e_drop| / sum|o|, rel_ren = sum|e_ren| / sum|o|
+    with o = p V, summed over the block's real queries and the d channels.
+    A query whose kept keys hold no mass (tau = 0) has no renormalised output;
+    its renormalisation term is taken as 0.  Returns [B, H, nblk] twice."""
+    B, H, n_pad, d = qc.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    real = real_slots(g)
+    real_idx = np.nonzero(real)[0]
+    key_blk = real_idx // g.block
+    drop = np.zeros((B, H, g.nblk))
+    ren = np.zeros((B, H, g.nblk))
+    for b in range(B):
+        for h in range(H):
+            q = np.asarray(qc[b, h], dtype=np.float64)
+            k = np.asarray(kc_[b, h], dtype=np.float64)[real]
+            v = np.asarray(vc[b, h], dtype=np.float64)[real]
+            for i in range(g.nblk):
+                m = np.isin(key_blk, lut[b, h, i, :counts[b, h, i]]).astype(np.float64)
+                num_d = num_r = den = 0.0
+                for x in range(i * g.block, (i + 1) * g.block):
+                    if not real[x]:
+                        continue
+                    s = (k @ q[x]) * scale
+                    p = np.exp(s - s.max())
+                    p /= p.sum()
+                    tau = float((p * m).sum())
+                    e_drop = (p * (1.0 - m)) @ v
+                    e_ren = (1.0 - 1.0 / tau) * ((p * m) @ v) if tau > 0 else np.zeros(d)
+                    num_d += np.abs(e_drop).sum()
+                    num_r += np.abs(e_ren).sum()
+                    den += np.abs(p @ v).sum()
+                drop[b, h, i] = num_d / den if den > 0 else 0.0
+                ren[b, h, i] = num_r / den if den > 0 else 0.0
+    return drop, ren
+
+
+def mask_report(scores: np.ndarray, counts: np.ndarray):
+    """Per (batch, head) summary of a mask and the block softmax it was chosen
+    on: realised block density sum(counts) / nblk^2, the mean sink mass
+    P[:, 0] (the share of each row's block probability on block 0, where the
+    SpargeAttention2 page's skewed "sink" rows put most of it), and the mean
+    row entropy -sum_j P_ij ln P_ij (ln nblk for a uniform row, near 0 for a
+    row held by one block).  Returns (density, sink, entropy), each [B, H]."""
+    s = np.asarray(scores, dtype=np.float64)
+    n = s.shape[-1]
+    p = block_softmax(s)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        plogp = np.where(p > 0, p * np.log(p), 0.0)
+    density = np.asarray(counts, dtype=np.float64).sum(axis=-1) / float(n * n)
+    sink = p[..., 0].mean(axis=-1)
+    entropy = (-plogp.sum(axis=-1)).mean(axis=-1)
+    return density, sink, entropy
 
 
 # ----------------------------------------------------------------------------

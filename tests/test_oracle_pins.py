@@ -65,12 +65,61 @@ def test_topp_sink_row_worked_example(golden):
     assert list(sel2.kept) == [0, 1]
 
 
+def _one_token_blocks(probs, values):
+    """One query (block 0) and one key per block, with blocks of a single
+    token, built so that the query's softmax over the keys is exactly `probs`
+    (up to rounding): q = e0, k_j = sqrt(d) ln(p_j) e0.  Returns (q, k, v, g)."""
+    n = len(probs)
+    d = len(values[0])
+    g = O.Geometry(1, 1, n, 1, 1, 1)
+    q = np.zeros((1, 1, n, d))
+    k = np.zeros((1, 1, n, d))
+    q[0, 0, :, 0] = 1.0
+    k[0, 0, :, 0] = math.sqrt(d) * np.log(np.asarray(probs, dtype=np.float64))
+    v = np.asarray(values, dtype=np.float64)[None, None]
+    return q, k, v, g
+
+
 def test_error_decomposition_worked_example(golden):
+    """Eq. 8 on the page's numerical example: p = [0.6, 0.2, 0.2] (and
+    [0.8, 0.1, 0.1] after fine-tuning) under the mask m = [1, 0, 0].  With the
+    values v_0 = 2 e_0, v_1 = e_1, v_2 = e_2, hand arithmetic gives o = pV,
+    o_s = v_0 = [2, 0, 0], tau = 1 - dropped mass, the dropped term
+    (p * (1 - m)) V = [0, p_1, p_2] and the renormalisation term
+    (1 - 1/tau) * 2 p_0 e_0; each L1 norm is taken relative to sum|o|."""
     ex = golden["error_decomposition_example"]
+    vals = [[2.0, 0.0, 0.0], [0.0, 1.0, 0.0], [0.0, 0.0, 1.0]]
     for key in ("before", "after"):
-        p = np.asarray(ex[key]["probs"])
-        m = np.asarray(ex[key]["mask"])
-        assert (p * (1 - m)).sum() == pytest.approx(ex[key]["dropped_mass"], abs=1e-15)
+        probs = ex[key]["probs"]
+        mask = ex[key]["mask"]
+        q, k, v, g = _one_token_blocks(probs, vals)
+        kept0 = [j for j in range(3) if mask[j]]
+        lut = np.full((1, 1, 3, 3), -1, dtype=np.int32)
+        lut[0, 0, 0, :len(kept0)] = kept0
+        lut[0, 0, 1:, :] = [0, 1, 2]
+        counts = np.array([[[len(kept0), 3, 3]]], dtype=np.int32)
+        tau, rel = O.mask_error(q, k, v, lut, counts, g)
+        drop, ren = O.error_terms(q, k, v, lut, counts, g)
+        p0, p1, p2 = probs
+        t = 1.0 - ex[key]["dropped_mass"]                 # the page's dropped mass
+        o_l1 = 2 * p0 + p1 + p2
+        want_rel = (abs(2 * p0 - 2) + p1 + p2) / o_l1     # |o - o_s| with o_s = [2, 0, 0]
+        assert tau[0, 0, 0] == pytest.approx(t, abs=1e-12)
+        assert rel[0, 0, 0] == pytest.approx(want_rel, abs=1e-12)
+        assert drop[0, 0, 0] == pytest.approx((p1 + p2) / o_l1, abs=1e-12)
+        assert ren[0, 0, 0] == pytest.approx(abs(1 - 1 / t) * 2 * p0 / o_l1, abs=1e-12)
+        # rows keeping every block: no error of either kind
+        np.testing.assert_allclose(rel[0, 0, 1:], 0.0, atol=1e-12)
+        np.testing.assert_allclose(drop[0, 0, 1:], 0.0, atol=1e-12)
+        np.testing.assert_allclose(ren[0, 0, 1:], 0.0, atol=1e-12)
+    # before: tau 0.6, rel-L1 1.2 / 1.6 = 0.75, terms 0.4 / 1.6 and 0.8 / 1.6
+    q, k, v, g = _one_token_blocks(ex["before"]["probs"], vals)
+    lut = np.array([[[[0, -1, -1], [0, 1, 2], [0, 1, 2]]]], dtype=np.int32)
+    counts = np.array([[[1, 3, 3]]], dtype=np.int32)
+    tau, rel = O.mask_error(q, k, v, lut, counts, g)
+    drop, ren = O.error_terms(q, k, v, lut, counts, g)
+    assert (tau[0, 0, 0], rel[0, 0, 0], drop[0, 0, 0], ren[0, 0, 0]) == pytest.approx((0.6, 0.75, 0.25, 0.5),
+                                                                                      abs=1e-12)
 
 
 def test_vsa_sparsity_worked_example(golden):
@@ -112,6 +161,10 @@ def test_token_slots_closed_form(grid):
             for w in range(W):
                 cube = (t // 4) * nh * nw + (h // 4) * nw + (w // 4)
                 assert slots[n] // 64 == cube
+                # the reading of the stripped within-cube term: row-major
+                # (t, h, w) inside the cube, the order the library's
+                # cube-major tensors use
+                assert slots[n] % 64 == (t % 4) * 16 + (h % 4) * 4 + (w % 4)
                 n += 1
     assert g.nblk == nt * nh * nw
 
@@ -266,6 +319,20 @@ def _check_invariants(s, probs, sel, kc, p):
         assert smaller < kc or (p > 0 and smaller_mass < p + 1e-12) or sel.near_tie
 
 
+def test_select_rows_matches_brute_force_per_row():
+    """Every row of a head's score matrix gets its own brute-force answer, in
+    row order."""
+    rng = np.random.default_rng(41)
+    n = 10
+    s = rng.standard_normal((n, n)) * rng.uniform(0.3, 3.0, (n, 1))
+    probs = O.block_softmax(s)
+    for kc, p in ((2, 0.5), (0, 0.8), (4, 0.0)):
+        rows = O.select_rows(s, kc, p)
+        assert len(rows) == n
+        for i, sel in enumerate(rows):
+            assert sorted(sel.kept.tolist()) == _brute_force_union(probs[i], kc, p), (i, kc, p)
+
+
 @pytest.mark.parametrize("seed", range(20))
 def test_select_invariants_random_rows(seed):
     rng = np.random.default_rng(seed)
@@ -390,6 +457,40 @@ def test_error_decomposition_identity():
             tau = (p * m).sum()
             e = (p * (1 - m) + (1 - 1 / tau) * (p * m)) @ vc[0, 0]
             np.testing.assert_allclose(o_full[r] - oc[0, 0, r], e, rtol=1e-9, atol=1e-12)
+
+
+def test_dense_attention_matches_library_attention():
+    """The oracle's dense attention against torch's scaled-dot-product
+    attention (float64, CPU) and scipy's log-sum-exp of the scaled scores."""
+    rng = np.random.default_rng(17)
+    q, k, v = (rng.standard_normal((2, 37, 12)) for _ in range(3))
+    o, lse = O.dense_attention(q, k, v)
+    want = torch.nn.functional.scaled_dot_product_attention(*(torch.from_numpy(x) for x in (q, k, v)))
+    np.testing.assert_allclose(o, want.numpy(), rtol=1e-12, atol=1e-13)
+    s = np.matmul(q, np.swapaxes(k, -1, -2)) / math.sqrt(12)
+    np.testing.assert_allclose(lse, scipy.special.logsumexp(s, axis=-1), rtol=1e-13)
+    o2, lse2 = O.dense_attention(q, k, v, scale=0.5)
+    want2 = torch.nn.functional.scaled_dot_product_attention(*(torch.from_numpy(x) for x in (q, k, v)), scale=0.5)
+    np.testing.assert_allclose(o2, want2.numpy(), rtol=1e-12, atol=1e-13)
+
+
+def test_build_mask_row_budgets_keep_each_rows_top_blocks():
+    """With per-row budgets (p = 0) every row keeps exactly its budget of
+    top-scoring blocks, lower ids first on equal scores (library stable sort
+    as the independent route)."""
+    g = O.Geometry(4, 9, 13)
+    rng = np.random.default_rng(23)
+    qc = O.reorder(rng.standard_normal((1, 2, g.n_real, 8)), g)
+    kc_ = O.reorder(rng.standard_normal((1, 2, g.n_real, 8)), g)
+    budget = rng.integers(0, g.nblk + 1, (1, 2, g.nblk)).astype(np.int32)
+    m = O.build_mask(qc, kc_, g, 0.5, 0.0, row_budget=budget)
+    np.testing.assert_array_equal(m.counts, budget)
+    np.testing.assert_array_equal(m.kc, budget)
+    for h in range(2):
+        for i in range(g.nblk):
+            c = budget[0, h, i]
+            top = np.sort(np.argsort(-m.scores[0, h, i], kind="stable")[:c])
+            np.testing.assert_array_equal(m.lut[0, h, i, :c], top)
 
 
 def test_zero_queries_average_kept_values():
@@ -600,6 +701,33 @@ def _coordinate_router(q, k, grid, R, cube=(4, 4, 4)):
     return out
 
 
+@pytest.mark.parametrize("R", [(2, 2, 2), (1, 2, 4), (4, 1, 2)])
+def test_subcube_means_follow_coordinates(R):
+    """Row blk * G + a of the sub-cube means is the mean of the real tokens of
+    cube blk whose offsets fall in sub-cube a, the sub-cubes numbered
+    row-major over the (4/rt, 4/rh, 4/rw) grid inside the cube (taken here
+    straight from the token coordinates); all-pad sub-cubes are absent."""
+    T, H, W, d = 5, 6, 7, 3
+    g = O.Geometry(T, H, W)
+    rng = np.random.default_rng(33)
+    x = rng.standard_normal((T * H * W, d))
+    xr, present = O.pool_r(O.reorder(x, g), g, R)
+    G = 64 // (R[0] * R[1] * R[2])
+    sh, sw = 4 // R[1], 4 // R[2]
+    sums = np.zeros((g.nblk * G, d))
+    cnt = np.zeros(g.nblk * G)
+    for t in range(T):
+        for h in range(H):
+            for w in range(W):
+                blk = ((t // 4) * g.nh + h // 4) * g.nw + w // 4
+                a = ((t % 4) // R[0] * sh + (h % 4) // R[1]) * sw + (w % 4) // R[2]
+                sums[blk * G + a] += x[(t * H + h) * W + w]
+                cnt[blk * G + a] += 1
+    np.testing.assert_array_equal(present, cnt > 0)
+    np.testing.assert_allclose(xr[cnt > 0], sums[cnt > 0] / cnt[cnt > 0, None], rtol=1e-13, atol=1e-15)
+    assert np.all(xr[cnt == 0] == 0.0)
+
+
 @pytest.mark.parametrize("grid", [(5, 6, 7), (4, 8, 8), (3, 5, 6)])
 def test_router_matches_coordinate_definition(grid):
     rng = np.random.default_rng(31)
@@ -741,6 +869,78 @@ def test_mask_error_tau_is_the_lse_gap_and_eq8_holds():
     np.testing.assert_allclose(rel_f, 0.0, atol=1e-12)
 
 
+def test_error_terms_with_constant_values_are_the_dropped_mass():
+    """With every value vector equal to ones, o = o_s = 1, so the relative L1
+    error is 0 while Eq. 8's terms cancel: the dropped term is (1 - tau) 1 and
+    the renormalisation term (tau - 1) 1, so each relative L1 norm is the
+    block mean of 1 - tau over its real queries."""
+    wl, q, k, _ = _tiny_inputs(grid=(5, 6, 7), heads=2, d=16, seed=9)
+    g = O.Geometry(*wl.grid)
+    qc, kc_ = (O.reorder(x, g) for x in (q, k))
+    vc = O.reorder(np.ones(q.shape), g)
+    m = O.build_mask(qc, kc_, g, 0.2, 0.3)
+    tau, rel = O.mask_error(qc, kc_, vc, m.lut, m.counts, g)
+    drop, ren = O.error_terms(qc, kc_, vc, m.lut, m.counts, g)
+    real = O.real_slots(g)
+    np.testing.assert_allclose(rel, 0.0, atol=1e-12)
+    for h in range(2):
+        for i in range(g.nblk):
+            rows = np.arange(64 * i, 64 * i + 64)
+            want = (1.0 - tau[0, h, rows[real[rows]]]).mean()
+            assert drop[0, h, i] == pytest.approx(want, rel=1e-10, abs=1e-13)
+            assert ren[0, h, i] == pytest.approx(want, rel=1e-10, abs=1e-13)
+
+
+def test_error_terms_bound_the_error_and_vanish_when_all_kept():
+    """|o - o_s| = |e_drop + e_ren| <= |e_drop| + |e_ren| per entry (Eq. 8), so
+    the relative L1 error never exceeds the sum of the two terms; keeping
+    every block zeroes both."""
+    wl, q, k, v = _tiny_inputs(grid=(5, 6, 7), heads=2, d=16, seed=13)
+    g = O.Geometry(*wl.grid)
+    qc, kc_, vc = (O.reorder(x, g) for x in (q, k, v))
+    m = O.build_mask(qc, kc_, g, 0.2, 0.2)
+    _, rel = O.mask_error(qc, kc_, vc, m.lut, m.counts, g)
+    drop, ren = O.error_terms(qc, kc_, vc, m.lut, m.counts, g)
+    assert np.all(drop > 0) and np.all(ren > 0)          # every row drops some mass here
+    assert np.all(rel <= drop + ren + 1e-12)
+    full = O.build_mask(qc, kc_, g, 1.0, 0.0)
+    drop_f, ren_f = O.error_terms(qc, kc_, vc, full.lut, full.counts, g)
+    np.testing.assert_allclose(drop_f, 0.0, atol=1e-13)
+    np.testing.assert_allclose(ren_f, 0.0, atol=1e-12)
+
+
+def test_mask_report_closed_forms():
+    """Density = kept pairs / nblk^2; a row of equal scores has sink mass 1/n
+    and entropy ln n; a row held by block 0 has sink mass near 1 and entropy
+    near 0; on random rows the entropy equals scipy's."""
+    n = 12
+    s = np.zeros((2, 3, n, n))
+    counts = np.zeros((2, 3, n), dtype=np.int32)
+    counts[0, 0] = 3
+    counts[1, 2, :5] = n
+    dens, sink, ent = O.mask_report(s, counts)
+    assert dens.shape == (2, 3)
+    assert dens[0, 0] == pytest.approx(3 * n / n ** 2) and dens[1, 2] == pytest.approx(5 * n / n ** 2)
+    assert dens[0, 1] == 0.0
+    np.testing.assert_allclose(sink, 1.0 / n, rtol=1e-14)
+    np.testing.assert_allclose(ent, math.log(n), rtol=1e-14)
+    a = 40.0
+    s2 = np.zeros((1, 1, n, n))
+    s2[..., 0] = a                                     # every row's mass on block 0
+    _, sink2, ent2 = O.mask_report(s2, np.zeros((1, 1, n), dtype=np.int32))
+    z = math.exp(a) + (n - 1)
+    p0, p1 = math.exp(a) / z, 1.0 / z
+    assert sink2[0, 0] == pytest.approx(p0, rel=1e-14)
+    assert ent2[0, 0] == pytest.approx(-p0 * math.log(p0) - (n - 1) * p1 * math.log(p1), rel=1e-9)
+    rng = np.random.default_rng(91)
+    s3 = rng.standard_normal((1, 2, n, n)) * 2.0
+    _, sink3, ent3 = O.mask_report(s3, np.zeros((1, 2, n), dtype=np.int32))
+    import scipy.stats
+    p3 = scipy.special.softmax(s3, axis=-1)
+    np.testing.assert_allclose(ent3, scipy.stats.entropy(p3, axis=-1).mean(axis=-1), rtol=1e-12)
+    np.testing.assert_allclose(sink3, p3[..., 0].mean(axis=-1), rtol=1e-12)
+
+
 def test_pooled_mass_closed_forms():
     rng = np.random.default_rng(51)
     s = rng.standard_normal((2, 3, 9, 9))
@@ -869,6 +1069,34 @@ def test_per_sequence_closed_forms():
     assert O.sequence_budget(1440, 1440, 0.03) == 1440 * 44
 
 
+def test_per_sequence_near_tie_flags():
+    """Rows are flagged only when the last winning probability of the head's
+    budget is (nearly) equal to the first losing one, and then exactly the
+    rows holding an entry at that value."""
+    s = np.array([[0.0, -1.0, -2.0],          # rows 0 and 1 equal: cross-row ties
+                  [0.0, -1.0, -2.0],
+                  [3.0, -5.0, -6.0],          # one clear leader
+                  [0.0, -0.5, -9.0]])
+    p = O.block_softmax(s)
+    order = np.sort(p.reshape(-1))[::-1]
+    assert order[1] == order[2]                          # rows 0 and 1 lead ties
+    none = [False] * 4
+    assert O.per_sequence_near_tie(s, 0).tolist() == none
+    assert O.per_sequence_near_tie(s, s.size).tolist() == none
+    assert O.per_sequence_near_tie(s, 1).tolist() == none          # p[2, 0] is far ahead
+    assert O.per_sequence_near_tie(s, 2).tolist() == [True, True, False, False]
+    assert O.per_sequence_near_tie(s, 3).tolist() == none          # 0.665 against 0.62
+    k6 = int(np.nonzero(np.isclose(order, p[0, 1]))[0][0]) + 1     # budget ending on p[0, 1]
+    assert O.per_sequence_near_tie(s, k6).tolist() == [True, True, False, False]
+    # near-equal across rows: a relative gap of 1e-9 is a near tie, 1e-4 is not
+    for gap, want in ((1e-9, [True, True, False, False]), (1e-4, none)):
+        s2 = s.copy()
+        s2[1, 1:] -= math.log1p(gap)     # row 1's leader gains a relative gap over row 0's
+        assert O.per_sequence_near_tie(s2, 2).tolist() == want, gap
+    # the per-row counts on the tie follow the lower row-major index
+    assert O.per_sequence_counts(s, 2).tolist() == [1, 0, 1, 0]
+
+
 def test_build_mask_per_sequence_total_and_rows():
     g = O.Geometry(4, 12, 12)
     rng = np.random.default_rng(76)
@@ -913,6 +1141,12 @@ def test_ideal_block_mass_rows_closed_forms_and_tau():
 
 
 def test_mask_recall_cases():
+    # three rows of four blocks, counts 1 and 3: recall divides by the row's count
+    mass3 = np.array([[[[0.1, 0.4, 0.2, 0.3], [0.1, 0.4, 0.2, 0.3], [0.1, 0.4, 0.2, 0.3]]]])
+    lut3 = np.array([[[[3, -1, -1, -1], [0, 1, 3, -1], [1, -1, -1, -1]]]], dtype=np.int32)
+    counts3 = np.array([[[1, 3, 1]]], dtype=np.int32)
+    # top-1 = {1}: row 0 misses it (0); top-3 = {1, 3, 2}: row 1 holds 2 of 3; row 2 holds it
+    np.testing.assert_allclose(O.mask_recall(mass3, lut3, counts3), [[[0.0, 2.0 / 3.0, 1.0]]])
     mass = np.array([[[[0.1, 0.4, 0.2, 0.3], [0.25, 0.25, 0.25, 0.25]]]])
     lut = np.array([[[[1, 3, -1, -1], [0, 3, -1, -1]]]], dtype=np.int32)
     counts = np.array([[[2, 2]]], dtype=np.int32)
