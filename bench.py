@@ -45,9 +45,14 @@ FWD_SOURCES = ("block_sparse_attention_hybrid_amd/csrc/fwd.hip", "block_sparse_a
                "block_sparse_attention_hybrid_amd/csrc/sa_launch.h", "block_sparse_attention_hybrid_amd/csrc/sa_rowmap.h",
                "block_sparse_attention_hybrid_amd/build.py")
 
-# name -> (synthetic workload id, k_frac, p, row budgets?)
+# name -> (synthetic workload id, k_frac, p, row budgets?).  The p of the
+# hybrid95 and 97 workloads is the oracle-calibrated Top-p threshold that
+# realises 95.0% / 97.0% block sparsity with the pages' Top-k fraction
+# (python -m oracle.calibrate --workload 2 --k-frac 0.03 --sparsity 0.95, and
+# --workload 3 --k-frac 0.02 --sparsity 0.97)
 WORKLOADS = {
     "720p-hybrid95": (2, 0.03, 0.073, False),
+    "720p-97": (3, 0.02, 0.052, False),
     "720p-literal": (2, 0.03, 0.85, False),
     "720p-extreme": (3, 0.02, 0.8, False),
     "720p-varbudget": (4, 0.0, 0.0, True),

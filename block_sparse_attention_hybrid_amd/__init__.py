@@ -37,7 +37,8 @@ EXPORTED = (
     "sparse_attn_build_mask", "sparse_attn_fwd_workspace_bytes", "sparse_attn_fwd",
     "sparse_attn_coarse", "sparse_attn_router_pool", "sparse_attn_router_scores",
     "sparse_attn_bwd_delta", "sparse_attn_transpose_workspace_bytes", "sparse_attn_transpose_lut",
-    "sparse_attn_bwd", "sparse_attn_pooled_mass", "sparse_attn_mask_error", "sparse_attn_attention",
+    "sparse_attn_bwd", "sparse_attn_pooled_mass", "sparse_attn_mask_error", "sparse_attn_mask_error_terms",
+    "sparse_attn_attention",
     "sparse_attn_mask_groups_workspace_bytes", "sparse_attn_build_mask_groups", "sparse_attn_fwd_groups",
     "sparse_attn_sequence_workspace_bytes", "sparse_attn_select_per_sequence",
     "sparse_attn_ideal_block_mass", "sparse_attn_recall_workspace_bytes", "sparse_attn_mask_recall",
@@ -110,6 +111,7 @@ _SIGS = {
     "sparse_attn_bwd": (_i32, [ctypes.POINTER(BwdArgs), _GP, _f32, _vp, _vp, _vp, _vp]),
     "sparse_attn_pooled_mass": (_i32, [_vp, _vp, _vp, _i32, _GP, _vp, _vp]),
     "sparse_attn_mask_error": (_i32, [_vp, _vp, _vp, _vp, _GP, _vp, _vp, _vp]),
+    "sparse_attn_mask_error_terms": (_i32, [_vp, _vp, _vp, _vp, _GP, _vp, _vp, _vp, _vp, _vp]),
     "sparse_attn_attention": (_i32, [ctypes.POINTER(PathBuffers), _GP, _f64, _f64, _f32, _i32, _vp, _vp]),
     "sparse_attn_mask_groups_workspace_bytes": (_sz, [_GP, _i32]),
     "sparse_attn_build_mask_groups": (_i32, [_vp, _vp, _GP, _i32, _f64, _f64, _vp, _vp, _i32, _vp, _sz, _vp]),
@@ -124,13 +126,14 @@ _SIGS = {
 
 
 def lib() -> ctypes.CDLL:
-    """The loaded library (built on first use if it has never been built)."""
+    """The loaded library, built first when it is missing or older than the
+    sources (its recorded source digest no longer matches)."""
     global _lib
     if _lib is None:
         with _lock:
             if _lib is None:
-                if not os.path.exists(LIB_PATH):
-                    from . import build as _build
+                from . import build as _build
+                if not _build.is_current():
                     _build.build()
                 handle = ctypes.CDLL(LIB_PATH)
                 for name, (res, args) in _SIGS.items():
@@ -311,6 +314,17 @@ def sparse_attn_mask_error(lse_s, lse_d, oc_s, oc_d, g: Geom, tau, rel_l1, strea
                                         _ptr(oc_s, torch.bfloat16, "oc_s"), _ptr(oc_d, torch.bfloat16, "oc_d"),
                                         ctypes.byref(g), _ptr(tau, torch.float32, "tau"),
                                         _ptr(rel_l1, torch.float32, "rel_l1"), _stream(stream, lse_s)))
+
+
+def sparse_attn_mask_error_terms(lse_s, lse_d, oc_s, oc_d, g: Geom, tau, rel_l1, rel_drop, rel_ren,
+                                 stream=None) -> None:
+    _check(lib().sparse_attn_mask_error_terms(_ptr(lse_s, torch.float32, "lse_s"),
+                                              _ptr(lse_d, torch.float32, "lse_d"),
+                                              _ptr(oc_s, torch.bfloat16, "oc_s"), _ptr(oc_d, torch.bfloat16, "oc_d"),
+                                              ctypes.byref(g), _ptr(tau, torch.float32, "tau"),
+                                              _ptr(rel_l1, torch.float32, "rel_l1"),
+                                              _ptr(rel_drop, torch.float32, "rel_drop"),
+                                              _ptr(rel_ren, torch.float32, "rel_ren"), _stream(stream, lse_s)))
 
 
 def sparse_attn_attention(buffers: PathBuffers, g: Geom, k_frac: float, p: float, scale: float = 0.0,
@@ -568,11 +582,13 @@ def backward(q, k, v, do, oc, lse_c, lut, counts, g: Geom, scale: float = 0.0, s
     return dq, dk, dv
 
 
-def mask_quality(qc, kc, vc, lut, counts, scores, g: Geom, stream=None):
+def mask_quality(qc, kc, vc, lut, counts, scores, g: Geom, stream=None, terms=False):
     """Diagnostics of a kept-block mask: pooled mass per row (from the scores
     the mask was selected on), retained attention mass tau per query and the
     relative L1 error per query block against dense attention (run here with
-    every block kept).  Returns (mass, tau, rel_l1)."""
+    every block kept).  Returns (mass, tau, rel_l1), and with terms=True also
+    Eq. 8's dropped and renormalisation terms per query block:
+    (mass, tau, rel_l1, rel_drop, rel_ren)."""
     nblk, _, n_pad = sparse_attn_geometry(g)
     mass = _empty((g.batch, g.heads, nblk), torch.float64, qc)
     sparse_attn_pooled_mass(scores, lut, counts, lut.shape[-1], g, mass, stream)
@@ -583,6 +599,10 @@ def mask_quality(qc, kc, vc, lut, counts, scores, g: Geom, stream=None):
     oc_d, lse_d = fwd(qc, kc, vc, full, full_counts, g, stream=stream)
     tau = _empty((g.batch, g.heads, n_pad), torch.float32, qc)
     rel = _empty((g.batch, g.heads, nblk), torch.float32, qc)
+    if terms:
+        drop, ren = _empty((g.batch, g.heads, nblk), torch.float32, qc), _empty((g.batch, g.heads, nblk), torch.float32, qc)
+        sparse_attn_mask_error_terms(lse_s, lse_d, oc_s, oc_d, g, tau, rel, drop, ren, stream)
+        return mass, tau, rel, drop, ren
     sparse_attn_mask_error(lse_s, lse_d, oc_s, oc_d, g, tau, rel, stream)
     return mass, tau, rel
 

@@ -8,6 +8,7 @@ disabled, then linked into one shared library next to this file.
 from __future__ import annotations
 
 import concurrent.futures as cf
+import hashlib
 import os
 import shutil
 import subprocess
@@ -18,6 +19,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsparse_attn.so")
+# sha256 of the sources, headers and flags the library was built from, written
+# beside it by build(); the binding rebuilds when it no longer matches
+STAMP = LIB + ".sha256"
 ARCH = "gfx950"
 
 # -amdgpu-mfma-vgpr-form: matrix-core accumulators live in VGPRs, which lets
@@ -40,6 +44,25 @@ def sources():
     return [os.path.join(CSRC, f) for f in names]
 
 
+def source_digest() -> str:
+    """sha256 over every source and header of the library and the flags."""
+    h = hashlib.sha256(" ".join(COMMON).encode())
+    names = sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp", ".h")))
+    for path in [os.path.join(CSRC, f) for f in names] + [os.path.join(INCLUDE, "sparse_attn.h")]:
+        h.update(os.path.basename(path).encode())
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def is_current() -> bool:
+    """True when the built library exists and was built from the present sources."""
+    if not (os.path.exists(LIB) and os.path.exists(STAMP)):
+        return False
+    with open(STAMP) as f:
+        return f.read().strip() == source_digest()
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(OBJ, os.path.basename(src) + ".o")
     cmd = [_hipcc(), "-c", src, "-o", obj] + COMMON
@@ -57,6 +80,7 @@ def _compile(src: str, verbose: bool) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(OBJ, exist_ok=True)
+    digest = source_digest()
     srcs = sources()
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
@@ -66,6 +90,9 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB)
+    with open(STAMP + ".tmp", "w") as f:
+        f.write(digest + "\n")
+    os.replace(STAMP + ".tmp", STAMP)
     return LIB
 
 

@@ -142,6 +142,10 @@ size_t mask_groups_ws_bytes(const sa::Geom& d, int qgroup) {
 
 }  // namespace
 
+int32_t sa_validate_build_mask(const void* qc, const void* kc, const sa_geom* g, int32_t block, double k_frac,
+                               double p, const int32_t* row_budget, const int32_t* lut, const int32_t* counts,
+                               int32_t cap, sa::Geom& d, int& kcount);
+
 extern "C" {
 
 int32_t sparse_attn_geometry(const sa_geom* g, int32_t* nblk, int64_t* n_real, int64_t* n_pad) {
@@ -355,9 +359,42 @@ int32_t sparse_attn_mask_error(const float* lse_s, const float* lse_d, const voi
                     "mask_error launch");
 }
 
+int32_t sparse_attn_mask_error_terms(const float* lse_s, const float* lse_d, const void* oc_s, const void* oc_d,
+                                     const sa_geom* g, float* tau, float* rel_l1, float* rel_drop,
+                                     float* rel_ren, void* stream) {
+  sa::Geom d;
+  SA_TRY(make_geom(g, d));
+  SA_TRY(check_ptr(lse_s, 4, "lse_s"));
+  SA_TRY(check_ptr(lse_d, 4, "lse_d"));
+  SA_TRY(check_ptr(oc_s, 16, "oc_s"));
+  SA_TRY(check_ptr(oc_d, 16, "oc_d"));
+  SA_TRY(check_ptr(tau, 4, "tau"));
+  SA_TRY(check_ptr(rel_l1, 4, "rel_l1"));
+  SA_TRY(check_ptr(rel_drop, 4, "rel_drop"));
+  SA_TRY(check_ptr(rel_ren, 4, "rel_ren"));
+  return hip_status(sa::launch_mask_error(lse_s, lse_d, oc_s, oc_d, d, tau, rel_l1, (hipStream_t)stream,
+                                          rel_drop, rel_ren),
+                    "mask_error launch");
+}
+
 }  // extern "C"
 
 int32_t sa_hip_status(hipError_t e, const char* what) { return hip_status(e, what); }
+
+int32_t sa_fail(int32_t code, const char* msg) { return fail(code, "%s", msg); }
+
+// Arguments of sparse_attn_build_mask other than the workspace (shared with
+// the allocation-free form).
+int32_t sa_validate_build_mask(const void* qc, const void* kc, const sa_geom* g, int32_t block, double k_frac,
+                               double p, const int32_t* row_budget, const int32_t* lut, const int32_t* counts,
+                               int32_t cap, sa::Geom& d, int& kcount) {
+  SA_TRY(make_geom(g, d));
+  if (block != 64) return fail(SA_ERR_UNSUPPORTED, "block must be 64 (got %d)", block);
+  SA_TRY(check_ptr(qc, 16, "qc"));
+  SA_TRY(check_ptr(kc, 16, "kc"));
+  SA_TRY(check_select_args(d, k_frac, p, row_budget, lut, counts, cap, kcount));
+  return ok();
+}
 
 int32_t sa_validate_path(const sa_path_buffers* b, const sa_geom* g, double k_frac, double p, float scale,
                          int32_t head_chunk, sa::Geom& d, int& kcount, float& scale_out) {
@@ -429,12 +466,8 @@ int32_t sparse_attn_build_mask(const void* qc, const void* kc, const sa_geom* g,
                                int32_t* counts, int32_t cap, void* workspace, size_t workspace_bytes,
                                void* stream) {
   sa::Geom d;
-  SA_TRY(make_geom(g, d));
-  if (block != 64) return fail(SA_ERR_UNSUPPORTED, "block must be 64 (got %d)", block);
-  SA_TRY(check_ptr(qc, 16, "qc"));
-  SA_TRY(check_ptr(kc, 16, "kc"));
   int kcount = 0;
-  SA_TRY(check_select_args(d, k_frac, p, row_budget, lut, counts, cap, kcount));
+  SA_TRY(sa_validate_build_mask(qc, kc, g, block, k_frac, p, row_budget, lut, counts, cap, d, kcount));
   SA_TRY(check_ptr(workspace, kWsAlign, "workspace"));
   const size_t need = mask_ws_bytes(d);
   if (workspace_bytes < need)

@@ -9,7 +9,9 @@
 //     the kept real keys (the two LSEs come from sparse_attn_fwd with the
 //     kept lists and with every block kept);
 //   * relative L1 error per query block: sum |o_s - o| / sum |o| over its real
-//     queries, o from the dense run;
+//     queries, o from the dense run, and optionally Eq. 8's two terms, the
+//     dropped term (p (1 - m)) V and the renormalisation term
+//     (1 - 1/tau)(p m) V, as L1 norms relative to the same sum |o|;
 //   * ideal block scores (VSA2 section 2.2, the MeanPool of the full attention
 //     matrix a router approximates): P_ideal[i][j] = the full softmax mass that
 //     block i's real queries put on block j's real keys, averaged over those
@@ -146,12 +148,17 @@ __global__ __launch_bounds__(64) void pooled_mass_kernel(const double* __restric
   if (lane == 0) mass[row] = kept / z;
 }
 
-// One wavefront per query block, lane = slot.
+// One wavefront per query block, lane = slot.  With TERMS, Eq. 8's two terms
+// are summed as well: per query e_drop = o_d - tau o_s (the dense output of
+// the dropped keys, (p (1 - m)) V) and e_ren = (tau - 1) o_s (= (1 - 1/tau)
+// (p m) V, since (p m) V = tau o_s).
+template <bool TERMS>
 __global__ __launch_bounds__(64) void mask_error_kernel(const float* __restrict__ lse_s,
                                                         const float* __restrict__ lse_d,
                                                         const bf16* __restrict__ o_s,
                                                         const bf16* __restrict__ o_d, Geom g,
-                                                        float* __restrict__ tau, float* __restrict__ rel) {
+                                                        float* __restrict__ tau, float* __restrict__ rel,
+                                                        float* __restrict__ rel_drop, float* __restrict__ rel_ren) {
   const int i = blockIdx.x;
   const long long bh = blockIdx.y;
   const int s = threadIdx.x, d = g.d;
@@ -161,7 +168,7 @@ __global__ __launch_bounds__(64) void mask_error_kernel(const float* __restrict_
   float t = 0.f;
   if (real && ld > -INFINITY) t = ls > -INFINITY ? expf(ls - ld) : 0.f;
   tau[slot] = t;
-  double num = 0.0, den = 0.0;
+  double num = 0.0, den = 0.0, nd = 0.0, nr = 0.0;
   if (real) {
     const u32x4* a = reinterpret_cast<const u32x4*>(o_s + slot * d);
     const u32x4* b = reinterpret_cast<const u32x4*>(o_d + slot * d);
@@ -173,12 +180,27 @@ __global__ __launch_bounds__(64) void mask_error_kernel(const float* __restrict_
         const float y0 = __uint_as_float(y[e] << 16), y1 = __uint_as_float(y[e] & 0xffff0000u);
         num += (double)fabsf(x0 - y0) + (double)fabsf(x1 - y1);
         den += (double)fabsf(y0) + (double)fabsf(y1);
+        if (TERMS) {
+          const double td = (double)t;
+          nd += fabs((double)y0 - td * x0) + fabs((double)y1 - td * x1);
+          nr += (1.0 - td) * ((double)fabsf(x0) + (double)fabsf(x1));
+        }
       }
     }
   }
   num = wave_sum(num);
   den = wave_sum(den);
-  if (s == 0) rel[bh * g.nblk + i] = den > 0.0 ? (float)(num / den) : 0.f;
+  if (TERMS) {
+    nd = wave_sum(nd);
+    nr = wave_sum(nr);
+  }
+  if (s == 0) {
+    rel[bh * g.nblk + i] = den > 0.0 ? (float)(num / den) : 0.f;
+    if (TERMS) {
+      rel_drop[bh * g.nblk + i] = den > 0.0 ? (float)(nd / den) : 0.f;
+      rel_ren[bh * g.nblk + i] = den > 0.0 ? (float)(nr / den) : 0.f;
+    }
+  }
 }
 
 }  // namespace
@@ -191,10 +213,15 @@ hipError_t launch_pooled_mass(const double* scores, const int32_t* lut, const in
 }
 
 hipError_t launch_mask_error(const float* lse_s, const float* lse_d, const void* o_s, const void* o_d,
-                             const Geom& g, float* tau, float* rel, hipStream_t s) {
+                             const Geom& g, float* tau, float* rel, hipStream_t s, float* rel_drop,
+                             float* rel_ren) {
   dim3 grid(g.nblk, g.batch * g.heads);
-  mask_error_kernel<<<grid, 64, 0, s>>>(lse_s, lse_d, static_cast<const bf16*>(o_s), static_cast<const bf16*>(o_d),
-                                        g, tau, rel);
+  const bf16* os = static_cast<const bf16*>(o_s);
+  const bf16* od = static_cast<const bf16*>(o_d);
+  if (rel_drop != nullptr)
+    mask_error_kernel<true><<<grid, 64, 0, s>>>(lse_s, lse_d, os, od, g, tau, rel, rel_drop, rel_ren);
+  else
+    mask_error_kernel<false><<<grid, 64, 0, s>>>(lse_s, lse_d, os, od, g, tau, rel, nullptr, nullptr);
   return hipGetLastError();
 }
 

@@ -56,8 +56,10 @@ hipError_t launch_transpose_lut(const int32_t* lut, const int32_t* counts, int c
 hipError_t launch_bwd(const BwdArgs& a, const Geom& g, float scale, void* dq, void* dk, void* dv, hipStream_t s);
 hipError_t launch_pooled_mass(const double* scores, const int32_t* lut, const int32_t* counts, int cap,
                               const Geom& g, double* mass, hipStream_t s);
+// rel_drop, rel_ren: Eq. 8's two terms per query block (both NULL: not computed)
 hipError_t launch_mask_error(const float* lse_s, const float* lse_d, const void* o_s, const void* o_d,
-                             const Geom& g, float* tau, float* rel, hipStream_t s);
+                             const Geom& g, float* tau, float* rel, hipStream_t s, float* rel_drop = nullptr,
+                             float* rel_ren = nullptr);
 // Per-sequence Top-K: per-row counts of the head-wide budget `total` over the
 // row-softmax of block scores, written to a region of the workspace
 // (*budget_out, [batch*heads*nblk] int32).

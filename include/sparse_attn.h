@@ -343,6 +343,20 @@ int32_t sparse_attn_mask_error(const float* lse_s, const float* lse_d,
                                const sa_geom* g, float* tau, float* rel_l1,
                                void* stream);
 
+/* sparse_attn_mask_error plus the two terms of [SA2] Eq. 8 ("The Sparse
+ * Attention Error Decomposition"), o - o_s = (p(1 - m) + (1 - 1/tau)(p m))V:
+ * per query the dropped term (p(1 - m))V = o_d - tau o_s and the
+ * renormalisation term (1 - 1/tau)(p m)V = (tau - 1) o_s, each summed in L1
+ * over the block's real queries and the head_dim channels and divided by
+ * sum |o_d| (0 for a block whose dense output is all zero).
+ *   inputs, tau, rel_l1 as for sparse_attn_mask_error
+ *   rel_drop, rel_ren [batch, heads, nblk] float32                     (outputs) */
+int32_t sparse_attn_mask_error_terms(const float* lse_s, const float* lse_d,
+                                     const void* oc_s, const void* oc_d,
+                                     const sa_geom* g, float* tau,
+                                     float* rel_l1, float* rel_drop,
+                                     float* rel_ren, void* stream);
+
 /* Hybrid Top-k U Top-p selection, [SA2] "The Hybrid Top-k+Top-p Masking Rule"
  * (Eq. 9), producing index lists as [VSA] "Kernel Implementation" describes
  * (contiguous block ids, not a binary mask).

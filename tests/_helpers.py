@@ -104,9 +104,23 @@ def compare_lists(lut: np.ndarray, counts: np.ndarray, ref: O.MaskResult, p: flo
     return bad, near, invalid
 
 
-def attn_errors(o_gpu: np.ndarray, o_ref: np.ndarray):
+def attn_errors(o_gpu: np.ndarray, o_ref: np.ndarray, real=None):
+    """Max and mean absolute error of O.  For cube-major outputs pass `real`,
+    the boolean real-slot mask of the slot axis (second to last): the errors,
+    the mean in particular, are then taken over real slots only, since pad
+    slots hold exact zeros on both sides and would dilute the mean."""
+    if real is not None:
+        o_gpu, o_ref = o_gpu[..., real, :], o_ref[..., real, :]
     d = np.abs(o_gpu - o_ref)
     return float(d.max()), float(d.mean())
+
+
+def grad_errors(got: np.ndarray, want: np.ndarray, real: np.ndarray):
+    """Max and mean absolute gradient error over the real slots of cube-major
+    gradients [..., n_pad, d], and the largest |gradient| (the relative bar's
+    scale)."""
+    err = np.abs(got[..., real, :] - want[..., real, :])
+    return float(err.max()), float(err.mean()), max(float(np.abs(want).max()), 1e-30)
 
 
 def lse_errors(l_gpu: np.ndarray, l_ref: np.ndarray):
