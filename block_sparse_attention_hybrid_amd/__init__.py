@@ -42,6 +42,7 @@ EXPORTED = (
     "sparse_attn_mask_groups_workspace_bytes", "sparse_attn_build_mask_groups", "sparse_attn_fwd_groups",
     "sparse_attn_sequence_workspace_bytes", "sparse_attn_select_per_sequence",
     "sparse_attn_ideal_block_mass", "sparse_attn_recall_workspace_bytes", "sparse_attn_mask_recall",
+    "sparse_attn_build_mask_noalloc_scratch_bytes", "sparse_attn_build_mask_noalloc",
     "sparse_attn_last_error",
 )
 
@@ -121,6 +122,8 @@ _SIGS = {
     "sparse_attn_ideal_block_mass": (_i32, [_vp, _vp, _vp, _GP, _f32, _vp, _vp]),
     "sparse_attn_recall_workspace_bytes": (_sz, [_GP]),
     "sparse_attn_mask_recall": (_i32, [_vp, _vp, _vp, _i32, _GP, _vp, _vp, _sz, _vp]),
+    "sparse_attn_build_mask_noalloc_scratch_bytes": (_sz, []),
+    "sparse_attn_build_mask_noalloc": (_i32, [_vp, _vp, _GP, _i32, _f64, _f64, _vp, _vp, _vp, _i32, _vp]),
     "sparse_attn_last_error": (ctypes.c_char_p, []),
 }
 
@@ -236,6 +239,19 @@ def sparse_attn_build_mask(qc, kc, g: Geom, block: int, k_frac: float, p: float,
                                         _ptr(lut, torch.int32, "lut"), _ptr(counts, torch.int32, "counts"),
                                         int(cap), _ptr(workspace, None, "workspace"), ws_bytes,
                                         _stream(stream, qc)))
+
+
+def sparse_attn_build_mask_noalloc_scratch_bytes() -> int:
+    return int(lib().sparse_attn_build_mask_noalloc_scratch_bytes())
+
+
+def sparse_attn_build_mask_noalloc(qc, kc, g: Geom, block: int, k_frac: float, p: float, row_budget,
+                                   lut, counts, cap: int, stream=None) -> None:
+    _check(lib().sparse_attn_build_mask_noalloc(_ptr(qc, torch.bfloat16, "qc"), _ptr(kc, torch.bfloat16, "kc"),
+                                                ctypes.byref(g), int(block), float(k_frac), float(p),
+                                                _ptr(row_budget, torch.int32, "row_budget"),
+                                                _ptr(lut, torch.int32, "lut"), _ptr(counts, torch.int32, "counts"),
+                                                int(cap), _stream(stream, qc)))
 
 
 def sparse_attn_fwd_workspace_bytes(g: Geom) -> int:

@@ -397,6 +397,26 @@ int32_t sparse_attn_build_mask(const void* qc, const void* kc,
                                void* workspace, size_t workspace_bytes,
                                void* stream);
 
+/* sparse_attn_build_mask for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments without the workspace, the same lists and
+ * counts.  The float64 block means and scores live in a device array of the
+ * library, fixed at sparse_attn_build_mask_noalloc_scratch_bytes() (64 MiB)
+ * per GPU and held until the process ends; the (batch, head) rows are taken
+ * in chunks that fit it, one after another on `stream`.  One (batch, head)
+ * needs 2*round256(nblk*head_dim*8) + round256(nblk*nblk*8) bytes; above the
+ * array's size (nblk above about 2,700 at head_dim 128) the call returns
+ * SA_ERR_CAPACITY and launches nothing.  The call allocates and frees
+ * nothing.  Calls on one GPU share the array: calls that overlap (other
+ * streams, other host threads) race and must be ordered by the caller. */
+size_t sparse_attn_build_mask_noalloc_scratch_bytes(void);
+int32_t sparse_attn_build_mask_noalloc(const void* qc, const void* kc,
+                                       const sa_geom* g, int32_t block,
+                                       double k_frac, double p,
+                                       const int32_t* row_budget,
+                                       int32_t* lut, int32_t* counts,
+                                       int32_t cap, void* stream);
+
 /* Bytes of workspace sparse_attn_fwd needs (its row schedule). */
 size_t sparse_attn_fwd_workspace_bytes(const sa_geom* g);
 

@@ -259,3 +259,24 @@ def test_fused_forward_argument_rules():
         sa.SA_ERR_INVALID_ARG
     assert lib.sparse_attn_fwd_tokens(FAKE, FAKE, FAKE, FAKE, FAKE, 16, None, 0.0, O_, FAKE, None) == \
         sa.SA_ERR_INVALID_ARG                                          # no geometry
+
+
+def test_noalloc_mask_rejects_before_any_launch():
+    """The allocation-free mask call validates like sparse_attn_build_mask and
+    refuses a (batch, head) whose means and scores exceed its fixed scratch
+    array, all before touching the device."""
+    lib = sa.lib()
+    assert lib.sparse_attn_build_mask_noalloc_scratch_bytes() == 64 << 20
+    g = geom(frames=16, height=128, width=128, head_dim=128)           # 4096 blocks: 142 MB per head
+    assert sa.sparse_attn_geometry(g)[0] == 4096
+    rc = lib.sparse_attn_build_mask_noalloc(FAKE, FAKE, ctypes.byref(g), 64, ctypes.c_double(0.03),
+                                            ctypes.c_double(0.5), None, FAKE, FAKE, 4096, None)
+    assert rc == sa.SA_ERR_CAPACITY
+    assert "scratch" in sa.sparse_attn_last_error()
+    g2 = geom()
+    assert lib.sparse_attn_build_mask_noalloc(FAKE, FAKE, ctypes.byref(g2), 32, ctypes.c_double(0.03),
+                                              ctypes.c_double(0.5), None, FAKE, FAKE, 16, None) == sa.SA_ERR_UNSUPPORTED
+    assert lib.sparse_attn_build_mask_noalloc(FAKE, FAKE, ctypes.byref(g2), 64, ctypes.c_double(0.03),
+                                              ctypes.c_double(0.5), None, FAKE, FAKE, 8, None) == sa.SA_ERR_CAPACITY
+    assert lib.sparse_attn_build_mask_noalloc(FAKE_MISALIGNED, FAKE, ctypes.byref(g2), 64, ctypes.c_double(0.03),
+                                              ctypes.c_double(0.5), None, FAKE, FAKE, 16, None) == sa.SA_ERR_INVALID_ARG
