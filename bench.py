@@ -82,6 +82,8 @@ def parse():
                          "next (-1: one chunk); 0 uses one stream")
     ap.add_argument("--no-next-rows", action="store_true",
                     help="skip timing the coarse-output and router kernels")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the forward timings on the other workloads")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
     return ap.parse_args()
@@ -135,8 +137,10 @@ class Path:
                               sa.sparse_attn_select(self.scores, g, self.k_frac, self.p, self.rb, self.lut,
                                                     self.counts, self.cap))),
             # the forward with the inverse re-indexing fused (O and LSE in token order)
+            # (the count-balanced row order where per-row budgets are given, as the whole-path call does)
             ("fwd", lambda: sa.sparse_attn_fwd_tokens(self.qc, self.kc, self.vc, self.lut, self.counts, self.cap,
-                                                      g, 0.0, self.o, self.lse)),
+                                                      g, 0.0, self.o, self.lse,
+                                                      self.fws if self.rb is not None else None)),
         ]
 
     def step(self):
@@ -178,8 +182,24 @@ def recorded_traffic(workload):
     return int(float(vals["traffic_bytes_per_launch"]))
 
 
+def min_bytes(path):
+    """The least HBM traffic of the mask path (per step), independent of how
+    it is built: Q, K and V each read once in token order and written once in
+    cube order (the pooling fused into that read), the block scores written
+    once and read once at float32 size, and the lists (counts and kept ids)
+    written once."""
+    wl = path.wl
+    B, H, d, n = wl.batch, wl.heads, wl.head_dim, path.nblk
+    tok = 2 * d
+    kept = int(path.counts.sum().item())
+    return {"reorder": B * H * 3 * (path.n_real + path.n_pad) * tok,
+            "mask": B * H * (n * n * 4 * 2 + n * 4) + kept * 4}
+
+
 def algorithmic_bytes(path):
-    """HBM bytes each stage must move at minimum (per step)."""
+    """HBM bytes each stage of this implementation moves at minimum (per
+    step): as min_bytes, plus the float64 block means written by the
+    re-indexing and read by the scores, and the scores at float64 size."""
     wl = path.wl
     B, H, d, n = wl.batch, wl.heads, wl.head_dim, path.nblk
     real, pad = path.n_real, path.n_pad
@@ -337,61 +357,114 @@ def machine_check(dev):
             "note": "1 GiB device copy (bytes read + written); 8192^3 bf16 torch.matmul"}
 
 
-def cpu_baseline(path, seconds):
-    """The oracle, as it stands, on a bounded sample of the same workload:
-    the mask of whole heads (pool, scores, selection of every row) and the
-    attention of sampled query blocks of those heads."""
+def _oracle_worker(task):
+    """One worker of the CPU baseline: the oracle's mask of one whole head,
+    then its attention on the head's query blocks (in a seeded random order)
+    until `seconds` have passed.  Returns (mask seconds, attention seconds,
+    flops, query blocks done)."""
+    wid, k_frac, p, budgets, h, seconds = task
     import oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
-    wl = path.wl
+    wl = synth.WORKLOADS[wid]
     og = O.Geometry(wl.frames, wl.height, wl.width)
-    kc_rows = O.ceil_k(path.k_frac, og.nblk)
-    rng = np.random.default_rng(0)
-    t_mask = t_attn = 0.0
-    flops = 0.0
-    heads_done = rows_done = 0
-    heads = list(range(min(3, wl.heads)))
-    budget_each = seconds / len(heads)
-    for h in heads:
-        q, k, v = synth.head_qkv(wl, 0, h, 0)
-        qc, kc, vc = (O.reorder(t.double().numpy(), og) for t in (q, k, v))
+    q, k, v = synth.head_qkv(wl, 0, h, 0)
+    qc, kc, vc = (O.reorder(t.double().numpy(), og) for t in (q, k, v))
+    t0 = time.perf_counter()
+    s = O.block_scores(O.pool(qc, og), O.pool(kc, og), wl.head_dim)
+    if budgets:
+        rb = synth.row_budgets(wl, 0)[0, h]
+        probs = O.block_softmax(s)
+        sels = [O.select_row(s[i], int(rb[i]), 0.0, probs[i]) for i in range(og.nblk)]
+    else:
+        sels = O.select_rows(s, O.ceil_k(k_frac, og.nblk), p)
+    t_mask = time.perf_counter() - t0
+    flops, done = 0.0, 0
+    t1 = time.perf_counter()
+    for i in np.random.default_rng(h).permutation(og.nblk):
+        O.attention_block(qc, kc, vc, sels[i].kept, og, int(i))
+        flops += sels[i].kept.size * 4.0 * 64 * 64 * wl.head_dim
+        done += 1
+        if time.perf_counter() - t1 > seconds:
+            break
+    return t_mask, time.perf_counter() - t1, flops, done
+
+
+def cpu_baseline(wl, seconds, workload, workers=16):
+    """The oracle, as it stands, on a bounded sample of the same workload, on
+    `workers` host processes with one BLAS thread each: one whole head per
+    worker (its mask, then the attention of its query blocks for at most
+    `seconds`); value = oracle flops on kept blocks / the slowest worker's
+    compute time."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+    wid, k_frac, p, budgets = WORKLOADS[workload]
+    heads = list(range(min(workers, wl.heads)))
+    tasks = [(wid, k_frac, p, budgets, h, seconds) for h in heads]
+    env_keys = ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")
+    saved = {k: os.environ.get(k) for k in env_keys}
+    for k in env_keys:
+        os.environ[k] = "1"            # one thread per worker process
+    try:
         t0 = time.perf_counter()
-        s = O.block_scores(O.pool(qc, og), O.pool(kc, og), wl.head_dim)
-        if path.rb is not None:
-            rb = path.rb[0, h].cpu().numpy()
-            probs = O.block_softmax(s)
-            sels = [O.select_row(s[i], int(rb[i]), 0.0, probs[i]) for i in range(og.nblk)]
-        else:
-            sels = O.select_rows(s, kc_rows, path.p)
-        t_mask += time.perf_counter() - t0
-        heads_done += 1
-        t1 = time.perf_counter()
-        for i in rng.permutation(og.nblk):
-            O.attention_block(qc, kc, vc, sels[i].kept, og, int(i))
-            flops += sels[i].kept.size * 4.0 * 64 * 64 * wl.head_dim
-            rows_done += 1
-            if time.perf_counter() - t1 > budget_each:
-                break
-        t_attn += time.perf_counter() - t1
-    # mask time is charged pro rata to the rows whose attention was run
-    rows_per_head = og.nblk
-    charged = t_mask * rows_done / (heads_done * rows_per_head) + t_attn
+        with cf.ProcessPoolExecutor(max_workers=len(tasks), mp_context=mp.get_context("spawn")) as ex:
+            res = list(ex.map(_oracle_worker, tasks))
+        wall = time.perf_counter() - t0
+    finally:
+        for k, val in saved.items():
+            if val is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = val
+    flops = sum(r[2] for r in res)
+    done = sum(r[3] for r in res)
+    busy = max(r[0] + r[1] for r in res)    # the slowest worker (process start-up excluded)
     return {
-        "value": flops / charged / 1e12,
+        "value": flops / busy / 1e12,
         "unit": "TFLOPS",
-        "cores": int(threads),
+        "cores": len(tasks),
         "kind": "oracle",
-        "sample": (f"fp64 numpy oracle: mask of {heads_done} whole heads (pool, scores, selection "
-                   f"of {rows_per_head} rows each; {t_mask:.2f}s) and attention of {rows_done} "
-                   f"sampled query blocks of those heads ({t_attn:.2f}s); mask time charged pro "
-                   f"rata to the sampled blocks"),
-        "seconds": round(t_mask + t_attn, 2),
+        "sample": (f"fp64 numpy oracle on {len(tasks)} processes of one thread each, one whole head "
+                   f"per process: the mask of {len(heads)} heads (pool, scores, selection of every row; "
+                   f"{max(r[0] for r in res):.2f}s at most) and the attention of {done} of their "
+                   f"{len(heads) * wl.n_blocks()} query blocks (at most {seconds:.0f}s per "
+                   f"process); value = kept-block flops / the slowest process's time"),
+        "seconds": round(busy, 2),
+        "wall_seconds_with_startup": round(wall, 2),
+        "host_cpus": os.cpu_count(),
         "cpu_model": cpu_model(),
     }
+
+
+def other_workloads(dev, names, reps=3):
+    """The forward as the whole-path call runs it (token order; the
+    count-balanced row order with per-row budgets) on the other workloads,
+    each on freshly generated inputs and its GPU-built lists: time, kept-block
+    TFLOP/s and fraction of the bf16 peak.  Not part of `value`."""
+    out = {}
+    for name in names:
+        wid, k_frac, p, budgets = WORKLOADS[name]
+        wl = synth.WORKLOADS[wid]
+        g = sa.make_geom(wl.batch, wl.heads, wl.frames, wl.height, wl.width, wl.head_dim)
+        nblk, n_real, _ = sa.sparse_attn_geometry(g)
+        q, k, v = synth.make_qkv(wl, 0)
+        qc = sa.reorder(q.to(dev), g, sa.SA_LAYOUT_QK)
+        kc = sa.reorder(k.to(dev), g, sa.SA_LAYOUT_QK)
+        vc = sa.reorder(v.to(dev), g, sa.SA_LAYOUT_V)
+        del q, k, v
+        rb = torch.from_numpy(synth.row_budgets(wl, 0)).to(dev) if budgets else None
+        lut, counts = sa.build_mask(qc, kc, g, k_frac, p, row_budget=rb)
+        o = torch.empty((wl.batch, wl.heads, n_real, wl.head_dim), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((wl.batch, wl.heads, n_real), dtype=torch.float32, device=dev)
+        ws = torch.empty(sa.sparse_attn_fwd_workspace_bytes(g), dtype=torch.uint8, device=dev) if budgets else None
+        ms = time_call(lambda: sa.sparse_attn_fwd_tokens(qc, kc, vc, lut, counts, nblk, g, 0.0, o, lse, ws), reps)
+        kept = int(counts.sum().item())
+        tf = kept * 4.0 * 64 * 64 * wl.head_dim / (ms * 1e-3) / 1e12
+        out[name] = {"fwd_ms": round(ms, 3), "fwd_tflops": round(tf, 1), "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                     "block_sparsity": round(1.0 - kept / (wl.batch * wl.heads * nblk * nblk), 5),
+                     "kept_blocks": kept, "heads": wl.heads, "k_frac": k_frac, "p": p, "row_budgets": budgets}
+        log(f"[bench] {name}: fwd {ms:.3f} ms, {tf:.1f} TFLOP/s")
+        del qc, kc, vc, lut, counts, o, lse
+        torch.cuda.empty_cache()
+    return out
 
 
 def cpu_model():
@@ -459,6 +532,9 @@ def main():
     gbps = {n: abytes[n] / (stage_ms[n] * 1e-3) / 1e9 for n in abytes}
     mask_path_gbps = (abytes["reorder"] + abytes["mask"]) / (
         (stage_ms["reorder"] + stage_ms["mask"]) * 1e-3) / 1e9
+    mbytes = min_bytes(path)
+    mask_path_gbps_min = (mbytes["reorder"] + mbytes["mask"]) / (
+        (stage_ms["reorder"] + stage_ms["mask"]) * 1e-3) / 1e9
 
     if args.copy_calibration:
         x = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -502,6 +578,14 @@ def main():
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "stage_gbps": {k: round(v, 1) for k, v in gbps.items()},
         "mask_path_gbps": round(mask_path_gbps, 1),
+        "mask_path_frac_of_hbm": round(mask_path_gbps / PEAK_HBM_GBPS, 4),
+        "mask_path_gbps_min_bytes": round(mask_path_gbps_min, 1),
+        "mask_path_min_bytes_frac_of_hbm": round(mask_path_gbps_min / PEAK_HBM_GBPS, 4),
+        "mask_path_bytes": {"implementation": int(abytes["reorder"] + abytes["mask"]),
+                            "minimum": int(mbytes["reorder"] + mbytes["mask"]),
+                            "note": ("implementation: float64 means and scores as this library keeps them; "
+                                     "minimum: Q/K/V read and written once, scores float32 written and read "
+                                     "once, lists written once")},
         "roofline": {
             "bound": "mfma",
             "achieved": round(fwd_tflops, 2),
@@ -515,9 +599,14 @@ def main():
         log("[bench] timing the coarse-output and router kernels")
         out["next_rows"] = next_rows(path)
         out["machine_check"] = machine_check(dev)
+    if not args.no_other_workloads:
+        del path
+        torch.cuda.empty_cache()
+        log("[bench] timing the forward on the other workloads")
+        out["other_workloads"] = other_workloads(dev, [w for w in WORKLOADS if w != args.workload])
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
-        out["cpu_baseline"] = cpu_baseline(path, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, args.workload)
     print(json.dumps(out))
 
 

@@ -102,7 +102,7 @@ _SIGS = {
     "sparse_attn_build_mask": (_i32, [_vp, _vp, _GP, _i32, _f64, _f64, _vp, _vp, _vp, _i32, _vp, _sz, _vp]),
     "sparse_attn_fwd_workspace_bytes": (_sz, [_GP]),
     "sparse_attn_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _GP, _f32, _vp, _vp, _vp, _sz, _vp]),
-    "sparse_attn_fwd_tokens": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _GP, _f32, _vp, _vp, _vp]),
+    "sparse_attn_fwd_tokens": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _GP, _f32, _vp, _vp, _vp, _sz, _vp]),
     "sparse_attn_coarse": (_i32, [_vp, _vp, _vp, _GP, _vp]),
     "sparse_attn_router_pool": (_i32, [_vp, _vp, _GP, _i32, _i32, _i32, _vp]),
     "sparse_attn_router_scores": (_i32, [_vp, _vp, _vp, _f64, _GP, _i32, _i32, _i32, _vp]),
@@ -259,12 +259,14 @@ def sparse_attn_fwd_workspace_bytes(g: Geom) -> int:
 
 
 def sparse_attn_fwd_tokens(qc, kc, vc, lut, counts, cap: int, g: Geom, scale: float, o, lse,
-                           stream=None) -> None:
+                           workspace=None, stream=None) -> None:
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().sparse_attn_fwd_tokens(_ptr(qc, torch.bfloat16, "qc"), _ptr(kc, torch.bfloat16, "kc"),
                                         _ptr(vc, torch.bfloat16, "vc"), _ptr(lut, torch.int32, "lut"),
                                         _ptr(counts, torch.int32, "counts"), int(cap), ctypes.byref(g),
                                         float(scale), _ptr(o, torch.bfloat16, "o"),
-                                        _ptr(lse, torch.float32, "lse"), _stream(stream, qc)))
+                                        _ptr(lse, torch.float32, "lse"), _ptr(workspace, None, "workspace"),
+                                        ws_bytes, _stream(stream, qc)))
 
 
 def sparse_attn_fwd(qc, kc, vc, lut, counts, cap: int, g: Geom, scale: float, oc, lse_c,
@@ -492,7 +494,8 @@ def fwd_tokens(qc, kc, vc, lut, counts, g: Geom, scale: float = 0.0, stream=None
     _, n_real, _ = sparse_attn_geometry(g)
     o = _empty((g.batch, g.heads, n_real, g.head_dim), torch.bfloat16, qc)
     lse = _empty((g.batch, g.heads, n_real), torch.float32, qc)
-    sparse_attn_fwd_tokens(qc, kc, vc, lut, counts, lut.shape[-1], g, scale, o, lse, stream)
+    ws = torch.empty(sparse_attn_fwd_workspace_bytes(g), dtype=torch.uint8, device=qc.device)
+    sparse_attn_fwd_tokens(qc, kc, vc, lut, counts, lut.shape[-1], g, scale, o, lse, ws, stream)
     return o, lse
 
 

@@ -643,9 +643,9 @@ int32_t sparse_attn_fwd(const void* qc, const void* kc, const void* vc, const in
   if (cap < 1) return fail(SA_ERR_INVALID_ARG, "cap must be >= 1");
   if (!std::isfinite(scale)) return fail(SA_ERR_INVALID_ARG, "scale must be finite");
   if (scale <= 0.f) scale = (float)(1.0 / std::sqrt((double)d.d));
-  const size_t need = sa::fwd_workspace_bytes(d);
-  if (need > 0) {
+  if (workspace != nullptr) {
     SA_TRY(check_ptr(workspace, kWsAlign, "workspace"));
+    const size_t need = sa::fwd_workspace_bytes(d);
     if (workspace_bytes < need)
       return fail(SA_ERR_CAPACITY, "workspace of %zu bytes is below the %zu needed", workspace_bytes, need);
   }
@@ -656,7 +656,7 @@ int32_t sparse_attn_fwd(const void* qc, const void* kc, const void* vc, const in
 
 int32_t sparse_attn_fwd_tokens(const void* qc, const void* kc, const void* vc, const int32_t* lut,
                                const int32_t* counts, int32_t cap, const sa_geom* g, float scale, void* o,
-                               float* lse, void* stream) {
+                               float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   sa::Geom d;
   SA_TRY(make_geom(g, d));
   SA_TRY(check_ptr(qc, 16, "qc"));
@@ -669,7 +669,14 @@ int32_t sparse_attn_fwd_tokens(const void* qc, const void* kc, const void* vc, c
   if (cap < 1) return fail(SA_ERR_INVALID_ARG, "cap must be >= 1");
   if (!std::isfinite(scale)) return fail(SA_ERR_INVALID_ARG, "scale must be finite");
   if (scale <= 0.f) scale = (float)(1.0 / std::sqrt((double)d.d));
-  return hip_status(sa::launch_fwd_tokens(qc, kc, vc, lut, counts, cap, d, scale, o, lse, (hipStream_t)stream),
+  if (workspace != nullptr) {
+    SA_TRY(check_ptr(workspace, kWsAlign, "workspace"));
+    const size_t need = sa::fwd_workspace_bytes(d);
+    if (workspace_bytes < need)
+      return fail(SA_ERR_CAPACITY, "workspace of %zu bytes is below the %zu needed", workspace_bytes, need);
+  }
+  return hip_status(sa::launch_fwd_tokens(qc, kc, vc, lut, counts, cap, d, scale, o, lse, (hipStream_t)stream,
+                                          workspace),
                     "fwd launch");
 }
 

@@ -84,24 +84,17 @@ struct CubeDiv {
 // TOK = false: O and LSE slot-major (oc [.., n_pad, D], lse_c [.., n_pad]);
 // TOK = true: straight to token order (o [.., N, D], lse [.., N]), pad slots
 // not written -- the inverse re-indexing fused into the epilogue.
+// One query block (row of batch*heads*nblk) of the forward, by one wavefront.
 template <int D, bool TOK>
-__global__ __launch_bounds__(64) void fwd_kernel(const u32x4* __restrict__ qc,
-                                                 const u32x4* __restrict__ kc,
-                                                 const u32x4* __restrict__ vc,
-                                                 const int32_t* __restrict__ lut,
-                                                 const int32_t* __restrict__ counts, int cap, Geom g,
-                                                 float sc_log2, bf16* __restrict__ oc,
-                                                 float* __restrict__ lse_c, RowMap map, CubeDiv cd,
-                                                 int qg_shift) {
+__device__ __forceinline__ void fwd_row(int row, const u32x4* __restrict__ qc, const u32x4* __restrict__ kc,
+                                        const u32x4* __restrict__ vc, const int32_t* __restrict__ lut,
+                                        const int32_t* __restrict__ counts, int cap, const Geom& g,
+                                        float sc_log2, bf16* __restrict__ oc, float* __restrict__ lse_c,
+                                        const CubeDiv& cd, int qg_shift) {
   constexpr int NDS = D / 16;     // 16-dim steps of S^T
   constexpr int NDT = D / 32;     // 32-dim tiles of O^T
   constexpr int BLK = 64 * D / 8; // 16-byte units per block
 
-  // workgroups are dispatched round-robin over the 8 XCDs; give each XCD a
-  // contiguous run of rows so neighbouring query blocks (overlapping lists)
-  // share K/V tiles in that XCD's L2
-  const int row = row_of_workgroup(blockIdx.x, map);
-  if (row < 0) return;
   const long long bh = row / g.nblk;
   const int i = row - (int)(bh * g.nblk);
 
@@ -396,40 +389,159 @@ __global__ __launch_bounds__(64) void fwd_kernel(const u32x4* __restrict__ qc,
   }
 }
 
+// One workgroup per row: workgroups are dispatched round-robin over the 8
+// XCDs, and the row map gives each XCD a contiguous run of rows so
+// neighbouring query blocks (overlapping lists) share K/V tiles in its L2.
+// With `order` (written by fwd_sched_kernel), workgroup w runs row
+// order[(w % 8) * per_xcd + w / 8] instead.
+template <int D, bool TOK>
+__global__ __launch_bounds__(64) void fwd_kernel(const u32x4* __restrict__ qc, const u32x4* __restrict__ kc,
+                                                 const u32x4* __restrict__ vc, const int32_t* __restrict__ lut,
+                                                 const int32_t* __restrict__ counts, int cap, Geom g,
+                                                 float sc_log2, bf16* __restrict__ oc, float* __restrict__ lse_c,
+                                                 RowMap map, CubeDiv cd, int qg_shift,
+                                                 const int32_t* __restrict__ order) {
+  const int row = order != nullptr
+                      ? order[(long long)(blockIdx.x % kXcds) * map.per_xcd + blockIdx.x / kXcds]
+                      : row_of_workgroup(blockIdx.x, map);
+  if (row < 0) return;
+  fwd_row<D, TOK>(row, qc, kc, vc, lut, counts, cap, g, sc_log2, oc, lse_c, cd, qg_shift);
+}
+
+// ---------------------------------------------------------------------------
+// Count-balanced row order.
+//
+// Rows have lists of different lengths.  When they differ little (Top-p and
+// Top-k keep 1 to 1.3 times the mean of a quarter head on the 720p
+// workloads), the hardware dispatcher balances them by itself: each SIMD takes
+// the next workgroup as soon as its row ends, and the sweep order keeps
+// neighbouring query blocks (overlapping lists) together in an XCD's L2.
+// When they differ a lot (per-row budgets spread over two orders of
+// magnitude), a long row dispatched late ends well after the others.  The
+// schedule kernel therefore writes the order in which each XCD's workgroups
+// take their rows: the row map's sweep, with each run of rows (a quarter of a
+// head) whose longest list exceeds twice the run's mean reordered longest
+// first, so that such a run ends with its shortest rows.  (A persistent grid
+// of resident wavefronts pulling rows from per-XCD queues in the same orders
+// was measured slower than hardware dispatch on every workload.)
+
+constexpr int kSortMax = 1024;   // rows sorted together (a longer run is split)
+
+struct SchedDims {
+  int per_xcd;   // workgroups per XCD
+  int chunk;     // rows per run (the row map's chunk, at most kSortMax)
+};
+
+inline SchedDims sched_dims(const RowMap& m) {
+  SchedDims s;
+  s.per_xcd = m.per_xcd;
+  s.chunk = m.chunk < kSortMax ? m.chunk : kSortMax;
+  return s;
+}
+
+// order[x * per_xcd + k] = the row of the k-th workgroup of XCD x (-1:
+// none).  One workgroup of 256 threads per (run, XCD).
+__global__ __launch_bounds__(256) void fwd_sched_kernel(const int32_t* __restrict__ counts, int cap, RowMap map,
+                                                        SchedDims sd, int nblk, int32_t* __restrict__ order) {
+  __shared__ int key[kSortMax];
+  __shared__ int rowv[kSortMax];
+  __shared__ int redm[4];
+  __shared__ long long reds[4];
+  const int x = blockIdx.y;
+  const int k0 = blockIdx.x * sd.chunk;
+  const int n = min(sd.chunk, sd.per_xcd - k0);
+  int mx = 0;
+  long long sum = 0;
+  for (int e = threadIdx.x; e < n; e += blockDim.x) {
+    const int row = row_of_workgroup(x + kXcds * (k0 + e), map);
+    int c = -1;
+    if (row >= 0) {
+      c = counts[row];
+      c = c < 0 ? 0 : (c > cap ? cap : c);
+      mx = max(mx, c);
+      sum += c;
+    }
+    key[e] = c;
+    rowv[e] = row;
+  }
+  // longest list and total of the run
+  mx = max(mx, __shfl_xor(mx, 32));
+  sum += __shfl_xor(sum, 32);
+#pragma unroll
+  for (int o = 16; o > 0; o >>= 1) {
+    mx = max(mx, __shfl_xor(mx, o));
+    sum += __shfl_xor(sum, o);
+  }
+  if ((threadIdx.x & 63) == 0) {
+    redm[threadIdx.x >> 6] = mx;
+    reds[threadIdx.x >> 6] = sum;
+  }
+  __syncthreads();
+  mx = max(max(redm[0], redm[1]), max(redm[2], redm[3]));
+  const long long total = reds[0] + reds[1] + reds[2] + reds[3];
+  const bool sort = (long long)mx * n > 2 * total;   // longest above twice the mean
+  int32_t* out = order + (long long)x * sd.per_xcd + k0;
+  for (int e = threadIdx.x; e < n; e += blockDim.x) {
+    int rank = e;
+    if (sort) {   // count descending, then position in the sweep
+      const int ke = key[e];
+      rank = 0;
+      for (int f = 0; f < n; ++f) {
+        const int kf = key[f];
+        rank += (kf > ke || (kf == ke && f < e)) ? 1 : 0;
+      }
+    }
+    out[rank] = rowv[e];
+  }
+}
+
 }  // namespace
 
-size_t fwd_workspace_bytes(const Geom&) { return 0; }
+size_t fwd_workspace_bytes(const Geom& g) {
+  const RowMap map = make_rowmap(g.nblk, g.batch * g.heads);
+  return ((size_t)kXcds * map.per_xcd * sizeof(int32_t) + 255) / 256 * 256;
+}
 
+// order: NULL (the row map's sweep) or a workspace for the count-balanced
+// order (one list per cube only)
 template <bool TOK>
 static hipError_t launch_fwd_any(const void* qc, const void* kc, const void* vc, const int32_t* lut,
                                  const int32_t* counts, int cap, const Geom& g, float scale, void* out,
-                                 float* lse_out, hipStream_t s, int qg_shift) {
+                                 float* lse_out, hipStream_t s, int qg_shift, void* order_ws) {
   const RowMap map = make_rowmap(g.nblk, g.batch * g.heads);
   const CubeDiv cd = {make_fastdiv((uint32_t)g.nw), make_fastdiv((uint32_t)g.nh)};
   const float sc_log2 = scale * 1.4426950408889634f;
   const dim3 grid((unsigned)((long long)map.per_xcd * kXcds));
+  int32_t* order = qg_shift == 0 ? static_cast<int32_t*>(order_ws) : nullptr;
+  if (order != nullptr) {
+    const SchedDims sd = sched_dims(map);
+    const dim3 sgrid((unsigned)((map.per_xcd + sd.chunk - 1) / sd.chunk), kXcds);
+    fwd_sched_kernel<<<sgrid, 256, 0, s>>>(counts, cap, map, sd, g.nblk, order);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const u32x4* q = static_cast<const u32x4*>(qc);
   const u32x4* k = static_cast<const u32x4*>(kc);
   const u32x4* v = static_cast<const u32x4*>(vc);
   if (g.d == 128)
     fwd_kernel<128, TOK><<<grid, 64, 0, s>>>(q, k, v, lut, counts, cap, g, sc_log2, static_cast<bf16*>(out),
-                                             lse_out, map, cd, qg_shift);
+                                             lse_out, map, cd, qg_shift, order);
   else
     fwd_kernel<64, TOK><<<grid, 64, 0, s>>>(q, k, v, lut, counts, cap, g, sc_log2, static_cast<bf16*>(out),
-                                            lse_out, map, cd, qg_shift);
+                                            lse_out, map, cd, qg_shift, order);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd(const void* qc, const void* kc, const void* vc, const int32_t* lut,
                       const int32_t* counts, int cap, const Geom& g, float scale, void* oc,
-                      float* lse_c, void*, hipStream_t s, int qg_shift) {
-  return launch_fwd_any<false>(qc, kc, vc, lut, counts, cap, g, scale, oc, lse_c, s, qg_shift);
+                      float* lse_c, void* workspace, hipStream_t s, int qg_shift) {
+  return launch_fwd_any<false>(qc, kc, vc, lut, counts, cap, g, scale, oc, lse_c, s, qg_shift, workspace);
 }
 
 hipError_t launch_fwd_tokens(const void* qc, const void* kc, const void* vc, const int32_t* lut,
                              const int32_t* counts, int cap, const Geom& g, float scale, void* o,
-                             float* lse, hipStream_t s) {
-  return launch_fwd_any<true>(qc, kc, vc, lut, counts, cap, g, scale, o, lse, s, 0);
+                             float* lse, hipStream_t s, void* workspace) {
+  return launch_fwd_any<true>(qc, kc, vc, lut, counts, cap, g, scale, o, lse, s, 0, workspace);
 }
 
 }  // namespace sa

@@ -139,10 +139,17 @@ extern "C" int32_t sparse_attn_attention(const sa_path_buffers* b, const sa_geom
   }
   // the forward chunk by chunk on the auxiliary stream; each chunk's output is
   // re-indexed on the main stream while the next chunk's forward runs (the
-  // re-indexing kernel is small enough to share the compute units with it)
+  // re-indexing kernel is small enough to share the compute units with it).
+  // With per-row budgets the rows' list lengths spread widely, and the forward
+  // takes its rows in the count-balanced order; the scores are no longer
+  // needed once the lists exist, so their buffer holds that order (the chunks
+  // run one after another on one stream, so they can share it).
   for (int c = 0; c < nchunks; ++c) {
     const int r0 = c * chunk, nr = (rows - r0) < chunk ? (rows - r0) : chunk;
     const sa::Geom gc = rows_of(d, nr);
+    void* fws = b->row_budget != nullptr && (size_t)rows * nb * nb * sizeof(double) >= sa::fwd_workspace_bytes(gc)
+                    ? (void*)b->scores
+                    : nullptr;
     const int32_t* lut = b->lut + (size_t)r0 * nb * b->cap;
     const int32_t* counts = b->counts + (size_t)r0 * nb;
     const char* qc = static_cast<const char*>(b->qc) + (size_t)r0 * head_c * 2;
@@ -152,7 +159,7 @@ extern "C" int32_t sparse_attn_attention(const sa_path_buffers* b, const sa_geom
     float* lse = b->lse + (size_t)r0 * d.n_real;
     if (b->oc == nullptr) {
       // no slot-major copy wanted: the forward writes token order itself
-      if ((e = sa::launch_fwd_tokens(qc, kc, vc, lut, counts, b->cap, gc, sc, o, lse, a)) != hipSuccess)
+      if ((e = sa::launch_fwd_tokens(qc, kc, vc, lut, counts, b->cap, gc, sc, o, lse, a, fws)) != hipSuccess)
         return sa_hip_status(e, "fwd launch");
       if (two) {
         if ((e = hipEventRecord((*evp)[3 + c], a)) != hipSuccess) return sa_hip_status(e, "event record");
@@ -163,7 +170,7 @@ extern "C" int32_t sparse_attn_attention(const sa_path_buffers* b, const sa_geom
     }
     char* oc = static_cast<char*>(b->oc) + (size_t)r0 * head_c * 2;
     float* lse_c = b->lse_c + (size_t)r0 * d.n_pad;
-    if ((e = sa::launch_fwd(qc, kc, vc, lut, counts, b->cap, gc, sc, oc, lse_c, nullptr, a)) != hipSuccess)
+    if ((e = sa::launch_fwd(qc, kc, vc, lut, counts, b->cap, gc, sc, oc, lse_c, fws, a)) != hipSuccess)
       return sa_hip_status(e, "fwd launch");
     if (two) {
       if ((e = hipEventRecord((*evp)[3 + c], a)) != hipSuccess) return sa_hip_status(e, "event record");

@@ -220,7 +220,9 @@ typedef struct sa_path_buffers {
   void* vc;
   double* qbar;         /* [batch, heads, nblk, head_dim] float64 block means (written) */
   double* kbar;
-  double* scores;       /* [batch, heads, nblk, nblk] float64 pooled scores (written) */
+  double* scores;       /* [batch, heads, nblk, nblk] float64 pooled scores (written; with
+                           row_budget its start is then reused for the forward's
+                           count-balanced row order, see sparse_attn_fwd) */
   int32_t* lut;         /* [batch, heads, nblk, cap] kept lists (written) */
   int32_t* counts;      /* [batch, heads, nblk] */
   int32_t cap;
@@ -417,7 +419,8 @@ int32_t sparse_attn_build_mask_noalloc(const void* qc, const void* kc,
                                        int32_t* lut, int32_t* counts,
                                        int32_t cap, void* stream);
 
-/* Bytes of workspace sparse_attn_fwd needs (its row schedule). */
+/* Bytes of workspace sparse_attn_fwd and sparse_attn_fwd_tokens use for the
+ * count-balanced order of their rows (one int32 per workgroup). */
 size_t sparse_attn_fwd_workspace_bytes(const sa_geom* g);
 
 /* Block-sparse attention forward, [SA2] "Kernel Implementation of the
@@ -435,8 +438,18 @@ size_t sparse_attn_fwd_workspace_bytes(const sa_geom* g);
  *   lse_c [batch, heads, n_pad] float32, natural log              (output)
  * Rows with count 0 and pad query slots get O = 0, LSE = -inf.  Products run
  * in bf16 on the matrix cores with float32 accumulation and an online
- * softmax in float32.  scale <= 0 selects 1/sqrt(head_dim).  workspace may be
- * NULL when sparse_attn_fwd_workspace_bytes() is 0. */
+ * softmax in float32.  scale <= 0 selects 1/sqrt(head_dim).
+ * One workgroup per query block; the rows go to the 8 XCDs in sweeps of
+ * neighbouring query blocks (four XCDs per head), so blocks with overlapping
+ * lists share K/V in an XCD's L2.  With workspace NULL that sweep order is
+ * used as is, which balances rows of similar list lengths.  With a workspace
+ * (>= sparse_attn_fwd_workspace_bytes, else SA_ERR_CAPACITY) a small kernel
+ * first writes a count-balanced order into it: each quarter-head run of the
+ * sweep whose longest list is above twice the run's mean is reordered
+ * longest list first, so rows of very different lengths (per-row budgets)
+ * end together.  The results are identical either way.  The call rewrites
+ * the workspace before the forward reads it (no memset), so it can be
+ * captured in a HIP graph; calls that overlap must not share a workspace. */
 int32_t sparse_attn_fwd(const void* qc, const void* kc, const void* vc,
                         const int32_t* lut, const int32_t* counts, int32_t cap,
                         const sa_geom* g, float scale, void* oc, float* lse_c,
@@ -449,11 +462,14 @@ int32_t sparse_attn_fwd(const void* qc, const void* kc, const void* vc,
  *   qc, kc, vc, lut, counts, cap, scale as for sparse_attn_fwd     (inputs)
  *   o    [batch, heads, N, head_dim] bf16, token order            (output)
  *   lse  [batch, heads, N] float32, natural log                   (output)
+ *   workspace, workspace_bytes  the count-balanced row order, as for
+ *        sparse_attn_fwd (NULL: the sweep order; the same results)
  * Bit-identical to sparse_attn_fwd followed by sparse_attn_unreorder. */
 int32_t sparse_attn_fwd_tokens(const void* qc, const void* kc, const void* vc,
                                const int32_t* lut, const int32_t* counts,
                                int32_t cap, const sa_geom* g, float scale,
-                               void* o, float* lse, void* stream);
+                               void* o, float* lse, void* workspace,
+                               size_t workspace_bytes, void* stream);
 
 /* Ideal block scores ([VSA2] section 2.2: MeanPool of the full attention
  * matrix, the target a router approximates): mass[i][j] = the full softmax

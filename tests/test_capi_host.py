@@ -248,17 +248,35 @@ def test_fused_forward_argument_rules():
     lib = sa.lib()
     B = ctypes.byref(g)
     O_ = ctypes.c_void_p(0x200000)
-    assert lib.sparse_attn_fwd_tokens(FAKE, FAKE, FAKE, FAKE, FAKE, 16, B, 0.0, O_, None, None) == \
+    WS = ctypes.c_void_p(0x300000)
+    need = sa.sparse_attn_fwd_workspace_bytes(g)
+    assert need > 0
+    assert lib.sparse_attn_fwd_tokens(FAKE, FAKE, FAKE, FAKE, FAKE, 16, B, 0.0, O_, None, None, 0, None) == \
         sa.SA_ERR_INVALID_ARG
     assert "lse" in sa.sparse_attn_last_error()
-    assert lib.sparse_attn_fwd_tokens(FAKE, FAKE, FAKE, FAKE, FAKE, 16, B, 0.0, FAKE_MISALIGNED, FAKE, None) == \
-        sa.SA_ERR_INVALID_ARG                                          # o misaligned
-    assert lib.sparse_attn_fwd_tokens(FAKE, FAKE, FAKE, FAKE, FAKE, 0, B, 0.0, O_, FAKE, None) == \
+    assert lib.sparse_attn_fwd_tokens(FAKE, FAKE, FAKE, FAKE, FAKE, 16, B, 0.0, FAKE_MISALIGNED, FAKE, None, 0,
+                                      None) == sa.SA_ERR_INVALID_ARG                 # o misaligned
+    assert lib.sparse_attn_fwd_tokens(FAKE, FAKE, FAKE, FAKE, FAKE, 0, B, 0.0, O_, FAKE, None, 0, None) == \
         sa.SA_ERR_INVALID_ARG                                          # cap < 1
-    assert lib.sparse_attn_fwd_tokens(FAKE, FAKE, FAKE, FAKE, FAKE, 16, B, float("nan"), O_, FAKE, None) == \
-        sa.SA_ERR_INVALID_ARG
-    assert lib.sparse_attn_fwd_tokens(FAKE, FAKE, FAKE, FAKE, FAKE, 16, None, 0.0, O_, FAKE, None) == \
+    assert lib.sparse_attn_fwd_tokens(FAKE, FAKE, FAKE, FAKE, FAKE, 16, B, float("nan"), O_, FAKE, None, 0,
+                                      None) == sa.SA_ERR_INVALID_ARG
+    assert lib.sparse_attn_fwd_tokens(FAKE, FAKE, FAKE, FAKE, FAKE, 16, None, 0.0, O_, FAKE, None, 0, None) == \
         sa.SA_ERR_INVALID_ARG                                          # no geometry
+    # a schedule workspace below the size the geometry needs, or misaligned
+    assert lib.sparse_attn_fwd_tokens(FAKE, FAKE, FAKE, FAKE, FAKE, 16, B, 0.0, O_, FAKE, WS, need - 1, None) == \
+        sa.SA_ERR_CAPACITY
+    assert lib.sparse_attn_fwd_tokens(FAKE, FAKE, FAKE, FAKE, FAKE, 16, B, 0.0, O_, FAKE, FAKE_MISALIGNED, need,
+                                      None) == sa.SA_ERR_INVALID_ARG
+
+
+def test_forward_workspace_covers_the_row_order():
+    """One int32 entry per workgroup of the forward's grid (every row at
+    least once), rounded up to 256 bytes."""
+    for grid, heads in (((4, 16, 16), 2), ((21, 45, 80), 40), ((1, 1, 1), 1)):
+        g = geom(frames=grid[0], height=grid[1], width=grid[2], heads=heads)
+        nblk = sa.sparse_attn_geometry(g)[0]
+        need = sa.sparse_attn_fwd_workspace_bytes(g)
+        assert need % 256 == 0 and need >= 4 * nblk * heads
 
 
 def test_noalloc_mask_rejects_before_any_launch():

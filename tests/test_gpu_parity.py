@@ -294,6 +294,23 @@ def test_fused_forward_equals_forward_then_unreorder(case):
     assert torch.equal(o2, o) and torch.equal(lse2, lse)
 
 
+def test_forward_row_order_gives_identical_bytes(case):
+    """The count-balanced row order (a workspace given) and the plain sweep
+    (no workspace) run the same per-row computation: identical bytes."""
+    g, ref = case["g"], case["ref_mask"]
+    qc, kc, vc = reorder3(case["qd"], case["kd"], case["vd"], g)
+    lut, counts = torch.from_numpy(ref.lut).to(DEV), torch.from_numpy(ref.counts).to(DEV)
+    _, n_real, _ = sa.sparse_attn_geometry(g)
+    outs = []
+    for ws in (None, torch.empty(sa.sparse_attn_fwd_workspace_bytes(g), dtype=torch.uint8, device=DEV)):
+        o = torch.empty((g.batch, g.heads, n_real, g.head_dim), dtype=torch.bfloat16, device=DEV)
+        lse = torch.empty((g.batch, g.heads, n_real), dtype=torch.float32, device=DEV)
+        sa.sparse_attn_fwd_tokens(qc, kc, vc, lut, counts, lut.shape[-1], g, 0.0, o, lse, ws)
+        outs.append((o, lse))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
 def test_keep_nothing_gives_zero_and_neg_inf():
     say("[edge keep-none]")
     wl, g, og, q, k, v = _small()
@@ -323,6 +340,14 @@ def test_row_budgets_and_variable_counts():
     assert mx <= O_MAX_ABS and mean <= O_MEAN_ABS
     lmx, lmean = lse_errors(lse_c.cpu().double().numpy(), lse_ref)
     assert lmx <= LSE_MAX_ABS and lmean <= LSE_MEAN_ABS
+    # counts from 0 to nblk: the count-balanced order reorders these runs; the
+    # bytes equal those of the plain sweep
+    n_pad = sa.sparse_attn_geometry(g)[2]
+    oc2 = torch.empty_like(oc)
+    lse2 = torch.empty_like(lse_c)
+    sa.sparse_attn_fwd(qd, kd, vd, lut, counts, lut.shape[-1], g, 0.0, oc2, lse2, None)
+    torch.cuda.synchronize()
+    assert torch.equal(oc2, oc) and torch.equal(lse2, lse_c)
 
 
 def test_fwd_skips_out_of_range_ids_and_honours_cap():
