@@ -32,13 +32,14 @@ SA_LAYOUT_V = 1
 
 EXPORTED = (
     "sparse_attn_geometry", "sparse_attn_ceil_k", "sparse_attn_reorder",
-    "sparse_attn_reorder_pool", "sparse_attn_unreorder", "sparse_attn_pool", "sparse_attn_block_scores",
+    "sparse_attn_reorder_pool", "sparse_attn_reorder_qkv", "sparse_attn_unreorder", "sparse_attn_pool",
+    "sparse_attn_block_scores",
     "sparse_attn_select", "sparse_attn_mask_workspace_bytes", "sparse_attn_fwd_tokens",
     "sparse_attn_build_mask", "sparse_attn_fwd_workspace_bytes", "sparse_attn_fwd",
     "sparse_attn_coarse", "sparse_attn_router_pool", "sparse_attn_router_scores",
     "sparse_attn_bwd_delta", "sparse_attn_transpose_workspace_bytes", "sparse_attn_transpose_lut",
     "sparse_attn_bwd", "sparse_attn_pooled_mass", "sparse_attn_mask_error", "sparse_attn_mask_error_terms",
-    "sparse_attn_attention",
+    "sparse_attn_attention", "sparse_attn_mask_path",
     "sparse_attn_mask_groups_workspace_bytes", "sparse_attn_build_mask_groups", "sparse_attn_fwd_groups",
     "sparse_attn_sequence_workspace_bytes", "sparse_attn_select_per_sequence",
     "sparse_attn_ideal_block_mass", "sparse_attn_recall_workspace_bytes", "sparse_attn_mask_recall",
@@ -94,6 +95,7 @@ _SIGS = {
     "sparse_attn_ceil_k": (_i32, [_f64, _i32]),
     "sparse_attn_reorder": (_i32, [_vp, _vp, _i32, _GP, _vp]),
     "sparse_attn_reorder_pool": (_i32, [_vp, _vp, _i32, _vp, _GP, _vp]),
+    "sparse_attn_reorder_qkv": (_i32, [_vp] * 8 + [_GP, _vp]),
     "sparse_attn_unreorder": (_i32, [_vp, _vp, _vp, _vp, _GP, _vp]),
     "sparse_attn_pool": (_i32, [_vp, _vp, _vp, _vp, _GP, _vp]),
     "sparse_attn_block_scores": (_i32, [_vp, _vp, _vp, _f64, _GP, _vp]),
@@ -114,6 +116,7 @@ _SIGS = {
     "sparse_attn_mask_error": (_i32, [_vp, _vp, _vp, _vp, _GP, _vp, _vp, _vp]),
     "sparse_attn_mask_error_terms": (_i32, [_vp, _vp, _vp, _vp, _GP, _vp, _vp, _vp, _vp, _vp]),
     "sparse_attn_attention": (_i32, [ctypes.POINTER(PathBuffers), _GP, _f64, _f64, _f32, _i32, _vp, _vp]),
+    "sparse_attn_mask_path": (_i32, [ctypes.POINTER(PathBuffers), _GP, _f64, _f64, _vp, _vp]),
     "sparse_attn_mask_groups_workspace_bytes": (_sz, [_GP, _i32]),
     "sparse_attn_build_mask_groups": (_i32, [_vp, _vp, _GP, _i32, _f64, _f64, _vp, _vp, _i32, _vp, _sz, _vp]),
     "sparse_attn_fwd_groups": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _GP, _f32, _vp, _vp, _vp]),
@@ -198,6 +201,14 @@ def sparse_attn_reorder_pool(x, xc, layout: int, xbar, g: Geom, stream=None) -> 
     _check(lib().sparse_attn_reorder_pool(_ptr(x, torch.bfloat16, "x"), _ptr(xc, torch.bfloat16, "xc"),
                                           int(layout), _ptr(xbar, torch.float64, "xbar"), ctypes.byref(g),
                                           _stream(stream, x)))
+
+
+def sparse_attn_reorder_qkv(q, k, v, qc, kc, vc, qbar, kbar, g: Geom, stream=None) -> None:
+    _check(lib().sparse_attn_reorder_qkv(_ptr(q, torch.bfloat16, "q"), _ptr(k, torch.bfloat16, "k"),
+                                         _ptr(v, torch.bfloat16, "v"), _ptr(qc, torch.bfloat16, "qc"),
+                                         _ptr(kc, torch.bfloat16, "kc"), _ptr(vc, torch.bfloat16, "vc"),
+                                         _ptr(qbar, torch.float64, "qbar"), _ptr(kbar, torch.float64, "kbar"),
+                                         ctypes.byref(g), _stream(stream, q)))
 
 
 def sparse_attn_unreorder(oc, o, lse_c, lse, g: Geom, stream=None) -> None:
@@ -351,6 +362,14 @@ def sparse_attn_attention(buffers: PathBuffers, g: Geom, k_frac: float, p: float
     a = None if aux_stream is None else ctypes.c_void_p(int(aux_stream))
     _check(lib().sparse_attn_attention(ctypes.byref(buffers), ctypes.byref(g), float(k_frac), float(p),
                                        float(scale), int(head_chunk), ctypes.c_void_p(s), a))
+
+
+def sparse_attn_mask_path(buffers: PathBuffers, g: Geom, k_frac: float, p: float, stream=None,
+                          aux_stream=None) -> None:
+    s = torch.cuda.current_stream().cuda_stream if stream is None else int(stream)
+    a = None if aux_stream is None else ctypes.c_void_p(int(aux_stream))
+    _check(lib().sparse_attn_mask_path(ctypes.byref(buffers), ctypes.byref(g), float(k_frac), float(p),
+                                       ctypes.c_void_p(s), a))
 
 
 def sparse_attn_last_error() -> str:

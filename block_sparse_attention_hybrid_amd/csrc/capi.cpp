@@ -187,6 +187,27 @@ int32_t sparse_attn_reorder_pool(const void* x, void* xc, int32_t layout, double
   return hip_status(sa::launch_reorder_pool(x, xc, layout, xbar, d, (hipStream_t)stream), "reorder_pool launch");
 }
 
+int32_t sparse_attn_reorder_qkv(const void* q, const void* k, const void* v, void* qc, void* kc, void* vc,
+                                double* qbar, double* kbar, const sa_geom* g, void* stream) {
+  sa::Geom d;
+  SA_TRY(make_geom(g, d));
+  SA_TRY(check_ptr(q, 16, "q"));
+  SA_TRY(check_ptr(k, 16, "k"));
+  SA_TRY(check_ptr(v, 16, "v"));
+  SA_TRY(check_ptr(qc, 16, "qc"));
+  SA_TRY(check_ptr(kc, 16, "kc"));
+  SA_TRY(check_ptr(vc, 16, "vc"));
+  SA_TRY(check_ptr(qbar, 8, "qbar"));
+  SA_TRY(check_ptr(kbar, 8, "kbar"));
+  const void* in[3] = {q, k, v};
+  const void* out[5] = {qc, kc, vc, qbar, kbar};
+  for (const void* a : in)
+    for (const void* b : out)
+      if (a == b) return fail(SA_ERR_INVALID_ARG, "an output of reorder_qkv is also one of its inputs");
+  return hip_status(sa::launch_reorder_qkv(q, k, v, qc, kc, vc, qbar, kbar, d, (hipStream_t)stream),
+                    "reorder_qkv launch");
+}
+
 int32_t sparse_attn_unreorder(const void* oc, void* o, const float* lse_c, float* lse,
                               const sa_geom* g, void* stream) {
   sa::Geom d;
@@ -396,8 +417,9 @@ int32_t sa_validate_build_mask(const void* qc, const void* kc, const sa_geom* g,
   return ok();
 }
 
+// outputs = false: the mask phase only (oc, lse_c, o and lse are not used)
 int32_t sa_validate_path(const sa_path_buffers* b, const sa_geom* g, double k_frac, double p, float scale,
-                         int32_t head_chunk, sa::Geom& d, int& kcount, float& scale_out) {
+                         int32_t head_chunk, bool outputs, sa::Geom& d, int& kcount, float& scale_out) {
   SA_TRY(make_geom(g, d));
   if (b == nullptr) return fail(SA_ERR_INVALID_ARG, "buffers pointer is NULL");
   if (d.nblk > 64 * 65535) return fail(SA_ERR_UNSUPPORTED, "too many blocks for the score grid");
@@ -411,14 +433,16 @@ int32_t sa_validate_path(const sa_path_buffers* b, const sa_geom* g, double k_fr
   SA_TRY(check_ptr(b->kbar, 8, "kbar"));
   SA_TRY(check_ptr(b->scores, 8, "scores"));
   // oc and lse_c: both given (slot-major O and LSE are written too) or both NULL
-  if ((b->oc == nullptr) != (b->lse_c == nullptr))
-    return fail(SA_ERR_INVALID_ARG, "oc and lse_c must both be given or both be NULL");
-  if (b->oc != nullptr) {
-    SA_TRY(check_ptr(b->oc, 16, "oc"));
-    SA_TRY(check_ptr(b->lse_c, 4, "lse_c"));
+  if (outputs) {
+    if ((b->oc == nullptr) != (b->lse_c == nullptr))
+      return fail(SA_ERR_INVALID_ARG, "oc and lse_c must both be given or both be NULL");
+    if (b->oc != nullptr) {
+      SA_TRY(check_ptr(b->oc, 16, "oc"));
+      SA_TRY(check_ptr(b->lse_c, 4, "lse_c"));
+    }
+    SA_TRY(check_ptr(b->o, 16, "o"));
+    SA_TRY(check_ptr(b->lse, 4, "lse"));
   }
-  SA_TRY(check_ptr(b->o, 16, "o"));
-  SA_TRY(check_ptr(b->lse, 4, "lse"));
   if (b->q == b->qc || b->k == b->kc || b->v == b->vc) return fail(SA_ERR_INVALID_ARG, "inputs and outputs overlap");
   SA_TRY(check_select_args(d, k_frac, p, b->row_budget, b->lut, b->counts, b->cap, kcount));
   if (head_chunk < 1) return fail(SA_ERR_INVALID_ARG, "head_chunk must be >= 1");

@@ -37,23 +37,29 @@ __device__ __forceinline__ void fill_slot_table(const Geom& g, int i, long long*
   __syncthreads();
 }
 
-template <bool kV, bool kPool>
-__global__ __launch_bounds__(kThreads) void reorder_kernel(const u32x4* __restrict__ x,
-                                                           u32x4* __restrict__ xc,
-                                                           double* __restrict__ xbar, Geom g) {
+// LDS of one block's re-indexing: the token-major tile, the slot table and
+// the pooling partial sums
+struct ReorderLds {
   // tile[s][c], token-major with row pitch d+8 (16-byte rows), for both layouts
-  __shared__ __attribute__((aligned(16))) uint16_t tile[kBlock * (128 + 8)];
-  __shared__ long long tok[kBlock];
-  const int i = blockIdx.x;
-  const long long bh = blockIdx.y;
+  __attribute__((aligned(16))) uint16_t tile[kBlock * (128 + 8)];
+  long long tok[kBlock];
+  double part[kThreads];
+};
+
+// Block i of (batch*head) bh: token rows -> tile -> operand chunks.
+template <bool kV, bool kPool>
+__device__ __forceinline__ void reorder_block(const u32x4* __restrict__ x, u32x4* __restrict__ xc,
+                                              double* __restrict__ xbar, const Geom& g, int i, long long bh,
+                                              ReorderLds& L) {
+  uint16_t* tile = L.tile;
   const int d = g.d, cpr = d / 8;
   const int ldq = d + 8;
   const long long src_head = bh * g.n_real * cpr;
   const long long dst_blk = (bh * g.n_pad + (long long)i * kBlock) * cpr;
-  fill_slot_table(g, i, tok);
+  fill_slot_table(g, i, L.tok);
   for (int idx = threadIdx.x; idx < kBlock * cpr; idx += kThreads) {
     const int s = idx / cpr, c8 = idx - s * cpr;
-    const long long n = tok[s];
+    const long long n = L.tok[s];
     u32x4 v = {0u, 0u, 0u, 0u};
     if (n >= 0) v = x[src_head + n * cpr + c8];
     *reinterpret_cast<u32x4*>(&tile[s * ldq + c8 * 8]) = v;
@@ -78,20 +84,44 @@ __global__ __launch_bounds__(kThreads) void reorder_kernel(const u32x4* __restri
   if (kPool) {
     // per = kThreads / d threads share a dim, each summing 64 / per slots
     // (pad slots hold zeros); partial sums meet in LDS in a fixed order
-    __shared__ double part[kThreads];
     const int per = kThreads / d, c = threadIdx.x % d, grp = threadIdx.x / d;
     const int ns = kBlock / per;
     double acc = 0.0;
     for (int s = grp * ns; s < (grp + 1) * ns; ++s)
       acc += (double)__uint_as_float((uint32_t)tile[s * ldq + c] << 16);
-    part[threadIdx.x] = acc;
+    L.part[threadIdx.x] = acc;
     __syncthreads();
     if (threadIdx.x < d) {
       double sum = 0.0;
-      for (int q = 0; q < per; ++q) sum += part[q * d + c];
+      for (int q = 0; q < per; ++q) sum += L.part[q * d + c];
       xbar[(bh * g.nblk + i) * (long long)d + c] = sum / (double)block_real_count(g, i);
     }
   }
+}
+
+// One workgroup per (batch*head, block).
+template <bool kV, bool kPool>
+__global__ __launch_bounds__(kThreads) void reorder_kernel(const u32x4* __restrict__ x,
+                                                           u32x4* __restrict__ xc,
+                                                           double* __restrict__ xbar, Geom g) {
+  __shared__ ReorderLds L;
+  reorder_block<kV, kPool>(x, xc, xbar, g, blockIdx.x, blockIdx.y, L);
+}
+
+// Queries and keys (with pooling) and values in one launch: grid z = 0, 1, 2.
+__global__ __launch_bounds__(kThreads) void reorder_qkv_kernel(const u32x4* __restrict__ q,
+                                                               const u32x4* __restrict__ k,
+                                                               const u32x4* __restrict__ v,
+                                                               u32x4* __restrict__ qc, u32x4* __restrict__ kc,
+                                                               u32x4* __restrict__ vc, double* __restrict__ qbar,
+                                                               double* __restrict__ kbar, Geom g) {
+  __shared__ ReorderLds L;
+  if (blockIdx.z == 0)
+    reorder_block<false, true>(q, qc, qbar, g, blockIdx.x, blockIdx.y, L);
+  else if (blockIdx.z == 1)
+    reorder_block<false, true>(k, kc, kbar, g, blockIdx.x, blockIdx.y, L);
+  else
+    reorder_block<true, false>(v, vc, nullptr, g, blockIdx.x, blockIdx.y, L);
 }
 
 __global__ __launch_bounds__(kThreads) void unreorder_kernel(const u32x4* __restrict__ oc,
@@ -139,6 +169,15 @@ hipError_t launch_reorder_pool(const void* x, void* xc, int layout, double* xbar
     reorder_kernel<true, true><<<grid, kThreads, 0, s>>>(src, dst, xbar, g);
   else
     reorder_kernel<false, true><<<grid, kThreads, 0, s>>>(src, dst, xbar, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_reorder_qkv(const void* q, const void* k, const void* v, void* qc, void* kc, void* vc,
+                              double* qbar, double* kbar, const Geom& g, hipStream_t s) {
+  dim3 grid(g.nblk, g.batch * g.heads, 3);
+  reorder_qkv_kernel<<<grid, kThreads, 0, s>>>(static_cast<const u32x4*>(q), static_cast<const u32x4*>(k),
+                                               static_cast<const u32x4*>(v), static_cast<u32x4*>(qc),
+                                               static_cast<u32x4*>(kc), static_cast<u32x4*>(vc), qbar, kbar, g);
   return hipGetLastError();
 }
 

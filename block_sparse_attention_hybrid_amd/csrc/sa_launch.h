@@ -12,6 +12,8 @@ namespace sa {
 hipError_t launch_reorder(const void* x, void* xc, int layout, const Geom& g, hipStream_t s);
 hipError_t launch_reorder_pool(const void* x, void* xc, int layout, double* xbar, const Geom& g,
                                hipStream_t s);
+hipError_t launch_reorder_qkv(const void* q, const void* k, const void* v, void* qc, void* kc, void* vc,
+                              double* qbar, double* kbar, const Geom& g, hipStream_t s);
 hipError_t launch_unreorder(const void* oc, void* o, const float* lse_c, float* lse,
                             const Geom& g, hipStream_t s);
 hipError_t launch_pool(const void* qc, const void* kc, double* qbar, double* kbar,

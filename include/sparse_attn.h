@@ -141,7 +141,25 @@ int32_t sparse_attn_reorder(const void* x, void* xc, int32_t layout,
 int32_t sparse_attn_reorder_pool(const void* x, void* xc, int32_t layout,
                                  double* xbar, const sa_geom* g, void* stream);
 
-/* Inverse re-indexing of the attention output (pad slots dropped).
+/* The three re-indexings of one attention call in one launch: queries and
+ * keys to SA_LAYOUT_QK with their block means (sparse_attn_reorder_pool) and
+ * values to SA_LAYOUT_V (sparse_attn_reorder).  [VSA] "Cube Partitioning and
+ * Token Re-Indexing"; [SA2] "Block-Pooled Attention for Efficient Mask
+ * Construction" step 2.
+ *   q, k, v    [batch, heads, N, head_dim] bf16, row-major tokens     (inputs)
+ *   qc, kc     [batch, heads, n_pad, head_dim] bf16, SA_LAYOUT_QK     (outputs)
+ *   vc         [batch, heads, n_pad, head_dim] bf16, SA_LAYOUT_V      (output)
+ *   qbar, kbar [batch, heads, nblk, head_dim] float64 block means     (outputs)
+ * Every output is bit-identical to that of the separate calls; one launch
+ * instead of three saves two kernel boundaries.  No output may overlap an
+ * input. */
+int32_t sparse_attn_reorder_qkv(const void* q, const void* k, const void* v,
+                                void* qc, void* kc, void* vc, double* qbar,
+                                double* kbar, const sa_geom* g, void* stream);
+
+/* Inverse re-indexing of the attention output (pad slots dropped): the
+ * inverse permutation of [VSA2] section 2.2 "Permutation", applied once at
+ * the end of the attention; [VSA] "Cube Partitioning and Token Re-Indexing".
  *   oc    [batch, heads, n_pad, head_dim] bf16, slot-major  (input)
  *   o     [batch, heads, N, head_dim] bf16       (output)
  *   lse_c [batch, heads, n_pad] float32          (input, may be NULL)
@@ -236,15 +254,33 @@ typedef struct sa_path_buffers {
   float* lse;           /* [batch, heads, N] (written) */
 } sa_path_buffers;
 
+/* The mask phase of sparse_attn_attention alone: re-indexing of Q, K (block
+ * means on the way) and V, block scores and selection ([VSA] "Cube
+ * Partitioning and Token Re-Indexing"; [SA2] "Block-Pooled Attention for
+ * Efficient Mask Construction" and "The Hybrid Top-k+Top-p Masking Rule").
+ * Writes qc, kc, vc, qbar, kbar, scores, lut and counts of `buffers`; oc,
+ * lse_c, o and lse are not used and may be NULL.  With aux_stream NULL (or
+ * equal to stream) the kernels run in order on `stream`.  Otherwise the
+ * batch*heads rows are cut into up to 4 parts: `stream` re-indexes the first
+ * part's queries and keys and then builds each part's mask as soon as its
+ * inputs are ready, while aux_stream re-indexes the other parts' queries and
+ * keys and then the values (the re-indexing is bound by HBM, the scores and
+ * selection by compute, so the two overlap).  `stream` waits for aux_stream's
+ * last work, so completion is observed on `stream`.  The results are the same
+ * either way.  Allocation, synchronisation and graph capture as for
+ * sparse_attn_attention. */
+int32_t sparse_attn_mask_path(const sa_path_buffers* buffers, const sa_geom* g,
+                              double k_frac, double p, void* stream,
+                              void* aux_stream);
+
 /* reorder_pool(Q), reorder_pool(K), reorder(V), block_scores, select, fwd,
  * unreorder -- the path of [SA2] Algorithm 1 and [VSA]'s two stages -- in one
  * call.  Block scores use 1/sqrt(head_dim); `scale` (<= 0: 1/sqrt(head_dim))
  * is the attention scale.  With aux_stream NULL (or equal to stream) the
  * kernels run in order on `stream`.  Otherwise two streams share the work:
- * `stream` re-indexes the queries and keys of the first half of the
- * batch*heads rows and builds their mask while aux_stream re-indexes the
- * second half's and then the values, and `stream` then builds the second
- * half's mask; the forward then runs on aux_stream in chunks of head_chunk
+ * the mask phase runs as in sparse_attn_mask_path (the rows in up to 4 parts,
+ * masks on `stream` beside the re-indexing on aux_stream); the forward then
+ * runs on aux_stream in chunks of head_chunk
  * batch*heads rows (head_chunk >= batch*heads: one chunk), and `stream`
  * re-indexes each chunk's output while the next chunk's forward runs (with
  * buffers->oc NULL the forward writes token order itself and `stream` only

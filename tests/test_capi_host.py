@@ -96,6 +96,12 @@ def test_null_and_misaligned_pointers_rejected():
                                         None) == sa.SA_ERR_INVALID_ARG   # xbar misaligned
     assert lib.sparse_attn_reorder_pool(FAKE, ctypes.c_void_p(0x200000), 3, ctypes.c_void_p(0x300000), B,
                                         None) == sa.SA_ERR_INVALID_ARG   # layout
+    P = [ctypes.c_void_p(a) for a in (0x100000, 0x200000, 0x300000, 0x400000, 0x500000, 0x600000, 0x700000,
+                                      0x800000)]
+    assert lib.sparse_attn_reorder_qkv(*P[:7], None, B, None) == sa.SA_ERR_INVALID_ARG
+    assert lib.sparse_attn_reorder_qkv(*P[:3], P[0], *P[4:], B, None) == sa.SA_ERR_INVALID_ARG   # qc is q
+    assert "input" in sa.sparse_attn_last_error()
+    assert lib.sparse_attn_reorder_qkv(*P[:6], ctypes.c_void_p(0x700004), P[7], B, None) == sa.SA_ERR_INVALID_ARG
     assert lib.sparse_attn_unreorder(FAKE, FAKE, FAKE, None, B, None) == sa.SA_ERR_INVALID_ARG
     assert lib.sparse_attn_pool(FAKE, FAKE, None, FAKE, B, None) == sa.SA_ERR_INVALID_ARG
     assert lib.sparse_attn_block_scores(FAKE, FAKE, None, 0.0, B, None) == sa.SA_ERR_INVALID_ARG
@@ -241,6 +247,13 @@ def test_whole_path_argument_rules():
     assert call(buffers(cap=15)) == sa.SA_ERR_CAPACITY               # Top-p may keep all 16 blocks
     assert call(buffers(), k_frac=float("nan")) == sa.SA_ERR_INVALID_ARG
     assert call(buffers(), chunk=0) == sa.SA_ERR_INVALID_ARG
+    # the mask phase alone takes no output buffers
+    def mask_call(buf, k_frac=0.25, p=0.5):
+        return lib.sparse_attn_mask_path(ctypes.byref(buf), B, k_frac, p, None, None)
+    assert mask_call(buffers(q=None, o=None, lse=None, oc=None, lse_c=None)) == sa.SA_ERR_INVALID_ARG
+    assert "q" in sa.sparse_attn_last_error() and "oc" not in sa.sparse_attn_last_error()
+    assert mask_call(buffers(o=None, lse=None, oc=None, cap=15)) == sa.SA_ERR_CAPACITY
+    assert mask_call(buffers(scores=None)) == sa.SA_ERR_INVALID_ARG
 
 
 def test_fused_forward_argument_rules():

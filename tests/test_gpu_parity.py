@@ -102,6 +102,24 @@ def test_reorder_pool_fused(case):
         np.testing.assert_array_equal(xbar.cpu().numpy(), want)
 
 
+def test_reorder_qkv_one_launch(case):
+    """Q, K (with pooling) and V re-indexed in one launch: the oracle's
+    cube-major bytes in both layouts and its exact block means."""
+    g, ref = case["g"], case["ref_mask"]
+    q, k, v = case["qd"], case["kd"], case["vd"]
+    B, H, _, d = q.shape
+    nblk, _, n_pad = sa.sparse_attn_geometry(g)
+    qc, kc, vc = (torch.full((B, H, n_pad, d), 7.0, dtype=torch.bfloat16, device=DEV) for _ in range(3))
+    qbar, kbar = (torch.full((B, H, nblk, d), 7.0, dtype=torch.float64, device=DEV) for _ in range(2))
+    sa.sparse_attn_reorder_qkv(q, k, v, qc, kc, vc, qbar, kbar, g)
+    torch.cuda.synchronize()
+    assert np.array_equal(to64(qc), to_layout(case["ref_qc"], False))
+    assert np.array_equal(to64(kc), to_layout(case["ref_kc"], False))
+    assert np.array_equal(to64(vc), to_layout(case["ref_vc"], True))
+    np.testing.assert_array_equal(qbar.cpu().numpy(), ref.qbar)
+    np.testing.assert_array_equal(kbar.cpu().numpy(), ref.kbar)
+
+
 def test_mask_from_pooled_matches_build_mask(case):
     g, ref = case["g"], case["ref_mask"]
     qc, qbar = sa.reorder_pool(case["qd"], g)
@@ -653,6 +671,26 @@ def test_whole_path_call_overlapped_equals_sequential(case, chunk):
         sa.sparse_attn_attention(buf3, g, case["k_frac"], case["p"], 0.0, chunk, aux_stream=aux_s)
         torch.cuda.synchronize()
         assert torch.equal(t3["o"], o) and torch.equal(t3["lse"], lse)
+
+
+def test_mask_path_call(case):
+    """sparse_attn_mask_path (one stream, and the rows in parts on two
+    streams) writes the cube-major operands, block means and lists of the
+    separate calls."""
+    g = case["g"]
+    _, _, lut, counts = sa.attention(case["qd"], case["kd"], case["vd"], g, case["k_frac"], case["p"])
+    qc, kc, vc = reorder3(case["qd"], case["kd"], case["vd"], g)
+    aux = torch.cuda.Stream()
+    for aux_s in (None, aux.cuda_stream):
+        buf, t = sa.path_buffers(case["qd"], case["kd"], case["vd"], g, slot_major=False)
+        sa.sparse_attn_mask_path(buf, g, case["k_frac"], case["p"], aux_stream=aux_s)
+        torch.cuda.synchronize()
+        assert torch.equal(t["qc"], qc) and torch.equal(t["kc"], kc) and torch.equal(t["vc"], vc)
+        assert torch.equal(t["counts"], counts)
+        c = counts.cpu().numpy()
+        a, b = t["lut"].cpu().numpy(), lut.cpu().numpy()
+        for idx in np.ndindex(c.shape):
+            assert np.array_equal(a[idx][:c[idx]], b[idx][:c[idx]])
 
 
 def test_whole_path_call_from_two_threads(case):
