@@ -81,6 +81,29 @@ struct CubeDiv {
   FastDiv w, h;
 };
 
+// Groups of neighbouring query blocks that fwd_group_kernel (below) runs with
+// K/V shared through LDS when their lists are dense.
+#ifndef SA_FWD_DENSE_DIV
+#define SA_FWD_DENSE_DIV 4
+#endif
+constexpr int kDenseDiv = SA_FWD_DENSE_DIV;   // dense: mean list >= nblk / kDenseDiv (0: never)
+constexpr int kGroup = 4;     // waves (query blocks) per workgroup
+constexpr int kSlots = 4;     // LDS ring of K/V tiles
+constexpr int kMaxBlocks = 4096;
+
+// Whether the group of query block i (blocks 4 (i/4) .. +3 of head bh) is dense.
+__device__ __forceinline__ bool group_dense(const int32_t* __restrict__ counts, int cap, int nblk, long long bh,
+                                            int i, int dense_div) {
+  const int i0 = i & ~(kGroup - 1);
+  const int active = min(kGroup, nblk - i0);
+  long long sum = 0;
+  for (int w = 0; w < active; ++w) {
+    int c = counts[bh * nblk + i0 + w];
+    sum += c < 0 ? 0 : (c > cap ? cap : c);
+  }
+  return sum * dense_div >= (long long)active * nblk;
+}
+
 // TOK = false: O and LSE slot-major (oc [.., n_pad, D], lse_c [.., n_pad]);
 // TOK = true: straight to token order (o [.., N, D], lse [.., N]), pad slots
 // not written -- the inverse re-indexing fused into the epilogue.
@@ -90,7 +113,7 @@ __device__ __forceinline__ void fwd_row(int row, const u32x4* __restrict__ qc, c
                                         const u32x4* __restrict__ vc, const int32_t* __restrict__ lut,
                                         const int32_t* __restrict__ counts, int cap, const Geom& g,
                                         float sc_log2, bf16* __restrict__ oc, float* __restrict__ lse_c,
-                                        const CubeDiv& cd, int qg_shift) {
+                                        const CubeDiv& cd, int qg_shift, int dense_div = 0) {
   constexpr int NDS = D / 16;     // 16-dim steps of S^T
   constexpr int NDT = D / 32;     // 32-dim tiles of O^T
   constexpr int BLK = 64 * D / 8; // 16-byte units per block
@@ -98,7 +121,7 @@ __device__ __forceinline__ void fwd_row(int row, const u32x4* __restrict__ qc, c
   const long long bh = row / g.nblk;
   const int i = row - (int)(bh * g.nblk);
 
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const int hf = lane >> 5, r = lane & 31;
   // K row fed to A-operand lane r: sigma(8a + 4b + c) = 16(a/2) + 8b + 4(a%2) + c
   const int sig = 16 * (r >> 4) + 8 * ((r >> 2) & 1) + 4 * ((r >> 3) & 1) + (r & 3);
@@ -121,6 +144,9 @@ __device__ __forceinline__ void fwd_row(int row, const u32x4* __restrict__ qc, c
   int count = counts[lrow_i];
   count = count < 0 ? 0 : (count > cap ? cap : count);
   const int32_t* lrow = lut + lrow_i * cap;
+  // rows of dense groups are left to fwd_group_kernel (the check's loads are
+  // queued behind those of Q, so they add no latency of their own)
+  if (dense_div > 0 && group_dense(counts, cap, g.nblk, bh, i, dense_div)) return;
 
   f32x16 acc[NDT][2];
 #pragma unroll
@@ -389,23 +415,437 @@ __device__ __forceinline__ void fwd_row(int row, const u32x4* __restrict__ qc, c
   }
 }
 
-// One workgroup per row: workgroups are dispatched round-robin over the 8
-// XCDs, and the row map gives each XCD a contiguous run of rows so
-// neighbouring query blocks (overlapping lists) share K/V tiles in its L2.
-// With `order` (written by fwd_sched_kernel), workgroup w runs row
-// order[(w % 8) * per_xcd + w / 8] instead.
 template <int D, bool TOK>
 __global__ __launch_bounds__(64) void fwd_kernel(const u32x4* __restrict__ qc, const u32x4* __restrict__ kc,
                                                  const u32x4* __restrict__ vc, const int32_t* __restrict__ lut,
                                                  const int32_t* __restrict__ counts, int cap, Geom g,
                                                  float sc_log2, bf16* __restrict__ oc, float* __restrict__ lse_c,
                                                  RowMap map, CubeDiv cd, int qg_shift,
-                                                 const int32_t* __restrict__ order) {
+                                                 const int32_t* __restrict__ order, int dense_div);
+
+// ---------------------------------------------------------------------------
+// Groups of neighbouring query blocks with K/V shared through LDS.
+//
+// A workgroup of kGroup waves takes kGroup consecutive query blocks of one
+// head (wave w: block 4g + w) and walks the union of their kept lists in
+// ascending block order.  Each K/V tile of the union is copied once from
+// global memory into a ring of kSlots LDS tiles with direct global-to-LDS
+// loads (kSlots - 1 tiles in flight ahead of use); every wave whose own list
+// holds the block reads its MFMA operands from LDS and runs the same block
+// step as fwd_row, in the same (ascending) order, so the result is
+// bit-identical to fwd_row's.  The waves pass one barrier per union entry.
+//
+// Dense lists are where this pays: there the union of four neighbouring
+// lists is little longer than one list, and every tile fetched serves up to
+// four query blocks.  With sparse lists the union is about twice the summed
+// length, so the waves would idle at the barriers; those groups stay with
+// fwd_kernel.  A group is dense when its summed count times dense_div is at
+// least its number of blocks times nblk.  fwd_kernel skips the rows of dense
+// groups and fwd_group_kernel the rows of the others, so every row runs in
+// exactly one of the two launches.  A group whose lists are not strictly
+// ascending ids in [0, nblk) runs each row with fwd_row instead.
+
+// One 1 KB chunk straight from global memory to LDS, 16 bytes per lane:
+// lane l's bytes at gbase + lane16 land at LDS byte address lds + 16 l
+// (gbase and lds wave-uniform, lane16 = 16 * lane).  No register receives
+// data.  The copy is written out here rather than through the builtin: with
+// the builtin the compiler's wait counting makes every LDS read wait for all
+// copies in flight, including those of the tiles ahead, which undoes the
+// prefetch.  The kernel waits for these copies explicitly instead.
+__device__ __forceinline__ void chunk_to_lds(uint32_t lds, const void* gbase, uint32_t lane16) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(lane16), "s"(gbase)
+               : "memory", "m0");
+#else
+  (void)lds;
+  (void)gbase;
+  (void)lane16;
+#endif
+}
+
+// s_waitcnt immediate for vmcnt(n) alone (expcnt and lgkmcnt at their maxima)
+constexpr int wait_vm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
+template <int D>
+struct GroupLds {
+  u32x4 ring[kSlots][2 * (64 * D / 8)];
+  int32_t ulist[kMaxBlocks];              // union entry: id | member mask << 16
+  uint32_t bits[kGroup][kMaxBlocks / 32];
+  int wpre[kMaxBlocks / 32 + 1];
+  int flag_bad;
+};
+
+// One group (row grow of the group map); returns at once unless it is dense.
+template <int D, bool TOK>
+__device__ __forceinline__ void fwd_group(int grow, GroupLds<D>& L, const u32x4* __restrict__ qc,
+                                          const u32x4* __restrict__ kc, const u32x4* __restrict__ vc,
+                                          const int32_t* __restrict__ lut, const int32_t* __restrict__ counts,
+                                          int cap, const Geom& g, float sc_log2, bf16* __restrict__ oc,
+                                          float* __restrict__ lse_c, int ngroups, const CubeDiv& cd,
+                                          int dense_div) {
+  constexpr int NDS = D / 16, NDT = D / 32, BLK = 64 * D / 8;
+  constexpr int PER_WAVE = 2 * BLK / 64 / kGroup;   // 1 KB copies per wave per tile (K then V)
+  auto& ring = L.ring;
+  auto& ulist = L.ulist;
+  auto& bits = L.bits;
+  auto& wpre = L.wpre;
+  auto& flag_bad = L.flag_bad;
+  const long long bh = grow / ngroups;
+  const int i0 = (grow - (int)(bh * ngroups)) * kGroup;
+  if (!group_dense(counts, cap, g.nblk, bh, i0, dense_div)) return;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int i = i0 + wave;
+  const bool active = i < g.nblk;
+  const int nwords = (g.nblk + 31) / 32;
+
+  // ---- union of the group's lists, in LDS -------------------------------
+  for (int t = threadIdx.x; t < kGroup * (kMaxBlocks / 32); t += 64 * kGroup) (&bits[0][0])[t] = 0u;
+  if (threadIdx.x == 0) flag_bad = 0;
+  __syncthreads();
+  int count = 0;
+  const int32_t* lrow = lut + (bh * g.nblk + i) * (long long)cap;
+  if (active) {
+    count = counts[bh * g.nblk + i];
+    count = count < 0 ? 0 : (count > cap ? cap : count);
+  }
+  bool bad = false;
+  for (int e = lane; e < count; e += 64) {
+    const int j = lrow[e];
+    const int jn = e + 1 < count ? lrow[e + 1] : g.nblk;
+    bad |= j < 0 || j >= g.nblk || jn <= j;
+    if (j >= 0 && j < g.nblk) atomicOr(&bits[wave][j >> 5], 1u << (j & 31));
+  }
+  if (__any(bad) && lane == 0) flag_bad = 1;
+  __syncthreads();
+  if (flag_bad) {   // not strictly ascending ids: each wave runs its own row
+    if (active) fwd_row<D, TOK>((int)(bh * g.nblk + i), qc, kc, vc, lut, counts, cap, g, sc_log2, oc, lse_c, cd, 0);
+    return;
+  }
+  // word t of the union: its population goes to wpre[t + 1], then a scan
+  for (int t = threadIdx.x; t < nwords; t += 64 * kGroup) {
+    uint32_t u = 0;
+#pragma unroll
+    for (int w = 0; w < kGroup; ++w) u |= bits[w][t];
+    wpre[t + 1] = __popc(u);
+  }
+  if (threadIdx.x == 0) wpre[0] = 0;
+  __syncthreads();
+  if (wave == 0) {   // inclusive scan of wpre[1 .. nwords], 64 words per pass
+    int carry = 0;
+    for (int t0 = 0; t0 < nwords; t0 += 64) {
+      const int t = t0 + lane;
+      int v = t < nwords ? wpre[t + 1] : 0;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(v, o, 64);
+        v += lane >= o ? y : 0;
+      }
+      if (t < nwords) wpre[t + 1] = v + carry;
+      carry += __shfl(v, 63, 64);
+    }
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < nwords; t += 64 * kGroup) {
+    uint32_t u = 0;
+#pragma unroll
+    for (int w = 0; w < kGroup; ++w) u |= bits[w][t];
+    int pos = wpre[t];
+    while (u) {
+      const int b = __ffs(u) - 1;
+      u &= u - 1;
+      int mask = 0;
+#pragma unroll
+      for (int w = 0; w < kGroup; ++w) mask |= ((bits[w][t] >> b) & 1u) << w;
+      ulist[pos++] = (32 * t + b) | (mask << 16);
+    }
+  }
+  __syncthreads();
+  const int U = wpre[nwords];
+
+  // ---- per-wave state (as fwd_row) --------------------------------------
+  const int hf = lane >> 5, r = lane & 31;
+  const int sig = 16 * (r >> 4) + 8 * ((r >> 2) & 1) + 4 * ((r >> 3) & 1) + (r & 3);
+  const int kpos = hf * 32 + sig;
+  const long long head = bh * (g.n_pad / 64) * (long long)BLK;
+  const u32x4* kh = kc + head;
+  const u32x4* vh = vc + head;
+  u32x4 qreg[2 * NDS];
+  {
+    const u32x4* qb = qc + head + (long long)(active ? i : 0) * BLK;
+#pragma unroll
+    for (int c = 0; c < 2 * NDS; ++c) qreg[c] = qb[c * 64 + lane];
+  }
+  f32x16 acc[NDT][2];
+#pragma unroll
+  for (int t = 0; t < NDT; ++t)
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[t][qt][e] = 0.f;
+  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+  u32x4 kreg[2][NDS];
+  u32x4 vreg[NDT][4];
+  int lt, lh, lw;
+  slot_offsets(g, lane, lt, lh, lw);
+  auto real_mask = [&](int j) -> uint64_t {
+    const uint32_t jj = (uint32_t)j;
+    const uint32_t rr = fdiv(jj, cd.w);
+    const int bw = (int)jj - (int)rr * g.nw;
+    const int bt = (int)fdiv(rr, cd.h);
+    const int bhh = (int)rr - bt * g.nh;
+    const int rt = min(g.ct, g.frames - bt * g.ct);
+    const int rh = min(g.ch, g.height - bhh * g.ch);
+    const int rw = min(g.cw, g.width - bw * g.cw);
+    return ballot(lt < rt && lh < rh && lw < rw);
+  };
+  auto lane_mask = [&](uint64_t real) -> uint32_t {
+    return (uint32_t)((real >> (8 * hf)) & 0xffu) | ((uint32_t)((real >> (16 + 8 * hf)) & 0xffu) << 8) |
+           ((uint32_t)((real >> (32 + 8 * hf)) & 0xffu) << 16) |
+           ((uint32_t)((real >> (48 + 8 * hf)) & 0xffu) << 24);
+  };
+  constexpr int G1 = 2 * NDS;
+  constexpr int G2 = 4 * NDT;
+  auto gemm1_step = [&](f32x16 (&st)[2], const u32x4& q, int step) {
+    const int ds = step >> 1, kt = step & 1;
+    st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kreg[kt][ds]), as_bf16x8(q), st[kt], 0, 0, 0);
+  };
+  auto qchunk = [&](int qt, int ds) { return qreg[qt * NDS + ds]; };
+  auto gemm1_first = [&](f32x16 (&st)[2], const u32x4& q, uint64_t real) {
+    if (real == ~0ull) {
+      const f32x16 z = {};
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+        st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kreg[kt][0]), as_bf16x8(q), z, 0, 0, 0);
+    } else {
+      uint32_t lm = lane_mask(real);
+      asm volatile("" : "+v"(lm));
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        f32x16 init;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) init[e] = ((lm >> (16 * kt + e)) & 1u) ? 0.f : -INFINITY;
+        st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kreg[kt][0]), as_bf16x8(q), init, 0, 0, 0);
+      }
+    }
+  };
+  auto gemm1_half = [&](int qt, f32x16 (&st)[2], uint64_t real) {
+    gemm1_first(st, qchunk(qt, 0), real);
+#pragma unroll
+    for (int k = 2; k < G1; ++k) gemm1_step(st, qchunk(qt, k >> 1), k);
+  };
+  auto exp_pair = [&](const f32x16 (&st)[2], uint32_t (&pw)[2][8], float nmu, float& ls, int step) {
+    const int kt = step >> 3, e = 2 * (step & 7);
+    const float p0 = __builtin_amdgcn_exp2f(fmaf(st[kt][e], sc_log2, nmu));
+    const float p1 = __builtin_amdgcn_exp2f(fmaf(st[kt][e + 1], sc_log2, nmu));
+    ls += p0 + p1;
+    pw[kt][e >> 1] = pack_bf16x2(p0, p1);
+  };
+  auto half_max = [&](const f32x16 (&st)[2]) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, st[kt][e]);
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+    return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * sc_log2;
+  };
+  auto gemm2_step = [&](int qt, const uint32_t (&pw)[2][8], int step) {
+    const int ks = step / NDT, dt = step % NDT;
+    const int kt = ks >> 1, o4 = 4 * (ks & 1);
+    const u32x4 bw = {pw[kt][o4], pw[kt][o4 + 1], pw[kt][o4 + 2], pw[kt][o4 + 3]};
+    acc[dt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vreg[dt][ks]), as_bf16x8(bw), acc[dt][qt],
+                                                          0, 0, 0);
+  };
+  auto pin = [](const uint32_t (&pw)[2][8]) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) asm volatile("" ::"v"(pw[kt][e]));
+  };
+  auto settle = [&](int qt, const f32x16 (&st)[2], uint32_t (&pw)[2][8], float& ls) {
+    const bool trig = !(ls <= kSumLimit) || m[qt] == -INFINITY;
+    if (__any(trig)) {
+      const float mx = half_max(st);
+      const float mn = fmaxf(m[qt], mx);
+      const float alpha = (m[qt] == -INFINITY || mn == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[qt] - mn);
+      m[qt] = mn;
+      l[qt] *= alpha;
+#pragma unroll
+      for (int t = 0; t < NDT; ++t)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[t][qt][e] *= alpha;
+      const float nmu = m[qt] == -INFINITY ? 0.f : -m[qt];
+      ls = 0.f;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) exp_pair(st, pw, nmu, ls, k);
+    }
+    l[qt] += ls;
+  };
+  auto neg_m = [&](int qt) { return m[qt] == -INFINITY ? 0.f : -m[qt]; };
+
+  // ---- the union walk -----------------------------------------------------
+  // copies of entry e into slot e % kSlots: wave w takes the 1 KB chunks
+  // [w PER_WAVE, (w + 1) PER_WAVE) of the K tile followed by the V tile
+  const uint32_t ring0 = (uint32_t)(size_t)(__attribute__((address_space(3))) const char*)(const char*)&ring[0][0];
+  const uint32_t lane16 = 16u * (uint32_t)lane;
+  auto issue = [&](int e) {
+    const int j = __builtin_amdgcn_readfirstlane(ulist[e] & 0xffff);
+    const u32x4* kb = kh + (long long)j * BLK;
+    const u32x4* vb = vh + (long long)j * BLK;
+    const uint32_t dst = ring0 + (uint32_t)((e % kSlots) * 2 * BLK * 16);
+#pragma unroll
+    for (int c = 0; c < PER_WAVE; ++c) {
+      const int ch = wave * PER_WAVE + c;   // chunk of the 2 BLK / 64 in the slot
+      const u32x4* src = ch < BLK / 64 ? kb + ch * 64 : vb + (ch - BLK / 64) * 64;
+      chunk_to_lds(dst + (uint32_t)(ch * 1024), src, lane16);
+    }
+  };
+  // everything loaded so far (lists, counts, Q) has landed before the first
+  // copy is queued, so the waits below count copies only
+  __builtin_amdgcn_s_waitcnt(wait_vm(0));
+#pragma unroll
+  for (int e = 0; e < kSlots - 1; ++e)
+    if (e < U) issue(e);
+  f32x16 stA[2], stB[2];
+  uint32_t pA[2][8], pB[2][8];
+  for (int u = 0; u < U; ++u) {
+    // this entry's copies are done once only the later entries' remain
+    const int later = min(U - 1 - u, kSlots - 2);
+    if (later >= 2)
+      __builtin_amdgcn_s_waitcnt(wait_vm(2 * PER_WAVE));
+    else if (later == 1)
+      __builtin_amdgcn_s_waitcnt(wait_vm(PER_WAVE));
+    else
+      __builtin_amdgcn_s_waitcnt(wait_vm(0));
+    // every wave's copies of this entry have landed, and every wave is done
+    // with the slot the next copy refills
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (u + kSlots - 1 < U) issue(u + kSlots - 1);
+    const int ent = ulist[u];
+    if (!((ent >> (16 + wave)) & 1)) continue;
+    const int j = ent & 0xffff;
+    const u32x4* ks = &ring[u % kSlots][0];
+    const u32x4* vs = ks + BLK;
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) kreg[kt][ds] = ks[(kt * NDS + ds) * 64 + kpos];
+    const uint64_t real = real_mask(j);
+    gemm1_half(0, stA, real);
+    {
+      const float nmu = neg_m(0);
+      float ls = 0.f;
+      gemm1_first(stB, qchunk(1, 0), real);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        if (k + 2 < G1) gemm1_step(stB, qchunk(1, (k + 2) >> 1), k + 2);
+        exp_pair(stA, pA, nmu, ls, k);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      pin(pA);
+#pragma unroll
+      for (int ks4 = 0; ks4 < 4; ++ks4)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) vreg[dt][ks4] = vs[(dt * 4 + ks4) * 64 + lane];
+      settle(0, stA, pA, ls);
+    }
+    {
+      const float nmu = neg_m(1);
+      float ls = 0.f;
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        if (k < G2) gemm2_step(0, pA, k);
+        exp_pair(stB, pB, nmu, ls, k);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      pin(pB);
+      settle(1, stB, pB, ls);
+    }
+#pragma unroll
+    for (int k = 0; k < G2; ++k) gemm2_step(1, pB, k);
+  }
+  if (!active) return;
+
+  // ---- epilogue (as fwd_row) --------------------------------------------
+  const uint64_t qreal = real_mask(i);
+  bf16* ob = oc + (bh * g.n_pad + (long long)i * 64) * D;
+  float* lb = lse_c + bh * g.n_pad + (long long)i * 64;
+  int ct0 = 0, ch0 = 0, cw0 = 0;
+  if (TOK) {
+    const uint32_t rr = fdiv((uint32_t)i, cd.w);
+    cw0 = (i - (int)rr * g.nw) * g.cw;
+    const int bt = (int)fdiv(rr, cd.h);
+    ch0 = ((int)rr - bt * g.nh) * g.ch;
+    ct0 = bt * g.ct;
+  }
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const float ltot = l[qt] + __shfl_xor(l[qt], 32, 64);
+    const int q = 32 * qt + r;
+    const bool real_q = (qreal >> q) & 1ull;
+    const bool live = real_q && ltot > 0.f;
+    const float inv = live ? 1.f / ltot : 0.f;
+    bf16* orow = ob + (long long)q * D;
+    long long tok = 0;
+    if (TOK) {
+      int tt, hh, ww;
+      slot_offsets(g, q, tt, hh, ww);
+      tok = ((long long)(ct0 + tt) * g.height + (ch0 + hh)) * g.width + (cw0 + ww);
+      orow = oc + (bh * g.n_real + tok) * D;
+      if (!real_q) continue;
+    }
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const u32x2 v = {pack_bf16x2(acc[dt][qt][4 * a] * inv, acc[dt][qt][4 * a + 1] * inv),
+                         pack_bf16x2(acc[dt][qt][4 * a + 2] * inv, acc[dt][qt][4 * a + 3] * inv)};
+        *reinterpret_cast<u32x2*>(orow + 32 * dt + 8 * a + 4 * hf) = v;
+      }
+    const float lse_q = live ? (m[qt] + __log2f(ltot)) * kLn2 : -INFINITY;
+    if (hf == 0) {
+      if (TOK)
+        lse_c[bh * g.n_real + tok] = lse_q;
+      else
+        lb[q] = lse_q;
+    }
+  }
+}
+
+// One workgroup per group (row of the group map).
+template <int D, bool TOK>
+__global__ __launch_bounds__(64 * kGroup) void fwd_group_kernel(
+    const u32x4* __restrict__ qc, const u32x4* __restrict__ kc, const u32x4* __restrict__ vc,
+    const int32_t* __restrict__ lut, const int32_t* __restrict__ counts, int cap, Geom g, float sc_log2,
+    bf16* __restrict__ oc, float* __restrict__ lse_c, RowMap map, int ngroups, CubeDiv cd, int dense_div) {
+  __shared__ GroupLds<D> L;
+  const int grow = row_of_workgroup(blockIdx.x, map);
+  if (grow < 0) return;
+  fwd_group<D, TOK>(grow, L, qc, kc, vc, lut, counts, cap, g, sc_log2, oc, lse_c, ngroups, cd, dense_div);
+}
+
+// One workgroup per row: workgroups are dispatched round-robin over the 8
+// XCDs, and the row map gives each XCD a contiguous run of rows so
+// neighbouring query blocks (overlapping lists) share K/V tiles in its L2.
+// With `order` (written by fwd_sched_kernel), workgroup w runs row
+// order[(w % 8) * per_xcd + w / 8] instead.  With dense_div > 0 the rows of
+// dense groups are left to fwd_group_kernel.
+template <int D, bool TOK>
+__global__ __launch_bounds__(64) void fwd_kernel(const u32x4* __restrict__ qc, const u32x4* __restrict__ kc,
+                                                 const u32x4* __restrict__ vc, const int32_t* __restrict__ lut,
+                                                 const int32_t* __restrict__ counts, int cap, Geom g,
+                                                 float sc_log2, bf16* __restrict__ oc, float* __restrict__ lse_c,
+                                                 RowMap map, CubeDiv cd, int qg_shift,
+                                                 const int32_t* __restrict__ order, int dense_div) {
   const int row = order != nullptr
                       ? order[(long long)(blockIdx.x % kXcds) * map.per_xcd + blockIdx.x / kXcds]
                       : row_of_workgroup(blockIdx.x, map);
   if (row < 0) return;
-  fwd_row<D, TOK>(row, qc, kc, vc, lut, counts, cap, g, sc_log2, oc, lse_c, cd, qg_shift);
+  fwd_row<D, TOK>(row, qc, kc, vc, lut, counts, cap, g, sc_log2, oc, lse_c, cd, qg_shift, dense_div);
 }
 
 // ---------------------------------------------------------------------------
@@ -523,12 +963,26 @@ static hipError_t launch_fwd_any(const void* qc, const void* kc, const void* vc,
   const u32x4* q = static_cast<const u32x4*>(qc);
   const u32x4* k = static_cast<const u32x4*>(kc);
   const u32x4* v = static_cast<const u32x4*>(vc);
+  // dense groups go to the LDS-sharing kernel (one list per cube only)
+  const int dense_div = (qg_shift == 0 && g.nblk <= kMaxBlocks) ? kDenseDiv : 0;
+  bf16* o = static_cast<bf16*>(out);
   if (g.d == 128)
-    fwd_kernel<128, TOK><<<grid, 64, 0, s>>>(q, k, v, lut, counts, cap, g, sc_log2, static_cast<bf16*>(out),
-                                             lse_out, map, cd, qg_shift, order);
+    fwd_kernel<128, TOK><<<grid, 64, 0, s>>>(q, k, v, lut, counts, cap, g, sc_log2, o, lse_out, map, cd, qg_shift,
+                                             order, dense_div);
   else
-    fwd_kernel<64, TOK><<<grid, 64, 0, s>>>(q, k, v, lut, counts, cap, g, sc_log2, static_cast<bf16*>(out),
-                                            lse_out, map, cd, qg_shift, order);
+    fwd_kernel<64, TOK><<<grid, 64, 0, s>>>(q, k, v, lut, counts, cap, g, sc_log2, o, lse_out, map, cd, qg_shift,
+                                            order, dense_div);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || dense_div == 0) return e;
+  const int ngroups = (g.nblk + kGroup - 1) / kGroup;
+  const RowMap gmap = make_rowmap(ngroups, g.batch * g.heads);
+  const dim3 ggrid((unsigned)((long long)gmap.per_xcd * kXcds));
+  if (g.d == 128)
+    fwd_group_kernel<128, TOK><<<ggrid, 64 * kGroup, 0, s>>>(q, k, v, lut, counts, cap, g, sc_log2, o, lse_out,
+                                                             gmap, ngroups, cd, dense_div);
+  else
+    fwd_group_kernel<64, TOK><<<ggrid, 64 * kGroup, 0, s>>>(q, k, v, lut, counts, cap, g, sc_log2, o, lse_out,
+                                                            gmap, ngroups, cd, dense_div);
   return hipGetLastError();
 }
 

@@ -477,7 +477,13 @@ size_t sparse_attn_fwd_workspace_bytes(const sa_geom* g);
  * softmax in float32.  scale <= 0 selects 1/sqrt(head_dim).
  * One workgroup per query block; the rows go to the 8 XCDs in sweeps of
  * neighbouring query blocks (four XCDs per head), so blocks with overlapping
- * lists share K/V in an XCD's L2.  With workspace NULL that sweep order is
+ * lists share K/V in an XCD's L2.  Groups of four neighbouring query blocks
+ * whose lists are dense (summed count at least nblk per block / 4) run
+ * instead in a second kernel whose four wavefronts walk the union of their
+ * lists together, each K/V tile copied once into an LDS ring (direct
+ * global-to-LDS loads) and read from there by every wavefront whose list
+ * holds it, in the same order: the results are the same bytes, with a
+ * quarter or less of the tile traffic.  With workspace NULL that sweep order is
  * used as is, which balances rows of similar list lengths.  With a workspace
  * (>= sparse_attn_fwd_workspace_bytes, else SA_ERR_CAPACITY) a small kernel
  * first writes a count-balanced order into it: each quarter-head run of the

@@ -329,6 +329,50 @@ def test_forward_row_order_gives_identical_bytes(case):
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
 
 
+@pytest.mark.parametrize("d,grid", [(128, (8, 20, 24)), (64, (5, 7, 9)), (128, (6, 6, 6))])
+def test_dense_groups_shared_kernel_gives_identical_bytes(d, grid):
+    """Rows of groups of four neighbouring query blocks whose lists are dense
+    run in the kernel that shares K/V tiles through LDS; the same row in a
+    sparse group runs in the one-wave kernel.  Row 4g keeps one random
+    ascending list (about half the blocks, some partial blocks among them) in
+    both calls; in the first its three neighbours hold dense lists too, in
+    the second they are empty.  Its output must be the same bytes, and the
+    first call must match the oracle."""
+    say(f"[dense groups d={d} grid={grid}]")
+    wl, g, og, q, k, v = _small(d=d, grid=grid, heads=2)
+    n = og.nblk
+    rng = np.random.default_rng(11)
+    lut = np.full((1, 2, n, n), -1, dtype=np.int32)
+    counts = np.zeros((1, 2, n), dtype=np.int32)
+    for h in range(2):
+        for i in range(n):
+            c = int(rng.integers(n // 3, n // 2 + 2))
+            ids = np.sort(rng.choice(n, size=min(c, n), replace=False))
+            lut[0, h, i, :ids.size] = ids
+            counts[0, h, i] = ids.size
+    qd, kd, vd = reorder3(q.to(DEV), k.to(DEV), v.to(DEV), g)
+    _, n_real, n_pad = sa.sparse_attn_geometry(g)
+    lut_d = torch.from_numpy(lut).to(DEV)
+    outs = []
+    for sparse_neighbours in (False, True):
+        c = counts.copy()
+        if sparse_neighbours:
+            c[:, :, np.arange(n) % 4 != 0] = 0
+        oc = torch.empty((1, 2, n_pad, d), dtype=torch.bfloat16, device=DEV)
+        lse_c = torch.empty((1, 2, n_pad), dtype=torch.float32, device=DEV)
+        sa.sparse_attn_fwd(qd, kd, vd, lut_d, torch.from_numpy(c).to(DEV), n, g, 0.0, oc, lse_c, None)
+        outs.append((oc.view(1, 2, n, 64, d), lse_c.view(1, 2, n, 64)))
+    torch.cuda.synchronize()
+    lead = np.arange(n) % 4 == 0
+    assert torch.equal(outs[0][0][:, :, lead], outs[1][0][:, :, lead])
+    assert torch.equal(outs[0][1][:, :, lead], outs[1][1][:, :, lead])
+    qc, kc, vc = (O.reorder(to64(t), og) for t in (q, k, v))
+    o_ref, lse_ref = O.sparse_attention(qc, kc, vc, lut, counts, og)
+    real = O.real_slots(og)
+    mx, mean = attn_errors(to64(outs[0][0].reshape(1, 2, n_pad, d)), o_ref, real)
+    assert mx <= O_MAX_ABS and mean <= O_MEAN_ABS
+
+
 def test_keep_nothing_gives_zero_and_neg_inf():
     say("[edge keep-none]")
     wl, g, og, q, k, v = _small()
