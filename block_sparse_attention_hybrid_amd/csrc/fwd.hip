@@ -81,12 +81,27 @@ struct CubeDiv {
   FastDiv w, h;
 };
 
+// Start value of a score accumulator: -inf for a pad key (bit b of pad set),
+// 0 otherwise.  The sign-extended one-bit field is all ones or zero, and its
+// AND with the bits of -inf gives -inf or +0: two plain VALU operations (the
+// opaque copy keeps the compiler from turning them back into a compare and a
+// select, which costs a VCC hazard wait per element).
+__device__ __forceinline__ float pad_start(uint32_t pad, int b) {
+  int t = __builtin_amdgcn_sbfe((int)pad, b, 1);
+  asm volatile("" : "+v"(t));
+  return __uint_as_float((uint32_t)t & 0xff800000u);
+}
+
 // Groups of neighbouring query blocks that fwd_group_kernel (below) runs with
 // K/V shared through LDS when their lists are dense.
 #ifndef SA_FWD_DENSE_DIV
 #define SA_FWD_DENSE_DIV 4
 #endif
 constexpr int kDenseDiv = SA_FWD_DENSE_DIV;   // dense: mean list >= nblk / kDenseDiv (0: never)
+#ifndef SA_FWD_DENSE_HEAD_MB
+#define SA_FWD_DENSE_HEAD_MB 32
+#endif
+constexpr size_t kDenseHeadBytes = (size_t)SA_FWD_DENSE_HEAD_MB << 20;   // K/V bytes per head
 constexpr int kGroup = 4;     // waves (query blocks) per workgroup
 constexpr int kSlots = 4;     // LDS ring of K/V tiles
 constexpr int kMaxBlocks = 4096;
@@ -225,13 +240,12 @@ __device__ __forceinline__ void fwd_row(int row, const u32x4* __restrict__ qc, c
       for (int kt = 0; kt < 2; ++kt)
         st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kreg[kt][0]), as_bf16x8(q), z, 0, 0, 0);
     } else {
-      uint32_t lm = lane_mask(real);
-      asm volatile("" : "+v"(lm));
+      const uint32_t pad = ~lane_mask(real);   // bit set: pad key
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         f32x16 init;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) init[e] = ((lm >> (16 * kt + e)) & 1u) ? 0.f : -INFINITY;
+        for (int e = 0; e < 16; ++e) init[e] = pad_start(pad, 16 * kt + e);
         st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kreg[kt][0]), as_bf16x8(q), init, 0, 0, 0);
       }
     }
@@ -618,13 +632,12 @@ __device__ __forceinline__ void fwd_group(int grow, GroupLds<D>& L, const u32x4*
       for (int kt = 0; kt < 2; ++kt)
         st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kreg[kt][0]), as_bf16x8(q), z, 0, 0, 0);
     } else {
-      uint32_t lm = lane_mask(real);
-      asm volatile("" : "+v"(lm));
+      const uint32_t pad = ~lane_mask(real);   // bit set: pad key
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         f32x16 init;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) init[e] = ((lm >> (16 * kt + e)) & 1u) ? 0.f : -INFINITY;
+        for (int e = 0; e < 16; ++e) init[e] = pad_start(pad, 16 * kt + e);
         st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kreg[kt][0]), as_bf16x8(q), init, 0, 0, 0);
       }
     }
@@ -963,8 +976,14 @@ static hipError_t launch_fwd_any(const void* qc, const void* kc, const void* vc,
   const u32x4* q = static_cast<const u32x4*>(qc);
   const u32x4* k = static_cast<const u32x4*>(kc);
   const u32x4* v = static_cast<const u32x4*>(vc);
-  // dense groups go to the LDS-sharing kernel (one list per cube only)
-  const int dense_div = (qg_shift == 0 && g.nblk <= kMaxBlocks) ? kDenseDiv : 0;
+  // dense groups go to the LDS-sharing kernel (one list per cube only), where a
+  // head's K/V is too large for the L2 of the four XCDs that sweep it (16 MB):
+  // there the one-wave kernel's dense sweeps run from beyond L2 (720p: 46 MB per
+  // head, 0.27 of the bf16 peak against 0.35 for the group kernel), while with
+  // smaller heads it keeps up (480p: 20 MB, 0.39 against 0.35)
+  const size_t kv_head = (size_t)g.nblk * 64 * g.d * 2 * 2;
+  const int dense_div =
+      (qg_shift == 0 && g.nblk <= kMaxBlocks && kv_head >= kDenseHeadBytes) ? kDenseDiv : 0;
   bf16* o = static_cast<bf16*>(out);
   if (g.d == 128)
     fwd_kernel<128, TOK><<<grid, 64, 0, s>>>(q, k, v, lut, counts, cap, g, sc_log2, o, lse_out, map, cd, qg_shift,

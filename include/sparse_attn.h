@@ -477,7 +477,8 @@ size_t sparse_attn_fwd_workspace_bytes(const sa_geom* g);
  * softmax in float32.  scale <= 0 selects 1/sqrt(head_dim).
  * One workgroup per query block; the rows go to the 8 XCDs in sweeps of
  * neighbouring query blocks (four XCDs per head), so blocks with overlapping
- * lists share K/V in an XCD's L2.  Groups of four neighbouring query blocks
+ * lists share K/V in an XCD's L2.  When a head's K/V is 32 MiB or more
+ * (nblk >= 1024 at head_dim 128), groups of four neighbouring query blocks
  * whose lists are dense (summed count at least nblk per block / 4) run
  * instead in a second kernel whose four wavefronts walk the union of their
  * lists together, each K/V tile copied once into an LDS ring (direct
