@@ -119,121 +119,84 @@ __device__ __forceinline__ bool group_dense(const int32_t* __restrict__ counts, 
   return sum * dense_div >= (long long)active * nblk;
 }
 
-// TOK = false: O and LSE slot-major (oc [.., n_pad, D], lse_c [.., n_pad]);
-// TOK = true: straight to token order (o [.., N, D], lse [.., N]), pad slots
-// not written -- the inverse re-indexing fused into the epilogue.
-// One query block (row of batch*heads*nblk) of the forward, by one wavefront.
-template <int D, bool TOK>
-__device__ __forceinline__ void fwd_row(int row, const u32x4* __restrict__ qc, const u32x4* __restrict__ kc,
-                                        const u32x4* __restrict__ vc, const int32_t* __restrict__ lut,
-                                        const int32_t* __restrict__ counts, int cap, const Geom& g,
-                                        float sc_log2, bf16* __restrict__ oc, float* __restrict__ lse_c,
-                                        const CubeDiv& cd, int qg_shift, int dense_div = 0) {
-  constexpr int NDS = D / 16;     // 16-dim steps of S^T
-  constexpr int NDT = D / 32;     // 32-dim tiles of O^T
-  constexpr int BLK = 64 * D / 8; // 16-byte units per block
+// The state of one wavefront's query block (64 queries, two 32-query halves)
+// and the steps of one kept key block, shared by both forward kernels: Q^T
+// operands, the O^T accumulators, the running reference m and sum l per
+// half, and the K and V operands of the current block (filled by the caller,
+// from global memory or from LDS).
+template <int D>
+struct RowState {
+  static constexpr int NDS = D / 16;       // 16-dim steps of S^T
+  static constexpr int NDT = D / 32;       // 32-dim tiles of O^T
+  static constexpr int G1 = 2 * NDS;       // MFMA steps of S^T for one half
+  static constexpr int G2 = 4 * NDT;       // MFMA steps of O^T for one half
 
-  const long long bh = row / g.nblk;
-  const int i = row - (int)(bh * g.nblk);
-
-  const int lane = threadIdx.x & 63;
-  const int hf = lane >> 5, r = lane & 31;
-  // K row fed to A-operand lane r: sigma(8a + 4b + c) = 16(a/2) + 8b + 4(a%2) + c
-  const int sig = 16 * (r >> 4) + 8 * ((r >> 2) & 1) + 4 * ((r >> 3) & 1) + (r & 3);
-  const int kpos = hf * 32 + sig;
-
-  const long long head = bh * (g.n_pad / 64) * (long long)BLK;
-  const u32x4* qb = qc + head + (long long)i * BLK;
-  const u32x4* kh = kc + head;
-  const u32x4* vh = vc + head;
-
-  // Q^T operand chunks, in registers for the whole row
-  u32x4 qreg[2 * NDS];
-#pragma unroll
-  for (int c = 0; c < 2 * NDS; ++c) qreg[c] = qb[c * 64 + lane];
-
-  // the list of this query block: one per cube, or one per group of
-  // 2^qg_shift consecutive cubes (asymmetric query blocks)
-  const int nlists = (g.nblk + (1 << qg_shift) - 1) >> qg_shift;
-  const long long lrow_i = bh * nlists + (i >> qg_shift);
-  int count = counts[lrow_i];
-  count = count < 0 ? 0 : (count > cap ? cap : count);
-  const int32_t* lrow = lut + lrow_i * cap;
-  // rows of dense groups are left to fwd_group_kernel (the check's loads are
-  // queued behind those of Q, so they add no latency of their own)
-  if (dense_div > 0 && group_dense(counts, cap, g.nblk, bh, i, dense_div)) return;
-
+  u32x4 qreg[2 * NDS];      // Q^T operand chunks, in registers for the whole row
+  u32x4 kreg[2][NDS];       // K operands of the current block: [32-key tile][dim step]
+  u32x4 vreg[NDT][4];       // V operands: [32-dim tile][16-key step]
   f32x16 acc[NDT][2];
-#pragma unroll
-  for (int t = 0; t < NDT; ++t)
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[t][qt][e] = 0.f;
-  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+  float m[2], l[2];
+  float sc_log2;
+  int hf;                   // lane / 32
+  int lt, lh, lw;           // cube offsets of this lane's slot
+  const Geom* g;
+  CubeDiv cd;
 
-  u32x4 kreg[2][NDS];
-  u32x4 vreg[NDT][4];
-  auto valid_id = [&](int j) { return j >= 0 && j < g.nblk; };
-  // bit s set iff slot s of block j holds a real token (one slot per lane)
-  // slot offsets of this lane's key slot, fixed for the whole row
-  int lt, lh, lw;
-  slot_offsets(g, lane, lt, lh, lw);
+  __device__ __forceinline__ void init(const Geom& geom, const CubeDiv& div, float scl2, int lane) {
+    g = &geom;
+    cd = div;
+    sc_log2 = scl2;
+    hf = lane >> 5;
+    slot_offsets(geom, lane, lt, lh, lw);
+#pragma unroll
+    for (int t = 0; t < NDT; ++t)
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[t][qt][e] = 0.f;
+    m[0] = m[1] = -INFINITY;
+    l[0] = l[1] = 0.f;
+  }
+
   // bit s set iff slot s of block j holds a real token; the cube coordinates
   // are uniform (scalar unit), only partial cubes need a per-lane test
-  auto real_mask = [&](int j) -> uint64_t {
-    const bool ok = valid_id(j);
+  __device__ __forceinline__ uint64_t real_mask(int j) const {
+    const bool ok = j >= 0 && j < g->nblk;
     const uint32_t jj = ok ? (uint32_t)j : 0u;
     const uint32_t r = fdiv(jj, cd.w);
-    const int bw = (int)jj - (int)r * g.nw;
+    const int bw = (int)jj - (int)r * g->nw;
     const int bt = (int)fdiv(r, cd.h);
-    const int bh = (int)r - bt * g.nh;
-    const int rt = min(g.ct, g.frames - bt * g.ct);
-    const int rh = min(g.ch, g.height - bh * g.ch);
-    const int rw = min(g.cw, g.width - bw * g.cw);
+    const int bhh = (int)r - bt * g->nh;
+    const int rt = min(g->ct, g->frames - bt * g->ct);
+    const int rh = min(g->ch, g->height - bhh * g->ch);
+    const int rw = min(g->cw, g->width - bw * g->cw);
     const uint64_t b = ballot(lt < rt && lh < rh && lw < rw);
     return ok ? b : 0ull;
-  };
-  // both tiles are requested in the order the products consume them, so a
-  // product waits only for the chunks it uses
-  auto load_k = [&](int j) {
-    const u32x4* kb = kh + (long long)(valid_id(j) ? j : 0) * BLK;
-#pragma unroll
-    for (int ds = 0; ds < NDS; ++ds)
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) kreg[kt][ds] = kb[(kt * NDS + ds) * 64 + kpos];
-  };
-  auto load_v = [&](int j) {
-    const u32x4* vb = vh + (long long)(valid_id(j) ? j : 0) * BLK;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) vreg[dt][ks] = vb[(dt * 4 + ks) * 64 + lane];
-  };
+  }
 
-  auto lane_mask = [&](uint64_t real) -> uint32_t {
-    // this lane's 32 key bits: byte (kt, g) = keys 32 kt + 16 g + 8 hf .. +7
+  // this lane's 32 key bits: byte (kt, g) = keys 32 kt + 16 g + 8 hf .. +7
+  __device__ __forceinline__ uint32_t lane_mask(uint64_t real) const {
     return (uint32_t)((real >> (8 * hf)) & 0xffu) | ((uint32_t)((real >> (16 + 8 * hf)) & 0xffu) << 8) |
            ((uint32_t)((real >> (32 + 8 * hf)) & 0xffu) << 16) |
            ((uint32_t)((real >> (48 + 8 * hf)) & 0xffu) << 24);
-  };  constexpr int G1 = 2 * NDS;       // MFMA steps of S^T for one half
-  constexpr int G2 = 4 * NDT;       // MFMA steps of O^T for one half
+  }
 
-  // ---- stages of one block, for one 32-query half qt ---------------------
+  __device__ __forceinline__ u32x4 qchunk(int qt, int ds) const { return qreg[qt * NDS + ds]; }
+
   // S^T = K Q^T, one MFMA per step (16 steps: ds = step / 2, kt = step % 2);
   // q holds the Q^T chunk of this step's ds
-  auto gemm1_step = [&](f32x16 (&st)[2], const u32x4& q, int step) {
+  __device__ __forceinline__ void gemm1_step(f32x16 (&st)[2], const u32x4& q, int step) {
     const int ds = step >> 1, kt = step & 1;
     st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kreg[kt][ds]), as_bf16x8(q), st[kt], 0, 0, 0);
-  };
-  auto qchunk = [&](int qt, int ds) { return qreg[qt * NDS + ds]; };
+  }
+
   // Register e of tile kt holds key 32 kt + 16 (e / 8) + 8 hf + e % 8, i.e.
   // bit 16 kt + e of the lane's key mask.  Pad keys of a partial block get
   // S = -inf (so P = 0 and they never set the max) by starting their
   // accumulators at -inf instead of 0: the first MFMA of each tile reads the
   // start value, so a full block (wave-uniform branch) keeps the free zero
-  // operand and a partial one pays 32 selects that wait on nothing.
-  auto gemm1_first = [&](f32x16 (&st)[2], const u32x4& q, uint64_t real) {
+  // operand and a partial one pays two plain operations per start value.
+  __device__ __forceinline__ void gemm1_first(f32x16 (&st)[2], const u32x4& q, uint64_t real) {
     if (real == ~0ull) {
       const f32x16 z = {};
 #pragma unroll
@@ -249,23 +212,27 @@ __device__ __forceinline__ void fwd_row(int row, const u32x4* __restrict__ qc, c
         st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kreg[kt][0]), as_bf16x8(q), init, 0, 0, 0);
       }
     }
-  };
+  }
+
   // the whole S^T half in one region
-  auto gemm1_half = [&](int qt, f32x16 (&st)[2], uint64_t real) {
+  __device__ __forceinline__ void gemm1_half(int qt, f32x16 (&st)[2], uint64_t real) {
     gemm1_first(st, qchunk(qt, 0), real);
 #pragma unroll
     for (int k = 2; k < G1; ++k) gemm1_step(st, qchunk(qt, k >> 1), k);
-  };
+  }
+
   // one register pair of P = exp2(scale S - m) (bf16-packed) and its sum
-  auto exp_pair = [&](const f32x16 (&st)[2], uint32_t (&pw)[2][8], float nmu, float& ls, int step) {
+  __device__ __forceinline__ void exp_pair(const f32x16 (&st)[2], uint32_t (&pw)[2][8], float nmu, float& ls,
+                                           int step) const {
     const int kt = step >> 3, e = 2 * (step & 7);
     const float p0 = __builtin_amdgcn_exp2f(fmaf(st[kt][e], sc_log2, nmu));
     const float p1 = __builtin_amdgcn_exp2f(fmaf(st[kt][e + 1], sc_log2, nmu));
     ls += p0 + p1;
     pw[kt][e >> 1] = pack_bf16x2(p0, p1);
-  };
+  }
+
   // row max of one half (raw scores; the scale is positive)
-  auto half_max = [&](const f32x16 (&st)[2]) {
+  __device__ __forceinline__ float half_max(const f32x16 (&st)[2]) const {
     float mx = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
@@ -274,32 +241,34 @@ __device__ __forceinline__ void fwd_row(int row, const u32x4* __restrict__ qc, c
     // the two half-waves hold the two halves of every query's keys
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
     return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * sc_log2;
-  };
+  }
+
   // O^T += V^T P^T, one MFMA per step (16 steps: ks = step / NDT, dt =
   // step % NDT at d = 128); k-step ks covers keys 16 ks .. +15 = registers
   // 8 (ks % 2) .. +7 of tile ks / 2
-  auto gemm2_step = [&](int qt, const uint32_t (&pw)[2][8], int step) {
+  __device__ __forceinline__ void gemm2_step(int qt, const uint32_t (&pw)[2][8], int step) {
     const int ks = step / NDT, dt = step % NDT;
     const int kt = ks >> 1, o4 = 4 * (ks & 1);
     const u32x4 bw = {pw[kt][o4], pw[kt][o4 + 1], pw[kt][o4 + 2], pw[kt][o4 + 3]};
     acc[dt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vreg[dt][ks]), as_bf16x8(bw), acc[dt][qt],
                                                           0, 0, 0);
-  };
+  }
 
   // empty asm "uses": keep a stage's results computed in its own region (the
   // compiler would otherwise sink the softmax past the next branch and lose
   // the overlap with the matrix cores)
-  auto pin = [](const uint32_t (&pw)[2][8]) {
+  static __device__ __forceinline__ void pin(const uint32_t (&pw)[2][8]) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int e = 0; e < 8; ++e) asm volatile("" ::"v"(pw[kt][e]));
-  };
+  }
+
   // The exponentials of a half are computed with the current m right away and
   // checked afterwards through their sum; the rare half whose sum exceeds the
   // limit, or that finds m unset (always the first block), takes the exact
   // max, raises m, rescales the accumulator and is redone with the new m.
-  auto settle = [&](int qt, const f32x16 (&st)[2], uint32_t (&pw)[2][8], float& ls) {
+  __device__ __forceinline__ void settle(int qt, const f32x16 (&st)[2], uint32_t (&pw)[2][8], float& ls) {
     const bool trig = !(ls <= kSumLimit) || m[qt] == -INFINITY;
     if (__any(trig)) {
       const float mx = half_max(st);
@@ -317,8 +286,126 @@ __device__ __forceinline__ void fwd_row(int row, const u32x4* __restrict__ qc, c
       for (int k = 0; k < 16; ++k) exp_pair(st, pw, nmu, ls, k);
     }
     l[qt] += ls;
+  }
+
+  __device__ __forceinline__ float neg_m(int qt) const { return m[qt] == -INFINITY ? 0.f : -m[qt]; }
+
+  // O = acc / l, LSE = (m + log2 l) ln 2 of query block i of (batch, head) bh;
+  // pad queries and empty rows -> 0, -inf.  TOK = false: O and LSE slot-major
+  // (oc [.., n_pad, D], lse_c [.., n_pad]); TOK = true: straight to token order
+  // (o [.., N, D], lse [.., N]), pad slots not written -- the inverse
+  // re-indexing fused into the epilogue.
+  template <bool TOK>
+  __device__ __forceinline__ void epilogue(long long bh, int i, int r, bf16* __restrict__ oc,
+                                           float* __restrict__ lse_c) const {
+    const Geom& G = *g;
+    const uint64_t qreal = real_mask(i);
+    bf16* ob = oc + (bh * G.n_pad + (long long)i * 64) * D;
+    float* lb = lse_c + bh * G.n_pad + (long long)i * 64;
+    // token order: cube coordinates of this query block (one division each on the scalar unit)
+    int ct0 = 0, ch0 = 0, cw0 = 0;
+    if (TOK) {
+      const uint32_t rr = fdiv((uint32_t)i, cd.w);
+      cw0 = (i - (int)rr * G.nw) * G.cw;
+      const int bt = (int)fdiv(rr, cd.h);
+      ch0 = ((int)rr - bt * G.nh) * G.ch;
+      ct0 = bt * G.ct;
+    }
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      const float ltot = l[qt] + __shfl_xor(l[qt], 32, 64);
+      const int q = 32 * qt + r;
+      const bool real_q = (qreal >> q) & 1ull;
+      const bool live = real_q && ltot > 0.f;
+      const float inv = live ? 1.f / ltot : 0.f;
+      bf16* orow = ob + (long long)q * D;
+      long long tok = 0;
+      if (TOK) {
+        int tt, hh, ww;
+        slot_offsets(G, q, tt, hh, ww);
+        tok = ((long long)(ct0 + tt) * G.height + (ch0 + hh)) * G.width + (cw0 + ww);
+        orow = oc + (bh * G.n_real + tok) * D;
+        if (!real_q) continue;   // pad slots have no token row
+      }
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const u32x2 v = {pack_bf16x2(acc[dt][qt][4 * a] * inv, acc[dt][qt][4 * a + 1] * inv),
+                           pack_bf16x2(acc[dt][qt][4 * a + 2] * inv, acc[dt][qt][4 * a + 3] * inv)};
+          *reinterpret_cast<u32x2*>(orow + 32 * dt + 8 * a + 4 * hf) = v;
+        }
+      const float lse_q = live ? (m[qt] + __log2f(ltot)) * kLn2 : -INFINITY;
+      if (hf == 0) {
+        if (TOK)
+          lse_c[bh * G.n_real + tok] = lse_q;
+        else
+          lb[q] = lse_q;
+      }
+    }
+  }
+};
+
+// One query block (row of batch*heads*nblk) of the forward, by one wavefront,
+// with K and V straight from global memory (L2) into registers.
+template <int D, bool TOK>
+__device__ __forceinline__ void fwd_row(int row, const u32x4* __restrict__ qc, const u32x4* __restrict__ kc,
+                                        const u32x4* __restrict__ vc, const int32_t* __restrict__ lut,
+                                        const int32_t* __restrict__ counts, int cap, const Geom& g,
+                                        float sc_log2, bf16* __restrict__ oc, float* __restrict__ lse_c,
+                                        const CubeDiv& cd, int qg_shift, int dense_div = 0) {
+  using RS = RowState<D>;
+  constexpr int NDS = RS::NDS, NDT = RS::NDT, G1 = RS::G1, G2 = RS::G2;
+  constexpr int BLK = 64 * D / 8; // 16-byte units per block
+
+  const long long bh = row / g.nblk;
+  const int i = row - (int)(bh * g.nblk);
+
+  const int lane = threadIdx.x & 63;
+  const int hf = lane >> 5, r = lane & 31;
+  // K row fed to A-operand lane r: sigma(8a + 4b + c) = 16(a/2) + 8b + 4(a%2) + c
+  const int sig = 16 * (r >> 4) + 8 * ((r >> 2) & 1) + 4 * ((r >> 3) & 1) + (r & 3);
+  const int kpos = hf * 32 + sig;
+
+  const long long head = bh * (g.n_pad / 64) * (long long)BLK;
+  const u32x4* qb = qc + head + (long long)i * BLK;
+  const u32x4* kh = kc + head;
+  const u32x4* vh = vc + head;
+
+  RS S;
+#pragma unroll
+  for (int c = 0; c < 2 * NDS; ++c) S.qreg[c] = qb[c * 64 + lane];
+
+  // the list of this query block: one per cube, or one per group of
+  // 2^qg_shift consecutive cubes (asymmetric query blocks)
+  const int nlists = (g.nblk + (1 << qg_shift) - 1) >> qg_shift;
+  const long long lrow_i = bh * nlists + (i >> qg_shift);
+  int count = counts[lrow_i];
+  count = count < 0 ? 0 : (count > cap ? cap : count);
+  const int32_t* lrow = lut + lrow_i * cap;
+  // rows of dense groups are left to fwd_group_kernel (the check's loads are
+  // queued behind those of Q, so they add no latency of their own)
+  if (dense_div > 0 && group_dense(counts, cap, g.nblk, bh, i, dense_div)) return;
+
+  S.init(g, cd, sc_log2, lane);
+  auto valid_id = [&](int j) { return j >= 0 && j < g.nblk; };
+  // both tiles are requested in the order the products consume them, so a
+  // product waits only for the chunks it uses
+  auto load_k = [&](int j) {
+    const u32x4* kb = kh + (long long)(valid_id(j) ? j : 0) * BLK;
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) S.kreg[kt][ds] = kb[(kt * NDS + ds) * 64 + kpos];
   };
-  auto neg_m = [&](int qt) { return m[qt] == -INFINITY ? 0.f : -m[qt]; };
+  auto load_v = [&](int j) {
+    const u32x4* vb = vh + (long long)(valid_id(j) ? j : 0) * BLK;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) S.vreg[dt][ks] = vb[(dt * 4 + ks) * 64 + lane];
+  };
+
   // Software pipeline over the kept blocks, per block t (halves 0 and 1):
   //   S^T(t,1) with exp(t,0) | settle(t,0) | O += (t,0) with exp(t,1) |
   //   settle(t,1) | O += (t,1) and S^T(t+1,0)
@@ -333,8 +420,8 @@ __device__ __forceinline__ void fwd_row(int row, const u32x4* __restrict__ qc, c
   if (count > 0) {
     load_k(j_cur);
     load_v(j_cur);
-    real = real_mask(j_cur);
-    gemm1_half(0, stA, real);
+    real = S.real_mask(j_cur);
+    S.gemm1_half(0, stA, real);
   }
   // the list entry of the next block is read one iteration ahead
   int j_ahead = count > 1 ? lrow[1] : j_cur;
@@ -346,87 +433,42 @@ __device__ __forceinline__ void fwd_row(int row, const u32x4* __restrict__ qc, c
     j_ahead = lrow[it + 2 < count ? it + 2 : count - 1];
     uint64_t real_next;
     {
-      const float nmu = neg_m(0);
+      const float nmu = S.neg_m(0);
       float ls = 0.f;
-      gemm1_first(stB, qchunk(1, 0), real);
+      S.gemm1_first(stB, S.qchunk(1, 0), real);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
-        if (k + 2 < G1) gemm1_step(stB, qchunk(1, (k + 2) >> 1), k + 2);
-        exp_pair(stA, pA, nmu, ls, k);
+        if (k + 2 < G1) S.gemm1_step(stB, S.qchunk(1, (k + 2) >> 1), k + 2);
+        S.exp_pair(stA, pA, nmu, ls, k);
         __builtin_amdgcn_sched_barrier(0);
       }
-      pin(pA);
+      RS::pin(pA);
       load_k(j_next);
-      settle(0, stA, pA, ls);
+      S.settle(0, stA, pA, ls);
     }
     {
-      const float nmu = neg_m(1);
+      const float nmu = S.neg_m(1);
       float ls = 0.f;
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
-        if (k < G2) gemm2_step(0, pA, k);
-        exp_pair(stB, pB, nmu, ls, k);
-        if (k == 4) real_next = real_mask(j_next);   // scalar work between matrix ops
+        if (k < G2) S.gemm2_step(0, pA, k);
+        S.exp_pair(stB, pB, nmu, ls, k);
+        if (k == 4) real_next = S.real_mask(j_next);   // scalar work between matrix ops
         __builtin_amdgcn_sched_barrier(0);
       }
-      pin(pB);
-      settle(1, stB, pB, ls);
+      RS::pin(pB);
+      S.settle(1, stB, pB, ls);
     }
 #pragma unroll
-    for (int k = 0; k < G2; ++k) gemm2_step(1, pB, k);
+    for (int k = 0; k < G2; ++k) S.gemm2_step(1, pB, k);
     real = real_next;
-    gemm1_half(0, stA, real);
+    S.gemm1_half(0, stA, real);
     load_v(j_next);
     j_cur = j_next;
   }
-
-  // epilogue: O = acc / l, LSE = (m + log2 l) ln 2; pad queries and empty rows -> 0, -inf
-  const uint64_t qreal = real_mask(i);
-  bf16* ob = oc + (bh * g.n_pad + (long long)i * 64) * D;
-  float* lb = lse_c + bh * g.n_pad + (long long)i * 64;
-  // token order: cube coordinates of this query block (one division each on the scalar unit)
-  int ct0 = 0, ch0 = 0, cw0 = 0;
-  if (TOK) {
-    const uint32_t rr = fdiv((uint32_t)i, cd.w);
-    cw0 = (i - (int)rr * g.nw) * g.cw;
-    const int bt = (int)fdiv(rr, cd.h);
-    ch0 = ((int)rr - bt * g.nh) * g.ch;
-    ct0 = bt * g.ct;
-  }
-#pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    const float lt = l[qt] + __shfl_xor(l[qt], 32, 64);
-    const int q = 32 * qt + r;
-    const bool real_q = (qreal >> q) & 1ull;
-    const bool live = real_q && lt > 0.f;
-    const float inv = live ? 1.f / lt : 0.f;
-    bf16* orow = ob + (long long)q * D;
-    long long tok = 0;
-    if (TOK) {
-      int tt, hh, ww;
-      slot_offsets(g, q, tt, hh, ww);
-      tok = ((long long)(ct0 + tt) * g.height + (ch0 + hh)) * g.width + (cw0 + ww);
-      orow = oc + (bh * g.n_real + tok) * D;
-      if (!real_q) continue;   // pad slots have no token row
-    }
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const u32x2 v = {pack_bf16x2(acc[dt][qt][4 * a] * inv, acc[dt][qt][4 * a + 1] * inv),
-                         pack_bf16x2(acc[dt][qt][4 * a + 2] * inv, acc[dt][qt][4 * a + 3] * inv)};
-        *reinterpret_cast<u32x2*>(orow + 32 * dt + 8 * a + 4 * hf) = v;
-      }
-    const float lse_q = live ? (m[qt] + __log2f(lt)) * kLn2 : -INFINITY;
-    if (hf == 0) {
-      if (TOK)
-        lse_c[bh * g.n_real + tok] = lse_q;
-      else
-        lb[q] = lse_q;
-    }
-  }
+  S.template epilogue<TOK>(bh, i, r, oc, lse_c);
 }
 
 template <int D, bool TOK>
@@ -465,11 +507,22 @@ __global__ __launch_bounds__(64) void fwd_kernel(const u32x4* __restrict__ qc, c
 // data.  The copy is written out here rather than through the builtin: with
 // the builtin the compiler's wait counting makes every LDS read wait for all
 // copies in flight, including those of the tiles ahead, which undoes the
-// prefetch.  The kernel waits for these copies explicitly instead.
+// prefetch.  The kernel waits for these copies explicitly instead.  M0 (the
+// LDS base of the copy) is a register the compiler reserves, so the block
+// saves and restores it itself rather than declaring a clobber, and leaves
+// one wait state between setting it and the copy.
 __device__ __forceinline__ void chunk_to_lds(uint32_t lds, const void* gbase, uint32_t lane16) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(lane16), "s"(gbase)
-               : "memory", "m0");
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"   // one wait state between writing M0 and the copy that reads it
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(lane16), "s"(gbase)
+      : "memory");
 #else
   (void)lds;
   (void)gbase;
@@ -577,127 +630,23 @@ __device__ __forceinline__ void fwd_group(int grow, GroupLds<D>& L, const u32x4*
   __syncthreads();
   const int U = wpre[nwords];
 
-  // ---- per-wave state (as fwd_row) --------------------------------------
+  // ---- per-wave state and the union walk ---------------------------------
+  using RS = RowState<D>;
+  constexpr int G1 = RS::G1, G2 = RS::G2;
   const int hf = lane >> 5, r = lane & 31;
   const int sig = 16 * (r >> 4) + 8 * ((r >> 2) & 1) + 4 * ((r >> 3) & 1) + (r & 3);
   const int kpos = hf * 32 + sig;
   const long long head = bh * (g.n_pad / 64) * (long long)BLK;
   const u32x4* kh = kc + head;
   const u32x4* vh = vc + head;
-  u32x4 qreg[2 * NDS];
+  RS S;
   {
     const u32x4* qb = qc + head + (long long)(active ? i : 0) * BLK;
 #pragma unroll
-    for (int c = 0; c < 2 * NDS; ++c) qreg[c] = qb[c * 64 + lane];
+    for (int c = 0; c < 2 * NDS; ++c) S.qreg[c] = qb[c * 64 + lane];
   }
-  f32x16 acc[NDT][2];
-#pragma unroll
-  for (int t = 0; t < NDT; ++t)
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[t][qt][e] = 0.f;
-  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
-  u32x4 kreg[2][NDS];
-  u32x4 vreg[NDT][4];
-  int lt, lh, lw;
-  slot_offsets(g, lane, lt, lh, lw);
-  auto real_mask = [&](int j) -> uint64_t {
-    const uint32_t jj = (uint32_t)j;
-    const uint32_t rr = fdiv(jj, cd.w);
-    const int bw = (int)jj - (int)rr * g.nw;
-    const int bt = (int)fdiv(rr, cd.h);
-    const int bhh = (int)rr - bt * g.nh;
-    const int rt = min(g.ct, g.frames - bt * g.ct);
-    const int rh = min(g.ch, g.height - bhh * g.ch);
-    const int rw = min(g.cw, g.width - bw * g.cw);
-    return ballot(lt < rt && lh < rh && lw < rw);
-  };
-  auto lane_mask = [&](uint64_t real) -> uint32_t {
-    return (uint32_t)((real >> (8 * hf)) & 0xffu) | ((uint32_t)((real >> (16 + 8 * hf)) & 0xffu) << 8) |
-           ((uint32_t)((real >> (32 + 8 * hf)) & 0xffu) << 16) |
-           ((uint32_t)((real >> (48 + 8 * hf)) & 0xffu) << 24);
-  };
-  constexpr int G1 = 2 * NDS;
-  constexpr int G2 = 4 * NDT;
-  auto gemm1_step = [&](f32x16 (&st)[2], const u32x4& q, int step) {
-    const int ds = step >> 1, kt = step & 1;
-    st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kreg[kt][ds]), as_bf16x8(q), st[kt], 0, 0, 0);
-  };
-  auto qchunk = [&](int qt, int ds) { return qreg[qt * NDS + ds]; };
-  auto gemm1_first = [&](f32x16 (&st)[2], const u32x4& q, uint64_t real) {
-    if (real == ~0ull) {
-      const f32x16 z = {};
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-        st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kreg[kt][0]), as_bf16x8(q), z, 0, 0, 0);
-    } else {
-      const uint32_t pad = ~lane_mask(real);   // bit set: pad key
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        f32x16 init;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) init[e] = pad_start(pad, 16 * kt + e);
-        st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kreg[kt][0]), as_bf16x8(q), init, 0, 0, 0);
-      }
-    }
-  };
-  auto gemm1_half = [&](int qt, f32x16 (&st)[2], uint64_t real) {
-    gemm1_first(st, qchunk(qt, 0), real);
-#pragma unroll
-    for (int k = 2; k < G1; ++k) gemm1_step(st, qchunk(qt, k >> 1), k);
-  };
-  auto exp_pair = [&](const f32x16 (&st)[2], uint32_t (&pw)[2][8], float nmu, float& ls, int step) {
-    const int kt = step >> 3, e = 2 * (step & 7);
-    const float p0 = __builtin_amdgcn_exp2f(fmaf(st[kt][e], sc_log2, nmu));
-    const float p1 = __builtin_amdgcn_exp2f(fmaf(st[kt][e + 1], sc_log2, nmu));
-    ls += p0 + p1;
-    pw[kt][e >> 1] = pack_bf16x2(p0, p1);
-  };
-  auto half_max = [&](const f32x16 (&st)[2]) {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, st[kt][e]);
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-    return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * sc_log2;
-  };
-  auto gemm2_step = [&](int qt, const uint32_t (&pw)[2][8], int step) {
-    const int ks = step / NDT, dt = step % NDT;
-    const int kt = ks >> 1, o4 = 4 * (ks & 1);
-    const u32x4 bw = {pw[kt][o4], pw[kt][o4 + 1], pw[kt][o4 + 2], pw[kt][o4 + 3]};
-    acc[dt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vreg[dt][ks]), as_bf16x8(bw), acc[dt][qt],
-                                                          0, 0, 0);
-  };
-  auto pin = [](const uint32_t (&pw)[2][8]) {
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) asm volatile("" ::"v"(pw[kt][e]));
-  };
-  auto settle = [&](int qt, const f32x16 (&st)[2], uint32_t (&pw)[2][8], float& ls) {
-    const bool trig = !(ls <= kSumLimit) || m[qt] == -INFINITY;
-    if (__any(trig)) {
-      const float mx = half_max(st);
-      const float mn = fmaxf(m[qt], mx);
-      const float alpha = (m[qt] == -INFINITY || mn == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[qt] - mn);
-      m[qt] = mn;
-      l[qt] *= alpha;
-#pragma unroll
-      for (int t = 0; t < NDT; ++t)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[t][qt][e] *= alpha;
-      const float nmu = m[qt] == -INFINITY ? 0.f : -m[qt];
-      ls = 0.f;
-#pragma unroll
-      for (int k = 0; k < 16; ++k) exp_pair(st, pw, nmu, ls, k);
-    }
-    l[qt] += ls;
-  };
-  auto neg_m = [&](int qt) { return m[qt] == -INFINITY ? 0.f : -m[qt]; };
+  S.init(g, cd, sc_log2, lane);
 
-  // ---- the union walk -----------------------------------------------------
   // copies of entry e into slot e % kSlots: wave w takes the 1 KB chunks
   // [w PER_WAVE, (w + 1) PER_WAVE) of the K tile followed by the V tile
   const uint32_t ring0 = (uint32_t)(size_t)(__attribute__((address_space(3))) const char*)(const char*)&ring[0][0];
@@ -739,94 +688,50 @@ __device__ __forceinline__ void fwd_group(int grow, GroupLds<D>& L, const u32x4*
     const int ent = ulist[u];
     if (!((ent >> (16 + wave)) & 1)) continue;
     const int j = ent & 0xffff;
+    // the block step of fwd_row, with the operands read from LDS
     const u32x4* ks = &ring[u % kSlots][0];
     const u32x4* vs = ks + BLK;
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds)
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) kreg[kt][ds] = ks[(kt * NDS + ds) * 64 + kpos];
-    const uint64_t real = real_mask(j);
-    gemm1_half(0, stA, real);
+      for (int kt = 0; kt < 2; ++kt) S.kreg[kt][ds] = ks[(kt * NDS + ds) * 64 + kpos];
+    const uint64_t real = S.real_mask(j);
+    S.gemm1_half(0, stA, real);
     {
-      const float nmu = neg_m(0);
+      const float nmu = S.neg_m(0);
       float ls = 0.f;
-      gemm1_first(stB, qchunk(1, 0), real);
+      S.gemm1_first(stB, S.qchunk(1, 0), real);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
-        if (k + 2 < G1) gemm1_step(stB, qchunk(1, (k + 2) >> 1), k + 2);
-        exp_pair(stA, pA, nmu, ls, k);
+        if (k + 2 < G1) S.gemm1_step(stB, S.qchunk(1, (k + 2) >> 1), k + 2);
+        S.exp_pair(stA, pA, nmu, ls, k);
         __builtin_amdgcn_sched_barrier(0);
       }
-      pin(pA);
+      RS::pin(pA);
 #pragma unroll
       for (int ks4 = 0; ks4 < 4; ++ks4)
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) vreg[dt][ks4] = vs[(dt * 4 + ks4) * 64 + lane];
-      settle(0, stA, pA, ls);
+        for (int dt = 0; dt < NDT; ++dt) S.vreg[dt][ks4] = vs[(dt * 4 + ks4) * 64 + lane];
+      S.settle(0, stA, pA, ls);
     }
     {
-      const float nmu = neg_m(1);
+      const float nmu = S.neg_m(1);
       float ls = 0.f;
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
-        if (k < G2) gemm2_step(0, pA, k);
-        exp_pair(stB, pB, nmu, ls, k);
+        if (k < G2) S.gemm2_step(0, pA, k);
+        S.exp_pair(stB, pB, nmu, ls, k);
         __builtin_amdgcn_sched_barrier(0);
       }
-      pin(pB);
-      settle(1, stB, pB, ls);
+      RS::pin(pB);
+      S.settle(1, stB, pB, ls);
     }
 #pragma unroll
-    for (int k = 0; k < G2; ++k) gemm2_step(1, pB, k);
+    for (int k = 0; k < G2; ++k) S.gemm2_step(1, pB, k);
   }
-  if (!active) return;
-
-  // ---- epilogue (as fwd_row) --------------------------------------------
-  const uint64_t qreal = real_mask(i);
-  bf16* ob = oc + (bh * g.n_pad + (long long)i * 64) * D;
-  float* lb = lse_c + bh * g.n_pad + (long long)i * 64;
-  int ct0 = 0, ch0 = 0, cw0 = 0;
-  if (TOK) {
-    const uint32_t rr = fdiv((uint32_t)i, cd.w);
-    cw0 = (i - (int)rr * g.nw) * g.cw;
-    const int bt = (int)fdiv(rr, cd.h);
-    ch0 = ((int)rr - bt * g.nh) * g.ch;
-    ct0 = bt * g.ct;
-  }
-#pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    const float ltot = l[qt] + __shfl_xor(l[qt], 32, 64);
-    const int q = 32 * qt + r;
-    const bool real_q = (qreal >> q) & 1ull;
-    const bool live = real_q && ltot > 0.f;
-    const float inv = live ? 1.f / ltot : 0.f;
-    bf16* orow = ob + (long long)q * D;
-    long long tok = 0;
-    if (TOK) {
-      int tt, hh, ww;
-      slot_offsets(g, q, tt, hh, ww);
-      tok = ((long long)(ct0 + tt) * g.height + (ch0 + hh)) * g.width + (cw0 + ww);
-      orow = oc + (bh * g.n_real + tok) * D;
-      if (!real_q) continue;
-    }
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const u32x2 v = {pack_bf16x2(acc[dt][qt][4 * a] * inv, acc[dt][qt][4 * a + 1] * inv),
-                         pack_bf16x2(acc[dt][qt][4 * a + 2] * inv, acc[dt][qt][4 * a + 3] * inv)};
-        *reinterpret_cast<u32x2*>(orow + 32 * dt + 8 * a + 4 * hf) = v;
-      }
-    const float lse_q = live ? (m[qt] + __log2f(ltot)) * kLn2 : -INFINITY;
-    if (hf == 0) {
-      if (TOK)
-        lse_c[bh * g.n_real + tok] = lse_q;
-      else
-        lb[q] = lse_q;
-    }
-  }
+  if (active) S.template epilogue<TOK>(bh, i, r, oc, lse_c);
 }
 
 // One workgroup per group (row of the group map).
