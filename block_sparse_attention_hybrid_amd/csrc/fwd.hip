@@ -865,7 +865,7 @@ size_t fwd_workspace_bytes(const Geom& g) {
 template <bool TOK>
 static hipError_t launch_fwd_any(const void* qc, const void* kc, const void* vc, const int32_t* lut,
                                  const int32_t* counts, int cap, const Geom& g, float scale, void* out,
-                                 float* lse_out, hipStream_t s, int qg_shift, void* order_ws) {
+                                 float* lse_out, hipStream_t s, int qg_shift, void* order_ws, int max_count) {
   const RowMap map = make_rowmap(g.nblk, g.batch * g.heads);
   const CubeDiv cd = {make_fastdiv((uint32_t)g.nw), make_fastdiv((uint32_t)g.nh)};
   const float sc_log2 = scale * 1.4426950408889634f;
@@ -887,8 +887,11 @@ static hipError_t launch_fwd_any(const void* qc, const void* kc, const void* vc,
   // head, 0.27 of the bf16 peak against 0.35 for the group kernel), while with
   // smaller heads it keeps up (480p: 20 MB, 0.39 against 0.35)
   const size_t kv_head = (size_t)g.nblk * 64 * g.d * 2 * 2;
+  // (and a known bound on the list lengths can rule dense groups out: a group
+  // is dense only when its mean list reaches nblk / kDenseDiv)
+  const bool maybe_dense = max_count < 0 || (long long)max_count * kDenseDiv >= g.nblk;
   const int dense_div =
-      (qg_shift == 0 && g.nblk <= kMaxBlocks && kv_head >= kDenseHeadBytes) ? kDenseDiv : 0;
+      (qg_shift == 0 && g.nblk <= kMaxBlocks && kv_head >= kDenseHeadBytes && maybe_dense) ? kDenseDiv : 0;
   bf16* o = static_cast<bf16*>(out);
   if (g.d == 128)
     fwd_kernel<128, TOK><<<grid, 64, 0, s>>>(q, k, v, lut, counts, cap, g, sc_log2, o, lse_out, map, cd, qg_shift,
@@ -912,14 +915,15 @@ static hipError_t launch_fwd_any(const void* qc, const void* kc, const void* vc,
 
 hipError_t launch_fwd(const void* qc, const void* kc, const void* vc, const int32_t* lut,
                       const int32_t* counts, int cap, const Geom& g, float scale, void* oc,
-                      float* lse_c, void* workspace, hipStream_t s, int qg_shift) {
-  return launch_fwd_any<false>(qc, kc, vc, lut, counts, cap, g, scale, oc, lse_c, s, qg_shift, workspace);
+                      float* lse_c, void* workspace, hipStream_t s, int qg_shift, int max_count) {
+  return launch_fwd_any<false>(qc, kc, vc, lut, counts, cap, g, scale, oc, lse_c, s, qg_shift, workspace,
+                               max_count);
 }
 
 hipError_t launch_fwd_tokens(const void* qc, const void* kc, const void* vc, const int32_t* lut,
                              const int32_t* counts, int cap, const Geom& g, float scale, void* o,
-                             float* lse, hipStream_t s, void* workspace) {
-  return launch_fwd_any<true>(qc, kc, vc, lut, counts, cap, g, scale, o, lse, s, 0, workspace);
+                             float* lse, hipStream_t s, void* workspace, int max_count) {
+  return launch_fwd_any<true>(qc, kc, vc, lut, counts, cap, g, scale, o, lse, s, 0, workspace, max_count);
 }
 
 }  // namespace sa

@@ -15,6 +15,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <vector>
 
@@ -206,6 +207,17 @@ extern "C" int32_t sparse_attn_attention(const sa_path_buffers* b, const sa_geom
   const size_t nb = (size_t)d.nblk;
   hipError_t e = mask_phase(b, d, kcount, p, s, a, two, ev);
   if (e != hipSuccess) return sa_hip_status(e, "mask phase");
+  // Without row budgets no list is longer than max(kc, pc): the Top-p prefix
+  // of a row holds at most ceil(p nblk) blocks, since the largest
+  // probabilities average at least 1 / nblk (one more for the rounding of the
+  // selection's fixed-point masses).  The forward uses the bound to skip the
+  // dense-group kernel when no group can be dense.
+  int max_count = -1;
+  if (b->row_budget == nullptr) {
+    const double pc = p >= 1.0 ? (double)d.nblk : std::ceil(p * (double)d.nblk) + 1.0;
+    const double bound = std::max((double)kcount, pc);
+    max_count = bound >= (double)d.nblk ? d.nblk : (int)bound;
+  }
   // the forward runs on the auxiliary stream after the last mask (the values
   // were re-indexed there already)
   if (two && (e = hipStreamWaitEvent(a, ev.masks(), 0)) != hipSuccess) return sa_hip_status(e, "stream wait");
@@ -231,7 +243,8 @@ extern "C" int32_t sparse_attn_attention(const sa_path_buffers* b, const sa_geom
     float* lse = b->lse + (size_t)r0 * d.n_real;
     if (b->oc == nullptr) {
       // no slot-major copy wanted: the forward writes token order itself
-      if ((e = sa::launch_fwd_tokens(qc, kc, vc, lut, counts, b->cap, gc, sc, o, lse, a, fws)) != hipSuccess)
+      if ((e = sa::launch_fwd_tokens(qc, kc, vc, lut, counts, b->cap, gc, sc, o, lse, a, fws, max_count)) !=
+          hipSuccess)
         return sa_hip_status(e, "fwd launch");
       if (two) {
         if ((e = hipEventRecord(ev.chunk(c), a)) != hipSuccess) return sa_hip_status(e, "event record");
@@ -241,7 +254,8 @@ extern "C" int32_t sparse_attn_attention(const sa_path_buffers* b, const sa_geom
     }
     char* oc = static_cast<char*>(b->oc) + (size_t)r0 * head_c * 2;
     float* lse_c = b->lse_c + (size_t)r0 * d.n_pad;
-    if ((e = sa::launch_fwd(qc, kc, vc, lut, counts, b->cap, gc, sc, oc, lse_c, fws, a)) != hipSuccess)
+    if ((e = sa::launch_fwd(qc, kc, vc, lut, counts, b->cap, gc, sc, oc, lse_c, fws, a, 0, max_count)) !=
+        hipSuccess)
       return sa_hip_status(e, "fwd launch");
     if (two) {
       if ((e = hipEventRecord(ev.chunk(c), a)) != hipSuccess) return sa_hip_status(e, "event record");

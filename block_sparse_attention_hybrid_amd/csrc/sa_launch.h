@@ -30,16 +30,19 @@ hipError_t launch_select(const double* scores, const Geom& g, int kc_default, do
                          int cap, hipStream_t s, int rows_per_head = -1);
 // cube i of a head reads list row i >> qg_shift of its head's nlists rows
 // (default: one list per cube).  With a workspace (fwd_workspace_bytes) and
-// one list per cube, the count-balanced persistent grid runs; without one,
-// one workgroup per row.
+// one list per cube, the rows run in the count-balanced order; without one,
+// in the sweep order.  max_count: an upper bound on every list's length that
+// the caller knows (-1: none); when it rules out dense groups, the
+// dense-group kernel is not launched.
 hipError_t launch_fwd(const void* qc, const void* kc, const void* vc, const int32_t* lut,
                       const int32_t* counts, int cap, const Geom& g, float scale, void* oc,
-                      float* lse_c, void* workspace, hipStream_t s, int qg_shift = 0);
+                      float* lse_c, void* workspace, hipStream_t s, int qg_shift = 0, int max_count = -1);
 // the forward with the inverse re-indexing fused: O [.., N, d] and LSE [.., N]
-// in token order (pad slots not written); workspace as for launch_fwd
+// in token order (pad slots not written); workspace and max_count as for
+// launch_fwd
 hipError_t launch_fwd_tokens(const void* qc, const void* kc, const void* vc, const int32_t* lut,
                              const int32_t* counts, int cap, const Geom& g, float scale, void* o,
-                             float* lse, hipStream_t s, void* workspace = nullptr);
+                             float* lse, hipStream_t s, void* workspace = nullptr, int max_count = -1);
 size_t fwd_workspace_bytes(const Geom& g);
 hipError_t launch_router_pool(const void* xc, double* xr, const Geom& g, int rt, int rh, int rw, hipStream_t s);
 hipError_t launch_router(const double* qr, const double* kr, double* scores, double scale, const Geom& g,
