@@ -376,6 +376,10 @@ def _oracle_worker(task):
     else:
         sels = O.select_rows(s, O.ceil_k(k_frac, og.nblk), p)
     t_mask = time.perf_counter() - t0
+    # the oracle's report of this head's mask (outside the timed parts)
+    counts = np.array([[[x.kept.size for x in sels]]])
+    density, sink, entropy = (float(a[0, 0]) for a in O.mask_report(s[None, None], counts))
+    report = (wl.head_types[h], density, sink, entropy)
     flops, done = 0.0, 0
     t1 = time.perf_counter()
     for i in np.random.default_rng(h).permutation(og.nblk):
@@ -384,7 +388,7 @@ def _oracle_worker(task):
         done += 1
         if time.perf_counter() - t1 > seconds:
             break
-    return t_mask, time.perf_counter() - t1, flops, done
+    return t_mask, time.perf_counter() - t1, flops, done, report
 
 
 def cpu_baseline(wl, seconds, workload, workers=16):
@@ -416,6 +420,18 @@ def cpu_baseline(wl, seconds, workload, workers=16):
     flops = sum(r[2] for r in res)
     done = sum(r[3] for r in res)
     busy = max(r[0] + r[1] for r in res)    # the slowest worker (process start-up excluded)
+    # the oracle's mask report of the sampled heads, by head type: realised
+    # block density, mean sink mass (probability on block 0) and mean row
+    # entropy of the block softmax (ln nblk for a flat row)
+    by_type = {}
+    for r in res:
+        kind, density, sink, entropy = r[4]
+        by_type.setdefault(kind, []).append((density, sink, entropy))
+    mask_report = {kind: {"heads": len(v), "density": round(float(np.mean([x[0] for x in v])), 5),
+                          "sink_mass": round(float(np.mean([x[1] for x in v])), 5),
+                          "row_entropy": round(float(np.mean([x[2] for x in v])), 4),
+                          "ln_nblk": round(math.log(wl.n_blocks()), 4)}
+                   for kind, v in sorted(by_type.items())}
     return {
         "value": flops / busy / 1e12,
         "unit": "TFLOPS",
@@ -428,6 +444,7 @@ def cpu_baseline(wl, seconds, workload, workers=16):
                    f"process); value = kept-block flops / the slowest process's time"),
         "seconds": round(busy, 2),
         "wall_seconds_with_startup": round(wall, 2),
+        "oracle_mask_report": mask_report,
         "host_cpus": os.cpu_count(),
         "cpu_model": cpu_model(),
     }
