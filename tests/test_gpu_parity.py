@@ -329,30 +329,33 @@ def test_forward_row_order_gives_identical_bytes(case):
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
 
 
-@pytest.mark.parametrize("d,grid", [(128, (9, 64, 124)), (64, (8, 128, 130)), (128, (8, 20, 24))])
-def test_dense_groups_shared_kernel_gives_identical_bytes(d, grid):
+@pytest.mark.parametrize("d,grid,batch", [(128, (9, 66, 122), 2), (64, (8, 128, 130), 1), (128, (8, 20, 24), 1)])
+def test_dense_groups_shared_kernel_gives_identical_bytes(d, grid, batch):
     """Rows of groups of four neighbouring query blocks whose lists are dense
     run in the kernel that shares K/V tiles through LDS when a head's K/V is
-    32 MiB or more (the first two shapes: 1,488 and 2,112 blocks, partial
-    cubes); the same row in a sparse group runs in the one-wave kernel.  Row
+    32 MiB or more (the first two shapes: 1,581 blocks with partial cubes on
+    every side and a last group of one block, batch 2; and 2,112 blocks at
+    d = 64); the same row in a sparse group runs in the one-wave kernel.  Row
     4g keeps one random ascending list (a third to a half of the blocks) in
-    both calls; in the first its three neighbours hold such lists too, in the
-    second they are empty.  Its output must be the same bytes, and sampled
-    query blocks of the first call must match the oracle.  The third shape
-    (small heads) runs both calls on the one-wave kernel."""
-    say(f"[dense groups d={d} grid={grid}]")
+    both calls; in the first its neighbours hold such lists too, in the second
+    they are empty.  Its output must be the same bytes, and sampled query
+    blocks of the first call (the short last group's included) must match the
+    oracle.  The third shape (small heads) runs both calls on the one-wave
+    kernel."""
+    say(f"[dense groups d={d} grid={grid} batch={batch}]")
     H = 2
-    wl, g, og, q, k, v = _small(d=d, grid=grid, heads=H)
+    wl, g, og, q, k, v = _small(d=d, grid=grid, heads=H, batch=batch)
     n = og.nblk
     rng = np.random.default_rng(11)
-    lut = np.full((1, H, n, n), -1, dtype=np.int32)
-    counts = np.zeros((1, H, n), dtype=np.int32)
-    for h in range(H):
-        for i in range(n):
-            c = int(rng.integers(n // 3, n // 2 + 2))
-            ids = np.sort(rng.choice(n, size=min(c, n), replace=False))
-            lut[0, h, i, :ids.size] = ids
-            counts[0, h, i] = ids.size
+    lut = np.full((batch, H, n, n), -1, dtype=np.int32)
+    counts = np.zeros((batch, H, n), dtype=np.int32)
+    for b in range(batch):
+        for h in range(H):
+            for i in range(n):
+                c = int(rng.integers(n // 3, n // 2 + 2))
+                ids = np.sort(rng.choice(n, size=min(c, n), replace=False))
+                lut[b, h, i, :ids.size] = ids
+                counts[b, h, i] = ids.size
     qd, kd, vd = reorder3(q.to(DEV), k.to(DEV), v.to(DEV), g)
     _, n_real, n_pad = sa.sparse_attn_geometry(g)
     lut_d = torch.from_numpy(lut).to(DEV)
@@ -361,10 +364,10 @@ def test_dense_groups_shared_kernel_gives_identical_bytes(d, grid):
         c = counts.copy()
         if sparse_neighbours:
             c[:, :, np.arange(n) % 4 != 0] = 0
-        oc = torch.empty((1, H, n_pad, d), dtype=torch.bfloat16, device=DEV)
-        lse_c = torch.empty((1, H, n_pad), dtype=torch.float32, device=DEV)
+        oc = torch.empty((batch, H, n_pad, d), dtype=torch.bfloat16, device=DEV)
+        lse_c = torch.empty((batch, H, n_pad), dtype=torch.float32, device=DEV)
         sa.sparse_attn_fwd(qd, kd, vd, lut_d, torch.from_numpy(c).to(DEV), n, g, 0.0, oc, lse_c, None)
-        outs.append((oc.view(1, H, n, 64, d), lse_c.view(1, H, n, 64)))
+        outs.append((oc.view(batch, H, n, 64, d), lse_c.view(batch, H, n, 64)))
     torch.cuda.synchronize()
     lead = torch.from_numpy(np.arange(n) % 4 == 0).to(DEV)
     assert torch.equal(outs[0][0][:, :, lead], outs[1][0][:, :, lead])
@@ -372,13 +375,14 @@ def test_dense_groups_shared_kernel_gives_identical_bytes(d, grid):
     # sampled query blocks of the dense call against the oracle (its own lists)
     o_gpu = outs[0][0].float().cpu().numpy()
     real = O.real_slots(og).reshape(n, 64)
-    for h in range(H):
-        qc, kc, vc = (O.reorder(t[0, h].double().numpy(), og) for t in (q, k, v))
-        for i in sorted({0, 1, 2, 3, n // 2, n - 1}):
-            o_ref, _ = O.attention_block(qc, kc, vc, lut[0, h, i, :counts[0, h, i]], og, i)
-            rr = real[i]
-            err = np.abs(o_gpu[0, h, i][rr] - o_ref[rr])
-            assert err.max() <= O_MAX_ABS and err.mean() <= O_MEAN_ABS, (h, i, err.max())
+    for b in range(batch):
+        for h in range(H):
+            qc, kc, vc = (O.reorder(t[b, h].double().numpy(), og) for t in (q, k, v))
+            for i in sorted({0, 1, 2, 3, n // 2, n - 2, n - 1}):
+                o_ref, _ = O.attention_block(qc, kc, vc, lut[b, h, i, :counts[b, h, i]], og, i)
+                rr = real[i]
+                err = np.abs(o_gpu[b, h, i][rr] - o_ref[rr])
+                assert err.max() <= O_MAX_ABS and err.mean() <= O_MEAN_ABS, (b, h, i, err.max())
 
 
 def test_keep_nothing_gives_zero_and_neg_inf():
