@@ -1,4 +1,5 @@
-// Hybrid Top-k U Top-p block selection, one workgroup per query block (gfx950).
+// Hybrid Top-k U Top-p block selection (gfx950): one wavefront per query block
+// for rows of up to 1536 blocks, one workgroup of four per longer row.
 //
 // SpargeAttention2 summary page, "The Hybrid Top-k+Top-p Masking Rule" (Eq. 9):
 // a row keeps the union of its Top-k blocks (ceil(k * Tn) largest scores) and
@@ -24,8 +25,9 @@
 // division.  Every round strictly shrinks the member set and the key rounds
 // consume 8 key bits each, so the loop ends after at most 10 rounds.
 //
-// Work split: the row's n scores are spread over the 4 waves of the
-// workgroup, wave w holding the contiguous ids [64 E w, 64 E (w + 1)) as E
+// Work split (rows above 1536 blocks; shorter rows use the one-wave kernel
+// further below, which runs the same steps): the row's n scores are spread
+// over the 4 waves of the workgroup, wave w holding the contiguous ids [64 E w, 64 E (w + 1)) as E
 // registers per lane, so every wave compacts its own kept ids in ascending
 // order with ballots and only per-wave totals cross waves (through LDS).  The
 // histogram is shared; wave 0 scans it and posts each round's decision in
@@ -51,6 +53,9 @@ constexpr double kLog2e = 1.4426950408889634;
 constexpr int kMaxRounds = 16;
 constexpr int kCountShift = 52;              // packed histogram word: count << 52 | mass
 constexpr uint64_t kMassMask = (1ull << kCountShift) - 1;
+#ifndef SA_SELECT_ONE_WAVE
+#define SA_SELECT_ONE_WAVE 1
+#endif
 
 __device__ __forceinline__ uint64_t to_fixed(float e) {
   return (uint64_t)((double)e * kFixOne + 0.5);
@@ -527,6 +532,270 @@ hipError_t launch_e(const double* scores, const Geom& g, int kc, double p, const
   return hipGetLastError();
 }
 
+// One wavefront per row, for rows of up to 1536 blocks (E <= 24 registers per
+// lane).  The same selection as select_kernel -- the same bucket functions,
+// fixed-point masses, decisions and exact finish, so the same lists -- with
+// the row held by a single wave: the reductions, the histogram scan and the
+// decision of every round are done once per row instead of by four waves
+// that then exchange them through LDS behind barriers.  A workgroup holds
+// four independent rows, each wave with its own LDS histogram and member
+// list; no barrier is needed (a wave's LDS operations are ordered, and the
+// wavefront fences below keep the compiler from moving reads of other
+// lanes' buckets across the atomics).
+constexpr int kRowsPerSelectGroup = 4;
+
+__device__ __forceinline__ void wave_fence() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); }
+
+template <int E>
+__global__ __launch_bounds__(kWave * kRowsPerSelectGroup) void select_wave_kernel(
+    const double* __restrict__ scores, int n, int kc_default, double p, const int32_t* __restrict__ row_budget,
+    int32_t* __restrict__ lut, int32_t* __restrict__ counts, int cap, long long rows) {
+  static_assert(E * kWave <= 2048, "packed histogram words need n <= 2048");
+  __shared__ unsigned long long hist_all[kRowsPerSelectGroup][256];
+  __shared__ unsigned long long ckey_all[kRowsPerSelectGroup][kWave], cmass_all[kRowsPerSelectGroup][kWave];
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  const long long row = (long long)blockIdx.x * kRowsPerSelectGroup + wave;
+  if (row >= rows) return;   // no barrier below: a wave past the rows just leaves
+  unsigned long long* hist = hist_all[wave];
+  unsigned long long* ckey = ckey_all[wave];
+  unsigned long long* cmass = cmass_all[wave];
+  const uint64_t lt = lanemask_lt();
+  const double* srow = scores + row * (long long)n;
+
+  // every load first, at clamped in-row addresses, then the masking
+  double s[E];
+  float ev[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = e * kWave + lane;
+    s[e] = srow[j < n ? j : n - 1];
+  }
+  int kc = row_budget != nullptr ? row_budget[row] : kc_default;
+  kc = kc < 0 ? 0 : (kc > n ? n : kc);
+  uint32_t valid = 0;
+  double mx = -INFINITY, lo0 = INFINITY;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const bool in = e * kWave + lane < n;
+    const double v = s[e] == 0.0 ? 0.0 : s[e];  // -0 and +0 are the same score
+    s[e] = in ? v : 0.0;
+    ev[e] = 0.f;
+    valid |= (uint32_t)in << e;
+    mx = fmax(mx, in ? v : -INFINITY);
+    lo0 = fmin(lo0, in ? v : INFINITY);
+  }
+  mx = wmax(mx);
+  lo0 = wmin(lo0);
+
+  const bool keep_all = (p >= 1.0) || (kc >= n);
+  const bool keep_none = !keep_all && kc == 0 && !(p > 0.0);
+  uint32_t above = 0, member = 0;
+  uint64_t kept_rank = 0;    // members kept by rank: bit = member index in ascending id
+  long long take = -1;       // >= 0: the first `take` members by id are kept
+
+  if (keep_all) {
+    above = valid;
+  } else if (!keep_none) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) ev[e] = ((valid >> e) & 1u) ? prob(s[e], mx) : 0.f;
+    member = valid;
+    int m = n;                 // members left
+    long long cnt_above = 0;
+    unsigned long long mass_above = 0, target = 0;
+    double eq = 0.0;
+    for (int round = 0; round < kMaxRounds && (round == 0 || m > kWave); ++round) {
+      double lo = lo0, hi = mx;
+      if (round > 0) {
+        lo = INFINITY;
+        hi = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const bool mem = (member >> e) & 1u;
+          lo = fmin(lo, mem ? s[e] : INFINITY);
+          hi = fmax(hi, mem ? s[e] : -INFINITY);
+        }
+        lo = wmin(lo);
+        hi = wmax(hi);
+      }
+      if (!(lo < hi)) {
+        eq = hi;
+        if (round == 0) {  // every score equal: every mass is exp2(0) = 1
+          const unsigned long long z = (unsigned long long)n * to_fixed(1.0f);
+          target = p > 0.0 ? (unsigned long long)ceil(p * (double)z) : 0ull;
+        }
+        break;
+      }
+      // bucket function of this round
+      const double w = 256.0 / (hi - lo);
+      const bool linear = round < 2 && w < 1e300;
+      int shift = 0;
+      if (!linear) {
+        uint64_t kmin = ~0ull, kmax = 0;
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          if ((member >> e) & 1u) {
+            const uint64_t k = desc_key(fresh(s[e]));
+            kmin = k < kmin ? k : kmin;
+            kmax = k > kmax ? k : kmax;
+          }
+        kmin = wmin_u64(kmin);
+        kmax = wmax_u64(kmax);
+        const int hb = 63 - __clzll((long long)(kmin ^ kmax));
+        shift = hb >= 7 ? hb - 7 : 0;
+      }
+      auto bucket = [&](double v) -> int {
+        if (linear) {
+          const int b = (int)((hi - v) * w);
+          return b > 255 ? 255 : b;
+        }
+        return (int)((desc_key(v) >> shift) & 255ull);
+      };
+
+#pragma unroll
+      for (int t = 0; t < 4; ++t) hist[lane * 4 + t] = 0ull;
+      wave_fence();
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if ((member >> e) & 1u) {
+          const int b = bucket(fresh(s[e]));
+          const unsigned long long f = to_fixed(fresh(ev[e]));
+          atomicAdd(&hist[b], (1ull << kCountShift) | f);
+        }
+      wave_fence();
+
+      // lane L takes buckets 4L .. 4L+3; the first bucket at which both
+      // conditions hold closes the kept prefix
+      uint32_t c4[4];
+      unsigned long long m4[4];
+      uint32_t lc = 0;
+      unsigned long long lm = 0;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const unsigned long long hw = hist[lane * 4 + t];
+        c4[t] = (uint32_t)(hw >> kCountShift);
+        m4[t] = hw & kMassMask;
+        lc += c4[t];
+        lm += m4[t];
+      }
+      uint32_t ic = lc;
+      uint64_t im = lm;
+      wave_scan(ic, im, lane);
+      if (round == 0) {  // every element is a member: the total is Z
+        const unsigned long long z = readlane64(im, kWave - 1);
+        target = p > 0.0 ? (unsigned long long)ceil(p * (double)z) : 0ull;
+      }
+      uint32_t xc = ic - lc;
+      unsigned long long xm = im - lm;
+      int first = 4;
+      uint32_t first_xc = 0, first_c = 0;
+      unsigned long long first_xm = 0;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const bool ok = (cnt_above + (long long)(xc + c4[t]) >= kc) && (mass_above + xm + m4[t] >= target);
+        if (ok && first == 4) {
+          first = t;
+          first_xc = xc;
+          first_xm = xm;
+          first_c = c4[t];
+        }
+        xc += c4[t];
+        xm += m4[t];
+      }
+      const uint64_t hit = ballot(first < 4);
+      const int src = hit ? (__ffsll((long long)hit) - 1) : (kWave - 1);
+      if (!hit && lane == kWave - 1) {  // unreachable: all members always satisfy both
+        first = 3;
+        first_xc = ic - c4[3];
+        first_xm = im - m4[3];
+        first_c = c4[3];
+      }
+      const int bstar = 4 * src + (int)readlane((uint32_t)first, src);
+      m = (int)readlane(first_c, src);
+      cnt_above += (long long)readlane(first_xc, src);
+      mass_above += readlane64(first_xm, src);
+      wave_fence();   // the histogram reads are done before the next round clears it
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const bool mem = (member >> e) & 1u;
+        const int b = bucket(fresh(s[e]));
+        above |= (uint32_t)(mem && b < bstar) << e;
+        member &= ~((uint32_t)(mem && b != bstar) << e);
+      }
+    }
+
+    if (m <= kWave) {
+      // exact finish: members to LDS in ascending id, then rank by one pass
+      int seen = 0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const bool is_mem = (member >> e) & 1u;
+        const uint64_t bm = ballot(is_mem);
+        if (bm) {
+          if (is_mem) {
+            const int idx = seen + __popcll(bm & lt);
+            ckey[idx] = desc_key(s[e]);
+            cmass[idx] = to_fixed(ev[e]);
+          }
+          seen += __popcll(bm);
+        }
+      }
+      wave_fence();
+      const bool mine = lane < m;
+      const unsigned long long kk = mine ? ckey[lane] : ~0ull;
+      int r = 0;                      // members ahead of this one in the order
+      unsigned long long pm = 0;      // mass of the members up to and including it
+      for (int j = 0; j < m; ++j) {
+        const unsigned long long kj = ckey[j];
+        const bool ahead = kj < kk || (kj == kk && j < lane);
+        r += ahead ? 1 : 0;
+        pm += (ahead || j == lane) ? cmass[j] : 0ull;
+      }
+      const bool ok = mine && (cnt_above + r + 1 >= kc) && (mass_above + pm >= target);
+      const int rstar = wmin_i32(ok ? r : kWave);
+      kept_rank = ballot(mine && r <= rstar);
+    } else {
+      // more than 64 members of one score: equal masses u, so the count taken
+      // is a division
+      const unsigned long long u = to_fixed(prob(eq, mx));
+      long long need = kc - cnt_above;
+      if (mass_above < target && u > 0) {
+        const long long need_p = (long long)((target - mass_above + u - 1) / u);
+        need = need_p > need ? need_p : need;
+      }
+      take = need < 0 ? 0 : (need > (long long)m ? (long long)m : need);
+    }
+  }
+
+  // ascending-id compaction: kept = above U (selected members)
+  int32_t* out = lut + row * (long long)cap;
+  int written = 0, seen = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const bool is_mem = (member >> e) & 1u;
+    const uint64_t bm = ballot(is_mem);
+    const int rank = seen + __popcll(bm & lt);
+    seen += __popcll(bm);
+    const bool sel = take >= 0 ? rank < take : (rank < kWave && ((kept_rank >> rank) & 1ull));
+    const bool keep = ((above >> e) & 1u) || (is_mem && sel);
+    const uint64_t bk = ballot(keep);
+    const int pos = written + __popcll(bk & lt);
+    written += __popcll(bk);
+    if (keep && pos < cap) out[pos] = e * kWave + lane;
+  }
+  if (lane == 0) counts[row] = (int32_t)written;
+}
+
+template <int E>
+hipError_t launch_wave_e(const double* scores, const Geom& g, int kc, double p, const int32_t* rb,
+                         int32_t* lut, int32_t* counts, int cap, hipStream_t s, int rows_per_head) {
+  const long long rows = (long long)g.batch * g.heads * rows_per_head;
+  if (rows == 0) return hipSuccess;
+  const long long grid = (rows + kRowsPerSelectGroup - 1) / kRowsPerSelectGroup;
+  select_wave_kernel<E><<<dim3((unsigned)grid), kWave * kRowsPerSelectGroup, 0, s>>>(scores, g.nblk, kc, p, rb,
+                                                                                    lut, counts, cap, rows);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_select(const double* scores, const Geom& g, int kc_default, double p,
@@ -534,6 +803,15 @@ hipError_t launch_select(const double* scores, const Geom& g, int kc_default, do
                          hipStream_t s, int rows_per_head) {
   const int n = g.nblk;  // at most 4096 (checked by the caller)
   if (rows_per_head < 0) rows_per_head = n;
+#if SA_SELECT_ONE_WAVE
+  // rows of up to 1536 blocks: one wavefront per row
+  if (n <= 64) return launch_wave_e<1>(scores, g, kc_default, p, row_budget, lut, counts, cap, s, rows_per_head);
+  if (n <= 256) return launch_wave_e<4>(scores, g, kc_default, p, row_budget, lut, counts, cap, s, rows_per_head);
+  if (n <= 512) return launch_wave_e<8>(scores, g, kc_default, p, row_budget, lut, counts, cap, s, rows_per_head);
+  if (n <= 768) return launch_wave_e<12>(scores, g, kc_default, p, row_budget, lut, counts, cap, s, rows_per_head);
+  if (n <= 1024) return launch_wave_e<16>(scores, g, kc_default, p, row_budget, lut, counts, cap, s, rows_per_head);
+  if (n <= 1536) return launch_wave_e<24>(scores, g, kc_default, p, row_budget, lut, counts, cap, s, rows_per_head);
+#endif
   if (n <= 256) return launch_e<1>(scores, g, kc_default, p, row_budget, lut, counts, cap, s, rows_per_head);
   if (n <= 512) return launch_e<2>(scores, g, kc_default, p, row_budget, lut, counts, cap, s, rows_per_head);
   if (n <= 1024) return launch_e<4>(scores, g, kc_default, p, row_budget, lut, counts, cap, s, rows_per_head);
