@@ -27,11 +27,11 @@
 //
 // Work split (rows above 1536 blocks; shorter rows use the one-wave kernel
 // further below, which runs the same steps): the row's n scores are spread
-// over the 4 waves of the workgroup, wave w holding the contiguous ids [64 E w, 64 E (w + 1)) as E
-// registers per lane, so every wave compacts its own kept ids in ascending
-// order with ballots and only per-wave totals cross waves (through LDS).  The
-// histogram is shared; wave 0 scans it and posts each round's decision in
-// LDS.
+// over the 4 waves of the workgroup, wave w holding the contiguous ids
+// [64 E w, 64 E (w + 1)) as E registers per lane, so every wave compacts its
+// own kept ids in ascending order with ballots and only per-wave totals cross
+// waves (through LDS).  The histogram is shared; wave 0 scans it and posts
+// each round's decision in LDS.
 //
 // Probabilities are exp2 of the float64 score differences in float32, summed
 // as 2^-40 fixed-point integers: integer LDS atomics make the histograms (and
