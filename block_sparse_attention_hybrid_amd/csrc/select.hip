@@ -35,7 +35,9 @@
 //
 // Probabilities are exp2 of the float64 score differences in float32, summed
 // as 2^-40 fixed-point integers: integer LDS atomics make the histograms (and
-// so the lists) independent of thread scheduling.  For rows of up to 2048
+// so the lists) independent of thread scheduling.  Only the scores are kept
+// in registers; a probability is taken again wherever it is used, which
+// leaves room for one more wave per SIMD.  For rows of up to 2048
 // blocks a bucket's count and mass share one 64-bit word (count above bit
 // 52), so each element costs one LDS atomic.
 #include "sa_launch.h"
@@ -223,7 +225,6 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const double* __restri
   // every load first, at clamped in-row addresses, then the masking: no load
   // waits behind a branch
   double s[E];
-  float ev[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int j = first_id + e * kWave + lane;
@@ -239,7 +240,6 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const double* __restri
     const bool in = first_id + e * kWave + lane < n;
     const double v = s[e] == 0.0 ? 0.0 : s[e];  // -0 and +0 are the same score
     s[e] = in ? v : 0.0;
-    ev[e] = 0.f;
     valid |= (uint32_t)in << e;
     mx = fmax(mx, in ? v : -INFINITY);
     lo0 = fmin(lo0, in ? v : INFINITY);
@@ -267,9 +267,6 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const double* __restri
   if (keep_all) {
     above = valid;
   } else if (!keep_none) {
-#pragma unroll
-    for (int e = 0; e < E; ++e) ev[e] = ((valid >> e) & 1u) ? prob(s[e], mx) : 0.f;
-
     member = valid;
     int m = n;                 // members left (uniform over the workgroup)
     long long cnt_above = 0;
@@ -354,7 +351,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const double* __restri
       for (int e = 0; e < E; ++e)
         if ((member >> e) & 1u) {
           const int b = bucket(fresh(s[e]));
-          const unsigned long long f = to_fixed(fresh(ev[e]));
+          const unsigned long long f = to_fixed(prob(fresh(s[e]), mx));
           if constexpr (kPacked) {
             atomicAdd(&hist[b], (1ull << kCountShift) | f);
           } else {
@@ -458,7 +455,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const double* __restri
           if (is_mem) {
             const int idx = seen + __popcll(bm & lt);
             ckey[idx] = desc_key(s[e]);
-            cmass[idx] = to_fixed(ev[e]);
+            cmass[idx] = to_fixed(prob(s[e], mx));
           }
           seen += __popcll(bm);
         }
