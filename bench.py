@@ -2,7 +2,7 @@
 """Throughput of the hybrid block-sparse attention hot path on one MI355X.
 
 One step = the whole path on one batch of resident synthetic input:
-reorder Q and K (pooling them on the way) and V -> float64 block scores ->
+reorder Q and K (pooling them on the way) and V -> float32 block scores ->
 hybrid selection -> block-sparse forward writing O and LSE back in token order
 (the inverse re-indexing fused into its epilogue), all HIP kernels of
 libsparse_attn.so called through the C ABI.
@@ -114,7 +114,8 @@ class Path:
         self.lut = torch.empty((B, H, n, n), dtype=torch.int32, device=dev)
         self.counts = torch.empty((B, H, n), dtype=torch.int32, device=dev)
         self.qbar, self.kbar = (torch.empty((B, H, n, d), dtype=torch.float64, device=dev) for _ in range(2))
-        self.scores = torch.empty((B, H, n, n), dtype=torch.float64, device=dev)
+        self.scores = torch.empty((B, H, n, n), dtype=torch.float64, device=dev)   # path workspace; float64 rows
+        self.scores32 = torch.empty((B, H, n, n), dtype=torch.float32, device=dev)
         self.rb = None
         if budgets:
             self.rb = torch.from_numpy(synth.row_budgets(wl, 0)).to(dev)
@@ -132,8 +133,9 @@ class Path:
         return [
             ("reorder", lambda: sa.sparse_attn_reorder_qkv(self.q, self.k, self.v, self.qc, self.kc, self.vc,
                                                            self.qbar, self.kbar, g)),
-            ("mask", lambda: (sa.sparse_attn_block_scores(self.qbar, self.kbar, self.scores, 0.0, g),
-                              sa.sparse_attn_select(self.scores, g, self.k_frac, self.p, self.rb, self.lut,
+            # float32 block scores and the selection on them, as the whole-path call runs them
+            ("mask", lambda: (sa.sparse_attn_block_scores_f32(self.qbar, self.kbar, self.scores32, 0.0, g),
+                              sa.sparse_attn_select_f32(self.scores32, g, self.k_frac, self.p, self.rb, self.lut,
                                                     self.counts, self.cap))),
             # the forward with the inverse re-indexing fused (O and LSE in token order)
             # (the count-balanced row order where per-row budgets are given, as the whole-path call does)
@@ -198,7 +200,8 @@ def min_bytes(path):
 def algorithmic_bytes(path):
     """HBM bytes each stage of this implementation moves at minimum (per
     step): as min_bytes, plus the float64 block means written by the
-    re-indexing and read by the scores, and the scores at float64 size."""
+    re-indexing and read by the scores (the scores are float32, as in
+    min_bytes)."""
     wl = path.wl
     B, H, d, n = wl.batch, wl.heads, wl.head_dim, path.nblk
     real, pad = path.n_real, path.n_pad
@@ -208,7 +211,7 @@ def algorithmic_bytes(path):
         "reorder": B * H * (3 * (real + pad) * tok            # Q, K, V read and written
                             + 2 * n * d * 8),                 # Qbar, Kbar written
         "mask": (B * H * (2 * n * d * 8                       # Qbar, Kbar read
-                          + n * n * 8 * 2                     # scores written and read
+                          + n * n * 4 * 2                     # float32 scores written and read
                           + n * 4) + kept * 4),               # counts + kept ids
     }
 
@@ -235,6 +238,8 @@ def next_rows(path, reps=3):
     vbar = torch.empty((B, H, n, d), dtype=torch.float64, device=dev)
     ocb = torch.empty_like(vbar)
     out = {}
+    # the rows below take the float64 block scores (the path's workspace holds float32 ones)
+    sa.sparse_attn_block_scores(path.qbar, path.kbar, path.scores, 0.0, g)
     t_vpool = time_call(lambda: sa.sparse_attn_reorder_pool(path.v, path.vc, sa.SA_LAYOUT_V, vbar, g), reps)
     t_coarse = time_call(lambda: sa.sparse_attn_coarse(path.scores, vbar, ocb, g), reps)
     fl = 2.0 * B * H * n * n * d
@@ -620,9 +625,9 @@ def main():
         "mask_path_overlapped": mask_overlapped,
         "mask_path_bytes": {"implementation": int(abytes["reorder"] + abytes["mask"]),
                             "minimum": int(mbytes["reorder"] + mbytes["mask"]),
-                            "note": ("implementation: float64 means and scores as this library keeps them; "
-                                     "minimum: Q/K/V read and written once, scores float32 written and read "
-                                     "once, lists written once")},
+                            "note": ("implementation: float64 means and float32 scores as this library keeps "
+                                     "them; minimum: Q/K/V read and written once, scores float32 written and "
+                                     "read once, lists written once")},
         "roofline": {
             "bound": "mfma",
             "achieved": round(fwd_tflops, 2),

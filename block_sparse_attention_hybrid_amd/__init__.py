@@ -34,7 +34,8 @@ EXPORTED = (
     "sparse_attn_geometry", "sparse_attn_ceil_k", "sparse_attn_reorder",
     "sparse_attn_reorder_pool", "sparse_attn_reorder_qkv", "sparse_attn_unreorder", "sparse_attn_pool",
     "sparse_attn_block_scores",
-    "sparse_attn_select", "sparse_attn_mask_workspace_bytes", "sparse_attn_fwd_tokens",
+    "sparse_attn_select", "sparse_attn_block_scores_f32", "sparse_attn_select_f32",
+    "sparse_attn_mask_workspace_bytes", "sparse_attn_fwd_tokens",
     "sparse_attn_build_mask", "sparse_attn_fwd_workspace_bytes", "sparse_attn_fwd",
     "sparse_attn_coarse", "sparse_attn_router_pool", "sparse_attn_router_scores",
     "sparse_attn_bwd_delta", "sparse_attn_transpose_workspace_bytes", "sparse_attn_transpose_lut",
@@ -99,7 +100,9 @@ _SIGS = {
     "sparse_attn_unreorder": (_i32, [_vp, _vp, _vp, _vp, _GP, _vp]),
     "sparse_attn_pool": (_i32, [_vp, _vp, _vp, _vp, _GP, _vp]),
     "sparse_attn_block_scores": (_i32, [_vp, _vp, _vp, _f64, _GP, _vp]),
+    "sparse_attn_block_scores_f32": (_i32, [_vp, _vp, _vp, _f64, _GP, _vp]),
     "sparse_attn_select": (_i32, [_vp, _GP, _f64, _f64, _vp, _vp, _vp, _i32, _vp]),
+    "sparse_attn_select_f32": (_i32, [_vp, _GP, _f64, _f64, _vp, _vp, _vp, _i32, _vp]),
     "sparse_attn_mask_workspace_bytes": (_sz, [_GP]),
     "sparse_attn_build_mask": (_i32, [_vp, _vp, _GP, _i32, _f64, _f64, _vp, _vp, _vp, _i32, _vp, _sz, _vp]),
     "sparse_attn_fwd_workspace_bytes": (_sz, [_GP]),
@@ -235,6 +238,20 @@ def sparse_attn_select(scores, g: Geom, k_frac: float, p: float, row_budget, lut
                                     float(k_frac), float(p), _ptr(row_budget, torch.int32, "row_budget"),
                                     _ptr(lut, torch.int32, "lut"), _ptr(counts, torch.int32, "counts"),
                                     int(cap), _stream(stream, scores)))
+
+
+def sparse_attn_block_scores_f32(qbar, kbar, scores, scale: float, g: Geom, stream=None) -> None:
+    _check(lib().sparse_attn_block_scores_f32(_ptr(qbar, torch.float64, "qbar"), _ptr(kbar, torch.float64, "kbar"),
+                                              _ptr(scores, torch.float32, "scores"), float(scale),
+                                              ctypes.byref(g), _stream(stream, qbar)))
+
+
+def sparse_attn_select_f32(scores, g: Geom, k_frac: float, p: float, row_budget, lut, counts,
+                           cap: int, stream=None) -> None:
+    _check(lib().sparse_attn_select_f32(_ptr(scores, torch.float32, "scores"), ctypes.byref(g),
+                                        float(k_frac), float(p), _ptr(row_budget, torch.int32, "row_budget"),
+                                        _ptr(lut, torch.int32, "lut"), _ptr(counts, torch.int32, "counts"),
+                                        int(cap), _stream(stream, scores)))
 
 
 def sparse_attn_mask_workspace_bytes(g: Geom) -> int:
@@ -403,16 +420,16 @@ def reorder_pool(x: torch.Tensor, g: Geom, layout: int = SA_LAYOUT_QK, stream=No
 
 def mask_from_pooled(qbar, kbar, g: Geom, k_frac: float, p: float, row_budget=None, cap=None,
                      scores=None, stream=None):
-    """Pooled block scores and hybrid selection from block means (the rest of
-    build_mask once reorder_pool has pooled).  Returns (lut, counts)."""
+    """Pooled block scores (float32) and hybrid selection from block means:
+    the rest of build_mask once reorder_pool has pooled.  Returns (lut, counts)."""
     nblk, _, _ = sparse_attn_geometry(g)
     cap = nblk if cap is None else cap
     if scores is None:
-        scores = _empty((g.batch, g.heads, nblk, nblk), torch.float64, qbar)
+        scores = _empty((g.batch, g.heads, nblk, nblk), torch.float32, qbar)
     lut = _empty((g.batch, g.heads, nblk, cap), torch.int32, qbar)
     counts = _empty((g.batch, g.heads, nblk), torch.int32, qbar)
-    sparse_attn_block_scores(qbar, kbar, scores, 0.0, g, stream)
-    sparse_attn_select(scores, g, k_frac, p, row_budget, lut, counts, cap, stream)
+    sparse_attn_block_scores_f32(qbar, kbar, scores, 0.0, g, stream)
+    sparse_attn_select_f32(scores, g, k_frac, p, row_budget, lut, counts, cap, stream)
     return lut, counts
 
 

@@ -467,6 +467,32 @@ int32_t sparse_attn_block_scores(const double* qbar, const double* kbar, double*
                     "block score launch");
 }
 
+int32_t sparse_attn_block_scores_f32(const double* qbar, const double* kbar, float* scores, double scale,
+                                     const sa_geom* g, void* stream) {
+  sa::Geom d;
+  SA_TRY(make_geom(g, d));
+  if (d.nblk > 64 * 65535) return fail(SA_ERR_UNSUPPORTED, "too many blocks for the score grid");
+  SA_TRY(check_ptr(qbar, 8, "qbar"));
+  SA_TRY(check_ptr(kbar, 8, "kbar"));
+  SA_TRY(check_ptr(scores, 4, "scores"));
+  if (!std::isfinite(scale)) return fail(SA_ERR_INVALID_ARG, "scale must be finite");
+  if (scale <= 0.0) scale = 1.0 / std::sqrt((double)d.d);
+  return hip_status(sa::launch_block_scores(qbar, kbar, scores, scale, d, (hipStream_t)stream),
+                    "block score launch");
+}
+
+int32_t sparse_attn_select_f32(const float* scores, const sa_geom* g, double k_frac, double p,
+                               const int32_t* row_budget, int32_t* lut, int32_t* counts, int32_t cap,
+                               void* stream) {
+  sa::Geom d;
+  SA_TRY(make_geom(g, d));
+  SA_TRY(check_ptr(scores, 4, "scores"));
+  int kc = 0;
+  SA_TRY(check_select_args(d, k_frac, p, row_budget, lut, counts, cap, kc));
+  return hip_status(sa::launch_select(scores, d, kc, p, row_budget, lut, counts, cap, (hipStream_t)stream),
+                    "select launch");
+}
+
 int32_t sparse_attn_select(const double* scores, const sa_geom* g, double k_frac, double p,
                            const int32_t* row_budget, int32_t* lut, int32_t* counts, int32_t cap,
                            void* stream) {
@@ -500,7 +526,7 @@ int32_t sparse_attn_build_mask(const void* qc, const void* kc, const sa_geom* g,
   char* ws = static_cast<char*>(workspace);
   double* qbar = reinterpret_cast<double*>(ws);
   double* kbar = reinterpret_cast<double*>(ws + round_up(rows * d.d * sizeof(double)));
-  double* scores = reinterpret_cast<double*>(ws + 2 * round_up(rows * d.d * sizeof(double)));
+  float* scores = reinterpret_cast<float*>(ws + 2 * round_up(rows * d.d * sizeof(double)));
   hipStream_t s = (hipStream_t)stream;
   SA_TRY(hip_status(sa::launch_pool(qc, kc, qbar, kbar, d, s), "pool launch"));
   SA_TRY(hip_status(sa::launch_block_scores(qbar, kbar, scores, 1.0 / std::sqrt((double)d.d), d, s),
@@ -535,8 +561,8 @@ int32_t sparse_attn_build_mask_groups(const void* qc, const void* kc, const sa_g
   char* ws = static_cast<char*>(workspace);
   double* qbar = reinterpret_cast<double*>(ws);
   double* kbar = reinterpret_cast<double*>(ws + round_up(bh * nq * d.d * sizeof(double)));
-  double* scores = reinterpret_cast<double*>(ws + round_up(bh * nq * d.d * sizeof(double)) +
-                                             round_up(bh * d.nblk * d.d * sizeof(double)));
+  float* scores = reinterpret_cast<float*>(ws + round_up(bh * nq * d.d * sizeof(double)) +
+                                           round_up(bh * d.nblk * d.d * sizeof(double)));
   hipStream_t s = (hipStream_t)stream;
   SA_TRY(hip_status(sa::launch_pool_groups(qc, qbar, qgroup, d, s), "group pool launch"));
   SA_TRY(hip_status(sa::launch_pool_groups(kc, kbar, 1, d, s), "pool launch"));

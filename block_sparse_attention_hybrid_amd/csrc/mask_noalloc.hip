@@ -1,5 +1,5 @@
 // sparse_attn_build_mask without a caller workspace: the float64 block means
-// and scores live in a fixed device array of this library, for callers that
+// and float32 scores live in a fixed device array of this library, for callers that
 // cannot allocate device memory (code under HIP graph capture, serving loops,
 // harnesses that forbid hipMalloc).
 //
@@ -65,11 +65,11 @@ hipError_t scratch_address(void** out) {
 }
 
 // Scratch bytes of `heads` (batch, head) rows: block means of Q and K
-// [heads, nblk, d] and the scores [heads, nblk, nblk], float64, each region
-// 256-byte aligned.
+// [heads, nblk, d], float64, and the scores [heads, nblk, nblk], float32,
+// each region 256-byte aligned.
 size_t chunk_bytes(const sa::Geom& d, size_t heads) {
   const size_t n = (size_t)d.nblk;
-  return 2 * round_up(heads * n * d.d * sizeof(double)) + round_up(heads * n * n * sizeof(double));
+  return 2 * round_up(heads * n * d.d * sizeof(double)) + round_up(heads * n * n * sizeof(float));
 }
 
 }  // namespace
@@ -111,7 +111,7 @@ extern "C" int32_t sparse_attn_build_mask_noalloc(const void* qc, const void* kc
     char* ws = static_cast<char*>(base);
     double* qbar = reinterpret_cast<double*>(ws);
     double* kbar = reinterpret_cast<double*>(ws + round_up((size_t)nr * n * d.d * sizeof(double)));
-    double* sc = reinterpret_cast<double*>(ws + 2 * round_up((size_t)nr * n * d.d * sizeof(double)));
+    float* sc = reinterpret_cast<float*>(ws + 2 * round_up((size_t)nr * n * d.d * sizeof(double)));
     const char* q = static_cast<const char*>(qc) + (size_t)r0 * head_c;
     const char* k = static_cast<const char*>(kc) + (size_t)r0 * head_c;
     e = sa::launch_pool(q, k, qbar, kbar, gc, s);

@@ -122,7 +122,7 @@ hipError_t mask_phase(const sa_path_buffers* b, const sa::Geom& d, int kcount, d
   };
   auto mask = [&](int r0, int nr, hipStream_t st) -> hipError_t {
     const sa::Geom gc = rows_of(d, nr);
-    double* scores = b->scores + (size_t)r0 * nb * nb;
+    float* scores = static_cast<float*>(b->scores) + (size_t)r0 * nb * nb;
     hipError_t r = sa::launch_block_scores(b->qbar + (size_t)r0 * nb * tok, b->kbar + (size_t)r0 * nb * tok,
                                            scores, bscale, gc, st);
     if (r != hipSuccess) return r;

@@ -24,8 +24,15 @@ hipError_t launch_pool_groups(const void* xc, double* xbar, int qg, const Geom& 
 // nrows query rows per head (default nblk) against nblk key blocks
 hipError_t launch_block_scores(const double* qbar, const double* kbar, double* scores,
                                double scale, const Geom& g, hipStream_t s, int nrows = -1);
+// the same scores on the float32 matrix cores, written as float32
+hipError_t launch_block_scores(const double* qbar, const double* kbar, float* scores,
+                               double scale, const Geom& g, hipStream_t s, int nrows = -1);
 // rows_per_head rows of nblk scores per head (default nblk)
 hipError_t launch_select(const double* scores, const Geom& g, int kc_default, double p,
+                         const int32_t* row_budget, int32_t* lut, int32_t* counts,
+                         int cap, hipStream_t s, int rows_per_head = -1);
+// the same selection on float32 scores (each widened exactly to float64)
+hipError_t launch_select(const float* scores, const Geom& g, int kc_default, double p,
                          const int32_t* row_budget, int32_t* lut, int32_t* counts,
                          int cap, hipStream_t s, int rows_per_head = -1);
 // cube i of a head reads list row i >> qg_shift of its head's nlists rows

@@ -201,8 +201,8 @@ __device__ __forceinline__ void wave_scan(uint32_t& c, uint64_t& m, int lane) {
   m += row == 0 ? 0ull : row == 1 ? m0 : row == 2 ? m0 + m1 : m0 + m1 + m2;
 }
 
-template <int E>
-__global__ __launch_bounds__(kThreads) void select_kernel(const double* __restrict__ scores, int n,
+template <typename T, int E>
+__global__ __launch_bounds__(kThreads) void select_kernel(const T* __restrict__ scores, int n,
                                                           int kc_default, double p,
                                                           const int32_t* __restrict__ row_budget,
                                                           int32_t* __restrict__ lut,
@@ -220,11 +220,11 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const double* __restri
   const int first_id = wave * kWave * E;
   const uint64_t lt = lanemask_lt();
   const long long row = blockIdx.x;
-  const double* srow = scores + row * (long long)n;
+  const T* srow = scores + row * (long long)n;
 
   // every load first, at clamped in-row addresses, then the masking: no load
   // waits behind a branch
-  double s[E];
+  double s[E];   // float32 scores are widened exactly on load
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int j = first_id + e * kWave + lane;
@@ -533,12 +533,12 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const double* __restri
   if (threadIdx.x == 0) counts[row] = (int32_t)total;
 }
 
-template <int E>
-hipError_t launch_e(const double* scores, const Geom& g, int kc, double p, const int32_t* rb,
+template <int E, typename T>
+hipError_t launch_e(const T* scores, const Geom& g, int kc, double p, const int32_t* rb,
                     int32_t* lut, int32_t* counts, int cap, hipStream_t s, int rows_per_head) {
   const long long rows = (long long)g.batch * g.heads * rows_per_head;
   if (rows == 0) return hipSuccess;
-  select_kernel<E><<<dim3((unsigned)rows), kThreads, 0, s>>>(scores, g.nblk, kc, p, rb, lut, counts, cap);
+  select_kernel<T, E><<<dim3((unsigned)rows), kThreads, 0, s>>>(scores, g.nblk, kc, p, rb, lut, counts, cap);
   return hipGetLastError();
 }
 
@@ -563,10 +563,10 @@ constexpr int kRowsPerSelectGroup = 4;
 
 __device__ __forceinline__ void wave_fence() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); }
 
-template <int E>
+template <typename T, int E>
 __global__ __launch_bounds__(kWave * kRowsPerSelectGroup) __attribute__((amdgpu_waves_per_eu(4)))
 void select_wave_kernel(
-    const double* __restrict__ scores, int n, int kc_default, double p, const int32_t* __restrict__ row_budget,
+    const T* __restrict__ scores, int n, int kc_default, double p, const int32_t* __restrict__ row_budget,
     int32_t* __restrict__ lut, int32_t* __restrict__ counts, int cap, long long rows) {
   static_assert(E * kWave <= 2048, "packed histogram words need n <= 2048");
   __shared__ unsigned long long hist_all[kRowsPerSelectGroup][256];
@@ -578,10 +578,10 @@ void select_wave_kernel(
   unsigned long long* ckey = ckey_all[wave];
   unsigned long long* cmass = cmass_all[wave];
   const uint64_t lt = lanemask_lt();
-  const double* srow = scores + row * (long long)n;
+  const T* srow = scores + row * (long long)n;
 
   // every load first, at clamped in-row addresses, then the masking
-  double s[E];
+  double s[E];   // float32 scores are widened exactly on load
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int j = e * kWave + lane;
@@ -798,22 +798,23 @@ void select_wave_kernel(
   if (lane == 0) counts[row] = (int32_t)written;
 }
 
-template <int E>
-hipError_t launch_wave_e(const double* scores, const Geom& g, int kc, double p, const int32_t* rb,
+template <int E, typename T>
+hipError_t launch_wave_e(const T* scores, const Geom& g, int kc, double p, const int32_t* rb,
                          int32_t* lut, int32_t* counts, int cap, hipStream_t s, int rows_per_head) {
   const long long rows = (long long)g.batch * g.heads * rows_per_head;
   if (rows == 0) return hipSuccess;
   const long long grid = (rows + kRowsPerSelectGroup - 1) / kRowsPerSelectGroup;
-  select_wave_kernel<E><<<dim3((unsigned)grid), kWave * kRowsPerSelectGroup, 0, s>>>(scores, g.nblk, kc, p, rb,
+  select_wave_kernel<T, E><<<dim3((unsigned)grid), kWave * kRowsPerSelectGroup, 0, s>>>(scores, g.nblk, kc, p, rb,
                                                                                     lut, counts, cap, rows);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_select(const double* scores, const Geom& g, int kc_default, double p,
-                         const int32_t* row_budget, int32_t* lut, int32_t* counts, int cap,
-                         hipStream_t s, int rows_per_head) {
+template <typename T>
+hipError_t select_t(const T* scores, const Geom& g, int kc_default, double p,
+                    const int32_t* row_budget, int32_t* lut, int32_t* counts, int cap, hipStream_t s,
+                    int rows_per_head) {
   const int n = g.nblk;  // at most 4096 (checked by the caller)
   if (rows_per_head < 0) rows_per_head = n;
 #if SA_SELECT_ONE_WAVE
@@ -832,6 +833,18 @@ hipError_t launch_select(const double* scores, const Geom& g, int kc_default, do
   if (n <= 2048) return launch_e<8>(scores, g, kc_default, p, row_budget, lut, counts, cap, s, rows_per_head);
   if (n <= 3072) return launch_e<12>(scores, g, kc_default, p, row_budget, lut, counts, cap, s, rows_per_head);
   return launch_e<16>(scores, g, kc_default, p, row_budget, lut, counts, cap, s, rows_per_head);
+}
+
+hipError_t launch_select(const double* scores, const Geom& g, int kc_default, double p,
+                         const int32_t* row_budget, int32_t* lut, int32_t* counts, int cap,
+                         hipStream_t s, int rows_per_head) {
+  return select_t(scores, g, kc_default, p, row_budget, lut, counts, cap, s, rows_per_head);
+}
+
+hipError_t launch_select(const float* scores, const Geom& g, int kc_default, double p,
+                         const int32_t* row_budget, int32_t* lut, int32_t* counts, int cap,
+                         hipStream_t s, int rows_per_head) {
+  return select_t(scores, g, kc_default, p, row_budget, lut, counts, cap, s, rows_per_head);
 }
 
 }  // namespace sa

@@ -5,7 +5,8 @@
  * The path (all steps are GPU kernels of this library):
  *   reorder      row-major video tokens -> cube-major blocks of 64 tokens
  *   pool         per-block mean of Q and K over the block's real tokens
- *   block_scores S = Qbar Kbar^T * scale (float64 matrix cores)
+ *   block_scores S = Qbar Kbar^T * scale (float32 matrix cores on the path;
+ *                a float64 form beside it)
  *   select       per query block: hybrid Top-k U Top-p kept-block list
  *   fwd          block-sparse attention over the kept blocks -> O, LSE
  *                (fwd_tokens: the same, writing token order -- unreorder fused)
@@ -186,6 +187,17 @@ int32_t sparse_attn_block_scores(const double* qbar, const double* kbar,
                                  double* scores, double scale,
                                  const sa_geom* g, void* stream);
 
+/* The same block scores on the float32 matrix cores, written as float32: the
+ * float64 means are rounded to float32 and the products summed in float32.
+ * The page fixes no precision for this step; the error is a few 1e-7 of a
+ * row's largest |score|, inside the 1e-6 relative margin at which two scores
+ * count as tied for the selection.  Half the bytes of the float64 form.
+ *   qbar, kbar [batch, heads, nblk, head_dim] float64   (inputs)
+ *   scores     [batch, heads, nblk, nblk] float32       (output) */
+int32_t sparse_attn_block_scores_f32(const double* qbar, const double* kbar,
+                                     float* scores, double scale,
+                                     const sa_geom* g, void* stream);
+
 /* Coarse branch output, [VSA] "The Coarse Stage" ([VSA2] section 2.2):
  * attention at block granularity on the pooled tokens,
  *   oc[i] = sum_j softmax(scores[i, :])_j * vbar[j],
@@ -238,7 +250,9 @@ typedef struct sa_path_buffers {
   void* vc;
   double* qbar;         /* [batch, heads, nblk, head_dim] float64 block means (written) */
   double* kbar;
-  double* scores;       /* [batch, heads, nblk, nblk] float64 pooled scores (written; with
+  void* scores;         /* workspace of batch*heads*nblk*nblk*8 bytes, 8-byte aligned; holds
+                           the float32 pooled scores [batch, heads, nblk, nblk] in its first
+                           half on return (as sparse_attn_block_scores_f32 writes them; with
                            row_budget its start is then reused for the forward's
                            count-balanced row order, see sparse_attn_fwd) */
   int32_t* lut;         /* [batch, heads, nblk, cap] kept lists (written) */
@@ -420,14 +434,25 @@ int32_t sparse_attn_select(const double* scores, const sa_geom* g,
                            int32_t* lut, int32_t* counts, int32_t cap,
                            void* stream);
 
-/* Bytes of workspace sparse_attn_build_mask needs (Qbar, Kbar and scores in
- * float64, each region 256-byte aligned). 0 on an invalid geometry. */
+/* sparse_attn_select on float32 scores (sparse_attn_block_scores_f32): each
+ * score is widened exactly to float64 when loaded, so the lists are those
+ * sparse_attn_select gives for the same values; same arguments and errors.
+ *   scores [batch, heads, nblk, nblk] float32                 (input) */
+int32_t sparse_attn_select_f32(const float* scores, const sa_geom* g,
+                               double k_frac, double p, const int32_t* row_budget,
+                               int32_t* lut, int32_t* counts, int32_t cap,
+                               void* stream);
+
+/* Bytes of workspace sparse_attn_build_mask needs (Qbar and Kbar in float64,
+ * then room for the scores at 8 bytes each, each region 256-byte aligned).
+ * 0 on an invalid geometry. */
 size_t sparse_attn_mask_workspace_bytes(const sa_geom* g);
 
-/* pool + block_scores + select in one call (scale 1/sqrt(head_dim)).  block
- * must be 64.  Arguments as for those functions; the float64 intermediates
- * live in `workspace` (>= sparse_attn_mask_workspace_bytes, else
- * SA_ERR_CAPACITY). */
+/* pool + block_scores_f32 + select_f32 in one call (scale 1/sqrt(head_dim)):
+ * float64 block means, float32 scores (the same lists as the float64 scores
+ * outside near ties; the whole-path calls use the same kernels).  block must
+ * be 64.  Arguments as for those functions; the intermediates live in
+ * `workspace` (>= sparse_attn_mask_workspace_bytes, else SA_ERR_CAPACITY). */
 int32_t sparse_attn_build_mask(const void* qc, const void* kc,
                                const sa_geom* g, int32_t block, double k_frac,
                                double p, const int32_t* row_budget,
@@ -438,12 +463,12 @@ int32_t sparse_attn_build_mask(const void* qc, const void* kc,
 /* sparse_attn_build_mask for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc): the same arguments without the workspace, the same lists and
- * counts.  The float64 block means and scores live in a device array of the
- * library, fixed at sparse_attn_build_mask_noalloc_scratch_bytes() (64 MiB)
- * per GPU and held until the process ends; the (batch, head) rows are taken
- * in chunks that fit it, one after another on `stream`.  One (batch, head)
- * needs 2*round256(nblk*head_dim*8) + round256(nblk*nblk*8) bytes; above the
- * array's size (nblk above about 2,700 at head_dim 128) the call returns
+ * counts.  The float64 block means and float32 scores live in a device array
+ * of the library, fixed at sparse_attn_build_mask_noalloc_scratch_bytes()
+ * (64 MiB) per GPU and held until the process ends; the (batch, head) rows are
+ * taken in chunks that fit it, one after another on `stream`.  One (batch,
+ * head) needs 2*round256(nblk*head_dim*8) + round256(nblk*nblk*4) bytes; above
+ * the array's size (nblk above about 3,800 at head_dim 128) the call returns
  * SA_ERR_CAPACITY and launches nothing.  The call allocates and frees
  * nothing.  Calls on one GPU share the array: calls that overlap (other
  * streams, other host threads) race and must be ordered by the caller. */

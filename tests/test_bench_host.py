@@ -36,9 +36,9 @@ def test_algorithmic_bytes_at_720p():
     # 256 B a row = 128,839,680 B, plus the float64 means of Q and K (2 x 1,440 x 128 x 8
     # = 2,949,120 B)
     assert got["reorder"] == 40 * (128_839_680 + 2_949_120)
-    # mask, per head: the means read back (2,949,120 B), the float64 scores written and
-    # read (2 x 1,440^2 x 8 = 33,177,600 B) and the counts (5,760 B); 4 B per kept id
-    assert got["mask"] == 40 * (2_949_120 + 33_177_600 + 5_760) + 4 * kept
+    # mask, per head: the means read back (2,949,120 B), the float32 scores written and
+    # read (2 x 1,440^2 x 4 = 16,588,800 B) and the counts (5,760 B); 4 B per kept id
+    assert got["mask"] == 40 * (2_949_120 + 16_588_800 + 5_760) + 4 * kept
 
 
 def test_recorded_traffic_only_for_the_profiled_kernel_and_workload():

@@ -136,6 +136,18 @@ def test_select_argument_rules():
     big = geom(frames=64, height=64, width=68)      # 16*16*17 = 4352 blocks > 4096
     assert lib.sparse_attn_select(FAKE, ctypes.byref(big), 0.1, 0.0, None, FAKE, FAKE, 5000,
                                   None) == sa.SA_ERR_UNSUPPORTED
+    # the float32 forms follow the same rules
+    assert lib.sparse_attn_select_f32(FAKE, B, 0.25, 0.5, None, FAKE, FAKE, 15, None) == sa.SA_ERR_CAPACITY
+    assert lib.sparse_attn_select_f32(FAKE, B, 0.0, 0.5, FAKE, FAKE, FAKE, 16, None) == sa.SA_ERR_INVALID_ARG
+    assert lib.sparse_attn_select_f32(None, B, 0.25, 0.5, None, FAKE, FAKE, 16, None) == sa.SA_ERR_INVALID_ARG
+    assert lib.sparse_attn_select_f32(ctypes.c_void_p(0x100002), B, 0.25, 0.5, None, FAKE, FAKE, 16,
+                                      None) == sa.SA_ERR_INVALID_ARG          # scores misaligned
+    assert lib.sparse_attn_select_f32(FAKE, ctypes.byref(big), 0.1, 0.0, None, FAKE, FAKE, 5000,
+                                      None) == sa.SA_ERR_UNSUPPORTED
+    assert lib.sparse_attn_block_scores_f32(FAKE, FAKE, None, 0.0, B, None) == sa.SA_ERR_INVALID_ARG
+    assert lib.sparse_attn_block_scores_f32(FAKE, FAKE, ctypes.c_void_p(0x200002), 0.0, B,
+                                            None) == sa.SA_ERR_INVALID_ARG    # scores misaligned
+    assert lib.sparse_attn_block_scores_f32(FAKE, FAKE, FAKE, float("nan"), B, None) == sa.SA_ERR_INVALID_ARG
 
 
 def test_build_mask_argument_rules():
@@ -298,7 +310,7 @@ def test_noalloc_mask_rejects_before_any_launch():
     array, all before touching the device."""
     lib = sa.lib()
     assert lib.sparse_attn_build_mask_noalloc_scratch_bytes() == 64 << 20
-    g = geom(frames=16, height=128, width=128, head_dim=128)           # 4096 blocks: 142 MB per head
+    g = geom(frames=16, height=128, width=128, head_dim=128)           # 4096 blocks: 75.5 MB per head
     assert sa.sparse_attn_geometry(g)[0] == 4096
     rc = lib.sparse_attn_build_mask_noalloc(FAKE, FAKE, ctypes.byref(g), 64, ctypes.c_double(0.03),
                                             ctypes.c_double(0.5), None, FAKE, FAKE, 4096, None)

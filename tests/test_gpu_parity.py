@@ -148,6 +148,40 @@ def test_select_on_oracle_scores(case):
     assert not bad and not invalid
 
 
+def test_block_scores_f32(case):
+    """The float32 block scores against the oracle's float64 ones: within
+    2e-6 of each row's largest |score| (float32 products of d terms round to a
+    few 1e-7 of it; the near-tie margin is 1e-6 of it)."""
+    g, ref = case["g"], case["ref_mask"]
+    qbar, kbar = torch.from_numpy(ref.qbar).to(DEV), torch.from_numpy(ref.kbar).to(DEV)
+    B, H, n, _ = ref.scores.shape
+    s = torch.full((B, H, n, n), 7.0, dtype=torch.float32, device=DEV)
+    sa.sparse_attn_block_scores_f32(qbar, kbar, s, 0.0, g)
+    torch.cuda.synchronize()
+    got = s.cpu().numpy().astype(np.float64)
+    scale = np.abs(ref.scores).max(axis=-1, keepdims=True)
+    rel = np.abs(got - ref.scores) / np.maximum(scale, 1e-300)
+    say(f"  scores f32: max error {rel.max():.2e} of the row's largest |score|")
+    assert rel.max() <= 2e-6
+
+
+def test_select_f32_on_rounded_oracle_scores(case):
+    """sparse_attn_select_f32 on the oracle's scores rounded to float32: the
+    oracle's lists of exactly those values (the kernel widens them exactly),
+    outside near ties."""
+    g, og, ref = case["g"], case["og"], case["ref_mask"]
+    s32 = ref.scores.astype(np.float32)
+    want = _ref_lists(s32.astype(np.float64), O.ceil_k(case["k_frac"], og.nblk), case["p"])
+    nblk = og.nblk
+    lut = torch.full((g.batch, g.heads, nblk, nblk), -7, dtype=torch.int32, device=DEV)
+    counts = torch.empty((g.batch, g.heads, nblk), dtype=torch.int32, device=DEV)
+    sa.sparse_attn_select_f32(torch.from_numpy(s32).to(DEV), g, case["k_frac"], case["p"], None, lut, counts, nblk)
+    torch.cuda.synchronize()
+    bad, near, invalid = compare_lists(lut.cpu().numpy(), counts.cpu().numpy(), want, case["p"])
+    say(f"  select f32: {len(bad)} mismatched rows, {near} near ties ({len(invalid)} invalid)")
+    assert not bad and not invalid
+
+
 def _select_rows_for(n, seed):
     """An n x n score matrix whose rows exercise the selection's paths: random
     rows at several scales, rows of few distinct values (exact ties at the
@@ -181,26 +215,34 @@ def _exact_tie_only(s_row, ref, i, p):
     return True
 
 
+@pytest.mark.parametrize("dtype", ["f64", "f32"])
 @pytest.mark.parametrize("grid,nblk", [((12, 40, 40), 300), ((16, 80, 80), 1600), ((20, 80, 84), 2100),
                                        ((16, 128, 128), 4096)])
-def test_select_large_rows(grid, nblk):
+def test_select_large_rows(grid, nblk, dtype):
     """The selection at 300-4096 blocks per row (the kernel's 2-, 8-, 12- and
     16-element-per-lane forms, the last two with separate count and mass
     histograms), on oracle-checked score matrices with ties, all-equal rows,
     large equal groups and per-row budgets."""
-    say(f"[select nblk={nblk}]")
+    say(f"[select nblk={nblk} {dtype}]")
     g = sa.make_geom(1, 1, *grid, 128)
     assert sa.sparse_attn_geometry(g)[0] == nblk
     s = _select_rows_for(nblk, nblk)[None, None]
-    sd = torch.from_numpy(s).to(DEV)
+    if dtype == "f32":
+        # float32 scores: the reference is the oracle on exactly those values
+        s32 = s.astype(np.float32)
+        s = s32.astype(np.float64)
+        sd = torch.from_numpy(s32).to(DEV)
+        select = sa.sparse_attn_select_f32
+    else:
+        sd = torch.from_numpy(s).to(DEV)
+        select = sa.sparse_attn_select
     for k_frac, p, budgets in ((0.03, 0.5, False), (0.01, 0.9, False), (0.0, 0.0, True)):
         rb = None
         if budgets:
             rb = np.random.default_rng(3).integers(0, nblk + 1, size=(1, 1, nblk)).astype(np.int32)
         lut = torch.full((1, 1, nblk, nblk), -7, dtype=torch.int32, device=DEV)
         counts = torch.empty((1, 1, nblk), dtype=torch.int32, device=DEV)
-        sa.sparse_attn_select(sd, g, k_frac, p, None if rb is None else torch.from_numpy(rb).to(DEV), lut,
-                              counts, nblk)
+        select(sd, g, k_frac, p, None if rb is None else torch.from_numpy(rb).to(DEV), lut, counts, nblk)
         torch.cuda.synchronize()
         if budgets:
             ref = _ref_budget_lists(s, rb)
