@@ -37,6 +37,7 @@ import synth  # noqa: E402
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
 PEAK_FP64_TFLOPS = 78.6        # MI355X float64 (vector and matrix)
+PEAK_FP32_MFMA_TFLOPS = 157.3  # MI355X float32 matrix cores
 
 # HBM-side traffic of the forward kernel, measured by rocprofv3 counters and
 # recorded with a hash of the sources it was measured on
@@ -257,7 +258,21 @@ def next_rows(path, reps=3):
     out["router_2x2x2"] = {"ms": round(t_router, 3), "pool_ms": round(t_rpool, 4),
                            "tflops_fp64": round(fl / t_router / 1e9, 2),
                            "frac_of_fp64_peak": round(fl / t_router / 1e9 / PEAK_FP64_TFLOPS, 4)}
-    del qr, kr, rs
+    # the float32 router on the same means, and how many rows' lists differ from the float64 ones
+    rs32 = torch.empty((B, H, n, n), dtype=torch.float32, device=dev)
+    t_r32 = time_call(lambda: sa.sparse_attn_router_scores_f32(qr, kr, rs32, 0.0, g, sub), 1)
+    la, ca = (torch.empty((B, H, n, n), dtype=torch.int32, device=dev), torch.empty((B, H, n), dtype=torch.int32,
+                                                                                       device=dev))
+    lb, cb = torch.empty_like(la), torch.empty_like(ca)
+    sa.sparse_attn_select(rs, g, path.k_frac, path.p, None, la, ca, n)
+    sa.sparse_attn_select_f32(rs32, g, path.k_frac, path.p, None, lb, cb, n)
+    m = torch.arange(n, device=dev)[None, None, None, :] < ca[..., None]
+    differ = int((~((ca == cb) & torch.where(m, la == lb, True).all(-1))).sum())
+    out["router_2x2x2_f32"] = {"ms": round(t_r32, 3),
+                               "tflops": round(fl / t_r32 / 1e9, 2),
+                               "frac_of_fp32_matrix_peak": round(fl / t_r32 / 1e9 / PEAK_FP32_MFMA_TFLOPS, 4),
+                               "rows_differing_from_fp64_lists": differ, "rows": B * H * n}
+    del qr, kr, rs, rs32, la, lb
     # backward over the same lists: the slot-major forward outputs and the
     # operand layouts it reads are prepared untimed
     sa.sparse_attn_fwd(path.qc, path.kc, path.vc, path.lut, path.counts, path.cap, g, 0.0, path.oc, path.lse_c,

@@ -37,7 +37,7 @@ EXPORTED = (
     "sparse_attn_select", "sparse_attn_block_scores_f32", "sparse_attn_select_f32",
     "sparse_attn_mask_workspace_bytes", "sparse_attn_fwd_tokens",
     "sparse_attn_build_mask", "sparse_attn_fwd_workspace_bytes", "sparse_attn_fwd",
-    "sparse_attn_coarse", "sparse_attn_router_pool", "sparse_attn_router_scores",
+    "sparse_attn_coarse", "sparse_attn_router_pool", "sparse_attn_router_scores", "sparse_attn_router_scores_f32",
     "sparse_attn_bwd_delta", "sparse_attn_transpose_workspace_bytes", "sparse_attn_transpose_lut",
     "sparse_attn_bwd", "sparse_attn_pooled_mass", "sparse_attn_mask_error", "sparse_attn_mask_error_terms",
     "sparse_attn_attention", "sparse_attn_mask_path",
@@ -111,6 +111,7 @@ _SIGS = {
     "sparse_attn_coarse": (_i32, [_vp, _vp, _vp, _GP, _vp]),
     "sparse_attn_router_pool": (_i32, [_vp, _vp, _GP, _i32, _i32, _i32, _vp]),
     "sparse_attn_router_scores": (_i32, [_vp, _vp, _vp, _f64, _GP, _i32, _i32, _i32, _vp]),
+    "sparse_attn_router_scores_f32": (_i32, [_vp, _vp, _vp, _f64, _GP, _i32, _i32, _i32, _vp]),
     "sparse_attn_bwd_delta": (_i32, [_vp, _vp, _vp, _GP, _vp]),
     "sparse_attn_transpose_workspace_bytes": (_sz, [_GP]),
     "sparse_attn_transpose_lut": (_i32, [_vp, _vp, _i32, _vp, _vp, _i32, _GP, _vp, _sz, _vp]),
@@ -323,6 +324,12 @@ def sparse_attn_router_scores(qr, kr, scores, scale: float, g: Geom, sub=(2, 2, 
     _check(lib().sparse_attn_router_scores(_ptr(qr, torch.float64, "qr"), _ptr(kr, torch.float64, "kr"),
                                            _ptr(scores, torch.float64, "scores"), float(scale), ctypes.byref(g),
                                            int(sub[0]), int(sub[1]), int(sub[2]), _stream(stream, qr)))
+
+
+def sparse_attn_router_scores_f32(qr, kr, scores, scale: float, g: Geom, sub=(2, 2, 2), stream=None) -> None:
+    _check(lib().sparse_attn_router_scores_f32(_ptr(qr, torch.float64, "qr"), _ptr(kr, torch.float64, "kr"),
+                                               _ptr(scores, torch.float32, "scores"), float(scale), ctypes.byref(g),
+                                               int(sub[0]), int(sub[1]), int(sub[2]), _stream(stream, qr)))
 
 
 def sparse_attn_bwd_delta(oc, do_qk, delta, g: Geom, stream=None) -> None:
@@ -589,21 +596,25 @@ def coarse(scores, vbar, g: Geom, stream=None) -> torch.Tensor:
 
 
 def router_mask(qc, kc, g: Geom, k_frac: float, p: float, sub=(2, 2, 2), row_budget=None, cap=None,
-                stream=None):
-    """Hybrid selection on the fine-grained router's block scores.
-    Returns (lut, counts, scores = log P_r)."""
+                stream=None, dtype=torch.float64):
+    """Hybrid selection on the fine-grained router's block scores, computed in
+    `dtype` (torch.float64 or torch.float32).  Returns (lut, counts, scores = log P_r)."""
     nblk, _, _ = sparse_attn_geometry(g)
     G = 64 // (sub[0] * sub[1] * sub[2])
     cap = nblk if cap is None else cap
     qr = _empty((g.batch, g.heads, nblk * G, g.head_dim), torch.float64, qc)
     kr = torch.empty_like(qr)
-    scores = _empty((g.batch, g.heads, nblk, nblk), torch.float64, qc)
+    scores = _empty((g.batch, g.heads, nblk, nblk), dtype, qc)
     lut = _empty((g.batch, g.heads, nblk, cap), torch.int32, qc)
     counts = _empty((g.batch, g.heads, nblk), torch.int32, qc)
     sparse_attn_router_pool(qc, qr, g, sub, stream)
     sparse_attn_router_pool(kc, kr, g, sub, stream)
-    sparse_attn_router_scores(qr, kr, scores, 0.0, g, sub, stream)
-    sparse_attn_select(scores, g, k_frac, p, row_budget, lut, counts, cap, stream)
+    if dtype == torch.float32:
+        sparse_attn_router_scores_f32(qr, kr, scores, 0.0, g, sub, stream)
+        sparse_attn_select_f32(scores, g, k_frac, p, row_budget, lut, counts, cap, stream)
+    else:
+        sparse_attn_router_scores(qr, kr, scores, 0.0, g, sub, stream)
+        sparse_attn_select(scores, g, k_frac, p, row_budget, lut, counts, cap, stream)
     return lut, counts, scores
 
 

@@ -278,6 +278,19 @@ int32_t sparse_attn_router_scores(const double* qr, const double* kr, double* sc
   return hip_status(sa::launch_router(qr, kr, scores, scale, d, rt, rh, rw, (hipStream_t)stream), "router launch");
 }
 
+int32_t sparse_attn_router_scores_f32(const double* qr, const double* kr, float* scores, double scale,
+                                      const sa_geom* g, int32_t rt, int32_t rh, int32_t rw, void* stream) {
+  sa::Geom d;
+  SA_TRY(make_geom(g, d));
+  SA_TRY(check_subcube(d, rt, rh, rw));
+  SA_TRY(check_ptr(qr, 8, "qr"));
+  SA_TRY(check_ptr(kr, 8, "kr"));
+  SA_TRY(check_ptr(scores, 4, "scores"));
+  if (!std::isfinite(scale)) return fail(SA_ERR_INVALID_ARG, "scale must be finite");
+  if (scale <= 0.0) scale = 1.0 / std::sqrt((double)d.d);
+  return hip_status(sa::launch_router(qr, kr, scores, scale, d, rt, rh, rw, (hipStream_t)stream), "router launch");
+}
+
 int32_t sparse_attn_bwd_delta(const void* oc, const void* do_qk, float* delta, const sa_geom* g, void* stream) {
   sa::Geom d;
   SA_TRY(make_geom(g, d));

@@ -21,6 +21,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace sa {
 
 namespace {
@@ -88,17 +90,22 @@ __global__ __launch_bounds__(kThreads) void router_pool_kernel(const bf16* __res
   }
 }
 
-// Router scores of a 64 x 64 tile (rows r0.., columns c0..) into LDS S.
+// Router scores of a 64 x 64 tile (rows r0.., columns c0..) into LDS S, in
+// float64 (v_mfma_f64_16x16x4f64: accumulator row lane/16 + 4r) or float32
+// (v_mfma_f32_16x16x4f32, the means rounded to float32 as they are staged:
+// accumulator row 4 (lane/16) + r).
+template <typename T>
 __device__ __forceinline__ void score_tile(const double* __restrict__ qh, const double* __restrict__ kh,
-                                           int nr, int d, int r0, int c0, double scale, double* As,
-                                           double* Bs, double* S) {
+                                           int nr, int d, int r0, int c0, double scale, T* As,
+                                           T* Bs, T* S) {
+  using Acc = typename std::conditional<std::is_same<T, double>::value, f64x4, f32x4>::type;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  f64x4 acc[2][2];
+  Acc acc[2][2];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
+    for (int b = 0; b < 2; ++b) acc[a][b] = Acc{0, 0, 0, 0};
   const int lr = threadIdx.x >> 2, lc = (threadIdx.x & 3) * 4;
   const int gi = r0 + lr, gj = c0 + lr;
   const double* qrow = qh + (long long)(gi < nr ? gi : nr - 1) * d + lc;
@@ -114,8 +121,8 @@ __device__ __forceinline__ void score_tile(const double* __restrict__ qh, const 
   for (int k0 = 0; k0 < d; k0 += kKc) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      As[lr * kLd + lc + e] = gi < nr ? an[e] : 0.0;
-      Bs[lr * kLd + lc + e] = gj < nr ? bn[e] : 0.0;
+      As[lr * kLd + lc + e] = gi < nr ? (T)an[e] : (T)0;
+      Bs[lr * kLd + lc + e] = gj < nr ? (T)bn[e] : (T)0;
     }
     __syncthreads();
     if (k0 + kKc < d) {
@@ -130,45 +137,57 @@ __device__ __forceinline__ void score_tile(const double* __restrict__ qh, const 
       const int kk = ks + (lane >> 4);
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
-        const double a = As[(wm * 32 + mt * 16 + (lane & 15)) * kLd + kk];
+        const T a = As[(wm * 32 + mt * 16 + (lane & 15)) * kLd + kk];
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
-          const double b = Bs[(wn * 32 + nt * 16 + (lane & 15)) * kLd + kk];
-          acc[mt][nt] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, acc[mt][nt], 0, 0, 0);
+          const T b = Bs[(wn * 32 + nt * 16 + (lane & 15)) * kLd + kk];
+          if constexpr (std::is_same<T, double>::value)
+            acc[mt][nt] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, acc[mt][nt], 0, 0, 0);
+          else
+            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc[mt][nt], 0, 0, 0);
         }
       }
     }
     __syncthreads();
   }
+  const T sc = (T)scale;
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int row = wm * 32 + mt * 16 + (lane >> 4) + 4 * r;
+        const int rr = std::is_same<T, double>::value ? (lane >> 4) + 4 * r : 4 * (lane >> 4) + r;
+        const int row = wm * 32 + mt * 16 + rr;
         const int col = wn * 32 + nt * 16 + (lane & 15);
-        S[row * (kTile + 1) + col] = acc[mt][nt][r] * scale;
+        S[row * (kTile + 1) + col] = acc[mt][nt][r] * sc;
       }
   __syncthreads();
 }
+
+__device__ __forceinline__ double exp_of(double x) { return exp(x); }
+__device__ __forceinline__ float exp_of(float x) { return __expf(x); }
 
 // One workgroup per (64 router rows, batch*head).  Pass 1: log-sum-exp of
 // every row over the present sub-cube keys.  Pass 2: P_hat = exp(S - lse),
 // aggregated per (query block, key block) pair of the tile.
 // Held to 128 registers and 34 KB of LDS: four workgroups (four waves per
 // SIMD) instead of three per compute unit, 5% faster with the same output.
+// T = float: the sub-cube scores, their exponentials and the tile in float32
+// (the log-sum-exp still accumulates in float64), and log P_r written as
+// float32 for the float32 selection.
+template <typename T>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
-void router_kernel(const double* __restrict__ qr, const double* __restrict__ kr, double* __restrict__ scores,
+void router_kernel(const double* __restrict__ qr, const double* __restrict__ kr, T* __restrict__ scores,
                    double scale, Geom g, SubCube sc) {
   // the staged operands and the score tile are never live at once (a barrier
   // separates the last operand read of a tile from its score writes, and the
   // last score read from the next tile's staging), so they share LDS
   constexpr int kStage = 2 * kTile * kLd, kScores = kTile * (kTile + 1);
-  __shared__ double smem[kStage > kScores ? kStage : kScores];
-  double* As = smem;
-  double* Bs = smem + kTile * kLd;
-  double* S = smem;
+  __shared__ T smem[kStage > kScores ? kStage : kScores];
+  T* As = smem;
+  T* Bs = smem + kTile * kLd;
+  T* S = smem;
   __shared__ double lse[kTile];
   __shared__ unsigned char kpres[kTile];
   const int G = sc.G, n = g.nblk, nr = n * G, d = g.d;
@@ -189,14 +208,14 @@ void router_kernel(const double* __restrict__ qr, const double* __restrict__ kr,
     double tm = -INFINITY;
     for (int e = 0; e < 16; ++e) {
       const int c = part * 16 + e;
-      if (kpres[c]) tm = fmax(tm, S[row * (kTile + 1) + c]);
+      if (kpres[c]) tm = fmax(tm, (double)S[row * (kTile + 1) + c]);
     }
     if (tm > -INFINITY) {
       const double mn = fmax(m, tm);
       double sum = 0.0;
       for (int e = 0; e < 16; ++e) {
         const int c = part * 16 + e;
-        if (kpres[c]) sum += exp(S[row * (kTile + 1) + c] - mn);
+        if (kpres[c]) sum += exp_of((T)((double)S[row * (kTile + 1) + c] - mn));
       }
       l = (m == -INFINITY ? 0.0 : l * exp(m - mn)) + sum;
       m = mn;
@@ -230,10 +249,10 @@ void router_kernel(const double* __restrict__ qr, const double* __restrict__ kr,
     //     the first score of that block's column range (in place, one owner)
     for (int u = threadIdx.x; u < kTile * nb; u += kThreads) {
       const int rr = u / nb, bj = u - rr * nb;
-      double e = 0.0;
+      T e = 0;
       for (int b = 0; b < G; ++b) {
         const int cc = bj * G + b;
-        if (kpres[cc]) e += exp(S[rr * (kTile + 1) + cc] - lse[rr]);
+        if (kpres[cc]) e += exp_of((T)((double)S[rr * (kTile + 1) + cc] - lse[rr]));
       }
       S[rr * (kTile + 1) + bj * G] = e;
     }
@@ -250,7 +269,7 @@ void router_kernel(const double* __restrict__ qr, const double* __restrict__ kr,
         ++na;
         acc += S[(bi * G + a) * (kTile + 1) + bj * G];
       }
-      scores[(bh * n + i) * (long long)n + j] = log(acc / (double)na);
+      scores[(bh * n + i) * (long long)n + j] = (T)log(acc / (double)na);
     }
     __syncthreads();
   }
@@ -276,13 +295,24 @@ hipError_t launch_router_pool(const void* xc, double* xr, const Geom& g, int rt,
   return hipGetLastError();
 }
 
-hipError_t launch_router(const double* qr, const double* kr, double* scores, double scale, const Geom& g,
-                         int rt, int rh, int rw, hipStream_t s) {
+template <typename T>
+hipError_t router_t(const double* qr, const double* kr, T* scores, double scale, const Geom& g, int rt, int rh,
+                    int rw, hipStream_t s) {
   const SubCube sc = make_subcube(g, rt, rh, rw);
   const long long nr = (long long)g.nblk * sc.G;
   dim3 grid((unsigned)((nr + kTile - 1) / kTile), g.batch * g.heads);
-  router_kernel<<<grid, kThreads, 0, s>>>(qr, kr, scores, scale, g, sc);
+  router_kernel<T><<<grid, kThreads, 0, s>>>(qr, kr, scores, scale, g, sc);
   return hipGetLastError();
+}
+
+hipError_t launch_router(const double* qr, const double* kr, double* scores, double scale, const Geom& g,
+                         int rt, int rh, int rw, hipStream_t s) {
+  return router_t(qr, kr, scores, scale, g, rt, rh, rw, s);
+}
+
+hipError_t launch_router(const double* qr, const double* kr, float* scores, double scale, const Geom& g,
+                         int rt, int rh, int rw, hipStream_t s) {
+  return router_t(qr, kr, scores, scale, g, rt, rh, rw, s);
 }
 
 }  // namespace sa

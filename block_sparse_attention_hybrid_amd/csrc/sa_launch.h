@@ -54,6 +54,9 @@ size_t fwd_workspace_bytes(const Geom& g);
 hipError_t launch_router_pool(const void* xc, double* xr, const Geom& g, int rt, int rh, int rw, hipStream_t s);
 hipError_t launch_router(const double* qr, const double* kr, double* scores, double scale, const Geom& g,
                          int rt, int rh, int rw, hipStream_t s);
+// the same in float32 (log-sum-exp in float64), log P_r written as float32
+hipError_t launch_router(const double* qr, const double* kr, float* scores, double scale, const Geom& g,
+                         int rt, int rh, int rw, hipStream_t s);
 // Operands of the backward pass (device pointers, see sparse_attn_bwd).
 struct BwdArgs {
   const void *q, *k, *v_qk, *k_v, *do_qk;

@@ -239,6 +239,16 @@ int32_t sparse_attn_router_scores(const double* qr, const double* kr,
                                   const sa_geom* g, int32_t rt, int32_t rh,
                                   int32_t rw, void* stream);
 
+/* sparse_attn_router_scores on the float32 matrix cores: the sub-cube means
+ * rounded to float32, the sub-cube scores and their exponentials in float32,
+ * the row log-sum-exp accumulated in float64, and log P_r written as float32
+ * for sparse_attn_select_f32.  Checked against the float64 lists of the
+ * oracle outside near ties; about twice as fast.
+ *   scores [batch, heads, nblk, nblk] float32 = log P_r               (output) */
+int32_t sparse_attn_router_scores_f32(const double* qr, const double* kr,
+                                      float* scores, double scale, const sa_geom* g,
+                                      int32_t rt, int32_t rh, int32_t rw, void* stream);
+
 /* ---- the whole path in one call ------------------------------------------
  * Buffers of sparse_attn_attention (device pointers the caller allocated). */
 typedef struct sa_path_buffers {

@@ -111,6 +111,10 @@ def test_null_and_misaligned_pointers_rejected():
     assert lib.sparse_attn_router_pool(FAKE, ctypes.c_void_p(0x200000), B, 0, 2, 2, None) == sa.SA_ERR_INVALID_ARG
     assert lib.sparse_attn_router_scores(FAKE, FAKE, None, 0.0, B, 2, 2, 2, None) == sa.SA_ERR_INVALID_ARG
     assert lib.sparse_attn_router_scores(FAKE, FAKE, FAKE, float("inf"), B, 2, 2, 2, None) == sa.SA_ERR_INVALID_ARG
+    assert lib.sparse_attn_router_scores_f32(FAKE, FAKE, None, 0.0, B, 2, 2, 2, None) == sa.SA_ERR_INVALID_ARG
+    assert lib.sparse_attn_router_scores_f32(FAKE, FAKE, ctypes.c_void_p(0x200002), 0.0, B, 2, 2, 2,
+                                             None) == sa.SA_ERR_INVALID_ARG   # scores misaligned
+    assert lib.sparse_attn_router_scores_f32(FAKE, FAKE, FAKE, 0.0, B, 3, 2, 2, None) == sa.SA_ERR_INVALID_ARG
     assert lib.sparse_attn_coarse(FAKE, ctypes.c_void_p(0x200000), FAKE, B, None) == sa.SA_ERR_INVALID_ARG
     assert lib.sparse_attn_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, 16, B, 0.0, FAKE, None, None, 0,
                                None) == sa.SA_ERR_INVALID_ARG

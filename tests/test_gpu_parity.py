@@ -591,6 +591,29 @@ def test_router_matches_oracle(case, sub):
     assert not bad and not invalid
 
 
+@pytest.mark.parametrize("sub", [(2, 2, 2), (1, 2, 2)], ids=["2x2x2", "1x2x2"])
+def test_router_f32_matches_oracle(case, sub):
+    """The float32 router: log P_r within 5e-6 of each row's largest |log P_r|
+    of the float64 oracle's, and its lists (float32 selection) the oracle's
+    outside near ties."""
+    g, og = case["g"], case["og"]
+    qc, kc = sa.reorder(case["qd"], g, QK), sa.reorder(case["kd"], g, QK)
+    want = O.router_scores(case["ref_qc"], case["ref_kc"], og, sub)
+    lut, counts, scores = sa.router_mask(qc, kc, g, case["k_frac"], case["p"], sub, dtype=torch.float32)
+    torch.cuda.synchronize()
+    got = scores.cpu().numpy().astype(np.float64)
+    fin = np.isfinite(want)
+    assert np.array_equal(np.isfinite(got), fin)
+    scale = np.abs(np.where(fin, want, 0.0)).max(axis=-1, keepdims=True)
+    rel = np.where(fin, np.abs(got - want), 0.0) / np.maximum(scale, 1e-300)
+    ref = _ref_lists(want, O.ceil_k(case["k_frac"], og.nblk), case["p"])
+    bad, near, invalid = compare_lists(lut.cpu().numpy(), counts.cpu().numpy(), ref, case["p"])
+    say(f"  router f32 {sub}: max error {rel.max():.2e} of the row's largest |log P_r|; {len(bad)} mismatched "
+        f"rows, {near} near ties ({len(invalid)} invalid)")
+    assert rel.max() <= 5e-6
+    assert not bad and not invalid
+
+
 def test_transpose_lut_exact(case):
     g, og, ref = case["g"], case["og"], case["ref_mask"]
     lut_t, counts_t = sa.transpose_lut(torch.from_numpy(ref.lut).to(DEV), torch.from_numpy(ref.counts).to(DEV), g)

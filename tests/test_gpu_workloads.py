@@ -137,9 +137,11 @@ def test_workload(name, wid, k_frac, p, budgets, heads, all_rows):
         f"LSE max {worst[2]:.2e} mean {worst[3]:.2e}")
 
 
-def test_router_full_size():
+@pytest.mark.parametrize("dtype", ["f64", "f32"])
+def test_router_full_size(dtype):
     """Fine-grained router (2x2x2 sub-cubes, G = 8) at the 720p shape on two
-    heads (a uniform and a skewed one): scores and kept lists against the oracle."""
+    heads (a uniform and a skewed one): scores and kept lists against the
+    oracle, in float64 and in float32."""
     wl = synth.WORKLOADS[2]
     heads = [0, 1]
     say(f"[router 720p] heads {heads} grid={wl.grid}")
@@ -147,12 +149,19 @@ def test_router_full_size():
     g = sa.make_geom(1, len(heads), wl.frames, wl.height, wl.width, wl.head_dim)
     og = ogeom_of(wl)
     qc, kc = sa.reorder(q.to(DEV), g, sa.SA_LAYOUT_QK), sa.reorder(k.to(DEV), g, sa.SA_LAYOUT_QK)
-    lut, counts, scores = sa.router_mask(qc, kc, g, 0.03, 0.073)
+    lut, counts, scores = sa.router_mask(qc, kc, g, 0.03, 0.073,
+                                         dtype=torch.float32 if dtype == "f32" else torch.float64)
     torch.cuda.synchronize()
-    say("  gpu router done")
+    say(f"  gpu router ({dtype}) done")
     ref_qc, ref_kc = O.reorder(to64(q), og), O.reorder(to64(k), og)
     want = np.stack([O.router_scores(ref_qc[0, h], ref_kc[0, h], og) for h in range(len(heads))])[None]
-    np.testing.assert_allclose(scores.cpu().numpy(), want, rtol=1e-10, atol=1e-11)
+    got = scores.cpu().numpy().astype(np.float64)
+    if dtype == "f32":
+        rel = np.abs(got - want) / np.abs(want).max(axis=-1, keepdims=True)
+        say(f"  router f32: max error {rel.max():.2e} of the row's largest |log P_r|")
+        assert rel.max() <= 5e-6
+    else:
+        np.testing.assert_allclose(got, want, rtol=1e-10, atol=1e-11)
     from test_gpu_parity import _ref_lists
     ref = _ref_lists(want, O.ceil_k(0.03, og.nblk), 0.073)
     bad, near, invalid = compare_lists(lut.cpu().numpy(), counts.cpu().numpy(), ref, 0.073)
