@@ -38,6 +38,7 @@ EXPORTED = (
     "sparse_attn_mask_workspace_bytes", "sparse_attn_fwd_tokens",
     "sparse_attn_build_mask", "sparse_attn_fwd_workspace_bytes", "sparse_attn_fwd",
     "sparse_attn_coarse", "sparse_attn_router_pool", "sparse_attn_router_scores", "sparse_attn_router_scores_f32",
+    "sparse_attn_router_workspace_bytes",
     "sparse_attn_bwd_delta", "sparse_attn_transpose_workspace_bytes", "sparse_attn_transpose_lut",
     "sparse_attn_bwd", "sparse_attn_pooled_mass", "sparse_attn_mask_error", "sparse_attn_mask_error_terms",
     "sparse_attn_attention", "sparse_attn_mask_path",
@@ -110,8 +111,9 @@ _SIGS = {
     "sparse_attn_fwd_tokens": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _GP, _f32, _vp, _vp, _vp, _sz, _vp]),
     "sparse_attn_coarse": (_i32, [_vp, _vp, _vp, _GP, _vp]),
     "sparse_attn_router_pool": (_i32, [_vp, _vp, _GP, _i32, _i32, _i32, _vp]),
-    "sparse_attn_router_scores": (_i32, [_vp, _vp, _vp, _f64, _GP, _i32, _i32, _i32, _vp]),
-    "sparse_attn_router_scores_f32": (_i32, [_vp, _vp, _vp, _f64, _GP, _i32, _i32, _i32, _vp]),
+    "sparse_attn_router_scores": (_i32, [_vp, _vp, _vp, _f64, _GP, _i32, _i32, _i32, _vp, _sz, _vp]),
+    "sparse_attn_router_scores_f32": (_i32, [_vp, _vp, _vp, _f64, _GP, _i32, _i32, _i32, _vp, _sz, _vp]),
+    "sparse_attn_router_workspace_bytes": (_sz, [_GP, _i32, _i32, _i32, _i32]),
     "sparse_attn_bwd_delta": (_i32, [_vp, _vp, _vp, _GP, _vp]),
     "sparse_attn_transpose_workspace_bytes": (_sz, [_GP]),
     "sparse_attn_transpose_lut": (_i32, [_vp, _vp, _i32, _vp, _vp, _i32, _GP, _vp, _sz, _vp]),
@@ -320,16 +322,27 @@ def sparse_attn_router_pool(xc, xr, g: Geom, sub=(2, 2, 2), stream=None) -> None
                                          _stream(stream, xc)))
 
 
-def sparse_attn_router_scores(qr, kr, scores, scale: float, g: Geom, sub=(2, 2, 2), stream=None) -> None:
+def sparse_attn_router_workspace_bytes(g: Geom, sub=(2, 2, 2), score_bytes: int = 8) -> int:
+    return int(lib().sparse_attn_router_workspace_bytes(ctypes.byref(g), int(sub[0]), int(sub[1]), int(sub[2]),
+                                                        int(score_bytes)))
+
+
+def sparse_attn_router_scores(qr, kr, scores, scale: float, g: Geom, sub=(2, 2, 2), workspace=None,
+                              stream=None) -> None:
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().sparse_attn_router_scores(_ptr(qr, torch.float64, "qr"), _ptr(kr, torch.float64, "kr"),
                                            _ptr(scores, torch.float64, "scores"), float(scale), ctypes.byref(g),
-                                           int(sub[0]), int(sub[1]), int(sub[2]), _stream(stream, qr)))
+                                           int(sub[0]), int(sub[1]), int(sub[2]),
+                                           _ptr(workspace, None, "workspace"), ws_bytes, _stream(stream, qr)))
 
 
-def sparse_attn_router_scores_f32(qr, kr, scores, scale: float, g: Geom, sub=(2, 2, 2), stream=None) -> None:
+def sparse_attn_router_scores_f32(qr, kr, scores, scale: float, g: Geom, sub=(2, 2, 2), workspace=None,
+                                  stream=None) -> None:
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().sparse_attn_router_scores_f32(_ptr(qr, torch.float64, "qr"), _ptr(kr, torch.float64, "kr"),
                                                _ptr(scores, torch.float32, "scores"), float(scale), ctypes.byref(g),
-                                               int(sub[0]), int(sub[1]), int(sub[2]), _stream(stream, qr)))
+                                               int(sub[0]), int(sub[1]), int(sub[2]),
+                                               _ptr(workspace, None, "workspace"), ws_bytes, _stream(stream, qr)))
 
 
 def sparse_attn_bwd_delta(oc, do_qk, delta, g: Geom, stream=None) -> None:
@@ -596,9 +609,11 @@ def coarse(scores, vbar, g: Geom, stream=None) -> torch.Tensor:
 
 
 def router_mask(qc, kc, g: Geom, k_frac: float, p: float, sub=(2, 2, 2), row_budget=None, cap=None,
-                stream=None, dtype=torch.float64):
+                stream=None, dtype=torch.float64, one_pass=True):
     """Hybrid selection on the fine-grained router's block scores, computed in
-    `dtype` (torch.float64 or torch.float32).  Returns (lut, counts, scores = log P_r)."""
+    `dtype` (torch.float64 or torch.float32), in one pass over the sub-cube
+    scores with a scratch workspace (one_pass) or in the two passes that need
+    none.  Returns (lut, counts, scores = log P_r)."""
     nblk, _, _ = sparse_attn_geometry(g)
     G = 64 // (sub[0] * sub[1] * sub[2])
     cap = nblk if cap is None else cap
@@ -607,13 +622,18 @@ def router_mask(qc, kc, g: Geom, k_frac: float, p: float, sub=(2, 2, 2), row_bud
     scores = _empty((g.batch, g.heads, nblk, nblk), dtype, qc)
     lut = _empty((g.batch, g.heads, nblk, cap), torch.int32, qc)
     counts = _empty((g.batch, g.heads, nblk), torch.int32, qc)
+    f32 = dtype == torch.float32
+    ws = None
+    if one_pass:
+        ws = torch.empty(sparse_attn_router_workspace_bytes(g, sub, 4 if f32 else 8), dtype=torch.uint8,
+                         device=qc.device)
     sparse_attn_router_pool(qc, qr, g, sub, stream)
     sparse_attn_router_pool(kc, kr, g, sub, stream)
-    if dtype == torch.float32:
-        sparse_attn_router_scores_f32(qr, kr, scores, 0.0, g, sub, stream)
+    if f32:
+        sparse_attn_router_scores_f32(qr, kr, scores, 0.0, g, sub, ws, stream)
         sparse_attn_select_f32(scores, g, k_frac, p, row_budget, lut, counts, cap, stream)
     else:
-        sparse_attn_router_scores(qr, kr, scores, 0.0, g, sub, stream)
+        sparse_attn_router_scores(qr, kr, scores, 0.0, g, sub, ws, stream)
         sparse_attn_select(scores, g, k_frac, p, row_budget, lut, counts, cap, stream)
     return lut, counts, scores
 

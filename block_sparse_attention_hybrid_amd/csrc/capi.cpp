@@ -265,30 +265,58 @@ int32_t sparse_attn_router_pool(const void* xc, double* xr, const sa_geom* g, in
   return hip_status(sa::launch_router_pool(xc, xr, d, rt, rh, rw, (hipStream_t)stream), "router_pool launch");
 }
 
-int32_t sparse_attn_router_scores(const double* qr, const double* kr, double* scores, double scale,
-                                  const sa_geom* g, int32_t rt, int32_t rh, int32_t rw, void* stream) {
+size_t sparse_attn_router_workspace_bytes(const sa_geom* g, int32_t rt, int32_t rh, int32_t rw,
+                                          int32_t score_bytes) {
   sa::Geom d;
+  if (make_geom(g, d) != SA_OK || check_subcube(d, rt, rh, rw) != SA_OK) return 0;
+  if (score_bytes != 4 && score_bytes != 8) return 0;
+  return sa::router_workspace_bytes(d, rt, rh, rw, (size_t)score_bytes, d.batch * d.heads);
+}
+
+namespace {
+
+// Arguments shared by the two router entry points; the workspace, when given,
+// must hold at least one (batch*head)'s share of the one-pass scratch.
+int32_t check_router(const double* qr, const double* kr, const void* scores, size_t score_bytes, double& scale,
+                     const sa_geom* g, int32_t rt, int32_t rh, int32_t rw, void* workspace,
+                     size_t workspace_bytes, sa::Geom& d) {
   SA_TRY(make_geom(g, d));
   SA_TRY(check_subcube(d, rt, rh, rw));
   SA_TRY(check_ptr(qr, 8, "qr"));
   SA_TRY(check_ptr(kr, 8, "kr"));
-  SA_TRY(check_ptr(scores, 8, "scores"));
+  SA_TRY(check_ptr(scores, score_bytes, "scores"));
   if (!std::isfinite(scale)) return fail(SA_ERR_INVALID_ARG, "scale must be finite");
   if (scale <= 0.0) scale = 1.0 / std::sqrt((double)d.d);
-  return hip_status(sa::launch_router(qr, kr, scores, scale, d, rt, rh, rw, (hipStream_t)stream), "router launch");
+  if (workspace != nullptr) {
+    SA_TRY(check_ptr(workspace, 256, "workspace"));
+    const size_t one = sa::router_workspace_bytes(d, rt, rh, rw, score_bytes, 1);
+    if (workspace_bytes < one)
+      return fail(SA_ERR_CAPACITY, "router workspace of %zu bytes holds no head (%zu needed per head)",
+                  workspace_bytes, one);
+  }
+  return SA_OK;
+}
+
+}  // namespace
+
+int32_t sparse_attn_router_scores(const double* qr, const double* kr, double* scores, double scale,
+                                  const sa_geom* g, int32_t rt, int32_t rh, int32_t rw, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  sa::Geom d;
+  SA_TRY(check_router(qr, kr, scores, 8, scale, g, rt, rh, rw, workspace, workspace_bytes, d));
+  return hip_status(sa::launch_router(qr, kr, scores, scale, d, rt, rh, rw, (hipStream_t)stream, workspace,
+                                      workspace_bytes),
+                    "router launch");
 }
 
 int32_t sparse_attn_router_scores_f32(const double* qr, const double* kr, float* scores, double scale,
-                                      const sa_geom* g, int32_t rt, int32_t rh, int32_t rw, void* stream) {
+                                      const sa_geom* g, int32_t rt, int32_t rh, int32_t rw, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
   sa::Geom d;
-  SA_TRY(make_geom(g, d));
-  SA_TRY(check_subcube(d, rt, rh, rw));
-  SA_TRY(check_ptr(qr, 8, "qr"));
-  SA_TRY(check_ptr(kr, 8, "kr"));
-  SA_TRY(check_ptr(scores, 4, "scores"));
-  if (!std::isfinite(scale)) return fail(SA_ERR_INVALID_ARG, "scale must be finite");
-  if (scale <= 0.0) scale = 1.0 / std::sqrt((double)d.d);
-  return hip_status(sa::launch_router(qr, kr, scores, scale, d, rt, rh, rw, (hipStream_t)stream), "router launch");
+  SA_TRY(check_router(qr, kr, scores, 4, scale, g, rt, rh, rw, workspace, workspace_bytes, d));
+  return hip_status(sa::launch_router(qr, kr, scores, scale, d, rt, rh, rw, (hipStream_t)stream, workspace,
+                                      workspace_bytes),
+                    "router launch");
 }
 
 int32_t sparse_attn_bwd_delta(const void* oc, const void* do_qk, float* delta, const sa_geom* g, void* stream) {

@@ -21,6 +21,7 @@
 
 #include <math.h>
 
+#include <algorithm>
 #include <type_traits>
 
 namespace sa {
@@ -275,6 +276,137 @@ void router_kernel(const double* __restrict__ qr, const double* __restrict__ kr,
   }
 }
 
+__device__ __forceinline__ float larger(float a, float b) { return a > b ? a : b; }
+__device__ __forceinline__ double larger(double a, double b) { return a > b ? a : b; }
+
+// One pass over the sub-cube scores instead of two, for callers that give the
+// router a scratch buffer.  The page's kernel recomputes every score in a
+// second pass because the row log-sum-exp is known only at the end of the
+// first; here each row's mass on each key block is kept instead, relative to
+// the row's running maximum at the time:
+//   E[row][j] = sum over the present sub-cubes b of key block j of
+//               exp(S[row][(j, b)] - m_t(row)),
+// with m_t(row) the running maximum after column tile t (the tile holding
+// j's sub-cubes).  E and m_t go to the scratch buffer; once the sweep has
+// passed every column, the log-sum-exp is known and
+//   P_hat summed over key block j = exp(m_t(row) - lse(row)) * E[row][j],
+// which the G x G aggregation then averages over the query sub-cubes.  So the
+// matrix products and the exponentials are computed once instead of twice.
+//
+// Scratch per (batch*head) of a chunk, for row tile x and column tile t:
+//   esum[((x * ntile) + t) * 64 * nb + row * nb + jb]   (nb = 64 / G blocks)
+//   emax[((x * ntile) + t) * 64 + row]
+template <typename T>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void router_onepass_kernel(const double* __restrict__ qr, const double* __restrict__ kr, T* __restrict__ scores,
+                           T* __restrict__ esum, T* __restrict__ emax, double scale, Geom g, SubCube sc,
+                           int bh0) {
+  constexpr int kStage = 2 * kTile * kLd, kScores = kTile * (kTile + 1);
+  constexpr int kCt = 16;   // column tiles per aggregation step
+  // the aggregation's rescaling factors reuse the staging area
+  constexpr int kWords = ((kStage > kScores ? kStage : kScores) * (int)sizeof(T) + 7) / 8;
+  static_assert(kWords >= kTile * kCt, "the factors fit the staging area");
+  __shared__ double smem_raw[kWords];
+  T* smem = reinterpret_cast<T*>(smem_raw);
+  T* As = smem;
+  T* Bs = smem + kTile * kLd;
+  T* S = smem;
+  double* fac = smem_raw;
+  __shared__ double lse[kTile];
+  __shared__ T mrow[kTile];
+  __shared__ unsigned char kpres[kTile];
+  const int G = sc.G, n = g.nblk, nr = n * G, d = g.d;
+  const int ntile = (nr + kTile - 1) / kTile, nb = kTile / G;
+  const int r0 = blockIdx.x * kTile;
+  const long long bh = bh0 + (long long)blockIdx.y;
+  const double* qh = qr + bh * (long long)nr * d;
+  const double* kh = kr + bh * (long long)nr * d;
+  const long long wt = (long long)blockIdx.y * ntile + blockIdx.x;   // this row tile's scratch
+  T* ew = esum + wt * ntile * (long long)(kTile * nb);
+  T* mw = emax + wt * ntile * (long long)kTile;
+  const int row = threadIdx.x >> 2, part = threadIdx.x & 3;   // 4 threads per tile row
+
+  // sweep: per column tile, the row maxima, then every (row, key block) sum
+  // relative to them; the running row sum l is rescaled when the maximum grows
+  T m = -INFINITY;
+  double l = 0.0;
+  for (int t = 0; t < ntile; ++t) {
+    const int c0 = t * kTile;
+    if (threadIdx.x < kTile) {
+      const int c = c0 + threadIdx.x;
+      kpres[threadIdx.x] = c < nr && subcube_present(g, sc, c / G, c % G);
+    }
+    score_tile(qh, kh, nr, d, r0, c0, scale, As, Bs, S);
+    T tm = -INFINITY;
+    for (int e = 0; e < 16; ++e) {
+      const int c = part * 16 + e;
+      if (kpres[c]) tm = larger(tm, S[row * (kTile + 1) + c]);
+    }
+    tm = larger(tm, __shfl_xor(tm, 1, kWave));
+    tm = larger(tm, __shfl_xor(tm, 2, kWave));
+    if (tm > m) {
+      if (m > -INFINITY) l *= exp((double)m - (double)tm);
+      m = tm;
+    }
+    if (part == 0) mrow[row] = m;
+    __syncthreads();
+    for (int u = threadIdx.x; u < kTile * nb; u += kThreads) {
+      const int rr = u / nb, bj = u - rr * nb;
+      const T mr = mrow[rr];
+      T e = 0;
+      if (mr > -INFINITY) {
+        for (int b = 0; b < G; ++b) {
+          const int cc = bj * G + b;
+          if (kpres[cc]) e += exp_of(S[rr * (kTile + 1) + cc] - mr);
+        }
+      }
+      ew[(long long)t * (kTile * nb) + u] = e;
+      S[rr * (kTile + 1) + bj * G] = e;
+    }
+    if (threadIdx.x < kTile) mw[(long long)t * kTile + threadIdx.x] = mrow[threadIdx.x];
+    __syncthreads();
+    double s = 0.0;
+    for (int bj = part; bj < nb; bj += 4) s += (double)S[row * (kTile + 1) + bj * G];
+    s += __shfl_xor(s, 1, kWave);
+    s += __shfl_xor(s, 2, kWave);
+    l += s;
+    __syncthreads();
+  }
+  if (part == 0) lse[row] = (double)m + log(l);
+  __syncthreads();
+
+  // aggregation: P_r[i][j] = mean over the present query sub-cubes a of
+  // exp(m_t(a) - lse(a)) * E[a][j]
+  const int i0 = r0 / G;
+  for (int t0 = 0; t0 < ntile; t0 += kCt) {
+    const int ct = min(kCt, ntile - t0);
+    for (int u = threadIdx.x; u < kTile * ct; u += kThreads) {
+      const int rr = u / ct, tt = u - rr * ct;
+      const T mr = mw[(long long)(t0 + tt) * kTile + rr];
+      fac[rr * kCt + tt] = mr > -INFINITY ? exp((double)mr - lse[rr]) : 0.0;
+    }
+    __syncthreads();
+    const int j0 = t0 * nb, nj = min(n, (t0 + ct) * nb) - j0;
+    for (int u = threadIdx.x; u < nb * nj; u += kThreads) {
+      const int bi = u / nj, jj = u - bi * nj;
+      const int i = i0 + bi;
+      if (i >= n) continue;
+      const int tt = jj / nb, bj = jj - tt * nb;
+      const T* et = ew + (long long)(t0 + tt) * (kTile * nb) + bj;
+      double acc = 0.0;
+      int na = 0;
+      for (int a = 0; a < G; ++a) {
+        if (!subcube_present(g, sc, i, a)) continue;
+        ++na;
+        const int rr = bi * G + a;
+        acc += fac[rr * kCt + tt] * (double)et[rr * nb];
+      }
+      scores[(bh * n + i) * (long long)n + j0 + jj] = (T)log(acc / (double)na);
+    }
+    __syncthreads();
+  }
+}
+
 SubCube make_subcube(const Geom& g, int rt, int rh, int rw) {
   SubCube s;
   s.rt = rt;
@@ -295,6 +427,8 @@ hipError_t launch_router_pool(const void* xc, double* xr, const Geom& g, int rt,
   return hipGetLastError();
 }
 
+namespace {
+
 template <typename T>
 hipError_t router_t(const double* qr, const double* kr, T* scores, double scale, const Geom& g, int rt, int rh,
                     int rw, hipStream_t s) {
@@ -305,14 +439,65 @@ hipError_t router_t(const double* qr, const double* kr, T* scores, double scale,
   return hipGetLastError();
 }
 
+// Scratch of the one-pass kernel for one (batch*head), in elements of T:
+// the sums E and, after them, the running maxima.
+size_t onepass_head_elems(const Geom& g, const SubCube& sc, size_t& emax_off) {
+  const size_t ntile = ((size_t)g.nblk * sc.G + kTile - 1) / kTile;
+  emax_off = ntile * ntile * kTile * (size_t)(kTile / sc.G);
+  return emax_off + ntile * ntile * kTile;
+}
+
+template <typename T>
+hipError_t router_onepass_t(const double* qr, const double* kr, T* scores, double scale, const Geom& g, int rt,
+                            int rh, int rw, void* workspace, size_t ws_bytes, hipStream_t s) {
+  const SubCube sc = make_subcube(g, rt, rh, rw);
+  size_t emax_off;
+  const size_t per_head = onepass_head_elems(g, sc, emax_off) * sizeof(T) + 256;
+  const int bh_total = g.batch * g.heads;
+  const int chunk = (int)std::min<size_t>((size_t)bh_total, ws_bytes / per_head);
+  if (chunk < 1) return hipErrorInvalidValue;   // the caller checks the size first
+  const long long nr = (long long)g.nblk * sc.G;
+  const unsigned ntile = (unsigned)((nr + kTile - 1) / kTile);
+  for (int bh0 = 0; bh0 < bh_total; bh0 += chunk) {
+    const int hc = std::min(chunk, bh_total - bh0);
+    T* esum = static_cast<T*>(workspace);
+    // the maxima start on a 256-byte boundary after the chunk's sums
+    const size_t esum_bytes = (size_t)hc * emax_off * sizeof(T);
+    T* emax = reinterpret_cast<T*>(static_cast<char*>(workspace) + ((esum_bytes + 255) & ~(size_t)255));
+    router_onepass_kernel<T><<<dim3(ntile, hc), kThreads, 0, s>>>(qr, kr, scores, esum, emax, scale, g, sc, bh0);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+size_t router_workspace_bytes(const Geom& g, int rt, int rh, int rw, size_t elem, int heads) {
+  const SubCube sc = make_subcube(g, rt, rh, rw);
+  size_t emax_off;
+  return (size_t)heads * (onepass_head_elems(g, sc, emax_off) * elem + 256);
+}
+
+namespace {
+
+template <typename T>
+hipError_t router_any(const double* qr, const double* kr, T* scores, double scale, const Geom& g, int rt, int rh,
+                      int rw, void* workspace, size_t ws_bytes, hipStream_t s) {
+  if (workspace == nullptr) return router_t(qr, kr, scores, scale, g, rt, rh, rw, s);
+  return router_onepass_t(qr, kr, scores, scale, g, rt, rh, rw, workspace, ws_bytes, s);
+}
+
+}  // namespace
+
 hipError_t launch_router(const double* qr, const double* kr, double* scores, double scale, const Geom& g,
-                         int rt, int rh, int rw, hipStream_t s) {
-  return router_t(qr, kr, scores, scale, g, rt, rh, rw, s);
+                         int rt, int rh, int rw, hipStream_t s, void* workspace, size_t ws_bytes) {
+  return router_any(qr, kr, scores, scale, g, rt, rh, rw, workspace, ws_bytes, s);
 }
 
 hipError_t launch_router(const double* qr, const double* kr, float* scores, double scale, const Geom& g,
-                         int rt, int rh, int rw, hipStream_t s) {
-  return router_t(qr, kr, scores, scale, g, rt, rh, rw, s);
+                         int rt, int rh, int rw, hipStream_t s, void* workspace, size_t ws_bytes) {
+  return router_any(qr, kr, scores, scale, g, rt, rh, rw, workspace, ws_bytes, s);
 }
 
 }  // namespace sa

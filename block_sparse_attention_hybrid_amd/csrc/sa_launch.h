@@ -52,11 +52,16 @@ hipError_t launch_fwd_tokens(const void* qc, const void* kc, const void* vc, con
                              float* lse, hipStream_t s, void* workspace = nullptr, int max_count = -1);
 size_t fwd_workspace_bytes(const Geom& g);
 hipError_t launch_router_pool(const void* xc, double* xr, const Geom& g, int rt, int rh, int rw, hipStream_t s);
+// workspace NULL: two passes over the sub-cube scores; otherwise one pass with
+// its per-block sums in the workspace (>= router_workspace_bytes for one head;
+// the heads then run in chunks of what it holds)
 hipError_t launch_router(const double* qr, const double* kr, double* scores, double scale, const Geom& g,
-                         int rt, int rh, int rw, hipStream_t s);
+                         int rt, int rh, int rw, hipStream_t s, void* workspace = nullptr, size_t ws_bytes = 0);
 // the same in float32 (log-sum-exp in float64), log P_r written as float32
 hipError_t launch_router(const double* qr, const double* kr, float* scores, double scale, const Geom& g,
-                         int rt, int rh, int rw, hipStream_t s);
+                         int rt, int rh, int rw, hipStream_t s, void* workspace = nullptr, size_t ws_bytes = 0);
+// bytes of one-pass scratch for `heads` (batch*head) rows of scores of elem bytes
+size_t router_workspace_bytes(const Geom& g, int rt, int rh, int rw, size_t elem, int heads);
 // Operands of the backward pass (device pointers, see sparse_attn_bwd).
 struct BwdArgs {
   const void *q, *k, *v_qk, *k_v, *do_qk;

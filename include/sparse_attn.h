@@ -225,29 +225,50 @@ int32_t sparse_attn_coarse(const double* scores, const double* vbar, double* oc,
  *   xr [batch, heads, nblk*G, head_dim] float64, row blk*G + a       (output)
  *      (sub-cube a row-major over the cube's sub-cube grid; an all-pad
  *      sub-cube gets zeros)
- * sparse_attn_router_scores: log P_r, float64, computed twice over the
- * sub-cube scores (log-sum-exp, then softmax and aggregation) without
- * materialising the router softmax.
+ * sparse_attn_router_scores: log P_r, float64, without materialising the
+ * router softmax.
  *   qr, kr [batch, heads, nblk*G, head_dim] float64                  (inputs)
  *   scores [batch, heads, nblk, nblk] float64 = log P_r               (output)
  *   scale <= 0 selects 1/sqrt(head_dim).
+ *   workspace NULL: the page's two passes over the sub-cube scores (the row
+ *     log-sum-exp first, then the softmax and the aggregation), no scratch.
+ *   workspace non-NULL (device, 256-byte aligned, workspace_bytes of it):
+ *     one pass.  Each row's mass on each key block is kept in the workspace,
+ *     relative to the row's running maximum, and rescaled by the row's
+ *     log-sum-exp once the sweep has ended, so the scores and their
+ *     exponentials are computed once.  Same values up to rounding.
+ *     sparse_attn_router_workspace_bytes gives the size for every head at
+ *     once; a smaller workspace runs the heads in chunks of what it holds,
+ *     and one smaller than a single head's share is SA_ERR_CAPACITY.  Calls
+ *     that overlap must not share a workspace.
  * The scores go to sparse_attn_select unchanged: their row softmax is P_r. */
 int32_t sparse_attn_router_pool(const void* xc, double* xr, const sa_geom* g,
                                 int32_t rt, int32_t rh, int32_t rw, void* stream);
 int32_t sparse_attn_router_scores(const double* qr, const double* kr,
                                   double* scores, double scale,
                                   const sa_geom* g, int32_t rt, int32_t rh,
-                                  int32_t rw, void* stream);
+                                  int32_t rw, void* workspace,
+                                  size_t workspace_bytes, void* stream);
 
 /* sparse_attn_router_scores on the float32 matrix cores: the sub-cube means
  * rounded to float32, the sub-cube scores and their exponentials in float32,
  * the row log-sum-exp accumulated in float64, and log P_r written as float32
  * for sparse_attn_select_f32.  Checked against the float64 lists of the
- * oracle outside near ties; about twice as fast.
+ * oracle outside near ties.  Workspace as above (its size for score_bytes 4).
  *   scores [batch, heads, nblk, nblk] float32 = log P_r               (output) */
 int32_t sparse_attn_router_scores_f32(const double* qr, const double* kr,
                                       float* scores, double scale, const sa_geom* g,
-                                      int32_t rt, int32_t rh, int32_t rw, void* stream);
+                                      int32_t rt, int32_t rh, int32_t rw,
+                                      void* workspace, size_t workspace_bytes,
+                                      void* stream);
+
+/* Bytes of workspace for the one-pass router over every (batch, head):
+ * score_bytes 8 for sparse_attn_router_scores, 4 for the float32 form (0 for
+ * an invalid geometry, sub-cube or score_bytes).  At 720p with 2x2x2
+ * sub-cubes that is about 150 MB (float64) or 75 MB (float32) per head. */
+size_t sparse_attn_router_workspace_bytes(const sa_geom* g, int32_t rt,
+                                          int32_t rh, int32_t rw,
+                                          int32_t score_bytes);
 
 /* ---- the whole path in one call ------------------------------------------
  * Buffers of sparse_attn_attention (device pointers the caller allocated). */

@@ -109,12 +109,16 @@ def test_null_and_misaligned_pointers_rejected():
     assert lib.sparse_attn_router_pool(FAKE, ctypes.c_void_p(0x200000), B, 3, 2, 2, None) == sa.SA_ERR_INVALID_ARG
     assert "tile" in sa.sparse_attn_last_error()
     assert lib.sparse_attn_router_pool(FAKE, ctypes.c_void_p(0x200000), B, 0, 2, 2, None) == sa.SA_ERR_INVALID_ARG
-    assert lib.sparse_attn_router_scores(FAKE, FAKE, None, 0.0, B, 2, 2, 2, None) == sa.SA_ERR_INVALID_ARG
-    assert lib.sparse_attn_router_scores(FAKE, FAKE, FAKE, float("inf"), B, 2, 2, 2, None) == sa.SA_ERR_INVALID_ARG
-    assert lib.sparse_attn_router_scores_f32(FAKE, FAKE, None, 0.0, B, 2, 2, 2, None) == sa.SA_ERR_INVALID_ARG
-    assert lib.sparse_attn_router_scores_f32(FAKE, FAKE, ctypes.c_void_p(0x200002), 0.0, B, 2, 2, 2,
+    assert lib.sparse_attn_router_scores(FAKE, FAKE, None, 0.0, B, 2, 2, 2, None, 0,
+                                         None) == sa.SA_ERR_INVALID_ARG
+    assert lib.sparse_attn_router_scores(FAKE, FAKE, FAKE, float("inf"), B, 2, 2, 2, None, 0,
+                                         None) == sa.SA_ERR_INVALID_ARG
+    assert lib.sparse_attn_router_scores_f32(FAKE, FAKE, None, 0.0, B, 2, 2, 2, None, 0,
+                                             None) == sa.SA_ERR_INVALID_ARG
+    assert lib.sparse_attn_router_scores_f32(FAKE, FAKE, ctypes.c_void_p(0x200002), 0.0, B, 2, 2, 2, None, 0,
                                              None) == sa.SA_ERR_INVALID_ARG   # scores misaligned
-    assert lib.sparse_attn_router_scores_f32(FAKE, FAKE, FAKE, 0.0, B, 3, 2, 2, None) == sa.SA_ERR_INVALID_ARG
+    assert lib.sparse_attn_router_scores_f32(FAKE, FAKE, FAKE, 0.0, B, 3, 2, 2, None, 0,
+                                             None) == sa.SA_ERR_INVALID_ARG
     assert lib.sparse_attn_coarse(FAKE, ctypes.c_void_p(0x200000), FAKE, B, None) == sa.SA_ERR_INVALID_ARG
     assert lib.sparse_attn_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, 16, B, 0.0, FAKE, None, None, 0,
                                None) == sa.SA_ERR_INVALID_ARG
@@ -327,3 +331,30 @@ def test_noalloc_mask_rejects_before_any_launch():
                                               ctypes.c_double(0.5), None, FAKE, FAKE, 8, None) == sa.SA_ERR_CAPACITY
     assert lib.sparse_attn_build_mask_noalloc(FAKE_MISALIGNED, FAKE, ctypes.byref(g2), 64, ctypes.c_double(0.03),
                                               ctypes.c_double(0.5), None, FAKE, FAKE, 16, None) == sa.SA_ERR_INVALID_ARG
+
+
+def test_router_workspace_rules():
+    """The one-pass router's scratch: one value per (router row, key block)
+    and one running maximum per (router row, column tile of 64 sub-cubes),
+    plus a 256-byte alignment pad per head; a workspace that holds no head is
+    a capacity error and a misaligned one an argument error, before any
+    launch."""
+    lib = sa.lib()
+    for dims, n in (((21, 45, 80), 1440), ((4, 16, 16), 16)):
+        g = geom(frames=dims[0], height=dims[1], width=dims[2])
+        for sub, G in (((2, 2, 2), 8), ((1, 2, 2), 16), ((4, 4, 4), 1)):
+            nt = -(-n * G // 64)
+            per_head_elems = nt * nt * 64 * (64 // G) + nt * nt * 64
+            for elem in (4, 8):
+                want = g.batch * g.heads * (per_head_elems * elem + 256)
+                assert sa.sparse_attn_router_workspace_bytes(g, sub, elem) == want
+    g720 = geom(frames=21, height=45, width=80)
+    assert sa.sparse_attn_router_workspace_bytes(g720, (2, 2, 2), 4) == 2 * 74_649_856   # 75 MB a head
+    assert sa.sparse_attn_router_workspace_bytes(g720, (2, 2, 2), 2) == 0
+    assert sa.sparse_attn_router_workspace_bytes(g720, (3, 2, 2), 4) == 0
+    one = sa.sparse_attn_router_workspace_bytes(g720, (2, 2, 2), 8) // 2
+    assert lib.sparse_attn_router_scores(FAKE, FAKE, FAKE, 0.0, g720, 2, 2, 2, FAKE, one - 1,
+                                         None) == sa.SA_ERR_CAPACITY
+    assert "workspace" in sa.sparse_attn_last_error()
+    assert lib.sparse_attn_router_scores_f32(FAKE, FAKE, FAKE, 0.0, g720, 2, 2, 2, FAKE_MISALIGNED, one,
+                                             None) == sa.SA_ERR_INVALID_ARG

@@ -565,8 +565,9 @@ def _ref_budget_lists(scores, budget):
                         kbar=None)
 
 
+@pytest.mark.parametrize("one_pass", [True, False], ids=["one-pass", "two-pass"])
 @pytest.mark.parametrize("sub", [(2, 2, 2), (1, 2, 2), (4, 4, 4)])
-def test_router_matches_oracle(case, sub):
+def test_router_matches_oracle(case, sub, one_pass):
     g, og = case["g"], case["og"]
     nblk = og.nblk
     G = 64 // (sub[0] * sub[1] * sub[2])
@@ -581,7 +582,7 @@ def test_router_matches_oracle(case, sub):
     np.testing.assert_array_equal(qr.cpu().numpy(), want_qr)
     np.testing.assert_array_equal(kr.cpu().numpy(), want_kr)
     want = O.router_scores(case["ref_qc"], case["ref_kc"], og, sub)
-    lut, counts, scores = sa.router_mask(qc, kc, g, case["k_frac"], case["p"], sub)
+    lut, counts, scores = sa.router_mask(qc, kc, g, case["k_frac"], case["p"], sub, one_pass=one_pass)
     torch.cuda.synchronize()
     got = scores.cpu().numpy()
     np.testing.assert_allclose(got, want, rtol=1e-11, atol=1e-12)
@@ -591,15 +592,17 @@ def test_router_matches_oracle(case, sub):
     assert not bad and not invalid
 
 
+@pytest.mark.parametrize("one_pass", [True, False], ids=["one-pass", "two-pass"])
 @pytest.mark.parametrize("sub", [(2, 2, 2), (1, 2, 2)], ids=["2x2x2", "1x2x2"])
-def test_router_f32_matches_oracle(case, sub):
+def test_router_f32_matches_oracle(case, sub, one_pass):
     """The float32 router: log P_r within 5e-6 of each row's largest |log P_r|
     of the float64 oracle's, and its lists (float32 selection) the oracle's
     outside near ties."""
     g, og = case["g"], case["og"]
     qc, kc = sa.reorder(case["qd"], g, QK), sa.reorder(case["kd"], g, QK)
     want = O.router_scores(case["ref_qc"], case["ref_kc"], og, sub)
-    lut, counts, scores = sa.router_mask(qc, kc, g, case["k_frac"], case["p"], sub, dtype=torch.float32)
+    lut, counts, scores = sa.router_mask(qc, kc, g, case["k_frac"], case["p"], sub, dtype=torch.float32,
+                                         one_pass=one_pass)
     torch.cuda.synchronize()
     got = scores.cpu().numpy().astype(np.float64)
     fin = np.isfinite(want)
@@ -612,6 +615,36 @@ def test_router_f32_matches_oracle(case, sub):
         f"rows, {near} near ties ({len(invalid)} invalid)")
     assert rel.max() <= 5e-6
     assert not bad and not invalid
+
+
+@pytest.mark.parametrize("dtype", [torch.float64, torch.float32], ids=["f64", "f32"])
+def test_router_workspace_chunks(case, dtype):
+    """A one-pass workspace that holds a single head's scratch runs the heads
+    one launch at a time; the scores are the bytes of the all-heads launch,
+    and a second call on the same workspace (old contents left in it) gives
+    them again."""
+    g = case["g"]
+    sub, G = (2, 2, 2), 8
+    nblk = case["og"].nblk
+    qc, kc = sa.reorder(case["qd"], g, QK), sa.reorder(case["kd"], g, QK)
+    qr = torch.empty(g.batch, g.heads, nblk * G, g.head_dim, dtype=torch.float64, device=DEV)
+    kr = torch.empty_like(qr)
+    sa.sparse_attn_router_pool(qc, qr, g, sub)
+    sa.sparse_attn_router_pool(kc, kr, g, sub)
+    f32 = dtype == torch.float32
+    call = sa.sparse_attn_router_scores_f32 if f32 else sa.sparse_attn_router_scores
+    total = sa.sparse_attn_router_workspace_bytes(g, sub, 4 if f32 else 8)
+    bh = g.batch * g.heads
+    ws_all = torch.empty(total, dtype=torch.uint8, device=DEV)
+    ws_one = torch.full((total // bh,), 255, dtype=torch.uint8, device=DEV)
+    full = torch.empty(g.batch, g.heads, nblk, nblk, dtype=dtype, device=DEV)
+    call(qr, kr, full, 0.0, g, sub, ws_all)
+    for _ in range(2):
+        part = torch.full_like(full, float("nan"))
+        call(qr, kr, part, 0.0, g, sub, ws_one)
+        torch.cuda.synchronize()
+        assert torch.equal(part, full)
+    say(f"  router workspace chunks ({'f32' if f32 else 'f64'}): {bh} heads one at a time, same bytes")
 
 
 def test_transpose_lut_exact(case):

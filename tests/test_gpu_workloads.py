@@ -4,6 +4,7 @@ every head's kept-block lists and the attention of sampled query blocks (every
 query block of one head, and the longest-list tenth of the others, on the
 sparsest workloads), with its own lists fed to the GPU attention; properties
 that hold at any size are checked on every row."""
+import functools
 import math
 
 import numpy as np
@@ -137,24 +138,36 @@ def test_workload(name, wid, k_frac, p, budgets, heads, all_rows):
         f"LSE max {worst[2]:.2e} mean {worst[3]:.2e}")
 
 
-@pytest.mark.parametrize("dtype", ["f64", "f32"])
-def test_router_full_size(dtype):
-    """Fine-grained router (2x2x2 sub-cubes, G = 8) at the 720p shape on two
-    heads (a uniform and a skewed one): scores and kept lists against the
-    oracle, in float64 and in float32."""
+@functools.lru_cache(maxsize=1)
+def _router_720p_oracle():
+    """The float64 oracle's router scores of two 720p heads (a uniform and a
+    skewed one), 2x2x2 sub-cubes."""
     wl = synth.WORKLOADS[2]
     heads = [0, 1]
-    say(f"[router 720p] heads {heads} grid={wl.grid}")
     q, k, _ = synth.make_qkv(wl, 0, heads=heads)
-    g = sa.make_geom(1, len(heads), wl.frames, wl.height, wl.width, wl.head_dim)
+    og = ogeom_of(wl)
+    ref_qc, ref_kc = O.reorder(to64(q), og), O.reorder(to64(k), og)
+    want = np.stack([O.router_scores(ref_qc[0, h], ref_kc[0, h], og) for h in range(len(heads))])[None]
+    return q, k, want
+
+
+@pytest.mark.parametrize("one_pass", [True, False], ids=["one-pass", "two-pass"])
+@pytest.mark.parametrize("dtype", ["f64", "f32"])
+def test_router_full_size(dtype, one_pass):
+    """Fine-grained router (2x2x2 sub-cubes, G = 8) at the 720p shape on two
+    heads (a uniform and a skewed one): scores and kept lists against the
+    oracle, in float64 and in float32, in one pass and in two."""
+    wl = synth.WORKLOADS[2]
+    say(f"[router 720p] {dtype}, {'one pass' if one_pass else 'two passes'}, grid={wl.grid}")
+    q, k, want = _router_720p_oracle()
+    g = sa.make_geom(1, 2, wl.frames, wl.height, wl.width, wl.head_dim)
     og = ogeom_of(wl)
     qc, kc = sa.reorder(q.to(DEV), g, sa.SA_LAYOUT_QK), sa.reorder(k.to(DEV), g, sa.SA_LAYOUT_QK)
     lut, counts, scores = sa.router_mask(qc, kc, g, 0.03, 0.073,
-                                         dtype=torch.float32 if dtype == "f32" else torch.float64)
+                                         dtype=torch.float32 if dtype == "f32" else torch.float64,
+                                         one_pass=one_pass)
     torch.cuda.synchronize()
     say(f"  gpu router ({dtype}) done")
-    ref_qc, ref_kc = O.reorder(to64(q), og), O.reorder(to64(k), og)
-    want = np.stack([O.router_scores(ref_qc[0, h], ref_kc[0, h], og) for h in range(len(heads))])[None]
     got = scores.cpu().numpy().astype(np.float64)
     if dtype == "f32":
         rel = np.abs(got - want) / np.abs(want).max(axis=-1, keepdims=True)
