@@ -166,6 +166,95 @@ __device__ __forceinline__ void score_tile(const double* __restrict__ qh, const 
   __syncthreads();
 }
 
+// The float32 tile engine of the one-pass kernel.
+//
+// K in float32, laid out by a pre-pass so that one wavefront load moves 1 KB
+// of consecutive bytes: per (batch*head) and column tile t, D/4 chunks c of
+// four k values, each holding the tile's 64 columns in turn,
+//   kt[((t * (D / 4) + c) * 64 + col) * 4 + e] = K[64 t + col][4 c + e]
+// (zeros past the last sub-cube).  The kernel loads the next tile's share of
+// kt into registers while the current tile is multiplied and its softmax
+// taken, and writes it into LDS (pitch D + 4 floats) at the next tile's start.
+//
+// Q's operands stay in registers for the whole sweep.  Wave w computes router
+// rows 16w .. 16w + 15 of the tile against its 64 columns with 16x16x4
+// products; product s = 4j + m of lane l takes k = 16j + 4(l >> 4) + m, so the
+// four products of one j read their K operands with one 16-byte LDS read:
+//   aq[4j + m] = Q[16w + (l & 15)][16j + 4(l >> 4) + m].
+__global__ __launch_bounds__(kThreads) void router_k32_kernel(const double* __restrict__ kr, float* __restrict__ kt,
+                                                              int nr, int d, int ntile, int bh0) {
+  const long long per_head = (long long)ntile * kTile * d;   // floats
+  const long long u = (long long)blockIdx.x * kThreads + threadIdx.x;   // one float4 each
+  if (u * 4 >= per_head) return;
+  const int bhc = blockIdx.y;
+  const int col = (int)(u & 63), c = (int)((u >> 6) % (d / 4)), t = (int)((u >> 6) / (d / 4));
+  const int j = t * kTile + col;
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (j < nr) {
+    const double* src = kr + ((long long)(bh0 + bhc) * nr + j) * d + 4 * c;
+    v = make_float4((float)src[0], (float)src[1], (float)src[2], (float)src[3]);
+  }
+  reinterpret_cast<float4*>(kt + (long long)bhc * per_head)[u] = v;
+}
+
+template <int D>
+__device__ __forceinline__ void load_q_operands(const double* __restrict__ qh, int nr, int r0, float (&aq)[D / 4]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int gi = r0 + wave * 16 + (lane & 15);
+  const double* qrow = qh + (long long)(gi < nr ? gi : nr - 1) * D + 4 * (lane >> 4);
+#pragma unroll
+  for (int j = 0; j < D / 16; ++j)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) aq[4 * j + m] = gi < nr ? (float)qrow[16 * j + m] : 0.f;
+}
+
+// This thread's share of column tile t of kt: chunks c = 4i + wave, column
+// lane, for i < D / 16.
+template <int D>
+__device__ __forceinline__ void load_k_share(const float* __restrict__ kth, int t, f32x4 (&kv)[D / 16]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const f32x4* src = reinterpret_cast<const f32x4*>(kth + (long long)t * kTile * D);
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) kv[i] = src[(4 * i + wave) * 64 + lane];
+}
+
+template <int D>
+__device__ __forceinline__ void store_k_share(const f32x4 (&kv)[D / 16], float* Ks) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i)
+    *reinterpret_cast<f32x4*>(Ks + lane * (D + 4) + 4 * (4 * i + wave)) = kv[i];
+}
+
+// Scores of the tile from the staged K (LDS, pitch D + 4) into S (pitch
+// kTile + 1), scaled.  Ends with a barrier; the caller's barrier before it
+// ordered the K writes.
+template <int D>
+__device__ __forceinline__ void score_tile_f32(const float (&aq)[D / 4], const float* Ks, float scale, float* S) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  f32x4 acc[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4{0, 0, 0, 0};
+#pragma unroll
+  for (int j = 0; j < D / 16; ++j) {
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const f32x4 b = *reinterpret_cast<const f32x4*>(Ks + (nt * 16 + (lane & 15)) * (D + 4) + 16 * j +
+                                                        4 * (lane >> 4));
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(aq[4 * j + m], b[m], acc[nt], 0, 0, 0);
+    }
+  }
+  __syncthreads();   // the staged K is dead; S takes its place
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      S[(wave * 16 + 4 * (lane >> 4) + r) * (kTile + 1) + nt * 16 + (lane & 15)] = acc[nt][r] * scale;
+  __syncthreads();
+}
+
 __device__ __forceinline__ double exp_of(double x) { return exp(x); }
 __device__ __forceinline__ float exp_of(float x) { return __expf(x); }
 
@@ -279,6 +368,29 @@ void router_kernel(const double* __restrict__ qr, const double* __restrict__ kr,
 __device__ __forceinline__ float larger(float a, float b) { return a > b ? a : b; }
 __device__ __forceinline__ double larger(double a, double b) { return a > b ? a : b; }
 
+// Sums of a thread's 16 consecutive exponentials over key blocks of GG
+// sub-cubes (GG <= 16: 16 / GG whole blocks), written to dst in order.
+template <int GG, typename T>
+__device__ __forceinline__ void fold_blocks(const T (&v)[16], T* __restrict__ dst) {
+#pragma unroll
+  for (int bj = 0; bj < 16 / GG; ++bj) {
+    T e = 0;
+#pragma unroll
+    for (int b = 0; b < GG; ++b) e += v[bj * GG + b];
+    dst[bj] = e;
+  }
+}
+
+// Bit c of word t: sub-cube 64 t + c of a head holds a real token (the same
+// for every head).  One wavefront per word.
+__global__ __launch_bounds__(kThreads) void router_present_kernel(unsigned long long* __restrict__ pmask, Geom g,
+                                                                  SubCube sc, int nr) {
+  const int c = blockIdx.x * kThreads + threadIdx.x;
+  const bool p = c < nr && subcube_present(g, sc, c / sc.G, c % sc.G);
+  const unsigned long long w = __ballot(p);
+  if ((threadIdx.x & 63) == 0 && c < ((nr + kTile - 1) / kTile) * kTile) pmask[c >> 6] = w;
+}
+
 // One pass over the sub-cube scores instead of two, for callers that give the
 // router a scratch buffer.  The page's kernel recomputes every score in a
 // second pass because the row log-sum-exp is known only at the end of the
@@ -296,26 +408,33 @@ __device__ __forceinline__ double larger(double a, double b) { return a > b ? a 
 // Scratch per (batch*head) of a chunk, for row tile x and column tile t:
 //   esum[((x * ntile) + t) * 64 * nb + row * nb + jb]   (nb = 64 / G blocks)
 //   emax[((x * ntile) + t) * 64 + row]
-template <typename T>
+template <typename T, int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void router_onepass_kernel(const double* __restrict__ qr, const double* __restrict__ kr, T* __restrict__ scores,
-                           T* __restrict__ esum, T* __restrict__ emax, double scale, Geom g, SubCube sc,
+                           T* __restrict__ esum, T* __restrict__ emax, const float* __restrict__ kt,
+                           const unsigned long long* __restrict__ pmask, double scale, Geom g, SubCube sc,
                            int bh0) {
-  constexpr int kStage = 2 * kTile * kLd, kScores = kTile * (kTile + 1);
+  // float32: the engine above (Q in registers, K from kt, a whole tile staged
+  // at once); float64, whose operands would take twice the registers: both
+  // operands staged 16 k columns at a time (score_tile)
+  constexpr bool kF32 = !std::is_same<T, double>::value;
+  constexpr int kStage = kF32 ? kTile * (D + 4) * 4 / (int)sizeof(T) : 2 * kTile * kLd;
+  constexpr int kScores = kTile * (kTile + 1);
   constexpr int kCt = 16;   // column tiles per aggregation step
   // the aggregation's rescaling factors reuse the staging area
   constexpr int kWords = ((kStage > kScores ? kStage : kScores) * (int)sizeof(T) + 7) / 8;
   static_assert(kWords >= kTile * kCt, "the factors fit the staging area");
-  __shared__ double smem_raw[kWords];
+  __shared__ __attribute__((aligned(16))) double smem_raw[kWords];   // 16-byte LDS reads of K
   T* smem = reinterpret_cast<T*>(smem_raw);
   T* As = smem;
   T* Bs = smem + kTile * kLd;
   T* S = smem;
+  float* Ks = reinterpret_cast<float*>(smem_raw);
   double* fac = smem_raw;
   __shared__ double lse[kTile];
-  __shared__ T mrow[kTile];
-  __shared__ unsigned char kpres[kTile];
-  const int G = sc.G, n = g.nblk, nr = n * G, d = g.d;
+  // (the float64 engine keeps its k loop on the run-time head size: unrolled,
+  // it spills)
+  const int G = sc.G, n = g.nblk, nr = n * G, d = kF32 ? D : g.d;
   const int ntile = (nr + kTile - 1) / kTile, nb = kTile / G;
   const int r0 = blockIdx.x * kTile;
   const long long bh = bh0 + (long long)blockIdx.y;
@@ -325,6 +444,13 @@ void router_onepass_kernel(const double* __restrict__ qr, const double* __restri
   T* ew = esum + wt * ntile * (long long)(kTile * nb);
   T* mw = emax + wt * ntile * (long long)kTile;
   const int row = threadIdx.x >> 2, part = threadIdx.x & 3;   // 4 threads per tile row
+  float aq[kF32 ? D / 4 : 1];
+  f32x4 kv[kF32 ? D / 16 : 1];
+  const float* kth = kt + (long long)blockIdx.y * ntile * kTile * D;
+  if constexpr (kF32) {
+    load_q_operands<D>(qh, nr, r0, aq);
+    load_k_share<D>(kth, 0, kv);
+  }
 
   // sweep: per column tile, the row maxima, then every (row, key block) sum
   // relative to them; the running row sum l is rescaled when the maximum grows
@@ -332,45 +458,63 @@ void router_onepass_kernel(const double* __restrict__ qr, const double* __restri
   double l = 0.0;
   for (int t = 0; t < ntile; ++t) {
     const int c0 = t * kTile;
-    if (threadIdx.x < kTile) {
-      const int c = c0 + threadIdx.x;
-      kpres[threadIdx.x] = c < nr && subcube_present(g, sc, c / G, c % G);
+    if constexpr (kF32) {
+      store_k_share<D>(kv, Ks);
+      __syncthreads();
+      load_k_share<D>(kth, min(t + 1, ntile - 1), kv);   // (the last tile reloads itself)
+      score_tile_f32<D>(aq, Ks, (float)scale, reinterpret_cast<float*>(S));
+    } else {
+      score_tile(qh, kh, nr, d, r0, c0, scale, As, Bs, S);
     }
-    score_tile(qh, kh, nr, d, r0, c0, scale, As, Bs, S);
+    // this thread's 16 columns of its row, the present ones among them, and
+    // the row maximum over the present columns of the tile
+    const unsigned pb = (unsigned)(pmask[t] >> (part * 16)) & 0xffffu;
+    T v[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) v[e] = S[row * (kTile + 1) + part * 16 + e];
     T tm = -INFINITY;
-    for (int e = 0; e < 16; ++e) {
-      const int c = part * 16 + e;
-      if (kpres[c]) tm = larger(tm, S[row * (kTile + 1) + c]);
-    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      if ((pb >> e) & 1u) tm = larger(tm, v[e]);
     tm = larger(tm, __shfl_xor(tm, 1, kWave));
     tm = larger(tm, __shfl_xor(tm, 2, kWave));
     if (tm > m) {
       if (m > -INFINITY) l *= exp((double)m - (double)tm);
       m = tm;
     }
-    if (part == 0) mrow[row] = m;
-    __syncthreads();
-    for (int u = threadIdx.x; u < kTile * nb; u += kThreads) {
-      const int rr = u / nb, bj = u - rr * nb;
-      const T mr = mrow[rr];
-      T e = 0;
-      if (mr > -INFINITY) {
-        for (int b = 0; b < G; ++b) {
-          const int cc = bj * G + b;
-          if (kpres[cc]) e += exp_of(S[rr * (kTile + 1) + cc] - mr);
+    // exponentials relative to the running maximum (pad sub-cubes: 0; a row
+    // with no present key so far has none in this tile either)
+    T rs = 0;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      v[e] = ((pb >> e) & 1u) ? exp_of(v[e] - m) : (T)0;
+      rs += v[e];
+    }
+    // per key block sums: 16 / G whole blocks of this thread (G <= 16), or
+    // one block over 2 or 4 threads of the row
+    T* et = ew + (long long)t * (kTile * nb) + row * nb;
+    switch (G) {
+      case 1: fold_blocks<1>(v, et + part * 16); break;
+      case 2: fold_blocks<2>(v, et + part * 8); break;
+      case 4: fold_blocks<4>(v, et + part * 4); break;
+      case 8: fold_blocks<8>(v, et + part * 2); break;
+      case 16: fold_blocks<16>(v, et + part); break;
+      default: {
+        T e = rs + __shfl_xor(rs, 1, kWave);
+        if (G == 32) {
+          if ((part & 1) == 0) et[part >> 1] = e;
+        } else {
+          e += __shfl_xor(e, 2, kWave);
+          if (part == 0) et[0] = e;
         }
       }
-      ew[(long long)t * (kTile * nb) + u] = e;
-      S[rr * (kTile + 1) + bj * G] = e;
     }
-    if (threadIdx.x < kTile) mw[(long long)t * kTile + threadIdx.x] = mrow[threadIdx.x];
-    __syncthreads();
-    double s = 0.0;
-    for (int bj = part; bj < nb; bj += 4) s += (double)S[row * (kTile + 1) + bj * G];
-    s += __shfl_xor(s, 1, kWave);
-    s += __shfl_xor(s, 2, kWave);
-    l += s;
-    __syncthreads();
+    if (part == 0) mw[(long long)t * kTile + row] = m;
+    double ds = (double)rs;
+    ds += __shfl_xor(ds, 1, kWave);
+    ds += __shfl_xor(ds, 2, kWave);
+    l += ds;
+    __syncthreads();   // S (and the staged K) are rewritten by the next tile
   }
   if (part == 0) lse[row] = (double)m + log(l);
   __syncthreads();
@@ -378,6 +522,7 @@ void router_onepass_kernel(const double* __restrict__ qr, const double* __restri
   // aggregation: P_r[i][j] = mean over the present query sub-cubes a of
   // exp(m_t(a) - lse(a)) * E[a][j]
   const int i0 = r0 / G;
+  const unsigned long long qpm = pmask[blockIdx.x];   // present query sub-cubes of the tile
   for (int t0 = 0; t0 < ntile; t0 += kCt) {
     const int ct = min(kCt, ntile - t0);
     for (int u = threadIdx.x; u < kTile * ct; u += kThreads) {
@@ -396,9 +541,9 @@ void router_onepass_kernel(const double* __restrict__ qr, const double* __restri
       double acc = 0.0;
       int na = 0;
       for (int a = 0; a < G; ++a) {
-        if (!subcube_present(g, sc, i, a)) continue;
-        ++na;
         const int rr = bi * G + a;
+        if (!((qpm >> rr) & 1ull)) continue;
+        ++na;
         acc += fac[rr * kCt + tt] * (double)et[rr * nb];
       }
       scores[(bh * n + i) * (long long)n + j0 + jj] = (T)log(acc / (double)na);
@@ -439,20 +584,33 @@ hipError_t router_t(const double* qr, const double* kr, T* scores, double scale,
   return hipGetLastError();
 }
 
-// Scratch of the one-pass kernel for one (batch*head), in elements of T:
-// the sums E and, after them, the running maxima.
+// Scratch of the one-pass kernel for one (batch*head), in elements of T: the
+// sums E and, after them, the running maxima; the float32 kernel also takes
+// K in float32 (kt, ntile * 64 * d floats).
 size_t onepass_head_elems(const Geom& g, const SubCube& sc, size_t& emax_off) {
   const size_t ntile = ((size_t)g.nblk * sc.G + kTile - 1) / kTile;
   emax_off = ntile * ntile * kTile * (size_t)(kTile / sc.G);
   return emax_off + ntile * ntile * kTile;
 }
 
+size_t onepass_head_bytes(const Geom& g, const SubCube& sc, size_t elem) {
+  size_t emax_off;
+  const size_t ntile = ((size_t)g.nblk * sc.G + kTile - 1) / kTile;
+  const size_t kt = elem == 4 ? ntile * kTile * (size_t)g.d * sizeof(float) : 0;
+  // three 256-byte alignments, and the presence words (counted per head for
+  // simplicity: one copy serves a chunk)
+  return onepass_head_elems(g, sc, emax_off) * elem + kt + ntile * 8 + 768;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
 template <typename T>
 hipError_t router_onepass_t(const double* qr, const double* kr, T* scores, double scale, const Geom& g, int rt,
                             int rh, int rw, void* workspace, size_t ws_bytes, hipStream_t s) {
   const SubCube sc = make_subcube(g, rt, rh, rw);
   size_t emax_off;
-  const size_t per_head = onepass_head_elems(g, sc, emax_off) * sizeof(T) + 256;
+  const size_t e_and_m = onepass_head_elems(g, sc, emax_off);
+  const size_t per_head = onepass_head_bytes(g, sc, sizeof(T));
   const int bh_total = g.batch * g.heads;
   const int chunk = (int)std::min<size_t>((size_t)bh_total, ws_bytes / per_head);
   if (chunk < 1) return hipErrorInvalidValue;   // the caller checks the size first
@@ -460,11 +618,27 @@ hipError_t router_onepass_t(const double* qr, const double* kr, T* scores, doubl
   const unsigned ntile = (unsigned)((nr + kTile - 1) / kTile);
   for (int bh0 = 0; bh0 < bh_total; bh0 += chunk) {
     const int hc = std::min(chunk, bh_total - bh0);
-    T* esum = static_cast<T*>(workspace);
-    // the maxima start on a 256-byte boundary after the chunk's sums
-    const size_t esum_bytes = (size_t)hc * emax_off * sizeof(T);
-    T* emax = reinterpret_cast<T*>(static_cast<char*>(workspace) + ((esum_bytes + 255) & ~(size_t)255));
-    router_onepass_kernel<T><<<dim3(ntile, hc), kThreads, 0, s>>>(qr, kr, scores, esum, emax, scale, g, sc, bh0);
+    // [E of the chunk][pad][maxima][pad][K in float32][pad][presence words]
+    char* base = static_cast<char*>(workspace);
+    T* esum = reinterpret_cast<T*>(base);
+    const size_t emax_at = align256((size_t)hc * emax_off * sizeof(T));
+    T* emax = reinterpret_cast<T*>(base + emax_at);
+    const size_t kt_at = align256(emax_at + (size_t)hc * (e_and_m - emax_off) * sizeof(T));
+    float* kt = reinterpret_cast<float*>(base + kt_at);
+    const size_t kt_bytes = std::is_same<T, float>::value ? (size_t)hc * ntile * kTile * g.d * sizeof(float) : 0;
+    unsigned long long* pmask = reinterpret_cast<unsigned long long*>(base + align256(kt_at + kt_bytes));
+    router_present_kernel<<<ntile * kTile / kThreads + 1, kThreads, 0, s>>>(pmask, g, sc, (int)nr);
+    if (std::is_same<T, float>::value) {
+      const long long quads = (long long)ntile * kTile * g.d / 4;
+      router_k32_kernel<<<dim3((unsigned)((quads + kThreads - 1) / kThreads), hc), kThreads, 0, s>>>(
+          kr, kt, (int)nr, g.d, (int)ntile, bh0);
+    }
+    if (g.d == 64)
+      router_onepass_kernel<T, 64><<<dim3(ntile, hc), kThreads, 0, s>>>(qr, kr, scores, esum, emax, kt, pmask,
+                                                                        scale, g, sc, bh0);
+    else
+      router_onepass_kernel<T, 128><<<dim3(ntile, hc), kThreads, 0, s>>>(qr, kr, scores, esum, emax, kt, pmask,
+                                                                         scale, g, sc, bh0);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -474,9 +648,7 @@ hipError_t router_onepass_t(const double* qr, const double* kr, T* scores, doubl
 }  // namespace
 
 size_t router_workspace_bytes(const Geom& g, int rt, int rh, int rw, size_t elem, int heads) {
-  const SubCube sc = make_subcube(g, rt, rh, rw);
-  size_t emax_off;
-  return (size_t)heads * (onepass_head_elems(g, sc, emax_off) * elem + 256);
+  return (size_t)heads * onepass_head_bytes(g, make_subcube(g, rt, rh, rw), elem);
 }
 
 namespace {
