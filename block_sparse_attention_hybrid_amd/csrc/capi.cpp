@@ -513,8 +513,8 @@ int32_t sparse_attn_block_scores_f32(const double* qbar, const double* kbar, flo
   sa::Geom d;
   SA_TRY(make_geom(g, d));
   if (d.nblk > 64 * 65535) return fail(SA_ERR_UNSUPPORTED, "too many blocks for the score grid");
-  SA_TRY(check_ptr(qbar, 8, "qbar"));
-  SA_TRY(check_ptr(kbar, 8, "kbar"));
+  SA_TRY(check_ptr(qbar, 16, "qbar"));
+  SA_TRY(check_ptr(kbar, 16, "kbar"));
   SA_TRY(check_ptr(scores, 4, "scores"));
   if (!std::isfinite(scale)) return fail(SA_ERR_INVALID_ARG, "scale must be finite");
   if (scale <= 0.0) scale = 1.0 / std::sqrt((double)d.d);

@@ -24,7 +24,7 @@ hipError_t launch_pool_groups(const void* xc, double* xbar, int qg, const Geom& 
 // nrows query rows per head (default nblk) against nblk key blocks
 hipError_t launch_block_scores(const double* qbar, const double* kbar, double* scores,
                                double scale, const Geom& g, hipStream_t s, int nrows = -1);
-// the same scores on the float32 matrix cores, written as float32
+// the same scores written as float32 (three-term bf16 splits on the bf16 matrix cores)
 hipError_t launch_block_scores(const double* qbar, const double* kbar, float* scores,
                                double scale, const Geom& g, hipStream_t s, int nrows = -1);
 // rows_per_head rows of nblk scores per head (default nblk)

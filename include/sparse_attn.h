@@ -5,8 +5,8 @@
  * The path (all steps are GPU kernels of this library):
  *   reorder      row-major video tokens -> cube-major blocks of 64 tokens
  *   pool         per-block mean of Q and K over the block's real tokens
- *   block_scores S = Qbar Kbar^T * scale (float32 matrix cores on the path;
- *                a float64 form beside it)
+ *   block_scores S = Qbar Kbar^T * scale (float32 scores from three-term
+ *                bf16 splits on the path; a float64 form beside it)
  *   select       per query block: hybrid Top-k U Top-p kept-block list
  *   fwd          block-sparse attention over the kept blocks -> O, LSE
  *                (fwd_tokens: the same, writing token order -- unreorder fused)
@@ -187,12 +187,16 @@ int32_t sparse_attn_block_scores(const double* qbar, const double* kbar,
                                  double* scores, double scale,
                                  const sa_geom* g, void* stream);
 
-/* The same block scores on the float32 matrix cores, written as float32: the
- * float64 means are rounded to float32 and the products summed in float32.
- * The page fixes no precision for this step; the error is a few 1e-7 of a
- * row's largest |score|, inside the 1e-6 relative margin at which two scores
- * count as tied for the selection.  Half the bytes of the float64 form.
- *   qbar, kbar [batch, heads, nblk, head_dim] float64   (inputs)
+/* The same block scores written as float32, computed on the bf16 matrix
+ * cores: each float64 mean is split into three bf16 terms (the remainder is
+ * below 2^-24 of the mean), the six term products that reach float32
+ * accuracy are summed in float32 (the largest apart from the five smaller),
+ * and the two sums are added and scaled in float64 before one rounding to
+ * float32.  The page fixes no precision for this step; the error is a few
+ * 1e-7 of a row's largest |score|, inside the 1e-6 relative margin at which
+ * two scores count as tied for the selection.  Half the bytes of the float64
+ * form.
+ *   qbar, kbar [batch, heads, nblk, head_dim] float64, 16-byte aligned (inputs)
  *   scores     [batch, heads, nblk, nblk] float32       (output) */
 int32_t sparse_attn_block_scores_f32(const double* qbar, const double* kbar,
                                      float* scores, double scale,

@@ -156,6 +156,10 @@ def test_select_argument_rules():
     assert lib.sparse_attn_block_scores_f32(FAKE, FAKE, ctypes.c_void_p(0x200002), 0.0, B,
                                             None) == sa.SA_ERR_INVALID_ARG    # scores misaligned
     assert lib.sparse_attn_block_scores_f32(FAKE, FAKE, FAKE, float("nan"), B, None) == sa.SA_ERR_INVALID_ARG
+    assert lib.sparse_attn_block_scores_f32(ctypes.c_void_p(0x100008), FAKE, FAKE, 0.0, B,
+                                            None) == sa.SA_ERR_INVALID_ARG    # means 8- but not 16-byte aligned
+    assert lib.sparse_attn_block_scores_f32(FAKE, ctypes.c_void_p(0x100008), FAKE, 0.0, B,
+                                            None) == sa.SA_ERR_INVALID_ARG
 
 
 def test_build_mask_argument_rules():

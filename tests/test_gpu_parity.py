@@ -165,6 +165,33 @@ def test_block_scores_f32(case):
     assert rel.max() <= 2e-6
 
 
+@pytest.mark.parametrize("grid,d", [((12, 40, 40), 128), ((16, 60, 52), 64), ((4, 16, 16), 128)])
+def test_block_scores_f32_tiles(grid, d):
+    """The float32 block scores over several 128 x 128 tiles with a ragged
+    last tile (300 and 780 blocks; 16 blocks: one partial tile), two heads,
+    means of mixed sign and magnitudes 1e-3..1e2 and exact zeros: within 2e-6
+    of each row's largest |score| of the oracle's float64 scores."""
+    g = sa.make_geom(1, 2, *grid, d)
+    nblk = sa.sparse_attn_geometry(g)[0]
+    say(f"[scores f32 tiles nblk={nblk} d={d}]")
+    rng = np.random.default_rng(11)
+    mag = 10.0 ** rng.uniform(-3, 2, size=(1, 2, nblk, 1))
+    qbar = rng.standard_normal((1, 2, nblk, d)) * mag
+    kbar = rng.standard_normal((1, 2, nblk, d)) * mag[:, ::-1]
+    qbar[0, 0, 5] = 0.0
+    kbar[0, 1, :, 7] = 0.0
+    want = np.stack([O.block_scores(qbar[0, h], kbar[0, h], d) for h in range(2)])[None]
+    s = torch.full((1, 2, nblk, nblk), 7.0, dtype=torch.float32, device=DEV)
+    sa.sparse_attn_block_scores_f32(torch.from_numpy(qbar).to(DEV), torch.from_numpy(kbar).to(DEV), s, 0.0, g)
+    torch.cuda.synchronize()
+    got = s.cpu().numpy().astype(np.float64)
+    scale = np.abs(want).max(axis=-1, keepdims=True)
+    rel = np.abs(got - want) / np.maximum(scale, 1e-300)
+    say(f"  scores f32: max error {rel.max():.2e} of the row's largest |score|")
+    assert np.all(got[0, 0, 5] == 0.0)
+    assert rel.max() <= 2e-6
+
+
 def test_select_f32_on_rounded_oracle_scores(case):
     """sparse_attn_select_f32 on the oracle's scores rounded to float32: the
     oracle's lists of exactly those values (the kernel widens them exactly),

@@ -84,20 +84,36 @@ def test_workload(name, wid, k_frac, p, budgets, heads, all_rows):
     del buf, t, o_ref_path, lse_ref_path
     say("  whole-path call (bench configuration) identical")
 
+    # the float32 block scores the path selects on, from its own means
+    qbar = torch.empty((wl.batch, wl.heads, n, wl.head_dim), dtype=torch.float64, device=DEV)
+    kbar = torch.empty_like(qbar)
+    sa.sparse_attn_pool(qc, kc, qbar, kbar, g)
+    s32 = torch.empty((wl.batch, wl.heads, n, n), dtype=torch.float32, device=DEV)
+    sa.sparse_attn_block_scores_f32(qbar, kbar, s32, 0.0, g)
+    s32_h = s32.cpu().numpy()
+    del qbar, kbar, s32
+
     # --- oracle lists on every head (one head at a time) ---------------------
     sel = list(heads)
     refs = {}
     n_bad = n_near = n_invalid = 0
+    worst_score = 0.0
     for h in range(wl.heads):
         qs, ks = (O.reorder(to64(t[:, h:h + 1]), og) for t in (q, k))
         ref = O.build_mask(qs, ks, og, k_frac, p, row_budget=None if not budgets else rb_np[:, h:h + 1])
+        # scores within 5e-7 of each row's largest |score|: a pair of scores
+        # at least the 1e-6 near-tie margin apart keeps its order
+        rowmax = np.abs(ref.scores[0, 0]).max(axis=-1, keepdims=True)
+        err = float((np.abs(s32_h[0, h].astype(np.float64) - ref.scores[0, 0]) / rowmax).max())
+        worst_score = max(worst_score, err)
+        assert err <= 5e-7, (h, err)
         bad, near, invalid = compare_lists(lut_h[:, h:h + 1], counts_h[:, h:h + 1], ref, p)
         n_bad, n_near, n_invalid = n_bad + len(bad), n_near + near, n_invalid + len(invalid)
         assert not bad and not invalid, (h, bad[:4], invalid[:4])
         if h in sel:
             refs[h] = ref
     say(f"  lists on all {wl.heads} heads: {n_bad} mismatches outside near ties, {n_near} near ties, "
-        f"{n_invalid} invalid")
+        f"{n_invalid} invalid; float32 scores within {worst_score:.2e} of each row's largest |score|")
 
     # oracle lists fed to the GPU attention, on the sampled heads at full shape
     ref_lut = np.concatenate([refs[h].lut for h in sel], axis=1)
