@@ -168,82 +168,135 @@ __device__ __forceinline__ void score_tile(const double* __restrict__ qh, const 
 
 // The float32 tile engine of the one-pass kernel.
 //
-// K in float32, laid out by a pre-pass so that one wavefront load moves 1 KB
-// of consecutive bytes: per (batch*head) and column tile t, D/4 chunks c of
-// four k values, each holding the tile's 64 columns in turn,
-//   kt[((t * (D / 4) + c) * 64 + col) * 4 + e] = K[64 t + col][4 c + e]
-// (zeros past the last sub-cube).  The kernel loads the next tile's share of
-// kt into registers while the current tile is multiplied and its softmax
-// taken, and writes it into LDS (pitch D + 4 floats) at the next tile's start.
+// The sub-cube scores come from exact three-term bf16 splits on the bf16
+// matrix cores: every float64 mean (Q's times the scale) is rounded to
+// float32 and that value split exactly into x0 + x1 + x2 (each the bf16
+// rounding of what the previous terms leave; |x1| <= 2^-8 |x|, |x2| <= 2^-16
+// |x|).  A score is the sum of the six term products of order <= 2, each
+// exact in float32, on v_mfma_f32_16x16x32_bf16 (16 times the float32 matrix
+// rate); the dropped products are below 2^-23 of |x y|, the level of the
+// operands' own float32 rounding.  x0 y0 and the five smaller products go to
+// two float32 accumulators, whose float32 sum is the score.
 //
-// Q's operands stay in registers for the whole sweep.  Wave w computes router
-// rows 16w .. 16w + 15 of the tile against its 64 columns with 16x16x4
-// products; product s = 4j + m of lane l takes k = 16j + 4(l >> 4) + m, so the
-// four products of one j read their K operands with one 16-byte LDS read:
-//   aq[4j + m] = Q[16w + (l & 15)][16j + 4(l >> 4) + m].
-__global__ __launch_bounds__(kThreads) void router_k32_kernel(const double* __restrict__ kr, float* __restrict__ kt,
-                                                              int nr, int d, int ntile, int bh0) {
-  const long long per_head = (long long)ntile * kTile * d;   // floats
-  const long long u = (long long)blockIdx.x * kThreads + threadIdx.x;   // one float4 each
-  if (u * 4 >= per_head) return;
-  const int bhc = blockIdx.y;
-  const int col = (int)(u & 63), c = (int)((u >> 6) % (d / 4)), t = (int)((u >> 6) / (d / 4));
-  const int j = t * kTile + col;
-  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (j < nr) {
-    const double* src = kr + ((long long)(bh0 + bhc) * nr + j) * d + 4 * c;
-    v = make_float4((float)src[0], (float)src[1], (float)src[2], (float)src[3]);
+// K's terms are laid out by a pre-pass so that one wavefront load moves 1 KB
+// of consecutive bytes: per (batch*head) and column tile t, 3 D / 8 chunks c =
+// term * (D / 8) + k8, each holding for the tile's 64 columns in turn the 8
+// bf16 of that term for k = 8 k8 .. +7 (zeros past the last sub-cube).  The
+// kernel loads the next tile's share into registers while the current tile
+// is multiplied and its softmax taken, and writes it into LDS at the next
+// tile's start: [term][column][k], a column's row padded to D + 8 bf16.
+//
+// Q's terms stay in registers for the whole sweep.  Wave w computes router
+// rows 16w .. 16w + 15 of the tile against its 64 columns; product j of lane
+// l takes k = 32j + 8 (l >> 4) .. +7 of row 16w + (l & 15) for A and of
+// column (l & 15) of each 16-column group for B; the accumulator's register r
+// holds row 4 (l >> 4) + r, column l & 15.
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  const f32x2v v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2v));
+}
+
+// two values -> their three bf16 terms, each pair packed (element 0 low): the
+// float32 rounding of each is the exact sum of its terms
+__device__ __forceinline__ void split_pair(double a, double b, uint32_t& t0, uint32_t& t1, uint32_t& t2) {
+  const float fa = (float)a, fb = (float)b;
+  t0 = pack2(fa, fb);
+  const float ra = fa - __uint_as_float(t0 << 16), rb = fb - __uint_as_float(t0 & 0xffff0000u);
+  t1 = pack2(ra, rb);
+  t2 = pack2(ra - __uint_as_float(t1 << 16), rb - __uint_as_float(t1 & 0xffff0000u));
+}
+
+__device__ __forceinline__ bf16x8 as_bf8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// the 8 values at p, scaled, as three u32x4 of bf16 terms
+__device__ __forceinline__ void split8(const double* p, double scale, u32x4& w0, u32x4& w1, u32x4& w2) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    uint32_t a, b, c;
+    split_pair(p[2 * e] * scale, p[2 * e + 1] * scale, a, b, c);
+    w0[e] = a;
+    w1[e] = b;
+    w2[e] = c;
   }
-  reinterpret_cast<float4*>(kt + (long long)bhc * per_head)[u] = v;
+}
+
+// One thread per (column tile, 8 k values, column): its three term chunks.
+__global__ __launch_bounds__(kThreads) void router_k32_kernel(const double* __restrict__ kr, u32x4* __restrict__ kt,
+                                                              int nr, int d, int ntile, int bh0) {
+  const int k8n = d / 8;
+  const long long per_head = (long long)ntile * k8n * kTile;   // threads (and chunks per term)
+  const long long u = (long long)blockIdx.x * kThreads + threadIdx.x;
+  if (u >= per_head) return;
+  const int bhc = blockIdx.y;
+  const int col = (int)(u & 63), k8 = (int)((u >> 6) % k8n), t = (int)((u >> 6) / k8n);
+  const int j = t * kTile + col;
+  u32x4 w0 = {0, 0, 0, 0}, w1 = w0, w2 = w0;
+  if (j < nr) split8(kr + ((long long)(bh0 + bhc) * nr + j) * d + 8 * k8, 1.0, w0, w1, w2);
+  u32x4* dst = kt + (long long)bhc * per_head * 3 + ((long long)t * 3 * k8n) * kTile + col;
+  dst[(0 * k8n + k8) * kTile] = w0;
+  dst[(1 * k8n + k8) * kTile] = w1;
+  dst[(2 * k8n + k8) * kTile] = w2;
 }
 
 template <int D>
-__device__ __forceinline__ void load_q_operands(const double* __restrict__ qh, int nr, int r0, float (&aq)[D / 4]) {
+__device__ __forceinline__ void load_q_operands(const double* __restrict__ qh, int nr, int r0, double scale,
+                                                u32x4 (&aq)[3][D / 32]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int gi = r0 + wave * 16 + (lane & 15);
-  const double* qrow = qh + (long long)(gi < nr ? gi : nr - 1) * D + 4 * (lane >> 4);
+  const double* qrow = qh + (long long)(gi < nr ? gi : nr - 1) * D + 8 * (lane >> 4);
 #pragma unroll
-  for (int j = 0; j < D / 16; ++j)
-#pragma unroll
-    for (int m = 0; m < 4; ++m) aq[4 * j + m] = gi < nr ? (float)qrow[16 * j + m] : 0.f;
+  for (int j = 0; j < D / 32; ++j) {
+    split8(qrow + 32 * j, gi < nr ? scale : 0.0, aq[0][j], aq[1][j], aq[2][j]);
+  }
 }
 
 // This thread's share of column tile t of kt: chunks c = 4i + wave, column
-// lane, for i < D / 16.
+// lane, for i < 3 D / 32.
 template <int D>
-__device__ __forceinline__ void load_k_share(const float* __restrict__ kth, int t, f32x4 (&kv)[D / 16]) {
+__device__ __forceinline__ void load_k_share(const u32x4* __restrict__ kth, int t, u32x4 (&kv)[3 * D / 32]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const f32x4* src = reinterpret_cast<const f32x4*>(kth + (long long)t * kTile * D);
+  const u32x4* src = kth + (long long)t * 3 * (D / 8) * kTile;
 #pragma unroll
-  for (int i = 0; i < D / 16; ++i) kv[i] = src[(4 * i + wave) * 64 + lane];
+  for (int i = 0; i < 3 * D / 32; ++i) kv[i] = src[(4 * i + wave) * 64 + lane];
 }
 
 template <int D>
-__device__ __forceinline__ void store_k_share(const f32x4 (&kv)[D / 16], float* Ks) {
+__device__ __forceinline__ void store_k_share(const u32x4 (&kv)[3 * D / 32], __bf16* Ks) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int i = 0; i < D / 16; ++i)
-    *reinterpret_cast<f32x4*>(Ks + lane * (D + 4) + 4 * (4 * i + wave)) = kv[i];
+  for (int i = 0; i < 3 * D / 32; ++i) {
+    const int c = 4 * i + wave, term = c / (D / 8), k8 = c % (D / 8);
+    *reinterpret_cast<u32x4*>(Ks + (term * kTile + lane) * (D + 8) + 8 * k8) = kv[i];
+  }
 }
 
-// Scores of the tile from the staged K (LDS, pitch D + 4) into S (pitch
-// kTile + 1), scaled.  Ends with a barrier; the caller's barrier before it
-// ordered the K writes.
+// Scores of the tile from the staged K terms (LDS) into S (pitch kTile + 1).
+// Ends with a barrier; the caller's barrier before it ordered the K writes.
 template <int D>
-__device__ __forceinline__ void score_tile_f32(const float (&aq)[D / 4], const float* Ks, float scale, float* S) {
+__device__ __forceinline__ void score_tile_f32(const u32x4 (&aq)[3][D / 32], const __bf16* Ks, float* S) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  f32x4 acc[4];
+  f32x4 big[4], small[4];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4{0, 0, 0, 0};
+  for (int nt = 0; nt < 4; ++nt) big[nt] = small[nt] = f32x4{0, 0, 0, 0};
 #pragma unroll
-  for (int j = 0; j < D / 16; ++j) {
+  for (int j = 0; j < D / 32; ++j) {
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
-      const f32x4 b = *reinterpret_cast<const f32x4*>(Ks + (nt * 16 + (lane & 15)) * (D + 4) + 16 * j +
-                                                        4 * (lane >> 4));
+      const __bf16* kb = Ks + (nt * 16 + (lane & 15)) * (D + 8) + 32 * j + 8 * (lane >> 4);
+      u32x4 b[3];
 #pragma unroll
-      for (int m = 0; m < 4; ++m)
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(aq[4 * j + m], b[m], acc[nt], 0, 0, 0);
+      for (int tb = 0; tb < 3; ++tb) b[tb] = *reinterpret_cast<const u32x4*>(kb + tb * kTile * (D + 8));
+      f32x4 c = small[nt];
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(aq[2][j]), as_bf8(b[0]), c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(aq[1][j]), as_bf8(b[1]), c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(aq[0][j]), as_bf8(b[2]), c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(aq[1][j]), as_bf8(b[0]), c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(aq[0][j]), as_bf8(b[1]), c, 0, 0, 0);
+      small[nt] = c;
+      big[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(aq[0][j]), as_bf8(b[0]), big[nt], 0, 0, 0);
     }
   }
   __syncthreads();   // the staged K is dead; S takes its place
@@ -251,7 +304,7 @@ __device__ __forceinline__ void score_tile_f32(const float (&aq)[D / 4], const f
   for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      S[(wave * 16 + 4 * (lane >> 4) + r) * (kTile + 1) + nt * 16 + (lane & 15)] = acc[nt][r] * scale;
+      S[(wave * 16 + 4 * (lane >> 4) + r) * (kTile + 1) + nt * 16 + (lane & 15)] = big[nt][r] + small[nt][r];
   __syncthreads();
 }
 
@@ -408,17 +461,23 @@ __global__ __launch_bounds__(kThreads) void router_present_kernel(unsigned long 
 // Scratch per (batch*head) of a chunk, for row tile x and column tile t:
 //   esum[((x * ntile) + t) * 64 * nb + row * nb + jb]   (nb = 64 / G blocks)
 //   emax[((x * ntile) + t) * 64 + row]
+// The float32 kernel at two waves per SIMD (168 registers at three spill;
+// 10.6 against 11.0 ms at 720p)
+#ifndef SA_ROUTER_F32_WAVES
+#define SA_ROUTER_F32_WAVES 2
+#endif
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(std::is_same<T, double>::value ? 4 : SA_ROUTER_F32_WAVES)))
 void router_onepass_kernel(const double* __restrict__ qr, const double* __restrict__ kr, T* __restrict__ scores,
-                           T* __restrict__ esum, T* __restrict__ emax, const float* __restrict__ kt,
+                           T* __restrict__ esum, T* __restrict__ emax, const u32x4* __restrict__ kt,
                            const unsigned long long* __restrict__ pmask, double scale, Geom g, SubCube sc,
                            int bh0) {
   // float32: the engine above (Q in registers, K from kt, a whole tile staged
   // at once); float64, whose operands would take twice the registers: both
   // operands staged 16 k columns at a time (score_tile)
   constexpr bool kF32 = !std::is_same<T, double>::value;
-  constexpr int kStage = kF32 ? kTile * (D + 4) * 4 / (int)sizeof(T) : 2 * kTile * kLd;
+  constexpr int kStage = kF32 ? 3 * kTile * (D + 8) * 2 / (int)sizeof(T) : 2 * kTile * kLd;
   constexpr int kScores = kTile * (kTile + 1);
   constexpr int kCt = 16;   // column tiles per aggregation step
   // the aggregation's rescaling factors reuse the staging area
@@ -429,7 +488,7 @@ void router_onepass_kernel(const double* __restrict__ qr, const double* __restri
   T* As = smem;
   T* Bs = smem + kTile * kLd;
   T* S = smem;
-  float* Ks = reinterpret_cast<float*>(smem_raw);
+  __bf16* Ks = reinterpret_cast<__bf16*>(smem_raw);
   double* fac = smem_raw;
   __shared__ double lse[kTile];
   // (the float64 engine keeps its k loop on the run-time head size: unrolled,
@@ -444,11 +503,11 @@ void router_onepass_kernel(const double* __restrict__ qr, const double* __restri
   T* ew = esum + wt * ntile * (long long)(kTile * nb);
   T* mw = emax + wt * ntile * (long long)kTile;
   const int row = threadIdx.x >> 2, part = threadIdx.x & 3;   // 4 threads per tile row
-  float aq[kF32 ? D / 4 : 1];
-  f32x4 kv[kF32 ? D / 16 : 1];
-  const float* kth = kt + (long long)blockIdx.y * ntile * kTile * D;
+  u32x4 aq[3][kF32 ? D / 32 : 1];
+  u32x4 kv[kF32 ? 3 * D / 32 : 1];
+  const u32x4* kth = kt + (long long)blockIdx.y * ntile * 3 * (D / 8) * kTile;
   if constexpr (kF32) {
-    load_q_operands<D>(qh, nr, r0, aq);
+    load_q_operands<D>(qh, nr, r0, scale, aq);
     load_k_share<D>(kth, 0, kv);
   }
 
@@ -462,7 +521,7 @@ void router_onepass_kernel(const double* __restrict__ qr, const double* __restri
       store_k_share<D>(kv, Ks);
       __syncthreads();
       load_k_share<D>(kth, min(t + 1, ntile - 1), kv);   // (the last tile reloads itself)
-      score_tile_f32<D>(aq, Ks, (float)scale, reinterpret_cast<float*>(S));
+      score_tile_f32<D>(aq, Ks, reinterpret_cast<float*>(S));
     } else {
       score_tile(qh, kh, nr, d, r0, c0, scale, As, Bs, S);
     }
@@ -586,7 +645,7 @@ hipError_t router_t(const double* qr, const double* kr, T* scores, double scale,
 
 // Scratch of the one-pass kernel for one (batch*head), in elements of T: the
 // sums E and, after them, the running maxima; the float32 kernel also takes
-// K in float32 (kt, ntile * 64 * d floats).
+// K's three bf16 terms (kt, 3 * ntile * 64 * d bf16).
 size_t onepass_head_elems(const Geom& g, const SubCube& sc, size_t& emax_off) {
   const size_t ntile = ((size_t)g.nblk * sc.G + kTile - 1) / kTile;
   emax_off = ntile * ntile * kTile * (size_t)(kTile / sc.G);
@@ -596,7 +655,7 @@ size_t onepass_head_elems(const Geom& g, const SubCube& sc, size_t& emax_off) {
 size_t onepass_head_bytes(const Geom& g, const SubCube& sc, size_t elem) {
   size_t emax_off;
   const size_t ntile = ((size_t)g.nblk * sc.G + kTile - 1) / kTile;
-  const size_t kt = elem == 4 ? ntile * kTile * (size_t)g.d * sizeof(float) : 0;
+  const size_t kt = elem == 4 ? 3 * ntile * kTile * (size_t)g.d * 2 : 0;
   // three 256-byte alignments, and the presence words (counted per head for
   // simplicity: one copy serves a chunk)
   return onepass_head_elems(g, sc, emax_off) * elem + kt + ntile * 8 + 768;
@@ -618,19 +677,19 @@ hipError_t router_onepass_t(const double* qr, const double* kr, T* scores, doubl
   const unsigned ntile = (unsigned)((nr + kTile - 1) / kTile);
   for (int bh0 = 0; bh0 < bh_total; bh0 += chunk) {
     const int hc = std::min(chunk, bh_total - bh0);
-    // [E of the chunk][pad][maxima][pad][K in float32][pad][presence words]
+    // [E of the chunk][pad][maxima][pad][K's bf16 terms][pad][presence words]
     char* base = static_cast<char*>(workspace);
     T* esum = reinterpret_cast<T*>(base);
     const size_t emax_at = align256((size_t)hc * emax_off * sizeof(T));
     T* emax = reinterpret_cast<T*>(base + emax_at);
     const size_t kt_at = align256(emax_at + (size_t)hc * (e_and_m - emax_off) * sizeof(T));
-    float* kt = reinterpret_cast<float*>(base + kt_at);
-    const size_t kt_bytes = std::is_same<T, float>::value ? (size_t)hc * ntile * kTile * g.d * sizeof(float) : 0;
+    u32x4* kt = reinterpret_cast<u32x4*>(base + kt_at);
+    const size_t kt_bytes = std::is_same<T, float>::value ? (size_t)hc * 3 * ntile * kTile * g.d * 2 : 0;
     unsigned long long* pmask = reinterpret_cast<unsigned long long*>(base + align256(kt_at + kt_bytes));
     router_present_kernel<<<ntile * kTile / kThreads + 1, kThreads, 0, s>>>(pmask, g, sc, (int)nr);
     if (std::is_same<T, float>::value) {
-      const long long quads = (long long)ntile * kTile * g.d / 4;
-      router_k32_kernel<<<dim3((unsigned)((quads + kThreads - 1) / kThreads), hc), kThreads, 0, s>>>(
+      const long long items = (long long)ntile * kTile * g.d / 8;
+      router_k32_kernel<<<dim3((unsigned)((items + kThreads - 1) / kThreads), hc), kThreads, 0, s>>>(
           kr, kt, (int)nr, g.d, (int)ntile, bh0);
     }
     if (g.d == 64)

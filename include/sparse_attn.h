@@ -254,11 +254,14 @@ int32_t sparse_attn_router_scores(const double* qr, const double* kr,
                                   int32_t rw, void* workspace,
                                   size_t workspace_bytes, void* stream);
 
-/* sparse_attn_router_scores on the float32 matrix cores: the sub-cube means
- * rounded to float32, the sub-cube scores and their exponentials in float32,
- * the row log-sum-exp accumulated in float64, and log P_r written as float32
- * for sparse_attn_select_f32.  Checked against the float64 lists of the
- * oracle outside near ties.  Workspace as above (its size for score_bytes 4).
+/* sparse_attn_router_scores in float32: the sub-cube means rounded to
+ * float32, the sub-cube scores (with a workspace: summed in float32 from
+ * exact three-term bf16 splits of those means on the bf16 matrix cores;
+ * without one: on the float32 matrix cores) and their exponentials in
+ * float32, the row log-sum-exp accumulated in float64, and log P_r written as
+ * float32 for sparse_attn_select_f32.  Checked against the float64 lists of
+ * the oracle outside near ties.  Workspace as above (its size for
+ * score_bytes 4).
  *   scores [batch, heads, nblk, nblk] float32 = log P_r               (output) */
 int32_t sparse_attn_router_scores_f32(const double* qr, const double* kr,
                                       float* scores, double scale, const sa_geom* g,
