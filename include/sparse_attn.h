@@ -272,7 +272,7 @@ int32_t sparse_attn_router_scores_f32(const double* qr, const double* kr,
 /* Bytes of workspace for the one-pass router over every (batch, head):
  * score_bytes 8 for sparse_attn_router_scores, 4 for the float32 form (0 for
  * an invalid geometry, sub-cube or score_bytes).  At 720p with 2x2x2
- * sub-cubes that is about 150 MB (float64) or 75 MB (float32) per head. */
+ * sub-cubes that is about 150 MB (float64) or 84 MB (float32) per head. */
 size_t sparse_attn_router_workspace_bytes(const sa_geom* g, int32_t rt,
                                           int32_t rh, int32_t rw,
                                           int32_t score_bytes);

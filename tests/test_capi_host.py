@@ -340,7 +340,7 @@ def test_noalloc_mask_rejects_before_any_launch():
 def test_router_workspace_rules():
     """The one-pass router's scratch, per head: one value per (router row,
     key block) and one running maximum per (router row, column tile of 64
-    sub-cubes); for the float32 form also K in float32; one 64-bit presence
+    sub-cubes); for the float32 form also K's three bf16 terms; one 64-bit presence
     word per column tile; three 256-byte alignment pads.  A workspace that
     holds no head is a capacity error and a misaligned one an argument error,
     before any launch."""
@@ -352,12 +352,12 @@ def test_router_workspace_rules():
                 nt = -(-n * G // 64)
                 per_head_elems = nt * nt * 64 * (64 // G) + nt * nt * 64
                 for elem in (4, 8):
-                    kt = nt * 64 * d * 4 if elem == 4 else 0
+                    kt = 3 * nt * 64 * d * 2 if elem == 4 else 0
                     want = g.batch * g.heads * (per_head_elems * elem + kt + nt * 8 + 768)
                     assert sa.sparse_attn_router_workspace_bytes(g, sub, elem) == want
     g720 = geom(frames=21, height=45, width=80, head_dim=128)
-    # 80.5 MB a head in float32
-    assert sa.sparse_attn_router_workspace_bytes(g720, (2, 2, 2), 4) == 2 * (74_649_600 + 5_898_240 + 1_440 + 768)
+    # 83.5 MB a head in float32
+    assert sa.sparse_attn_router_workspace_bytes(g720, (2, 2, 2), 4) == 2 * (74_649_600 + 8_847_360 + 1_440 + 768)
     assert sa.sparse_attn_router_workspace_bytes(g720, (2, 2, 2), 2) == 0
     assert sa.sparse_attn_router_workspace_bytes(g720, (3, 2, 2), 4) == 0
     one = sa.sparse_attn_router_workspace_bytes(g720, (2, 2, 2), 8) // 2
