@@ -31,6 +31,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kTile = 64;          // router rows / columns per tile
 constexpr int kKc = 16;            // k columns staged per step
+constexpr int kSPitch32 = kTile + 4; // float32 score tile pitch of the one-pass kernel
 constexpr int kLd = kKc + 1;
 
 struct SubCube {
@@ -273,7 +274,10 @@ __device__ __forceinline__ void store_k_share(const u32x4 (&kv)[3 * D / 32], __b
   }
 }
 
-// Scores of the tile from the staged K terms (LDS) into S (pitch kTile + 1).
+// Scores of the tile from the staged K terms (LDS) into S (pitch kSPitch32:
+// 4 mod 64 floats, so a wavefront's writes of four rows by 16 columns hit 64
+// different banks, and 16-byte aligned rows for the 16-byte reads of a
+// thread's 16 columns).
 // Ends with a barrier; the caller's barrier before it ordered the K writes.
 template <int D>
 __device__ __forceinline__ void score_tile_f32(const u32x4 (&aq)[3][D / 32], const __bf16* Ks, float* S) {
@@ -304,7 +308,7 @@ __device__ __forceinline__ void score_tile_f32(const u32x4 (&aq)[3][D / 32], con
   for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      S[(wave * 16 + 4 * (lane >> 4) + r) * (kTile + 1) + nt * 16 + (lane & 15)] = big[nt][r] + small[nt][r];
+      S[(wave * 16 + 4 * (lane >> 4) + r) * kSPitch32 + nt * 16 + (lane & 15)] = big[nt][r] + small[nt][r];
   __syncthreads();
 }
 
@@ -478,7 +482,8 @@ void router_onepass_kernel(const double* __restrict__ qr, const double* __restri
   // operands staged 16 k columns at a time (score_tile)
   constexpr bool kF32 = !std::is_same<T, double>::value;
   constexpr int kStage = kF32 ? 3 * kTile * (D + 8) * 2 / (int)sizeof(T) : 2 * kTile * kLd;
-  constexpr int kScores = kTile * (kTile + 1);
+  constexpr int kSP = kF32 ? kSPitch32 : kTile + 1;   // score tile pitch
+  constexpr int kScores = kTile * kSP;
   constexpr int kCt = 16;   // column tiles per aggregation step
   // the aggregation's rescaling factors reuse the staging area
   constexpr int kWords = ((kStage > kScores ? kStage : kScores) * (int)sizeof(T) + 7) / 8;
@@ -530,7 +535,7 @@ void router_onepass_kernel(const double* __restrict__ qr, const double* __restri
     const unsigned pb = (unsigned)(pmask[t] >> (part * 16)) & 0xffffu;
     T v[16];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) v[e] = S[row * (kTile + 1) + part * 16 + e];
+    for (int e = 0; e < 16; ++e) v[e] = S[row * kSP + part * 16 + e];
     T tm = -INFINITY;
 #pragma unroll
     for (int e = 0; e < 16; ++e)
