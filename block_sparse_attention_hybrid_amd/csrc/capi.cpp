@@ -470,8 +470,8 @@ int32_t sa_validate_path(const sa_path_buffers* b, const sa_geom* g, double k_fr
   SA_TRY(check_ptr(b->qc, 16, "qc"));
   SA_TRY(check_ptr(b->kc, 16, "kc"));
   SA_TRY(check_ptr(b->vc, 16, "vc"));
-  SA_TRY(check_ptr(b->qbar, 8, "qbar"));
-  SA_TRY(check_ptr(b->kbar, 8, "kbar"));
+  SA_TRY(check_ptr(b->qbar, 16, "qbar"));   // read in 16-byte pieces by the float32 block scores
+  SA_TRY(check_ptr(b->kbar, 16, "kbar"));
   SA_TRY(check_ptr(b->scores, 8, "scores"));
   // oc and lse_c: both given (slot-major O and LSE are written too) or both NULL
   if (outputs) {

@@ -286,7 +286,8 @@ typedef struct sa_path_buffers {
   void* qc;             /* [batch, heads, n_pad, head_dim] bf16, cube-major operands (written) */
   void* kc;
   void* vc;
-  double* qbar;         /* [batch, heads, nblk, head_dim] float64 block means (written) */
+  double* qbar;         /* [batch, heads, nblk, head_dim] float64 block means (written),
+                           16-byte aligned (as kbar) */
   double* kbar;
   void* scores;         /* workspace of batch*heads*nblk*nblk*8 bytes, 8-byte aligned; holds
                            the float32 pooled scores [batch, heads, nblk, nblk] in its first

@@ -271,6 +271,10 @@ def test_whole_path_argument_rules():
     assert call(buffers(cap=15)) == sa.SA_ERR_CAPACITY               # Top-p may keep all 16 blocks
     assert call(buffers(), k_frac=float("nan")) == sa.SA_ERR_INVALID_ARG
     assert call(buffers(), chunk=0) == sa.SA_ERR_INVALID_ARG
+    # the block means are read in 16-byte pieces
+    assert call(buffers(qbar=F + 0x60008)) == sa.SA_ERR_INVALID_ARG
+    assert "qbar" in sa.sparse_attn_last_error()
+    assert call(buffers(kbar=F + 0x70008)) == sa.SA_ERR_INVALID_ARG
     # the mask phase alone takes no output buffers
     def mask_call(buf, k_frac=0.25, p=0.5):
         return lib.sparse_attn_mask_path(ctypes.byref(buf), B, k_frac, p, None, None)
