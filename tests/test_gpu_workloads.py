@@ -284,3 +284,43 @@ def test_per_sequence_full_size():
     bad, near = check_per_sequence(lut.cpu().numpy(), c, s.cpu().numpy(), 0.03)
     say(f"  per-sequence: {bad} count mismatches, {near} near-tie rows; counts min {c.min()} max {c.max()}")
     assert bad == 0
+
+
+@pytest.mark.parametrize("p", [0.1, 0.999], ids=["one-wave", "dense-groups"])
+def test_largest_head(p):
+    """The whole path at the largest head the library takes (4,096 blocks:
+    a 16x128x128 latent grid, 262,144 tokens, one skewed head, d = 128), on
+    lists of about a tenth of the blocks (the one-wave forward) and on nearly
+    dense ones (the dense-group kernel, whose LDS list bitmaps are sized for
+    4,096 blocks): every row's list against the
+    oracle's, and the attention of sampled query blocks with the oracle's
+    lists fed to the GPU forward."""
+    wl = synth.custom_workload(1, 1, 128, 16, 128, 128, head_types=("skewed",), wid=101, name="largest")
+    g, og = geom_of(wl), ogeom_of(wl)
+    n = og.nblk
+    assert n == 4096 and sa.sparse_attn_geometry(g)[0] == n
+    say(f"[largest head] nblk={n} tokens={og.n_real} p={p}")
+    q, k, v = synth.make_qkv(wl, 0)
+    qc = sa.reorder(q.to(DEV), g, sa.SA_LAYOUT_QK)
+    kc = sa.reorder(k.to(DEV), g, sa.SA_LAYOUT_QK)
+    vc = sa.reorder(v.to(DEV), g, sa.SA_LAYOUT_V)
+    lut, counts = sa.build_mask(qc, kc, g, 0.03, p)
+    torch.cuda.synchronize()
+    qs, ks, vs = (O.reorder(to64(t), og) for t in (q, k, v))
+    ref = O.build_mask(qs, ks, og, 0.03, p)
+    bad, near, invalid = compare_lists(lut.cpu().numpy(), counts.cpu().numpy(), ref, p)
+    say(f"  lists: {len(bad)} mismatches outside near ties, {near} near ties, {len(invalid)} invalid; "
+        f"mean count {ref.counts.mean():.1f}")
+    assert not bad and not invalid
+    oc, lse_c = sa.fwd(qc, kc, vc, torch.from_numpy(ref.lut).to(DEV), torch.from_numpy(ref.counts).to(DEV), g)
+    torch.cuda.synchronize()
+    oc_h, lse_h = to64(oc), lse_c.cpu().double().numpy()
+    real = O.real_slots(og)
+    for i in (0, 1, n // 2, n - 1):
+        kept = ref.lut[0, 0, i, :ref.counts[0, 0, i]]
+        o_ref, l_ref = O.attention_block(qs[0, 0], ks[0, 0], vs[0, 0], kept, og, i)
+        mx, mean = attn_errors(oc_h[0, 0, i * 64:(i + 1) * 64], o_ref, real[i * 64:(i + 1) * 64])
+        lmx, lmean = lse_errors(lse_h[0, 0, i * 64:(i + 1) * 64], l_ref)
+        assert mx <= O_MAX_ABS and mean <= O_MEAN_ABS, (i, mx, mean)
+        assert lmx <= LSE_MAX_ABS and lmean <= LSE_MEAN_ABS, (i, lmx, lmean)
+    say(f"  attention of 4 query blocks within the bars")
